@@ -1,0 +1,195 @@
+"""CPU oracle for the expert-parallel dispatch/combine core.
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg may import this package; the product path never does.  It
+wraps ``ep_oracle.c`` (plain single-threaded C, built with gcc) through ctypes
+and numpy.  It shares no code with the HIP library.
+
+Every function takes and returns numpy arrays; shapes follow the definitions
+in ``ep_oracle.c`` (each cites the page passage it follows).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+SOURCE = os.path.join(_HERE, "ep_oracle.c")
+LIBRARY = os.path.join(_HERE, "libep_oracle.so")
+CFLAGS = ["-O2", "-ffp-contract=off", "-fPIC", "-shared", "-std=c11", "-Wall", "-Wextra"]
+
+BAD_TOPK_IDX = 1
+RECV_OVERFLOW = 2
+COUNT_MISMATCH = 4
+BAD_SEND_SLOT = 8
+
+
+def build(source: str = SOURCE, out: str = LIBRARY) -> str:
+    """Compile the oracle with gcc; returns the path of the shared library."""
+    cmd = ["gcc", *CFLAGS, source, "-o", out + ".tmp", "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(out + ".tmp", out)
+    return out
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_L = ctypes.c_int64
+
+
+def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    lib.oracle_layout.argtypes = [_I, _I, _I, _I, _P, _P, _P, _P, _P]
+    lib.oracle_notify.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]
+    lib.oracle_dispatch.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I] + [_P] * 11
+    lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
+    lib.oracle_combine_f64.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P]
+    lib.oracle_bf16_round.argtypes = [_P, _P, _L]
+    for name in ("oracle_layout", "oracle_notify", "oracle_dispatch", "oracle_combine", "oracle_combine_f64"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.oracle_bf16_round.restype = None
+    return lib
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load a built oracle library (building it first if it is absent)."""
+    if not os.path.exists(path):
+        build(out=path)
+    return _declare(ctypes.CDLL(path))
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        _lib = load()
+    return _lib
+
+
+def _ptr(a: np.ndarray | None) -> int | None:
+    if a is None:
+        return None
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data
+
+
+def num_nodes(R: int) -> int:
+    return max(1, R // 8)
+
+
+class Oracle:
+    """Numpy front end of one oracle library (the default one, or a variant)."""
+
+    def __init__(self, handle: ctypes.CDLL | None = None):
+        self.lib = handle if handle is not None else lib()
+
+    def layout(self, topk_idx: np.ndarray, E: int, R: int):
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        T, K = topk_idx.shape
+        per_rank = np.zeros(R, np.int32)
+        per_node = np.zeros(num_nodes(R), np.int32)
+        per_expert = np.zeros(E, np.int32)
+        in_rank = np.zeros((T, R), np.uint8)
+        st = self.lib.oracle_layout(T, K, E, R, _ptr(topk_idx), _ptr(per_rank), _ptr(per_node),
+                                    _ptr(per_expert), _ptr(in_rank))
+        return dict(num_tokens_per_rank=per_rank, num_tokens_per_rdma_rank=per_node,
+                    num_tokens_per_expert=per_expert, is_token_in_rank=in_rank, status=st)
+
+    def notify(self, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank,
+               num_tokens_per_expert, C: int, expert_alignment: int = 1):
+        in_rank = np.ascontiguousarray(is_token_in_rank, dtype=np.uint8)
+        T, R = in_rank.shape
+        E = len(num_tokens_per_expert)
+        nodes = num_nodes(R)
+        gbl = np.zeros((R, C), np.int32)
+        rdma = np.zeros((nodes, C), np.int32)
+        recv_gbl = np.zeros(R, np.int32)
+        recv_rdma = np.zeros(nodes, np.int32)
+        recv_per_expert = np.zeros(E, np.int32)
+        n_recv = np.zeros(1, np.int32)
+        a = [np.ascontiguousarray(v, dtype=np.int32) for v in
+             (num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert)]
+        st = self.lib.oracle_notify(T, E, R, C, expert_alignment, _ptr(in_rank), _ptr(a[0]), _ptr(a[1]),
+                                    _ptr(a[2]), _ptr(gbl), _ptr(rdma), _ptr(recv_gbl), _ptr(recv_rdma),
+                                    _ptr(recv_per_expert), _ptr(n_recv))
+        return dict(gbl_channel_prefix_matrix=gbl, rdma_channel_prefix_matrix=rdma,
+                    recv_gbl_rank_prefix_sum=recv_gbl, recv_rdma_rank_prefix_sum=recv_rdma,
+                    num_recv_tokens_per_expert=recv_per_expert, num_recv_tokens=int(n_recv[0]), status=st)
+
+    def dispatch(self, x, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+                 recv_gbl_rank_prefix_sum, E: int, my_rank: int = 0, recv_capacity: int | None = None,
+                 with_topk_idx: bool = True):
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        topk_weights = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        in_rank = np.ascontiguousarray(is_token_in_rank, dtype=np.uint8)
+        gbl = np.ascontiguousarray(gbl_channel_prefix_matrix, dtype=np.int32)
+        recv_gbl = np.ascontiguousarray(recv_gbl_rank_prefix_sum, dtype=np.int32)
+        T, H = x.shape
+        K = topk_idx.shape[1]
+        R, C = gbl.shape
+        n = int(recv_gbl[-1]) if R else 0
+        cap = n if recv_capacity is None else recv_capacity
+        recv_x = np.zeros((cap, H), np.uint16)
+        recv_w = np.zeros((cap, K), np.float32)
+        recv_idx = np.zeros((cap, K), np.int64) if with_topk_idx else None
+        src_info = np.zeros((cap, 2), np.int32)
+        send_slot = np.zeros((T, R), np.int32)
+        st = self.lib.oracle_dispatch(T, H, K, E, R, C, my_rank, cap, _ptr(x), _ptr(topk_idx),
+                                      _ptr(topk_weights), _ptr(in_rank), _ptr(gbl), _ptr(recv_gbl),
+                                      _ptr(recv_x), _ptr(recv_w), _ptr(recv_idx), _ptr(src_info),
+                                      _ptr(send_slot))
+        return dict(recv_x=recv_x, recv_topk_weights=recv_w, recv_topk_idx=recv_idx,
+                    recv_src_info=src_info, send_slot=send_slot, status=st)
+
+    def combine(self, y, recv_topk_weights, send_slot, num_recv: int, with_weights: bool = True):
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        recv_w = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
+        send_slot = np.ascontiguousarray(send_slot, dtype=np.int32)
+        T, R = send_slot.shape
+        H = y.shape[1]
+        K = recv_w.shape[1]
+        out = np.zeros((T, H), np.uint16)
+        cw = np.zeros((T, K), np.float32) if with_weights else None
+        scratch = np.zeros(max(H, 1), np.float32)
+        st = self.lib.oracle_combine(T, H, K, R, num_recv, _ptr(y), _ptr(recv_w), _ptr(send_slot),
+                                     _ptr(out), _ptr(cw), _ptr(scratch))
+        return dict(combined_x=out, combined_topk_weights=cw, status=st)
+
+    def combine_f64(self, y, recv_topk_weights, send_slot, num_recv: int):
+        y = np.ascontiguousarray(y, dtype=np.uint16)
+        recv_w = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
+        send_slot = np.ascontiguousarray(send_slot, dtype=np.int32)
+        T, R = send_slot.shape
+        H = y.shape[1]
+        K = recv_w.shape[1]
+        out = np.zeros((T, H), np.float64)
+        st = self.lib.oracle_combine_f64(T, H, K, R, num_recv, _ptr(y), _ptr(recv_w), _ptr(send_slot),
+                                         _ptr(out))
+        return out, st
+
+    def bf16_round(self, f: np.ndarray) -> np.ndarray:
+        f = np.ascontiguousarray(f, dtype=np.float32)
+        out = np.zeros(f.shape, np.uint16)
+        self.lib.oracle_bf16_round(_ptr(f), _ptr(out), f.size)
+        return out
+
+    def full(self, x, topk_idx, topk_weights, E: int, R: int, C: int, expert_alignment: int = 1,
+             my_rank: int = 0, y=None):
+        """All four stages in order; combine reads ``y`` (identity experts when None)."""
+        lay = self.layout(topk_idx, E, R)
+        note = self.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"],
+                           lay["num_tokens_per_rdma_rank"], lay["num_tokens_per_expert"], C, expert_alignment)
+        dis = self.dispatch(x, topk_idx, topk_weights, lay["is_token_in_rank"],
+                            note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], E, my_rank)
+        yy = dis["recv_x"] if y is None else y
+        com = self.combine(yy, dis["recv_topk_weights"], dis["send_slot"], note["num_recv_tokens"])
+        return lay, note, dis, com
+
+
+def default() -> Oracle:
+    return Oracle()

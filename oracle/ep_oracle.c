@@ -1,0 +1,326 @@
+/*
+ * ep_oracle.c -- plain, slow, single-threaded CPU oracle for the expert-parallel
+ * dispatch/combine core (layout, notify, dispatch, combine) on one GPU's share.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
+ * leg of the benchmark may load this library.  The product path (the HIP library
+ * and its Python binding) never links, imports or calls it, and it shares no
+ * code, header, table or helper with the HIP sources.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared -std=c11 ep_oracle.c -lm
+ * (-ffp-contract=off keeps every a*b+c as two roundings unless fmaf() is written.)
+ *
+ * Sources (web pages; cited by page title and section):
+ *   [notes]   "DeepEP+NVSHMEM/DeepEP/internode.cu" notes, section
+ *             "1. notify_dispatch(internode.cu)": sm0 stage 6 (reductions and
+ *             inclusive prefix sums), sm1-x stages 1-3 (per-channel counting).
+ *   [qa]      "【cuda】deepep" Q&A on channels inside SymBuffer.
+ *   [mscclpp] mscclpp src/ext/ep/ht_runtime.cc mirror: getDispatchLayout,
+ *             internodeNotifyDispatch, internodeDispatch, internodeCombine,
+ *             intranodeDispatch, intranodeCombine.
+ *   [article] "CUDA与DeepEP：分布式MoE系统中的高效通信机制解析": section 2.2
+ *             (rank -> node mapping), 3.2 (expert sums, prefix sums),
+ *             4.1 (SrcInfo), 4.2 (combine routing loop).
+ *
+ * Every function below computes the plain definition with nested loops, in the
+ * order the definition states.  Where the pages leave a step open, the reading
+ * taken is written next to the code.
+ *
+ * Status bits returned by every function (0 = clean):
+ *   ORC_BAD_TOPK_IDX   1  a topk id outside [-1, E); the slot is treated as masked
+ *   ORC_RECV_OVERFLOW  2  a receive row index >= the receive capacity; row skipped
+ *   ORC_COUNT_MISMATCH 4  per-rank/per-node counts disagree with is_token_in_rank
+ *   ORC_BAD_SEND_SLOT  8  combine met a send_slot outside [-1, num_recv); skipped
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#define ORC_BAD_TOPK_IDX 1
+#define ORC_RECV_OVERFLOW 2
+#define ORC_COUNT_MISMATCH 4
+#define ORC_BAD_SEND_SLOT 8
+
+/* Ranks per node is fixed at 8 ([mscclpp] NUM_MAX_NVL_PEERS; [article] §2.2:
+ * node = rank / 8, GPU-in-node = rank % 8).  With fewer than 8 ranks there is
+ * one node ([mscclpp] constructor: num_rdma_ranks = max(1, ranks / 8)). */
+static int32_t orc_num_nodes(int32_t num_ranks) {
+    int32_t n = num_ranks / 8;
+    return n > 0 ? n : 1;
+}
+
+/* Channel c owns the contiguous token range [c*Tc, min((c+1)*Tc, T)) with
+ * Tc = ceil(T / C).  The pages give only "channel = block / 2" ([qa]); the plain
+ * reading is balanced contiguous ranges, so a channel can be empty when T < C. */
+static int64_t orc_channel_begin(int64_t T, int64_t C, int64_t c) {
+    int64_t tc = (T + C - 1) / C;
+    int64_t b = c * tc;
+    return b < T ? b : T;
+}
+static int64_t orc_channel_end(int64_t T, int64_t C, int64_t c) {
+    return orc_channel_begin(T, C, c + 1);
+}
+
+/* a topk id is valid when 0 <= e < E; -1 marks a masked slot. */
+static int orc_topk_valid(int64_t e, int32_t E, int *status) {
+    if (e == -1) return 0;
+    if (e < -1 || e >= E) {
+        *status |= ORC_BAD_TOPK_IDX;
+        return 0;
+    }
+    return 1;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stage 1: dispatch layout.  [mscclpp] getDispatchLayout takes topk_idx and
+ * yields tokens per rank, per RDMA rank (node), per expert and the
+ * is_token_in_rank map; the kernel body is not on the pages.  Reading:
+ *   is_token_in_rank[t][r] = 1 iff some valid slot j has expert_of_rank == r,
+ *     with rank_of(e) = e / (E / R)  (experts are split evenly, E % R == 0);
+ *   num_tokens_per_rank[r] = #tokens with is_token_in_rank[t][r];
+ *   num_tokens_per_rdma_rank[n] = #tokens with ANY rank of node n
+ *     ([notes] sm1-x stage 1 tests the 8 bytes of a node at once, != 0);
+ *   num_tokens_per_expert[e] = #valid slots equal to e (counted per slot). */
+int oracle_layout(int32_t T, int32_t K, int32_t E, int32_t R, const int64_t *topk_idx,
+                  int32_t *num_tokens_per_rank, int32_t *num_tokens_per_rdma_rank,
+                  int32_t *num_tokens_per_expert, uint8_t *is_token_in_rank) {
+    int status = 0;
+    const int32_t nodes = orc_num_nodes(R);
+    const int32_t experts_per_rank = E / R;
+    for (int32_t r = 0; r < R; ++r) num_tokens_per_rank[r] = 0;
+    for (int32_t n = 0; n < nodes; ++n) num_tokens_per_rdma_rank[n] = 0;
+    for (int32_t e = 0; e < E; ++e) num_tokens_per_expert[e] = 0;
+
+    for (int64_t t = 0; t < T; ++t) {
+        uint8_t *row = is_token_in_rank + t * R;
+        for (int32_t r = 0; r < R; ++r) row[r] = 0;
+        for (int32_t j = 0; j < K; ++j) {
+            int64_t e = topk_idx[t * K + j];
+            if (!orc_topk_valid(e, E, &status)) continue;
+            num_tokens_per_expert[e] += 1;
+            row[e / experts_per_rank] = 1;
+        }
+        for (int32_t r = 0; r < R; ++r)
+            if (row[r]) num_tokens_per_rank[r] += 1;
+        for (int32_t n = 0; n < nodes; ++n) {
+            int any = 0;
+            for (int32_t r = n * 8; r < R && r < (n + 1) * 8; ++r) any |= row[r];
+            if (any) num_tokens_per_rdma_rank[n] += 1;
+        }
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stage 2: notify.  [notes] sm1-x: per channel, count the tokens sent to each
+ * rank and to each node, and store per-channel prefix sums in
+ * gbl_channel_prefix_matrix [R][C] and rdma_channel_prefix_matrix [nodes][C].
+ * Reading: inclusive prefix over channels (last column = the total), matching
+ * the inclusive receive prefix sums of sm0 stage 6.
+ * [notes] sm0 stage 6 / [article] §3.2: inclusive prefix sums of received
+ * counts, the last value being the total received; per-expert received counts
+ * rounded up to expert_alignment.  With one source rank and R emulated
+ * destinations the receive prefix runs over destination ranks (nodes). */
+int oracle_notify(int32_t T, int32_t E, int32_t R, int32_t C, int32_t expert_alignment,
+                  const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
+                  const int32_t *num_tokens_per_rdma_rank, const int32_t *num_tokens_per_expert,
+                  int32_t *gbl_channel_prefix_matrix, int32_t *rdma_channel_prefix_matrix,
+                  int32_t *recv_gbl_rank_prefix_sum, int32_t *recv_rdma_rank_prefix_sum,
+                  int32_t *num_recv_tokens_per_expert, int32_t *num_recv_tokens) {
+    int status = 0;
+    const int32_t nodes = orc_num_nodes(R);
+
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t running = 0;
+        for (int32_t c = 0; c < C; ++c) {
+            for (int64_t t = orc_channel_begin(T, C, c); t < orc_channel_end(T, C, c); ++t)
+                running += is_token_in_rank[t * R + r] != 0;
+            gbl_channel_prefix_matrix[(int64_t)r * C + c] = running;
+        }
+        if (running != num_tokens_per_rank[r]) status |= ORC_COUNT_MISMATCH;
+    }
+    for (int32_t n = 0; n < nodes; ++n) {
+        int32_t running = 0;
+        for (int32_t c = 0; c < C; ++c) {
+            for (int64_t t = orc_channel_begin(T, C, c); t < orc_channel_end(T, C, c); ++t) {
+                int any = 0;
+                for (int32_t r = n * 8; r < R && r < (n + 1) * 8; ++r)
+                    any |= is_token_in_rank[t * R + r] != 0;
+                running += any;
+            }
+            rdma_channel_prefix_matrix[(int64_t)n * C + c] = running;
+        }
+        if (running != num_tokens_per_rdma_rank[n]) status |= ORC_COUNT_MISMATCH;
+    }
+
+    int32_t sum = 0;
+    for (int32_t r = 0; r < R; ++r) {
+        sum += num_tokens_per_rank[r];
+        recv_gbl_rank_prefix_sum[r] = sum;
+    }
+    *num_recv_tokens = sum;
+    sum = 0;
+    for (int32_t n = 0; n < nodes; ++n) {
+        sum += num_tokens_per_rdma_rank[n];
+        recv_rdma_rank_prefix_sum[n] = sum;
+    }
+    for (int32_t e = 0; e < E; ++e) {
+        int32_t n = num_tokens_per_expert[e];
+        num_recv_tokens_per_expert[e] = (n + expert_alignment - 1) / expert_alignment * expert_alignment;
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stages 3+4: dispatch.  The receive region is one allocation laid out
+ * [dst_rank][channel]: slab r starts at the exclusive prefix of the receive
+ * prefix sum, and inside a slab the channel segments follow in channel order,
+ * tokens ascending (a channel's segment for rank r starts at
+ * gbl_channel_prefix_matrix[r][c-1]).  So rows are handed out by walking
+ * r, then c, then t, with one running row counter.
+ * For each (t, r) routed:
+ *   recv_x[row]          = x[t]                      (bitwise copy of the bf16 row)
+ *   recv_topk_weights[row][j] = w[t][j] if slot j's expert lives on r, else 0
+ *   recv_topk_idx[row][j]     = e - r*(E/R) (the receiver's local expert id) if
+ *                               slot j's expert lives on r, else -1
+ *   recv_src_info[row]   = {my_rank, t}   ([article] §4.1 SrcInfo)
+ *   send_slot[t][r]      = row, -1 where token t is not sent to r
+ *                          ([mscclpp] the per-(token, rank) gather map the dispatch
+ *                          sender fills and combine reads).
+ * Rows at or beyond recv_capacity are not written, their send_slot stays -1
+ * and ORC_RECV_OVERFLOW is raised.  recv_topk_idx may be NULL. */
+int oracle_dispatch(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t C,
+                    int32_t my_rank, int32_t recv_capacity, const uint16_t *x,
+                    const int64_t *topk_idx, const float *topk_weights,
+                    const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
+                    const int32_t *recv_gbl_rank_prefix_sum, uint16_t *recv_x,
+                    float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
+                    int32_t *send_slot) {
+    int status = 0;
+    const int32_t experts_per_rank = E / R;
+    for (int64_t i = 0; i < (int64_t)T * R; ++i) send_slot[i] = -1;
+
+    for (int32_t r = 0; r < R; ++r) {
+        const int64_t slab_begin = r > 0 ? recv_gbl_rank_prefix_sum[r - 1] : 0;
+        int64_t row = slab_begin;
+        for (int32_t c = 0; c < C; ++c) {
+            const int64_t seg_begin = slab_begin + (c > 0 ? gbl_channel_prefix_matrix[(int64_t)r * C + c - 1] : 0);
+            if (row != seg_begin) status |= ORC_COUNT_MISMATCH;
+            for (int64_t t = orc_channel_begin(T, C, c); t < orc_channel_end(T, C, c); ++t) {
+                if (!is_token_in_rank[t * R + r]) continue;
+                if (row >= recv_capacity) {
+                    status |= ORC_RECV_OVERFLOW;
+                    ++row;
+                    continue;
+                }
+                send_slot[t * R + r] = (int32_t)row;
+                memcpy(recv_x + row * H, x + t * H, (size_t)H * sizeof(uint16_t));
+                for (int32_t j = 0; j < K; ++j) {
+                    int64_t e = topk_idx[t * K + j];
+                    int on_r = orc_topk_valid(e, E, &status) && e / experts_per_rank == r;
+                    recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K + j] : 0.0f;
+                    if (recv_topk_idx) recv_topk_idx[row * K + j] = on_r ? e - (int64_t)r * experts_per_rank : -1;
+                }
+                recv_src_info[row * 2 + 0] = my_rank;
+                recv_src_info[row * 2 + 1] = (int32_t)t;
+                ++row;
+            }
+        }
+        if (row != (int64_t)recv_gbl_rank_prefix_sum[r]) status |= ORC_COUNT_MISMATCH;
+    }
+    return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* bf16 helpers (IEEE binary32 truncated to its upper 16 bits). */
+static float orc_bf16_to_f32(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* Round a binary32 value to the nearest bf16, ties to the even bf16 pattern:
+ * compare the 16 dropped bits with the half-way point 0x8000.  NaN stays NaN
+ * (quiet bit forced).  Infinities and the largest finite values overflow to
+ * infinity as round-to-nearest prescribes. */
+static uint16_t orc_f32_to_bf16_rne(float f) {
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
+    uint32_t kept = u >> 16;
+    uint32_t dropped = u & 0xffffu;
+    if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;
+    return (uint16_t)kept;
+}
+
+/* Exposed for the rounding pin (compared against a library conversion). */
+void oracle_bf16_round(const float *in, uint16_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_f32_to_bf16_rne(in[i]);
+}
+
+/* ------------------------------------------------------------------------- */
+/* Stage 5: combine.  [mscclpp] internodeCombine / intranodeCombine return
+ * combined_x (bf16) and combined_topk_weights from the received rows and their
+ * topk weights; [article] §4.2: each received row goes back to output[src_idx]
+ * of its source.  The reduction order is not on the pages.  Reading:
+ *   for each token t, over destination ranks r ascending with s = send_slot[t][r] >= 0:
+ *     W = sum_j recv_topk_weights[s][j]   (fp32 adds, j ascending, from +0)
+ *     acc[i] = fmaf(W, y[s][i], acc[i])   (fp32, acc starting at +0)
+ *   combined_x[t][i] = bf16_rne(acc[i]);
+ *   combined_topk_weights[t][j] = sum over the same r of recv_topk_weights[s][j]
+ *                                 (fp32 adds, r ascending, from +0).
+ * A token sent nowhere gets +0 rows and weights.  send_slot entries outside
+ * [-1, num_recv) raise ORC_BAD_SEND_SLOT and are skipped.
+ * combined_topk_weights may be NULL. */
+int oracle_combine(int32_t T, int32_t H, int32_t K, int32_t R, int32_t num_recv, const uint16_t *y,
+                   const float *recv_topk_weights, const int32_t *send_slot, uint16_t *combined_x,
+                   float *combined_topk_weights, float *acc_scratch /* [H] */) {
+    int status = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t i = 0; i < H; ++i) acc_scratch[i] = 0.0f;
+        if (combined_topk_weights)
+            for (int32_t j = 0; j < K; ++j) combined_topk_weights[t * K + j] = 0.0f;
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t s = send_slot[t * R + r];
+            if (s == -1) continue;
+            if (s < -1 || s >= num_recv) {
+                status |= ORC_BAD_SEND_SLOT;
+                continue;
+            }
+            float W = 0.0f;
+            for (int32_t j = 0; j < K; ++j) W = W + recv_topk_weights[(int64_t)s * K + j];
+            const uint16_t *yrow = y + (int64_t)s * H;
+            for (int32_t i = 0; i < H; ++i) acc_scratch[i] = fmaf(W, orc_bf16_to_f32(yrow[i]), acc_scratch[i]);
+            if (combined_topk_weights)
+                for (int32_t j = 0; j < K; ++j)
+                    combined_topk_weights[t * K + j] = combined_topk_weights[t * K + j] + recv_topk_weights[(int64_t)s * K + j];
+        }
+        for (int32_t i = 0; i < H; ++i) combined_x[t * H + i] = orc_f32_to_bf16_rne(acc_scratch[i]);
+    }
+    return status;
+}
+
+/* The same weighted sum evaluated in binary64 without the final rounding:
+ * out[t][i] = sum_r (sum_j w[s_r][j]) * y[s_r][i].  Used only to bound the
+ * rounding error of the fp32 combine (a pin, not a parity target). */
+int oracle_combine_f64(int32_t T, int32_t H, int32_t K, int32_t R, int32_t num_recv, const uint16_t *y,
+                       const float *recv_topk_weights, const int32_t *send_slot, double *out) {
+    int status = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        double *o = out + t * H;
+        for (int32_t i = 0; i < H; ++i) o[i] = 0.0;
+        for (int32_t r = 0; r < R; ++r) {
+            int32_t s = send_slot[t * R + r];
+            if (s == -1) continue;
+            if (s < -1 || s >= num_recv) {
+                status |= ORC_BAD_SEND_SLOT;
+                continue;
+            }
+            double W = 0.0;
+            for (int32_t j = 0; j < K; ++j) W += (double)recv_topk_weights[(int64_t)s * K + j];
+            for (int32_t i = 0; i < H; ++i) o[i] += W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);
+        }
+    }
+    return status;
+}

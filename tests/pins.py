@@ -1,0 +1,389 @@
+"""Checks that pin the CPU oracle to things other than itself.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` (the real one, or a variant
+built from a planted mistake) and returns a list of failure strings; an empty
+list means the pin holds.  The pins are:
+
+* the hand-worked example under ``tests/golden/`` (derived from the definitions
+  on the pages, which print no numeric example themselves);
+* invariants the definitions imply (counts, totals, monotone prefixes, a row
+  bijection, slab and channel segment boundaries, metadata masking);
+* closed forms: identity experts return x bit-exactly, power-of-two scaled
+  experts return the exact weighted sum within half a bf16 ulp, aligned
+  counts equal ceil(n/a)*a;
+* brute force over every routing of 1 or 2 tokens on tiny shapes, compared
+  with a second formulation written independently here (sets, sorting,
+  channel index by integer division);
+* the bf16 rounding against torch's own round-to-nearest-even conversion.
+"""
+from __future__ import annotations
+
+import itertools
+import json
+import math
+import os
+from collections import Counter
+
+import numpy as np
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "worked_example.json")
+
+
+def _bf16_from_float(a) -> np.ndarray:
+    """Exact floats (small integers, dyadic fractions) to bf16 bit patterns."""
+    f = np.asarray(a, dtype=np.float32)
+    bits = f.view(np.uint32)
+    assert np.all((bits & 0xFFFF) == 0), "value not exact in bf16"
+    return (bits >> 16).astype(np.uint16)
+
+
+def bf16_to_f64(u: np.ndarray) -> np.ndarray:
+    return (np.asarray(u, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _eq(name, got, want, errs):
+    got = np.asarray(got)
+    want = np.asarray(want)
+    if got.shape != want.shape or not np.array_equal(got, want):
+        errs.append(f"{name}: got {got.tolist()} want {want.tolist()}")
+
+
+# --------------------------------------------------------------------------- golden
+def pin_golden(o) -> list[str]:
+    g = json.load(open(GOLDEN))
+    s, inp, exp = g["shape"], g["inputs"], g["expected"]
+    T, H, K, E, R, C = (s[k] for k in ("tokens", "hidden", "topk", "experts", "ranks", "channels"))
+    idx = np.array(inp["topk_idx"], np.int64)
+    w = np.array(inp["topk_weights"], np.float32)
+    x = _bf16_from_float([[(t + 1) * (i + 1) for i in range(H)] for t in range(T)])
+    errs: list[str] = []
+    lay = o.layout(idx, E, R)
+    for key in ("is_token_in_rank", "num_tokens_per_rank", "num_tokens_per_rdma_rank", "num_tokens_per_expert"):
+        _eq(key, lay[key], exp[key], errs)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, s["expert_alignment"])
+    for key in ("gbl_channel_prefix_matrix", "rdma_channel_prefix_matrix", "recv_gbl_rank_prefix_sum",
+                "recv_rdma_rank_prefix_sum", "num_recv_tokens_per_expert", "num_recv_tokens"):
+        _eq(key, note[key], exp[key], errs)
+    dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                     note["recv_gbl_rank_prefix_sum"], E, s["my_rank"])
+    for key in ("send_slot", "recv_src_info", "recv_topk_idx", "recv_topk_weights"):
+        _eq(key, dis[key], exp[key], errs)
+    _eq("recv_x", dis["recv_x"], x[np.array(exp["recv_x_source_token"])], errs)
+    n = note["num_recv_tokens"]
+    com = o.combine(dis["recv_x"], dis["recv_topk_weights"], dis["send_slot"], n)
+    want_id = x.copy()
+    want_id[4] = 0
+    _eq("combined_x(identity)", com["combined_x"], want_id, errs)
+    _eq("combined_topk_weights", com["combined_topk_weights"], exp["combined_topk_weights"], errs)
+    y = _bf16_from_float([[s_ + 1] * H for s_ in range(n)])
+    com = o.combine(y, dis["recv_topk_weights"], dis["send_slot"], n)
+    want = _bf16_from_float([[v] * H for v in exp["combined_x_with_y"]])
+    _eq("combined_x(y)", com["combined_x"], want, errs)
+    for st, name in ((lay, "layout"), (note, "notify"), (dis, "dispatch"), (com, "combine")):
+        if st["status"] != 0:
+            errs.append(f"{name} status {st['status']}")
+    return errs
+
+
+# --------------------------------------------------------------------------- invariants
+def layout_invariants(idx: np.ndarray, E: int, R: int, lay: dict) -> list[str]:
+    errs = []
+    T, K = idx.shape
+    er = E // R
+    nodes = max(1, R // 8)
+    in_rank = lay["is_token_in_rank"].astype(np.int64)
+    per_rank = lay["num_tokens_per_rank"].astype(np.int64)
+    per_node = lay["num_tokens_per_rdma_rank"].astype(np.int64)
+    per_exp = lay["num_tokens_per_expert"].astype(np.int64)
+    valid = int(((idx >= 0) & (idx < E)).sum())
+    if per_exp.sum() != valid:
+        errs.append(f"sum(per_expert)={per_exp.sum()} != valid slots {valid}")
+    if not np.array_equal(in_rank.sum(0), per_rank):
+        errs.append("column sums of is_token_in_rank != num_tokens_per_rank")
+    if not set(np.unique(in_rank)).issubset({0, 1}):
+        errs.append("is_token_in_rank not boolean")
+    by_rank = per_exp.reshape(R, er)
+    if np.any(by_rank.max(1) > per_rank) or np.any(per_rank > by_rank.sum(1)):
+        errs.append("max_e count <= per_rank <= sum_e count violated")
+    for n in range(nodes):
+        sl = per_rank[n * 8:(n + 1) * 8]
+        if not (sl.max(initial=0) <= per_node[n] <= sl.sum()):
+            errs.append(f"node {n}: per-node count {per_node[n]} outside [max, sum] of its ranks")
+    # tokens whose every slot is masked reach no rank and no node
+    dead = ~((idx >= 0) & (idx < E)).any(1)
+    if in_rank[dead].any():
+        errs.append("fully masked token routed")
+    if np.any(per_node > T - dead.sum()):
+        errs.append("a node receives more tokens than there are live tokens")
+    return errs
+
+
+def notify_invariants(lay: dict, note: dict, C: int, align: int) -> list[str]:
+    errs = []
+    gbl = note["gbl_channel_prefix_matrix"].astype(np.int64)
+    rdma = note["rdma_channel_prefix_matrix"].astype(np.int64)
+    per_rank = lay["num_tokens_per_rank"]
+    per_node = lay["num_tokens_per_rdma_rank"]
+    in_rank = lay["is_token_in_rank"]
+    T = in_rank.shape[0]
+    tc = -(-T // C) if C else 0
+    if np.any(np.diff(gbl, axis=1) < 0) or np.any(np.diff(rdma, axis=1) < 0):
+        errs.append("channel prefix not monotone")
+    if not np.array_equal(gbl[:, -1], per_rank):
+        errs.append("gbl last column != per-rank totals")
+    if not np.array_equal(rdma[:, -1], per_node):
+        errs.append("rdma last column != per-node totals")
+    if not np.array_equal(gbl[:, 0], in_rank[:min(tc, T)].astype(np.int64).sum(0)):
+        errs.append("gbl first column != channel-0 counts")
+    recv = note["recv_gbl_rank_prefix_sum"].astype(np.int64)
+    if not np.array_equal(np.diff(np.concatenate([[0], recv])), per_rank):
+        errs.append("recv_gbl increments != per-rank counts")
+    if note["num_recv_tokens"] != int(per_rank.sum()):
+        errs.append("num_recv_tokens != sum per_rank")
+    rr = note["recv_rdma_rank_prefix_sum"].astype(np.int64)
+    if not np.array_equal(np.diff(np.concatenate([[0], rr])), per_node):
+        errs.append("recv_rdma increments != per-node counts")
+    n = lay["num_tokens_per_expert"].astype(np.int64)
+    a = note["num_recv_tokens_per_expert"].astype(np.int64)
+    if np.any(a % align) or np.any(a < n) or np.any(a >= n + align):
+        errs.append("aligned per-expert counts not ceil(n/a)*a")
+    return errs
+
+
+def dispatch_invariants(x, idx, w, E, R, C, my_rank, lay, note, dis) -> list[str]:
+    errs = []
+    T, K = idx.shape
+    er = E // R
+    n = note["num_recv_tokens"]
+    slot = dis["send_slot"].astype(np.int64)
+    in_rank = lay["is_token_in_rank"].astype(bool)
+    if not np.array_equal(slot >= 0, in_rank):
+        errs.append("send_slot >= 0 pattern != is_token_in_rank")
+    used = np.sort(slot[slot >= 0])
+    if not np.array_equal(used, np.arange(n)):
+        errs.append("send_slot is not a bijection onto [0, N)")
+        return errs
+    tt, rr = np.nonzero(slot >= 0)
+    ss = slot[tt, rr]
+    src = dis["recv_src_info"]
+    if not (np.all(src[ss, 0] == my_rank) and np.array_equal(src[ss, 1], tt)):
+        errs.append("src_info does not point back to (my_rank, t)")
+    recv = note["recv_gbl_rank_prefix_sum"].astype(np.int64)
+    base = np.concatenate([[0], recv[:-1]])
+    if np.any(ss < base[rr]) or np.any(ss >= recv[rr]):
+        errs.append("row outside its rank's slab")
+    # inside a slab, source tokens strictly increase
+    order = np.argsort(ss)
+    s_rank, s_tok = rr[order], tt[order]
+    same = s_rank[1:] == s_rank[:-1]
+    if np.any(s_tok[1:][same] <= s_tok[:-1][same]):
+        errs.append("source tokens not increasing inside a slab")
+    # channel segment boundaries inside each slab
+    gbl = note["gbl_channel_prefix_matrix"].astype(np.int64)
+    tc = -(-T // C)
+    ch = tt // tc if tc else tt
+    lo = base[rr] + np.where(ch > 0, gbl[rr, np.maximum(ch - 1, 0)], 0)
+    hi = base[rr] + gbl[rr, ch]
+    if np.any(ss < lo) or np.any(ss >= hi):
+        errs.append("row outside its [rank][channel] segment")
+    if x is not None and not np.array_equal(dis["recv_x"][ss], x[tt]):
+        errs.append("recv_x row != x[src]")
+    # metadata: weights / local ids only for experts living on the receiving rank
+    rw = dis["recv_topk_weights"][ss]
+    ri = dis["recv_topk_idx"][ss] if dis["recv_topk_idx"] is not None else None
+    e = idx[tt]
+    on = (e >= 0) & (e < E) & (e // max(er, 1) == rr[:, None])
+    if not np.array_equal(rw, np.where(on, w[tt], np.float32(0))):
+        errs.append("recv_topk_weights masking wrong")
+    if ri is not None:
+        if not np.array_equal(ri, np.where(on, e - rr[:, None] * er, -1)):
+            errs.append("recv_topk_idx local ids wrong")
+        if np.any(ri < -1) or np.any(ri >= er):
+            errs.append("recv_topk_idx outside [-1, E/R)")
+            return errs
+        cnt = np.zeros(E, np.int64)
+        valid = ri >= 0
+        np.add.at(cnt, (rr[:, None] * er + ri)[valid], 1)
+        if not np.array_equal(cnt, lay["num_tokens_per_expert"]):
+            errs.append("per-local-expert receive counts != num_tokens_per_expert")
+    return errs
+
+
+def _ulp_bf16(v: np.ndarray) -> np.ndarray:
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
+
+
+def combine_closed_forms(o, x, idx, w, E, R, lay, note, dis) -> list[str]:
+    errs = []
+    T, K = idx.shape
+    er = E // R
+    n = note["num_recv_tokens"]
+    # 1) identity experts: combined == x where the token went anywhere, +0 elsewhere
+    com = o.combine(dis["recv_x"], dis["recv_topk_weights"], dis["send_slot"], n)
+    live = lay["is_token_in_rank"].any(1)
+    want = np.where(live[:, None], x, np.uint16(0))
+    # weights of a live token sum to 1 only when every valid slot carries weight;
+    # the generator's softmax guarantees it.
+    if not np.array_equal(com["combined_x"], want):
+        bad = int((com["combined_x"] != want).sum())
+        errs.append(f"identity combine != x on {bad} elements")
+    valid = (idx >= 0) & (idx < E)
+    if not np.array_equal(com["combined_topk_weights"], np.where(valid, w, np.float32(0))):
+        errs.append("combined_topk_weights != masked topk_weights")
+    # 2) power-of-two scaled experts: y[s] = 2^((r mod 4) - 1) * x[src]
+    slot = dis["send_slot"]
+    tt, rr = np.nonzero(slot >= 0)
+    ss = slot[tt, rr]
+    scale = 2.0 ** ((rr % 4) - 1)
+    y = np.zeros_like(dis["recv_x"])
+    yf = bf16_to_f64(x[tt]) * scale[:, None]
+    y[ss] = (yf.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # exact: power-of-two scaling
+    W = np.zeros((T, R))
+    for j in range(K):
+        ok = valid[:, j]
+        np.add.at(W, (np.nonzero(ok)[0], idx[ok, j] // er), w[ok, j].astype(np.float64))
+    coef = (W * (2.0 ** ((np.arange(R) % 4) - 1))[None, :]).sum(1)
+    exact = coef[:, None] * bf16_to_f64(x)
+    got = bf16_to_f64(o.combine(y, dis["recv_topk_weights"], slot, n)["combined_x"])
+    tol = 0.5 * _ulp_bf16(exact) * 1.001
+    if np.any(np.abs(got - exact) > tol):
+        errs.append(f"scaled combine off by {np.max(np.abs(got - exact) - tol):.3g} beyond half-ulp")
+    return errs
+
+
+# --------------------------------------------------------------------------- brute force
+def _second_formulation(idx, E, R, C, my_rank):
+    """Independent restatement: destination sets, a sorted (rank, token) list."""
+    T, K = idx.shape
+    er = E // R
+    dest = [sorted({int(e) // er for e in row if 0 <= e < E}) for row in idx]
+    nodes = max(1, R // 8)
+    tc = -(-T // C) if T else 1
+    chan = [t // tc for t in range(T)]
+    per_rank = [sum(r in d for d in dest) for r in range(R)]
+    per_node = [sum(any(r // 8 == nd for r in d) for d in dest) for nd in range(nodes)]
+    cnt = Counter(int(e) for row in idx for e in row if 0 <= e < E)
+    per_exp = [cnt[e] for e in range(E)]
+    gbl = [[sum(1 for t in range(T) if r in dest[t] and chan[t] <= c) for c in range(C)] for r in range(R)]
+    rdma = [[sum(1 for t in range(T) if any(r // 8 == nd for r in dest[t]) and chan[t] <= c)
+             for c in range(C)] for nd in range(nodes)]
+    pairs = sorted((r, t) for t in range(T) for r in dest[t])
+    slot = [[-1] * R for _ in range(T)]
+    for i, (r, t) in enumerate(pairs):
+        slot[t][r] = i
+    return dict(per_rank=per_rank, per_node=per_node, per_exp=per_exp, gbl=gbl, rdma=rdma, slot=slot,
+                n=len(pairs), dest=dest)
+
+
+def pin_bruteforce(o, max_cases: int | None = None) -> list[str]:
+    errs: list[str] = []
+    rng = np.random.default_rng(7)
+    E, K = 4, 2
+    slot_vals = [-1, 0, 1, 2, 3]
+    rows = [r for r in itertools.product(slot_vals, repeat=K)]
+    cases = 0
+    for R in (1, 2, 4):
+        for T in (1, 2):
+            for routing in itertools.product(rows, repeat=T):
+                idx = np.array(routing, np.int64).reshape(T, K)
+                for C in (1, 2, 3, 5):
+                    cases += 1
+                    if max_cases and cases > max_cases:
+                        return errs
+                    ref = _second_formulation(idx, E, R, C, 1)
+                    lay = o.layout(idx, E, R)
+                    if lay["num_tokens_per_rank"].tolist() != ref["per_rank"] or \
+                       lay["num_tokens_per_rdma_rank"].tolist() != ref["per_node"] or \
+                       lay["num_tokens_per_expert"].tolist() != ref["per_exp"]:
+                        errs.append(f"layout mismatch idx={idx.tolist()} R={R}")
+                        continue
+                    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"],
+                                    lay["num_tokens_per_rdma_rank"], lay["num_tokens_per_expert"], C, 1)
+                    if note["gbl_channel_prefix_matrix"].tolist() != ref["gbl"] or \
+                       note["rdma_channel_prefix_matrix"].tolist() != ref["rdma"]:
+                        errs.append(f"notify mismatch idx={idx.tolist()} R={R} C={C}")
+                        continue
+                    H = 8
+                    x = _bf16_from_float(rng.integers(-8, 9, size=(T, H)).astype(np.float32))
+                    w = (rng.integers(1, 8, size=(T, K)) / 8.0).astype(np.float32)
+                    dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                                     note["recv_gbl_rank_prefix_sum"], E, 1)
+                    if dis["send_slot"].tolist() != ref["slot"]:
+                        errs.append(f"dispatch slots mismatch idx={idx.tolist()} R={R} C={C}")
+                        continue
+                    n = ref["n"]
+                    y = _bf16_from_float(rng.integers(-8, 9, size=(max(n, 1), H)).astype(np.float32))[:n]
+                    com = o.combine(y, dis["recv_topk_weights"], dis["send_slot"], n)
+                    er = E // R
+                    want = np.zeros((T, H))
+                    for t in range(T):
+                        for r in ref["dest"][t]:
+                            wsum = sum(float(w[t, j]) for j in range(K) if 0 <= idx[t, j] < E and idx[t, j] // er == r)
+                            want[t] += wsum * bf16_to_f64(y[ref["slot"][t][r]])
+                    got = bf16_to_f64(com["combined_x"])
+                    if np.any(np.abs(got - want) > 0.5 * _ulp_bf16(want) * 1.001):
+                        errs.append(f"combine mismatch idx={idx.tolist()} R={R} C={C}")
+    return errs
+
+
+# --------------------------------------------------------------------------- bf16 rounding
+def pin_bf16_rounding(o) -> list[str]:
+    import torch
+
+    rng = np.random.default_rng(3)
+    vals = [rng.standard_normal(20000).astype(np.float32),
+            (rng.standard_normal(20000) * 1e30).astype(np.float32),
+            (rng.standard_normal(2000) * 1e-40).astype(np.float32)]
+    # exact ties: kept bits odd/even with dropped half exactly 0x8000
+    base = rng.integers(0, 1 << 15, size=4000, dtype=np.uint32) << 16
+    base = base[(base & 0x7F800000) != 0x7F800000]  # NaN payloads are implementation-defined
+    ties = (base | 0x8000).view(np.float32)
+    specials = np.array([0.0, -0.0, np.inf, -np.inf, 3.3895314e38, -3.3895314e38, 1.0, -1.0], np.float32)
+    f = np.concatenate(vals + [ties, specials])
+    got = o.bf16_round(f)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    errs = []
+    if not np.array_equal(got, want):
+        errs.append(f"bf16 rounding differs from torch on {int((got != want).sum())} values")
+    nan = o.bf16_round(np.array([np.nan], np.float32))
+    if not ((nan[0] & 0x7F80) == 0x7F80 and (nan[0] & 0x7F) != 0):
+        errs.append("NaN not kept as NaN")
+    return errs
+
+
+# --------------------------------------------------------------------------- whole-workload pin
+def pin_workload(o, inputs: dict, hidden: int | None = None) -> list[str]:
+    """All invariants and closed forms on one generated workload.  ``hidden``
+    narrows x (slot logic does not depend on it) to keep CPU runs short."""
+    wl = inputs["workload"]
+    x = inputs["x"]
+    if hidden is not None and x is not None:
+        x = np.ascontiguousarray(x[:, :hidden])
+    idx, w = inputs["topk_idx"], inputs["topk_weights"]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    errs = []
+    lay = o.layout(idx, E, R)
+    errs += layout_invariants(idx, E, R, lay)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, wl.expert_alignment)
+    errs += notify_invariants(lay, note, C, wl.expert_alignment)
+    if x is None:
+        return errs
+    dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                     note["recv_gbl_rank_prefix_sum"], E, 0)
+    errs += dispatch_invariants(x, idx, w, E, R, C, 0, lay, note, dis)
+    if not errs:
+        errs += combine_closed_forms(o, x, idx, w, E, R, lay, note, dis)
+    for st, name in ((lay, "layout"), (note, "notify"), (dis, "dispatch")):
+        if st["status"] != 0:
+            errs.append(f"{name} status {st['status']}")
+    return errs
+
+
+def expected_ranks_per_token(E: int, R: int, K: int) -> float:
+    """Closed form for uniform routing without replacement: R*(1 - C(E-E/R, K)/C(E, K))."""
+    er = E // R
+    return R * (1.0 - math.comb(E - er, K) / math.comb(E, K))

@@ -1,0 +1,91 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a one-spot textual edit of ``oracle/ep_oracle.c`` (a dropped
+term, a wrong index or sign, a transposed operand, an off-by-one), compiled
+with gcc into a temporary library and run through the pins in a child
+process, so a mutant that crashes cannot take the test run down with it
+(a crash on a signal counts as caught).  Runs on the CPU only.
+"""
+import os
+import subprocess
+import sys
+import textwrap
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "ep_oracle.c")
+
+MUTANTS = {
+    "rank_of_expert_modulo": ("row[e / experts_per_rank] = 1;", "row[e % R] = 1;"),
+    "expert_count_dropped": ("num_tokens_per_expert[e] += 1;", ";"),
+    "node_skips_first_rank": ("for (int32_t r = n * 8; r < R && r < (n + 1) * 8; ++r) any |= row[r];",
+                              "for (int32_t r = n * 8 + 1; r < R && r < (n + 1) * 8; ++r) any |= row[r];"),
+    "node_size_four": ("for (int32_t r = n * 8; r < R && r < (n + 1) * 8; ++r) any |= row[r];",
+                       "for (int32_t r = n * 4; r < R && r < (n + 1) * 4; ++r) any |= row[r];"),
+    "channel_len_floor": ("int64_t tc = (T + C - 1) / C;", "int64_t tc = T / C;"),
+    "gbl_transposed": ("gbl_channel_prefix_matrix[(int64_t)r * C + c] = running;",
+                       "gbl_channel_prefix_matrix[(int64_t)c * R + r] = running;"),
+    "rdma_counts_ranks_not_tokens": ("any |= is_token_in_rank[t * R + r] != 0;",
+                                     "any += is_token_in_rank[t * R + r] != 0;"),
+    "recv_prefix_exclusive": ("sum += num_tokens_per_rank[r];\n        recv_gbl_rank_prefix_sum[r] = sum;",
+                              "recv_gbl_rank_prefix_sum[r] = sum;\n        sum += num_tokens_per_rank[r];"),
+    "alignment_floor": ("(n + expert_alignment - 1) / expert_alignment * expert_alignment",
+                        "n / expert_alignment * expert_alignment"),
+    "slab_base_off_by_one": ("r > 0 ? recv_gbl_rank_prefix_sum[r - 1] : 0;",
+                             "r > 1 ? recv_gbl_rank_prefix_sum[r - 2] : 0;"),
+    "local_id_unscaled": ("on_r ? e - (int64_t)r * experts_per_rank : -1", "on_r ? e - (int64_t)r : -1"),
+    "weights_unmasked": ("recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K + j] : 0.0f;",
+                         "recv_topk_weights[row * K + j] = topk_weights[t * K + j];"),
+    "src_idx_is_row": ("recv_src_info[row * 2 + 1] = (int32_t)t;", "recv_src_info[row * 2 + 1] = (int32_t)row;"),
+    "src_rank_dropped": ("recv_src_info[row * 2 + 0] = my_rank;", "recv_src_info[row * 2 + 0] = 0;"),
+    "tokens_descending_in_channel": (
+        "for (int64_t t = orc_channel_begin(T, C, c); t < orc_channel_end(T, C, c); ++t) {\n"
+        "                if (!is_token_in_rank[t * R + r]) continue;",
+        "for (int64_t t = orc_channel_end(T, C, c) - 1; t >= orc_channel_begin(T, C, c); --t) {\n"
+        "                if (!is_token_in_rank[t * R + r]) continue;"),
+    "W_keeps_last_term": ("W = W + recv_topk_weights[(int64_t)s * K + j];", "W = recv_topk_weights[(int64_t)s * K + j];"),
+    "combine_reads_rank_row": ("const uint16_t *yrow = y + (int64_t)s * H;",
+                               "const uint16_t *yrow = y + (int64_t)(s > 0 ? s - 1 : s) * H;"),
+    "combine_fma_operands_swapped": ("fmaf(W, orc_bf16_to_f32(yrow[i]), acc_scratch[i])",
+                                     "fmaf(acc_scratch[i], orc_bf16_to_f32(yrow[i]), W)"),
+    "combined_weights_last_only": (
+        "combined_topk_weights[t * K + j] = combined_topk_weights[t * K + j] + recv_topk_weights[(int64_t)s * K + j];",
+        "combined_topk_weights[t * K + j] = recv_topk_weights[(int64_t)s * K + j];"),
+    "rounding_ties_away": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;",
+                           "if (dropped >= 0x8000u) kept += 1u;"),
+    "rounding_truncates": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", ";"),
+    "bf16_widen_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+}
+
+CHILD = textwrap.dedent("""
+    import sys
+    sys.path.insert(0, {root!r}); sys.path.insert(0, {tests!r})
+    import oracle, pins
+    from combine_ep_get_02_amd import inputs
+    o = oracle.Oracle(oracle.load({lib!r}))
+    errs = pins.pin_golden(o) + pins.pin_bf16_rounding(o) + pins.pin_workload(o, inputs.generate("tiny"))
+    errs += pins.pin_workload(o, inputs.generate("sweep"), hidden=64)
+    if not errs:
+        errs += pins.pin_bruteforce(o)
+    print("CAUGHT" if errs else "MISSED", errs[:2])
+""")
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    import oracle
+
+    before, after = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(before) == 1, f"mutation site for {name} not unique/present"
+    mut_c = tmp_path / "mutant.c"
+    mut_c.write_text(src.replace(before, after))
+    lib = str(tmp_path / "libmutant.so")
+    oracle.build(str(mut_c), lib)
+    code = CHILD.format(root=ROOT, tests=os.path.join(ROOT, "tests"), lib=lib)
+    p = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    # caught: a pin failed, or the mutant crashed the child on a signal; a Python
+    # exception inside the pins would be a broken pin, not a catch.
+    caught = "CAUGHT" in p.stdout or p.returncode < 0
+    assert caught, f"mutant {name} passed every pin: {p.stdout[-500:]} {p.stderr[-500:]}"

@@ -1,0 +1,125 @@
+"""The CPU oracle against its pins: the hand-worked example, invariants,
+closed forms, brute force and the bf16 rounding (no GPU needed)."""
+import numpy as np
+import pytest
+
+import pins
+from combine_ep_get_02_amd.inputs import WORKLOADS
+
+pytestmark = pytest.mark.filterwarnings("ignore")
+
+
+def test_golden_worked_example(orc):
+    assert pins.pin_golden(orc) == []
+
+
+def test_bruteforce_tiny_shapes(orc):
+    assert pins.pin_bruteforce(orc) == []
+
+
+def test_bf16_rounding_matches_library(orc):
+    assert pins.pin_bf16_rounding(orc) == []
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep"])
+def test_small_workloads_full_hidden(orc, workload_inputs, name):
+    assert pins.pin_workload(orc, workload_inputs(name)) == []
+
+
+@pytest.mark.parametrize("name", ["prefill", "skew", "large"])
+def test_big_workloads_routing_and_narrow_rows(orc, workload_inputs, name):
+    # full routing (t, R, E, k, C) with x narrowed to 64 columns: the slot
+    # logic does not depend on the row width, and the CPU suite stays short.
+    assert pins.pin_workload(orc, workload_inputs(name), hidden=64) == []
+
+
+@pytest.mark.parametrize("name", ["sweep", "prefill", "large"])
+def test_generator_mean_ranks_per_token(workload_inputs, name):
+    d = workload_inputs(name, with_x=False)
+    wl = d["workload"]
+    er = wl.experts // wl.ranks
+    ranks = np.array([len({int(e) // er for e in row}) for row in d["topk_idx"]])
+    want = pins.expected_ranks_per_token(wl.experts, wl.ranks, wl.topk)
+    # standard error of the mean is below 0.03 at these sizes
+    assert abs(ranks.mean() - want) < 0.15, (ranks.mean(), want)
+
+
+def test_skew_generator_masks_and_zipf(workload_inputs):
+    d = workload_inputs("skew", with_x=False)
+    idx = d["topk_idx"]
+    assert (idx == -1).sum() == int(0.1 * idx.size)
+    w = d["topk_weights"]
+    live = (idx >= 0).any(1)
+    np.testing.assert_allclose(w[live].sum(1), 1.0, rtol=1e-5)
+    assert np.all(w[idx < 0] == 0)
+    counts = np.bincount(idx[idx >= 0], minlength=256)
+    # Zipf(1.2): the most popular expert is chosen far more often than the median one
+    assert counts.max() > 5 * np.median(counts)
+    # no duplicate ids within a token
+    for row in idx:
+        v = row[row >= 0]
+        assert len(set(v.tolist())) == len(v)
+
+
+@pytest.mark.parametrize("align", [1, 4, 128])
+def test_expert_alignment_closed_form(orc, workload_inputs, align):
+    d = workload_inputs("tiny")
+    lay = orc.layout(d["topk_idx"], 16, 8)
+    note = orc.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                      lay["num_tokens_per_expert"], 4, align)
+    n = lay["num_tokens_per_expert"]
+    assert np.array_equal(note["num_recv_tokens_per_expert"], -(-n // align) * align)
+
+
+def test_edge_empty_and_ragged(orc):
+    rng = np.random.default_rng(1)
+    # t = 0
+    idx = np.zeros((0, 2), np.int64)
+    lay = orc.layout(idx, 16, 8)
+    assert lay["num_tokens_per_rank"].sum() == 0
+    note = orc.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                      lay["num_tokens_per_expert"], 4, 1)
+    assert note["num_recv_tokens"] == 0 and not note["gbl_channel_prefix_matrix"].any()
+    # t < C: empty channels, R = 1, R = 4
+    for T, R, C in ((3, 8, 7), (5, 1, 3), (9, 4, 2), (70, 16, 5)):
+        E = 2 * R
+        idx = np.stack([rng.choice(E, 2, replace=False) for _ in range(T)]).astype(np.int64)
+        x = rng.integers(0, 1 << 15, size=(T, 8), dtype=np.uint16)
+        w = rng.random((T, 2)).astype(np.float32)
+        lay, note, dis, com = orc.full(x, idx, w, E, R, C)
+        assert pins.layout_invariants(idx, E, R, lay) == []
+        assert pins.notify_invariants(lay, note, C, 1) == []
+        assert pins.dispatch_invariants(x, idx, w, E, R, C, 0, lay, note, dis) == []
+
+
+def test_edge_masked_duplicates_bad_ids(orc):
+    # all-masked token, duplicate expert id, out-of-range id (flagged, treated as masked)
+    idx = np.array([[-1, -1], [3, 3], [5, 16], [0, -7]], np.int64)
+    lay = orc.layout(idx, 16, 8)
+    assert lay["status"] == 1
+    assert lay["num_tokens_per_expert"][3] == 2  # counted per slot
+    assert lay["is_token_in_rank"].sum(1).tolist() == [0, 1, 1, 1]
+    x = np.arange(4 * 8, dtype=np.uint16).reshape(4, 8)
+    w = np.array([[0, 0], [0.25, 0.5], [1.0, 0.5], [1.0, 0.5]], np.float32)
+    note = orc.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                      lay["num_tokens_per_expert"], 2, 1)
+    dis = orc.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                       note["recv_gbl_rank_prefix_sum"], 16)
+    s = dis["send_slot"][1, 1]
+    assert dis["recv_topk_weights"][s].tolist() == [0.25, 0.5]
+    assert dis["recv_topk_idx"][s].tolist() == [1, 1]
+    com = orc.combine(dis["recv_x"], dis["recv_topk_weights"], dis["send_slot"], note["num_recv_tokens"])
+    assert not com["combined_x"][0].any()
+    assert com["combined_topk_weights"][2].tolist() == [1.0, 0.0]
+
+
+def test_edge_receive_capacity_overflow(orc, workload_inputs):
+    d = workload_inputs("tiny")
+    lay = orc.layout(d["topk_idx"], 16, 8)
+    note = orc.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                      lay["num_tokens_per_expert"], 4, 1)
+    cap = note["num_recv_tokens"] - 10
+    dis = orc.dispatch(d["x"], d["topk_idx"], d["topk_weights"], lay["is_token_in_rank"],
+                       note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], 16, recv_capacity=cap)
+    assert dis["status"] == 2
+    assert np.sort(dis["send_slot"][dis["send_slot"] >= 0]).tolist() == list(range(cap))
