@@ -1,0 +1,220 @@
+"""Benchmark of the expert-parallel dispatch/combine core on one MI355X.
+
+One step = the whole path on one batch: ep_get_layout, ep_notify, ep_dispatch,
+ep_combine (identity experts: combine reads dispatch's receive rows), all on
+torch's current stream, inputs already resident in HBM.  The default workload
+is the prefill one: 4096 tokens, hidden 7168 bf16, top-8 of 256 experts over 64
+emulated ranks (8 nodes x 8), 24 channels, seed 0.
+
+The metric is dispatch+combine HBM throughput: the bytes the method must move
+(x read once per token, each receive row written once and read back once,
+metadata) over the measured dispatch+combine kernel time (HIP events around each
+call, averaged over the timed steps).  ``ms_per_step`` is the wall time of a
+whole step including layout and notify.  Prints one JSON line.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E
+
+
+def dispatch_bytes(T, H, K, R, N) -> int:
+    """x read once per token, topk ids (i64) and weights (f32) read, every
+    receive row written with its weights (f32), local ids (i64) and src_info
+    (2 x i32), and the [t][R] send_slot map written."""
+    return T * 2 * H + T * K * 12 + N * (2 * H + 4 * K + 8 * K + 8) + 4 * T * R
+
+
+def combine_bytes(T, H, K, R, N) -> int:
+    """every receive row and its weights read once, the send_slot map read,
+    the combined rows (bf16) and weights (f32) written."""
+    return N * 2 * H + N * 4 * K + 4 * T * R + T * 2 * H + T * 4 * K
+
+
+def layout_notify_bytes(T, K, R, E, C) -> int:
+    nodes = max(1, R // 8)
+    return T * K * 8 + T * R + 4 * (R + nodes + E) + T * R + 4 * (R + nodes + E) + 4 * (R + nodes) * (C + 1) + 4 * E
+
+
+def cpu_baseline(d, wl, n_recv, budget_s: float = 12.0) -> dict:
+    """The oracle (single-threaded C) on the same workload, full steps repeated
+    until about budget_s of CPU time has passed."""
+    import oracle
+
+    o = oracle.Oracle()
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    reps, t0 = 0, time.perf_counter()
+    t_disp = t_comb = 0.0
+    while True:
+        lay = o.layout(idx, wl.experts, wl.ranks)
+        note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                        lay["num_tokens_per_expert"], wl.channels, wl.expert_alignment)
+        a = time.perf_counter()
+        dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                         note["recv_gbl_rank_prefix_sum"], wl.experts)
+        b = time.perf_counter()
+        o.combine(dis["recv_x"], dis["recv_topk_weights"], dis["send_slot"], note["num_recv_tokens"])
+        c = time.perf_counter()
+        t_disp += b - a
+        t_comb += c - b
+        reps += 1
+        if time.perf_counter() - t0 > budget_s or reps >= 20:
+            break
+    T, H, K, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
+    alg = dispatch_bytes(T, H, K, R, n_recv) + combine_bytes(T, H, K, R, n_recv)
+    dc = (t_disp + t_comb) / reps
+    return {"value": round(alg / dc / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{reps} full {wl.name} steps (layout+notify+dispatch+combine, t={T}, h={H}, k={K}, "
+                      f"R={R}); value = dispatch+combine algorithmic bytes / oracle dispatch+combine time",
+            "us_dispatch_plus_combine": round(dc * 1e6, 1), "host_cores": os.cpu_count()}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="extra steps with a 1 GiB scratch write before each, untimed, to evict the caches")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
+              f"(this build has no multi-GPU path)", file=sys.stderr)
+        return 2
+
+    import torch
+
+    from combine_ep_get_02_amd import ep, inputs
+
+    if not os.path.exists(ep.LIBRARY):
+        import __graft_entry__
+
+        __graft_entry__.build()
+
+    torch.cuda.set_device(0)
+    d = inputs.generate(args.workload)
+    wl = d["workload"]
+    T, H, K, E, R, C = wl.tokens, wl.hidden, wl.topk, wl.experts, wl.ranks, wl.channels
+    shape = ep.make_shape(T, H, K, E, R, C, 0, wl.expert_alignment)
+    x = torch.from_numpy(d["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    w = torch.from_numpy(d["topk_weights"]).cuda()
+
+    probe = ep.allocate(shape, 0)
+    ep.run_layout(probe, idx)
+    n_recv = ep.run_notify(probe, read_back=True)
+    del probe
+    b = ep.allocate(shape, n_recv)
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record()
+        ep.run_layout(b, idx)
+        if ev is not None:
+            ev[1].record()
+        ep.run_notify(b)
+        if ev is not None:
+            ev[2].record()
+        ep.run_dispatch(b, x, idx, w)
+        if ev is not None:
+            ev[3].record()
+        ep.run_combine(b)
+        if ev is not None:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(events[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    def mean_ms(a, c):
+        return float(np.mean([ev[a].elapsed_time(ev[c]) for ev in events]))
+
+    ms_layout, ms_notify = mean_ms(0, 1), mean_ms(1, 2)
+    ms_dispatch, ms_combine = mean_ms(2, 3), mean_ms(3, 4)
+
+    # correctness guard on the measured buffers: identity experts return x
+    live = b.in_rank.bool().any(1)
+    ok = bool(torch.equal(b.combined_x[live], x[live])) and int(b.dev_status.item()) == 0
+
+    # cold-cache cross-check: evict with a 1 GiB write before each (untimed) step
+    cold = None
+    if args.cold_steps > 0:
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            scratch.fill_(i & 0xFF)
+            step(cev[i])
+        torch.cuda.synchronize()
+        cold = {"us_dispatch": round(float(np.mean([e[2].elapsed_time(e[3]) for e in cev])) * 1e3, 2),
+                "us_combine": round(float(np.mean([e[3].elapsed_time(e[4]) for e in cev])) * 1e3, 2)}
+        del scratch
+
+    db, cb = dispatch_bytes(T, H, K, R, n_recv), combine_bytes(T, H, K, R, n_recv)
+    gbps = (db + cb) / ((ms_dispatch + ms_combine) * 1e-3) / 1e9
+    if ms_dispatch >= ms_combine:
+        dom, dom_bytes, dom_ms = "dispatch_kernel", db, ms_dispatch
+    else:
+        dom, dom_bytes, dom_ms = "combine_kernel", cb, ms_combine
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    out = {
+        "metric": "dispatch+combine µs/iter and HBM GB/s (% peak) at t=4096,h=7168,topk=8",
+        "value": round(gbps, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed / args.steps * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: t={T}, h={H}, topk={K}, experts={E}, emulated ranks={R} "
+                               f"({max(1, R // 8)} nodes x 8), channels={C}, uniform routing, seed {wl.seed}",
+                   "global_batch": T, "seq_len": 1, "parallelism": "single GPU share (one source rank)"},
+        "us_per_iter_dispatch_plus_combine": round((ms_dispatch + ms_combine) * 1e3, 2),
+        "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+        "us_layout": round(ms_layout * 1e3, 2),
+        "us_notify": round(ms_notify * 1e3, 2),
+        "us_dispatch": round(ms_dispatch * 1e3, 2),
+        "us_combine": round(ms_combine * 1e3, 2),
+        "num_recv_tokens": n_recv,
+        "bytes_dispatch": db,
+        "bytes_combine": cb,
+        "bytes_layout_notify": layout_notify_bytes(T, K, R, E, C),
+        "identity_check": ok,
+        "cold": cold,
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(d, wl, n_recv)
+    print(json.dumps(out), flush=True)
+    return 0 if ok else 1
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,133 @@
+// ep_api.hip -- the extern "C" entry points of libep.so (declared in ep.h):
+// argument checks, then kernel launches on the caller's stream.
+//
+// Every check runs on the host before anything is enqueued, so a rejected call
+// leaves the stream untouched.  The argument rules restate the host asserts of
+// the mscclpp ht_runtime.cc mirror (constructor: fewer than 8 ranks or a
+// multiple of 8; experts split evenly over ranks; rows a whole number of
+// 16-byte units in internodeCombine / intranodeCombine).
+#include <limits.h>
+
+#include "ep_internal.h"
+
+namespace {
+
+using namespace ep;
+
+ep_status_t check_shape(const ep_shape_t *s) {
+    if (s == nullptr) return EP_ERR_INVALID_ARG;
+    if (s->num_tokens < 0 || s->hidden < 8 || s->hidden % 8 != 0 || s->num_topk < 1 || s->num_experts < 1 ||
+        s->num_ranks < 1 || s->num_channels < 1 || s->expert_alignment < 1 || s->my_rank < 0 ||
+        s->my_rank >= s->num_ranks)
+        return EP_ERR_INVALID_ARG;
+    if (s->num_ranks >= kRanksPerNode && s->num_ranks % kRanksPerNode != 0) return EP_ERR_INVALID_ARG;
+    if (s->num_experts % s->num_ranks != 0) return EP_ERR_INVALID_ARG;
+    if (s->num_ranks > kMaxRanks || s->num_topk > kMaxTopk || s->num_channels > kMaxChannels)
+        return EP_ERR_UNSUPPORTED;
+    // every receive row index and every send_slot entry must fit int32
+    if ((int64_t)s->num_tokens * s->num_ranks > INT_MAX) return EP_ERR_UNSUPPORTED;
+    return EP_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char *ep_status_string(ep_status_t status) {
+    switch (status) {
+        case EP_OK: return "EP_OK";
+        case EP_ERR_INVALID_ARG: return "EP_ERR_INVALID_ARG: malformed shape or pointer";
+        case EP_ERR_UNSUPPORTED: return "EP_ERR_UNSUPPORTED: shape beyond this version's limits";
+        case EP_ERR_HIP: return "EP_ERR_HIP: a HIP launch or copy failed";
+    }
+    return "unknown ep_status_t";
+}
+
+size_t ep_workspace_bytes(const ep_shape_t *s) {
+    if (check_shape(s) != EP_OK) return 0;
+    return workspace_layout(s->num_tokens, s->num_ranks, s->num_channels).total;
+}
+
+ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                          int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                          uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (topk_idx == nullptr || is_token_in_rank == nullptr)) return EP_ERR_INVALID_ARG;
+    return from_hip(launch_layout(*s, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                                  num_tokens_per_expert, is_token_in_rank, dev_status, stream));
+}
+
+ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
+                      const int32_t *num_tokens_per_rdma_rank, const int32_t *num_tokens_per_expert,
+                      int32_t *gbl_channel_prefix_matrix, int32_t *rdma_channel_prefix_matrix,
+                      int32_t *recv_gbl_rank_prefix_sum, int32_t *recv_rdma_rank_prefix_sum,
+                      int32_t *num_recv_tokens_per_expert, int32_t *num_recv_tokens, int32_t *num_recv_tokens_host,
+                      void *workspace, size_t workspace_bytes, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr ||
+        gbl_channel_prefix_matrix == nullptr || rdma_channel_prefix_matrix == nullptr ||
+        recv_gbl_rank_prefix_sum == nullptr || recv_rdma_rank_prefix_sum == nullptr ||
+        num_recv_tokens_per_expert == nullptr || num_recv_tokens == nullptr || workspace == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && is_token_in_rank == nullptr) return EP_ERR_INVALID_ARG;
+    if (workspace_bytes < ep_workspace_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return EP_ERR_INVALID_ARG;
+    hipError_t e = launch_notify(*s, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                                 num_tokens_per_expert, gbl_channel_prefix_matrix, rdma_channel_prefix_matrix,
+                                 recv_gbl_rank_prefix_sum, recv_rdma_rank_prefix_sum, num_recv_tokens_per_expert,
+                                 num_recv_tokens, static_cast<char *>(workspace), dev_status, stream);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    if (num_recv_tokens_host != nullptr) {
+        e = hipMemcpyAsync(num_recv_tokens_host, num_recv_tokens, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return EP_ERR_HIP;
+    }
+    return EP_OK;
+}
+
+ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_idx, const float *topk_weights,
+                        const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
+                        int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
+                        int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (recv_capacity < 0) return EP_ERR_INVALID_ARG;
+    if (s->num_tokens == 0) return EP_OK;
+    if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || recv_gbl_rank_prefix_sum == nullptr ||
+        workspace == nullptr || send_slot == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
+    if (workspace_bytes < ep_workspace_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+        return EP_ERR_INVALID_ARG;
+    return from_hip(launch_dispatch(*s, static_cast<const uint4 *>(x), topk_idx, topk_weights,
+                                    recv_gbl_rank_prefix_sum, static_cast<const char *>(workspace), recv_capacity,
+                                    static_cast<uint4 *>(recv_x), recv_topk_weights, recv_topk_idx, recv_src_info,
+                                    send_slot, dev_status, stream));
+}
+
+ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_topk_weights, const int32_t *send_slot,
+                       int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
+                       hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (num_recv_rows < 0) return EP_ERR_INVALID_ARG;
+    if (s->num_tokens == 0) return EP_OK;
+    if (send_slot == nullptr || combined_x == nullptr) return EP_ERR_INVALID_ARG;
+    if (num_recv_rows > 0 && (y == nullptr || recv_topk_weights == nullptr)) return EP_ERR_INVALID_ARG;
+    if (!aligned16(combined_x) || (y != nullptr && !aligned16(y))) return EP_ERR_INVALID_ARG;
+    return from_hip(launch_combine(*s, static_cast<const uint4 *>(y), recv_topk_weights, send_slot, num_recv_rows,
+                                   static_cast<uint4 *>(combined_x), combined_topk_weights, dev_status, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,185 @@
+// ep_dispatch.hip -- stages 3+4, dispatch: row assignment and packing (gfx950).
+//
+// Definitions (mscclpp ht_runtime.cc mirror, internodeDispatch /
+// intranodeDispatch; CUDA与DeepEP article 4.1, SrcInfo): the receive region
+// holds every destination rank's slab in one allocation, laid out
+// [dst_rank][channel]; inside a slab the channel segments follow in channel
+// order with tokens ascending.  Because channels are contiguous ascending token
+// ranges, token t's row on rank r is
+//     slab_begin(r) + #{t' < t : t' goes to r},   slab_begin(r) = recv_gbl[r-1].
+// For each routed (t, r): recv_x[row] = x[t] (bitwise), the topk weights and
+// local expert ids of the slots whose expert lives on r (0 / -1 elsewhere),
+// src_info[row] = {my_rank, t}, send_slot[t][r] = row.
+//
+// Design (the pages' sender/forwarder rings are transport machinery and are not
+// reproduced): one wave per (token, row segment).  Notify left each token's
+// 64-bit rank mask and, per 64-token chunk, the exclusive row offset inside
+// every slab; the wave loads its chunk's 64 masks (one per lane), and for each
+// destination r a ballot over "lane's token goes to r" masked to the lanes
+// before this token gives the in-chunk rank, so rows come out in the canonical
+// order with no serial scan.  Lane r ends up holding the row for rank r.  The
+// token's row segment is read once into VGPRs (16-byte loads, coalesced along
+// the row) and stored to every destination with 16-byte non-temporal stores:
+// x is read once per token, the ~8x larger receive region is written once.
+#include "ep_internal.h"
+
+namespace ep {
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kDispatchWaves = 4;
+
+struct DispatchParams {
+    const u32x4 *x;
+    const int64_t *topk_idx;
+    const float *topk_w;
+    const int32_t *recv_gbl;
+    const uint64_t *mask;
+    const int32_t *rank_off;
+    u32x4 *recv_x;
+    float *recv_w;
+    int64_t *recv_idx;
+    int32_t *src_info;
+    int32_t *send_slot;
+    int32_t *dev_status;
+    int64_t T;
+    int64_t row_units;  // 16-byte units per row
+    int R, K, E, experts_per_rank, my_rank, cap, S;
+};
+
+template <int VPL, bool EXACT>
+__global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(DispatchParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * kDispatchWaves + (threadIdx.x >> 6);
+    if (w >= p.T * p.S) return;  // whole wave leaves together
+    const int64_t t = w / p.S;
+    const int seg = (int)(w - t * p.S);
+    const int64_t q = t / kChunk;
+    const int my = (int)(t - q * kChunk);
+    const int R = p.R;
+
+    // ---- row assignment (a3)
+    const int64_t tok = q * kChunk + lane;
+    const uint64_t m = tok < p.T ? p.mask[tok] : 0ull;
+    const uint64_t mine = readlane64(m, my);
+    int slot = -1;
+    if (mine != 0ull) {
+        int base = 0;
+        if (lane < R && ((mine >> lane) & 1ull))
+            base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
+        const uint64_t before = (1ull << my) - 1ull;
+        for (uint64_t mm = mine; mm != 0ull; mm &= mm - 1ull) {
+            const int r = __builtin_ctzll(mm);
+            const uint64_t b = ballot64((m >> r) & 1ull);
+            if (lane == r) slot = base + __popcll(b & before);
+        }
+    }
+    const bool over = slot >= p.cap;
+    if (over) slot = -1;
+    const uint64_t dests = ballot64(slot >= 0);
+
+    if (seg == 0) {
+        if (lane < R) p.send_slot[t * R + lane] = slot;
+        if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+        // ---- metadata (a4): weights / local ids of the slots living on each destination
+        int64_t e = -1;
+        float wt = 0.0f;
+        int erank = -1;
+        if (lane < p.K) {
+            e = p.topk_idx[t * p.K + lane];
+            wt = p.topk_w[t * p.K + lane];
+            if (e >= 0 && e < p.E) erank = (int)e / p.experts_per_rank;
+        }
+        for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+            const int r = __builtin_ctzll(dd);
+            const int64_t s = readlane32(slot, r);
+            if (lane < p.K) {
+                const bool on = erank == r;
+                p.recv_w[s * p.K + lane] = on ? wt : 0.0f;
+                if (p.recv_idx != nullptr) p.recv_idx[s * p.K + lane] = on ? e - (int64_t)r * p.experts_per_rank : -1;
+            }
+            if (lane == 0) reinterpret_cast<int2 *>(p.src_info)[s] = make_int2(p.my_rank, (int)t);
+        }
+    }
+    if (dests == 0ull) return;
+
+    // ---- row copy (a4): read the segment once, store it to every destination
+    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
+    const u32x4 *src = p.x + t * p.row_units + c0;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+    for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+        const int r = __builtin_ctzll(dd);
+        const int64_t s = readlane32(slot, r);
+        u32x4 *dst = p.recv_x + s * p.row_units + c0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
+    }
+}
+
+template <int VPL, bool EXACT>
+hipError_t run(const DispatchParams &p, hipStream_t stream) {
+    const int64_t waves = p.T * p.S;
+    const int64_t blocks = (waves + kDispatchWaves - 1) / kDispatchWaves;
+    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT>), dim3((unsigned)blocks), dim3(kDispatchWaves * kWave), 0,
+                       stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *topk_idx, const float *topk_w,
+                           const int32_t *recv_gbl, const char *ws, int32_t cap, uint4 *recv_x, float *recv_w,
+                           int64_t *recv_idx, int32_t *src_info, int32_t *send_slot, int32_t *dev_status,
+                           hipStream_t stream) {
+    if (s.num_tokens == 0) return hipSuccess;
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_channels);
+    DispatchParams p;
+    p.x = reinterpret_cast<const u32x4 *>(x);
+    p.topk_idx = topk_idx;
+    p.topk_w = topk_w;
+    p.recv_gbl = recv_gbl;
+    p.mask = reinterpret_cast<const uint64_t *>(ws + w.mask);
+    p.rank_off = reinterpret_cast<const int32_t *>(ws + w.rank_off);
+    p.recv_x = reinterpret_cast<u32x4 *>(recv_x);
+    p.recv_w = recv_w;
+    p.recv_idx = recv_idx;
+    p.src_info = src_info;
+    p.send_slot = send_slot;
+    p.dev_status = dev_status;
+    p.T = s.num_tokens;
+    p.row_units = s.hidden / 8;
+    p.R = s.num_ranks;
+    p.K = s.num_topk;
+    p.E = s.num_experts;
+    p.experts_per_rank = s.num_experts / s.num_ranks;
+    p.my_rank = s.my_rank;
+    p.cap = cap;
+    // per-lane 16-byte units held in registers: a whole number of wave-wide
+    // passes when the row allows it
+    const int64_t U = p.row_units;
+    if (U % (14 * kWave) == 0) {
+        p.S = (int)(U / (14 * kWave));
+        return run<14, true>(p, stream);
+    }
+    if (U % (8 * kWave) == 0) {
+        p.S = (int)(U / (8 * kWave));
+        return run<8, true>(p, stream);
+    }
+    if (U % (4 * kWave) == 0) {
+        p.S = (int)(U / (4 * kWave));
+        return run<4, true>(p, stream);
+    }
+    if (U % kWave == 0) {
+        p.S = (int)(U / kWave);
+        return run<1, true>(p, stream);
+    }
+    p.S = (int)((U + 4 * kWave - 1) / (4 * kWave));
+    return run<4, false>(p, stream);
+}
+
+}  // namespace ep

@@ -1,0 +1,206 @@
+"""Thin Python binding of libep.so (the C ABI in include/ep.h).
+
+The functions carry the C names and only marshal arguments: torch tensors
+become raw device pointers, the stream defaults to torch's current stream,
+and a non-OK status becomes an ``EpError``.  All computation happens in the
+library's HIP kernels; there is no fallback path.  Torch is used for device
+memory and streams only.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(_PKG, "libep.so")
+
+EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
+EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
+
+EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_combine", "ep_workspace_bytes", "ep_status_string")
+
+
+class EpError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {ep_status_string(status)}")
+
+
+class ep_shape_t(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_int32) for name in (
+        "num_tokens", "hidden", "num_topk", "num_experts", "num_ranks", "num_channels", "my_rank",
+        "expert_alignment")]
+
+
+_P = ctypes.c_void_p
+_S = ctypes.POINTER(ep_shape_t)
+_lib: ctypes.CDLL | None = None
+
+
+def load(path: str = LIBRARY) -> ctypes.CDLL:
+    """Load libep.so.  A missing library is an error: there is no fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"libep.so not built at {path}; run `python -m combine_ep_get_02_amd.build`")
+    lib = ctypes.CDLL(path)
+    lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P]
+    lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
+    lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
+    lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
+    for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_combine"):
+        getattr(lib, name).restype = ctypes.c_int
+    lib.ep_workspace_bytes.argtypes = [_S]
+    lib.ep_workspace_bytes.restype = ctypes.c_size_t
+    lib.ep_status_string.argtypes = [ctypes.c_int]
+    lib.ep_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str) -> None:
+    if status != EP_OK:
+        raise EpError(status, where)
+
+
+def make_shape(num_tokens, hidden, num_topk, num_experts, num_ranks, num_channels, my_rank=0,
+               expert_alignment=1) -> ep_shape_t:
+    return ep_shape_t(num_tokens, hidden, num_topk, num_experts, num_ranks, num_channels, my_rank,
+                      expert_alignment)
+
+
+def ep_status_string(status: int) -> str:
+    return load().ep_status_string(status).decode()
+
+
+def ep_workspace_bytes(shape: ep_shape_t) -> int:
+    return int(load().ep_workspace_bytes(ctypes.byref(shape)))
+
+
+def ep_get_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert,
+                  is_token_in_rank, dev_status=None, stream=None) -> None:
+    _check(load().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx), _ptr(num_tokens_per_rank),
+                                _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
+                                _ptr(is_token_in_rank), _ptr(dev_status), _stream(stream)), "ep_get_layout")
+
+
+def ep_notify(shape, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert,
+              gbl_channel_prefix_matrix, rdma_channel_prefix_matrix, recv_gbl_rank_prefix_sum,
+              recv_rdma_rank_prefix_sum, num_recv_tokens_per_expert, num_recv_tokens, workspace,
+              read_back: bool = False, dev_status=None, stream=None) -> int | None:
+    """Returns N (host int) when ``read_back`` is set; the call then waits for the stream."""
+    host = ctypes.c_int32(-1)
+    _check(load().ep_notify(ctypes.byref(shape), _ptr(is_token_in_rank), _ptr(num_tokens_per_rank),
+                            _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
+                            _ptr(gbl_channel_prefix_matrix), _ptr(rdma_channel_prefix_matrix),
+                            _ptr(recv_gbl_rank_prefix_sum), _ptr(recv_rdma_rank_prefix_sum),
+                            _ptr(num_recv_tokens_per_expert), _ptr(num_recv_tokens),
+                            ctypes.addressof(host) if read_back else None, _ptr(workspace),
+                            workspace.numel() * workspace.element_size(), _ptr(dev_status), _stream(stream)),
+           "ep_notify")
+    return int(host.value) if read_back else None
+
+
+def ep_dispatch(shape, x, topk_idx, topk_weights, recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x,
+                recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status=None, stream=None) -> None:
+    _check(load().ep_dispatch(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_weights),
+                              _ptr(recv_gbl_rank_prefix_sum), _ptr(workspace),
+                              workspace.numel() * workspace.element_size(), int(recv_capacity), _ptr(recv_x),
+                              _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info), _ptr(send_slot),
+                              _ptr(dev_status), _stream(stream)), "ep_dispatch")
+
+
+def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x, combined_topk_weights=None,
+               dev_status=None, stream=None) -> None:
+    _check(load().ep_combine(ctypes.byref(shape), _ptr(y), _ptr(recv_topk_weights), _ptr(send_slot),
+                             int(num_recv_rows), _ptr(combined_x), _ptr(combined_topk_weights), _ptr(dev_status),
+                             _stream(stream)), "ep_combine")
+
+
+# ----------------------------------------------------------------------------- buffers
+@dataclass
+class Buffers:
+    """Every device buffer of one pass, allocated by torch for a shape."""
+    shape: ep_shape_t
+    capacity: int
+    per_rank: torch.Tensor
+    per_node: torch.Tensor
+    per_expert: torch.Tensor
+    in_rank: torch.Tensor
+    gbl: torch.Tensor
+    rdma: torch.Tensor
+    recv_gbl: torch.Tensor
+    recv_rdma: torch.Tensor
+    recv_per_expert: torch.Tensor
+    num_recv: torch.Tensor
+    workspace: torch.Tensor
+    recv_x: torch.Tensor
+    recv_w: torch.Tensor
+    recv_idx: torch.Tensor | None
+    src_info: torch.Tensor
+    send_slot: torch.Tensor
+    combined_x: torch.Tensor
+    combined_w: torch.Tensor
+    dev_status: torch.Tensor
+
+
+def allocate(shape: ep_shape_t, capacity: int, device="cuda", with_recv_idx: bool = True) -> Buffers:
+    T, H, K = shape.num_tokens, shape.hidden, shape.num_topk
+    R, E, C = shape.num_ranks, shape.num_experts, shape.num_channels
+    nodes = max(1, R // 8)
+    i32 = dict(dtype=torch.int32, device=device)
+    cap = max(int(capacity), 0)
+    return Buffers(
+        shape=shape, capacity=cap,
+        per_rank=torch.empty(R, **i32), per_node=torch.empty(nodes, **i32), per_expert=torch.empty(E, **i32),
+        in_rank=torch.empty((T, R), dtype=torch.uint8, device=device),
+        gbl=torch.empty((R, C), **i32), rdma=torch.empty((nodes, C), **i32), recv_gbl=torch.empty(R, **i32),
+        recv_rdma=torch.empty(nodes, **i32), recv_per_expert=torch.empty(E, **i32), num_recv=torch.empty(1, **i32),
+        workspace=torch.empty(max(ep_workspace_bytes(shape), 256), dtype=torch.uint8, device=device),
+        recv_x=torch.empty((cap, H), dtype=torch.bfloat16, device=device),
+        recv_w=torch.empty((cap, K), dtype=torch.float32, device=device),
+        recv_idx=torch.empty((cap, K), dtype=torch.int64, device=device) if with_recv_idx else None,
+        src_info=torch.empty((cap, 2), **i32), send_slot=torch.empty((T, R), **i32),
+        combined_x=torch.empty((T, H), dtype=torch.bfloat16, device=device),
+        combined_w=torch.empty((T, K), dtype=torch.float32, device=device),
+        dev_status=torch.zeros(1, **i32))
+
+
+def run_layout(b: Buffers, topk_idx, stream=None) -> None:
+    ep_get_layout(b.shape, topk_idx, b.per_rank, b.per_node, b.per_expert, b.in_rank, b.dev_status, stream)
+
+
+def run_notify(b: Buffers, read_back: bool = False, stream=None) -> int | None:
+    return ep_notify(b.shape, b.in_rank, b.per_rank, b.per_node, b.per_expert, b.gbl, b.rdma, b.recv_gbl,
+                     b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, read_back, b.dev_status, stream)
+
+
+def run_dispatch(b: Buffers, x, topk_idx, topk_weights, stream=None) -> None:
+    ep_dispatch(b.shape, x, topk_idx, topk_weights, b.recv_gbl, b.workspace, b.capacity, b.recv_x, b.recv_w,
+                b.recv_idx, b.src_info, b.send_slot, b.dev_status, stream)
+
+
+def run_combine(b: Buffers, y=None, num_recv_rows=None, with_weights: bool = True, stream=None) -> None:
+    ep_combine(b.shape, b.recv_x if y is None else y, b.recv_w, b.send_slot,
+               b.capacity if num_recv_rows is None else num_recv_rows, b.combined_x,
+               b.combined_w if with_weights else None, b.dev_status, stream)

@@ -1,0 +1,173 @@
+/*
+ * ep.h -- C ABI of libep.so: the expert-parallel dispatch/combine core for one
+ * GPU's share of the work (one source rank, num_ranks emulated destination
+ * ranks whose receive slabs share one HBM allocation), on AMD MI355X (gfx950).
+ *
+ * Four stages, each a call below:
+ *   ep_get_layout  topk_idx -> token counts per rank / node / expert, is_token_in_rank
+ *   ep_notify      counts   -> channel prefix matrices, receive prefix sums,
+ *                              aligned per-expert receive counts, N_recv
+ *   ep_dispatch    x rows   -> receive region laid out [dst_rank][channel]
+ *   ep_combine     expert outputs in receive layout -> weighted sum in token order
+ *
+ * Sources (web pages, cited by page title and section/function):
+ *   mscclpp src/ext/ep/ht_runtime.cc mirror -- the torch-free host runtime:
+ *     getDispatchLayout, internodeNotifyDispatch, internodeDispatch,
+ *     internodeCombine, intranodeDispatch, intranodeCombine.  It turned tensor
+ *     arguments into raw device pointers plus sizes, outputs into caller-owned
+ *     buffers and the torch stream into a plain stream, which this ABI keeps.
+ *   "DeepEP+NVSHMEM/DeepEP/internode.cu" notes, section 1 notify_dispatch
+ *     (sm0 stage 6: prefix sums and expert alignment; sm1-x: channel counts).
+ *   "CUDA与DeepEP" article, sections 2.2 (rank -> node), 3.2 (prefix sums),
+ *     4.1 (SrcInfo), 4.2 (combine routing).
+ *
+ * Conventions for every call:
+ *   - Pointers are DEVICE pointers unless marked (host).  The caller allocates
+ *     and frees every buffer; the library never allocates device memory and
+ *     keeps no state between calls.  Calls on different streams with disjoint
+ *     buffers may run concurrently.
+ *   - Each call only enqueues kernels on `stream` and returns, except
+ *     ep_notify when num_recv_tokens_host is non-NULL (it then waits for the
+ *     stream).  Outputs are valid in stream order after the call's kernels.
+ *   - Shape or pointer errors are reported synchronously, before any launch:
+ *     EP_ERR_INVALID_ARG for malformed arguments, EP_ERR_UNSUPPORTED for shapes
+ *     beyond this version's limits.  EP_ERR_HIP reports a failed launch.
+ *   - Data-dependent problems never trap: the kernels skip the offending item
+ *     and OR a bit (EP_DEV_*) into *dev_status when dev_status is non-NULL.
+ *     The caller zeroes *dev_status when it wants a fresh reading.
+ *   - Row buffers (x, recv_x, y, combined_x) are bf16 rows of `hidden`
+ *     elements and must be 16-byte aligned; rows move in 16-byte units.
+ */
+#ifndef EP_H
+#define EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_INVALID_ARG = 1,
+    EP_ERR_UNSUPPORTED = 2,
+    EP_ERR_HIP = 3
+} ep_status_t;
+
+/* Bits OR-ed into *dev_status by the kernels. */
+enum {
+    EP_DEV_BAD_TOPK_IDX = 1,   /* a topk id outside [-1, num_experts): that slot is treated as masked */
+    EP_DEV_RECV_OVERFLOW = 2,  /* a receive row >= recv_capacity: the row is not written, send_slot = -1 */
+    EP_DEV_COUNT_MISMATCH = 4, /* num_tokens_per_rank / _per_rdma_rank disagree with is_token_in_rank */
+    EP_DEV_BAD_SEND_SLOT = 8   /* combine met a send_slot outside [-1, num_recv_rows): skipped */
+};
+
+/* Problem shape (host struct, read during the call only). */
+typedef struct {
+    int32_t num_tokens;       /* t >= 0 tokens on this rank                                      */
+    int32_t hidden;           /* h >= 8, h % 8 == 0 (a bf16 row is a whole number of 16-byte units)*/
+    int32_t num_topk;         /* 1 <= k <= 32                                                    */
+    int32_t num_experts;      /* E >= 1, E % num_ranks == 0; expert e lives on rank e / (E / R)  */
+    int32_t num_ranks;        /* 1 <= R <= 64, and R < 8 or R % 8 == 0 (8 ranks per node)        */
+    int32_t num_channels;     /* 1 <= C <= 4096; channel c = tokens [c*ceil(t/C), (c+1)*ceil(t/C)) */
+    int32_t my_rank;          /* 0 <= my_rank < R; stored as src_rank in recv_src_info           */
+    int32_t expert_alignment; /* >= 1; per-expert receive counts are rounded up to a multiple    */
+} ep_shape_t;
+
+/*
+ * Stage 1, dispatch layout.  [mscclpp ht_runtime.cc, getDispatchLayout]
+ * In:  topk_idx [t][k] int64, -1 = masked slot.
+ * Out: num_tokens_per_rank      [R]     int32: tokens with at least one expert on rank r
+ *      num_tokens_per_rdma_rank [nodes] int32: tokens with at least one expert on a rank of
+ *                                              node n (node = rank / 8, nodes = max(1, R / 8))
+ *      num_tokens_per_expert    [E]     int32: valid topk slots naming expert e
+ *      is_token_in_rank         [t][R]  uint8 (0/1, row-major)
+ * dev_status (nullable): EP_DEV_BAD_TOPK_IDX.
+ */
+ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                          int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                          uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Stage 2, notify.  [mscclpp ht_runtime.cc, internodeNotifyDispatch; internode.cu notes,
+ * notify_dispatch sm1-x stages 1-3 and sm0 stage 6]
+ * In:  is_token_in_rank [t][R] uint8 (any non-zero byte counts as 1) and the three count
+ *      arrays of stage 1.
+ * Out: gbl_channel_prefix_matrix  [R][C]     int32: inclusive prefix over channels of the
+ *                                                   tokens of each channel sent to rank r
+ *      rdma_channel_prefix_matrix [nodes][C] int32: the same per node
+ *      recv_gbl_rank_prefix_sum   [R]        int32: inclusive prefix of num_tokens_per_rank;
+ *                                                   slab r of the receive region is rows
+ *                                                   [prefix[r-1], prefix[r])
+ *      recv_rdma_rank_prefix_sum  [nodes]    int32: inclusive prefix of num_tokens_per_rdma_rank
+ *      num_recv_tokens_per_expert [E]        int32: ceil(n_e / expert_alignment) * expert_alignment
+ *      num_recv_tokens            [1]        int32: N = total receive rows (device)
+ *      num_recv_tokens_host  (host, nullable): when non-NULL the call waits for the stream
+ *                                              and stores N there.
+ *      workspace: ep_workspace_bytes(s) bytes of device memory, written here and read by
+ *                 ep_dispatch (per-token rank masks and per-64-token-chunk row offsets).
+ *                 Its contents are opaque; it needs no initialisation.
+ * dev_status (nullable): EP_DEV_COUNT_MISMATCH.
+ */
+ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
+                      const int32_t *num_tokens_per_rdma_rank, const int32_t *num_tokens_per_expert,
+                      int32_t *gbl_channel_prefix_matrix, int32_t *rdma_channel_prefix_matrix,
+                      int32_t *recv_gbl_rank_prefix_sum, int32_t *recv_rdma_rank_prefix_sum,
+                      int32_t *num_recv_tokens_per_expert, int32_t *num_recv_tokens, int32_t *num_recv_tokens_host,
+                      void *workspace, size_t workspace_bytes, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Stages 3+4, dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch;
+ * CUDA与DeepEP article 4.1 SrcInfo]
+ * The receive region is laid out [dst_rank][channel]: slab r holds the tokens sent to r,
+ * channel segments in channel order, tokens ascending inside a segment; so token t's row
+ * on rank r is  prefix[r-1] + #{t' < t sent to r}.
+ * In:  x [t][h] bf16; topk_idx [t][k] int64; topk_weights [t][k] f32;
+ *      recv_gbl_rank_prefix_sum [R] from ep_notify; workspace as filled by ep_notify
+ *      for the same is_token_in_rank.
+ * Out (recv_capacity rows allocated by the caller):
+ *      recv_x            [cap][h] bf16: bitwise copy of x[t]
+ *      recv_topk_weights [cap][k] f32:  w[t][j] where slot j's expert lives on the
+ *                                       receiving rank, else 0
+ *      recv_topk_idx     [cap][k] int64 (nullable): the receiver's local expert id
+ *                                       e - r*(E/R) for those slots, else -1
+ *      recv_src_info     [cap][2] int32: {my_rank, t} (8-byte aligned)
+ *      send_slot         [t][R]   int32: the row of (t, r), -1 where t is not sent to r
+ * Rows >= recv_capacity are skipped and flagged (EP_DEV_RECV_OVERFLOW); their send_slot is -1.
+ */
+ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_idx, const float *topk_weights,
+                        const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
+                        int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
+                        int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Stage 5, combine.  [mscclpp ht_runtime.cc, internodeCombine / intranodeCombine (bf16 out,
+ * combined topk weights); CUDA与DeepEP article 4.2 (rows return to their source token)]
+ * For each token t, over ranks r ascending with s = send_slot[t][r] >= 0:
+ *     W = sum_j recv_topk_weights[s][j]       (fp32 adds, j ascending, from +0)
+ *     acc[i] = fmaf(W, y[s][i], acc[i])       (fp32, from +0)
+ *   combined_x[t][i] = acc[i] rounded to bf16 (nearest, ties to even)
+ *   combined_topk_weights[t][j] = sum over the same r of recv_topk_weights[s][j] (fp32, r ascending)
+ * In:  y [num_recv_rows][h] bf16 (expert outputs in receive layout; y = recv_x for identity
+ *      experts); recv_topk_weights [num_recv_rows][k]; send_slot [t][R].
+ * Out: combined_x [t][h] bf16; combined_topk_weights [t][k] f32 (nullable).
+ * dev_status (nullable): EP_DEV_BAD_SEND_SLOT.
+ */
+ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_topk_weights, const int32_t *send_slot,
+                       int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
+                       hipStream_t stream);
+
+/* Bytes of workspace ep_notify / ep_dispatch need for this shape (0 if s is invalid). */
+size_t ep_workspace_bytes(const ep_shape_t *s);
+
+/* Static text for a status code. */
+const char *ep_status_string(ep_status_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_H */

@@ -226,9 +226,11 @@ def combine_closed_forms(o, x, idx, w, E, R, lay, note, dis) -> list[str]:
     live = lay["is_token_in_rank"].any(1)
     want = np.where(live[:, None], x, np.uint16(0))
     # weights of a live token sum to 1 only when every valid slot carries weight;
-    # the generator's softmax guarantees it.
-    if not np.array_equal(com["combined_x"], want):
-        bad = int((com["combined_x"] != want).sum())
+    # the generator's softmax guarantees it.  Compared as values: the
+    # accumulator starts at +0, so an x element of -0 comes back as +0.
+    got_v, want_v = bf16_to_f64(com["combined_x"]), bf16_to_f64(want)
+    if not np.array_equal(got_v, want_v):
+        bad = int((got_v != want_v).sum())
         errs.append(f"identity combine != x on {bad} elements")
     valid = (idx >= 0) & (idx < E)
     if not np.array_equal(com["combined_topk_weights"], np.where(valid, w, np.float32(0))):

@@ -21,8 +21,8 @@ def test_bf16_rounding_matches_library(orc):
     assert pins.pin_bf16_rounding(orc) == []
 
 
-@pytest.mark.parametrize("name", ["tiny", "sweep"])
-def test_small_workloads_full_hidden(orc, workload_inputs, name):
+@pytest.mark.parametrize("name", ["tiny", "sweep", "prefill"])
+def test_workloads_full_hidden(orc, workload_inputs, name):
     assert pins.pin_workload(orc, workload_inputs(name)) == []
 
 
