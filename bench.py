@@ -91,7 +91,21 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 1 GiB scratch write before each, untimed, to evict the caches")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device-to-device copy of MIB MiB (3 times) and exit; used to "
+                         "scale the HBM byte counters of a profiler against a copy of known size")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+
+        n = args.copy_calibration << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty(n, dtype=torch.uint8, device="cuda")
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n}))
+        return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
               f"(this build has no multi-GPU path)", file=sys.stderr)

@@ -33,6 +33,11 @@ bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
+bool workspace_ok(const ep_shape_t *s, const void *ws, size_t bytes) {
+    return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 &&
+           bytes >= workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels).total;
+}
+
 }  // namespace
 
 extern "C" {
@@ -49,19 +54,22 @@ const char *ep_status_string(ep_status_t status) {
 
 size_t ep_workspace_bytes(const ep_shape_t *s) {
     if (check_shape(s) != EP_OK) return 0;
-    return workspace_layout(s->num_tokens, s->num_ranks, s->num_channels).total;
+    return workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels).total;
 }
 
 ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
                           int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
-                          uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream) {
+                          uint8_t *is_token_in_rank, void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                          hipStream_t stream) {
     ep_status_t st = check_shape(s);
     if (st != EP_OK) return st;
     if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr)
         return EP_ERR_INVALID_ARG;
     if (s->num_tokens > 0 && (topk_idx == nullptr || is_token_in_rank == nullptr)) return EP_ERR_INVALID_ARG;
+    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
     return from_hip(launch_layout(*s, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
-                                  num_tokens_per_expert, is_token_in_rank, dev_status, stream));
+                                  num_tokens_per_expert, is_token_in_rank, static_cast<char *>(workspace),
+                                  dev_status, stream));
 }
 
 ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
@@ -75,11 +83,10 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
     if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr ||
         gbl_channel_prefix_matrix == nullptr || rdma_channel_prefix_matrix == nullptr ||
         recv_gbl_rank_prefix_sum == nullptr || recv_rdma_rank_prefix_sum == nullptr ||
-        num_recv_tokens_per_expert == nullptr || num_recv_tokens == nullptr || workspace == nullptr)
+        num_recv_tokens_per_expert == nullptr || num_recv_tokens == nullptr)
         return EP_ERR_INVALID_ARG;
     if (s->num_tokens > 0 && is_token_in_rank == nullptr) return EP_ERR_INVALID_ARG;
-    if (workspace_bytes < ep_workspace_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return EP_ERR_INVALID_ARG;
+    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
     hipError_t e = launch_notify(*s, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank,
                                  num_tokens_per_expert, gbl_channel_prefix_matrix, rdma_channel_prefix_matrix,
                                  recv_gbl_rank_prefix_sum, recv_rdma_rank_prefix_sum, num_recv_tokens_per_expert,
@@ -102,14 +109,13 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
     if (recv_capacity < 0) return EP_ERR_INVALID_ARG;
     if (s->num_tokens == 0) return EP_OK;
     if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || recv_gbl_rank_prefix_sum == nullptr ||
-        workspace == nullptr || send_slot == nullptr)
+        send_slot == nullptr)
         return EP_ERR_INVALID_ARG;
     if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
         return EP_ERR_INVALID_ARG;
     if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
     if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
-    if (workspace_bytes < ep_workspace_bytes(s) || (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-        return EP_ERR_INVALID_ARG;
+    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
     return from_hip(launch_dispatch(*s, static_cast<const uint4 *>(x), topk_idx, topk_weights,
                                     recv_gbl_rank_prefix_sum, static_cast<const char *>(workspace), recv_capacity,
                                     static_cast<uint4 *>(recv_x), recv_topk_weights, recv_topk_idx, recv_src_info,

@@ -10,14 +10,17 @@
 //   combined_x[t][i] = bf16 round-to-nearest-even of acc[i]
 //   combined_topk_weights[t][j] = sum over the same r of recv_topk_weights[s][j]
 //
-// Design: one wave per (token, row segment); a token-parallel gather driven by
-// send_slot, the map dispatch recorded.  Lane r reads send_slot[t][r] and sums
-// its row's weights, so the wave knows every contribution's row and weight at
-// once; the segment of each contributing row is then streamed in with 16-byte
-// non-temporal loads (8 bf16 per lane per load) and folded into per-lane fp32
-// accumulators with v_fma_f32 in ascending rank order.  One bf16 store per
-// element leaves the wave.  HBM traffic is the ~8 rows read per token plus the
-// one row written.
+// Design: a token-parallel gather driven by send_slot, the map dispatch
+// recorded; one wave per (token, row segment of VPL*1 KiB).  Lane r reads
+// send_slot[t][r], so the wave knows every contributing row at once and starts
+// loading the first row's segment.  The weights arrive in one round trip: lane
+// (i, j) loads weight j of the i-th contributing row, a K-step lane scan adds
+// each row's weights in j order (W), and the first segment's wave also adds
+// the rows' weights column by column in rank order (the combined weights).  The
+// row segments stream in with 16-byte non-temporal loads -- the next row's
+// while the current one is folded -- into per-lane fp32 accumulators with
+// v_fma_f32 in ascending rank order, and the wave ends with one bf16 store per
+// element.  HBM traffic: the ~8 rows read per token plus the one row written.
 #include "ep_internal.h"
 
 namespace ep {
@@ -25,7 +28,6 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kCombineWaves = 4;
 
 struct CombineParams {
     const u32x4 *y;
@@ -52,12 +54,37 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
 }
 
 template <int VPL, bool EXACT>
-__global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(CombineParams p) {
+__device__ __forceinline__ void load_seg(u32x4 (&v)[VPL], const u32x4 *src, int64_t c0, int64_t units) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (EXACT || c0 + i * kWave < units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+}
+
+template <int VPL, bool EXACT>
+__device__ __forceinline__ void fma_seg(float (&acc)[VPL][8], const u32x4 (&v)[VPL], float w, int64_t c0,
+                                        int64_t units) {
+#pragma unroll
+    for (int i = 0; i < VPL; ++i) {
+        if (EXACT || c0 + i * kWave < units) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                acc[i][2 * k] = __builtin_fmaf(w, bf16_lo(v[i][k]), acc[i][2 * k]);
+                acc[i][2 * k + 1] = __builtin_fmaf(w, bf16_hi(v[i][k]), acc[i][2 * k + 1]);
+            }
+        }
+    }
+}
+
+template <int VPL, bool EXACT, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = (int64_t)blockIdx.x * kCombineWaves + (threadIdx.x >> 6);
+    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
     if (w >= p.T * p.S) return;  // whole wave leaves together
     const int64_t t = w / p.S;
     const int seg = (int)(w - t * p.S);
+    const int K = p.K;
+    const int64_t U = p.row_units;
+    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
 
     int slot = -1;
     bool bad = false;
@@ -69,55 +96,71 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(CombinePa
         }
     }
     const uint64_t dests = ballot64(slot >= 0);
-    float W = 0.0f;
-    if (slot >= 0) {
-        const float *wr = p.recv_w + (int64_t)slot * p.K;
-        for (int j = 0; j < p.K; ++j) W = W + wr[j];
+    const int nd = __popcll(dests);
+
+    // first contributing row's segment, in flight while the weights are summed
+    u32x4 cur[VPL];
+    if (dests != 0ull) {
+        const int64_t s0 = readlane32(slot, __builtin_ctzll(dests));
+        load_seg<VPL, EXACT>(cur, p.y + s0 * U + c0, c0, U);
+    }
+
+    // weights, one pass per kWave / K contributing rows: lane (i, j) holds weight
+    // j of row d0 + i.  A K-step lane scan adds each row's weights in j order,
+    // so lane (i, K-1) ends with W of row d0 + i; Wsum keeps lane d = W of row d.
+    const int per_pass = kWave / K;
+    const int li = lane / K, lj = lane - li * K;
+    float Wsum = 0.0f;  // lane d: W of the d-th contributing row
+    float cw = 0.0f;    // lane j: combined weight j (first segment only)
+    uint64_t dd = dests;
+    for (int d0 = 0; d0 < nd; d0 += per_pass) {
+        int my_s = -1;
+        for (int i = 0; i < per_pass && dd != 0ull; ++i, dd &= dd - 1ull) {
+            const int s = readlane32(slot, __builtin_ctzll(dd));
+            if (li == i) my_s = s;
+        }
+        const float v = (my_s >= 0 && li < per_pass) ? p.recv_w[(int64_t)my_s * K + lj] : 0.0f;
+        float run = 0.0f + v;
+        for (int j = 1; j < K; ++j) {
+            const float up = __shfl_up(run, 1, kWave);
+            if (lj == j) run = up + v;
+        }
+        for (int i = 0; i < per_pass && d0 + i < nd; ++i) {
+            const float Wd = readlanef(run, i * K + K - 1);
+            if (lane == d0 + i) Wsum = Wd;
+            if (seg == 0) cw = cw + __shfl(v, i * K + (lane < K ? lane : 0), kWave);
+        }
     }
     if (seg == 0) {
         if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
-        if (p.out_w != nullptr) {
-            float cw = 0.0f;
-            for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
-                const int64_t s = readlane32(slot, __builtin_ctzll(dd));
-                if (lane < p.K) cw = cw + p.recv_w[s * p.K + lane];
-            }
-            if (lane < p.K) p.out_w[t * p.K + lane] = cw;
-        }
+        if (p.out_w != nullptr && lane < K) p.out_w[t * K + lane] = cw;
     }
 
-    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
     float acc[VPL][8];
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[i][k] = 0.0f;
 
-    for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
-        const int r = __builtin_ctzll(dd);
-        const int64_t s = readlane32(slot, r);
-        const float wr = readlanef(W, r);
-        const u32x4 *src = p.y + s * p.row_units + c0;
-        u32x4 v[VPL];
-#pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) {
-            if (EXACT || c0 + i * kWave < p.row_units) {
-#pragma unroll
-                for (int k = 0; k < 4; ++k) {
-                    acc[i][2 * k] = __builtin_fmaf(wr, bf16_lo(v[i][k]), acc[i][2 * k]);
-                    acc[i][2 * k + 1] = __builtin_fmaf(wr, bf16_hi(v[i][k]), acc[i][2 * k + 1]);
-                }
-            }
+    // rows in ascending rank order; the next row's segment loads while the
+    // current one is folded in
+    int d = 0;
+    for (uint64_t ee = dests; ee != 0ull; ++d) {
+        ee &= ee - 1ull;
+        u32x4 nxt[VPL];
+        if (ee != 0ull) {
+            const int64_t sn = readlane32(slot, __builtin_ctzll(ee));
+            load_seg<VPL, EXACT>(nxt, p.y + sn * U + c0, c0, U);
         }
+        fma_seg<VPL, EXACT>(acc, cur, readlanef(Wsum, d), c0, U);
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) cur[i] = nxt[i];
     }
 
-    u32x4 *dst = p.out + t * p.row_units + c0;
+    u32x4 *dst = p.out + t * U + c0;
 #pragma unroll
     for (int i = 0; i < VPL; ++i) {
-        if (EXACT || c0 + i * kWave < p.row_units) {
+        if (EXACT || c0 + i * kWave < U) {
             u32x4 o;
 #pragma unroll
             for (int k = 0; k < 4; ++k) o[k] = to_bf16(acc[i][2 * k]) | (to_bf16(acc[i][2 * k + 1]) << 16);
@@ -126,13 +169,34 @@ __global__ __launch_bounds__(kCombineWaves *kWave) void combine_kernel(CombinePa
     }
 }
 
-template <int VPL, bool EXACT>
-hipError_t run(const CombineParams &p, hipStream_t stream) {
+template <int VPL, bool EXACT, int WPB>
+hipError_t run(CombineParams p, hipStream_t stream) {
+    p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
-    const int64_t blocks = (waves + kCombineWaves - 1) / kCombineWaves;
-    hipLaunchKernelGGL((combine_kernel<VPL, EXACT>), dim3((unsigned)blocks), dim3(kCombineWaves * kWave), 0, stream,
-                       p);
+    const int64_t blocks = (waves + WPB - 1) / WPB;
+    hipLaunchKernelGGL((combine_kernel<VPL, EXACT, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
+}
+
+hipError_t run_tiled(const CombineParams &p, int vpl, int wpb, hipStream_t stream) {
+    const bool exact = p.row_units % (vpl * kWave) == 0;
+#define EP_COMBINE_CASE(V, W) \
+    if (vpl == V && wpb == W) return exact ? run<V, true, W>(p, stream) : run<V, false, W>(p, stream);
+    EP_COMBINE_CASE(1, 4)
+    EP_COMBINE_CASE(2, 4)
+    EP_COMBINE_CASE(2, 8)
+    EP_COMBINE_CASE(4, 4)
+    EP_COMBINE_CASE(7, 4)
+    EP_COMBINE_CASE(8, 4)
+#undef EP_COMBINE_CASE
+    return hipErrorInvalidValue;
+}
+
+// Measured on MI355X: 2 KiB row segments per wave, 8 waves per block.
+void combine_tiling(int64_t row_units, int *vpl, int *wpb) {
+    (void)row_units;
+    *vpl = 2;
+    *wpb = 8;
 }
 
 }  // namespace
@@ -153,25 +217,10 @@ hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv
     p.R = s.num_ranks;
     p.K = s.num_topk;
     p.nrows = num_recv_rows;
-    const int64_t U = p.row_units;
-    if (U % (7 * kWave) == 0) {
-        p.S = (int)(U / (7 * kWave));
-        return run<7, true>(p, stream);
-    }
-    if (U % (8 * kWave) == 0) {
-        p.S = (int)(U / (8 * kWave));
-        return run<8, true>(p, stream);
-    }
-    if (U % (4 * kWave) == 0) {
-        p.S = (int)(U / (4 * kWave));
-        return run<4, true>(p, stream);
-    }
-    if (U % kWave == 0) {
-        p.S = (int)(U / kWave);
-        return run<1, true>(p, stream);
-    }
-    p.S = (int)((U + 4 * kWave - 1) / (4 * kWave));
-    return run<4, false>(p, stream);
+    p.S = 1;
+    int vpl, wpb;
+    combine_tiling(p.row_units, &vpl, &wpb);
+    return run_tiled(p, vpl, wpb, stream);
 }
 
 }  // namespace ep

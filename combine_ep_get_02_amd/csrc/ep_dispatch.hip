@@ -12,23 +12,24 @@
 // src_info[row] = {my_rank, t}, send_slot[t][r] = row.
 //
 // Design (the pages' sender/forwarder rings are transport machinery and are not
-// reproduced): one wave per (token, row segment).  Notify left each token's
-// 64-bit rank mask and, per 64-token chunk, the exclusive row offset inside
-// every slab; the wave loads its chunk's 64 masks (one per lane), and for each
-// destination r a ballot over "lane's token goes to r" masked to the lanes
-// before this token gives the in-chunk rank, so rows come out in the canonical
-// order with no serial scan.  Lane r ends up holding the row for rank r.  The
-// token's row segment is read once into VGPRs (16-byte loads, coalesced along
-// the row) and stored to every destination with 16-byte non-temporal stores:
-// x is read once per token, the ~8x larger receive region is written once.
+// reproduced): one wave per (token, row segment of VPL*1 KiB).  The wave first
+// issues the 16-byte loads of its x segment (one read of x per token overall),
+// then resolves the token's rows while they are in flight: notify left each
+// token's 64-bit rank mask and, per 64-token chunk, the exclusive row offset
+// inside every slab; the wave loads its chunk's 64 masks (one per lane) and for
+// each destination r a ballot over "lane's token goes to r", masked to the
+// lanes before this token, gives the in-chunk rank -- rows come out in the
+// canonical order without a serial scan, and lane r ends up holding the row
+// for rank r.  The segment is then stored to every destination with 16-byte
+// non-temporal stores.  The tiling (whole rows per wave, or 1 KiB segments
+// with consecutive waves writing consecutive pieces of the same rows) is picked
+// per row width from measurements.
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int kDispatchWaves = 4;
 
 struct DispatchParams {
     const u32x4 *x;
@@ -48,32 +49,45 @@ struct DispatchParams {
     int R, K, E, experts_per_rank, my_rank, cap, S;
 };
 
-template <int VPL, bool EXACT>
-__global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(DispatchParams p) {
+template <int VPL, bool EXACT, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = (int64_t)blockIdx.x * kDispatchWaves + (threadIdx.x >> 6);
+    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
     if (w >= p.T * p.S) return;  // whole wave leaves together
     const int64_t t = w / p.S;
     const int seg = (int)(w - t * p.S);
-    const int64_t q = t / kChunk;
-    const int my = (int)(t - q * kChunk);
     const int R = p.R;
 
-    // ---- row assignment (a3)
+    // ---- the x segment: issued first, consumed last
+    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
+    const u32x4 *src = p.x + t * p.row_units + c0;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+
+    // ---- routing state: chunk masks, slab bases, this token's topk slots
+    const int64_t q = t / kChunk;
+    const int my = (int)(t - q * kChunk);
     const int64_t tok = q * kChunk + lane;
     const uint64_t m = tok < p.T ? p.mask[tok] : 0ull;
+    int base = 0;
+    if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
+    int64_t e = -1;
+    float wt = 0.0f;
+    if (seg == 0 && lane < p.K) {
+        e = p.topk_idx[t * p.K + lane];
+        wt = p.topk_w[t * p.K + lane];
+    }
+
+    // ---- row assignment (a3): lane r gets the row for rank r
     const uint64_t mine = readlane64(m, my);
+    const uint64_t before = (1ull << my) - 1ull;
     int slot = -1;
-    if (mine != 0ull) {
-        int base = 0;
-        if (lane < R && ((mine >> lane) & 1ull))
-            base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
-        const uint64_t before = (1ull << my) - 1ull;
-        for (uint64_t mm = mine; mm != 0ull; mm &= mm - 1ull) {
-            const int r = __builtin_ctzll(mm);
-            const uint64_t b = ballot64((m >> r) & 1ull);
-            if (lane == r) slot = base + __popcll(b & before);
-        }
+    for (uint64_t mm = mine; mm != 0ull; mm &= mm - 1ull) {
+        const int r = __builtin_ctzll(mm);
+        const uint64_t b = ballot64((m >> r) & 1ull);
+        if (lane == r) slot = base + __popcll(b & before);
     }
     const bool over = slot >= p.cap;
     if (over) slot = -1;
@@ -83,14 +97,7 @@ __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(Dispatc
         if (lane < R) p.send_slot[t * R + lane] = slot;
         if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
         // ---- metadata (a4): weights / local ids of the slots living on each destination
-        int64_t e = -1;
-        float wt = 0.0f;
-        int erank = -1;
-        if (lane < p.K) {
-            e = p.topk_idx[t * p.K + lane];
-            wt = p.topk_w[t * p.K + lane];
-            if (e >= 0 && e < p.E) erank = (int)e / p.experts_per_rank;
-        }
+        const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
         for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
             const int r = __builtin_ctzll(dd);
             const int64_t s = readlane32(slot, r);
@@ -102,15 +109,8 @@ __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(Dispatc
             if (lane == 0) reinterpret_cast<int2 *>(p.src_info)[s] = make_int2(p.my_rank, (int)t);
         }
     }
-    if (dests == 0ull) return;
 
-    // ---- row copy (a4): read the segment once, store it to every destination
-    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
-    const u32x4 *src = p.x + t * p.row_units + c0;
-    u32x4 v[VPL];
-#pragma unroll
-    for (int i = 0; i < VPL; ++i)
-        if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+    // ---- row copy (a4): the segment to every destination
     for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
         const int r = __builtin_ctzll(dd);
         const int64_t s = readlane32(slot, r);
@@ -121,13 +121,44 @@ __global__ __launch_bounds__(kDispatchWaves *kWave) void dispatch_kernel(Dispatc
     }
 }
 
-template <int VPL, bool EXACT>
-hipError_t run(const DispatchParams &p, hipStream_t stream) {
+template <int VPL, bool EXACT, int WPB>
+hipError_t run(DispatchParams p, hipStream_t stream) {
+    p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
-    const int64_t blocks = (waves + kDispatchWaves - 1) / kDispatchWaves;
-    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT>), dim3((unsigned)blocks), dim3(kDispatchWaves * kWave), 0,
-                       stream, p);
+    const int64_t blocks = (waves + WPB - 1) / WPB;
+    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
+}
+
+// Tiling: 16-byte units per lane per segment (VPL) and waves per block (WPB).
+// Only the tilings below are instantiated; dispatch_tiling picks one per row width.
+hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, hipStream_t stream) {
+    const bool exact = p.row_units % (vpl * kWave) == 0;
+#define EP_DISPATCH_CASE(V, W) \
+    if (vpl == V && wpb == W) return exact ? run<V, true, W>(p, stream) : run<V, false, W>(p, stream);
+    EP_DISPATCH_CASE(1, 4)
+    EP_DISPATCH_CASE(1, 8)
+    EP_DISPATCH_CASE(2, 4)
+    EP_DISPATCH_CASE(2, 8)
+    EP_DISPATCH_CASE(4, 4)
+    EP_DISPATCH_CASE(7, 4)
+    EP_DISPATCH_CASE(8, 4)
+    EP_DISPATCH_CASE(14, 4)
+#undef EP_DISPATCH_CASE
+    return hipErrorInvalidValue;
+}
+
+// Measured on MI355X (prefill / skew / large workloads): one wave per whole
+// 14 KiB row is best when the row is 7168 bf16 wide; other widths use 1 KiB
+// segments with 8 waves per block.
+void dispatch_tiling(int64_t row_units, int *vpl, int *wpb) {
+    if (row_units % (14 * kWave) == 0 && row_units / (14 * kWave) == 1) {
+        *vpl = 14;
+        *wpb = 4;
+    } else {
+        *vpl = 1;
+        *wpb = 8;
+    }
 }
 
 }  // namespace
@@ -137,7 +168,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *t
                            int64_t *recv_idx, int32_t *src_info, int32_t *send_slot, int32_t *dev_status,
                            hipStream_t stream) {
     if (s.num_tokens == 0) return hipSuccess;
-    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_channels);
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
     DispatchParams p;
     p.x = reinterpret_cast<const u32x4 *>(x);
     p.topk_idx = topk_idx;
@@ -159,27 +190,10 @@ hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *t
     p.experts_per_rank = s.num_experts / s.num_ranks;
     p.my_rank = s.my_rank;
     p.cap = cap;
-    // per-lane 16-byte units held in registers: a whole number of wave-wide
-    // passes when the row allows it
-    const int64_t U = p.row_units;
-    if (U % (14 * kWave) == 0) {
-        p.S = (int)(U / (14 * kWave));
-        return run<14, true>(p, stream);
-    }
-    if (U % (8 * kWave) == 0) {
-        p.S = (int)(U / (8 * kWave));
-        return run<8, true>(p, stream);
-    }
-    if (U % (4 * kWave) == 0) {
-        p.S = (int)(U / (4 * kWave));
-        return run<4, true>(p, stream);
-    }
-    if (U % kWave == 0) {
-        p.S = (int)(U / kWave);
-        return run<1, true>(p, stream);
-    }
-    p.S = (int)((U + 4 * kWave - 1) / (4 * kWave));
-    return run<4, false>(p, stream);
+    p.S = 1;
+    int vpl, wpb;
+    dispatch_tiling(p.row_units, &vpl, &wpb);
+    return run_tiled(p, vpl, wpb, stream);
 }
 
 }  // namespace ep

@@ -8,46 +8,40 @@
 // ranks receives it -- follows the internode.cu notes, notify_dispatch sm1-x
 // stage 1, which tests a node's 8 bytes of is_token_in_rank at once.
 //
-// Design: one thread per token builds the token's 64-bit rank mask (R <= 64,
-// so rank r is bit r).  Per-rank and per-node counts come from wave64 ballots
-// (lane r keeps the popcount for rank r), experts go to an LDS histogram, and
-// each block adds its partial counts to the outputs with one atomic per
-// non-zero entry.  Integer atomics commute, so the result is deterministic.
-// The block's is_token_in_rank rows are staged as masks in LDS and written
-// out as a contiguous byte range with 16/4/1-byte stores.
+// Design: one launch.  One thread per token builds the token's 64-bit rank
+// mask (R <= 64, so rank r is bit r).  Per-rank and per-node counts come from
+// wave64 ballots (lane r keeps the popcount for rank r), experts go to an LDS
+// histogram, and each block adds its non-zero partial counts into running
+// counters in the workspace.  The block's is_token_in_rank rows are staged as
+// masks in LDS and written out as one contiguous byte range with 16/4/1-byte
+// stores.  The last block to finish moves the running counters into the
+// outputs and zeroes them for the next call, so no separate zero-fill launch
+// is needed.  Integer atomics commute: the result is deterministic.
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
 constexpr int kLayoutThreads = 256;
-constexpr int kMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E counts in global memory
-
-__global__ void layout_zero_kernel(int32_t *per_rank, int R, int32_t *per_node, int nodes, int32_t *per_expert,
-                                   int E) {
-    const int n = R + nodes + E;
-    for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += blockDim.x * gridDim.x) {
-        if (i < R)
-            per_rank[i] = 0;
-        else if (i < R + nodes)
-            per_node[i - R] = 0;
-        else
-            per_expert[i - R - nodes] = 0;
-    }
-}
+constexpr int kMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E counts in the workspace directly
 
 // byte i of the result = bit i of the low 4 bits of `nib`
 __device__ __forceinline__ uint32_t spread4(uint32_t nib) {
     return (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
 }
 
-__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *__restrict__ topk_idx, int T, int K,
-                                                                int E, int R, int nodes, int store_unit,
-                                                                int32_t *__restrict__ per_rank,
-                                                                int32_t *__restrict__ per_node,
-                                                                int32_t *__restrict__ per_expert,
-                                                                uint8_t *__restrict__ in_rank,
-                                                                int32_t *__restrict__ dev_status) {
+struct LayoutParams {
+    const int64_t *topk_idx;
+    int32_t *per_rank, *per_node, *per_expert;
+    uint8_t *in_rank;
+    int32_t *acc;  // [R + nodes + E] running counts, zero between calls
+    uint32_t *ticket;
+    int32_t *dev_status;
+    int64_t T;
+    int K, E, R, nodes, store_unit;
+};
+
+__global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) {
     __shared__ int32_t s_rank[kMaxRanks];
     __shared__ int32_t s_node[kMaxRanks / kRanksPerNode];
     __shared__ uint64_t s_mask[kLayoutThreads];
@@ -55,7 +49,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
+    const int R = p.R, E = p.E, K = p.K, nodes = p.nodes;
     const bool lds_experts = E <= kMaxLdsExperts;
+    int32_t *acc_rank = p.acc, *acc_node = p.acc + R, *acc_expert = p.acc + R + nodes;
     for (int i = tid; i < R; i += kLayoutThreads) s_rank[i] = 0;
     for (int i = tid; i < nodes; i += kLayoutThreads) s_node[i] = 0;
     if (lds_experts)
@@ -67,8 +63,8 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
     const int experts_per_rank = E / R;
     uint64_t mask = 0;
     int bad = 0;
-    if (t < T) {
-        const int64_t *row = topk_idx + t * K;
+    if (t < p.T) {
+        const int64_t *row = p.topk_idx + t * K;
         for (int j = 0; j < K; ++j) {
             const int64_t e = row[j];
             if (e == -1) continue;
@@ -80,7 +76,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
             if (lds_experts)
                 atomicAdd(&s_expert[ei], 1);
             else
-                atomicAdd(&per_expert[ei], 1);
+                atomicAdd(&acc_expert[ei], 1);
             mask |= 1ull << (ei / experts_per_rank);
         }
     }
@@ -100,14 +96,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
         node_cnt = (lane == n) ? c : node_cnt;
     }
     if (lane < nodes && node_cnt != 0) atomicAdd(&s_node[lane], node_cnt);
-    if (ballot64(bad != 0) != 0 && lane == 0) flag(dev_status, EP_DEV_BAD_TOPK_IDX);
+    if (ballot64(bad != 0) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_TOPK_IDX);
     __syncthreads();
 
     // is_token_in_rank rows of this block: one contiguous range of nt*R bytes
-    const int nt = (int)((T - t0) < kLayoutThreads ? (T - t0) : kLayoutThreads);
+    const int64_t left = p.T - t0;
+    const int nt = (int)(left < kLayoutThreads ? (left > 0 ? left : 0) : kLayoutThreads);
     const int64_t nbytes = (int64_t)nt * R;
-    uint8_t *dst = in_rank + t0 * R;
-    if (store_unit == 16) {  // R % 16 == 0, 16-byte aligned
+    uint8_t *dst = p.in_rank + t0 * R;
+    if (p.store_unit == 16) {  // R % 16 == 0, 16-byte aligned
         for (int64_t u = tid; u < nbytes / 16; u += kLayoutThreads) {
             const int64_t b = u * 16;
             const uint64_t m = s_mask[b / R] >> (b % R);
@@ -118,7 +115,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
             v.w = spread4((uint32_t)(m >> 12) & 0xfu);
             reinterpret_cast<uint4 *>(dst)[u] = v;
         }
-    } else if (store_unit == 4) {  // R % 4 == 0, 4-byte aligned
+    } else if (p.store_unit == 4) {  // R % 4 == 0, 4-byte aligned
         for (int64_t u = tid; u < nbytes / 4; u += kLayoutThreads) {
             const int64_t b = u * 4;
             reinterpret_cast<uint32_t *>(dst)[u] = spread4((uint32_t)(s_mask[b / R] >> (b % R)) & 0xfu);
@@ -128,37 +125,56 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(const int64_t *_
             dst[b] = (uint8_t)((s_mask[b / R] >> (b % R)) & 1ull);
     }
 
+    // this block's partial counts into the running counters
     for (int i = tid; i < R; i += kLayoutThreads)
-        if (s_rank[i] != 0) atomicAdd(&per_rank[i], s_rank[i]);
+        if (s_rank[i] != 0) atomicAdd(&acc_rank[i], s_rank[i]);
     for (int i = tid; i < nodes; i += kLayoutThreads)
-        if (s_node[i] != 0) atomicAdd(&per_node[i], s_node[i]);
+        if (s_node[i] != 0) atomicAdd(&acc_node[i], s_node[i]);
     if (lds_experts)
         for (int i = tid; i < E; i += kLayoutThreads)
-            if (s_expert[i] != 0) atomicAdd(&per_expert[i], s_expert[i]);
+            if (s_expert[i] != 0) atomicAdd(&acc_expert[i], s_expert[i]);
+
+    if (!elect_last_block(p.ticket)) return;
+    // last block: publish the totals and leave the counters at zero
+    for (int i = tid; i < R + nodes + E; i += kLayoutThreads) {
+        const int32_t v = atomicExch(&p.acc[i], 0);
+        if (i < R)
+            p.per_rank[i] = v;
+        else if (i < R + nodes)
+            p.per_node[i - R] = v;
+        else
+            p.per_expert[i - R - nodes] = v;
+    }
 }
 
 }  // namespace
 
 hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
-                         int32_t *per_expert, uint8_t *in_rank, int32_t *dev_status, hipStream_t stream) {
-    const int R = s.num_ranks, E = s.num_experts, nodes = num_nodes(R);
-    const int64_t T = s.num_tokens;
-    const int nzero = R + nodes + E;
-    const int zblocks = (nzero + 255) / 256 < 64 ? (nzero + 255) / 256 : 64;
-    hipLaunchKernelGGL(layout_zero_kernel, dim3(zblocks), dim3(256), 0, stream, per_rank, R, per_node, nodes,
-                       per_expert, E);
-    if (T > 0) {
-        int unit = 1;
-        if (R % 16 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 16 == 0)
-            unit = 16;
-        else if (R % 4 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 4 == 0)
-            unit = 4;
-        const size_t lds = E <= kMaxLdsExperts ? sizeof(int32_t) * (size_t)E : 0;
-        const int64_t blocks = (T + kLayoutThreads - 1) / kLayoutThreads;
-        hipLaunchKernelGGL(layout_kernel, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, topk_idx,
-                           (int)T, s.num_topk, E, R, nodes, unit, per_rank, per_node, per_expert, in_rank,
-                           dev_status);
-    }
+                         int32_t *per_expert, uint8_t *in_rank, char *ws, int32_t *dev_status, hipStream_t stream) {
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
+    LayoutParams p;
+    p.topk_idx = topk_idx;
+    p.per_rank = per_rank;
+    p.per_node = per_node;
+    p.per_expert = per_expert;
+    p.in_rank = in_rank;
+    p.acc = reinterpret_cast<int32_t *>(ws + w.acc);
+    p.ticket = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketLayout;
+    p.dev_status = dev_status;
+    p.T = s.num_tokens;
+    p.K = s.num_topk;
+    p.E = s.num_experts;
+    p.R = s.num_ranks;
+    p.nodes = num_nodes(p.R);
+    p.store_unit = 1;
+    if (p.R % 16 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 16 == 0)
+        p.store_unit = 16;
+    else if (p.R % 4 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 4 == 0)
+        p.store_unit = 4;
+    const size_t lds = p.E <= kMaxLdsExperts ? sizeof(int32_t) * (size_t)p.E : 0;
+    // one block even for t = 0: the last (only) block publishes the zero counts
+    const int64_t blocks = p.T > 0 ? (p.T + kLayoutThreads - 1) / kLayoutThreads : 1;
+    hipLaunchKernelGGL(layout_kernel, dim3((unsigned)blocks), dim3(kLayoutThreads), lds, stream, p);
     return hipGetLastError();
 }
 

@@ -12,25 +12,28 @@
 //   num_recv_tokens                  = last entry of recv_gbl_rank_prefix_sum
 // Channel c owns tokens [c*Tc, min((c+1)*Tc, t)), Tc = ceil(t / C).
 //
-// Design (not the pages' one-SM-per-channel loop): the token axis is cut into
-// 64-token chunks, one chunk per wave and one token per lane.
-//   count kernel (grid over chunks): lane j turns its token's is_token_in_rank
-//     row into a 64-bit rank mask, stores it for dispatch, and R ballots give
-//     every (chunk, rank) count (lane r keeps rank r's ballot).  For each channel
-//     whose end falls inside the chunk it also stores the count of the chunk's
-//     tokens before that end.  Every value has one writer: no atomics.
-//   scan kernel (one workgroup): an LDS-staged two-level scan over the chunks
-//     turns the counts into exclusive row offsets inside each rank's slab (what
-//     dispatch needs); a channel's prefix is then the offset of the chunk holding
-//     its end plus the partial count stored for it.  The receive prefixes over
-//     ranks and nodes, the aligned expert counts and N follow.
+// Design (not the pages' one-SM-per-channel loop): one launch.  The token axis
+// is cut into 64-token chunks, one chunk per wave and one token per lane.
+//   Every wave turns its lanes' is_token_in_rank rows into 64-bit rank masks
+//   (stored for dispatch), and R ballots give each (chunk, rank) count (lane r
+//   keeps rank r's ballot).  For each channel whose end falls inside the chunk
+//   it also stores the count of the chunk's tokens before that end.  Every
+//   value has one writer: no atomics.
+//   The last block to finish then scans: it brings the counts, the partials
+//   and the per-rank totals into LDS in one round trip (or works in the
+//   workspace when they do not fit), one wave per column (rank or node), each
+//   lane summing a run of chunks and a wave-wide shuffle scan combining the
+//   runs, which turns the counts into exclusive row offsets inside each rank's
+//   slab (what dispatch needs).  A channel's prefix is the offset of the chunk
+//   holding its end plus the partial count stored for it.  The receive
+//   prefixes over ranks and nodes are one wave scan each.
 #include "ep_internal.h"
 
 namespace ep {
 namespace {
 
-constexpr int kCountWaves = 4;
-constexpr int kScanThreads = 1024;
+constexpr int kNotifyWaves = 16;
+constexpr int kNotifyThreads = kNotifyWaves * kWave;
 
 struct NotifyParams {
     const uint8_t *in_rank;
@@ -38,6 +41,7 @@ struct NotifyParams {
     int32_t *gbl, *rdma, *recv_gbl, *recv_rdma, *recv_per_expert, *num_recv;
     uint64_t *mask;
     int32_t *rank_off, *node_off, *rank_part, *node_part;
+    uint32_t *ticket;
     int32_t *dev_status;
     int64_t T, Tc;
     int R, C, E, nodes, align, load_unit;
@@ -66,15 +70,10 @@ __device__ __forceinline__ uint64_t load_rank_mask(const uint8_t *row, int R, in
     return m;
 }
 
-__global__ __launch_bounds__(kCountWaves *kWave) void notify_count_kernel(NotifyParams p) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t q = (int64_t)blockIdx.x * kCountWaves + (threadIdx.x >> 6);
-    const int64_t Q = num_chunks(p.T);
-    if (q >= Q) return;  // whole wave leaves together
+__device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
     const int64_t first = q * kChunk;
     const int64_t tok = first + lane;
     const int R = p.R, nodes = p.nodes;
-
     uint64_t m = 0;
     if (tok < p.T) {
         m = load_rank_mask(p.in_rank + tok * R, R, p.load_unit);
@@ -93,71 +92,161 @@ __global__ __launch_bounds__(kCountWaves *kWave) void notify_count_kernel(Notify
     }
     if (lane < R) p.rank_off[q * R + lane] = __popcll(my_bits);
     if (lane < nodes) p.node_off[q * nodes + lane] = __popcll(my_node_bits);
-
     // channels whose end lies strictly inside this chunk
-    if (p.Tc > 0) {
-        for (int64_t c = first / p.Tc; c < p.C; ++c) {
-            const int64_t end = (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
-            if (end >= first + kChunk) break;
-            if (end <= first) continue;
-            const uint64_t below = (1ull << (end - first)) - 1ull;
-            if (lane < R) p.rank_part[c * R + lane] = __popcll(my_bits & below);
-            if (lane < nodes) p.node_part[c * nodes + lane] = __popcll(my_node_bits & below);
-        }
+    for (int64_t c = first / p.Tc; c < p.C; ++c) {
+        const int64_t end = (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
+        if (end >= first + kChunk) break;
+        if (end <= first) continue;
+        const uint64_t below = (1ull << (end - first)) - 1ull;
+        if (lane < R) p.rank_part[c * R + lane] = __popcll(my_bits & below);
+        if (lane < nodes) p.node_part[c * nodes + lane] = __popcll(my_node_bits & below);
     }
 }
 
-__global__ __launch_bounds__(kScanThreads) void notify_scan_kernel(NotifyParams p) {
-    __shared__ int32_t part[kScanThreads];
-    const int tid = threadIdx.x;
+// One wave scans one column of the [Q][stride] count matrix into exclusive
+// offsets, and writes the total into row Q.  Returns the total.
+__device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
+    const int64_t per = (Q + kWave - 1) / kWave;
+    const int64_t b = lane * per;
+    const int64_t e = (b + per) < Q ? (b + per) : Q;
+    int32_t s = 0;
+    for (int64_t row = b; row < e; ++row) s += col[row * stride];
+    const int32_t incl = wave_inclusive_scan(s);
+    int32_t run = incl - s;
+    for (int64_t row = b; row < e; ++row) {
+        const int32_t v = col[row * stride];
+        col[row * stride] = run;
+        run += v;
+    }
+    const int32_t total = readlane32(incl, kWave - 1);
+    if (lane == 0) col[Q * stride] = total;
+    return total;
+}
+
+// LDS capacity of the last block for the [Q][NC] counts plus the [C][NC]
+// partials; larger problems scan in global memory instead.
+constexpr int kScanLds = 12288;
+
+__device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c) {
+    return (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
+}
+
+// Last block, small problems: the counts, the partials and the per-rank / per-node
+// totals come into LDS in one round trip, are scanned there, and every output is
+// written from LDS.
+__device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave) {
+    __shared__ int32_t s_cnt[kScanLds];  // [Q+1][NC], then [C][NC] partials behind it
+    __shared__ int32_t s_tot[kMaxRanks + kMaxRanks / kRanksPerNode];
     const int R = p.R, nodes = p.nodes, NC = R + nodes;
     const int64_t Q = num_chunks(p.T);
-    const int G = kScanThreads / NC;
-    const int64_t per = (Q + G - 1) / G;
-    const int g = tid / NC, col = tid % NC;
-    int32_t *colp = col < R ? p.rank_off + col : p.node_off + (col - R);
-    const int stride = col < R ? R : nodes;
+    int32_t *s_part = s_cnt + (Q + 1) * NC;
 
-    // pass 1: each group sums its run of chunks for its column
-    if (g < G) {
-        int32_t s = 0;
-        const int64_t b = g * per, e = (b + per) < Q ? (b + per) : Q;
-        for (int64_t row = b; row < e; ++row) s += colp[row * stride];
-        part[g * NC + col] = s;
+    // ---- one round trip of loads
+    for (int64_t i = tid; i < Q * NC; i += kNotifyThreads) {
+        const int64_t q = i / NC;
+        const int col = (int)(i - q * NC);
+        s_cnt[i] = col < R ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)];
     }
-    __syncthreads();
-    // pass 2: exclusive scan over groups, one thread per column; row Q = total
-    if (tid < NC) {
-        int32_t run = 0;
-        for (int gg = 0; gg < G; ++gg) {
-            const int32_t v = part[gg * NC + tid];
-            part[gg * NC + tid] = run;
-            run += v;
-        }
-        int32_t *cp = tid < R ? p.rank_off + tid : p.node_off + (tid - R);
-        cp[Q * (tid < R ? R : nodes)] = run;
-        const int32_t want = tid < R ? p.per_rank[tid] : p.per_node[tid - R];
-        if (run != want) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+    for (int64_t i = tid; i < (int64_t)p.C * NC; i += kNotifyThreads) {
+        const int64_t c = i / NC;
+        const int col = (int)(i - c * NC);
+        const int64_t end = channel_end(p, c);
+        s_part[i] = (end % kChunk) == 0 ? 0 : (col < R ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)]);
     }
-    __syncthreads();
-    // pass 3: rewrite each group's run as exclusive offsets
-    if (g < G) {
-        int32_t run = part[g * NC + col];
-        const int64_t b = g * per, e = (b + per) < Q ? (b + per) : Q;
-        for (int64_t row = b; row < e; ++row) {
-            const int32_t v = colp[row * stride];
-            colp[row * stride] = run;
-            run += v;
-        }
-    }
+    const int32_t per_rank = lane < R ? p.per_rank[lane] : 0;
+    const int32_t per_node = lane < nodes ? p.per_node[lane] : 0;
     __syncthreads();
 
-    // channel prefix matrices: offset of the chunk holding the channel's end
-    // plus the partial count inside that chunk
-    for (int64_t i = tid; i < (int64_t)NC * p.C; i += kScanThreads) {
+    // ---- scans: one wave per column, lanes over runs of chunks
+    const int64_t per = (Q + kWave - 1) / kWave;
+    for (int col = wave; col < NC; col += kNotifyWaves) {
+        const int64_t b = lane * per;
+        const int64_t e = (b + per) < Q ? (b + per) : Q;
+        int32_t sum = 0;
+        for (int64_t q = b; q < e; ++q) sum += s_cnt[q * NC + col];
+        const int32_t incl = wave_inclusive_scan(sum);
+        int32_t run = incl - sum;
+        for (int64_t q = b; q < e; ++q) {
+            const int32_t v = s_cnt[q * NC + col];
+            s_cnt[q * NC + col] = run;
+            run += v;
+        }
+        const int32_t total = readlane32(incl, kWave - 1);
+        if (lane == 0) {
+            s_cnt[Q * NC + col] = total;
+            s_tot[col] = total;
+        }
+    }
+    // receive prefix sums over destination ranks and nodes (inclusive)
+    if (wave == kNotifyWaves - 1) {
+        const int32_t incl = wave_inclusive_scan(per_rank);
+        if (lane < R) p.recv_gbl[lane] = incl;
+        if (lane == R - 1) p.num_recv[0] = incl;
+    } else if (wave == kNotifyWaves - 2) {
+        const int32_t incl = wave_inclusive_scan(per_node);
+        if (lane < nodes) p.recv_rdma[lane] = incl;
+    }
+    __syncthreads();
+
+    // ---- outputs
+    if (wave == kNotifyWaves - 3) {
+        const bool bad = (lane < R && s_tot[lane] != per_rank) || (lane < nodes && s_tot[R + lane] != per_node);
+        if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+    }
+    for (int64_t i = tid; i < (Q + 1) * NC; i += kNotifyThreads) {
+        const int64_t q = i / NC;
+        const int col = (int)(i - q * NC);
+        if (col < R)
+            p.rank_off[q * R + col] = s_cnt[i];
+        else
+            p.node_off[q * nodes + (col - R)] = s_cnt[i];
+    }
+    for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
+        const int col = (int)(i / p.C);
+        const int64_t c = i - (int64_t)col * p.C;
+        const int64_t qe = channel_end(p, c) / kChunk;
+        const int32_t v = s_cnt[qe * NC + col] + s_part[c * NC + col];
+        if (col < R)
+            p.gbl[(int64_t)col * p.C + c] = v;
+        else
+            p.rdma[(int64_t)(col - R) * p.C + c] = v;
+    }
+    for (int e = tid; e < p.E; e += kNotifyThreads) {
+        const int64_t n = p.per_expert[e];
+        p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
+    }
+}
+
+// Last block, large problems: the same steps on the workspace in global memory.
+__device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int wave) {
+    const int R = p.R, nodes = p.nodes, NC = R + nodes;
+    const int64_t Q = num_chunks(p.T);
+    for (int col = wave; col < NC; col += kNotifyWaves) {
+        const bool is_rank = col < R;
+        int32_t *cp = is_rank ? p.rank_off + col : p.node_off + (col - R);
+        const int32_t total = scan_column(cp, is_rank ? R : nodes, Q, lane);
+        const int32_t want = is_rank ? p.per_rank[col] : p.per_node[col - R];
+        if (lane == 0 && total != want) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+    }
+    if (wave == kNotifyWaves - 1) {
+        const int32_t v = lane < R ? p.per_rank[lane] : 0;
+        const int32_t incl = wave_inclusive_scan(v);
+        if (lane < R) p.recv_gbl[lane] = incl;
+        if (lane == R - 1) p.num_recv[0] = incl;
+    } else if (wave == kNotifyWaves - 2) {
+        const int32_t v = lane < nodes ? p.per_node[lane] : 0;
+        const int32_t incl = wave_inclusive_scan(v);
+        if (lane < nodes) p.recv_rdma[lane] = incl;
+    }
+    for (int e = tid; e < p.E; e += kNotifyThreads) {
+        const int64_t n = p.per_expert[e];
+        p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
+    }
+    __syncthreads();  // scanned offsets visible to the whole block
+    for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
         const int cc = (int)(i / p.C);
         const int64_t c = i % p.C;
-        const int64_t end = (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
+        const int64_t end = channel_end(p, c);
         const int64_t qe = end / kChunk;
         const bool inside = (end % kChunk) != 0;
         if (cc < R) {
@@ -167,25 +256,23 @@ __global__ __launch_bounds__(kScanThreads) void notify_scan_kernel(NotifyParams 
             p.rdma[n * (int64_t)p.C + c] = p.node_off[qe * nodes + n] + (inside ? p.node_part[c * nodes + n] : 0);
         }
     }
-    // receive prefix sums over destination ranks / nodes (inclusive)
-    if (tid == 0) {
-        int32_t run = 0;
-        for (int r = 0; r < R; ++r) {
-            run += p.per_rank[r];
-            p.recv_gbl[r] = run;
-        }
-        p.num_recv[0] = run;
-    } else if (tid == kWave) {
-        int32_t run = 0;
-        for (int n = 0; n < nodes; ++n) {
-            run += p.per_node[n];
-            p.recv_rdma[n] = run;
-        }
-    }
-    for (int e = tid; e < p.E; e += kScanThreads) {
-        const int64_t n = p.per_expert[e];
-        p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
-    }
+}
+
+__global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) {
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int64_t Q = num_chunks(p.T);
+
+    const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
+    if (q < Q) count_chunk(p, q, lane);
+
+    if (!elect_last_block(p.ticket)) return;
+    const int64_t NC = p.R + p.nodes;
+    if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
+        finish_in_lds(p, tid, lane, wave);
+    else
+        finish_in_global(p, tid, lane, wave);
 }
 
 }  // namespace
@@ -194,7 +281,7 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
                          const int32_t *per_node, const int32_t *per_expert, int32_t *gbl, int32_t *rdma,
                          int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,
                          char *ws, int32_t *dev_status, hipStream_t stream) {
-    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_channels);
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
     NotifyParams p;
     p.in_rank = in_rank;
     p.per_rank = per_rank;
@@ -211,6 +298,7 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
     p.node_off = reinterpret_cast<int32_t *>(ws + w.node_off);
     p.rank_part = reinterpret_cast<int32_t *>(ws + w.rank_part);
     p.node_part = reinterpret_cast<int32_t *>(ws + w.node_part);
+    p.ticket = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketNotify;
     p.dev_status = dev_status;
     p.T = s.num_tokens;
     p.C = s.num_channels;
@@ -223,11 +311,9 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
     p.load_unit = (p.R % 16 == 0 && a % 16 == 0) ? 16 : (p.R % 8 == 0 && a % 8 == 0) ? 8 : 1;
 
     const int64_t Q = num_chunks(p.T);
-    if (Q > 0) {
-        const int64_t blocks = (Q + kCountWaves - 1) / kCountWaves;
-        hipLaunchKernelGGL(notify_count_kernel, dim3((unsigned)blocks), dim3(kCountWaves * kWave), 0, stream, p);
-    }
-    hipLaunchKernelGGL(notify_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
+    // at least one block: the last (only) block also handles t = 0
+    const int64_t blocks = Q > 0 ? (Q + kNotifyWaves - 1) / kNotifyWaves : 1;
+    hipLaunchKernelGGL(notify_kernel, dim3((unsigned)blocks), dim3(kNotifyThreads), 0, stream, p);
     return hipGetLastError();
 }
 

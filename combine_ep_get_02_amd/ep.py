@@ -48,7 +48,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     if not os.path.exists(path):
         raise RuntimeError(f"libep.so not built at {path}; run `python -m combine_ep_get_02_amd.build`")
     lib = ctypes.CDLL(path)
-    lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P]
+    lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
     lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
@@ -98,10 +98,11 @@ def ep_workspace_bytes(shape: ep_shape_t) -> int:
 
 
 def ep_get_layout(shape, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert,
-                  is_token_in_rank, dev_status=None, stream=None) -> None:
+                  is_token_in_rank, workspace, dev_status=None, stream=None) -> None:
     _check(load().ep_get_layout(ctypes.byref(shape), _ptr(topk_idx), _ptr(num_tokens_per_rank),
                                 _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
-                                _ptr(is_token_in_rank), _ptr(dev_status), _stream(stream)), "ep_get_layout")
+                                _ptr(is_token_in_rank), _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                _ptr(dev_status), _stream(stream)), "ep_get_layout")
 
 
 def ep_notify(shape, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert,
@@ -176,7 +177,7 @@ def allocate(shape: ep_shape_t, capacity: int, device="cuda", with_recv_idx: boo
         in_rank=torch.empty((T, R), dtype=torch.uint8, device=device),
         gbl=torch.empty((R, C), **i32), rdma=torch.empty((nodes, C), **i32), recv_gbl=torch.empty(R, **i32),
         recv_rdma=torch.empty(nodes, **i32), recv_per_expert=torch.empty(E, **i32), num_recv=torch.empty(1, **i32),
-        workspace=torch.empty(max(ep_workspace_bytes(shape), 256), dtype=torch.uint8, device=device),
+        workspace=torch.zeros(max(ep_workspace_bytes(shape), 256), dtype=torch.uint8, device=device),
         recv_x=torch.empty((cap, H), dtype=torch.bfloat16, device=device),
         recv_w=torch.empty((cap, K), dtype=torch.float32, device=device),
         recv_idx=torch.empty((cap, K), dtype=torch.int64, device=device) if with_recv_idx else None,
@@ -187,7 +188,8 @@ def allocate(shape: ep_shape_t, capacity: int, device="cuda", with_recv_idx: boo
 
 
 def run_layout(b: Buffers, topk_idx, stream=None) -> None:
-    ep_get_layout(b.shape, topk_idx, b.per_rank, b.per_node, b.per_expert, b.in_rank, b.dev_status, stream)
+    ep_get_layout(b.shape, topk_idx, b.per_rank, b.per_node, b.per_expert, b.in_rank, b.workspace, b.dev_status,
+                  stream)
 
 
 def run_notify(b: Buffers, read_back: bool = False, stream=None) -> int | None:

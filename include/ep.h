@@ -85,11 +85,14 @@ typedef struct {
  *                                              node n (node = rank / 8, nodes = max(1, R / 8))
  *      num_tokens_per_expert    [E]     int32: valid topk slots naming expert e
  *      is_token_in_rank         [t][R]  uint8 (0/1, row-major)
+ * workspace: see ep_workspace_bytes (its control words must be zero before the first
+ *            call; every call leaves them zero).
  * dev_status (nullable): EP_DEV_BAD_TOPK_IDX.
  */
 ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
                           int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
-                          uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream);
+                          uint8_t *is_token_in_rank, void *workspace, size_t workspace_bytes, int32_t *dev_status,
+                          hipStream_t stream);
 
 /*
  * Stage 2, notify.  [mscclpp ht_runtime.cc, internodeNotifyDispatch; internode.cu notes,
@@ -107,9 +110,8 @@ ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t 
  *      num_recv_tokens            [1]        int32: N = total receive rows (device)
  *      num_recv_tokens_host  (host, nullable): when non-NULL the call waits for the stream
  *                                              and stores N there.
- *      workspace: ep_workspace_bytes(s) bytes of device memory, written here and read by
- *                 ep_dispatch (per-token rank masks and per-64-token-chunk row offsets).
- *                 Its contents are opaque; it needs no initialisation.
+ *      workspace: the same workspace as ep_get_layout; notify writes the per-token rank
+ *                 masks and per-64-token-chunk row offsets that ep_dispatch reads.
  * dev_status (nullable): EP_DEV_COUNT_MISMATCH.
  */
 ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
@@ -160,7 +162,11 @@ ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_top
                        int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
                        hipStream_t stream);
 
-/* Bytes of workspace ep_notify / ep_dispatch need for this shape (0 if s is invalid). */
+/* Bytes of workspace ep_get_layout / ep_notify / ep_dispatch need for this shape (0 if s
+ * is invalid).  The workspace is device memory, 256-byte aligned, owned by the caller, and
+ * must be zero-filled before its first use (hipMemset once at allocation): its completion
+ * counters and running counts must start at zero, and every call leaves them at zero
+ * again.  Calls that run concurrently must not share a workspace. */
 size_t ep_workspace_bytes(const ep_shape_t *s);
 
 /* Static text for a status code. */

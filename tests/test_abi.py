@@ -51,8 +51,9 @@ def test_status_strings(ep):
 def test_workspace_bytes(ep):
     s = ep.make_shape(4096, 7168, 8, 256, 64, 24)
     n = ep.ep_workspace_bytes(s)
-    # masks (8 B/token) + 65 x 64 chunk offsets + 65 x 8 + 24 x 64 + 24 x 8, each 256-aligned
-    assert n == 32768 + 16640 + 2304 + 6144 + 768
+    # tickets 256 + running counts (64+8+256) + masks (8 B/token) + 65 x 64 chunk offsets
+    # + 65 x 8 + 24 x 64 + 24 x 8, each 256-aligned
+    assert n == 256 + 1536 + 32768 + 16640 + 2304 + 6144 + 768
     assert ep.ep_workspace_bytes(ep.make_shape(4096, 7168, 8, 255, 64, 24)) == 0  # E % R != 0
 
 
@@ -82,7 +83,7 @@ def _call_all(ep, s):
     lib = ep.load()
     p = ctypes.c_void_p(256)  # never dereferenced: every call must fail its host checks first
     codes = [
-        lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, None, None),
+        lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, p, 1 << 30, None, None),
         lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
         lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None, None),
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
@@ -105,7 +106,8 @@ def test_null_and_misaligned_pointers_rejected(ep):
     s = _shape(ep)
     p = ctypes.c_void_p(256)
     odd = ctypes.c_void_p(264)
-    assert lib.ep_get_layout(ctypes.byref(s), None, p, p, p, p, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.byref(s), None, p, p, p, p, p, 1 << 30, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, p, 16, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, None, 1 << 30, None,
                          None) == ep.EP_ERR_INVALID_ARG  # no workspace
     assert lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 16, None,
@@ -116,7 +118,7 @@ def test_null_and_misaligned_pointers_rejected(ep):
                            None) == ep.EP_ERR_INVALID_ARG  # negative capacity
     assert lib.ep_combine(ctypes.byref(s), p, p, p, 10, odd, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(s), p, p, None, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_get_layout(None, p, p, p, p, p, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_get_layout(None, p, p, p, p, p, p, 1 << 30, None, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_empty_dispatch_and_combine_enqueue_nothing(ep):
