@@ -49,6 +49,36 @@ def layout_notify_bytes(T, K, R, E, C) -> int:
     return T * K * 8 + T * R + 4 * (R + nodes + E) + T * R + 4 * (R + nodes + E) + 4 * (R + nodes) * (C + 1) + 4 * E
 
 
+PROFILE = os.path.join(ROOT, "profiles", "ep_kernels_prefill_hbm_bytes.txt")
+KERNEL_SOURCES = {"dispatch_kernel": ["ep_dispatch.hip", "ep_internal.h"],
+                  "combine_kernel": ["ep_combine.hip", "ep_internal.h"]}
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
+    size), or None when that summary does not cover this workload or the
+    kernel's sources changed since the counters were taken."""
+    import hashlib
+
+    if workload != "prefill" or not os.path.exists(PROFILE):
+        return None
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "combine_ep_get_02_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    fields = {}
+    with open(PROFILE) as fh:
+        for line in fh:
+            parts = line.split()
+            if len(parts) == 3 and parts[0] in ("traffic_bytes", "source_sha256"):
+                fields[(parts[0], parts[1])] = parts[2]
+    if fields.get(("source_sha256", kernel)) != h.hexdigest()[:16]:
+        return None
+    v = fields.get(("traffic_bytes", kernel))
+    return int(v) if v is not None else None
+
+
 def cpu_baseline(d, wl, n_recv, budget_s: float = 12.0) -> dict:
     """The oracle (single-threaded C) on the same workload, full steps repeated
     until about budget_s of CPU time has passed."""
@@ -222,7 +252,8 @@ def main() -> int:
         "identity_check": ok,
         "cold": cold,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(dom, wl.name), "algorithmic_bytes": dom_bytes},
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, wl, n_recv)
