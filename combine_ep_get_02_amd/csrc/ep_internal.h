@@ -91,15 +91,37 @@ __device__ __forceinline__ float readlanef(float v, int src) {
     return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), src));
 }
 
-// Inclusive prefix sum over the 64 lanes of a wave.
+// Inclusive prefix sum over the 64 lanes of a wave with DPP moves (no LDS):
+// shifts by 1, 2, 4, 8 inside each row of 16 lanes (lanes whose source falls
+// outside the row read 0), then lane 15 of each row is broadcast into the next
+// row (rows 1 and 3) and lane 31 into rows 2 and 3.
 __device__ __forceinline__ int wave_inclusive_scan(int v) {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int u = __shfl_up(v, d, kWave);
-        if (lane >= d) v += u;
-    }
+    v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, true);  // row_shr:1
+    v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, true);  // row_shr:2
+    v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, true);  // row_shr:4
+    v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, true);  // row_shr:8
+    v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
+    v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
     return v;
+}
+
+// Transpose of the 64x64 bit matrix whose row t is lane t's 64-bit value:
+// lane r receives column r, i.e. bit t of the result is bit r of lane t -- the
+// same as 64 ballots of "bit r is set", in six butterfly exchange steps (at
+// step s, rows t and t^s swap the s-wide off-diagonal sub-blocks).
+__device__ __forceinline__ uint64_t transpose64(uint64_t x) {
+    const int lane = __lane_id();
+    constexpr uint64_t keep[6] = {0x00000000ffffffffull, 0x0000ffff0000ffffull, 0x00ff00ff00ff00ffull,
+                                  0x0f0f0f0f0f0f0f0full, 0x3333333333333333ull, 0x5555555555555555ull};
+#pragma unroll
+    for (int k = 0; k < 6; ++k) {
+        const int s = 32 >> k;
+        const uint32_t lo = __shfl_xor((unsigned)(uint32_t)x, s, kWave);
+        const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(x >> 32), s, kWave);
+        const uint64_t y = ((uint64_t)hi << 32) | lo;
+        x = (lane & s) == 0 ? (x & keep[k]) | ((y & keep[k]) << s) : (x & ~keep[k]) | ((y & ~keep[k]) >> s);
+    }
+    return x;
 }
 
 // Nonzero-byte test of four packed bytes -> 4 bits (bit i set when byte i != 0).

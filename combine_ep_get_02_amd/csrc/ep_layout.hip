@@ -9,8 +9,9 @@
 // stage 1, which tests a node's 8 bytes of is_token_in_rank at once.
 //
 // Design: one launch.  One thread per token builds the token's 64-bit rank
-// mask (R <= 64, so rank r is bit r).  Per-rank and per-node counts come from
-// wave64 ballots (lane r keeps the popcount for rank r), experts go to an LDS
+// mask (R <= 64, so rank r is bit r).  Per-rank counts come from a 64x64 bit
+// transpose across the wave (lane r gets the column of rank r and counts it),
+// per-node counts from wave64 ballots, experts go to an LDS
 // histogram, and each block adds its non-zero partial counts into running
 // counters in the workspace.  The block's is_token_in_rank rows are staged as
 // masks in LDS and written out as one contiguous byte range with 16/4/1-byte
@@ -65,29 +66,33 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     int bad = 0;
     if (t < p.T) {
         const int64_t *row = p.topk_idx + t * K;
-        for (int j = 0; j < K; ++j) {
-            const int64_t e = row[j];
-            if (e == -1) continue;
-            if (e < -1 || e >= E) {
-                bad = 1;
-                continue;
+        // slots in batches of 8: a batch's loads are all in flight before any is used
+        for (int j0 = 0; j0 < K; j0 += 8) {
+            int64_t ev[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ev[u] = j0 + u < K ? row[j0 + u] : -1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t e = ev[u];
+                if (e == -1) continue;
+                if (e < -1 || e >= E) {
+                    bad = 1;
+                    continue;
+                }
+                const int ei = (int)e;
+                if (lds_experts)
+                    atomicAdd(&s_expert[ei], 1);
+                else
+                    atomicAdd(&acc_expert[ei], 1);
+                mask |= 1ull << (ei / experts_per_rank);
             }
-            const int ei = (int)e;
-            if (lds_experts)
-                atomicAdd(&s_expert[ei], 1);
-            else
-                atomicAdd(&acc_expert[ei], 1);
-            mask |= 1ull << (ei / experts_per_rank);
         }
     }
     s_mask[tid] = mask;
 
-    // lane r of each wave collects the wave's count for rank r
-    int rank_cnt = 0;
-    for (int r = 0; r < R; ++r) {
-        const int c = __popcll(ballot64((mask >> r) & 1ull));
-        rank_cnt = (lane == r) ? c : rank_cnt;
-    }
+    // lane r of each wave collects the wave's count for rank r: the bit
+    // transpose hands lane r the column "token goes to r" of the wave
+    const int rank_cnt = __popcll(transpose64(mask));
     if (lane < R && rank_cnt != 0) atomicAdd(&s_rank[lane], rank_cnt);
     int node_cnt = 0;
     for (int n = 0; n < nodes; ++n) {
@@ -102,12 +107,13 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     // is_token_in_rank rows of this block: one contiguous range of nt*R bytes
     const int64_t left = p.T - t0;
     const int nt = (int)(left < kLayoutThreads ? (left > 0 ? left : 0) : kLayoutThreads);
-    const int64_t nbytes = (int64_t)nt * R;
+    const int nbytes = nt * R;  // <= 256 * 64
     uint8_t *dst = p.in_rank + t0 * R;
     if (p.store_unit == 16) {  // R % 16 == 0, 16-byte aligned
-        for (int64_t u = tid; u < nbytes / 16; u += kLayoutThreads) {
-            const int64_t b = u * 16;
-            const uint64_t m = s_mask[b / R] >> (b % R);
+        const int upr = R / 16;  // 16-byte units per row
+        for (int u = tid; u < nbytes / 16; u += kLayoutThreads) {
+            const int row = u / upr, part = u - row * upr;
+            const uint64_t m = s_mask[row] >> (16 * part);
             uint4 v;
             v.x = spread4((uint32_t)m & 0xfu);
             v.y = spread4((uint32_t)(m >> 4) & 0xfu);
@@ -116,13 +122,16 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
             reinterpret_cast<uint4 *>(dst)[u] = v;
         }
     } else if (p.store_unit == 4) {  // R % 4 == 0, 4-byte aligned
-        for (int64_t u = tid; u < nbytes / 4; u += kLayoutThreads) {
-            const int64_t b = u * 4;
-            reinterpret_cast<uint32_t *>(dst)[u] = spread4((uint32_t)(s_mask[b / R] >> (b % R)) & 0xfu);
+        const int upr = R / 4;
+        for (int u = tid; u < nbytes / 4; u += kLayoutThreads) {
+            const int row = u / upr, part = u - row * upr;
+            reinterpret_cast<uint32_t *>(dst)[u] = spread4((uint32_t)(s_mask[row] >> (4 * part)) & 0xfu);
         }
     } else {
-        for (int64_t b = tid; b < nbytes; b += kLayoutThreads)
-            dst[b] = (uint8_t)((s_mask[b / R] >> (b % R)) & 1ull);
+        for (int b = tid; b < nbytes; b += kLayoutThreads) {
+            const int row = b / R, r = b - row * R;
+            dst[b] = (uint8_t)((s_mask[row] >> r) & 1ull);
+        }
     }
 
     // this block's partial counts into the running counters
@@ -135,15 +144,27 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
             if (s_expert[i] != 0) atomicAdd(&acc_expert[i], s_expert[i]);
 
     if (!elect_last_block(p.ticket)) return;
-    // last block: publish the totals and leave the counters at zero
-    for (int i = tid; i < R + nodes + E; i += kLayoutThreads) {
-        const int32_t v = atomicExch(&p.acc[i], 0);
-        if (i < R)
-            p.per_rank[i] = v;
-        else if (i < R + nodes)
-            p.per_node[i - R] = v;
-        else
-            p.per_expert[i - R - nodes] = v;
+    // last block: publish the totals and leave the counters at zero, four
+    // counters per thread in flight at a time
+    const int n = R + nodes + E;
+    for (int i0 = tid; i0 < n; i0 += 4 * kLayoutThreads) {
+        int32_t v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kLayoutThreads;
+            v[u] = i < n ? atomicExch(&p.acc[i], 0) : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int i = i0 + u * kLayoutThreads;
+            if (i >= n) continue;
+            if (i < R)
+                p.per_rank[i] = v[u];
+            else if (i < R + nodes)
+                p.per_node[i - R] = v[u];
+            else
+                p.per_expert[i - R - nodes] = v[u];
+        }
     }
 }
 

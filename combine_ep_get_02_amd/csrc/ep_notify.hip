@@ -15,8 +15,8 @@
 // Design (not the pages' one-SM-per-channel loop): one launch.  The token axis
 // is cut into 64-token chunks, one chunk per wave and one token per lane.
 //   Every wave turns its lanes' is_token_in_rank rows into 64-bit rank masks
-//   (stored for dispatch), and R ballots give each (chunk, rank) count (lane r
-//   keeps rank r's ballot).  For each channel whose end falls inside the chunk
+//   (stored for dispatch); a 64x64 bit transpose across the wave hands lane r
+//   the chunk's column for rank r, whose popcount is the (chunk, rank) count.  For each channel whose end falls inside the chunk
 //   it also stores the count of the chunk's tokens before that end.  Every
 //   value has one writer: no atomics.
 //   The last block to finish then scans: it brings the counts, the partials
@@ -49,20 +49,33 @@ struct NotifyParams {
 
 __device__ __forceinline__ uint64_t load_rank_mask(const uint8_t *row, int R, int load_unit) {
     uint64_t m = 0;
+    // fixed-bound unrolled loops so all of a row's loads are in flight together
     if (load_unit == 16) {
         const uint4 *p = reinterpret_cast<const uint4 *>(row);
-        for (int g = 0; g < R / 16; ++g) {
-            const uint4 v = p[g];
-            const uint64_t bits = nonzero_bytes4(v.x) | (nonzero_bytes4(v.y) << 4) | (nonzero_bytes4(v.z) << 8) |
-                                  (nonzero_bytes4(v.w) << 12);
-            m |= bits << (16 * g);
+        uint4 v[kMaxRanks / 16];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 16; ++g)
+            if (g < R / 16) v[g] = p[g];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 16; ++g) {
+            if (g < R / 16) {
+                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4) |
+                                      (nonzero_bytes4(v[g].z) << 8) | (nonzero_bytes4(v[g].w) << 12);
+                m |= bits << (16 * g);
+            }
         }
     } else if (load_unit == 8) {
         const uint2 *p = reinterpret_cast<const uint2 *>(row);
-        for (int g = 0; g < R / 8; ++g) {
-            const uint2 v = p[g];
-            const uint64_t bits = nonzero_bytes4(v.x) | (nonzero_bytes4(v.y) << 4);
-            m |= bits << (8 * g);
+        uint2 v[kMaxRanks / 8];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 8; ++g)
+            if (g < R / 8) v[g] = p[g];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 8; ++g) {
+            if (g < R / 8) {
+                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4);
+                m |= bits << (8 * g);
+            }
         }
     } else {
         for (int r = 0; r < R; ++r) m |= (uint64_t)(row[r] != 0) << r;
@@ -79,11 +92,7 @@ __device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
         m = load_rank_mask(p.in_rank + tok * R, R, p.load_unit);
         p.mask[tok] = m;
     }
-    uint64_t my_bits = 0;  // lane r: which tokens of the chunk go to rank r
-    for (int r = 0; r < R; ++r) {
-        const uint64_t b = ballot64((m >> r) & 1ull);
-        my_bits = (lane == r) ? b : my_bits;
-    }
+    const uint64_t my_bits = transpose64(m);  // lane r: which tokens of the chunk go to rank r
     uint64_t my_node_bits = 0;  // lane n: which tokens of the chunk reach node n
     for (int n = 0; n < nodes; ++n) {
         const bool any = R < kRanksPerNode ? m != 0 : ((m >> (n * kRanksPerNode)) & 0xffull) != 0;
@@ -126,6 +135,8 @@ __device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
 // LDS capacity of the last block for the [Q][NC] counts plus the [C][NC]
 // partials; larger problems scan in global memory instead.
 constexpr int kScanLds = 12288;
+// rows of either matrix one thread loads: ceil(kScanLds / NC / (kNotifyThreads / NC)) for any NC <= 72
+constexpr int kPasses = 14;
 
 __device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c) {
     return (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
@@ -137,44 +148,73 @@ __device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c)
 __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave) {
     __shared__ int32_t s_cnt[kScanLds];  // [Q+1][NC], then [C][NC] partials behind it
     __shared__ int32_t s_tot[kMaxRanks + kMaxRanks / kRanksPerNode];
-    const int R = p.R, nodes = p.nodes, NC = R + nodes;
-    const int64_t Q = num_chunks(p.T);
+    // everything below fits kScanLds entries, so 32-bit indices suffice
+    const int R = p.R, nodes = p.nodes, NC = R + nodes, C = p.C;
+    const int Q = (int)num_chunks(p.T);
     int32_t *s_part = s_cnt + (Q + 1) * NC;
+    // fixed (row, column) of this thread: rows advance by RP per pass
+    const int RP = kNotifyThreads / NC;
+    const int r0 = tid / NC, col = tid - r0 * NC;
+    const bool active = r0 < RP;
+    const bool is_rank = col < R;
 
-    // ---- one round trip of loads
-    for (int64_t i = tid; i < Q * NC; i += kNotifyThreads) {
-        const int64_t q = i / NC;
-        const int col = (int)(i - q * NC);
-        s_cnt[i] = col < R ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)];
-    }
-    for (int64_t i = tid; i < (int64_t)p.C * NC; i += kNotifyThreads) {
-        const int64_t c = i / NC;
-        const int col = (int)(i - c * NC);
-        const int64_t end = channel_end(p, c);
-        s_part[i] = (end % kChunk) == 0 ? 0 : (col < R ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)]);
+    // ---- one round trip of loads: at most kPasses rows per thread for each
+    // matrix (rows <= kScanLds / NC, RP = kNotifyThreads / NC), all issued
+    // before any is written to LDS
+    if (active) {
+        int32_t vq[kPasses], vc[kPasses];
+#pragma unroll
+        for (int k = 0; k < kPasses; ++k) {
+            const int q = r0 + k * RP;
+            vq[k] = q < Q ? (is_rank ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)]) : 0;
+            const int c = r0 + k * RP;
+            vc[k] = (c < C && (channel_end(p, c) % kChunk) != 0)
+                        ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
+                        : 0;
+        }
+#pragma unroll
+        for (int k = 0; k < kPasses; ++k) {
+            const int q = r0 + k * RP;
+            if (q < Q) s_cnt[q * NC + col] = vq[k];
+            const int c = r0 + k * RP;
+            if (c < C) s_part[c * NC + col] = vc[k];
+        }
+        // rows beyond kPasses passes (none within the LDS size limit)
+        for (int q = r0 + kPasses * RP; q < Q; q += RP)
+            s_cnt[q * NC + col] = is_rank ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)];
+        for (int c = r0 + kPasses * RP; c < C; c += RP)
+            s_part[c * NC + col] = (channel_end(p, c) % kChunk) != 0
+                                       ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
+                                       : 0;
     }
     const int32_t per_rank = lane < R ? p.per_rank[lane] : 0;
     const int32_t per_node = lane < nodes ? p.per_node[lane] : 0;
+    // aligned per-expert counts need nothing from the scan: done here, while
+    // the loads above are in flight
+    for (int e = tid; e < p.E; e += kNotifyThreads) {
+        const int32_t n = p.per_expert[e];
+        p.recv_per_expert[e] = (int32_t)(((int64_t)n + p.align - 1) / p.align * p.align);
+    }
     __syncthreads();
 
     // ---- scans: one wave per column, lanes over runs of chunks
-    const int64_t per = (Q + kWave - 1) / kWave;
-    for (int col = wave; col < NC; col += kNotifyWaves) {
-        const int64_t b = lane * per;
-        const int64_t e = (b + per) < Q ? (b + per) : Q;
+    const int per = (Q + kWave - 1) / kWave;
+    for (int cc = wave; cc < NC; cc += kNotifyWaves) {
+        const int b = lane * per;
+        const int e = (b + per) < Q ? (b + per) : Q;
         int32_t sum = 0;
-        for (int64_t q = b; q < e; ++q) sum += s_cnt[q * NC + col];
+        for (int q = b; q < e; ++q) sum += s_cnt[q * NC + cc];
         const int32_t incl = wave_inclusive_scan(sum);
         int32_t run = incl - sum;
-        for (int64_t q = b; q < e; ++q) {
-            const int32_t v = s_cnt[q * NC + col];
-            s_cnt[q * NC + col] = run;
+        for (int q = b; q < e; ++q) {
+            const int32_t v = s_cnt[q * NC + cc];
+            s_cnt[q * NC + cc] = run;
             run += v;
         }
         const int32_t total = readlane32(incl, kWave - 1);
         if (lane == 0) {
-            s_cnt[Q * NC + col] = total;
-            s_tot[col] = total;
+            s_cnt[Q * NC + cc] = total;
+            s_tot[cc] = total;
         }
     }
     // receive prefix sums over destination ranks and nodes (inclusive)
@@ -193,27 +233,21 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
         const bool bad = (lane < R && s_tot[lane] != per_rank) || (lane < nodes && s_tot[R + lane] != per_node);
         if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
     }
-    for (int64_t i = tid; i < (Q + 1) * NC; i += kNotifyThreads) {
-        const int64_t q = i / NC;
-        const int col = (int)(i - q * NC);
-        if (col < R)
-            p.rank_off[q * R + col] = s_cnt[i];
-        else
-            p.node_off[q * nodes + (col - R)] = s_cnt[i];
-    }
-    for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
-        const int col = (int)(i / p.C);
-        const int64_t c = i - (int64_t)col * p.C;
-        const int64_t qe = channel_end(p, c) / kChunk;
-        const int32_t v = s_cnt[qe * NC + col] + s_part[c * NC + col];
-        if (col < R)
-            p.gbl[(int64_t)col * p.C + c] = v;
-        else
-            p.rdma[(int64_t)(col - R) * p.C + c] = v;
-    }
-    for (int e = tid; e < p.E; e += kNotifyThreads) {
-        const int64_t n = p.per_expert[e];
-        p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
+    if (active) {
+        for (int q = r0; q <= Q; q += RP) {
+            if (is_rank)
+                p.rank_off[q * R + col] = s_cnt[q * NC + col];
+            else
+                p.node_off[q * nodes + (col - R)] = s_cnt[q * NC + col];
+        }
+        for (int c = r0; c < C; c += RP) {
+            const int qe = (int)(channel_end(p, c) / kChunk);
+            const int32_t v = s_cnt[qe * NC + col] + s_part[c * NC + col];
+            if (is_rank)
+                p.gbl[col * C + c] = v;
+            else
+                p.rdma[(col - R) * C + c] = v;
+        }
     }
 }
 
