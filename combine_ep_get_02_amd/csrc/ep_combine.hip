@@ -13,14 +13,13 @@
 // Design: a token-parallel gather driven by send_slot, the map dispatch
 // recorded; one wave per (token, row segment of VPL*1 KiB).  Lane r reads
 // send_slot[t][r], so the wave knows every contributing row at once and starts
-// loading the first row's segment.  The weights arrive in one round trip: lane
-// (i, j) loads weight j of the i-th contributing row, a K-step lane scan adds
-// each row's weights in j order (W), and the first segment's wave also adds
-// the rows' weights column by column in rank order (the combined weights).  The
-// row segments stream in with 16-byte non-temporal loads -- the next row's
-// while the current one is folded -- into per-lane fp32 accumulators with
-// v_fma_f32 in ascending rank order, and the wave ends with one bf16 store per
-// element.  HBM traffic: the ~8 rows read per token plus the one row written.
+// loading the first two rows' segments.  Lane r loads its row's weights in one
+// batch and adds them in j order (W); the first segment's wave also adds the
+// rows' weights column by column in rank order (the combined weights).  The
+// row segments stream in pairs with 16-byte non-temporal loads and are folded
+// in ascending rank order into per-lane fp32 accumulators with v_fma_f32; the
+// wave ends with one bf16 store per element.  HBM traffic: the ~8 rows read per
+// token plus the one row written.
 #include "ep_internal.h"
 
 namespace ep {
@@ -95,45 +94,59 @@ __global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
             slot = -1;
         }
     }
-    const uint64_t dests = ballot64(slot >= 0);
-    const int nd = __popcll(dests);
+    uint64_t ee = ballot64(slot >= 0);  // contributing ranks not yet loaded
 
-    // first contributing row's segment, in flight while the weights are summed
-    u32x4 cur[VPL];
-    if (dests != 0ull) {
-        const int64_t s0 = readlane32(slot, __builtin_ctzll(dests));
-        load_seg<VPL, EXACT>(cur, p.y + s0 * U + c0, c0, U);
-    }
+    // rows in pairs, ranks ascending: the first pair is in flight while the
+    // weights are summed
+    u32x4 a[VPL], b[VPL];
+    int ra = -1, rb = -1;
+    auto fetch = [&](u32x4(&v)[VPL], int &rk) {
+        if (ee != 0ull) {
+            rk = __builtin_ctzll(ee);
+            ee &= ee - 1ull;
+            const int64_t s = readlane32(slot, rk);
+            load_seg<VPL, EXACT>(v, p.y + s * U + c0, c0, U);
+        } else {
+            rk = -1;
+        }
+    };
+    const uint64_t dests = ee;
+    fetch(a, ra);
+    fetch(b, rb);
 
-    // weights, one pass per kWave / K contributing rows: lane (i, j) holds weight
-    // j of row d0 + i.  A K-step lane scan adds each row's weights in j order,
-    // so lane (i, K-1) ends with W of row d0 + i; Wsum keeps lane d = W of row d.
-    const int per_pass = kWave / K;
-    const int li = lane / K, lj = lane - li * K;
-    float Wsum = 0.0f;  // lane d: W of the d-th contributing row
-    float cw = 0.0f;    // lane j: combined weight j (first segment only)
-    uint64_t dd = dests;
-    for (int d0 = 0; d0 < nd; d0 += per_pass) {
-        int my_s = -1;
-        for (int i = 0; i < per_pass && dd != 0ull; ++i, dd &= dd - 1ull) {
-            const int s = readlane32(slot, __builtin_ctzll(dd));
-            if (li == i) my_s = s;
-        }
-        const float v = (my_s >= 0 && li < per_pass) ? p.recv_w[(int64_t)my_s * K + lj] : 0.0f;
-        float run = 0.0f + v;
-        for (int j = 1; j < K; ++j) {
-            const float up = __shfl_up(run, 1, kWave);
-            if (lj == j) run = up + v;
-        }
-        for (int i = 0; i < per_pass && d0 + i < nd; ++i) {
-            const float Wd = readlanef(run, i * K + K - 1);
-            if (lane == d0 + i) Wsum = Wd;
-            if (seg == 0) cw = cw + __shfl(v, i * K + (lane < K ? lane : 0), kWave);
-        }
+    // lane r: W of its row, the row's weights added in j order (batches of 8
+    // loads in flight together)
+    float W = 0.0f;
+    float wv[8];
+    for (int j0 = 0; j0 < K; j0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) wv[u] = (slot >= 0 && j0 + u < K) ? p.recv_w[(int64_t)slot * K + j0 + u] : 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+            if (j0 + u < K) W = W + wv[u];
     }
     if (seg == 0) {
         if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
-        if (p.out_w != nullptr && lane < K) p.out_w[t * K + lane] = cw;
+        if (p.out_w != nullptr) {
+            // combined weight j: the rows' weight j added in rank order (lane j)
+            float cw = 0.0f;
+            for (int j0 = 0; j0 < K; j0 += 8) {
+                if (K > 8) {  // wv holds the last batch of the W loop: reload this one
+#pragma unroll
+                    for (int u = 0; u < 8; ++u)
+                        wv[u] = (slot >= 0 && j0 + u < K) ? p.recv_w[(int64_t)slot * K + j0 + u] : 0.0f;
+                }
+                for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+                    const int r = __builtin_ctzll(dd);
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) {
+                        const float x = readlanef(wv[u], r);
+                        if (lane == j0 + u) cw = cw + x;
+                    }
+                }
+            }
+            if (lane < K) p.out_w[t * K + lane] = cw;
+        }
     }
 
     float acc[VPL][8];
@@ -141,20 +154,11 @@ __global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
     for (int i = 0; i < VPL; ++i)
 #pragma unroll
         for (int k = 0; k < 8; ++k) acc[i][k] = 0.0f;
-
-    // rows in ascending rank order; the next row's segment loads while the
-    // current one is folded in
-    int d = 0;
-    for (uint64_t ee = dests; ee != 0ull; ++d) {
-        ee &= ee - 1ull;
-        u32x4 nxt[VPL];
-        if (ee != 0ull) {
-            const int64_t sn = readlane32(slot, __builtin_ctzll(ee));
-            load_seg<VPL, EXACT>(nxt, p.y + sn * U + c0, c0, U);
-        }
-        fma_seg<VPL, EXACT>(acc, cur, readlanef(Wsum, d), c0, U);
-#pragma unroll
-        for (int i = 0; i < VPL; ++i) cur[i] = nxt[i];
+    while (ra >= 0) {
+        fma_seg<VPL, EXACT>(acc, a, readlanef(W, ra), c0, U);
+        if (rb >= 0) fma_seg<VPL, EXACT>(acc, b, readlanef(W, rb), c0, U);
+        fetch(a, ra);
+        fetch(b, rb);
     }
 
     u32x4 *dst = p.out + t * U + c0;

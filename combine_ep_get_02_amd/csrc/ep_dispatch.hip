@@ -49,11 +49,17 @@ struct DispatchParams {
     int R, K, E, experts_per_rank, my_rank, cap, S;
 };
 
-template <int VPL, bool EXACT, int WPB>
+// GRAN > 0: the block's waves sweep the destination ranks in order and meet at
+// a barrier every GRAN ranks, so the blocks' concurrent stores gather in a few
+// slabs instead of spreading over all of them.  GRAN == 0: free-running waves.
+template <int VPL, bool EXACT, int WPB, int GRAN>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) {
     const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
-    if (w >= p.T * p.S) return;  // whole wave leaves together
+    const int64_t w0 = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    const bool live = w0 < p.T * p.S;
+    if (GRAN == 0 && !live) return;  // whole wave leaves together
+    // with barriers every wave stays to the end; idle ones work on token 0 and store nothing
+    const int64_t w = live ? w0 : 0;
     const int64_t t = w / p.S;
     const int seg = (int)(w - t * p.S);
     const int R = p.R;
@@ -75,7 +81,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
     int64_t e = -1;
     float wt = 0.0f;
-    if (seg == 0 && lane < p.K) {
+    if (live && seg == 0 && lane < p.K) {
         e = p.topk_idx[t * p.K + lane];
         wt = p.topk_w[t * p.K + lane];
     }
@@ -90,10 +96,10 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
         if (lane == r) slot = base + __popcll(b & before);
     }
     const bool over = slot >= p.cap;
-    if (over) slot = -1;
+    if (over || !live) slot = -1;
     const uint64_t dests = ballot64(slot >= 0);
 
-    if (seg == 0) {
+    if (live && seg == 0) {
         if (lane < R) p.send_slot[t * R + lane] = slot;
         if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
         // ---- metadata (a4): weights / local ids of the slots living on each destination
@@ -110,54 +116,80 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
         }
     }
 
-    // ---- row copy (a4): the segment to every destination
-    for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
-        const int r = __builtin_ctzll(dd);
-        const int64_t s = readlane32(slot, r);
-        u32x4 *dst = p.recv_x + s * p.row_units + c0;
+    // ---- row copy (a4): the segment to every destination, ranks ascending
+    auto store_to = [&](uint64_t dd) {
+        for (; dd != 0ull; dd &= dd - 1ull) {
+            const int r = __builtin_ctzll(dd);
+            const int64_t s = readlane32(slot, r);
+            u32x4 *dst = p.recv_x + s * p.row_units + c0;
 #pragma unroll
-        for (int i = 0; i < VPL; ++i)
-            if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
+            for (int i = 0; i < VPL; ++i)
+                if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
+        }
+    };
+    if (GRAN == 0) {
+        store_to(dests);
+    } else {
+        for (int r0 = 0; r0 < R; r0 += GRAN) {
+            const uint64_t window = (GRAN >= kWave ? ~0ull : ((1ull << GRAN) - 1ull)) << r0;
+            store_to(dests & window);
+            __syncthreads();
+        }
     }
 }
 
-template <int VPL, bool EXACT, int WPB>
+template <int VPL, bool EXACT, int WPB, int GRAN>
 hipError_t run(DispatchParams p, hipStream_t stream) {
     p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, stream, p);
+    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN>), dim3((unsigned)blocks), dim3(WPB * kWave), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
-// Tiling: 16-byte units per lane per segment (VPL) and waves per block (WPB).
-// Only the tilings below are instantiated; dispatch_tiling picks one per row width.
-hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, hipStream_t stream) {
+// Tiling: 16-byte units per lane per segment (VPL), waves per block (WPB) and
+// the rank-sweep barrier granularity (GRAN, 0 = none).  Only the tilings below
+// are instantiated; dispatch_tiling picks one per row width.
+hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStream_t stream) {
     const bool exact = p.row_units % (vpl * kWave) == 0;
-#define EP_DISPATCH_CASE(V, W) \
-    if (vpl == V && wpb == W) return exact ? run<V, true, W>(p, stream) : run<V, false, W>(p, stream);
-    EP_DISPATCH_CASE(1, 4)
-    EP_DISPATCH_CASE(1, 8)
-    EP_DISPATCH_CASE(2, 4)
-    EP_DISPATCH_CASE(2, 8)
-    EP_DISPATCH_CASE(4, 4)
-    EP_DISPATCH_CASE(7, 4)
-    EP_DISPATCH_CASE(8, 4)
-    EP_DISPATCH_CASE(14, 4)
+#define EP_DISPATCH_CASE(V, W, G) \
+    if (vpl == V && wpb == W && gran == G) return exact ? run<V, true, W, G>(p, stream) : run<V, false, W, G>(p, stream);
+    EP_DISPATCH_CASE(1, 4, 0)
+    EP_DISPATCH_CASE(1, 8, 0)
+    EP_DISPATCH_CASE(1, 8, 1)
+    EP_DISPATCH_CASE(1, 8, 4)
+    EP_DISPATCH_CASE(2, 4, 0)
+    EP_DISPATCH_CASE(2, 8, 0)
+    EP_DISPATCH_CASE(2, 8, 1)
+    EP_DISPATCH_CASE(4, 4, 0)
+    EP_DISPATCH_CASE(7, 4, 0)
+    EP_DISPATCH_CASE(8, 4, 0)
+    EP_DISPATCH_CASE(8, 8, 1)
+    EP_DISPATCH_CASE(14, 4, 0)
+    EP_DISPATCH_CASE(14, 4, 1)
+    EP_DISPATCH_CASE(14, 8, 0)
+    EP_DISPATCH_CASE(14, 8, 1)
+    EP_DISPATCH_CASE(14, 8, 4)
+    EP_DISPATCH_CASE(14, 16, 1)
+    EP_DISPATCH_CASE(14, 16, 4)
 #undef EP_DISPATCH_CASE
     return hipErrorInvalidValue;
 }
 
 // Measured on MI355X (prefill / skew / large workloads): one wave per whole
-// 14 KiB row is best when the row is 7168 bf16 wide; other widths use 1 KiB
-// segments with 8 waves per block.
-void dispatch_tiling(int64_t row_units, int *vpl, int *wpb) {
+// 14 KiB row, 16 waves per block sweeping the ranks with a barrier every 4
+// ranks, is best when the row is 7168 bf16 wide; other widths use free-running
+// waves on 1 KiB segments, 8 waves per block.
+void dispatch_tiling(int64_t row_units, int *vpl, int *wpb, int *gran) {
     if (row_units % (14 * kWave) == 0 && row_units / (14 * kWave) == 1) {
         *vpl = 14;
-        *wpb = 4;
+        *wpb = 16;
+        *gran = 4;
     } else {
         *vpl = 1;
         *wpb = 8;
+        *gran = 0;
     }
 }
 
@@ -191,9 +223,9 @@ hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *t
     p.my_rank = s.my_rank;
     p.cap = cap;
     p.S = 1;
-    int vpl, wpb;
-    dispatch_tiling(p.row_units, &vpl, &wpb);
-    return run_tiled(p, vpl, wpb, stream);
+    int vpl, wpb, gran;
+    dispatch_tiling(p.row_units, &vpl, &wpb, &gran);
+    return run_tiled(p, vpl, wpb, gran, stream);
 }
 
 }  // namespace ep
