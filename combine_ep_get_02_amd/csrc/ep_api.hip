@@ -38,6 +38,49 @@ bool workspace_ok(const ep_shape_t *s, const void *ws, size_t bytes) {
            bytes >= workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels).total;
 }
 
+// Shared checks and launch of the bf16 and fp8 dispatch entry points.
+ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_bytes, const float *x_scales,
+                             int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                             const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
+                             int32_t recv_capacity, void *recv_x, float *recv_x_scales, float *recv_topk_weights,
+                             int64_t *recv_topk_idx, int32_t *recv_src_info, int32_t *send_slot,
+                             int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (row_bytes % 16 != 0 || recv_capacity < 0 || num_scales < 0) return EP_ERR_INVALID_ARG;
+    if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
+    if (s->num_tokens == 0) return EP_OK;
+    if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || recv_gbl_rank_prefix_sum == nullptr ||
+        send_slot == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
+        return EP_ERR_INVALID_ARG;
+    if (num_scales > 0 && (x_scales == nullptr || (recv_capacity > 0 && recv_x_scales == nullptr)))
+        return EP_ERR_INVALID_ARG;
+    if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
+    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
+    DispatchArgs a = {};
+    a.x = x;
+    a.row_units = row_bytes / 16;
+    a.x_scales = x_scales;
+    a.num_scales = num_scales;
+    a.topk_idx = topk_idx;
+    a.topk_w = topk_weights;
+    a.recv_gbl = recv_gbl_rank_prefix_sum;
+    a.ws = static_cast<const char *>(workspace);
+    a.cached_slot = nullptr;
+    a.cap = recv_capacity;
+    a.recv_x = recv_x;
+    a.recv_scales = recv_x_scales;
+    a.recv_w = recv_topk_weights;
+    a.recv_idx = recv_topk_idx;
+    a.src_info = recv_src_info;
+    a.send_slot = send_slot;
+    a.dev_status = dev_status;
+    return from_hip(launch_dispatch(*s, a, stream));
+}
+
 }  // namespace
 
 extern "C" {
@@ -104,22 +147,49 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
                         int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+    return dispatch_checked(s, x, s ? (int64_t)s->hidden * 2 : 0, nullptr, 0, topk_idx, topk_weights,
+                            recv_gbl_rank_prefix_sum, workspace, workspace_bytes, recv_capacity, recv_x, nullptr,
+                            recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status, stream);
+}
+
+ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_scales, int32_t num_scales,
+                            const int64_t *topk_idx, const float *topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                            const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
+                            float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
+                            int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+    return dispatch_checked(s, x, s ? (int64_t)s->hidden : 0, x_scales, num_scales, topk_idx, topk_weights,
+                            recv_gbl_rank_prefix_sum, workspace, workspace_bytes, recv_capacity, recv_x,
+                            recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status,
+                            stream);
+}
+
+ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
+                               int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,
+                               float *recv_x_scales, int32_t *dev_status, hipStream_t stream) {
     ep_status_t st = check_shape(s);
     if (st != EP_OK) return st;
-    if (recv_capacity < 0) return EP_ERR_INVALID_ARG;
+    if (elem_bytes != 1 && elem_bytes != 2) return EP_ERR_INVALID_ARG;
+    const int64_t row_bytes = (int64_t)s->hidden * elem_bytes;
+    if (row_bytes % 16 != 0 || recv_capacity < 0) return EP_ERR_INVALID_ARG;
+    if (num_scales < 0) return EP_ERR_INVALID_ARG;
+    if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
     if (s->num_tokens == 0) return EP_OK;
-    if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || recv_gbl_rank_prefix_sum == nullptr ||
-        send_slot == nullptr)
-        return EP_ERR_INVALID_ARG;
-    if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
+    if (x == nullptr || send_slot == nullptr) return EP_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && recv_x == nullptr) return EP_ERR_INVALID_ARG;
+    if (num_scales > 0 && (x_scales == nullptr || (recv_capacity > 0 && recv_x_scales == nullptr)))
         return EP_ERR_INVALID_ARG;
     if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
-    if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
-    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
-    return from_hip(launch_dispatch(*s, static_cast<const uint4 *>(x), topk_idx, topk_weights,
-                                    recv_gbl_rank_prefix_sum, static_cast<const char *>(workspace), recv_capacity,
-                                    static_cast<uint4 *>(recv_x), recv_topk_weights, recv_topk_idx, recv_src_info,
-                                    send_slot, dev_status, stream));
+    DispatchArgs a = {};
+    a.x = x;
+    a.row_units = row_bytes / 16;
+    a.x_scales = x_scales;
+    a.num_scales = num_scales;
+    a.cached_slot = send_slot;
+    a.cap = recv_capacity;
+    a.recv_x = recv_x;
+    a.recv_scales = recv_x_scales;
+    a.dev_status = dev_status;
+    return from_hip(launch_dispatch(*s, a, stream));
 }
 
 ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_topk_weights, const int32_t *send_slot,

@@ -33,12 +33,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 struct DispatchParams {
     const u32x4 *x;
+    const float *x_scales;
     const int64_t *topk_idx;
     const float *topk_w;
     const int32_t *recv_gbl;
     const uint64_t *mask;
     const int32_t *rank_off;
+    const int32_t *cached_slot;
     u32x4 *recv_x;
+    float *recv_scales;
     float *recv_w;
     int64_t *recv_idx;
     int32_t *src_info;
@@ -46,13 +49,15 @@ struct DispatchParams {
     int32_t *dev_status;
     int64_t T;
     int64_t row_units;  // 16-byte units per row
-    int R, K, E, experts_per_rank, my_rank, cap, S;
+    int R, K, E, experts_per_rank, my_rank, cap, S, num_scales;
 };
 
 // GRAN > 0: the block's waves sweep the destination ranks in order and meet at
 // a barrier every GRAN ranks, so the blocks' concurrent stores gather in a few
 // slabs instead of spreading over all of them.  GRAN == 0: free-running waves.
-template <int VPL, bool EXACT, int WPB, int GRAN>
+// CACHED: the rows come from send_slot of an earlier dispatch with the same
+// routing (p.cached_slot); no routing, metadata or send_slot output.
+template <int VPL, bool EXACT, int WPB, int GRAN, bool CACHED>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t w0 = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
@@ -72,36 +77,62 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     for (int i = 0; i < VPL; ++i)
         if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
 
-    // ---- routing state: chunk masks, slab bases, this token's topk slots
-    const int64_t q = t / kChunk;
-    const int my = (int)(t - q * kChunk);
-    const int64_t tok = q * kChunk + lane;
-    const uint64_t m = tok < p.T ? p.mask[tok] : 0ull;
-    int base = 0;
-    if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
+    int slot = -1;
     int64_t e = -1;
     float wt = 0.0f;
-    if (live && seg == 0 && lane < p.K) {
-        e = p.topk_idx[t * p.K + lane];
-        wt = p.topk_w[t * p.K + lane];
-    }
+    if (CACHED) {
+        // ---- rows recorded by an earlier dispatch
+        bool bad = false;
+        if (live && lane < R) {
+            slot = p.cached_slot[t * R + lane];
+            if (slot < -1 || slot >= p.cap) {
+                bad = true;
+                slot = -1;
+            }
+        }
+        if (ballot64(bad) != 0ull && lane == 0 && seg == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
+    } else {
+        // ---- routing state: chunk masks, slab bases, this token's topk slots
+        const int64_t q = t / kChunk;
+        const int my = (int)(t - q * kChunk);
+        const int64_t tok = q * kChunk + lane;
+        const uint64_t m = tok < p.T ? p.mask[tok] : 0ull;
+        int base = 0;
+        if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
+        if (live && seg == 0 && lane < p.K) {
+            e = p.topk_idx[t * p.K + lane];
+            wt = p.topk_w[t * p.K + lane];
+        }
 
-    // ---- row assignment (a3): lane r gets the row for rank r
-    const uint64_t mine = readlane64(m, my);
-    const uint64_t before = (1ull << my) - 1ull;
-    int slot = -1;
-    for (uint64_t mm = mine; mm != 0ull; mm &= mm - 1ull) {
-        const int r = __builtin_ctzll(mm);
-        const uint64_t b = ballot64((m >> r) & 1ull);
-        if (lane == r) slot = base + __popcll(b & before);
+        // ---- row assignment (a3): lane r gets the row for rank r
+        const uint64_t mine = readlane64(m, my);
+        const uint64_t before = (1ull << my) - 1ull;
+        for (uint64_t mm = mine; mm != 0ull; mm &= mm - 1ull) {
+            const int r = __builtin_ctzll(mm);
+            const uint64_t b = ballot64((m >> r) & 1ull);
+            if (lane == r) slot = base + __popcll(b & before);
+        }
+        const bool over = slot >= p.cap;
+        if (over) slot = -1;
+        if (live && seg == 0 && ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
     }
-    const bool over = slot >= p.cap;
-    if (over || !live) slot = -1;
+    if (!live) slot = -1;
     const uint64_t dests = ballot64(slot >= 0);
 
-    if (live && seg == 0) {
+    // ---- per-token scales (fp8 rows) travel beside the rows
+    if (live && seg == 0 && p.num_scales > 0) {
+        for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
+            const int i = i0 + lane;
+            const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
+            for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+                const int64_t s = readlane32(slot, __builtin_ctzll(dd));
+                if (i < p.num_scales) p.recv_scales[s * p.num_scales + i] = sc;
+            }
+        }
+    }
+
+    if (!CACHED && live && seg == 0) {
         if (lane < R) p.send_slot[t * R + lane] = slot;
-        if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
         // ---- metadata (a4): weights / local ids of the slots living on each destination
         const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
         for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
@@ -143,8 +174,12 @@ hipError_t run(DispatchParams p, hipStream_t stream) {
     p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN>), dim3((unsigned)blocks), dim3(WPB * kWave), 0,
-                       stream, p);
+    if (p.cached_slot != nullptr)
+        hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, true>), dim3((unsigned)blocks), dim3(WPB * kWave),
+                           0, stream, p);
+    else
+        hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, false>), dim3((unsigned)blocks),
+                           dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
 }
 
@@ -164,6 +199,8 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
     EP_DISPATCH_CASE(2, 8, 1)
     EP_DISPATCH_CASE(4, 4, 0)
     EP_DISPATCH_CASE(7, 4, 0)
+    EP_DISPATCH_CASE(7, 8, 0)
+    EP_DISPATCH_CASE(7, 16, 4)
     EP_DISPATCH_CASE(8, 4, 0)
     EP_DISPATCH_CASE(8, 8, 1)
     EP_DISPATCH_CASE(14, 4, 0)
@@ -182,8 +219,12 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
 // ranks, is best when the row is 7168 bf16 wide; other widths use free-running
 // waves on 1 KiB segments, 8 waves per block.
 void dispatch_tiling(int64_t row_units, int *vpl, int *wpb, int *gran) {
-    if (row_units % (14 * kWave) == 0 && row_units / (14 * kWave) == 1) {
+    if (row_units == 14 * kWave) {  // 7168 bf16
         *vpl = 14;
+        *wpb = 16;
+        *gran = 4;
+    } else if (row_units == 7 * kWave) {  // 7168 fp8 (or 3584 bf16)
+        *vpl = 7;
         *wpb = 16;
         *gran = 4;
     } else {
@@ -195,33 +236,38 @@ void dispatch_tiling(int64_t row_units, int *vpl, int *wpb, int *gran) {
 
 }  // namespace
 
-hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *topk_idx, const float *topk_w,
-                           const int32_t *recv_gbl, const char *ws, int32_t cap, uint4 *recv_x, float *recv_w,
-                           int64_t *recv_idx, int32_t *src_info, int32_t *send_slot, int32_t *dev_status,
-                           hipStream_t stream) {
+hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream) {
     if (s.num_tokens == 0) return hipSuccess;
-    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
     DispatchParams p;
-    p.x = reinterpret_cast<const u32x4 *>(x);
-    p.topk_idx = topk_idx;
-    p.topk_w = topk_w;
-    p.recv_gbl = recv_gbl;
-    p.mask = reinterpret_cast<const uint64_t *>(ws + w.mask);
-    p.rank_off = reinterpret_cast<const int32_t *>(ws + w.rank_off);
-    p.recv_x = reinterpret_cast<u32x4 *>(recv_x);
-    p.recv_w = recv_w;
-    p.recv_idx = recv_idx;
-    p.src_info = src_info;
-    p.send_slot = send_slot;
-    p.dev_status = dev_status;
+    p.x = reinterpret_cast<const u32x4 *>(a.x);
+    p.x_scales = a.x_scales;
+    p.topk_idx = a.topk_idx;
+    p.topk_w = a.topk_w;
+    p.recv_gbl = a.recv_gbl;
+    p.mask = nullptr;
+    p.rank_off = nullptr;
+    if (a.ws != nullptr) {
+        const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
+        p.mask = reinterpret_cast<const uint64_t *>(a.ws + w.mask);
+        p.rank_off = reinterpret_cast<const int32_t *>(a.ws + w.rank_off);
+    }
+    p.cached_slot = a.cached_slot;
+    p.recv_x = reinterpret_cast<u32x4 *>(a.recv_x);
+    p.recv_scales = a.recv_scales;
+    p.recv_w = a.recv_w;
+    p.recv_idx = a.recv_idx;
+    p.src_info = a.src_info;
+    p.send_slot = a.send_slot;
+    p.dev_status = a.dev_status;
     p.T = s.num_tokens;
-    p.row_units = s.hidden / 8;
+    p.row_units = a.row_units;
     p.R = s.num_ranks;
     p.K = s.num_topk;
     p.E = s.num_experts;
     p.experts_per_rank = s.num_experts / s.num_ranks;
     p.my_rank = s.my_rank;
-    p.cap = cap;
+    p.cap = a.cap;
+    p.num_scales = a.num_scales;
     p.S = 1;
     int vpl, wpb, gran;
     dispatch_tiling(p.row_units, &vpl, &wpb, &gran);

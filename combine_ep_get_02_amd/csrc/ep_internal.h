@@ -15,6 +15,7 @@ constexpr int kRanksPerNode = 8;      // ranks per node (rank -> node is rank / 
 constexpr int kMaxRanks = 64;         // one rank per lane of a wave
 constexpr int kMaxTopk = 32;
 constexpr int kMaxChannels = 4096;
+constexpr int kMaxScales = 1024;      // per-token scales of fp8 rows
 constexpr int kChunk = 64;            // tokens per routing chunk (one per lane)
 
 __host__ __device__ inline int num_nodes(int R) { return R / kRanksPerNode > 0 ? R / kRanksPerNode : 1; }
@@ -66,10 +67,29 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
                          int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,
                          char *ws, int32_t *dev_status, hipStream_t stream);
 
-hipError_t launch_dispatch(const ep_shape_t &s, const uint4 *x, const int64_t *topk_idx, const float *topk_w,
-                           const int32_t *recv_gbl, const char *ws, int32_t cap, uint4 *recv_x, float *recv_w,
-                           int64_t *recv_idx, int32_t *src_info, int32_t *send_slot, int32_t *dev_status,
-                           hipStream_t stream);
+// Arguments of one dispatch launch.  Rows are row_units 16-byte units (bf16:
+// hidden / 8, fp8: hidden / 16); cached_slot non-null selects cached mode.
+struct DispatchArgs {
+    const void *x;
+    int64_t row_units;
+    const float *x_scales;  // [t][num_scales], may be null when num_scales == 0
+    int num_scales;
+    const int64_t *topk_idx;
+    const float *topk_w;
+    const int32_t *recv_gbl;
+    const char *ws;
+    const int32_t *cached_slot;  // [t][R] rows of an earlier dispatch (cached mode)
+    int32_t cap;
+    void *recv_x;
+    float *recv_scales;
+    float *recv_w;
+    int64_t *recv_idx;
+    int32_t *src_info;
+    int32_t *send_slot;
+    int32_t *dev_status;
+};
+
+hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream);
 
 hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv_w, const int32_t *send_slot,
                           int32_t num_recv_rows, uint4 *combined_x, float *combined_w, int32_t *dev_status,

@@ -20,7 +20,8 @@ LIBRARY = os.path.join(_PKG, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
 EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
 
-EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_combine", "ep_workspace_bytes", "ep_status_string")
+EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached", "ep_combine",
+            "ep_workspace_bytes", "ep_status_string")
 
 
 class EpError(RuntimeError):
@@ -51,8 +52,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
     lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
+    lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + \
+        [_P] * 8
+    lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
-    for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_combine"):
+    for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
+                 "ep_combine"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -129,6 +134,24 @@ def ep_dispatch(shape, x, topk_idx, topk_weights, recv_gbl_rank_prefix_sum, work
                               workspace.numel() * workspace.element_size(), int(recv_capacity), _ptr(recv_x),
                               _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info), _ptr(send_slot),
                               _ptr(dev_status), _stream(stream)), "ep_dispatch")
+
+
+def ep_dispatch_fp8(shape, x, x_scales, num_scales, topk_idx, topk_weights, recv_gbl_rank_prefix_sum, workspace,
+                    recv_capacity, recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot,
+                    dev_status=None, stream=None) -> None:
+    _check(load().ep_dispatch_fp8(ctypes.byref(shape), _ptr(x), _ptr(x_scales), int(num_scales), _ptr(topk_idx),
+                                  _ptr(topk_weights), _ptr(recv_gbl_rank_prefix_sum), _ptr(workspace),
+                                  workspace.numel() * workspace.element_size(), int(recv_capacity), _ptr(recv_x),
+                                  _ptr(recv_x_scales), _ptr(recv_topk_weights), _ptr(recv_topk_idx),
+                                  _ptr(recv_src_info), _ptr(send_slot), _ptr(dev_status), _stream(stream)),
+           "ep_dispatch_fp8")
+
+
+def ep_dispatch_cached(shape, x, elem_bytes, x_scales, num_scales, send_slot, recv_capacity, recv_x,
+                       recv_x_scales=None, dev_status=None, stream=None) -> None:
+    _check(load().ep_dispatch_cached(ctypes.byref(shape), _ptr(x), int(elem_bytes), _ptr(x_scales), int(num_scales),
+                                     _ptr(send_slot), int(recv_capacity), _ptr(recv_x), _ptr(recv_x_scales),
+                                     _ptr(dev_status), _stream(stream)), "ep_dispatch_cached")
 
 
 def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x, combined_topk_weights=None,

@@ -117,3 +117,19 @@ def generate(w: Workload | str, seed: int | None = None, with_x: bool = True) ->
     topk_idx, topk_weights = draw_routing(rng, w)
     return dict(workload=w, x=x, topk_idx=topk_idx, topk_weights=topk_weights)
 
+
+def fp8_rows(x_bits: np.ndarray, block: int = 128) -> tuple[np.ndarray, np.ndarray]:
+    """fp8 inputs of the fp8 dispatch workload, prepared the way a caller would
+    (per token, per `block` elements: scale = amax / 448, element = x / scale
+    cast to float8 e4m3 by torch).  Returns (uint8 bit patterns [t][h],
+    float32 scales [t][h / block])."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(x_bits).view(np.int16)).view(torch.bfloat16).float()
+    T, H = t.shape
+    g = t.reshape(T, H // block, block)
+    amax = g.abs().amax(dim=2, keepdim=True).clamp(min=1e-12)
+    scale = amax / 448.0
+    q = (g / scale).to(torch.float8_e4m3fn).reshape(T, H)
+    return q.view(torch.uint8).numpy().copy(), scale.reshape(T, H // block).numpy().astype(np.float32).copy()
+

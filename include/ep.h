@@ -62,7 +62,7 @@ enum {
     EP_DEV_BAD_TOPK_IDX = 1,   /* a topk id outside [-1, num_experts): that slot is treated as masked */
     EP_DEV_RECV_OVERFLOW = 2,  /* a receive row >= recv_capacity: the row is not written, send_slot = -1 */
     EP_DEV_COUNT_MISMATCH = 4, /* num_tokens_per_rank / _per_rdma_rank disagree with is_token_in_rank */
-    EP_DEV_BAD_SEND_SLOT = 8   /* combine met a send_slot outside [-1, num_recv_rows): skipped */
+    EP_DEV_BAD_SEND_SLOT = 8   /* a send_slot entry outside its valid range (combine, cached dispatch): skipped */
 };
 
 /* Problem shape (host struct, read during the call only). */
@@ -144,6 +144,36 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
                         int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Dispatch of fp8 rows.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch:
+ * x_scales with num_scales per token are dispatched beside the rows and returned as
+ * recv_x_scales (the FP8 scale buffer); the combine side stays bf16]
+ * Same as ep_dispatch, with rows of `hidden` one-byte elements (hidden % 16 == 0) moved
+ * bit for bit, plus the token's num_scales float scales (0 <= num_scales <= 1024):
+ *   x [t][h] fp8 (any 1-byte format), x_scales [t][num_scales] f32 (nullable if num_scales == 0)
+ *   recv_x [cap][h], recv_x_scales [cap][num_scales] (nullable if num_scales == 0)
+ * Every other argument and output is as in ep_dispatch.
+ */
+ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_scales, int32_t num_scales,
+                            const int64_t *topk_idx, const float *topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                            const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
+                            float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
+                            int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Cached-mode dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch with
+ * cachedMode: the layout of an earlier call is reused -- no counting, no notification]
+ * Copies row t to recv_x[send_slot[t][r]] for every r with send_slot[t][r] >= 0, where
+ * send_slot [t][R] was written by an earlier ep_dispatch / ep_dispatch_fp8 for the same
+ * routing.  Rows are hidden * elem_bytes bytes (elem_bytes 2 = bf16, 1 = fp8; a multiple
+ * of 16); num_scales float scales per token go along when num_scales > 0.  No metadata
+ * is written.  Entries outside [-1, recv_capacity) are skipped and flagged
+ * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.
+ */
+ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
+                               int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,
+                               float *recv_x_scales, int32_t *dev_status, hipStream_t stream);
 
 /*
  * Stage 5, combine.  [mscclpp ht_runtime.cc, internodeCombine / intranodeCombine (bf16 out,

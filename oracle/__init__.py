@@ -46,8 +46,11 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_dispatch.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I] + [_P] * 11
     lib.oracle_combine.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _P]
     lib.oracle_combine_f64.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P]
+    lib.oracle_dispatch_fp8.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I] + [_P] * 11
+    lib.oracle_dispatch_cached.argtypes = [_I, _I, _L, _P, _P, _I, _P, _I, _P, _P]
     lib.oracle_bf16_round.argtypes = [_P, _P, _L]
-    for name in ("oracle_layout", "oracle_notify", "oracle_dispatch", "oracle_combine", "oracle_combine_f64"):
+    for name in ("oracle_layout", "oracle_notify", "oracle_dispatch", "oracle_combine", "oracle_combine_f64",
+                 "oracle_dispatch_fp8", "oracle_dispatch_cached"):
         getattr(lib, name).restype = ctypes.c_int
     lib.oracle_bf16_round.restype = None
     return lib
@@ -145,6 +148,51 @@ class Oracle:
                                       _ptr(send_slot))
         return dict(recv_x=recv_x, recv_topk_weights=recv_w, recv_topk_idx=recv_idx,
                     recv_src_info=src_info, send_slot=send_slot, status=st)
+
+    def dispatch_fp8(self, x8, x_scales, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+                     recv_gbl_rank_prefix_sum, E: int, my_rank: int = 0, recv_capacity: int | None = None,
+                     with_topk_idx: bool = True):
+        """fp8 rows (uint8 bit patterns [t][h]) plus float scales [t][num_scales]."""
+        x8 = np.ascontiguousarray(x8, dtype=np.uint8)
+        x_scales = np.ascontiguousarray(x_scales, dtype=np.float32)
+        topk_idx = np.ascontiguousarray(topk_idx, dtype=np.int64)
+        topk_weights = np.ascontiguousarray(topk_weights, dtype=np.float32)
+        in_rank = np.ascontiguousarray(is_token_in_rank, dtype=np.uint8)
+        gbl = np.ascontiguousarray(gbl_channel_prefix_matrix, dtype=np.int32)
+        recv_gbl = np.ascontiguousarray(recv_gbl_rank_prefix_sum, dtype=np.int32)
+        T, H = x8.shape
+        NS = x_scales.shape[1]
+        K = topk_idx.shape[1]
+        R, C = gbl.shape
+        n = int(recv_gbl[-1]) if R else 0
+        cap = n if recv_capacity is None else recv_capacity
+        recv_x = np.zeros((cap, H), np.uint8)
+        recv_s = np.zeros((cap, NS), np.float32)
+        recv_w = np.zeros((cap, K), np.float32)
+        recv_idx = np.zeros((cap, K), np.int64) if with_topk_idx else None
+        src_info = np.zeros((cap, 2), np.int32)
+        send_slot = np.zeros((T, R), np.int32)
+        st = self.lib.oracle_dispatch_fp8(T, H, K, E, R, C, my_rank, cap, _ptr(x8), _ptr(x_scales), NS,
+                                          _ptr(topk_idx), _ptr(topk_weights), _ptr(in_rank), _ptr(gbl),
+                                          _ptr(recv_gbl), _ptr(recv_x), _ptr(recv_s), _ptr(recv_w), _ptr(recv_idx),
+                                          _ptr(src_info), _ptr(send_slot))
+        return dict(recv_x=recv_x, recv_x_scales=recv_s, recv_topk_weights=recv_w, recv_topk_idx=recv_idx,
+                    recv_src_info=src_info, send_slot=send_slot, status=st)
+
+    def dispatch_cached(self, x, send_slot, recv_capacity: int, x_scales=None):
+        """Rows of any element type (moved as bytes) to the rows send_slot names."""
+        x = np.ascontiguousarray(x)
+        T = x.shape[0]
+        row_bytes = int(np.prod(x.shape[1:], dtype=np.int64)) * x.itemsize
+        send_slot = np.ascontiguousarray(send_slot, dtype=np.int32)
+        R = send_slot.shape[1]
+        NS = 0 if x_scales is None else x_scales.shape[1]
+        xs = None if x_scales is None else np.ascontiguousarray(x_scales, dtype=np.float32)
+        recv_x = np.zeros((recv_capacity,) + x.shape[1:], x.dtype)
+        recv_s = np.zeros((recv_capacity, NS), np.float32) if NS else None
+        st = self.lib.oracle_dispatch_cached(T, R, row_bytes, _ptr(x), _ptr(xs), NS, _ptr(send_slot),
+                                             recv_capacity, _ptr(recv_x), _ptr(recv_s))
+        return dict(recv_x=recv_x, recv_x_scales=recv_s, status=st)
 
     def combine(self, y, recv_topk_weights, send_slot, num_recv: int, with_weights: bool = True):
         y = np.ascontiguousarray(y, dtype=np.uint16)

@@ -30,7 +30,7 @@
  *   ORC_BAD_TOPK_IDX   1  a topk id outside [-1, E); the slot is treated as masked
  *   ORC_RECV_OVERFLOW  2  a receive row index >= the receive capacity; row skipped
  *   ORC_COUNT_MISMATCH 4  per-rank/per-node counts disagree with is_token_in_rank
- *   ORC_BAD_SEND_SLOT  8  combine met a send_slot outside [-1, num_recv); skipped
+ *   ORC_BAD_SEND_SLOT  8  a send_slot outside [-1, rows) in combine or cached dispatch; skipped
  */
 #include <math.h>
 #include <stdint.h>
@@ -189,13 +189,13 @@ int oracle_notify(int32_t T, int32_t E, int32_t R, int32_t C, int32_t expert_ali
  *                          sender fills and combine reads).
  * Rows at or beyond recv_capacity are not written, their send_slot stays -1
  * and ORC_RECV_OVERFLOW is raised.  recv_topk_idx may be NULL. */
-int oracle_dispatch(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t C,
-                    int32_t my_rank, int32_t recv_capacity, const uint16_t *x,
-                    const int64_t *topk_idx, const float *topk_weights,
-                    const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
-                    const int32_t *recv_gbl_rank_prefix_sum, uint16_t *recv_x,
-                    float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
-                    int32_t *send_slot) {
+static int orc_dispatch_rows(int32_t T, int64_t row_bytes, int32_t K, int32_t E, int32_t R, int32_t C,
+                             int32_t my_rank, int32_t recv_capacity, const uint8_t *x, const float *x_scales,
+                             int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                             const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
+                             const int32_t *recv_gbl_rank_prefix_sum, uint8_t *recv_x, float *recv_x_scales,
+                             float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
+                             int32_t *send_slot) {
     int status = 0;
     const int32_t experts_per_rank = E / R;
     for (int64_t i = 0; i < (int64_t)T * R; ++i) send_slot[i] = -1;
@@ -214,7 +214,9 @@ int oracle_dispatch(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32
                     continue;
                 }
                 send_slot[t * R + r] = (int32_t)row;
-                memcpy(recv_x + row * H, x + t * H, (size_t)H * sizeof(uint16_t));
+                memcpy(recv_x + row * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+                for (int32_t i = 0; i < num_scales; ++i)
+                    recv_x_scales[row * num_scales + i] = x_scales[t * num_scales + i];
                 for (int32_t j = 0; j < K; ++j) {
                     int64_t e = topk_idx[t * K + j];
                     int on_r = orc_topk_valid(e, E, &status) && e / experts_per_rank == r;
@@ -227,6 +229,59 @@ int oracle_dispatch(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32
             }
         }
         if (row != (int64_t)recv_gbl_rank_prefix_sum[r]) status |= ORC_COUNT_MISMATCH;
+    }
+    return status;
+}
+
+/* bf16 rows of H elements. */
+int oracle_dispatch(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t C,
+                    int32_t my_rank, int32_t recv_capacity, const uint16_t *x,
+                    const int64_t *topk_idx, const float *topk_weights,
+                    const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
+                    const int32_t *recv_gbl_rank_prefix_sum, uint16_t *recv_x,
+                    float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
+                    int32_t *send_slot) {
+    return orc_dispatch_rows(T, (int64_t)H * 2, K, E, R, C, my_rank, recv_capacity, (const uint8_t *)x, NULL, 0,
+                             topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+                             recv_gbl_rank_prefix_sum, (uint8_t *)recv_x, NULL, recv_topk_weights, recv_topk_idx,
+                             recv_src_info, send_slot);
+}
+
+/* fp8 rows: H one-byte elements per token plus num_scales float scales per token,
+ * both moved bit for bit ([mscclpp] internodeDispatch / intranodeDispatch take
+ * x_scales with num_scales per token and return recv_x_scales; the FP8 scale
+ * buffer travels beside the rows).  The combine side stays bf16. */
+int oracle_dispatch_fp8(int32_t T, int32_t H, int32_t K, int32_t E, int32_t R, int32_t C, int32_t my_rank,
+                        int32_t recv_capacity, const uint8_t *x, const float *x_scales, int32_t num_scales,
+                        const int64_t *topk_idx, const float *topk_weights, const uint8_t *is_token_in_rank,
+                        const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
+                        uint8_t *recv_x, float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
+                        int32_t *recv_src_info, int32_t *send_slot) {
+    return orc_dispatch_rows(T, (int64_t)H, K, E, R, C, my_rank, recv_capacity, x, x_scales, num_scales, topk_idx,
+                             topk_weights, is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum,
+                             recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot);
+}
+
+/* Cached mode ([mscclpp] internodeDispatch with cachedMode: the layout of an
+ * earlier call is reused, no counting or notification).  Rows (and scales, when
+ * num_scales > 0) go where send_slot [t][R] -- recorded by an earlier dispatch
+ * with the same routing -- says; no metadata is produced.  Entries outside
+ * [-1, recv_capacity) raise ORC_BAD_SEND_SLOT and are skipped. */
+int oracle_dispatch_cached(int32_t T, int32_t R, int64_t row_bytes, const uint8_t *x, const float *x_scales,
+                           int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, uint8_t *recv_x,
+                           float *recv_x_scales) {
+    int status = 0;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t r = 0; r < R; ++r) {
+            int64_t s = send_slot[t * R + r];
+            if (s == -1) continue;
+            if (s < -1 || s >= recv_capacity) {
+                status |= ORC_BAD_SEND_SLOT;
+                continue;
+            }
+            memcpy(recv_x + s * row_bytes, x + t * row_bytes, (size_t)row_bytes);
+            for (int32_t i = 0; i < num_scales; ++i) recv_x_scales[s * num_scales + i] = x_scales[t * num_scales + i];
+        }
     }
     return status;
 }

@@ -385,6 +385,62 @@ def pin_workload(o, inputs: dict, hidden: int | None = None) -> list[str]:
     return errs
 
 
+def pin_fp8_and_cached(o, inputs: dict, hidden: int | None = None) -> list[str]:
+    """fp8 dispatch moves the fp8 rows and their scales to the rows the bf16
+    routing defines; cached dispatch reproduces a full dispatch from its
+    send_slot, and a random injective send_slot places row t at exactly the
+    rows it names (numpy assignment as the independent formulation)."""
+    from combine_ep_get_02_amd.inputs import fp8_rows
+
+    wl = inputs["workload"]
+    x = inputs["x"] if hidden is None else np.ascontiguousarray(inputs["x"][:, :hidden])
+    idx, w = inputs["topk_idx"], inputs["topk_weights"]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    errs = []
+    x8, sc = fp8_rows(x)
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, 1)
+    args = (idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], E)
+    d16 = o.dispatch(x, *args)
+    d8 = o.dispatch_fp8(x8, sc, *args)
+    for k in ("send_slot", "recv_topk_weights", "recv_topk_idx", "recv_src_info"):
+        if not np.array_equal(d16[k], d8[k]):
+            errs.append(f"fp8 dispatch {k} differs from the bf16 routing")
+    slot = d8["send_slot"]
+    tt, rr = np.nonzero(slot >= 0)
+    ss = slot[tt, rr]
+    if not np.array_equal(d8["recv_x"][ss], x8[tt]):
+        errs.append("fp8 recv_x row != x8[src]")
+    if not np.array_equal(d8["recv_x_scales"][ss], sc[tt]):
+        errs.append("fp8 recv_x_scales != x_scales[src]")
+    n = note["num_recv_tokens"]
+    c16 = o.dispatch_cached(x, slot, n)
+    if not np.array_equal(c16["recv_x"], d16["recv_x"]) or c16["status"]:
+        errs.append("cached bf16 dispatch != full dispatch")
+    c8 = o.dispatch_cached(x8, slot, n, sc)
+    if not np.array_equal(c8["recv_x"], d8["recv_x"]) or not np.array_equal(c8["recv_x_scales"], d8["recv_x_scales"]):
+        errs.append("cached fp8 dispatch != full dispatch")
+    # random injective map with some bad entries
+    rng = np.random.default_rng(5)
+    T = x.shape[0]
+    cap = T * 2
+    rs = np.full((T, R), -1, np.int32)
+    picks = rng.choice(T * R, min(cap, T * R), replace=False)
+    rs.reshape(-1)[picks] = rng.permutation(cap)[: len(picks)]
+    rs[0, 0] = cap + 3
+    rs[min(1, T - 1), R - 1] = -5
+    want = np.zeros((cap,) + x.shape[1:], x.dtype)
+    ok = rs >= 0
+    ok &= rs < cap
+    tt, rr = np.nonzero(ok)
+    want[rs[tt, rr]] = x[tt]
+    got = o.dispatch_cached(x, rs, cap)
+    if not np.array_equal(got["recv_x"], want) or got["status"] != 8:
+        errs.append("cached dispatch with a random map is wrong")
+    return errs
+
+
 def expected_ranks_per_token(E: int, R: int, K: int) -> float:
     """Closed form for uniform routing without replacement: R*(1 - C(E-E/R, K)/C(E, K))."""
     er = E // R

@@ -27,12 +27,13 @@ def ep():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ep_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ep_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["ep_get_layout", "ep_notify", "ep_dispatch", "ep_combine",
-                                          "ep_workspace_bytes", "ep_status_string"])
+    assert declared_functions() == sorted(["ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8",
+                                          "ep_dispatch_cached", "ep_combine", "ep_workspace_bytes",
+                                          "ep_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ep):
@@ -87,18 +88,20 @@ def _call_all(ep, s):
         lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
         lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None, None),
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
+        lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None, None),
+        lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, None, None),
     ]
     return codes
 
 
 @pytest.mark.parametrize("name", sorted(BAD_SHAPES))
 def test_malformed_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 4
+    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 6
 
 
 @pytest.mark.parametrize("name", sorted(UNSUPPORTED))
 def test_unsupported_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 4
+    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 6
 
 
 def test_null_and_misaligned_pointers_rejected(ep):
@@ -119,6 +122,25 @@ def test_null_and_misaligned_pointers_rejected(ep):
     assert lib.ep_combine(ctypes.byref(s), p, p, p, 10, odd, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(s), p, p, None, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_get_layout(None, p, p, p, p, p, p, 1 << 30, None, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_fp8_and_cached_argument_checks(ep):
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    s = _shape(ep)
+    # fp8 rows must be a whole number of 16-byte units
+    s12 = _shape(ep, hidden=7160)
+    assert lib.ep_dispatch_fp8(ctypes.byref(s12), p, p, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
+                               None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, None, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
+                               None) == ep.EP_ERR_INVALID_ARG  # scales missing
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 2000, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
+                               None) == ep.EP_ERR_UNSUPPORTED
+    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 3, None, 0, p, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, None, 10, p, None, None,
+                                  None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_cached(ctypes.byref(s12), p, 1, None, 0, p, 10, p, None, None,
+                                  None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_empty_dispatch_and_combine_enqueue_nothing(ep):

@@ -168,3 +168,125 @@ def test_combine_flags_bad_send_slot():
     assert np.array_equal(H.bf16_host(out), ref["combined_x"])
     assert np.array_equal(cw.cpu().numpy(), ref["combined_topk_weights"])
     assert int(st.item()) == 8 and ref["status"] == 8
+
+
+# ---------------------------------------------------------------- fp8 rows and cached mode
+def _fp8_case(x, idx, w, E, R, C, num_scales_block=128, capacity=None):
+    """GPU: layout, notify, ep_dispatch_fp8, then ep_dispatch_cached of the same
+    fp8 rows; oracle: the same stages.  Returns (gpu, ref) dicts."""
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+    from combine_ep_get_02_amd.inputs import fp8_rows
+
+    x8, sc = fp8_rows(x, num_scales_block) if num_scales_block else (x.view(np.uint8)[:, : x.shape[1]].copy(), None)
+    T, H = x8.shape
+    NS = 0 if sc is None else sc.shape[1]
+    K = idx.shape[1]
+    shape = ep.make_shape(T, H, K, E, R, C)
+    cap = capacity if capacity is not None else T * min(R, K)
+    b = ep.allocate(shape, 0)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    n = ep.run_notify(b, read_back=True)
+    dx = torch.from_numpy(x8).cuda()
+    dsc = torch.from_numpy(sc).cuda() if NS else None
+    rx = torch.full((max(cap, 1), H), 0xAB, dtype=torch.uint8, device="cuda")
+    rs = torch.full((max(cap, 1), max(NS, 1)), -2.0, dtype=torch.float32, device="cuda")
+    rw = torch.full((max(cap, 1), K), -3.0, dtype=torch.float32, device="cuda")
+    ri = torch.full((max(cap, 1), K), -777, dtype=torch.int64, device="cuda")
+    si = torch.full((max(cap, 1), 2), -777, dtype=torch.int32, device="cuda")
+    ss = torch.full((T, R), -777, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_fp8(shape, dx, dsc, NS, didx, dw, b.recv_gbl, b.workspace, cap, rx, rs if NS else None, rw, ri, si,
+                       ss, st)
+    rows = min(n, cap)
+    # cached mode: same rows again, into fresh buffers, from the recorded send_slot
+    cx = torch.full((max(cap, 1), H), 0xCD, dtype=torch.uint8, device="cuda")
+    cs = torch.full((max(cap, 1), max(NS, 1)), -4.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch_cached(shape, dx, 1, dsc, NS, ss, cap, cx, cs if NS else None, st)
+    torch.cuda.synchronize()
+    gpu = dict(send_slot=ss.cpu().numpy(), recv_x=rx[:rows].cpu().numpy(), recv_topk_weights=rw[:rows].cpu().numpy(),
+               recv_topk_idx=ri[:rows].cpu().numpy(), recv_src_info=si[:rows].cpu().numpy(),
+               cached_x=cx[:rows].cpu().numpy(), status=int(st.item()))
+    if NS:
+        gpu["recv_x_scales"] = rs[:rows].cpu().numpy()
+        gpu["cached_scales"] = cs[:rows].cpu().numpy()
+    o = oracle.Oracle()
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, 1)
+    d = o.dispatch_fp8(x8, sc if NS else np.zeros((T, 0), np.float32), idx, w, lay["is_token_in_rank"],
+                       note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], E, recv_capacity=cap)
+    c = o.dispatch_cached(x8, d["send_slot"], cap, sc if NS else None)
+    ref = dict(send_slot=d["send_slot"], recv_x=d["recv_x"][:rows], recv_topk_weights=d["recv_topk_weights"][:rows],
+               recv_topk_idx=d["recv_topk_idx"][:rows], recv_src_info=d["recv_src_info"][:rows],
+               cached_x=c["recv_x"][:rows], status=d["status"] | c["status"])
+    if NS:
+        ref["recv_x_scales"] = d["recv_x_scales"][:rows]
+        ref["cached_scales"] = c["recv_x_scales"][:rows]
+    return gpu, ref
+
+
+def _exact(gpu, ref):
+    bad = []
+    for k, r in ref.items():
+        g = gpu[k]
+        if k == "status":
+            continue
+        g, r = np.asarray(g), np.asarray(r)
+        if g.shape != r.shape or not np.array_equal(g.view(np.uint8), r.view(np.uint8)):
+            bad.append(k)
+    return bad
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep", "prefill", "skew", "large"])
+def test_fp8_and_cached_dispatch_parity(name):
+    print(f"[parity] fp8+cached workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    gpu, ref = _fp8_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels)
+    assert _exact(gpu, ref) == []
+    assert gpu["status"] == 0 == ref["status"]
+
+
+def test_fp8_many_scales_and_overflow():
+    # 70 scales per token (more than one wave of lanes), and a receive capacity overflow
+    x, idx, w = _random_case(300, 16, 64, 4, 5, 70 * 16, seed=12)
+    import oracle
+    n = int(oracle.Oracle().layout(idx, 64, 16)["num_tokens_per_rank"].sum())
+    gpu, ref = _fp8_case(x, idx, w, 64, 16, 5, num_scales_block=16, capacity=n - 11)
+    assert _exact(gpu, ref) == []
+    assert gpu["status"] & 2 and ref["status"] & 2
+
+
+def test_fp8_without_scales():
+    x, idx, w = _random_case(200, 8, 32, 3, 4, 256, seed=13)
+    gpu, ref = _fp8_case(x, idx, w, 32, 8, 4, num_scales_block=0)
+    assert _exact(gpu, ref) == []
+
+
+def test_cached_dispatch_bad_slots_bf16():
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+
+    rng = np.random.default_rng(21)
+    T, R, Hd, cap = 150, 16, 512, 600
+    x = H.random_rows(rng, T, Hd)
+    slot = np.full((T, R), -1, np.int32)
+    picks = rng.choice(T * R, cap - 20, replace=False)
+    slot.reshape(-1)[picks] = rng.permutation(cap)[: cap - 20]
+    slot[4, 3] = cap + 9
+    slot[7, 0] = -3
+    shape = ep.make_shape(T, Hd, 2, 16, R, 4)
+    out = torch.zeros((cap, Hd), dtype=torch.bfloat16, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_cached(shape, H.to_dev_bf16(x), 2, None, 0, torch.from_numpy(slot).cuda(), cap, out, None, st)
+    torch.cuda.synchronize()
+    ref = oracle.Oracle().dispatch_cached(x, slot, cap)
+    assert np.array_equal(H.bf16_host(out), ref["recv_x"])
+    assert int(st.item()) == 8 and ref["status"] == 8

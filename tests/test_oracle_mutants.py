@@ -56,6 +56,11 @@ MUTANTS = {
                            "if (dropped >= 0x8000u) kept += 1u;"),
     "rounding_truncates": ("if (dropped > 0x8000u || (dropped == 0x8000u && (kept & 1u))) kept += 1u;", ";"),
     "bf16_widen_shift": ("uint32_t u = (uint32_t)h << 16;", "uint32_t u = (uint32_t)h << 15;"),
+    "fp8_scales_not_copied": ("recv_x_scales[row * num_scales + i] = x_scales[t * num_scales + i];", ";"),
+    "cached_wrong_source_row": ("memcpy(recv_x + s * row_bytes, x + t * row_bytes, (size_t)row_bytes);",
+                                "memcpy(recv_x + s * row_bytes, x + (t > 0 ? t - 1 : t) * row_bytes, (size_t)row_bytes);"),
+    "cached_bad_slot_not_flagged": ("                status |= ORC_BAD_SEND_SLOT;\n                continue;\n            }\n            memcpy(recv_x",
+                                    "                continue;\n            }\n            memcpy(recv_x"),
 }
 
 CHILD = textwrap.dedent("""
@@ -66,6 +71,7 @@ CHILD = textwrap.dedent("""
     o = oracle.Oracle(oracle.load({lib!r}))
     errs = pins.pin_golden(o) + pins.pin_bf16_rounding(o) + pins.pin_workload(o, inputs.generate("tiny"))
     errs += pins.pin_workload(o, inputs.generate("sweep"), hidden=64)
+    errs += pins.pin_fp8_and_cached(o, inputs.generate("tiny"))
     if not errs:
         errs += pins.pin_bruteforce(o)
     print("CAUGHT" if errs else "MISSED", errs[:2])

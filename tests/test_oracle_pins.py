@@ -123,3 +123,9 @@ def test_edge_receive_capacity_overflow(orc, workload_inputs):
                        note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], 16, recv_capacity=cap)
     assert dis["status"] == 2
     assert np.sort(dis["send_slot"][dis["send_slot"] >= 0]).tolist() == list(range(cap))
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep", "skew"])
+def test_fp8_and_cached_dispatch(orc, workload_inputs, name):
+    assert pins.pin_fp8_and_cached(orc, workload_inputs(name), hidden=None if name == "tiny" else 512) == []
+
