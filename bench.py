@@ -8,9 +8,13 @@ emulated ranks (8 nodes x 8), 24 channels, seed 0.
 
 The metric is dispatch+combine HBM throughput: the bytes the method must move
 (x read once per token, each receive row written once and read back once,
-metadata) over the measured dispatch+combine kernel time (HIP events around each
-call, averaged over the timed steps).  ``ms_per_step`` is the wall time of a
-whole step including layout and notify.  Prints one JSON line.
+metadata) over the dispatch+combine time of the timed steps (one HIP event
+pair per step around the two calls, averaged).  Each kernel's own average
+launch duration -- the roofline figure -- is taken from back-to-back launches
+between one event pair, which is what a kernel trace reports for it.
+``ms_per_step`` is the wall time of a whole step including layout and notify.
+Beside the metric: the cached-mode and fp8-row dispatch forms, a cold-cache
+cross-check and the oracle's throughput on the host.  Prints one JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline]
 """
@@ -44,6 +48,17 @@ def combine_bytes(T, H, K, R, N) -> int:
     return N * 2 * H + N * 4 * K + 4 * T * R + T * 2 * H + T * 4 * K
 
 
+def dispatch_fp8_bytes(T, H, K, R, N, S) -> int:
+    """as dispatch_bytes with 1-byte rows and S fp32 scales per row moved beside them."""
+    return T * (H + 4 * S) + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
+
+
+def dispatch_cached_bytes(T, R, N, row_bytes, S) -> int:
+    """rows (and their scales) read once per token, the [t][R] send_slot map
+    read, every receive row (and its scales) written."""
+    return T * (row_bytes + 4 * S) + 4 * T * R + N * (row_bytes + 4 * S)
+
+
 def layout_notify_bytes(T, K, R, E, C) -> int:
     nodes = max(1, R // 8)
     return T * K * 8 + T * R + 4 * (R + nodes + E) + T * R + 4 * (R + nodes + E) + 4 * (R + nodes) * (C + 1) + 4 * E
@@ -51,6 +66,9 @@ def layout_notify_bytes(T, K, R, E, C) -> int:
 
 PROFILE = os.path.join(ROOT, "profiles", "ep_kernels_prefill_hbm_bytes.txt")
 KERNEL_SOURCES = {"dispatch_kernel": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dispatch_kernel_fp8": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
 
@@ -112,6 +130,124 @@ def cpu_baseline(d, wl, n_recv, budget_s: float = 12.0) -> dict:
             "us_dispatch_plus_combine": round(dc * 1e6, 1), "host_cores": os.cpu_count()}
 
 
+class HipEvents:
+    """HIP events on torch's current stream, created with
+    hipEventDisableSystemFence: recording one then skips the system-scope
+    cache write-back that a default event performs, which otherwise adds a few
+    microseconds to every bracketed launch.  Uses the HIP runtime the process
+    has already loaded (torch's), so the events and torch's streams belong to
+    the same runtime."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+
+        import torch
+
+        torch.zeros(1, device="cuda")  # runtime loaded and device initialised
+        paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln})
+        if not paths:
+            raise RuntimeError("HIP runtime library not found in this process")
+        self._ct = ctypes
+        self._hip = ctypes.CDLL(paths[0])
+        self._torch = torch
+        self._live = []
+
+    def _check(self, rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what} failed with HIP error {rc}")
+
+    def event(self):
+        e = self._ct.c_void_p()
+        self._check(self._hip.hipEventCreateWithFlags(self._ct.byref(e), self._ct.c_uint(self.DISABLE_SYSTEM_FENCE)),
+                    "hipEventCreateWithFlags")
+        self._live.append(e)
+        return e
+
+    def pair(self):
+        return self.event(), self.event()
+
+    def record(self, e):
+        stream = self._ct.c_void_p(self._torch.cuda.current_stream().cuda_stream)
+        self._check(self._hip.hipEventRecord(e, stream), "hipEventRecord")
+
+    def elapsed_us(self, a, c) -> float:
+        ms = self._ct.c_float()
+        self._check(self._hip.hipEventSynchronize(c), "hipEventSynchronize")
+        self._check(self._hip.hipEventElapsedTime(self._ct.byref(ms), a, c), "hipEventElapsedTime")
+        return ms.value * 1e3
+
+    def mean_us(self, fn, n: int) -> float:
+        """mean duration of n back-to-back calls of fn between one event pair"""
+        a, c = self.pair()
+        self.record(a)
+        for _ in range(n):
+            fn()
+        self.record(c)
+        return self.elapsed_us(a, c) / n
+
+    def close(self):
+        self._torch.cuda.synchronize()
+        for e in self._live:
+            self._hip.hipEventDestroy(e)
+        self._live = []
+
+
+def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer) -> dict:
+    """Cached-mode and fp8-row dispatch on the same workload, reported beside
+    the metric (which stays the bf16 path).  Each call's duration is the mean
+    of `steps` back-to-back launches after one warm-up; each result is checked
+    against the bf16 dispatch just measured (cached rows equal, fp8 rows and
+    scales found at the same send_slot rows)."""
+    import torch
+
+    wl = d["workload"]
+    T, H, K, R = wl.tokens, wl.hidden, wl.topk, wl.ranks
+
+    def mean_us(fn):
+        fn()
+        return timer.mean_us(fn, steps)
+
+    def rate(nbytes, us):
+        return {"us": round(us, 2), "bytes": nbytes, "GB/s": round(nbytes / us / 1e3, 2),
+                "pct_peak": round(100 * nbytes / us / 1e3 / HBM_PEAK_GBPS, 2)}
+
+    out = {}
+    live = b.send_slot >= 0
+    rows = b.send_slot[live].long()
+    tok = torch.arange(T, device=x.device).unsqueeze(1).expand(T, R)[live]
+
+    cx = torch.empty_like(b.recv_x)
+    out["dispatch_cached_bf16"] = rate(dispatch_cached_bytes(T, R, n_recv, 2 * H, 0), mean_us(
+        lambda: ep.ep_dispatch_cached(shape, x, 2, None, 0, b.send_slot, n_recv, cx, None, b.dev_status)))
+    out["dispatch_cached_bf16"]["check"] = bool(torch.equal(cx.view(torch.int16), b.recv_x.view(torch.int16)))
+    del cx
+
+    # fp8 rows: e4m3 with one fp32 scale per 128-element block, as a caller would quantise them
+    x8n, scn = inputs.fp8_rows(d["x"])
+    x8, sc = torch.from_numpy(x8n).cuda(), torch.from_numpy(scn).cuda()
+    S = sc.shape[1]
+    rx = torch.empty((n_recv, H), dtype=torch.uint8, device=x.device)
+    rs = torch.empty((n_recv, S), dtype=torch.float32, device=x.device)
+    slot8 = torch.empty_like(b.send_slot)
+    out["dispatch_fp8"] = rate(dispatch_fp8_bytes(T, H, K, R, n_recv, S), mean_us(
+        lambda: ep.ep_dispatch_fp8(shape, x8, sc, S, idx, w, b.recv_gbl, b.workspace, n_recv, rx, rs, b.recv_w,
+                                   b.recv_idx, b.src_info, slot8, b.dev_status)))
+    out["dispatch_fp8"]["check"] = bool(torch.equal(slot8, b.send_slot) and torch.equal(rx[rows], x8[tok])
+                                        and torch.equal(rs[rows], sc[tok]))
+    out["dispatch_fp8"]["num_scales"] = S
+    cx8, cs8 = torch.empty_like(rx), torch.empty_like(rs)
+    out["dispatch_cached_fp8"] = rate(dispatch_cached_bytes(T, R, n_recv, H, S), mean_us(
+        lambda: ep.ep_dispatch_cached(shape, x8, 1, sc, S, b.send_slot, n_recv, cx8, cs8, b.dev_status)))
+    out["dispatch_cached_fp8"]["check"] = bool(torch.equal(cx8, rx) and torch.equal(cs8, rs))
+    for key, kernel in (("dispatch_cached_bf16", "dispatch_kernel_cached_bf16"), ("dispatch_fp8", "dispatch_kernel_fp8"),
+                        ("dispatch_cached_fp8", "dispatch_kernel_cached_fp8")):
+        out[key]["traffic"] = measured_traffic(kernel, wl.name)
+    out["dev_status"] = int(b.dev_status.item())
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -119,6 +255,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the cached-mode and fp8-row dispatch timings reported beside the metric")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 1 GiB scratch write before each, untimed, to evict the caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -165,64 +303,75 @@ def main() -> int:
     del probe
     b = ep.allocate(shape, n_recv)
 
+    timer = HipEvents()
+    calls = {"layout": lambda: ep.run_layout(b, idx), "notify": lambda: ep.run_notify(b),
+             "dispatch": lambda: ep.run_dispatch(b, x, idx, w), "combine": lambda: ep.run_combine(b)}
+
     def step(ev=None):
+        calls["layout"]()
+        calls["notify"]()
         if ev is not None:
-            ev[0].record()
-        ep.run_layout(b, idx)
+            timer.record(ev[0])
+        calls["dispatch"]()
+        calls["combine"]()
         if ev is not None:
-            ev[1].record()
-        ep.run_notify(b)
-        if ev is not None:
-            ev[2].record()
-        ep.run_dispatch(b, x, idx, w)
-        if ev is not None:
-            ev[3].record()
-        ep.run_combine(b)
-        if ev is not None:
-            ev[4].record()
+            timer.record(ev[1])
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    # timed region: K whole steps; one event pair per step around dispatch+combine
+    events = [timer.pair() for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    us_dc = float(np.mean([timer.elapsed_us(a, c) for a, c in events]))
 
-    def mean_ms(a, c):
-        return float(np.mean([ev[a].elapsed_time(ev[c]) for ev in events]))
-
-    ms_layout, ms_notify = mean_ms(0, 1), mean_ms(1, 2)
-    ms_dispatch, ms_combine = mean_ms(2, 3), mean_ms(3, 4)
+    # each kernel's average launch duration: K back-to-back launches between one event pair
+    us = {k: timer.mean_us(f, args.steps) for k, f in calls.items()}
 
     # correctness guard on the measured buffers: identity experts return x
     live = b.in_rank.bool().any(1)
     ok = bool(torch.equal(b.combined_x[live], x[live])) and int(b.dev_status.item()) == 0
 
-    # cold-cache cross-check: evict with a 1 GiB write before each (untimed) step
+    # cold-cache cross-check: evict with a 1 GiB write before each (untimed) dispatch+combine
     cold = None
     if args.cold_steps > 0:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.cold_steps)]
-        for i in range(args.cold_steps):
-            scratch.fill_(i & 0xFF)
-            step(cev[i])
+        cev = [(timer.pair(), timer.pair()) for _ in range(args.cold_steps)]
+        for (d0, d1), (c0, c1) in cev:
+            calls["layout"]()
+            calls["notify"]()
+            scratch.fill_(7)
+            timer.record(d0)
+            calls["dispatch"]()
+            timer.record(d1)
+            scratch.fill_(9)
+            timer.record(c0)
+            calls["combine"]()
+            timer.record(c1)
         torch.cuda.synchronize()
-        cold = {"us_dispatch": round(float(np.mean([e[2].elapsed_time(e[3]) for e in cev])) * 1e3, 2),
-                "us_combine": round(float(np.mean([e[3].elapsed_time(e[4]) for e in cev])) * 1e3, 2)}
+        cold = {"us_dispatch": round(float(np.mean([timer.elapsed_us(*dp) for dp, _ in cev])), 2),
+                "us_combine": round(float(np.mean([timer.elapsed_us(*cp) for _, cp in cev])), 2),
+                "note": "one launch each after a 1 GiB scratch write, single-call events"}
         del scratch
 
+    variants = None if args.no_variants else time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, args.steps,
+                                                             timer)
+    if variants is not None:
+        ok = ok and variants["dev_status"] == 0 and all(v["check"] for k, v in variants.items() if k != "dev_status")
+
     db, cb = dispatch_bytes(T, H, K, R, n_recv), combine_bytes(T, H, K, R, n_recv)
-    gbps = (db + cb) / ((ms_dispatch + ms_combine) * 1e-3) / 1e9
-    if ms_dispatch >= ms_combine:
-        dom, dom_bytes, dom_ms = "dispatch_kernel", db, ms_dispatch
+    gbps = (db + cb) / us_dc / 1e3
+    if us["dispatch"] >= us["combine"]:
+        dom, dom_bytes, dom_us = "dispatch_kernel", db, us["dispatch"]
     else:
-        dom, dom_bytes, dom_ms = "combine_kernel", cb, ms_combine
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        dom, dom_bytes, dom_us = "combine_kernel", cb, us["combine"]
+    achieved = dom_bytes / dom_us / 1e3
     out = {
         "metric": "dispatch+combine µs/iter and HBM GB/s (% peak) at t=4096,h=7168,topk=8",
         "value": round(gbps, 2),
@@ -239,22 +388,28 @@ def main() -> int:
         "config": {"workload": f"{wl.name}: t={T}, h={H}, topk={K}, experts={E}, emulated ranks={R} "
                                f"({max(1, R // 8)} nodes x 8), channels={C}, uniform routing, seed {wl.seed}",
                    "global_batch": T, "seq_len": 1, "parallelism": "single GPU share (one source rank)"},
-        "us_per_iter_dispatch_plus_combine": round((ms_dispatch + ms_combine) * 1e3, 2),
+        "us_per_iter_dispatch_plus_combine": round(us_dc, 2),
         "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
-        "us_layout": round(ms_layout * 1e3, 2),
-        "us_notify": round(ms_notify * 1e3, 2),
-        "us_dispatch": round(ms_dispatch * 1e3, 2),
-        "us_combine": round(ms_combine * 1e3, 2),
+        "us_layout": round(us["layout"], 2),
+        "us_notify": round(us["notify"], 2),
+        "us_dispatch": round(us["dispatch"], 2),
+        "us_combine": round(us["combine"], 2),
+        "timing": "value: dispatch+combine bytes / mean time between one event pair per timed step around "
+                  "dispatch+combine; us_<kernel>: mean of back-to-back launches between one event pair; "
+                  "events created with hipEventDisableSystemFence",
         "num_recv_tokens": n_recv,
         "bytes_dispatch": db,
         "bytes_combine": cb,
         "bytes_layout_notify": layout_notify_bytes(T, K, R, E, C),
         "identity_check": ok,
         "cold": cold,
+        "variants": variants,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                     "traffic": measured_traffic(dom, wl.name), "algorithmic_bytes": dom_bytes},
+                     "traffic": measured_traffic(dom, wl.name), "algorithmic_bytes": dom_bytes,
+                     "us_per_launch": round(dom_us, 2)},
     }
+    timer.close()
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(d, wl, n_recv)
     print(json.dumps(out), flush=True)
