@@ -48,6 +48,7 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_combine_f64.argtypes = [_I, _I, _I, _I, _I, _P, _P, _P, _P]
     lib.oracle_dispatch_fp8.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _P, _P, _I] + [_P] * 11
     lib.oracle_dispatch_cached.argtypes = [_I, _I, _L, _P, _P, _I, _P, _I, _P, _P]
+    lib.oracle_group_by_expert.argtypes = [_I, _I, _I, _L, _P, _P, _I, _P, _P, _P, _P, _I, _I] + [_P] * 6
     lib.oracle_bf16_round.argtypes = [_P, _P, _L]
     for name in ("oracle_layout", "oracle_notify", "oracle_dispatch", "oracle_combine", "oracle_combine_f64",
                  "oracle_dispatch_fp8", "oracle_dispatch_cached"):
@@ -193,6 +194,35 @@ class Oracle:
         st = self.lib.oracle_dispatch_cached(T, R, row_bytes, _ptr(x), _ptr(xs), NS, _ptr(send_slot),
                                              recv_capacity, _ptr(recv_x), _ptr(recv_s))
         return dict(recv_x=recv_x, recv_x_scales=recv_s, status=st)
+
+    def group_by_expert(self, recv_x, recv_topk_idx, recv_topk_weights, recv_gbl_rank_prefix_sum,
+                        aligned_per_expert, E: int, grouped_capacity: int | None = None, recv_x_scales=None,
+                        num_recv_rows: int | None = None):
+        """Receive rows grouped into per-expert segments padded to the aligned
+        counts.  Positions the call does not write (at or past the grouped row
+        total) keep the fill values: rows 0, grouped_row -2, weight NaN."""
+        recv_x = np.ascontiguousarray(recv_x)
+        idx = np.ascontiguousarray(recv_topk_idx, dtype=np.int64)
+        w = np.ascontiguousarray(recv_topk_weights, dtype=np.float32)
+        gbl = np.ascontiguousarray(recv_gbl_rank_prefix_sum, dtype=np.int32)
+        aligned = np.ascontiguousarray(aligned_per_expert, dtype=np.int32)
+        R, K = gbl.shape[0], idx.shape[1]
+        n = idx.shape[0] if num_recv_rows is None else int(num_recv_rows)
+        cap = int(aligned.sum()) if grouped_capacity is None else int(grouped_capacity)
+        row_bytes = int(np.prod(recv_x.shape[1:], dtype=np.int64)) * recv_x.itemsize
+        NS = 0 if recv_x_scales is None else recv_x_scales.shape[1]
+        xs = None if recv_x_scales is None else np.ascontiguousarray(recv_x_scales, dtype=np.float32)
+        gx = np.zeros((cap,) + recv_x.shape[1:], recv_x.dtype)
+        gs = np.zeros((cap, NS), np.float32) if NS else None
+        grow = np.full(cap, -2, np.int32)
+        gw = np.full(cap, np.nan, np.float32)
+        pos = np.zeros((n, K), np.int32)
+        m = np.zeros(1, np.int32)
+        st = self.lib.oracle_group_by_expert(E, R, K, row_bytes, _ptr(recv_x), _ptr(xs), NS, _ptr(idx), _ptr(w),
+                                             _ptr(gbl), _ptr(aligned), n, cap, _ptr(gx), _ptr(gs), _ptr(grow),
+                                             _ptr(gw), _ptr(pos), _ptr(m))
+        return dict(grouped_x=gx, grouped_x_scales=gs, grouped_row=grow, grouped_weights=gw, slot_pos=pos,
+                    num_grouped_rows=int(m[0]), status=st)
 
     def combine(self, y, recv_topk_weights, send_slot, num_recv: int, with_weights: bool = True):
         y = np.ascontiguousarray(y, dtype=np.uint16)

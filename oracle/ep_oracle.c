@@ -1,6 +1,7 @@
 /*
  * ep_oracle.c -- plain, slow, single-threaded CPU oracle for the expert-parallel
- * dispatch/combine core (layout, notify, dispatch, combine) on one GPU's share.
+ * dispatch/combine core (layout, notify, dispatch, combine, and the grouping of
+ * received rows by local expert) on one GPU's share.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
  * leg of the benchmark may load this library.  The product path (the HIP library
@@ -28,7 +29,8 @@
  *
  * Status bits returned by every function (0 = clean):
  *   ORC_BAD_TOPK_IDX   1  a topk id outside [-1, E); the slot is treated as masked
- *   ORC_RECV_OVERFLOW  2  a receive row index >= the receive capacity; row skipped
+ *   ORC_RECV_OVERFLOW  2  a receive row index >= the receive capacity (or a grouped
+ *                         entry past its segment or the grouped capacity); skipped
  *   ORC_COUNT_MISMATCH 4  per-rank/per-node counts disagree with is_token_in_rank
  *   ORC_BAD_SEND_SLOT  8  a send_slot outside [-1, rows) in combine or cached dispatch; skipped
  */
@@ -377,5 +379,76 @@ int oracle_combine_f64(int32_t T, int32_t H, int32_t K, int32_t R, int32_t num_r
             for (int32_t i = 0; i < H; ++i) o[i] += W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);
         }
     }
+    return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* Grouping of the receive rows by local expert (the step after dispatch that
+ * grouped expert GEMMs consume).  The pages give only its sizes: [notes] sm0
+ * stage 6 and [mscclpp] internodeNotifyDispatch hand back, per local expert,
+ * the received slot count rounded up to expert_alignment.  Reading (the
+ * grouping order itself is not on the pages):
+ *   a receive row of slab r holds, for slot j, local expert
+ *   le = recv_topk_idx[row][j] (-1 = not on r); its global expert is
+ *   e = r * (E / R) + le.  Segment e of the grouped region starts at
+ *   sum_{e' < e} aligned[e'] and holds, in (row, j) ascending order, one entry
+ *   per (row, j) with that expert; positions past the entries up to aligned[e]
+ *   are padding (zero row, grouped_row -1, weight 0).
+ *   grouped_x[pos] = recv_x[row] (bitwise, with its scales), grouped_row[pos] =
+ *   row, grouped_weights[pos] = recv_topk_weights[row][j], slot_pos[row][j] =
+ *   pos (-1 for slots with no entry).  *num_grouped_rows = sum_e aligned[e].
+ * Rows at or beyond num_recv_rows are outside every slab.  An entry beyond its
+ * segment's aligned size or at/after grouped_capacity is skipped with
+ * ORC_RECV_OVERFLOW; a local id outside [-1, E/R) with ORC_BAD_TOPK_IDX. */
+int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, const uint8_t *recv_x,
+                           const float *recv_x_scales, int32_t num_scales, const int64_t *recv_topk_idx,
+                           const float *recv_topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                           const int32_t *aligned_per_expert, int32_t num_recv_rows, int32_t grouped_capacity,
+                           uint8_t *grouped_x, float *grouped_x_scales, int32_t *grouped_row,
+                           float *grouped_weights, int32_t *slot_pos, int32_t *num_grouped_rows) {
+    int status = 0;
+    const int32_t er = E / R;
+    for (int64_t i = 0; i < (int64_t)num_recv_rows * K; ++i) {
+        slot_pos[i] = -1;
+        if (recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er) status |= ORC_BAD_TOPK_IDX;
+    }
+    int64_t offset = 0; /* start of segment e */
+    for (int32_t r = 0; r < R; ++r) {
+        int64_t lo = r > 0 ? recv_gbl_rank_prefix_sum[r - 1] : 0;
+        int64_t hi = recv_gbl_rank_prefix_sum[r];
+        if (hi > num_recv_rows) hi = num_recv_rows;
+        if (lo > hi) lo = hi;
+        for (int32_t le = 0; le < er; ++le) {
+            const int32_t e = r * er + le;
+            int64_t used = 0; /* entries placed so far in segment e */
+            for (int64_t row = lo; row < hi; ++row) {
+                for (int32_t j = 0; j < K; ++j) {
+                    if (recv_topk_idx[row * K + j] != le) continue;
+                    const int64_t pos = offset + used;
+                    if (used >= aligned_per_expert[e] || pos >= grouped_capacity) {
+                        status |= ORC_RECV_OVERFLOW;
+                        continue;
+                    }
+                    memcpy(grouped_x + pos * row_bytes, recv_x + row * row_bytes, (size_t)row_bytes);
+                    for (int32_t i = 0; i < num_scales; ++i)
+                        grouped_x_scales[pos * num_scales + i] = recv_x_scales[row * num_scales + i];
+                    grouped_row[pos] = (int32_t)row;
+                    grouped_weights[pos] = recv_topk_weights[row * K + j];
+                    slot_pos[row * K + j] = (int32_t)pos;
+                    ++used;
+                }
+            }
+            for (int64_t i = used; i < aligned_per_expert[e]; ++i) { /* padding */
+                const int64_t pos = offset + i;
+                if (pos >= grouped_capacity) break;
+                memset(grouped_x + pos * row_bytes, 0, (size_t)row_bytes);
+                for (int32_t s = 0; s < num_scales; ++s) grouped_x_scales[pos * num_scales + s] = 0.0f;
+                grouped_row[pos] = -1;
+                grouped_weights[pos] = 0.0f;
+            }
+            offset += aligned_per_expert[e];
+        }
+    }
+    *num_grouped_rows = (int32_t)offset;
     return status;
 }

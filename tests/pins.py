@@ -441,6 +441,137 @@ def pin_fp8_and_cached(o, inputs: dict, hidden: int | None = None) -> list[str]:
     return errs
 
 
+def pin_golden_grouping(o) -> list[str]:
+    """The grouping of the hand-worked example, at alignment 2 and 1 (values
+    derived by hand in golden/worked_example.md)."""
+    g = json.load(open(GOLDEN))
+    s, exp = g["shape"], g["expected"]
+    K, E = s["topk"], s["experts"]
+    idx = np.array(exp["recv_topk_idx"], np.int64)
+    w = np.array(exp["recv_topk_weights"], np.float32)
+    n = exp["num_recv_tokens"]
+    rows = np.arange(n * 8, dtype=np.int16).reshape(n, 8)  # row s holds 8s .. 8s+7
+    errs: list[str] = []
+    for align, key in ((2, "alignment_2"), (1, "alignment_1")):
+        want = exp["grouping"][key]
+        aligned = [(c + align - 1) // align * align for c in exp["num_tokens_per_expert"]]
+        got = o.group_by_expert(rows, idx, w, exp["recv_gbl_rank_prefix_sum"], aligned, E)
+        _eq(f"{key}: num_grouped_rows", got["num_grouped_rows"], want["num_grouped_rows"], errs)
+        _eq(f"{key}: grouped_row", got["grouped_row"], want["grouped_row"], errs)
+        _eq(f"{key}: grouped_weights", got["grouped_weights"], want["grouped_weights"], errs)
+        _eq(f"{key}: slot_pos", got["slot_pos"], want["slot_pos"], errs)
+        gr = np.array(want["grouped_row"])
+        want_x = np.where(gr[:, None] >= 0, rows[np.maximum(gr, 0)], 0)
+        _eq(f"{key}: grouped_x", got["grouped_x"], want_x, errs)
+        if got["status"] != 0:
+            errs.append(f"{key}: status {got['status']}")
+    return errs
+
+
+def _grouping_by_sorting(idx, gbl, aligned, er, num_rows, cap):
+    """Second formulation of the grouping: list every (expert, row, slot) with
+    a valid local id, sort the triples with Python's sort, and lay the segments
+    out at the running sums of the aligned sizes."""
+    triples = []
+    lo = 0
+    for r, hi in enumerate(gbl):
+        for row in range(lo, min(int(hi), num_rows)):
+            for j, le in enumerate(idx[row]):
+                if 0 <= le < er:
+                    triples.append((r * er + int(le), row, j))
+        lo = min(int(hi), num_rows)
+    triples.sort()
+    start = np.concatenate([[0], np.cumsum(aligned)])
+    grow = np.full(cap, -2, np.int64)
+    pos = np.full(idx.shape, -1, np.int64)
+    seen = Counter()
+    overflow = False
+    for e, row, j in triples:
+        i = seen[e]
+        seen[e] += 1
+        p = start[e] + i
+        if i >= aligned[e] or p >= cap:
+            overflow = True
+            continue
+        grow[p] = row
+        pos[row, j] = p
+    for e in range(len(aligned)):
+        for i in range(seen[e], aligned[e]):
+            if start[e] + i < cap:
+                grow[start[e] + i] = -1
+    return grow, pos, int(start[-1]), overflow
+
+
+def pin_group_by_expert(o, inputs: dict, align: int, hidden: int | None = None) -> list[str]:
+    """Grouping on a workload's real routing: equal to the sorting formulation;
+    each segment's entries are exactly the source tokens that chose that
+    expert (read back through src_info and the source topk ids), rows
+    ascending; sizes equal the layout's per-expert counts; padding is zero;
+    then a short grouped capacity and a too-small segment size are flagged."""
+    wl = inputs["workload"]
+    x = inputs["x"] if hidden is None else np.ascontiguousarray(inputs["x"][:, :hidden])
+    idx, w = inputs["topk_idx"], inputs["topk_weights"]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    er = E // R
+    errs: list[str] = []
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, align)
+    dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                     note["recv_gbl_rank_prefix_sum"], E)
+    n = note["num_recv_tokens"]
+    aligned = note["num_recv_tokens_per_expert"].astype(np.int64)
+    ridx, rw = dis["recv_topk_idx"][:n], dis["recv_topk_weights"][:n]
+    got = o.group_by_expert(dis["recv_x"][:n], ridx, rw, note["recv_gbl_rank_prefix_sum"], aligned, E)
+    m = int(aligned.sum())
+    grow, pos, m2, _ = _grouping_by_sorting(ridx, note["recv_gbl_rank_prefix_sum"], aligned, er, n, m)
+    if got["num_grouped_rows"] != m or m2 != m:
+        errs.append("num_grouped_rows != sum of the aligned counts")
+    if not np.array_equal(got["grouped_row"], grow) or not np.array_equal(got["slot_pos"], pos):
+        errs.append("grouping differs from the sorting formulation")
+    live = grow >= 0
+    if not np.array_equal(got["grouped_x"][live], dis["recv_x"][grow[live]]) or np.any(got["grouped_x"][~live] != 0):
+        errs.append("grouped_x rows wrong or padding not zero")
+    rr, jj = np.nonzero(pos >= 0)
+    if not np.array_equal(got["grouped_weights"][pos[rr, jj]], rw[rr, jj]) or np.any(got["grouped_weights"][~live] != 0):
+        errs.append("grouped weights wrong")
+    # source side: segment e holds, rows ascending, one entry per source slot (t, j) with topk_idx == e
+    start = np.concatenate([[0], np.cumsum(aligned)])
+    src_t = dis["recv_src_info"][:, 1]
+    for e in range(E):
+        seg = got["grouped_row"][start[e]:start[e + 1]]
+        ent = seg[seg >= 0]
+        if len(ent) != lay["num_tokens_per_expert"][e]:
+            errs.append(f"expert {e}: {len(ent)} entries, layout counted {lay['num_tokens_per_expert'][e]}")
+            break
+        if np.any(np.diff(ent) < 0):
+            errs.append(f"expert {e}: rows not ascending")
+            break
+        want_t = Counter(int(t) for t in np.nonzero(idx == e)[0])
+        if Counter(int(src_t[r]) for r in ent) != want_t:
+            errs.append(f"expert {e}: source tokens differ from the tokens that chose it")
+            break
+        if len(ent) and not np.all((ent >= (note["recv_gbl_rank_prefix_sum"][e // er - 1] if e // er else 0))
+                                   & (ent < note["recv_gbl_rank_prefix_sum"][e // er])):
+            errs.append(f"expert {e}: an entry outside slab {e // er}")
+            break
+    if got["status"] != 0:
+        errs.append(f"status {got['status']}")
+    # a short grouped capacity and one segment sized too small: flagged, the rest as the formulation says
+    small = aligned.copy()
+    e_big = int(np.argmax(lay["num_tokens_per_expert"]))
+    small[e_big] = max(0, small[e_big] - align - 1)
+    cap = int(small.sum()) - 3
+    got = o.group_by_expert(dis["recv_x"][:n], ridx, rw, note["recv_gbl_rank_prefix_sum"], small, E,
+                            grouped_capacity=cap)
+    grow, pos, _, over = _grouping_by_sorting(ridx, note["recv_gbl_rank_prefix_sum"], small, er, n, cap)
+    if not over or got["status"] != 2:
+        errs.append(f"overflow not flagged (status {got['status']})")
+    if not np.array_equal(got["grouped_row"], grow) or not np.array_equal(got["slot_pos"], pos):
+        errs.append("grouping with overflow differs from the sorting formulation")
+    return errs
+
+
 def expected_ranks_per_token(E: int, R: int, K: int) -> float:
     """Closed form for uniform routing without replacement: R*(1 - C(E-E/R, K)/C(E, K))."""
     er = E // R

@@ -61,6 +61,16 @@ MUTANTS = {
                                 "memcpy(recv_x + s * row_bytes, x + (t > 0 ? t - 1 : t) * row_bytes, (size_t)row_bytes);"),
     "cached_bad_slot_not_flagged": ("                status |= ORC_BAD_SEND_SLOT;\n                continue;\n            }\n            memcpy(recv_x",
                                     "                continue;\n            }\n            memcpy(recv_x"),
+    "group_slot_major_order": ("for (int64_t row = lo; row < hi; ++row) {\n                for (int32_t j = 0; j < K; ++j) {",
+                               "for (int32_t j = 0; j < K; ++j) {\n                for (int64_t row = lo; row < hi; ++row) {"),
+    "group_offsets_unaligned": ("offset += aligned_per_expert[e];", "offset += used;"),
+    "group_local_id_as_global": ("if (recv_topk_idx[row * K + j] != le) continue;",
+                                 "if (recv_topk_idx[row * K + j] != e) continue;"),
+    "group_padding_row_not_marked": ("grouped_row[pos] = -1;", "grouped_row[pos] = 0;"),
+    "group_weight_of_slot0": ("grouped_weights[pos] = recv_topk_weights[row * K + j];",
+                              "grouped_weights[pos] = recv_topk_weights[row * K];"),
+    "group_segment_bound_ignored": ("if (used >= aligned_per_expert[e] || pos >= grouped_capacity) {",
+                                    "if (pos >= grouped_capacity) {"),
 }
 
 CHILD = textwrap.dedent("""
@@ -72,6 +82,8 @@ CHILD = textwrap.dedent("""
     errs = pins.pin_golden(o) + pins.pin_bf16_rounding(o) + pins.pin_workload(o, inputs.generate("tiny"))
     errs += pins.pin_workload(o, inputs.generate("sweep"), hidden=64)
     errs += pins.pin_fp8_and_cached(o, inputs.generate("tiny"))
+    errs += pins.pin_golden_grouping(o) + pins.pin_group_by_expert(o, inputs.generate("tiny"), 4)
+    errs += pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32)
     if not errs:
         errs += pins.pin_bruteforce(o)
     print("CAUGHT" if errs else "MISSED", errs[:2])

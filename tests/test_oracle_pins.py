@@ -129,3 +129,13 @@ def test_edge_receive_capacity_overflow(orc, workload_inputs):
 def test_fp8_and_cached_dispatch(orc, workload_inputs, name):
     assert pins.pin_fp8_and_cached(orc, workload_inputs(name), hidden=None if name == "tiny" else 512) == []
 
+
+
+def test_golden_grouping(orc):
+    assert pins.pin_golden_grouping(orc) == []
+
+
+@pytest.mark.parametrize("name,align", [("tiny", 1), ("tiny", 4), ("sweep", 128), ("skew", 4), ("prefill", 1),
+                                        ("large", 8)])
+def test_group_by_expert(orc, workload_inputs, name, align):
+    assert pins.pin_group_by_expert(orc, workload_inputs(name), align, hidden=None if name == "tiny" else 32) == []
