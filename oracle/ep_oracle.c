@@ -414,7 +414,7 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
     }
     int64_t offset = 0; /* start of segment e */
     for (int32_t r = 0; r < R; ++r) {
-        int64_t lo = r > 0 ? recv_gbl_rank_prefix_sum[r - 1] : 0;
+        int64_t lo = (r == 0) ? 0 : recv_gbl_rank_prefix_sum[r - 1]; /* slab r */
         int64_t hi = recv_gbl_rank_prefix_sum[r];
         if (hi > num_recv_rows) hi = num_recv_rows;
         if (lo > hi) lo = hi;

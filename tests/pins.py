@@ -561,7 +561,7 @@ def pin_group_by_expert(o, inputs: dict, align: int, hidden: int | None = None) 
     small = aligned.copy()
     e_big = int(np.argmax(lay["num_tokens_per_expert"]))
     small[e_big] = max(0, small[e_big] - align - 1)
-    cap = int(small.sum()) - 3
+    cap = max(0, int(small.sum()) - 3)
     got = o.group_by_expert(dis["recv_x"][:n], ridx, rw, note["recv_gbl_rank_prefix_sum"], small, E,
                             grouped_capacity=cap)
     grow, pos, _, over = _grouping_by_sorting(ridx, note["recv_gbl_rank_prefix_sum"], small, er, n, cap)

@@ -79,13 +79,18 @@ CHILD = textwrap.dedent("""
     import oracle, pins
     from combine_ep_get_02_amd import inputs
     o = oracle.Oracle(oracle.load({lib!r}))
-    errs = pins.pin_golden(o) + pins.pin_bf16_rounding(o) + pins.pin_workload(o, inputs.generate("tiny"))
-    errs += pins.pin_workload(o, inputs.generate("sweep"), hidden=64)
-    errs += pins.pin_fp8_and_cached(o, inputs.generate("tiny"))
-    errs += pins.pin_golden_grouping(o) + pins.pin_group_by_expert(o, inputs.generate("tiny"), 4)
-    errs += pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32)
-    if not errs:
-        errs += pins.pin_bruteforce(o)
+    checks = [lambda: pins.pin_golden(o), lambda: pins.pin_bf16_rounding(o),
+              lambda: pins.pin_workload(o, inputs.generate("tiny")),
+              lambda: pins.pin_workload(o, inputs.generate("sweep"), hidden=64),
+              lambda: pins.pin_fp8_and_cached(o, inputs.generate("tiny")),
+              lambda: pins.pin_golden_grouping(o), lambda: pins.pin_group_by_expert(o, inputs.generate("tiny"), 4),
+              lambda: pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32),
+              lambda: pins.pin_bruteforce(o)]
+    errs = []
+    for check in checks:  # in order, stopping at the first pin that fails
+        errs = check()
+        if errs:
+            break
     print("CAUGHT" if errs else "MISSED", errs[:2])
 """)
 
