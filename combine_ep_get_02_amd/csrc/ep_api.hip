@@ -192,6 +192,51 @@ ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_
     return from_hip(launch_dispatch(*s, a, stream));
 }
 
+ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t elem_bytes,
+                               const float *recv_x_scales, int32_t num_scales, const int64_t *recv_topk_idx,
+                               const float *recv_topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                               const int32_t *num_recv_tokens_per_expert, int32_t num_recv_rows,
+                               int32_t grouped_capacity, void *grouped_x, float *grouped_x_scales,
+                               int32_t *grouped_row, float *grouped_weights, int32_t *slot_pos,
+                               int32_t *num_grouped_rows, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (elem_bytes != 1 && elem_bytes != 2) return EP_ERR_INVALID_ARG;
+    const int64_t row_bytes = (int64_t)s->hidden * elem_bytes;
+    if (row_bytes % 16 != 0 || num_recv_rows < 0 || grouped_capacity < 0 || num_scales < 0) return EP_ERR_INVALID_ARG;
+    if (num_scales > kMaxScales || s->num_experts / s->num_ranks > kMaxGroupExperts) return EP_ERR_UNSUPPORTED;
+    if ((int64_t)num_recv_rows * s->num_topk > INT32_MAX) return EP_ERR_UNSUPPORTED;
+    if (recv_gbl_rank_prefix_sum == nullptr || num_recv_tokens_per_expert == nullptr || num_grouped_rows == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (num_recv_rows > 0 && (recv_x == nullptr || recv_topk_idx == nullptr)) return EP_ERR_INVALID_ARG;
+    if (grouped_capacity > 0 && (grouped_x == nullptr || grouped_row == nullptr)) return EP_ERR_INVALID_ARG;
+    if (grouped_weights != nullptr && num_recv_rows > 0 && recv_topk_weights == nullptr) return EP_ERR_INVALID_ARG;
+    if (num_scales > 0 && ((num_recv_rows > 0 && recv_x_scales == nullptr) ||
+                           (grouped_capacity > 0 && grouped_x_scales == nullptr)))
+        return EP_ERR_INVALID_ARG;
+    if ((recv_x != nullptr && !aligned16(recv_x)) || (grouped_x != nullptr && !aligned16(grouped_x)))
+        return EP_ERR_INVALID_ARG;
+    GroupArgs a = {};
+    a.recv_x = recv_x;
+    a.row_units = row_bytes / 16;
+    a.recv_scales = recv_x_scales;
+    a.num_scales = num_scales;
+    a.recv_idx = recv_topk_idx;
+    a.recv_w = recv_topk_weights;
+    a.recv_gbl = recv_gbl_rank_prefix_sum;
+    a.aligned = num_recv_tokens_per_expert;
+    a.num_rows = num_recv_rows;
+    a.cap = grouped_capacity;
+    a.grouped_x = grouped_x;
+    a.grouped_scales = grouped_x_scales;
+    a.grouped_row = grouped_row;
+    a.grouped_w = grouped_weights;
+    a.slot_pos = slot_pos;
+    a.num_grouped = num_grouped_rows;
+    a.dev_status = dev_status;
+    return from_hip(launch_group(*s, a, stream));
+}
+
 ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_topk_weights, const int32_t *send_slot,
                        int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
                        hipStream_t stream) {

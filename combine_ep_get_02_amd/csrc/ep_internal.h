@@ -91,6 +91,31 @@ struct DispatchArgs {
 
 hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream);
 
+// Arguments of the grouping by local expert (one launch computing positions,
+// one copying rows).  Rows are row_units 16-byte units.
+struct GroupArgs {
+    const void *recv_x;
+    int64_t row_units;
+    const float *recv_scales;  // [N][num_scales], null when num_scales == 0
+    int num_scales;
+    const int64_t *recv_idx;   // [N][k] local expert ids
+    const float *recv_w;       // [N][k], may be null
+    const int32_t *recv_gbl;   // [R] inclusive slab ends
+    const int32_t *aligned;    // [E] segment sizes
+    int32_t num_rows;          // N
+    int32_t cap;               // grouped rows allocated
+    void *grouped_x;
+    float *grouped_scales;
+    int32_t *grouped_row;      // [cap]
+    float *grouped_w;          // [cap], may be null
+    int32_t *slot_pos;         // [N][k], may be null
+    int32_t *num_grouped;      // [1]
+    int32_t *dev_status;
+};
+constexpr int kMaxGroupExperts = 512;  // local experts per rank the grouping supports
+
+hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t stream);
+
 hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv_w, const int32_t *send_slot,
                           int32_t num_recv_rows, uint4 *combined_x, float *combined_w, int32_t *dev_status,
                           hipStream_t stream);

@@ -20,8 +20,8 @@ LIBRARY = os.path.join(_PKG, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
 EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
 
-EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached", "ep_combine",
-            "ep_workspace_bytes", "ep_status_string")
+EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
+            "ep_group_by_expert", "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
 class EpError(RuntimeError):
@@ -55,9 +55,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + \
         [_P] * 8
     lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
+    lib.ep_group_by_expert.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
+                                       ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
     for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-                 "ep_combine"):
+                 "ep_group_by_expert", "ep_combine"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -154,6 +156,19 @@ def ep_dispatch_cached(shape, x, elem_bytes, x_scales, num_scales, send_slot, re
                                      _ptr(dev_status), _stream(stream)), "ep_dispatch_cached")
 
 
+def ep_group_by_expert(shape, recv_x, elem_bytes, recv_x_scales, num_scales, recv_topk_idx, recv_topk_weights,
+                       recv_gbl_rank_prefix_sum, num_recv_tokens_per_expert, num_recv_rows, grouped_capacity,
+                       grouped_x, grouped_x_scales, grouped_row, grouped_weights, slot_pos, num_grouped_rows,
+                       dev_status=None, stream=None) -> None:
+    _check(load().ep_group_by_expert(ctypes.byref(shape), _ptr(recv_x), int(elem_bytes), _ptr(recv_x_scales),
+                                     int(num_scales), _ptr(recv_topk_idx), _ptr(recv_topk_weights),
+                                     _ptr(recv_gbl_rank_prefix_sum), _ptr(num_recv_tokens_per_expert),
+                                     int(num_recv_rows), int(grouped_capacity), _ptr(grouped_x),
+                                     _ptr(grouped_x_scales), _ptr(grouped_row), _ptr(grouped_weights), _ptr(slot_pos),
+                                     _ptr(num_grouped_rows), _ptr(dev_status), _stream(stream)),
+           "ep_group_by_expert")
+
+
 def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x, combined_topk_weights=None,
                dev_status=None, stream=None) -> None:
     _check(load().ep_combine(ctypes.byref(shape), _ptr(y), _ptr(recv_topk_weights), _ptr(send_slot),
@@ -229,3 +244,30 @@ def run_combine(b: Buffers, y=None, num_recv_rows=None, with_weights: bool = Tru
     ep_combine(b.shape, b.recv_x if y is None else y, b.recv_w, b.send_slot,
                b.capacity if num_recv_rows is None else num_recv_rows, b.combined_x,
                b.combined_w if with_weights else None, b.dev_status, stream)
+
+
+@dataclass
+class GroupBuffers:
+    """Outputs of the grouping by local expert for `capacity` grouped rows."""
+    capacity: int
+    grouped_x: torch.Tensor
+    grouped_row: torch.Tensor
+    grouped_w: torch.Tensor
+    slot_pos: torch.Tensor
+    num_grouped: torch.Tensor
+
+
+def allocate_group(b: Buffers, capacity: int, device="cuda") -> GroupBuffers:
+    """capacity: grouped rows, normally the sum of b.recv_per_expert after notify."""
+    cap = max(int(capacity), 0)
+    i32 = dict(dtype=torch.int32, device=device)
+    return GroupBuffers(capacity=cap,
+                        grouped_x=torch.empty((cap, b.shape.hidden), dtype=torch.bfloat16, device=device),
+                        grouped_row=torch.empty(cap, **i32), grouped_w=torch.empty(cap, dtype=torch.float32, device=device),
+                        slot_pos=torch.empty((b.capacity, b.shape.num_topk), **i32), num_grouped=torch.empty(1, **i32))
+
+
+def run_group(b: Buffers, g: GroupBuffers, num_recv_rows=None, stream=None) -> None:
+    ep_group_by_expert(b.shape, b.recv_x, 2, None, 0, b.recv_idx, b.recv_w, b.recv_gbl, b.recv_per_expert,
+                       b.capacity if num_recv_rows is None else num_recv_rows, g.capacity, g.grouped_x, None,
+                       g.grouped_row, g.grouped_w, g.slot_pos, g.num_grouped, b.dev_status, stream)

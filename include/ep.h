@@ -176,6 +176,43 @@ ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_
                                float *recv_x_scales, int32_t *dev_status, hipStream_t stream);
 
 /*
+ * Grouping of the received rows by local expert, the layout grouped expert GEMMs read.
+ * [DeepEP internode.cu notes, notify_dispatch sm0 stage 6, and mscclpp ht_runtime.cc,
+ * internodeNotifyDispatch: per local expert, the received slot count rounded up to
+ * expert_alignment -- the sizes below.  The order inside the segments is this library's
+ * reading; the pages do not show one.]
+ * Segment e = r*(E/R) + le (slab r of the receive region, local expert le) starts at
+ * sum_{e' < e} num_recv_tokens_per_expert[e'] and holds one entry per (row, slot) of slab r
+ * with recv_topk_idx[row][slot] == le, rows ascending, then slots; the rest of the segment,
+ * up to num_recv_tokens_per_expert[e], is padding.  For the entry at grouped position g:
+ *   grouped_x        [cap][h] (elem_bytes 2 = bf16, 1 = fp8; h*elem_bytes % 16 == 0):
+ *                    recv_x[row] bit for bit; padding rows are zero
+ *   grouped_x_scales [cap][num_scales] f32: the row's scales, padding 0 (nullable if
+ *                    num_scales == 0; 0 <= num_scales <= 1024)
+ *   grouped_row      [cap] int32: row; padding -1
+ *   grouped_weights  [cap] f32 (nullable): recv_topk_weights[row][slot]; padding 0
+ *   slot_pos         [num_recv_rows][k] int32 (nullable): g of each placed (row, slot), else -1
+ *   num_grouped_rows [1] int32 (device): sum of the segment sizes
+ * Positions at or past min(num_grouped_rows, grouped_capacity) are not written.
+ * In:  recv_x [num_recv_rows][h], recv_x_scales [num_recv_rows][num_scales],
+ *      recv_topk_idx [num_recv_rows][k] and recv_topk_weights (nullable unless
+ *      grouped_weights is given and num_recv_rows > 0) as ep_dispatch / ep_dispatch_fp8 wrote them;
+ *      recv_gbl_rank_prefix_sum [R] and num_recv_tokens_per_expert [E] as ep_notify wrote
+ *      them (slab ends non-decreasing; a negative size counts as 0).
+ * dev_status (nullable): EP_DEV_RECV_OVERFLOW (an entry past its segment's size or the
+ * grouped capacity: skipped, slot_pos -1), EP_DEV_BAD_TOPK_IDX (a local id outside
+ * [-1, E/R): skipped).  E/R > 512 or num_recv_rows * k >= 2^31: EP_ERR_UNSUPPORTED.
+ * Two launches (positions, then the row copy); no workspace.
+ */
+ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t elem_bytes,
+                               const float *recv_x_scales, int32_t num_scales, const int64_t *recv_topk_idx,
+                               const float *recv_topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                               const int32_t *num_recv_tokens_per_expert, int32_t num_recv_rows,
+                               int32_t grouped_capacity, void *grouped_x, float *grouped_x_scales,
+                               int32_t *grouped_row, float *grouped_weights, int32_t *slot_pos,
+                               int32_t *num_grouped_rows, int32_t *dev_status, hipStream_t stream);
+
+/*
  * Stage 5, combine.  [mscclpp ht_runtime.cc, internodeCombine / intranodeCombine (bf16 out,
  * combined topk weights); CUDA与DeepEP article 4.2 (rows return to their source token)]
  * For each token t, over ranks r ascending with s = send_slot[t][r] >= 0:

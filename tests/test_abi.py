@@ -32,7 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8",
-                                          "ep_dispatch_cached", "ep_combine", "ep_workspace_bytes",
+                                          "ep_dispatch_cached", "ep_group_by_expert", "ep_combine",
+                                          "ep_workspace_bytes",
                                           "ep_status_string"])
 
 
@@ -90,18 +91,19 @@ def _call_all(ep, s):
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
         lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None, None),
         lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, None, None),
+        lib.ep_group_by_expert(ctypes.byref(s), p, 2, None, 0, p, p, p, p, 10, 10, p, None, p, p, p, p, None, None),
     ]
     return codes
 
 
 @pytest.mark.parametrize("name", sorted(BAD_SHAPES))
 def test_malformed_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 6
+    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 7
 
 
 @pytest.mark.parametrize("name", sorted(UNSUPPORTED))
 def test_unsupported_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 6
+    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 7
 
 
 def test_null_and_misaligned_pointers_rejected(ep):
@@ -141,6 +143,35 @@ def test_fp8_and_cached_argument_checks(ep):
                                   None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_dispatch_cached(ctypes.byref(s12), p, 1, None, 0, p, 10, p, None, None,
                                   None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_group_by_expert_argument_checks(ep):
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(264)
+    s = _shape(ep)
+
+    def group(shape=s, recv_x=p, elem=2, scales=None, ns=0, idx=p, w=p, gbl=p, aligned=p, rows=10, cap=10,
+              gx=p, gscales=None, grow=p, gw=p, pos=p, m=p):
+        return lib.ep_group_by_expert(ctypes.byref(shape), recv_x, elem, scales, ns, idx, w, gbl, aligned, rows, cap,
+                                      gx, gscales, grow, gw, pos, m, None, None)
+
+    assert group(elem=3) == ep.EP_ERR_INVALID_ARG
+    assert group(shape=_shape(ep, hidden=7160), elem=1) == ep.EP_ERR_INVALID_ARG  # not whole 16-byte units
+    assert group(rows=-1) == ep.EP_ERR_INVALID_ARG
+    assert group(cap=-1) == ep.EP_ERR_INVALID_ARG
+    assert group(m=None) == ep.EP_ERR_INVALID_ARG  # num_grouped_rows is required
+    assert group(gbl=None) == ep.EP_ERR_INVALID_ARG
+    assert group(aligned=None) == ep.EP_ERR_INVALID_ARG
+    assert group(idx=None) == ep.EP_ERR_INVALID_ARG
+    assert group(grow=None) == ep.EP_ERR_INVALID_ARG
+    assert group(w=None) == ep.EP_ERR_INVALID_ARG  # grouped weights need the receive weights
+    assert group(ns=4) == ep.EP_ERR_INVALID_ARG  # scales missing
+    assert group(gx=odd) == ep.EP_ERR_INVALID_ARG
+    assert group(recv_x=odd) == ep.EP_ERR_INVALID_ARG
+    assert group(ns=2000, scales=p, gscales=p) == ep.EP_ERR_UNSUPPORTED
+    assert group(shape=_shape(ep, num_experts=1024, num_ranks=1)) == ep.EP_ERR_UNSUPPORTED  # 1024 local experts
+    assert group(rows=(1 << 31) // 8) == ep.EP_ERR_UNSUPPORTED  # rows * k reaches 2^31
 
 
 def test_empty_dispatch_and_combine_enqueue_nothing(ep):

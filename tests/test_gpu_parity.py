@@ -290,3 +290,152 @@ def test_cached_dispatch_bad_slots_bf16():
     ref = oracle.Oracle().dispatch_cached(x, slot, cap)
     assert np.array_equal(H.bf16_host(out), ref["recv_x"])
     assert int(st.item()) == 8 and ref["status"] == 8
+
+
+def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0, bad_ids=False, extra_rows=0,
+                optional=True):
+    """Both sides run layout, notify, dispatch (bf16 or fp8 rows) and then the
+    grouping by local expert, from the same inputs; the same host-side edits
+    (a segment size shrunk, bad local ids, rows past the last slab) are made
+    on both.  Returns (gpu, ref) dicts of the grouping outputs."""
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+    from combine_ep_get_02_amd.inputs import fp8_rows
+
+    T, K = idx.shape
+    er = E // R
+    xs, sc = (fp8_rows(x) if fp8 else (x, None))
+    NS = 0 if sc is None else sc.shape[1]
+    Hd = xs.shape[1]
+    o = oracle.Oracle()
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, align)
+    n = note["num_recv_tokens"]
+    rows = n + extra_rows
+    args = (idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], E)
+    d = o.dispatch_fp8(xs, sc, *args, recv_capacity=rows) if fp8 else o.dispatch(xs, *args, recv_capacity=rows)
+    aligned = note["num_recv_tokens_per_expert"].astype(np.int32).copy()
+    e_big = int(np.argmax(aligned)) if E else 0
+    if shrink:
+        aligned[e_big] -= align + 1
+    r_idx, r_x = d["recv_topk_idx"].copy(), d["recv_x"].copy()
+    r_w = d["recv_topk_weights"]
+    if extra_rows:
+        r_idx[n:] = min(1, er - 1)
+        r_x[n:] = 0
+    if bad_ids and n > 1:
+        r_idx[0, 0] = er + 3
+        r_idx[min(5, n - 1), K - 1] = -5
+    cap = max(int(np.maximum(aligned, 0).sum()) + cap_delta, 0)
+    ref = o.group_by_expert(r_x, r_idx, r_w, note["recv_gbl_rank_prefix_sum"], aligned, E, grouped_capacity=cap,
+                            recv_x_scales=d["recv_x_scales"] if fp8 else None)
+
+    shape = ep.make_shape(T, x.shape[1], K, E, R, C, 0, align)
+    b = ep.allocate(shape, rows)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    ep.run_notify(b)
+    if fp8:
+        rx = torch.zeros((max(rows, 1), Hd), dtype=torch.uint8, device="cuda")
+        rs = torch.zeros((max(rows, 1), NS), dtype=torch.float32, device="cuda")
+        ep.ep_dispatch_fp8(shape, torch.from_numpy(xs).cuda(), torch.from_numpy(sc).cuda(), NS, didx, dw, b.recv_gbl,
+                           b.workspace, rows, rx, rs, b.recv_w, b.recv_idx, b.src_info, b.send_slot, b.dev_status)
+    else:
+        rx = b.recv_x
+        rx[n:].zero_()
+        rs = None
+        ep.run_dispatch(b, torch.from_numpy(np.ascontiguousarray(xs).view(np.int16)).cuda().view(torch.bfloat16),
+                        didx, dw)
+    g_aligned = b.recv_per_expert.clone()
+    if shrink:
+        g_aligned[e_big] -= align + 1
+    if extra_rows:
+        b.recv_idx[n:] = min(1, er - 1)
+    if bad_ids and n > 1:
+        b.recv_idx[0, 0] = er + 3
+        b.recv_idx[min(5, n - 1), K - 1] = -5
+    elem = 1 if fp8 else 2
+    gx = torch.full((max(cap, 1), Hd * elem), 0x5A, dtype=torch.uint8, device="cuda")
+    gs = torch.full((max(cap, 1), max(NS, 1)), -9.0, dtype=torch.float32, device="cuda")
+    grow = torch.full((max(cap, 1),), -777, dtype=torch.int32, device="cuda")
+    gw = torch.full((max(cap, 1),), -9.0, dtype=torch.float32, device="cuda")
+    pos = torch.full((max(rows, 1), K), -777, dtype=torch.int32, device="cuda")
+    m = torch.full((1,), -777, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_group_by_expert(shape, rx, elem, rs, NS, b.recv_idx, b.recv_w, b.recv_gbl, g_aligned, rows, cap, gx,
+                          gs if NS else None, grow, gw if optional else None, pos if optional else None, m, st)
+    torch.cuda.synchronize()
+    mm = min(ref["num_grouped_rows"], cap)
+    gpu = dict(num_grouped_rows=int(m.item()), grouped_x=gx[:mm].cpu().numpy().view(r_x.dtype),
+               grouped_row=grow[:mm].cpu().numpy(), status=int(st.item()),
+               untouched=bool((grow[mm:cap] == -777).all().item()) and bool((gx[mm:cap] == 0x5A).all().item()))
+    want = dict(num_grouped_rows=ref["num_grouped_rows"], grouped_x=ref["grouped_x"][:mm],
+                grouped_row=ref["grouped_row"][:mm], status=ref["status"], untouched=True)
+    if optional:
+        gpu["grouped_weights"] = gw[:mm].cpu().numpy()
+        gpu["slot_pos"] = pos[:rows].cpu().numpy()
+        want["grouped_weights"] = ref["grouped_weights"][:mm]
+        want["slot_pos"] = ref["slot_pos"]
+    if NS:
+        gpu["grouped_x_scales"] = gs[:mm].cpu().numpy()
+        want["grouped_x_scales"] = ref["grouped_x_scales"][:mm]
+    return gpu, want
+
+
+def _group_diff(gpu, want):
+    bad = [k for k in ("num_grouped_rows", "status", "untouched") if gpu[k] != want[k]]
+    return bad + _exact({k: v for k, v in gpu.items() if k not in bad},
+                        {k: v for k, v in want.items() if k not in ("num_grouped_rows", "status", "untouched")})
+
+
+@pytest.mark.parametrize("name,align", [("tiny", 4), ("sweep", 128), ("prefill", 1), ("skew", 4), ("large", 8)])
+def test_group_by_expert_parity(name, align):
+    print(f"[parity] group_by_expert workload={name} align={align}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    gpu, want = _group_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels, align)
+    assert _group_diff(gpu, want) == []
+    assert want["status"] == 0
+
+
+def test_group_fp8_rows_with_scales():
+    print("[parity] group_by_expert fp8 rows, sweep", flush=True)
+    d = generate("sweep")
+    wl = d["workload"]
+    gpu, want = _group_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels, 2, fp8=True)
+    assert _group_diff(gpu, want) == []
+
+
+def test_group_overflow_bad_ids_and_rows_past_the_slabs():
+    print("[parity] group_by_expert overflow / bad ids / extra rows", flush=True)
+    x, idx, w = _random_case(600, 8, 64, 6, 5, 256, seed=31, mask_frac=0.1)
+    gpu, want = _group_case(x, idx, w, 64, 8, 5, 4, shrink=True, cap_delta=-7, bad_ids=True, extra_rows=3)
+    assert _group_diff(gpu, want) == []
+    assert want["status"] == 3  # overflow and bad ids, both flagged
+
+
+def test_group_512_local_experts_k32_duplicates():
+    print("[parity] group_by_expert 512 local experts, k=32", flush=True)
+    x, idx, w = _random_case(300, 2, 1024, 32, 3, 64, seed=32, mask_frac=0.2, dup=True)
+    gpu, want = _group_case(x, idx, w, 1024, 2, 3, 2)
+    assert _group_diff(gpu, want) == []
+
+
+def test_group_without_optional_outputs():
+    print("[parity] group_by_expert no weights / slot_pos", flush=True)
+    d = generate("tiny")
+    wl = d["workload"]
+    gpu, want = _group_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels, 3,
+                            optional=False)
+    assert _group_diff(gpu, want) == []
+
+
+def test_group_no_rows():
+    print("[parity] group_by_expert with no received rows", flush=True)
+    x, idx, w = _random_case(40, 8, 16, 2, 4, 64, seed=33, mask_frac=1.0)
+    gpu, want = _group_case(x, idx, w, 16, 8, 4, 4)
+    assert _group_diff(gpu, want) == [] and gpu["num_grouped_rows"] == 0

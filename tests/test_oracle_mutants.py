@@ -63,13 +63,13 @@ MUTANTS = {
                                     "                continue;\n            }\n            memcpy(recv_x"),
     "group_slot_major_order": ("for (int64_t row = lo; row < hi; ++row) {\n                for (int32_t j = 0; j < K; ++j) {",
                                "for (int32_t j = 0; j < K; ++j) {\n                for (int64_t row = lo; row < hi; ++row) {"),
-    "group_offsets_unaligned": ("offset += aligned_per_expert[e];", "offset += used;"),
+    "group_offsets_unaligned": ("offset += size;", "offset += used;"),
     "group_local_id_as_global": ("if (recv_topk_idx[row * K + j] != le) continue;",
                                  "if (recv_topk_idx[row * K + j] != e) continue;"),
     "group_padding_row_not_marked": ("grouped_row[pos] = -1;", "grouped_row[pos] = 0;"),
     "group_weight_of_slot0": ("grouped_weights[pos] = recv_topk_weights[row * K + j];",
                               "grouped_weights[pos] = recv_topk_weights[row * K];"),
-    "group_segment_bound_ignored": ("if (used >= aligned_per_expert[e] || pos >= grouped_capacity) {",
+    "group_segment_bound_ignored": ("if (used >= size || pos >= grouped_capacity) {",
                                     "if (pos >= grouped_capacity) {"),
 }
 
