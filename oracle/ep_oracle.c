@@ -397,9 +397,10 @@ int oracle_combine_f64(int32_t T, int32_t H, int32_t K, int32_t R, int32_t num_r
  *   grouped_x[pos] = recv_x[row] (bitwise, with its scales), grouped_row[pos] =
  *   row, grouped_weights[pos] = recv_topk_weights[row][j], slot_pos[row][j] =
  *   pos (-1 for slots with no entry).  *num_grouped_rows = sum_e aligned[e].
- * Rows at or beyond num_recv_rows are outside every slab.  An entry beyond its
- * segment's aligned size or at/after grouped_capacity is skipped with
- * ORC_RECV_OVERFLOW; a local id outside [-1, E/R) with ORC_BAD_TOPK_IDX. */
+ * Rows at or beyond num_recv_rows are outside every slab; a negative segment
+ * size counts as 0.  An entry beyond its segment's aligned size or at/after
+ * grouped_capacity is skipped with ORC_RECV_OVERFLOW; a local id outside
+ * [-1, E/R) with ORC_BAD_TOPK_IDX. */
 int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, const uint8_t *recv_x,
                            const float *recv_x_scales, int32_t num_scales, const int64_t *recv_topk_idx,
                            const float *recv_topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
@@ -420,12 +421,13 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
         if (lo > hi) lo = hi;
         for (int32_t le = 0; le < er; ++le) {
             const int32_t e = r * er + le;
+            const int64_t size = aligned_per_expert[e] > 0 ? aligned_per_expert[e] : 0;
             int64_t used = 0; /* entries placed so far in segment e */
             for (int64_t row = lo; row < hi; ++row) {
                 for (int32_t j = 0; j < K; ++j) {
                     if (recv_topk_idx[row * K + j] != le) continue;
                     const int64_t pos = offset + used;
-                    if (used >= aligned_per_expert[e] || pos >= grouped_capacity) {
+                    if (used >= size || pos >= grouped_capacity) {
                         status |= ORC_RECV_OVERFLOW;
                         continue;
                     }
@@ -438,7 +440,7 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
                     ++used;
                 }
             }
-            for (int64_t i = used; i < aligned_per_expert[e]; ++i) { /* padding */
+            for (int64_t i = used; i < size; ++i) { /* padding */
                 const int64_t pos = offset + i;
                 if (pos >= grouped_capacity) break;
                 memset(grouped_x + pos * row_bytes, 0, (size_t)row_bytes);
@@ -446,7 +448,7 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
                 grouped_row[pos] = -1;
                 grouped_weights[pos] = 0.0f;
             }
-            offset += aligned_per_expert[e];
+            offset += size;
         }
     }
     *num_grouped_rows = (int32_t)offset;
