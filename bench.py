@@ -59,6 +59,13 @@ def dispatch_cached_bytes(T, R, N, row_bytes, S) -> int:
     return T * (row_bytes + 4 * S) + 4 * T * R + N * (row_bytes + 4 * S)
 
 
+def group_bytes(H, K, N, M) -> int:
+    """every receive row read once and every grouped row (M = sum of the
+    aligned per-expert sizes) written, the receive ids (i64) and weights read,
+    the slot->position map, grouped row indices and weights written."""
+    return N * 2 * H + M * 2 * H + N * K * (8 + 4 + 4) + M * (4 + 4)
+
+
 def layout_notify_bytes(T, K, R, E, C) -> int:
     nodes = max(1, R // 8)
     return T * K * 8 + T * R + 4 * (R + nodes + E) + T * R + 4 * (R + nodes + E) + 4 * (R + nodes) * (C + 1) + 4 * E
@@ -69,6 +76,7 @@ KERNEL_SOURCES = {"dispatch_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
+                  "group_kernels": ["ep_group.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
 
@@ -241,9 +249,24 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
     out["dispatch_cached_fp8"] = rate(dispatch_cached_bytes(T, R, n_recv, H, S), mean_us(
         lambda: ep.ep_dispatch_cached(shape, x8, 1, sc, S, b.send_slot, n_recv, cx8, cs8, b.dev_status)))
     out["dispatch_cached_fp8"]["check"] = bool(torch.equal(cx8, rx) and torch.equal(cs8, rs))
+    del cx8, cs8, rx, rs, x8, sc
+
+    # grouping of the receive rows by local expert (bf16 rows of the dispatch just measured)
+    M = int(b.recv_per_expert.sum().item())
+    g = ep.allocate_group(b, M)
+    out["group_by_expert"] = rate(group_bytes(H, K, n_recv, M), mean_us(lambda: ep.run_group(b, g, n_recv)))
+    entries = g.grouped_row >= 0
+    gr = g.grouped_row[entries].long()
+    out["group_by_expert"]["check"] = bool(
+        int(g.num_grouped.item()) == M and int(entries.sum().item()) == int((idx >= 0).sum().item())
+        and torch.equal(g.grouped_x[entries].view(torch.int16), b.recv_x[gr].view(torch.int16))
+        and not bool(g.grouped_x[~entries].view(torch.int16).any().item()))
+    out["group_by_expert"]["grouped_rows"] = M
+    del g
     for key, kernel in (("dispatch_cached_bf16", "dispatch_kernel_cached_bf16"), ("dispatch_fp8", "dispatch_kernel_fp8"),
                         ("dispatch_cached_fp8", "dispatch_kernel_cached_fp8")):
         out[key]["traffic"] = measured_traffic(kernel, wl.name)
+    out["group_by_expert"]["traffic"] = measured_traffic("group_kernels", wl.name)
     out["dev_status"] = int(b.dev_status.item())
     return out
 

@@ -11,15 +11,18 @@
 // -1, weight 0).
 //
 // Design: two launches.
-//  positions: one 1024-thread block per slab walks it in groups of 16 tiles
-//   of 64 rows, one tile per wave, one row per lane.  A wave enumerates the
+//  positions: one 1024-thread block per group of 1024 rows of a slab (one
+//   tile of 64 rows per wave, one row per lane); a block first counts, per
+//   local id, the entries in the slab's rows before its group.  A wave enumerates the
 //   distinct local ids present in its tile (the lowest lane still holding an
-//   unplaced slot names the next id); for each id a DPP wave scan of the
-//   lanes' slot counts ranks every slot inside the tile, stably in (row, slot)
-//   order.  The tiles' totals are scanned across the 16 waves in LDS and added
-//   to running per-id counts, and a second pass over the same ids writes each
-//   slot's position, the grouped row index and the weight.  Padding positions
-//   are marked last.
+//   unranked slot names the next id); for each id a DPP wave scan of the
+//   lanes' slot counts gives every slot of that id its rank inside the tile,
+//   stably in (row, slot) order, kept in a register per slot.  The tiles'
+//   totals are scanned across the 16 waves in LDS and added to running per-id
+//   counts; then each slot's position is its segment start + its wave's start
+//   + its rank, and the grouped row index and weight are written there.
+//   Padding positions are marked last.  The kernel is instantiated for up to
+//   8, 16 or 32 slots per row so the per-slot loops are no longer than k.
 //  copy: one wave per grouped row copies the receive row it names (zeros for
 //   padding) with 16-byte non-temporal loads and stores; the grouped rows are
 //   written in order, as one contiguous stream.
@@ -58,28 +61,37 @@ __device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
 }
 
 // Key of the lowest set slot of `pending` (the slot order is the entry order).
-__device__ __forceinline__ int lowest_key(const int (&key)[kMaxTopk], uint32_t pending) {
+template <int KB>
+__device__ __forceinline__ int lowest_key(const int (&key)[KB], uint32_t pending) {
     int first = -1;
 #pragma unroll
-    for (int j = kMaxTopk - 1; j >= 0; --j)
+    for (int j = KB - 1; j >= 0; --j)
         if ((pending >> j) & 1u) first = key[j];
     return first;
 }
 
-__device__ __forceinline__ uint32_t slots_with_key(const int (&key)[kMaxTopk], uint32_t pending, int id) {
-    uint32_t m = 0;
-#pragma unroll
-    for (int j = 0; j < kMaxTopk; ++j)
-        if (((pending >> j) & 1u) && key[j] == id) m |= 1u << j;
-    return m;
+// Clamped bounds of slab r: rows [lo, hi) with 0 <= lo <= hi <= num_rows.
+__device__ __forceinline__ void slab_bounds(const int32_t *recv_gbl, int r, int64_t num_rows, int64_t *lo,
+                                            int64_t *hi) {
+    int64_t h = recv_gbl[r];
+    h = h < num_rows ? h : num_rows;
+    h = h > 0 ? h : 0;
+    int64_t l = r > 0 ? recv_gbl[r - 1] : 0;
+    l = l < h ? l : h;
+    *lo = l > 0 ? l : 0;
+    *hi = h;
 }
 
+// KB: slots per row the kernel is built for (k <= KB).  One block per group of
+// up to 1024 rows of one slab (at least one block per slab, so that empty
+// slabs still get their padding).
+template <int KB>
 __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(PositionParams p) {
     // dynamic LDS: int64 s_off[er] | int32 s_size[er] | int32 s_run[er] | int32 s_tile[16][er]
     extern __shared__ int64_t s_dyn[];
-    __shared__ unsigned long long s_base;
+    __shared__ unsigned long long s_base, s_total;
     __shared__ int64_t s_wsum[kGroupWaves];
-    const int er = p.er, K = p.K;
+    const int er = p.er, K = p.K, R = p.R;
     int64_t *s_off = s_dyn;
     int32_t *s_size = reinterpret_cast<int32_t *>(s_off + er);
     int32_t *s_run = s_size + er;
@@ -88,21 +100,53 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
-    const int r = blockIdx.x;
 
-    // ---- where this slab's first segment starts: the sizes of all earlier slabs' segments
-    if (tid == 0) s_base = 0;
+    // ---- which slab and which group of it: lane l of every wave counts slab l's groups
+    int groups = 0;
+    if (lane < R) {
+        int64_t l0, h0;
+        slab_bounds(p.recv_gbl, lane, p.num_rows, &l0, &h0);
+        const int64_t n = h0 - l0;
+        groups = n > 0 ? (int)((n + kGroupThreads - 1) / kGroupThreads) : 1;
+    }
+    const int ends = wave_inclusive_scan(groups);  // lane l: groups of slabs 0..l
+    const int total_groups = readlane32(ends, kWave - 1);
+    const int b = blockIdx.x;
+    if (b >= total_groups) return;  // the same decision in every wave of the block
+    const int r = __popcll(ballot64(lane < R && ends <= b));
+    const int group = b - (r > 0 ? readlane32(ends, r - 1) : 0);
+    const bool last_group = group == readlane32(groups, r) - 1;
+    int64_t lo, hi;
+    slab_bounds(p.recv_gbl, r, p.num_rows, &lo, &hi);
+    const int64_t g0 = lo + (int64_t)group * kGroupThreads;  // this block's rows: [g0, min(g0 + 1024, hi))
+
+    // ---- segment starts: the sizes of all segments of earlier slabs, then a scan over this slab's
+    if (tid == 0) {
+        s_base = 0;
+        s_total = 0;
+    }
+    for (int i = tid; i < er; i += kGroupThreads) s_run[i] = 0;
     __syncthreads();
-    int64_t part = 0;
+    int64_t part = 0, all = 0;
     for (int64_t e = tid; e < (int64_t)r * er; e += kGroupThreads) {
         const int32_t a = p.aligned[e];
         part += a > 0 ? a : 0;
     }
     if (part != 0) atomicAdd(&s_base, (unsigned long long)part);
-
-    // ---- this slab's segment starts and sizes (er <= 512 < 1024 threads: one each)
+    if (b == 0) {  // one block reports the total
+        for (int64_t e = tid; e < (int64_t)R * er; e += kGroupThreads) {
+            const int32_t a = p.aligned[e];
+            all += a > 0 ? a : 0;
+        }
+        if (all != 0) atomicAdd(&s_total, (unsigned long long)all);
+    }
+    // entries of each local id in the slab's rows before this group (counts only: any order)
+    for (int64_t i = lo * K + tid; i < g0 * K; i += kGroupThreads) {
+        const int64_t v = p.recv_idx[i];
+        if (v >= 0 && v < er) atomicAdd(&s_run[(int)v], 1);
+    }
     int64_t size = 0;
-    if (tid < er) {
+    if (tid < er) {  // er <= 512 < 1024 threads: one each
         const int32_t a = p.aligned[(int64_t)r * er + tid];
         size = a > 0 ? a : 0;
     }
@@ -114,114 +158,106 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     if (tid < er) {
         s_off[tid] = start;
         s_size[tid] = (int32_t)(size < INT32_MAX ? size : INT32_MAX);
-        s_run[tid] = 0;
     }
-    if (r == p.R - 1 && tid == 0) {
-        int64_t total = (int64_t)s_base;
-        for (int w = 0; w < kGroupWaves; ++w) total += s_wsum[w];
-        p.num_grouped[0] = (int32_t)(total < INT32_MAX ? total : INT32_MAX);
-    }
+    if (b == 0 && tid == 0) p.num_grouped[0] = (int32_t)(s_total < INT32_MAX ? s_total : INT32_MAX);
 
-    // ---- the slab's rows
-    int64_t hi = p.recv_gbl[r];
-    hi = hi < p.num_rows ? hi : p.num_rows;
-    hi = hi > 0 ? hi : 0;
-    int64_t lo = r > 0 ? p.recv_gbl[r - 1] : 0;
-    lo = lo < hi ? lo : hi;
-    lo = lo > 0 ? lo : 0;
+    // ---- this group's rows: one tile of 64 rows per wave, one row per lane
     bool bad = false, over = false;
     int32_t *tile = s_tile + wave * er;
+    const int64_t row = g0 + tid;
+    const bool in = row < hi;
+    int key[KB];
+    int rank[KB];        // rank of the slot among the tile's entries of its id
+    float wt[KB];        // the slot's weight (fetched with the ids when KB <= 16)
+    uint32_t valid = 0;  // bit j: slot j holds a local id of this slab
+    const bool want_w = p.grouped_w != nullptr;
+#pragma unroll
+    for (int j = 0; j < KB; ++j) {
+        key[j] = -1;
+        rank[j] = 0;
+        wt[j] = 0.0f;
+        if (j < K && in) {
+            const int64_t v = p.recv_idx[row * K + j];
+            if (KB <= 16 && want_w) wt[j] = p.recv_w[row * K + j];
+            if (v >= 0 && v < er) {
+                key[j] = (int)v;
+                valid |= 1u << j;
+            } else if (v != -1) {
+                bad = true;
+            }
+        }
+    }
+    __syncthreads();  // s_off, s_size and the earlier rows' counts are complete
+
+    // ranks inside the tile and the tile's entry count per local id
+    for (int i = lane; i < er; i += kWave) tile[i] = 0;
+    for (uint32_t pending = valid;;) {
+        const uint64_t holders = ballot64(pending != 0u);
+        if (holders == 0ull) break;
+        const int id = readlane32(lowest_key<KB>(key, pending), __builtin_ctzll(holders));
+        uint32_t m = 0;
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+            if (((pending >> j) & 1u) && key[j] == id) m |= 1u << j;
+        const int cnt = __popc(m);
+        const int incl_c = wave_inclusive_scan(cnt);
+        const int before = incl_c - cnt;
+#pragma unroll
+        for (int j = 0; j < KB; ++j)
+            if ((m >> j) & 1u) rank[j] = before + __popc(m & ((1u << j) - 1u));
+        if (lane == kWave - 1) tile[id] = incl_c;
+        pending &= ~m;
+    }
+    __syncthreads();
+    // exclusive start of each wave's entries per local id, after the slab's earlier rows
+    for (int i = tid; i < er; i += kGroupThreads) {
+        int32_t run = s_run[i];
+        for (int w = 0; w < kGroupWaves; ++w) {
+            const int32_t c = s_tile[w * er + i];
+            s_tile[w * er + i] = run;
+            run += c;
+        }
+        s_run[i] = run;
+    }
     __syncthreads();
 
-    for (int64_t g0 = lo; g0 < hi; g0 += kGroupThreads) {
-        const int64_t row = g0 + tid;  // wave w takes rows g0 + 64w .. g0 + 64w + 63
-        const bool in = row < hi;
-        int key[kMaxTopk];
-        uint32_t valid = 0;  // bit j: slot j holds a local id of this slab
+    // positions: segment start + the wave's start + the rank in the tile
+    if (in) {
 #pragma unroll
-        for (int j = 0; j < kMaxTopk; ++j) {
-            key[j] = -1;
-            if (j < K && in) {
-                const int64_t v = p.recv_idx[row * K + j];
-                if (v >= 0 && v < er) {
-                    key[j] = (int)v;
-                    valid |= 1u << j;
-                } else if (v != -1) {
-                    bad = true;
-                }
-            }
-        }
-
-        // pass 1: the tile's entry count per local id
-        for (int i = lane; i < er; i += kWave) tile[i] = 0;
-        for (uint32_t pending = valid;;) {
-            const uint64_t holders = ballot64(pending != 0u);
-            if (holders == 0ull) break;
-            const int id = readlane32(lowest_key(key, pending), __builtin_ctzll(holders));
-            const uint32_t m = slots_with_key(key, pending, id);
-            const int c = wave_inclusive_scan(__popc(m));
-            if (lane == kWave - 1) tile[id] = c;
-            pending &= ~m;
-        }
-        __syncthreads();
-        // exclusive starts of each wave's entries, per local id, after the earlier groups
-        for (int i = tid; i < er; i += kGroupThreads) {
-            int32_t run = s_run[i];
-            for (int w = 0; w < kGroupWaves; ++w) {
-                const int32_t c = s_tile[w * er + i];
-                s_tile[w * er + i] = run;
-                run += c;
-            }
-            s_run[i] = run;
-        }
-        __syncthreads();
-
-        // pass 2: positions
-        for (uint32_t pending = valid;;) {
-            const uint64_t holders = ballot64(pending != 0u);
-            if (holders == 0ull) break;
-            const int id = readlane32(lowest_key(key, pending), __builtin_ctzll(holders));
-            const uint32_t m = slots_with_key(key, pending, id);
-            const int cnt = __popc(m);
-            const int64_t first = (int64_t)tile[id] + (wave_inclusive_scan(cnt) - cnt);
-            const int64_t seg = s_off[id];
-            const int32_t seg_size = s_size[id];
-            for (uint32_t mm = m; mm != 0u; mm &= mm - 1u) {
-                const int j = __builtin_ctz(mm);
-                const int64_t li = first + __popc(m & ((1u << j) - 1u));
-                const int64_t pos = seg + li;
-                const bool ok = li < seg_size && pos < p.cap;
-                if (ok) {
+        for (int j = 0; j < KB; ++j) {
+            if (j >= K) continue;
+            int32_t at = -1;
+            if ((valid >> j) & 1u) {
+                const int id = key[j];
+                const int64_t li = (int64_t)tile[id] + rank[j];
+                const int64_t pos = s_off[id] + li;
+                if (li < s_size[id] && pos < p.cap) {
                     p.grouped_row[pos] = (int32_t)row;
-                    if (p.grouped_w != nullptr) p.grouped_w[pos] = p.recv_w[row * K + j];
+                    if (want_w) p.grouped_w[pos] = KB <= 16 ? wt[j] : p.recv_w[row * K + j];
+                    at = (int32_t)pos;
                 } else {
                     over = true;
                 }
-                if (p.slot_pos != nullptr) p.slot_pos[row * K + j] = ok ? (int32_t)pos : -1;
             }
-            pending &= ~m;
-        }
-        if (p.slot_pos != nullptr && in) {
-#pragma unroll
-            for (int j = 0; j < kMaxTopk; ++j)
-                if (j < K && !((valid >> j) & 1u)) p.slot_pos[row * K + j] = -1;
-        }
-        __syncthreads();  // the tile counts are reused by the next group
-    }
-
-    // ---- padding: the positions of each segment past its entries
-    for (int i = wave; i < er; i += kGroupWaves) {
-        const int64_t seg_size = s_size[i];
-        const int64_t used = s_run[i] < seg_size ? s_run[i] : seg_size;
-        const int64_t seg = s_off[i];
-        for (int64_t q = used + lane; q < seg_size && seg + q < p.cap; q += kWave) {
-            p.grouped_row[seg + q] = -1;
-            if (p.grouped_w != nullptr) p.grouped_w[seg + q] = 0.0f;
+            if (p.slot_pos != nullptr) p.slot_pos[row * K + j] = at;
         }
     }
 
-    // ---- rows past the last slab: in no segment
-    if (r == p.R - 1) {
+    // ---- padding, by the slab's last group once every entry is counted
+    if (last_group) {
+        for (int i = wave; i < er; i += kGroupWaves) {
+            const int64_t seg_size = s_size[i];
+            const int64_t used = s_run[i] < seg_size ? s_run[i] : seg_size;
+            const int64_t seg = s_off[i];
+            for (int64_t q = used + lane; q < seg_size && seg + q < p.cap; q += kWave) {
+                p.grouped_row[seg + q] = -1;
+                if (want_w) p.grouped_w[seg + q] = 0.0f;
+            }
+        }
+    }
+
+    // ---- rows past the last slab: in no segment (the last block)
+    if (b == total_groups - 1) {
         for (int64_t i = hi * K + tid; i < p.num_rows * K; i += kGroupThreads) {
             const int64_t v = p.recv_idx[i];
             if (v < -1 || v >= er) bad = true;
@@ -305,15 +341,12 @@ hipError_t run_copy_tiled(const CopyParams &p, int vpl, int wpb, hipStream_t str
     return hipErrorInvalidValue;
 }
 
-// One wave per whole row at the 7168-element widths, 1 KiB segments otherwise.
+// Measured on MI355X (prefill, skew, large workloads): 2 KiB segments, 8
+// waves per block, ahead of whole-row waves and of 1 KiB segments.
 void copy_tiling(int64_t row_units, int *vpl, int *wpb) {
+    (void)row_units;
+    *vpl = 2;
     *wpb = 8;
-    if (row_units == 14 * kWave)
-        *vpl = 14;
-    else if (row_units == 7 * kWave)
-        *vpl = 7;
-    else
-        *vpl = 1;
 }
 
 }  // namespace
@@ -336,8 +369,15 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
     q.R = s.num_ranks;
     q.K = s.num_topk;
     q.er = s.num_experts / s.num_ranks;
-    hipLaunchKernelGGL(group_positions_kernel, dim3((unsigned)q.R), dim3(kGroupThreads), group_lds_bytes(q.er), stream,
-                       q);
+    const size_t lds = group_lds_bytes(q.er);
+    // enough blocks for every slab's groups of 1024 rows, at least one per slab
+    const dim3 grid((unsigned)((q.num_rows + kGroupThreads - 1) / kGroupThreads + q.R));
+    if (q.K <= 8)
+        hipLaunchKernelGGL(group_positions_kernel<8>, grid, dim3(kGroupThreads), lds, stream, q);
+    else if (q.K <= 16)
+        hipLaunchKernelGGL(group_positions_kernel<16>, grid, dim3(kGroupThreads), lds, stream, q);
+    else
+        hipLaunchKernelGGL(group_positions_kernel<32>, grid, dim3(kGroupThreads), lds, stream, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.cap == 0) return err;
 
