@@ -1,4 +1,5 @@
-"""Build libep.so (the HIP kernels and the C ABI) for gfx950 with hipcc.
+"""Build libep.so (the HIP kernels and the C ABI) for gfx950 with hipcc, and
+the plain-C example program that the GPU tests run against it.
 
     python -m combine_ep_get_02_amd.build
 
@@ -31,6 +32,24 @@ FLAGS = [
 ]
 
 
+C_EXAMPLE_SOURCE = os.path.join(ROOT, "tests", "c_abi_roundtrip.c")
+C_EXAMPLE = os.path.join(ROOT, "tests", "c_abi_roundtrip")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_c_example(verbose: bool = False) -> str:
+    """gcc (C11) build of tests/c_abi_roundtrip.c linked against libep.so and the
+    HIP runtime, with run paths so it runs from the tree as it is."""
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-I", os.path.join(ROOT, "include"), "-I",
+           os.path.join(ROCM, "include"), C_EXAMPLE_SOURCE, "-L", PKG, "-lep", "-L", os.path.join(ROCM, "lib"),
+           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../combine_ep_get_02_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+           "-o", C_EXAMPLE]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    subprocess.run(cmd, check=True)
+    return C_EXAMPLE
+
+
 def build(out: str = LIBRARY, extra: list[str] | None = None, verbose: bool = False) -> str:
     tmp = out + ".tmp"
     cmd = ["hipcc", *FLAGS, *(extra or []), *SOURCES, "-o", tmp]
@@ -43,4 +62,5 @@ def build(out: str = LIBRARY, extra: list[str] | None = None, verbose: bool = Fa
 
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_c_example(verbose=True))
     sys.exit(0)
