@@ -195,11 +195,58 @@ class HipEvents:
         self.record(c)
         return self.elapsed_us(a, c) / n
 
+    def brackets_us(self, fn, brackets: int, per: int) -> list[float]:
+        """per-launch means of `brackets` groups of `per` back-to-back calls"""
+        return [self.mean_us(fn, per) for _ in range(brackets)]
+
     def close(self):
         self._torch.cuda.synchronize()
         for e in self._live:
             self._hip.hipEventDestroy(e)
         self._live = []
+
+
+def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) -> dict:
+    """dispatch and combine on other workloads (identity experts, inputs in
+    HBM): each kernel's per-launch time as the median and minimum over
+    `brackets` groups of `per` back-to-back launches, GB/s from the median."""
+    import torch
+
+    out = {}
+    for name in names:
+        d = inputs.generate(name)
+        wl = d["workload"]
+        T, H, K, E, R, C = wl.tokens, wl.hidden, wl.topk, wl.experts, wl.ranks, wl.channels
+        shape = ep.make_shape(T, H, K, E, R, C, 0, wl.expert_alignment)
+        x = torch.from_numpy(d["x"].view(np.int16)).cuda().view(torch.bfloat16)
+        idx = torch.from_numpy(d["topk_idx"]).cuda()
+        w = torch.from_numpy(d["topk_weights"]).cuda()
+        probe = ep.allocate(shape, 0)
+        ep.run_layout(probe, idx)
+        n = ep.run_notify(probe, read_back=True)
+        del probe
+        b = ep.allocate(shape, n)
+        calls = {"layout": lambda: ep.run_layout(b, idx), "notify": lambda: ep.run_notify(b),
+                 "dispatch": lambda: ep.run_dispatch(b, x, idx, w), "combine": lambda: ep.run_combine(b)}
+        for f in calls.values():
+            f()
+        t = {k: sorted(timer.brackets_us(f, brackets, per)) for k, f in calls.items()}
+        med = {k: float(np.median(v)) for k, v in t.items()}
+        db, cb = dispatch_bytes(T, H, K, R, n), combine_bytes(T, H, K, R, n)
+        live = b.in_rank.bool().any(1)
+        # identity experts return x (compared as values: the accumulator starts at +0, so -0 returns as +0)
+        ok = bool(torch.equal(b.combined_x[live].float(), x[live].float())) and int(b.dev_status.item()) == 0
+        out[name] = {
+            "config": f"t={T}, h={H}, topk={K}, experts={E}, ranks={R}, channels={C}", "num_recv_tokens": n,
+            "us_dispatch_median": round(med["dispatch"], 2), "us_dispatch_min": round(t["dispatch"][0], 2),
+            "us_combine_median": round(med["combine"], 2), "us_combine_min": round(t["combine"][0], 2),
+            "us_layout_median": round(med["layout"], 2), "us_notify_median": round(med["notify"], 2),
+            "GB/s_dispatch_plus_combine": round((db + cb) / (med["dispatch"] + med["combine"]) / 1e3, 2),
+            "pct_peak": round(100 * (db + cb) / (med["dispatch"] + med["combine"]) / 1e3 / HBM_PEAK_GBPS, 2),
+            "identity_check": ok}
+        del b, x, idx, w
+        torch.cuda.empty_cache()
+    return out
 
 
 def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer) -> dict:
@@ -280,6 +327,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the cached-mode and fp8-row dispatch timings reported beside the metric")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the dispatch/combine timings of the other four workloads reported beside the metric")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="extra steps with a 1 GiB scratch write before each, untimed, to evict the caches")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -388,6 +437,13 @@ def main() -> int:
     if variants is not None:
         ok = ok and variants["dev_status"] == 0 and all(v["check"] for k, v in variants.items() if k != "dev_status")
 
+    # median and minimum at this workload, over brackets of back-to-back launches
+    spread = {k: sorted(timer.brackets_us(calls[k], 5, max(1, args.steps // 5))) for k in ("dispatch", "combine")}
+    others = None
+    if not args.no_other_workloads:
+        others = time_workloads(ep, inputs, [n for n in inputs.WORKLOADS if n != wl.name], timer)
+        ok = ok and all(v["identity_check"] for v in others.values())
+
     db, cb = dispatch_bytes(T, H, K, R, n_recv), combine_bytes(T, H, K, R, n_recv)
     gbps = (db + cb) / us_dc / 1e3
     if us["dispatch"] >= us["combine"]:
@@ -425,8 +481,11 @@ def main() -> int:
         "bytes_combine": cb,
         "bytes_layout_notify": layout_notify_bytes(T, K, R, E, C),
         "identity_check": ok,
+        "us_dispatch_median_min": [round(float(np.median(spread["dispatch"])), 2), round(spread["dispatch"][0], 2)],
+        "us_combine_median_min": [round(float(np.median(spread["combine"])), 2), round(spread["combine"][0], 2)],
         "cold": cold,
         "variants": variants,
+        "other_workloads": others,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": measured_traffic(dom, wl.name), "algorithmic_bytes": dom_bytes,
