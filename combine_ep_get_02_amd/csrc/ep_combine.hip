@@ -196,11 +196,18 @@ hipError_t run_tiled(const CombineParams &p, int vpl, int wpb, hipStream_t strea
     return hipErrorInvalidValue;
 }
 
-// Measured on MI355X: 2 KiB row segments per wave, 8 waves per block.
-void combine_tiling(int64_t row_units, int *vpl, int *wpb) {
-    (void)row_units;
-    *vpl = 2;
-    *wpb = 8;
+// Measured on MI355X (prefill, skew and large workloads, and 512..2048-token
+// cuts of prefill): rows of 14 KiB and more in 2 KiB segments, 8 waves per
+// block from 4096 tokens and 4 below; narrower rows in 1 KiB segments, 4 waves
+// per block.
+void combine_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb) {
+    if (row_units >= 14 * kWave) {
+        *vpl = 2;
+        *wpb = num_tokens >= 4096 ? 8 : 4;
+    } else {
+        *vpl = 1;
+        *wpb = 4;
+    }
 }
 
 }  // namespace
@@ -223,7 +230,7 @@ hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv
     p.nrows = num_recv_rows;
     p.S = 1;
     int vpl, wpb;
-    combine_tiling(p.row_units, &vpl, &wpb);
+    combine_tiling(p.row_units, p.T, &vpl, &wpb);
     return run_tiled(p, vpl, wpb, stream);
 }
 

@@ -214,23 +214,33 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
     return hipErrorInvalidValue;
 }
 
-// Measured on MI355X (prefill / skew / large workloads): one wave per whole
-// 14 KiB row, 16 waves per block sweeping the ranks with a barrier every 4
-// ranks, is best when the row is 7168 bf16 wide; other widths use free-running
-// waves on 1 KiB segments, 8 waves per block.
-void dispatch_tiling(int64_t row_units, int *vpl, int *wpb, int *gran) {
+// Measured on MI355X (rows of 7168 bf16 or fp8 elements at 128..4096 tokens,
+// and the skew / large workloads).  Whole rows per wave with the rank sweep
+// (16 waves per block, a barrier every 4 ranks) win once there are enough
+// tokens to give every compute unit a block; below that the rows are split so
+// more waves share the copy.  Other widths: 1 KiB segments, 8 waves per block.
+void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, int *gran) {
+    *vpl = 1;
+    *wpb = 8;
+    *gran = 0;
     if (row_units == 14 * kWave) {  // 7168 bf16
-        *vpl = 14;
-        *wpb = 16;
-        *gran = 4;
+        if (num_tokens >= 2048) {
+            *vpl = 14;
+            *wpb = 16;
+            *gran = 4;
+        } else {
+            *vpl = 7;
+            *wpb = 4;
+        }
     } else if (row_units == 7 * kWave) {  // 7168 fp8 (or 3584 bf16)
-        *vpl = 7;
-        *wpb = 16;
-        *gran = 4;
-    } else {
-        *vpl = 1;
-        *wpb = 8;
-        *gran = 0;
+        if (num_tokens >= 4096) {
+            *vpl = 7;
+            *wpb = 16;
+            *gran = 4;
+        } else {
+            *vpl = 4;
+            *wpb = 4;
+        }
     }
 }
 
@@ -270,7 +280,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.num_scales = a.num_scales;
     p.S = 1;
     int vpl, wpb, gran;
-    dispatch_tiling(p.row_units, &vpl, &wpb, &gran);
+    dispatch_tiling(p.row_units, p.T, &vpl, &wpb, &gran);
     return run_tiled(p, vpl, wpb, gran, stream);
 }
 
