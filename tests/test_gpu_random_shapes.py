@@ -1,0 +1,52 @@
+"""Parity on seeded random shapes: every stage, the grouping by expert and
+(on alternate cases) fp8 plus cached dispatch, compared with the oracle on
+24 configurations drawn from a fixed seed -- token counts around the
+64-token chunk boundaries, 1 to 64 ranks (with 3- and 5-node layouts),
+1 to 32 local experts, topk up to 32, 1 to 49 channels, rows of 8 to 1024
+elements, expert alignments, masked and duplicate ids, and now and then a
+receive capacity a few rows short."""
+import numpy as np
+import pytest
+
+import gpu_harness as H
+import oracle
+from test_gpu_parity import _exact, _fp8_case, _group_case, _group_diff, _random_case
+
+pytestmark = pytest.mark.gpu
+
+CASES = 24
+
+
+def draw(case: int) -> dict:
+    rng = np.random.default_rng(4000 + case)
+    R = int(rng.choice([1, 2, 4, 8, 16, 24, 32, 40, 64]))
+    er = int(rng.choice([1, 2, 3, 4, 8, 16, 32]))
+    E = R * er
+    K = int(rng.integers(1, min(8, E) + 1))
+    if case % 7 == 3:
+        K = int(min(E, rng.integers(9, 33)))
+    return dict(
+        T=int(rng.choice([1, 2, 63, 64, 65, 127, 200, 333, 511, 700])), R=R, E=E, K=K,
+        C=int(rng.integers(1, 50)), H=int(rng.choice([16, 64, 256, 1024] if case % 2 == 0 else [8, 24, 200, 520])),
+        align=int(rng.choice([1, 2, 4, 16])), mask=float(rng.choice([0.0, 0.0, 0.1, 0.5])),
+        dup=bool(case % 3 == 1), short=bool(case % 5 == 2))
+
+
+@pytest.mark.parametrize("case", range(CASES))
+def test_random_shape(case):
+    s = draw(case)
+    print(f"[parity] random case {case}: {s}", flush=True)
+    x, idx, w = _random_case(s["T"], s["R"], s["E"], s["K"], s["C"], s["H"], seed=5000 + case, mask_frac=s["mask"],
+                             dup=s["dup"])
+    n = int(oracle.Oracle().layout(idx, s["E"], s["R"])["num_tokens_per_rank"].sum())
+    cap = max(0, n - 3) if s["short"] else None
+    gpu, ref = H.run_both(x, idx, w, s["E"], s["R"], s["C"], align=s["align"], capacity=cap)
+    assert H.compare(gpu, ref) == []
+    assert H.combine_bit_differences(gpu, ref) == {"combined_x": 0}
+    assert gpu["dev_status"] == ref["status"]
+    g, want = _group_case(x, idx, w, s["E"], s["R"], s["C"], s["align"])
+    assert _group_diff(g, want) == []
+    if case % 2 == 0:  # rows of whole 16-byte units as fp8 (H % 16 == 0), 8-element scale blocks
+        g8, r8 = _fp8_case(x, idx, w, s["E"], s["R"], s["C"], num_scales_block=8, capacity=cap)
+        assert _exact(g8, r8) == []
+        assert g8["status"] == r8["status"]
