@@ -16,7 +16,8 @@ between one event pair, which is what a kernel trace reports for it.
 Beside the metric: the cached-mode and fp8-row dispatch forms, a cold-cache
 cross-check and the oracle's throughput on the host.  Prints one JSON line.
 
-    python bench.py [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline] [--no-variants]
+                    [--no-other-workloads] [--cold-steps N]
 """
 from __future__ import annotations
 
@@ -321,8 +322,8 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
@@ -438,7 +439,7 @@ def main() -> int:
         ok = ok and variants["dev_status"] == 0 and all(v["check"] for k, v in variants.items() if k != "dev_status")
 
     # median and minimum at this workload, over brackets of back-to-back launches
-    spread = {k: sorted(timer.brackets_us(calls[k], 5, max(1, args.steps // 5))) for k in ("dispatch", "combine")}
+    spread = {k: sorted(timer.brackets_us(calls[k], 5, max(1, args.steps // 5))) for k in calls}
     others = None
     if not args.no_other_workloads:
         others = time_workloads(ep, inputs, [n for n in inputs.WORKLOADS if n != wl.name], timer)
@@ -481,8 +482,7 @@ def main() -> int:
         "bytes_combine": cb,
         "bytes_layout_notify": layout_notify_bytes(T, K, R, E, C),
         "identity_check": ok,
-        "us_dispatch_median_min": [round(float(np.median(spread["dispatch"])), 2), round(spread["dispatch"][0], 2)],
-        "us_combine_median_min": [round(float(np.median(spread["combine"])), 2), round(spread["combine"][0], 2)],
+        "us_median_min": {k: [round(float(np.median(v)), 2), round(v[0], 2)] for k, v in spread.items()},
         "cold": cold,
         "variants": variants,
         "other_workloads": others,
