@@ -397,10 +397,12 @@ int oracle_combine_f64(int32_t T, int32_t H, int32_t K, int32_t R, int32_t num_r
  *   grouped_x[pos] = recv_x[row] (bitwise, with its scales), grouped_row[pos] =
  *   row, grouped_weights[pos] = recv_topk_weights[row][j], slot_pos[row][j] =
  *   pos (-1 for slots with no entry).  *num_grouped_rows = sum_e aligned[e].
- * Rows at or beyond num_recv_rows are outside every slab; a negative segment
- * size counts as 0.  An entry beyond its segment's aligned size or at/after
- * grouped_capacity is skipped with ORC_RECV_OVERFLOW; a local id outside
- * [-1, E/R) with ORC_BAD_TOPK_IDX. */
+ * Rows at or past the end of the last slab (or num_recv_rows) hold no
+ * received token -- capacity slack -- so their ids are not read; their
+ * slot_pos entries are -1.  A negative segment size counts as 0.  An entry
+ * beyond its segment's aligned size or at/after grouped_capacity is skipped
+ * with ORC_RECV_OVERFLOW; a local id outside [-1, E/R) in a slab row with
+ * ORC_BAD_TOPK_IDX. */
 int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, const uint8_t *recv_x,
                            const float *recv_x_scales, int32_t num_scales, const int64_t *recv_topk_idx,
                            const float *recv_topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
@@ -409,9 +411,11 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
                            float *grouped_weights, int32_t *slot_pos, int32_t *num_grouped_rows) {
     int status = 0;
     const int32_t er = E / R;
+    int64_t last = recv_gbl_rank_prefix_sum[R - 1]; /* end of the last slab */
+    if (last > num_recv_rows) last = num_recv_rows;
     for (int64_t i = 0; i < (int64_t)num_recv_rows * K; ++i) {
         slot_pos[i] = -1;
-        if (recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er) status |= ORC_BAD_TOPK_IDX;
+        if (i < last * K && (recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er)) status |= ORC_BAD_TOPK_IDX;
     }
     int64_t offset = 0; /* start of segment e */
     for (int32_t r = 0; r < R; ++r) {

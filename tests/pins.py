@@ -557,6 +557,14 @@ def pin_group_by_expert(o, inputs: dict, align: int, hidden: int | None = None) 
             break
     if got["status"] != 0:
         errs.append(f"status {got['status']}")
+    # rows past the last slab are capacity slack: their ids (here out of range) are not read
+    slack_idx = np.concatenate([ridx, np.full((3, ridx.shape[1]), er + 5, np.int64)])
+    slack_x = np.concatenate([dis["recv_x"][:n], dis["recv_x"][:3]])
+    slack_w = np.concatenate([rw, np.ones((3, rw.shape[1]), np.float32)])
+    slack = o.group_by_expert(slack_x, slack_idx, slack_w, note["recv_gbl_rank_prefix_sum"], aligned, E)
+    if slack["status"] != 0 or not np.array_equal(slack["grouped_row"], got["grouped_row"]) or \
+            np.any(slack["slot_pos"][n:] != -1):
+        errs.append("capacity slack rows were read")
     # a short grouped capacity and one segment sized too small: flagged, the rest as the formulation says
     small = aligned.copy()
     e_big = int(np.argmax(lay["num_tokens_per_expert"]))
