@@ -256,13 +256,10 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
         }
     }
 
-    // ---- rows past the last slab: in no segment (the last block)
-    if (b == total_groups - 1) {
-        for (int64_t i = hi * K + tid; i < p.num_rows * K; i += kGroupThreads) {
-            const int64_t v = p.recv_idx[i];
-            if (v < -1 || v >= er) bad = true;
-            if (p.slot_pos != nullptr) p.slot_pos[i] = -1;
-        }
+    // ---- rows past the last slab hold no received token (capacity slack): their ids
+    // are not read, their slots are in no segment (the last block)
+    if (b == total_groups - 1 && p.slot_pos != nullptr) {
+        for (int64_t i = hi * K + tid; i < p.num_rows * K; i += kGroupThreads) p.slot_pos[i] = -1;
     }
     if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_TOPK_IDX);
     if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);

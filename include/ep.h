@@ -199,9 +199,12 @@ ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_
  *      grouped_weights is given and num_recv_rows > 0) as ep_dispatch / ep_dispatch_fp8 wrote them;
  *      recv_gbl_rank_prefix_sum [R] and num_recv_tokens_per_expert [E] as ep_notify wrote
  *      them (slab ends non-decreasing; a negative size counts as 0).
+ * Rows at or past the end of the last slab (capacity slack, e.g. num_recv_rows = the
+ * allocated capacity when N is not known on the host) are not read; their slot_pos is -1.
  * dev_status (nullable): EP_DEV_RECV_OVERFLOW (an entry past its segment's size or the
  * grouped capacity: skipped, slot_pos -1), EP_DEV_BAD_TOPK_IDX (a local id outside
- * [-1, E/R): skipped).  E/R > 512 or num_recv_rows * k >= 2^31: EP_ERR_UNSUPPORTED.
+ * [-1, E/R) in a slab row: skipped).  E/R > 512 or num_recv_rows * k >= 2^31:
+ * EP_ERR_UNSUPPORTED.
  * Two launches (positions, then the row copy); no workspace.
  */
 ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t elem_bytes,

@@ -293,7 +293,7 @@ def test_cached_dispatch_bad_slots_bf16():
 
 
 def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0, bad_ids=False, extra_rows=0,
-                optional=True):
+                optional=True, extra_id=None):
     """Both sides run layout, notify, dispatch (bf16 or fp8 rows) and then the
     grouping by local expert, from the same inputs; the same host-side edits
     (a segment size shrunk, bad local ids, rows past the last slab) are made
@@ -323,8 +323,9 @@ def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0,
         aligned[e_big] -= align + 1
     r_idx, r_x = d["recv_topk_idx"].copy(), d["recv_x"].copy()
     r_w = d["recv_topk_weights"]
+    slack_id = min(1, er - 1) if extra_id is None else extra_id
     if extra_rows:
-        r_idx[n:] = min(1, er - 1)
+        r_idx[n:] = slack_id
         r_x[n:] = 0
     if bad_ids and n > 1:
         r_idx[0, 0] = er + 3
@@ -354,7 +355,7 @@ def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0,
     if shrink:
         g_aligned[e_big] -= align + 1
     if extra_rows:
-        b.recv_idx[n:] = min(1, er - 1)
+        b.recv_idx[n:] = slack_id
     if bad_ids and n > 1:
         b.recv_idx[0, 0] = er + 3
         b.recv_idx[min(5, n - 1), K - 1] = -5
@@ -439,3 +440,13 @@ def test_group_no_rows():
     x, idx, w = _random_case(40, 8, 16, 2, 4, 64, seed=33, mask_frac=1.0)
     gpu, want = _group_case(x, idx, w, 16, 8, 4, 4)
     assert _group_diff(gpu, want) == [] and gpu["num_grouped_rows"] == 0
+
+
+def test_group_ignores_capacity_slack():
+    # rows past the last slab (a capacity larger than N, as inside a captured graph) hold
+    # out-of-range ids: not read, not flagged, their slot positions -1
+    print("[parity] group_by_expert capacity slack", flush=True)
+    x, idx, w = _random_case(500, 16, 64, 4, 7, 128, seed=34)
+    gpu, want = _group_case(x, idx, w, 64, 16, 7, 2, extra_rows=37, extra_id=999)
+    assert _group_diff(gpu, want) == []
+    assert want["status"] == 0
