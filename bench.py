@@ -233,6 +233,12 @@ def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) ->
             f()
         t = {k: sorted(timer.brackets_us(f, brackets, per)) for k, f in calls.items()}
         med = {k: float(np.median(v)) for k, v in t.items()}
+        # the whole step from a HIP graph: no host launch cost between the kernels
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for f in calls.values():
+                f()
+        graph_us = timer.mean_us(graph.replay, brackets * per)
         db, cb = dispatch_bytes(T, H, K, R, n), combine_bytes(T, H, K, R, n)
         live = b.in_rank.bool().any(1)
         # identity experts return x (compared as values: the accumulator starts at +0, so -0 returns as +0)
@@ -242,6 +248,7 @@ def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) ->
             "us_dispatch_median": round(med["dispatch"], 2), "us_dispatch_min": round(t["dispatch"][0], 2),
             "us_combine_median": round(med["combine"], 2), "us_combine_min": round(t["combine"][0], 2),
             "us_layout_median": round(med["layout"], 2), "us_notify_median": round(med["notify"], 2),
+            "us_step_graph": round(graph_us, 2),
             "GB/s_dispatch_plus_combine": round((db + cb) / (med["dispatch"] + med["combine"]) / 1e3, 2),
             "pct_peak": round(100 * (db + cb) / (med["dispatch"] + med["combine"]) / 1e3 / HBM_PEAK_GBPS, 2),
             "identity_check": ok}
@@ -328,6 +335,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
                     help="skip the cached-mode and fp8-row dispatch timings reported beside the metric")
+    ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the dispatch/combine timings of the other four workloads reported beside the metric")
     ap.add_argument("--cold-steps", type=int, default=10,
@@ -407,6 +415,32 @@ def main() -> int:
     # each kernel's average launch duration: K back-to-back launches between one event pair
     us = {k: timer.mean_us(f, args.steps) for k, f in calls.items()}
 
+    # the same step captured once in a HIP graph and replayed K times
+    graph = None
+    if not args.no_graph:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        ga, gc = timer.pair()
+        w0 = time.perf_counter()
+        timer.record(ga)
+        for _ in range(args.steps):
+            g.replay()
+        timer.record(gc)
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) / args.steps
+        graph = {"us_per_step_gpu": round(timer.elapsed_us(ga, gc) / args.steps, 2),
+                 "ms_per_step_wall": round(wall * 1e3, 4),
+                 "note": "layout+notify+dispatch+combine captured with torch.cuda.graph, K replays back to back"}
+
     # correctness guard on the measured buffers: identity experts return x
     live = b.in_rank.bool().any(1)
     ok = bool(torch.equal(b.combined_x[live], x[live])) and int(b.dev_status.item()) == 0
@@ -484,6 +518,7 @@ def main() -> int:
         "identity_check": ok,
         "us_median_min": {k: [round(float(np.median(v)), 2), round(v[0], 2)] for k, v in spread.items()},
         "cold": cold,
+        "graph": graph,
         "variants": variants,
         "other_workloads": others,
         "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
