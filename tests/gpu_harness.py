@@ -39,6 +39,9 @@ def run_both(x, topk_idx, topk_weights, E, R, C, my_rank=0, align=1, capacity=No
     for t in (b.gbl, b.rdma, b.recv_gbl, b.recv_rdma, b.recv_per_expert, b.num_recv, b.send_slot, b.src_info):
         t.fill_(SENTINEL_I32)
     b.recv_w.fill_(-3.0)
+    # receive rows poisoned with all-ones bytes (a NaN pattern in bf16): a row dispatch
+    # fails to write cannot match the oracle's row by accident
+    b.recv_x.view(torch.int16).fill_(-1)
     if b.recv_idx is not None:
         b.recv_idx.fill_(-777)
     b.combined_w.fill_(-3.0)
