@@ -9,6 +9,13 @@
  *                              aligned per-expert receive counts, N_recv
  *   ep_dispatch    x rows   -> receive region laid out [dst_rank][channel]
  *   ep_combine     expert outputs in receive layout -> weighted sum in token order
+ * and beside them:
+ *   ep_dispatch_fp8     dispatch of 1-byte (fp8) rows with their per-token scales
+ *   ep_dispatch_cached  new rows to the rows an earlier dispatch assigned (cached mode)
+ *   ep_group_by_expert  receive rows regrouped into per-expert segments for grouped GEMMs
+ *   ep_workspace_bytes, ep_status_string
+ * Every call is stream-ordered and allocates nothing, so a sequence of them can be
+ * captured in a HIP graph (ep_notify without its host read-back).
  *
  * Sources (web pages, cited by page title and section/function):
  *   mscclpp src/ext/ep/ht_runtime.cc mirror -- the torch-free host runtime:
@@ -35,8 +42,9 @@
  *   - Data-dependent problems never trap: the kernels skip the offending item
  *     and OR a bit (EP_DEV_*) into *dev_status when dev_status is non-NULL.
  *     The caller zeroes *dev_status when it wants a fresh reading.
- *   - Row buffers (x, recv_x, y, combined_x) are bf16 rows of `hidden`
- *     elements and must be 16-byte aligned; rows move in 16-byte units.
+ *   - Row buffers (x, recv_x, y, combined_x, grouped_x) must be 16-byte aligned;
+ *     rows move in 16-byte units (bf16 rows of `hidden` elements, or 1-byte
+ *     elements where a call says so).
  */
 #ifndef EP_H
 #define EP_H
