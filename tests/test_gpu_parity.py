@@ -69,6 +69,9 @@ EDGE = {
     "huge_expert_count_global_atomics": (700, 64, 16384, 8, 24, 128, {}),
     "masked_and_duplicates": (400, 32, 256, 8, 24, 256, dict(mask_frac=0.3, dup=True)),
     "fully_masked_tokens": (129, 16, 64, 4, 3, 128, dict(mask_frac=1.0)),
+    # 1563 chunks at 64 ranks: the counts do not fit LDS, notify scans in global memory
+    "t100k_global_scan": (100000, 64, 256, 8, 24, 64, {}),
+    "hidden_32768": (33, 8, 16, 2, 3, 32768, {}),
 }
 
 
@@ -450,3 +453,13 @@ def test_group_ignores_capacity_slack():
     gpu, want = _group_case(x, idx, w, 64, 16, 7, 2, extra_rows=37, extra_id=999)
     assert _group_diff(gpu, want) == []
     assert want["status"] == 0
+
+
+def test_fp8_max_scales():
+    # 1024 scales per token, the limit (16384 one-byte elements in 16-element blocks)
+    print("[parity] fp8 with 1024 scales per token", flush=True)
+    x, idx, w = _random_case(50, 8, 32, 4, 3, 16384, seed=14)
+    gpu, ref = _fp8_case(x, idx, w, 32, 8, 3, num_scales_block=16)
+    assert gpu["recv_x_scales"].shape[1] == 1024
+    assert _exact(gpu, ref) == []
+    assert gpu["status"] == 0 == ref["status"]
