@@ -21,9 +21,10 @@
 // lanes before this token, gives the in-chunk rank -- rows come out in the
 // canonical order without a serial scan, and lane r ends up holding the row
 // for rank r.  The segment is then stored to every destination with 16-byte
-// non-temporal stores.  The tiling (whole rows per wave, or 1 KiB segments
-// with consecutive waves writing consecutive pieces of the same rows) is picked
-// per row width from measurements.
+// non-temporal stores.  The tiling (whole rows per wave with the block's waves
+// sweeping the destinations together, or row segments with consecutive waves
+// writing consecutive pieces of the same rows) is picked per row width and
+// token count from measurements.
 #include "ep_internal.h"
 
 namespace ep {
