@@ -156,10 +156,13 @@ class HipEvents:
 
         torch.zeros(1, device="cuda")  # runtime loaded and device initialised
         paths = sorted({ln.split()[-1] for ln in open("/proc/self/maps") if "libamdhip64" in ln})
-        if not paths:
-            raise RuntimeError("HIP runtime library not found in this process")
+        # the events must come from the runtime that owns torch's streams
+        torch_dir = os.path.dirname(torch.__file__)
+        own = [q for q in paths if q.startswith(torch_dir)] or paths
+        if len(own) != 1:
+            raise RuntimeError(f"cannot tell which HIP runtime owns torch's streams: {paths}")
         self._ct = ctypes
-        self._hip = ctypes.CDLL(paths[0])
+        self._hip = ctypes.CDLL(own[0])
         self._torch = torch
         self._live = []
 
