@@ -463,3 +463,29 @@ def test_fp8_max_scales():
     assert gpu["recv_x_scales"].shape[1] == 1024
     assert _exact(gpu, ref) == []
     assert gpu["status"] == 0 == ref["status"]
+
+
+def test_combine_without_combined_weights():
+    # combined_topk_weights is optional: the rows must not change and the buffer stays untouched
+    print("[parity] combine without combined weights", flush=True)
+    import torch
+
+    from combine_ep_get_02_amd import ep
+
+    d = generate("sweep")
+    wl = d["workload"]
+    gpu, ref = H.run_both(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels)
+    assert H.compare(gpu, ref) == []
+    shape = ep.make_shape(wl.tokens, wl.hidden, wl.topk, wl.experts, wl.ranks, wl.channels)
+    n = ref["num_recv_tokens"]
+    b = ep.allocate(shape, n)
+    didx = torch.from_numpy(d["topk_idx"]).cuda()
+    ep.run_layout(b, didx)
+    ep.run_notify(b)
+    ep.run_dispatch(b, H.to_dev_bf16(d["x"]), didx, torch.from_numpy(d["topk_weights"]).cuda())
+    b.combined_w.fill_(-5.0)
+    ep.run_combine(b, with_weights=False)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bf16_host(b.combined_x), ref["combined_x"])
+    assert bool((b.combined_w == -5.0).all().item())
+    assert int(b.dev_status.item()) == 0
