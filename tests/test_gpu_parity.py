@@ -489,3 +489,43 @@ def test_combine_without_combined_weights():
     assert np.array_equal(H.bf16_host(b.combined_x), ref["combined_x"])
     assert bool((b.combined_w == -5.0).all().item())
     assert int(b.dev_status.item()) == 0
+
+
+def test_every_call_without_a_status_word():
+    # dev_status is optional in every entry point: same outputs with and without it,
+    # on inputs that would set flags (bad ids, a short receive capacity)
+    print("[parity] every entry point with dev_status = NULL", flush=True)
+    import torch
+
+    from combine_ep_get_02_amd import ep
+
+    x, idx, w = _random_case(300, 16, 64, 4, 5, 128, seed=41)
+    idx[3, 1] = 999  # a bad id: flagged when a status word is given
+    shape = ep.make_shape(300, 128, 4, 64, 16, 5, 0, 2)
+    didx, dw, dx = torch.from_numpy(idx).cuda(), torch.from_numpy(w).cuda(), H.to_dev_bf16(x)
+    outs = []
+    for with_status in (True, False):
+        st = torch.zeros(1, dtype=torch.int32, device="cuda") if with_status else None
+        b = ep.allocate(shape, 0)
+        ep.ep_get_layout(shape, didx, b.per_rank, b.per_node, b.per_expert, b.in_rank, b.workspace, st)
+        n = ep.ep_notify(shape, b.in_rank, b.per_rank, b.per_node, b.per_expert, b.gbl, b.rdma, b.recv_gbl,
+                         b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, True, st)
+        cap = n - 5
+        b2 = ep.allocate(shape, cap)
+        ep.ep_get_layout(shape, didx, b2.per_rank, b2.per_node, b2.per_expert, b2.in_rank, b2.workspace, st)
+        ep.ep_notify(shape, b2.in_rank, b2.per_rank, b2.per_node, b2.per_expert, b2.gbl, b2.rdma, b2.recv_gbl,
+                     b2.recv_rdma, b2.recv_per_expert, b2.num_recv, b2.workspace, False, st)
+        ep.ep_dispatch(shape, dx, didx, dw, b2.recv_gbl, b2.workspace, cap, b2.recv_x, b2.recv_w, b2.recv_idx,
+                       b2.src_info, b2.send_slot, st)
+        ep.ep_combine(shape, b2.recv_x, b2.recv_w, b2.send_slot, cap, b2.combined_x, b2.combined_w, st)
+        m = int(b2.recv_per_expert.sum().item())
+        g = ep.allocate_group(b2, m)
+        ep.ep_group_by_expert(shape, b2.recv_x, 2, None, 0, b2.recv_idx, b2.recv_w, b2.recv_gbl, b2.recv_per_expert,
+                              cap, m, g.grouped_x, None, g.grouped_row, g.grouped_w, g.slot_pos, g.num_grouped, st)
+        torch.cuda.synchronize()
+        mm = min(int(g.num_grouped.item()), m)
+        outs.append([b2.send_slot.cpu(), b2.recv_x[:cap].view(torch.int16).cpu(), b2.combined_x.view(torch.int16).cpu(),
+                     b2.combined_w.cpu(), g.grouped_row[:mm].cpu(), g.grouped_x[:mm].view(torch.int16).cpu()])
+        if with_status:
+            assert int(st.item()) & 3 == 3  # the bad id and the overflow were flagged
+    assert all(torch.equal(a, b) for a, b in zip(*outs))
