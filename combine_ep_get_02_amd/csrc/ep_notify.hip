@@ -137,6 +137,10 @@ __device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
 constexpr int kScanLds = 12288;
 // rows of either matrix one thread loads: ceil(kScanLds / NC / (kNotifyThreads / NC)) for any NC <= 72
 constexpr int kPasses = 14;
+// per-expert counts a thread of the last block loads with the others (E <= 4096 in one go)
+constexpr int kExpertBatch = 4;
+// columns (ranks + nodes <= 72) a wave scans together: ceil(72 / 16)
+constexpr int kColBatch = 5;
 
 __device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c) {
     return (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
@@ -159,10 +163,10 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
     const bool is_rank = col < R;
 
     // ---- one round trip of loads: at most kPasses rows per thread for each
-    // matrix (rows <= kScanLds / NC, RP = kNotifyThreads / NC), all issued
-    // before any is written to LDS
+    // matrix (rows <= kScanLds / NC, RP = kNotifyThreads / NC), the per-rank,
+    // per-node and first per-expert counts, all issued before any is used
+    int32_t vq[kPasses], vc[kPasses], pe[kExpertBatch];
     if (active) {
-        int32_t vq[kPasses], vc[kPasses];
 #pragma unroll
         for (int k = 0; k < kPasses; ++k) {
             const int q = r0 + k * RP;
@@ -172,6 +176,15 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
                         ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
                         : 0;
         }
+    }
+    const int32_t per_rank = lane < R ? p.per_rank[lane] : 0;
+    const int32_t per_node = lane < nodes ? p.per_node[lane] : 0;
+#pragma unroll
+    for (int k = 0; k < kExpertBatch; ++k) {
+        const int e = tid + k * kNotifyThreads;
+        pe[k] = e < p.E ? p.per_expert[e] : 0;
+    }
+    if (active) {
 #pragma unroll
         for (int k = 0; k < kPasses; ++k) {
             const int q = r0 + k * RP;
@@ -187,34 +200,47 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
                                        ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
                                        : 0;
     }
-    const int32_t per_rank = lane < R ? p.per_rank[lane] : 0;
-    const int32_t per_node = lane < nodes ? p.per_node[lane] : 0;
-    // aligned per-expert counts need nothing from the scan: done here, while
-    // the loads above are in flight
-    for (int e = tid; e < p.E; e += kNotifyThreads) {
-        const int32_t n = p.per_expert[e];
-        p.recv_per_expert[e] = (int32_t)(((int64_t)n + p.align - 1) / p.align * p.align);
+    // aligned per-expert counts need nothing from the scan
+    auto aligned = [&](int32_t n) { return (int32_t)(((int64_t)n + p.align - 1) / p.align * p.align); };
+#pragma unroll
+    for (int k = 0; k < kExpertBatch; ++k) {
+        const int e = tid + k * kNotifyThreads;
+        if (e < p.E) p.recv_per_expert[e] = aligned(pe[k]);
     }
+    for (int e = tid + kExpertBatch * kNotifyThreads; e < p.E; e += kNotifyThreads)
+        p.recv_per_expert[e] = aligned(p.per_expert[e]);
     __syncthreads();
 
-    // ---- scans: one wave per column, lanes over runs of chunks
+    // ---- scans: one wave per column, lanes over runs of chunks; a wave's
+    // columns (up to kColBatch) are read together so their LDS loads overlap
     const int per = (Q + kWave - 1) / kWave;
-    for (int cc = wave; cc < NC; cc += kNotifyWaves) {
-        const int b = lane * per;
-        const int e = (b + per) < Q ? (b + per) : Q;
-        int32_t sum = 0;
-        for (int q = b; q < e; ++q) sum += s_cnt[q * NC + cc];
-        const int32_t incl = wave_inclusive_scan(sum);
-        int32_t run = incl - sum;
-        for (int q = b; q < e; ++q) {
-            const int32_t v = s_cnt[q * NC + cc];
-            s_cnt[q * NC + cc] = run;
-            run += v;
+    const int b = lane * per;
+    const int e = (b + per) < Q ? (b + per) : Q;
+    for (int c0 = wave; c0 < NC; c0 += kNotifyWaves * kColBatch) {
+        int32_t sum[kColBatch];
+#pragma unroll
+        for (int k = 0; k < kColBatch; ++k) {
+            const int cc = c0 + k * kNotifyWaves;
+            sum[k] = 0;
+            if (cc < NC)
+                for (int q = b; q < e; ++q) sum[k] += s_cnt[q * NC + cc];
         }
-        const int32_t total = readlane32(incl, kWave - 1);
-        if (lane == 0) {
-            s_cnt[Q * NC + cc] = total;
-            s_tot[cc] = total;
+#pragma unroll
+        for (int k = 0; k < kColBatch; ++k) {
+            const int cc = c0 + k * kNotifyWaves;  // the same for the whole wave
+            if (cc >= NC) break;
+            const int32_t incl = wave_inclusive_scan(sum[k]);
+            int32_t run = incl - sum[k];
+            for (int q = b; q < e; ++q) {
+                const int32_t v = s_cnt[q * NC + cc];
+                s_cnt[q * NC + cc] = run;
+                run += v;
+            }
+            const int32_t total = readlane32(incl, kWave - 1);
+            if (lane == 0) {
+                s_cnt[Q * NC + cc] = total;
+                s_tot[cc] = total;
+            }
         }
     }
     // receive prefix sums over destination ranks and nodes (inclusive)
