@@ -60,6 +60,12 @@ __device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
     return v;
 }
 
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+#pragma unroll
+    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
 // Key of the lowest set slot of `pending` (the slot order is the entry order).
 template <int KB>
 __device__ __forceinline__ int lowest_key(const int (&key)[KB], uint32_t pending) {
@@ -89,8 +95,7 @@ template <int KB>
 __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(PositionParams p) {
     // dynamic LDS: int64 s_off[er] | int32 s_size[er] | int32 s_run[er] | int32 s_tile[16][er]
     extern __shared__ int64_t s_dyn[];
-    __shared__ unsigned long long s_base, s_total;
-    __shared__ int64_t s_wsum[kGroupWaves];
+    __shared__ int64_t s_wsum[kGroupWaves], s_wbase[kGroupWaves], s_wall[kGroupWaves];
     const int er = p.er, K = p.K, R = p.R;
     int64_t *s_off = s_dyn;
     int32_t *s_size = reinterpret_cast<int32_t *>(s_off + er);
@@ -120,50 +125,58 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     slab_bounds(p.recv_gbl, r, p.num_rows, &lo, &hi);
     const int64_t g0 = lo + (int64_t)group * kGroupThreads;  // this block's rows: [g0, min(g0 + 1024, hi))
 
-    // ---- segment starts: the sizes of all segments of earlier slabs, then a scan over this slab's
-    if (tid == 0) {
-        s_base = 0;
-        s_total = 0;
-    }
-    for (int i = tid; i < er; i += kGroupThreads) s_run[i] = 0;
-    __syncthreads();
+    // this slab's segment sizes (er <= 512 < 1024 threads: one each)
+    const int32_t size_raw = tid < er ? p.aligned[(int64_t)r * er + tid] : 0;
+
+    // ---- segment starts: the sizes of all segments of earlier slabs (a block sum),
+    // then a scan over this slab's
     int64_t part = 0, all = 0;
     for (int64_t e = tid; e < (int64_t)r * er; e += kGroupThreads) {
         const int32_t a = p.aligned[e];
         part += a > 0 ? a : 0;
     }
-    if (part != 0) atomicAdd(&s_base, (unsigned long long)part);
     if (b == 0) {  // one block reports the total
         for (int64_t e = tid; e < (int64_t)R * er; e += kGroupThreads) {
             const int32_t a = p.aligned[e];
             all += a > 0 ? a : 0;
         }
-        if (all != 0) atomicAdd(&s_total, (unsigned long long)all);
     }
-    // entries of each local id in the slab's rows before this group (counts only: any order)
-    for (int64_t i = lo * K + tid; i < g0 * K; i += kGroupThreads) {
-        const int64_t v = p.recv_idx[i];
-        if (v >= 0 && v < er) atomicAdd(&s_run[(int)v], 1);
+    part = wave_sum64(part);
+    all = wave_sum64(all);
+    if (lane == 0) {
+        s_wbase[wave] = part;
+        s_wall[wave] = all;
     }
-    int64_t size = 0;
-    if (tid < er) {  // er <= 512 < 1024 threads: one each
-        const int32_t a = p.aligned[(int64_t)r * er + tid];
-        size = a > 0 ? a : 0;
-    }
-    const int64_t incl = wave_inclusive_scan64(size);
-    if (lane == kWave - 1) s_wsum[wave] = incl;
-    __syncthreads();
-    int64_t start = (int64_t)s_base + incl - size;
-    for (int w = 0; w < wave; ++w) start += s_wsum[w];
-    if (tid < er) {
-        s_off[tid] = start;
-        s_size[tid] = (int32_t)(size < INT32_MAX ? size : INT32_MAX);
-    }
-    if (b == 0 && tid == 0) p.num_grouped[0] = (int32_t)(s_total < INT32_MAX ? s_total : INT32_MAX);
 
-    // ---- this group's rows: one tile of 64 rows per wave, one row per lane
-    bool bad = false, over = false;
+    // ---- entries of each local id in the slab's rows before this group: each wave
+    // counts tiles of 64 of those rows into its own row of the tile table with LDS
+    // atomics (only lanes of the same wave can meet on an address), then the rows
+    // are added up; TU tiles per pass, their ids all loaded before any is counted
     int32_t *tile = s_tile + wave * er;
+    for (int i = lane; i < er; i += kWave) tile[i] = 0;
+    constexpr int TU = KB <= 8 ? 4 : 1;
+    for (int64_t t0 = lo + (int64_t)wave * kWave; t0 < g0; t0 += (int64_t)TU * kGroupThreads) {
+        int pkey[TU][KB];
+#pragma unroll
+        for (int u = 0; u < TU; ++u) {
+            const int64_t prow = t0 + (int64_t)u * kGroupThreads + lane;
+#pragma unroll
+            for (int j = 0; j < KB; ++j) {
+                pkey[u][j] = -1;
+                if (j < K && prow < g0) {
+                    const int64_t v = p.recv_idx[prow * K + j];
+                    if (v >= 0 && v < er) pkey[u][j] = (int)v;
+                }
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < TU; ++u)
+#pragma unroll
+            for (int j = 0; j < KB; ++j)
+                if (pkey[u][j] >= 0) atomicAdd(&tile[pkey[u][j]], 1);
+    }
+    // ---- this group's rows (one tile of 64 rows per wave, one row per lane): ids and weights
+    bool bad = false, over = false;
     const int64_t row = g0 + tid;
     const bool in = row < hi;
     int key[KB];
@@ -187,6 +200,29 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
             }
         }
     }
+
+    const int64_t size = size_raw > 0 ? size_raw : 0;
+    const int64_t incl = wave_inclusive_scan64(size);
+    if (lane == kWave - 1) s_wsum[wave] = incl;
+    __syncthreads();
+    int64_t base = 0, total_all = 0, start = incl - size;
+    for (int w = 0; w < kGroupWaves; ++w) {
+        base += s_wbase[w];
+        total_all += s_wall[w];
+        if (w < wave) start += s_wsum[w];
+    }
+    start += base;
+    if (tid < er) {
+        s_off[tid] = start;
+        s_size[tid] = (int32_t)(size < INT32_MAX ? size : INT32_MAX);
+    }
+    for (int i = tid; i < er; i += kGroupThreads) {
+        int32_t run = 0;
+        for (int w = 0; w < kGroupWaves; ++w) run += s_tile[w * er + i];
+        s_run[i] = run;
+    }
+    if (b == 0 && tid == 0) p.num_grouped[0] = (int32_t)(total_all < INT32_MAX ? total_all : INT32_MAX);
+
     __syncthreads();  // s_off, s_size and the earlier rows' counts are complete
 
     // ranks inside the tile and the tile's entry count per local id
