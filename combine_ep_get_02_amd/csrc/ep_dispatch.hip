@@ -12,19 +12,21 @@
 // src_info[row] = {my_rank, t}, send_slot[t][r] = row.
 //
 // Design (the pages' sender/forwarder rings are transport machinery and are not
-// reproduced): one wave per (token, row segment of VPL*1 KiB).  The wave first
-// issues the 16-byte loads of its x segment (one read of x per token overall),
-// then resolves the token's rows while they are in flight: notify left each
-// token's 64-bit rank mask and, per 64-token chunk, the exclusive row offset
-// inside every slab; the wave loads its chunk's 64 masks (one per lane) and for
-// each destination r a ballot over "lane's token goes to r", masked to the
-// lanes before this token, gives the in-chunk rank -- rows come out in the
-// canonical order without a serial scan, and lane r ends up holding the row
-// for rank r.  The segment is then stored to every destination with 16-byte
-// non-temporal stores.  The tiling (whole rows per wave with the block's waves
-// sweeping the destinations together, or row segments with consecutive waves
-// writing consecutive pieces of the same rows) is picked per row width and
-// token count from measurements.
+// reproduced).  notify left each token's 64-bit rank mask and, per 64-token
+// chunk, the exclusive row offset inside every slab; with those every row's
+// position is known without a serial scan.  Two forms:
+//  - pull (from 2048 tokens, rows of 1 KiB to 1 MiB): the rows are produced in
+//    receive order.  Each XCD takes groups of 128 tokens in turn; a wave finds
+//    the group's rows per rank with a 64x64 bit transpose of the masks and a
+//    wave scan, and the XCD's waves write the group's output as one advancing
+//    window of small tasks, reading x from the XCD's L2 (dispatch_pull_kernel);
+//  - push (fewer tokens, other widths, cached mode): one wave per (token, row
+//    segment) loads its x segment once and stores it to every destination
+//    (dispatch_kernel).  For each destination r a ballot over the chunk's
+//    masks, masked to the lanes before the token, gives the in-chunk rank, so
+//    lane r ends up holding the row for rank r.
+// All row traffic uses 16-byte accesses with non-temporal stores.  The form
+// and tiling are picked per row width and token count from measurements.
 #include "ep_internal.h"
 
 namespace ep {
@@ -52,6 +54,39 @@ struct DispatchParams {
     int64_t row_units;  // 16-byte units per row
     int R, K, E, experts_per_rank, my_rank, cap, S, num_scales;
 };
+
+// Per-token scales (fp8 rows) travel beside the rows: lane r holds the row of
+// destination r (or -1), `dests` has bit r set for every routed destination.
+__device__ __forceinline__ void copy_scales(const DispatchParams &p, int64_t t, int slot, uint64_t dests, int lane) {
+    if (p.num_scales <= 0) return;
+    for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
+        const int i = i0 + lane;
+        const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
+        for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+            const int64_t s = readlane32(slot, __builtin_ctzll(dd));
+            if (i < p.num_scales) p.recv_scales[s * p.num_scales + i] = sc;
+        }
+    }
+}
+
+// send_slot of token t and the metadata (a4) of its rows: weights / local ids
+// of the topk slots living on each destination (lane j < k holds slot j's
+// expert id e and weight wt) and {my_rank, t} as the row's source.
+__device__ __forceinline__ void token_metadata(const DispatchParams &p, int64_t t, int slot, uint64_t dests,
+                                               int64_t e, float wt, int lane) {
+    if (lane < p.R) p.send_slot[t * p.R + lane] = slot;
+    const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
+    for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+        const int r = __builtin_ctzll(dd);
+        const int64_t s = readlane32(slot, r);
+        if (lane < p.K) {
+            const bool on = erank == r;
+            p.recv_w[s * p.K + lane] = on ? wt : 0.0f;
+            if (p.recv_idx != nullptr) p.recv_idx[s * p.K + lane] = on ? e - (int64_t)r * p.experts_per_rank : -1;
+        }
+        if (lane == 0) reinterpret_cast<int2 *>(p.src_info)[s] = make_int2(p.my_rank, (int)t);
+    }
+}
 
 // GRAN > 0: the block's waves sweep the destination ranks in order and meet at
 // a barrier every GRAN ranks, so the blocks' concurrent stores gather in a few
@@ -120,33 +155,8 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     if (!live) slot = -1;
     const uint64_t dests = ballot64(slot >= 0);
 
-    // ---- per-token scales (fp8 rows) travel beside the rows
-    if (live && seg == 0 && p.num_scales > 0) {
-        for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
-            const int i = i0 + lane;
-            const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
-            for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
-                const int64_t s = readlane32(slot, __builtin_ctzll(dd));
-                if (i < p.num_scales) p.recv_scales[s * p.num_scales + i] = sc;
-            }
-        }
-    }
-
-    if (!CACHED && live && seg == 0) {
-        if (lane < R) p.send_slot[t * R + lane] = slot;
-        // ---- metadata (a4): weights / local ids of the slots living on each destination
-        const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
-        for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
-            const int r = __builtin_ctzll(dd);
-            const int64_t s = readlane32(slot, r);
-            if (lane < p.K) {
-                const bool on = erank == r;
-                p.recv_w[s * p.K + lane] = on ? wt : 0.0f;
-                if (p.recv_idx != nullptr) p.recv_idx[s * p.K + lane] = on ? e - (int64_t)r * p.experts_per_rank : -1;
-            }
-            if (lane == 0) reinterpret_cast<int2 *>(p.src_info)[s] = make_int2(p.my_rank, (int)t);
-        }
-    }
+    if (live && seg == 0) copy_scales(p, t, slot, dests, lane);
+    if (!CACHED && live && seg == 0) token_metadata(p, t, slot, dests, e, wt, lane);
 
     // ---- row copy (a4): the segment to every destination, ranks ascending
     auto store_to = [&](uint64_t dd) {
@@ -168,6 +178,173 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
             __syncthreads();
         }
     }
+}
+
+// XCDs of the MI355X.  Consecutive workgroup ids are placed round-robin over
+// them, and each XCD has its own L2, so blocks with the same id modulo 8 share
+// one L2.  A different placement changes only the speed, never the result.
+constexpr int kXcds = 8;
+constexpr int64_t kMaxPullRowUnits = 1 << 16;  // 1 MiB rows
+
+// Pull form (many tokens): the rows are produced in receive order instead of
+// token order.  Tokens are taken in groups of CPG 64-token chunks; XCD j owns
+// groups j, j+8, ...  A group's rows for rank r are contiguous in slab r
+// (`rank_off` gives where they start and how many there are), so the group's
+// output is R runs of rows, ranks ascending.  The XCD's waves cut it into 1 KiB
+// pieces (64 lanes x 16 bytes) and take piece k, k+W, k+2W, ... (W = the XCD's
+// wave count): at any moment the XCD writes one narrow, advancing window,
+// like a fill.  Every piece reads its token's x piece with an ordinary load;
+// a token has ~R*(1-(1-1/R)^k) rows, and all but the first read hit the
+// group's x in the XCD's L2.  Before the pieces, the first GT waves of the XCD
+// each take one token of the group and write its send_slot, metadata and scales.
+template <int CPG, int U, bool EXACT, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParams p) {
+    constexpr int GT = CPG * kChunk;  // tokens per group
+    const int lane = threadIdx.x & (kWave - 1);
+    const int xcd = (int)(blockIdx.x % kXcds);
+    const int W = (int)(gridDim.x / kXcds) * WPB;  // waves per XCD; the grid is a multiple of kXcds
+    // wave index inside the XCD, made visibly wave-uniform so that the piece
+    // arithmetic below stays on the scalar unit
+    const int wx = (int)(blockIdx.x / kXcds) * WPB + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const uint64_t lanes_below = (1ull << lane) - 1ull;
+    const int R = p.R;
+    const int64_t G = (num_chunks(p.T) + CPG - 1) / CPG;
+    const int TPR = (int)((p.row_units + U * kWave - 1) / (U * kWave));  // tasks per row
+    const int step_rows = W / TPR, step_part = W - step_rows * TPR;
+
+    for (int64_t g = xcd; g < G; g += kXcds) {
+        const int64_t q0 = g * CPG;  // first chunk of the group
+        // The group's GT token tasks (send_slot, metadata, scales) go to waves
+        // kt = 0..GT-1, counted from an offset that moves on by GT every group so
+        // that they spread evenly over the XCD's waves.  A wave's first token's
+        // ids, weights and chunk offsets are loaded here, together with the
+        // group's masks, so its token task does not wait on memory later.
+        const int rot = (int)(((g / kXcds) * GT) % W);
+        const int kt = wx >= rot ? wx - rot : wx - rot + W;
+        const int64_t t1 = q0 * kChunk + kt;
+        const bool tok1 = kt < GT && t1 < p.T;
+        int64_t e1 = -1;
+        float w1 = 0.0f;
+        int base1 = 0;
+        if (tok1) {
+            if (lane < p.K) {
+                e1 = p.topk_idx[t1 * p.K + lane];
+                w1 = p.topk_w[t1 * p.K + lane];
+            }
+            if (lane < R) base1 = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[(q0 + kt / kChunk) * R + lane];
+        }
+        // lane r: bit l of col[c] set when token (q0 + c)*64 + l goes to rank r
+        uint64_t col[CPG];
+        int n = 0;
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) {
+            const int64_t tok = (q0 + c) * kChunk + lane;
+            col[c] = transpose64(tok < p.T ? p.mask[tok] : 0ull);
+            n += __popcll(col[c]);  // 0 on lanes >= R
+        }
+        // the group's rows on rank r: [s0, s0 + n) in slab r, run r of the
+        // group's output starting at pex
+        int s0 = 0;
+        if (lane < R) s0 = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q0 * R + lane];
+        const int incl = wave_inclusive_scan(n);
+        const int pex = lane < R ? incl - n : INT32_MAX;
+        const int rows = readlane32(incl, kWave - 1);
+
+        // ---- token tasks: send_slot, metadata, scales (more than one per wave
+        // only when the XCD has fewer than GT waves)
+        for (int k = kt; k < GT; k += W) {
+            const int64_t t = q0 * kChunk + k;
+            if (t >= p.T) break;  // wave-uniform; later k are larger
+            const int c = k / kChunk, l = k - c * kChunk;
+            uint64_t cc = col[0];
+#pragma unroll
+            for (int c2 = 1; c2 < CPG; ++c2)
+                if (c == c2) cc = col[c2];
+            int64_t e = e1;
+            float wt = w1;
+            int base = base1;
+            if (k != kt) {
+                e = -1;
+                wt = 0.0f;
+                if (lane < p.K) {
+                    e = p.topk_idx[t * p.K + lane];
+                    wt = p.topk_w[t * p.K + lane];
+                }
+                if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[(q0 + c) * R + lane];
+            }
+            int slot = -1;
+            if (lane < R && ((cc >> l) & 1ull)) slot = base + __popcll(cc & ((1ull << l) - 1ull));
+            const bool over = slot >= p.cap;
+            if (over) slot = -1;
+            if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+            const uint64_t dests = ballot64(slot >= 0);
+            copy_scales(p, t, slot, dests, lane);
+            token_metadata(p, t, slot, dests, e, wt, lane);
+        }
+
+        // ---- the group's rows in receive order.  A task is U consecutive
+        // pieces of one row (TPR tasks per row); the XCD's waves take tasks
+        // wx, wx+W, ... so its concurrent stores cover W*U KiB of consecutive
+        // output.  The routing is resolved once per task, and the task's row and
+        // part advance by a fixed step instead of a division per task.
+        // (rows * TPR < 2^31: at most 64*CPG*R rows, and the pull form is used
+        // for rows of at most kMaxPullRowUnits units.)
+        const int tasks = rows * TPR;
+        int rr = wx / TPR;  // row of the group's output
+        int part = wx - rr * TPR;
+        for (int k = wx; k < tasks; k += W) {
+            // its rank: the last lane whose run starts at or before rr
+            const int r = 63 - __builtin_clzll(ballot64(pex <= rr));
+            const int o = rr - readlane32(pex, r);
+            const int row = readlane32(s0, r) + o;
+            // its token: the o-th token of the group that goes to r
+            uint64_t cc = readlane64(col[0], r);
+            int c = 0, oc = o;
+#pragma unroll
+            for (int c2 = 1; c2 < CPG; ++c2) {
+                const int pc = __popcll(cc);
+                if (c == c2 - 1 && oc >= pc) {
+                    oc -= pc;
+                    c = c2;
+                    cc = readlane64(col[c2], r);
+                }
+            }
+            const bool hit = ((cc >> lane) & 1ull) && __popcll(cc & lanes_below) == oc;
+            const uint64_t sel = ballot64(hit);  // one bit: o < the run's length by construction
+            const int64_t t = sel != 0ull ? (q0 + c) * kChunk + __builtin_ctzll(sel) : q0 * kChunk;
+            // rows beyond the capacity are dropped (the token's wave flags them)
+            const bool row_ok = sel != 0ull && row >= 0 && row < p.cap;
+            const u32x4 *src = p.x + t * p.row_units + (int64_t)part * U * kWave + lane;
+            u32x4 *dst = p.recv_x + (int64_t)row * p.row_units + (int64_t)part * U * kWave + lane;
+            if (row_ok && (EXACT || (int64_t)(part + 1) * U * kWave <= p.row_units)) {
+                // a whole task: U loads in flight, then U stores, no branch between
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = src[u * kWave];
+#pragma unroll
+                for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + u * kWave);
+            } else if (row_ok) {
+                // the ragged last task of a row
+                const int64_t left = p.row_units - (int64_t)part * U * kWave - lane;
+#pragma unroll
+                for (int u = 0; u < U; ++u)
+                    if (u * kWave < left) __builtin_nontemporal_store(src[u * kWave], dst + u * kWave);
+            }
+            rr += step_rows;
+            part += step_part;
+            if (part >= TPR) {
+                part -= TPR;
+                ++rr;
+            }
+        }
+    }
+}
+
+template <int CPG, int U, bool EXACT, int WPB>
+hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
+    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
+                       dim3(WPB * kWave), 0, stream, p);
+    return hipGetLastError();
 }
 
 template <int VPL, bool EXACT, int WPB, int GRAN>
@@ -215,11 +392,43 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
     return hipErrorInvalidValue;
 }
 
-// Measured on MI355X (rows of 7168 bf16 or fp8 elements at 128..4096 tokens,
-// and the skew / large workloads).  Whole rows per wave with the rank sweep
+// Push-form tiling (cached mode at any size, and fewer than 2048 tokens
+// otherwise).  Measured on MI355X (rows of 7168 bf16 or fp8 elements at
+// 128..4096 tokens, and the skew / large workloads).  Whole rows per wave with the rank sweep
 // (16 waves per block, a barrier every 4 ranks) win once there are enough
 // tokens to give every compute unit a block; below that the rows are split so
 // more waves share the copy.  Other widths: 1 KiB segments, 8 waves per block.
+// Pull-form tiling: chunks per token group (cpg), pieces per task (u), waves
+// per block (wpb) and blocks per XCD (bpx); cpg == 0 selects the push form.
+struct PullTiling {
+    int cpg, u, wpb, bpx;
+};
+
+hipError_t run_pull_tiled(const DispatchParams &p, const PullTiling &t, hipStream_t stream) {
+    const bool exact = p.row_units % ((int64_t)t.u * kWave) == 0;
+#define EP_PULL_CASE(C, U, W) \
+    if (t.cpg == C && t.u == U && t.wpb == W) \
+        return exact ? run_pull<C, U, true, W>(p, t.bpx, stream) : run_pull<C, U, false, W>(p, t.bpx, stream);
+    EP_PULL_CASE(2, 2, 8)
+    EP_PULL_CASE(2, 4, 8)
+    EP_PULL_CASE(2, 8, 8)
+#undef EP_PULL_CASE
+    return hipErrorInvalidValue;
+}
+
+// Measured on MI355X (7168-element bf16 and fp8 rows at 1024..4096 tokens, and
+// 4096-element rows at 16384 tokens): from 2048 tokens (16 groups of 128, two
+// per XCD) the pull form is 6-19% faster than the push form; below that, and
+// for rows under 1 KiB, the push form is kept.  Groups of 128 tokens (1.8 MiB of
+// 7168-element bf16 rows) sit well inside an XCD's 4 MiB L2.  Tasks of two
+// pieces win for rows of 8 KiB and more; shorter rows take the whole row as
+// one task (4 or 8 pieces).  64 blocks of 8 waves per XCD: 16 waves per CU.
+PullTiling pull_tiling(int64_t row_units, int64_t num_tokens) {
+    if (row_units < kWave || row_units > kMaxPullRowUnits || num_tokens < 2048) return PullTiling{0, 0, 0, 0};
+    const int u = row_units >= 8 * kWave ? 2 : (row_units > 4 * kWave ? 8 : 4);
+    return PullTiling{2, u, 8, 64};
+}
+
 void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, int *gran) {
     *vpl = 1;
     *wpb = 8;
@@ -280,6 +489,10 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.cap = a.cap;
     p.num_scales = a.num_scales;
     p.S = 1;
+    if (p.cached_slot == nullptr) {
+        const PullTiling pt = pull_tiling(p.row_units, p.T);
+        if (pt.cpg > 0) return run_pull_tiled(p, pt, stream);
+    }
     int vpl, wpb, gran;
     dispatch_tiling(p.row_units, p.T, &vpl, &wpb, &gran);
     return run_tiled(p, vpl, wpb, gran, stream);

@@ -529,3 +529,54 @@ def test_every_call_without_a_status_word():
         if with_status:
             assert int(st.item()) & 3 == 3  # the bad id and the overflow were flagged
     assert all(torch.equal(a, b) for a, b in zip(*outs))
+
+
+# ---- the pull form of dispatch (from 2048 tokens, rows of 1 KiB or more):
+# ragged groups and chunks, ragged last tasks of a row, 1 / 3-node / 64 ranks,
+# duplicates and masked slots, k = 32, and a receive capacity below N.
+PULL = {
+    # name: (T, R, E, K, C, H, extra)
+    "groups_ragged_rows_513_units": (2100, 8, 64, 8, 6, 4104, {}),
+    "rows_1kib_r24_masked": (2049, 24, 48, 4, 7, 512, dict(mask_frac=0.2)),
+    "rows_7kib_r64_duplicates": (2304, 64, 256, 8, 24, 3584, dict(dup=True)),
+    "single_rank": (2048, 1, 4, 2, 3, 1024, {}),
+    "k32_r64": (2200, 64, 128, 32, 9, 2048, {}),
+    "half_masked": (4096, 32, 256, 8, 24, 1024, dict(mask_frac=0.5)),
+    "rows_16kib": (2048, 16, 64, 6, 5, 8192, {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PULL))
+def test_pull_dispatch_parity(name):
+    T, R, E, K, C, H_, extra = PULL[name]
+    print(f"[parity] pull={name}", flush=True)
+    x, idx, w = _random_case(T, R, E, K, C, H_, seed=len(name) + 100, **extra)
+    gpu, ref = H.run_both(x, idx, w, E, R, C)
+    assert H.compare(gpu, ref) == []
+    assert all(v == 0 for v in H.combine_bit_differences(gpu, ref).values())
+    assert gpu["dev_status"] == ref["status"] == 0
+
+
+def test_pull_dispatch_capacity_overflow():
+    print("[parity] pull capacity overflow", flush=True)
+    x, idx, w = _random_case(2100, 16, 64, 6, 5, 4104, seed=21)
+    import oracle
+    n = int(oracle.Oracle().layout(idx, 64, 16)["num_tokens_per_rank"].sum())
+    gpu, ref = H.run_both(x, idx, w, 64, 16, 5, capacity=n - 1000)
+    assert H.compare(gpu, ref) == []
+    assert gpu["dev_status"] & 2 and ref["status"] & 2
+    s = gpu["send_slot"]
+    assert np.array_equal(np.sort(s[s >= 0]), np.arange(n - 1000))
+
+
+def test_pull_fp8_ragged_groups_and_overflow():
+    print("[parity] pull fp8", flush=True)
+    x, idx, w = _random_case(2100, 64, 256, 8, 24, 7168, seed=22)
+    import oracle
+    n = int(oracle.Oracle().layout(idx, 256, 64)["num_tokens_per_rank"].sum())
+    gpu, ref = _fp8_case(x, idx, w, 256, 64, 24)
+    assert _exact(gpu, ref) == []
+    assert gpu["status"] == 0 == ref["status"]
+    gpu, ref = _fp8_case(x, idx, w, 256, 64, 24, capacity=n - 333)
+    assert _exact(gpu, ref) == []
+    assert gpu["status"] & 2 and ref["status"] & 2
