@@ -180,6 +180,23 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     }
 }
 
+// Position of the n-th (from 0) set bit of x, for n < popcount(x): a binary
+// search on the popcounts of halves.  With wave-uniform arguments it runs on
+// the scalar unit and leaves no vector register behind.
+// (Integer steps only: a bool here would be widened through a vector register.)
+__device__ __forceinline__ int nth_set_bit(uint64_t x, int n) {
+    int pos = 0;
+#pragma unroll
+    for (int w = 32; w >= 1; w >>= 1) {
+        const int c = __popcll(x & ((1ull << w) - 1ull));
+        const int take = (int)((uint32_t)(c - 1 - n) >> 31);  // 1 when n >= c
+        n -= take * c;
+        x >>= take * w;
+        pos += take * w;
+    }
+    return pos;
+}
+
 // XCDs of the MI355X.  Consecutive workgroup ids are placed round-robin over
 // them, and each XCD has its own L2, so blocks with the same id modulo 8 share
 // one L2.  A different placement changes only the speed, never the result.
@@ -190,14 +207,15 @@ constexpr int64_t kMaxPullRowUnits = 1 << 16;  // 1 MiB rows
 // token order.  Tokens are taken in groups of CPG 64-token chunks; XCD j owns
 // groups j, j+8, ...  A group's rows for rank r are contiguous in slab r
 // (`rank_off` gives where they start and how many there are), so the group's
-// output is R runs of rows, ranks ascending.  The XCD's waves cut it into 1 KiB
-// pieces (64 lanes x 16 bytes) and take piece k, k+W, k+2W, ... (W = the XCD's
-// wave count): at any moment the XCD writes one narrow, advancing window,
-// like a fill.  Every piece reads its token's x piece with an ordinary load;
-// a token has ~R*(1-(1-1/R)^k) rows, and all but the first read hit the
-// group's x in the XCD's L2.  Before the pieces, the first GT waves of the XCD
-// each take one token of the group and write its send_slot, metadata and scales.
-template <int CPG, int U, bool EXACT, int WPB>
+// output is R runs of rows, ranks ascending.  The XCD's waves cut it into
+// tasks of U 1 KiB pieces (a piece is 64 lanes x 16 bytes) and take task k,
+// k+W, k+2W, ... (W = the XCD's wave count): at any moment the XCD writes one
+// narrow, advancing window, like a fill.  Every task reads its token's x with
+// ordinary loads; a token has ~R*(1-(1-1/R)^k) rows, and all but the first
+// read hit the group's x in the XCD's L2.  Before its tasks, each group's GT
+// token tasks (send_slot, metadata, scales) go to GT of the XCD's waves, a
+// different set for each group.
+template <int CPG, int U, int NT, bool EXACT, int WPB>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParams p) {
     constexpr int GT = CPG * kChunk;  // tokens per group
     const int lane = threadIdx.x & (kWave - 1);
@@ -206,11 +224,9 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
     // wave index inside the XCD, made visibly wave-uniform so that the piece
     // arithmetic below stays on the scalar unit
     const int wx = (int)(blockIdx.x / kXcds) * WPB + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const uint64_t lanes_below = (1ull << lane) - 1ull;
     const int R = p.R;
     const int64_t G = (num_chunks(p.T) + CPG - 1) / CPG;
     const int TPR = (int)((p.row_units + U * kWave - 1) / (U * kWave));  // tasks per row
-    const int step_rows = W / TPR, step_part = W - step_rows * TPR;
 
     for (int64_t g = xcd; g < G; g += kXcds) {
         const int64_t q0 = g * CPG;  // first chunk of the group
@@ -290,59 +306,104 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
         // (rows * TPR < 2^31: at most 64*CPG*R rows, and the pull form is used
         // for rows of at most kMaxPullRowUnits units.)
         const int tasks = rows * TPR;
-        int rr = wx / TPR;  // row of the group's output
-        int part = wx - rr * TPR;
-        for (int k = wx; k < tasks; k += W) {
-            // its rank: the last lane whose run starts at or before rr
-            const int r = 63 - __builtin_clzll(ballot64(pex <= rr));
-            const int o = rr - readlane32(pex, r);
-            const int row = readlane32(s0, r) + o;
-            // its token: the o-th token of the group that goes to r
-            uint64_t cc = readlane64(col[0], r);
-            int c = 0, oc = o;
+        // The wave's tasks are k = wx + n*W, n = 0, 1, ...  They are routed 64 at
+        // a time, lane i taking task n = base + i on the vector unit: the row of
+        // the group's output and the part of it (rr, part), the rank (a binary
+        // search over the run starts), the row in the slab and the token (the
+        // o-th set bit of the rank's column).  The task loop then reads them
+        // back with two readlanes, so each task costs the scalar unit little
+        // more than its address arithmetic.
+        for (int base = 0; wx + base * W < tasks; base += kWave) {
+            int rt_row, rt_pack;  // lane i: task base + i: slab row; token | part << 8 | ok << 30
+            {
+                const int n = base + lane;
+                const int kk = wx + n * W;
+                const bool valid = kk < tasks;
+                const int k = valid ? kk : wx + base * W;
+                const int rr = k / TPR, part = k - rr * TPR;
+                int r = 0;
 #pragma unroll
-            for (int c2 = 1; c2 < CPG; ++c2) {
-                const int pc = __popcll(cc);
-                if (c == c2 - 1 && oc >= pc) {
-                    oc -= pc;
-                    c = c2;
-                    cc = readlane64(col[c2], r);
+                for (int step = 32; step >= 1; step >>= 1) {
+                    const int cand = r + step;
+                    if (__shfl(pex, cand, kWave) <= rr) r = cand;
                 }
+                const int o = rr - __shfl(pex, r, kWave);
+                const int row = __shfl(s0, r, kWave) + o;
+                uint64_t cc = 0;
+                int c = 0, oc = o;
+#pragma unroll
+                for (int c2 = 0; c2 < CPG; ++c2) {
+                    const uint32_t lo = __shfl((unsigned)(uint32_t)col[c2], r, kWave);
+                    const uint32_t hi = __shfl((unsigned)(uint32_t)(col[c2] >> 32), r, kWave);
+                    const uint64_t cq = ((uint64_t)hi << 32) | lo;
+                    if (c2 == 0) {
+                        cc = cq;
+                    } else {
+                        const int pc = __popcll(cc);
+                        if (c == c2 - 1 && oc >= pc) {
+                            oc -= pc;
+                            c = c2;
+                            cc = cq;
+                        }
+                    }
+                }
+                // o < the run's length by construction; checked, so that a bad
+                // offset can only drop the row, never pick a token past t
+                const bool found = oc < __popcll(cc);
+                const int tok = found ? c * kChunk + nth_set_bit(cc, oc) : 0;
+                const bool ok = valid && found && row >= 0 && row < p.cap;  // rows past the capacity: dropped
+                rt_row = ok ? row : 0;
+                rt_pack = tok | (part << 8) | ((int)ok << 30);
             }
-            const bool hit = ((cc >> lane) & 1ull) && __popcll(cc & lanes_below) == oc;
-            const uint64_t sel = ballot64(hit);  // one bit: o < the run's length by construction
-            const int64_t t = sel != 0ull ? (q0 + c) * kChunk + __builtin_ctzll(sel) : q0 * kChunk;
-            // rows beyond the capacity are dropped (the token's wave flags them)
-            const bool row_ok = sel != 0ull && row >= 0 && row < p.cap;
-            const u32x4 *src = p.x + t * p.row_units + (int64_t)part * U * kWave + lane;
-            u32x4 *dst = p.recv_x + (int64_t)row * p.row_units + (int64_t)part * U * kWave + lane;
-            if (row_ok && (EXACT || (int64_t)(part + 1) * U * kWave <= p.row_units)) {
-                // a whole task: U loads in flight, then U stores, no branch between
-                u32x4 v[U];
+            const int nb = (tasks - wx - base * W + W - 1) / W;  // tasks of this batch
+            const int nbatch = nb < kWave ? nb : kWave;
+            for (int j = 0; j < nbatch; j += NT) {
+                // NT tasks per pass: all their loads are issued, then all their
+                // stores.  A task past the batch, or lanes past a ragged row end,
+                // still load (from a valid place) so that no branch sits between
+                // the loads; only their stores are skipped.  Addresses are a
+                // wave-uniform base plus the fixed per-lane offset.
+                u32x4 v[NT][U];
+                u32x4 *dst[NT];
+                int lim[NT];
+                bool ok[NT];
 #pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = src[u * kWave];
+                for (int q = 0; q < NT; ++q) {
+                    const int jq = j + q < nbatch ? j + q : j;
+                    const int pk = readlane32(rt_pack, jq);
+                    const int row = readlane32(rt_row, jq);
+                    ok[q] = j + q < nbatch && (pk >> 30) != 0;
+                    const int64_t t = q0 * kChunk + (pk & 0xff);
+                    const int64_t first = (int64_t)((pk >> 8) & 0x3fffff) * U * kWave;
+                    lim[q] = (int)(p.row_units - first);
+                    const u32x4 *src = p.x + t * p.row_units + first;
+                    dst[q] = p.recv_x + (int64_t)row * p.row_units + first;
 #pragma unroll
-                for (int u = 0; u < U; ++u) __builtin_nontemporal_store(v[u], dst + u * kWave);
-            } else if (row_ok) {
-                // the ragged last task of a row
-                const int64_t left = p.row_units - (int64_t)part * U * kWave - lane;
+                    for (int u = 0; u < U; ++u) {
+                        const int cu = u * kWave + lane;
+                        v[q][u] = src[(EXACT || cu < lim[q]) ? cu : lim[q] - 1];
+                    }
+                }
+                // keeps the compiler from moving a load into its store's branch (a
+                // load there would be waited for before the next one is issued)
+                asm volatile("" ::: "memory");
 #pragma unroll
-                for (int u = 0; u < U; ++u)
-                    if (u * kWave < left) __builtin_nontemporal_store(src[u * kWave], dst + u * kWave);
-            }
-            rr += step_rows;
-            part += step_part;
-            if (part >= TPR) {
-                part -= TPR;
-                ++rr;
+                for (int q = 0; q < NT; ++q) {
+                    if (!ok[q]) continue;
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int cu = u * kWave + lane;
+                        if (EXACT || cu < lim[q]) __builtin_nontemporal_store(v[q][u], dst[q] + cu);
+                    }
+                }
             }
         }
     }
 }
 
-template <int CPG, int U, bool EXACT, int WPB>
+template <int CPG, int U, int NT, bool EXACT, int WPB>
 hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
-    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
+    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, NT, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
                        dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
 }
@@ -401,32 +462,36 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
 // Pull-form tiling: chunks per token group (cpg), pieces per task (u), waves
 // per block (wpb) and blocks per XCD (bpx); cpg == 0 selects the push form.
 struct PullTiling {
-    int cpg, u, wpb, bpx;
+    int cpg, u, nt, wpb, bpx;
 };
 
 hipError_t run_pull_tiled(const DispatchParams &p, const PullTiling &t, hipStream_t stream) {
     const bool exact = p.row_units % ((int64_t)t.u * kWave) == 0;
-#define EP_PULL_CASE(C, U, W) \
-    if (t.cpg == C && t.u == U && t.wpb == W) \
-        return exact ? run_pull<C, U, true, W>(p, t.bpx, stream) : run_pull<C, U, false, W>(p, t.bpx, stream);
-    EP_PULL_CASE(2, 2, 8)
-    EP_PULL_CASE(2, 4, 8)
-    EP_PULL_CASE(2, 8, 8)
+#define EP_PULL_CASE(C, U, N, W) \
+    if (t.cpg == C && t.u == U && t.nt == N && t.wpb == W) \
+        return exact ? run_pull<C, U, N, true, W>(p, t.bpx, stream) : run_pull<C, U, N, false, W>(p, t.bpx, stream);
+    EP_PULL_CASE(2, 1, 1, 8)
+    EP_PULL_CASE(2, 2, 1, 8)
+    EP_PULL_CASE(2, 4, 1, 8)
+    EP_PULL_CASE(2, 8, 1, 8)
 #undef EP_PULL_CASE
     return hipErrorInvalidValue;
 }
 
 // Measured on MI355X (7168-element bf16 and fp8 rows at 1024..4096 tokens, and
 // 4096-element rows at 16384 tokens): from 2048 tokens (16 groups of 128, two
-// per XCD) the pull form is 6-19% faster than the push form; below that, and
+// per XCD) the pull form is 9-20% faster than the push form; below that, and
 // for rows under 1 KiB, the push form is kept.  Groups of 128 tokens (1.8 MiB of
-// 7168-element bf16 rows) sit well inside an XCD's 4 MiB L2.  Tasks of two
-// pieces win for rows of 8 KiB and more; shorter rows take the whole row as
-// one task (4 or 8 pieces).  64 blocks of 8 waves per XCD: 16 waves per CU.
+// 7168-element bf16 rows) sit well inside an XCD's 4 MiB L2.  Tasks: one piece
+// for rows of 14 KiB and more (two tasks per pass, or more pieces per task,
+// measured slower); two pieces for rows of 7 to 14 KiB (as fast as one piece
+// with x in cache, and 12-15% faster than one piece when x has to come from
+// memory); the whole row (4 or 8 pieces) for shorter rows.  64 blocks of 8
+// waves per XCD: 16 waves per CU.
 PullTiling pull_tiling(int64_t row_units, int64_t num_tokens) {
-    if (row_units < kWave || row_units > kMaxPullRowUnits || num_tokens < 2048) return PullTiling{0, 0, 0, 0};
-    const int u = row_units >= 8 * kWave ? 2 : (row_units > 4 * kWave ? 8 : 4);
-    return PullTiling{2, u, 8, 64};
+    if (row_units < kWave || row_units > kMaxPullRowUnits || num_tokens < 2048) return PullTiling{0, 0, 0, 0, 0};
+    const int u = row_units >= 14 * kWave ? 1 : row_units >= 7 * kWave ? 2 : row_units > 4 * kWave ? 8 : 4;
+    return PullTiling{2, u, 1, 8, 64};
 }
 
 void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, int *gran) {
