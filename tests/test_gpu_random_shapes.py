@@ -4,7 +4,9 @@
 64-token chunk boundaries, 1 to 64 ranks (with 3- and 5-node layouts),
 1 to 32 local experts, topk up to 32, 1 to 49 channels, rows of 8 to 1024
 elements, expert alignments, masked and duplicate ids, and now and then a
-receive capacity a few rows short."""
+receive capacity a few rows short.  Eight more configurations take dispatch's
+pull form: 2048 to 4100 tokens (ragged 128-token groups), rows of 512 to 7168
+elements (ragged last tasks), 1 to 64 ranks, a capacity 500 rows short."""
 import numpy as np
 import pytest
 
@@ -47,6 +49,43 @@ def test_random_shape(case):
     g, want = _group_case(x, idx, w, s["E"], s["R"], s["C"], s["align"])
     assert _group_diff(g, want) == []
     if case % 2 == 0:  # rows of whole 16-byte units as fp8 (H % 16 == 0), 8-element scale blocks
+        g8, r8 = _fp8_case(x, idx, w, s["E"], s["R"], s["C"], num_scales_block=8, capacity=cap)
+        assert _exact(g8, r8) == []
+        assert g8["status"] == r8["status"]
+
+
+PULL_CASES = 8
+
+
+def draw_pull(case: int) -> dict:
+    """Shapes that take dispatch's pull form: 2048 tokens or more (ragged 128-token
+    groups), rows of 1 KiB or more, ragged last tasks of a row."""
+    rng = np.random.default_rng(6000 + case)
+    R = int(rng.choice([1, 8, 16, 24, 32, 64]))
+    er = int(rng.choice([1, 2, 4, 8]))
+    E = R * er
+    K = int(rng.integers(1, min(8, E) + 1))
+    return dict(
+        T=int(rng.choice([2048, 2049, 2111, 2176, 3000, 4100])), R=R, E=E, K=K, C=int(rng.integers(1, 40)),
+        H=int(rng.choice([512, 520, 1000, 2056, 3592, 7168])), align=int(rng.choice([1, 4, 8])),
+        mask=float(rng.choice([0.0, 0.2])), dup=bool(case % 3 == 1), short=bool(case % 4 == 2))
+
+
+@pytest.mark.parametrize("case", range(PULL_CASES))
+def test_random_shape_pull(case):
+    s = draw_pull(case)
+    print(f"[parity] random pull case {case}: {s}", flush=True)
+    x, idx, w = _random_case(s["T"], s["R"], s["E"], s["K"], s["C"], s["H"], seed=7000 + case, mask_frac=s["mask"],
+                             dup=s["dup"])
+    n = int(oracle.Oracle().layout(idx, s["E"], s["R"])["num_tokens_per_rank"].sum())
+    cap = max(0, n - 500) if s["short"] else None
+    gpu, ref = H.run_both(x, idx, w, s["E"], s["R"], s["C"], align=s["align"], capacity=cap)
+    assert H.compare(gpu, ref) == []
+    assert H.combine_bit_differences(gpu, ref) == {"combined_x": 0}
+    assert gpu["dev_status"] == ref["status"]
+    g, want = _group_case(x, idx, w, s["E"], s["R"], s["C"], s["align"])
+    assert _group_diff(g, want) == []
+    if case % 2 == 0 and s["H"] % 16 == 0:  # fp8 rows of whole 16-byte units, 8-element scale blocks
         g8, r8 = _fp8_case(x, idx, w, s["E"], s["R"], s["C"], num_scales_block=8, capacity=cap)
         assert _exact(g8, r8) == []
         assert g8["status"] == r8["status"]
