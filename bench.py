@@ -67,6 +67,13 @@ def group_bytes(H, K, N, M) -> int:
     return N * 2 * H + M * 2 * H + N * K * (8 + 4 + 4) + M * (4 + 4)
 
 
+def dispatch_grouped_bytes(T, H, K, R, N, M) -> int:
+    """dispatch straight into the grouped layout: x, ids and weights read once,
+    the receive metadata and send_slot written, the slot->position map, and
+    every grouped row with its index and weight written (no receive rows)."""
+    return T * 2 * H + 12 * T * K + 4 * T * R + N * (12 * K + 8) + 4 * N * K + M * (2 * H + 8)
+
+
 def layout_notify_bytes(T, K, R, E, C) -> int:
     nodes = max(1, R // 8)
     return T * K * 8 + T * R + 4 * (R + nodes + E) + T * R + 4 * (R + nodes + E) + 4 * (R + nodes) * (C + 1) + 4 * E
@@ -78,6 +85,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
+                  "dispatch_grouped_kernels": ["ep_dispatch.hip", "ep_group.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
 
@@ -325,6 +333,20 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
                         ("dispatch_cached_fp8", "dispatch_kernel_cached_fp8")):
         out[key]["traffic"] = measured_traffic(kernel, wl.name)
     out["group_by_expert"]["traffic"] = measured_traffic("group_kernels", wl.name)
+    # dispatch straight into the grouped layout: same grouped rows, no receive rows
+    # (the two-call result it is checked against is made first)
+    g = ep.allocate_group(b, M)
+    ep.run_group(b, g, n_recv)
+    g2 = ep.allocate_group(b, M)
+    out["dispatch_grouped"] = rate(dispatch_grouped_bytes(T, H, K, R, n_recv, M),
+                                   mean_us(lambda: ep.run_dispatch_grouped(b, g2, x, idx, w)))
+    torch.cuda.synchronize()
+    out["dispatch_grouped"]["check"] = bool(
+        int(g2.num_grouped.item()) == M and torch.equal(g2.grouped_row, g.grouped_row)
+        and torch.equal(g2.grouped_x.view(torch.int16), g.grouped_x.view(torch.int16)))
+    out["dispatch_grouped"]["grouped_rows"] = M
+    out["dispatch_grouped"]["traffic"] = measured_traffic("dispatch_grouped_kernels", wl.name)
+    del g, g2
     out["dev_status"] = int(b.dev_status.item())
     return out
 

@@ -237,6 +237,83 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
     return from_hip(launch_group(*s, a, stream));
 }
 
+ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
+                                int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                                const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
+                                const void *workspace, size_t workspace_bytes, int32_t recv_capacity,
+                                float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
+                                int32_t *send_slot, int32_t grouped_capacity, void *grouped_x,
+                                float *grouped_x_scales, int32_t *grouped_row, float *grouped_weights,
+                                int32_t *slot_pos, int32_t *num_grouped_rows, int32_t *dev_status,
+                                hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (elem_bytes != 1 && elem_bytes != 2) return EP_ERR_INVALID_ARG;
+    const int64_t row_bytes = (int64_t)s->hidden * elem_bytes;
+    if (row_bytes % 16 != 0 || recv_capacity < 0 || grouped_capacity < 0 || num_scales < 0)
+        return EP_ERR_INVALID_ARG;
+    if (num_scales > kMaxScales || s->num_experts / s->num_ranks > kMaxGroupExperts) return EP_ERR_UNSUPPORTED;
+    if ((int64_t)recv_capacity * s->num_topk > INT32_MAX) return EP_ERR_UNSUPPORTED;
+    if (recv_gbl_rank_prefix_sum == nullptr || num_recv_tokens_per_expert == nullptr || num_grouped_rows == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && (recv_topk_weights == nullptr || recv_topk_idx == nullptr || recv_src_info == nullptr ||
+                              slot_pos == nullptr))
+        return EP_ERR_INVALID_ARG;
+    if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
+    if (grouped_capacity > 0 && (grouped_x == nullptr || grouped_row == nullptr)) return EP_ERR_INVALID_ARG;
+    if (grouped_x != nullptr && !aligned16(grouped_x)) return EP_ERR_INVALID_ARG;
+    if (num_scales > 0 && ((s->num_tokens > 0 && x_scales == nullptr) ||
+                           (grouped_capacity > 0 && grouped_x_scales == nullptr)))
+        return EP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0) {
+        if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr)
+            return EP_ERR_INVALID_ARG;
+        if (!aligned16(x) || !workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
+        // 1. the receive metadata, with no receive rows
+        DispatchArgs d = {};
+        d.x = x;
+        d.row_units = row_bytes / 16;
+        d.topk_idx = topk_idx;
+        d.topk_w = topk_weights;
+        d.recv_gbl = recv_gbl_rank_prefix_sum;
+        d.ws = static_cast<const char *>(workspace);
+        d.cap = recv_capacity;
+        d.recv_w = recv_topk_weights;
+        d.recv_idx = recv_topk_idx;
+        d.src_info = recv_src_info;
+        d.send_slot = send_slot;
+        d.dev_status = dev_status;
+        hipError_t e = launch_dispatch(*s, d, stream);
+        if (e != hipSuccess) return EP_ERR_HIP;
+    }
+    // 2. positions over the capacity's rows (rows past the last slab are not read),
+    // 3. each token's row read once from x and stored at its slots' grouped positions,
+    //    then the padding rows zeroed
+    GroupArgs a = {};
+    a.recv_x = x;
+    a.from_x = true;
+    a.topk_idx = topk_idx;
+    a.send_slot = send_slot;
+    a.num_tokens = s->num_tokens;
+    a.row_units = row_bytes / 16;
+    a.recv_scales = x_scales;
+    a.num_scales = num_scales;
+    a.recv_idx = recv_topk_idx;
+    a.recv_w = recv_topk_weights;
+    a.recv_gbl = recv_gbl_rank_prefix_sum;
+    a.aligned = num_recv_tokens_per_expert;
+    a.num_rows = recv_capacity;
+    a.cap = grouped_capacity;
+    a.grouped_x = grouped_x;
+    a.grouped_scales = grouped_x_scales;
+    a.grouped_row = grouped_row;
+    a.grouped_w = grouped_weights;
+    a.slot_pos = slot_pos;
+    a.num_grouped = num_grouped_rows;
+    a.dev_status = dev_status;
+    return from_hip(launch_group(*s, a, stream));
+}
+
 ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_topk_weights, const int32_t *send_slot,
                        int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
                        hipStream_t stream) {

@@ -108,7 +108,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     // ---- the x segment: issued first, consumed last
     const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
     const u32x4 *src = p.x + t * p.row_units + c0;
-    u32x4 v[VPL];
+    u32x4 v[VPL > 0 ? VPL : 1];  // VPL == 0: metadata only, no row
 #pragma unroll
     for (int i = 0; i < VPL; ++i)
         if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
@@ -158,6 +158,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     if (live && seg == 0) copy_scales(p, t, slot, dests, lane);
     if (!CACHED && live && seg == 0) token_metadata(p, t, slot, dests, e, wt, lane);
 
+    if (VPL == 0) return;  // metadata only
     // ---- row copy (a4): the segment to every destination, ranks ascending
     auto store_to = [&](uint64_t dd) {
         for (; dd != 0ull; dd &= dd - 1ull) {
@@ -521,6 +522,15 @@ void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, 
 
 }  // namespace
 
+// Metadata only (no receive rows): send_slot, weights, local ids, src_info,
+// one wave per token.
+hipError_t run_meta(DispatchParams p, hipStream_t stream) {
+    p.S = 1;
+    const int64_t blocks = (p.T + 7) / 8;
+    hipLaunchKernelGGL((dispatch_kernel<0, true, 8, 0, false>), dim3((unsigned)blocks), dim3(8 * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
 hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream) {
     if (s.num_tokens == 0) return hipSuccess;
     DispatchParams p;
@@ -554,6 +564,10 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.cap = a.cap;
     p.num_scales = a.num_scales;
     p.S = 1;
+    if (p.recv_x == nullptr && p.cached_slot == nullptr) {
+        p.num_scales = 0;  // no rows, so no scales beside them
+        return run_meta(p, stream);
+    }
     if (p.cached_slot == nullptr) {
         const PullTiling pt = pull_tiling(p.row_units, p.T);
         if (pt.cpg > 0) return run_pull_tiled(p, pt, stream);

@@ -327,10 +327,11 @@ __global__ __launch_bounds__(WPB *kWave) void group_copy_kernel(CopyParams p) {
         if (lane == 0 && seg == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
         row = -1;
     }
+    const int64_t srow = row;
     const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
     u32x4 *dst = p.dst + g * p.row_units + c0;
     if (row >= 0) {
-        const u32x4 *src = p.src + (int64_t)row * p.row_units + c0;
+        const u32x4 *src = p.src + srow * p.row_units + c0;
         u32x4 v[VPL];
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
@@ -346,8 +347,88 @@ __global__ __launch_bounds__(WPB *kWave) void group_copy_kernel(CopyParams p) {
     }
     if (seg == 0) {
         for (int i = lane; i < p.num_scales; i += kWave)
-            p.dst_scales[g * p.num_scales + i] = row >= 0 ? p.src_scales[(int64_t)row * p.num_scales + i] : 0.0f;
+            p.dst_scales[g * p.num_scales + i] = row >= 0 ? p.src_scales[srow * p.num_scales + i] : 0.0f;
     }
+}
+
+// ---- straight from x (dispatch into the grouped layout): each token's row is
+// read once and stored to every grouped position of its slots, found through
+// send_slot (the receive row on the slot's rank) and slot_pos (the row's entry);
+// then the padding rows are zeroed.
+struct PushParams {
+    const u32x4 *x;
+    const float *x_scales;
+    const int64_t *topk_idx;
+    const int32_t *send_slot;
+    const int32_t *slot_pos;
+    const int32_t *num_grouped;
+    u32x4 *dst;
+    float *dst_scales;
+    int64_t T, row_units, num_rows, cap;
+    int R, K, E, er, S, num_scales;
+};
+
+template <int VPL, bool EXACT, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void group_push_kernel(PushParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    if (w >= p.T * p.S) return;  // whole wave
+    const int64_t t = w / p.S;
+    const int seg = (int)(w - t * p.S);
+    // the x segment first, consumed last
+    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
+    const u32x4 *src = p.x + t * p.row_units + c0;
+    u32x4 v[VPL];
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+        if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+    // lane j < k: the grouped position of slot j, or -1 (masked, dropped, or past the
+    // written grouped rows)
+    int64_t limit = p.num_grouped[0];
+    limit = limit < p.cap ? limit : p.cap;
+    int pos = -1;
+    if (lane < p.K) {
+        const int64_t e = p.topk_idx[t * p.K + lane];
+        if (e >= 0 && e < p.E) {
+            const int s = p.send_slot[t * p.R + (int)(e / p.er)];
+            if (s >= 0 && s < p.num_rows) pos = p.slot_pos[(int64_t)s * p.K + lane];
+        }
+        if (pos >= limit) pos = -1;
+    }
+    const uint64_t dests = ballot64(pos >= 0);
+    for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
+        const int64_t g = readlane32(pos, __builtin_ctzll(dd));
+        u32x4 *dst = p.dst + g * p.row_units + c0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
+        if (seg == 0)
+            for (int i = lane; i < p.num_scales; i += kWave)
+                p.dst_scales[g * p.num_scales + i] = p.x_scales[t * p.num_scales + i];
+    }
+}
+
+// Padding rows (grouped_row -1) of the written grouped rows: zero rows and scales.
+__global__ __launch_bounds__(256) void group_pad_kernel(const int32_t *grouped_row, const int32_t *num_grouped,
+                                                        u32x4 *dst, float *dst_scales, int64_t row_units,
+                                                        int64_t cap, int num_scales) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t g = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    int64_t limit = num_grouped[0];
+    limit = limit < cap ? limit : cap;
+    if (g >= limit || grouped_row[g] != -1) return;  // whole wave
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t u = lane; u < row_units; u += kWave) __builtin_nontemporal_store(z, dst + g * row_units + u);
+    for (int i = lane; i < num_scales; i += kWave) dst_scales[g * num_scales + i] = 0.0f;
+}
+
+template <int VPL, bool EXACT, int WPB>
+hipError_t run_push(PushParams p, hipStream_t stream) {
+    p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
+    const int64_t blocks = (p.T * p.S + WPB - 1) / WPB;
+    hipLaunchKernelGGL((group_push_kernel<VPL, EXACT, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, stream,
+                       p);
+    return hipGetLastError();
 }
 
 template <int VPL, bool EXACT, int WPB>
@@ -413,6 +494,43 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
         hipLaunchKernelGGL(group_positions_kernel<32>, grid, dim3(kGroupThreads), lds, stream, q);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.cap == 0) return err;
+
+    if (a.from_x) {  // rows straight from x
+        if (a.num_tokens > 0) {
+            PushParams u;
+            u.x = reinterpret_cast<const u32x4 *>(a.recv_x);
+            u.x_scales = a.recv_scales;
+            u.topk_idx = a.topk_idx;
+            u.send_slot = a.send_slot;
+            u.slot_pos = a.slot_pos;
+            u.num_grouped = a.num_grouped;
+            u.dst = reinterpret_cast<u32x4 *>(a.grouped_x);
+            u.dst_scales = a.grouped_scales;
+            u.T = a.num_tokens;
+            u.row_units = a.row_units;
+            u.num_rows = a.num_rows;
+            u.cap = a.cap;
+            u.R = s.num_ranks;
+            u.K = s.num_topk;
+            u.E = s.num_experts;
+            u.er = s.num_experts / s.num_ranks;
+            u.num_scales = a.num_scales;
+            u.S = 1;
+            // the push tiling of the receive dispatch: 7 KiB segments, 4 waves per block
+            // for 7168-element bf16 rows, 1 KiB segments otherwise
+            if (a.row_units % (7 * kWave) == 0)
+                err = run_push<7, true, 4>(u, stream);
+            else if (a.row_units % kWave == 0)
+                err = run_push<1, true, 8>(u, stream);
+            else
+                err = run_push<1, false, 8>(u, stream);
+            if (err != hipSuccess) return err;
+        }
+        hipLaunchKernelGGL(group_pad_kernel, dim3((unsigned)((a.cap + 3) / 4)), dim3(256), 0, stream, a.grouped_row,
+                           a.num_grouped, reinterpret_cast<u32x4 *>(a.grouped_x), a.grouped_scales, a.row_units, a.cap,
+                           a.num_scales);
+        return hipGetLastError();
+    }
 
     CopyParams c;
     c.src = reinterpret_cast<const u32x4 *>(a.recv_x);

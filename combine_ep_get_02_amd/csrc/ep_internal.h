@@ -94,9 +94,13 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
 // Arguments of the grouping by local expert (one launch computing positions,
 // one copying rows).  Rows are row_units 16-byte units.
 struct GroupArgs {
-    const void *recv_x;
+    const void *recv_x;        // [N][row]; or x [t][row] when topk_idx is given
+    bool from_x;               // rows straight from x (through topk_idx, send_slot, slot_pos), not recv_x
+    const int64_t *topk_idx;   // [t][k] (from_x)
+    const int32_t *send_slot;  // [t][R] (from_x)
+    int64_t num_tokens;        // t (from_x)
     int64_t row_units;
-    const float *recv_scales;  // [N][num_scales], null when num_scales == 0
+    const float *recv_scales;  // [N][num_scales] (or x's [t][num_scales]), null when num_scales == 0
     int num_scales;
     const int64_t *recv_idx;   // [N][k] local expert ids
     const float *recv_w;       // [N][k], may be null
@@ -108,7 +112,7 @@ struct GroupArgs {
     float *grouped_scales;
     int32_t *grouped_row;      // [cap]
     float *grouped_w;          // [cap], may be null
-    int32_t *slot_pos;         // [N][k], may be null
+    int32_t *slot_pos;         // [N][k], may be null (not with from_x)
     int32_t *num_grouped;      // [1]
     int32_t *dev_status;
 };

@@ -21,7 +21,7 @@ EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
 EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
 
 EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-            "ep_group_by_expert", "ep_combine", "ep_workspace_bytes", "ep_status_string")
+            "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
 class EpError(RuntimeError):
@@ -57,9 +57,11 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
     lib.ep_group_by_expert.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
                                        ctypes.c_int32] + [_P] * 8
+    lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+                                        ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
     for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-                 "ep_group_by_expert", "ep_combine"):
+                 "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -169,6 +171,21 @@ def ep_group_by_expert(shape, recv_x, elem_bytes, recv_x_scales, num_scales, rec
            "ep_group_by_expert")
 
 
+def ep_dispatch_grouped(shape, x, elem_bytes, x_scales, num_scales, topk_idx, topk_weights, recv_gbl_rank_prefix_sum,
+                        num_recv_tokens_per_expert, workspace, recv_capacity, recv_topk_weights, recv_topk_idx,
+                        recv_src_info, send_slot, grouped_capacity, grouped_x, grouped_x_scales, grouped_row,
+                        grouped_weights, slot_pos, num_grouped_rows, dev_status=None, stream=None) -> None:
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().ep_dispatch_grouped(ctypes.byref(shape), _ptr(x), int(elem_bytes), _ptr(x_scales), int(num_scales),
+                                      _ptr(topk_idx), _ptr(topk_weights), _ptr(recv_gbl_rank_prefix_sum),
+                                      _ptr(num_recv_tokens_per_expert), _ptr(workspace), ws_bytes, int(recv_capacity),
+                                      _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info),
+                                      _ptr(send_slot), int(grouped_capacity), _ptr(grouped_x), _ptr(grouped_x_scales),
+                                      _ptr(grouped_row), _ptr(grouped_weights), _ptr(slot_pos),
+                                      _ptr(num_grouped_rows), _ptr(dev_status), _stream(stream)),
+           "ep_dispatch_grouped")
+
+
 def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x, combined_topk_weights=None,
                dev_status=None, stream=None) -> None:
     _check(load().ep_combine(ctypes.byref(shape), _ptr(y), _ptr(recv_topk_weights), _ptr(send_slot),
@@ -271,3 +288,10 @@ def run_group(b: Buffers, g: GroupBuffers, num_recv_rows=None, stream=None) -> N
     ep_group_by_expert(b.shape, b.recv_x, 2, None, 0, b.recv_idx, b.recv_w, b.recv_gbl, b.recv_per_expert,
                        b.capacity if num_recv_rows is None else num_recv_rows, g.capacity, g.grouped_x, None,
                        g.grouped_row, g.grouped_w, g.slot_pos, g.num_grouped, b.dev_status, stream)
+
+
+def run_dispatch_grouped(b: Buffers, g: GroupBuffers, x, topk_idx, topk_weights, stream=None) -> None:
+    """Dispatch of bf16 rows straight into g's grouped layout (b.recv_x is neither written nor read)."""
+    ep_dispatch_grouped(b.shape, x, 2, None, 0, topk_idx, topk_weights, b.recv_gbl, b.recv_per_expert, b.workspace,
+                        b.capacity, b.recv_w, b.recv_idx, b.src_info, b.send_slot, g.capacity, g.grouped_x, None,
+                        g.grouped_row, g.grouped_w, g.slot_pos, g.num_grouped, b.dev_status, stream)

@@ -13,6 +13,7 @@
  *   ep_dispatch_fp8     dispatch of 1-byte (fp8) rows with their per-token scales
  *   ep_dispatch_cached  new rows to the rows an earlier dispatch assigned (cached mode)
  *   ep_group_by_expert  receive rows regrouped into per-expert segments for grouped GEMMs
+ *   ep_dispatch_grouped dispatch straight into those segments, with no receive rows
  *   ep_workspace_bytes, ep_status_string
  * Every call is stream-ordered and allocates nothing, so a sequence of them can be
  * captured in a HIP graph (ep_notify without its host read-back).
@@ -222,6 +223,34 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
                                int32_t grouped_capacity, void *grouped_x, float *grouped_x_scales,
                                int32_t *grouped_row, float *grouped_weights, int32_t *slot_pos,
                                int32_t *num_grouped_rows, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Dispatch straight into the grouped layout: the outputs of ep_dispatch (or ep_dispatch_fp8)
+ * followed by ep_group_by_expert with num_recv_rows = recv_capacity, without the receive rows.
+ * [the pages' dispatch as for ep_dispatch; the grouping as for ep_group_by_expert]
+ * Writes recv_topk_weights, recv_topk_idx, recv_src_info and send_slot exactly as ep_dispatch
+ * does, and every output of ep_group_by_expert for those rows (recv_topk_idx and slot_pos are
+ * required here: the grouping reads the ids, and each token's row is read once from x and
+ * stored at the grouped positions slot_pos gives its slots):
+ *   grouped_x [grouped_capacity][h] = x[t] of the entry's row (bf16 when elem_bytes == 2,
+ *             1-byte elements when elem_bytes == 1); grouped_x_scales = that token's
+ *             x_scales (num_scales per token, nullable when 0); padding rows are zero.
+ * No recv_x is written or read.  In: x, x_scales, topk_idx, topk_weights as for
+ * ep_dispatch / ep_dispatch_fp8; recv_gbl_rank_prefix_sum and num_recv_tokens_per_expert as
+ * ep_notify wrote them; the workspace as ep_notify left it.  Receive rows at or past
+ * recv_capacity are dropped as in ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.
+ * dev_status (nullable): the flags of both calls.  Limits as for both calls.
+ * Four launches (receive metadata, positions, rows, padding).
+ */
+ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
+                                int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                                const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
+                                const void *workspace, size_t workspace_bytes, int32_t recv_capacity,
+                                float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
+                                int32_t *send_slot, int32_t grouped_capacity, void *grouped_x,
+                                float *grouped_x_scales, int32_t *grouped_row, float *grouped_weights,
+                                int32_t *slot_pos, int32_t *num_grouped_rows, int32_t *dev_status,
+                                hipStream_t stream);
 
 /*
  * Stage 5, combine.  [mscclpp ht_runtime.cc, internodeCombine / intranodeCombine (bf16 out,

@@ -32,9 +32,8 @@ def declared_functions():
 
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8",
-                                          "ep_dispatch_cached", "ep_group_by_expert", "ep_combine",
-                                          "ep_workspace_bytes",
-                                          "ep_status_string"])
+                                          "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
+                                          "ep_combine", "ep_workspace_bytes", "ep_status_string"])
 
 
 def test_library_exports_every_declared_symbol(ep):
@@ -172,6 +171,45 @@ def test_group_by_expert_argument_checks(ep):
     assert group(ns=2000, scales=p, gscales=p) == ep.EP_ERR_UNSUPPORTED
     assert group(shape=_shape(ep, num_experts=1024, num_ranks=1)) == ep.EP_ERR_UNSUPPORTED  # 1024 local experts
     assert group(rows=(1 << 31) // 8) == ep.EP_ERR_UNSUPPORTED  # rows * k reaches 2^31
+
+
+def test_dispatch_grouped_argument_checks(ep):
+    # every call below breaks exactly one rule, so it is refused before any launch
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    odd = ctypes.c_void_p(264)
+    s = _shape(ep)
+
+    def grouped(shape=s, x=p, elem=2, xs=None, ns=0, idx=p, w=p, gbl=p, aligned=p, ws=p, wsb=1 << 30, cap=10, rw=p,
+                ridx=p, src=p, slot=p, gcap=10, gx=p, gxs=None, grow=p, gw=p, pos=p, m=p):
+        return lib.ep_dispatch_grouped(ctypes.byref(shape), x, elem, xs, ns, idx, w, gbl, aligned, ws, wsb, cap, rw,
+                                       ridx, src, slot, gcap, gx, gxs, grow, gw, pos, m, None, None)
+
+    assert grouped(elem=3) == ep.EP_ERR_INVALID_ARG
+    assert grouped(shape=_shape(ep, hidden=7160), elem=1) == ep.EP_ERR_INVALID_ARG  # not whole 16-byte units
+    assert grouped(cap=-1) == ep.EP_ERR_INVALID_ARG
+    assert grouped(gcap=-1) == ep.EP_ERR_INVALID_ARG
+    assert grouped(m=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(gbl=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(aligned=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(ridx=None) == ep.EP_ERR_INVALID_ARG  # the grouping reads the receive ids
+    assert grouped(rw=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(src=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(pos=None) == ep.EP_ERR_INVALID_ARG  # the rows are stored through slot_pos
+    assert grouped(src=ctypes.c_void_p(260)) == ep.EP_ERR_INVALID_ARG  # src_info is 8-byte aligned
+    assert grouped(grow=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(gx=odd) == ep.EP_ERR_INVALID_ARG
+    assert grouped(x=odd) == ep.EP_ERR_INVALID_ARG
+    assert grouped(x=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(idx=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(w=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(slot=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(wsb=10) == ep.EP_ERR_INVALID_ARG  # short workspace
+    assert grouped(ns=4, gxs=p) == ep.EP_ERR_INVALID_ARG  # x scales missing
+    assert grouped(ns=4, xs=p) == ep.EP_ERR_INVALID_ARG  # grouped scales missing
+    assert grouped(ns=2000, xs=p, gxs=p) == ep.EP_ERR_UNSUPPORTED
+    assert grouped(shape=_shape(ep, num_experts=1024, num_ranks=1)) == ep.EP_ERR_UNSUPPORTED  # 1024 local experts
+    assert grouped(cap=(1 << 31) // 8) == ep.EP_ERR_UNSUPPORTED  # rows * k reaches 2^31
 
 
 def test_empty_dispatch_and_combine_enqueue_nothing(ep):

@@ -580,3 +580,112 @@ def test_pull_fp8_ragged_groups_and_overflow():
     gpu, ref = _fp8_case(x, idx, w, 256, 64, 24, capacity=n - 333)
     assert _exact(gpu, ref) == []
     assert gpu["status"] & 2 and ref["status"] & 2
+
+
+# ---- dispatch straight into the grouped layout (ep_dispatch_grouped): every output
+# equals the oracle's dispatch followed by its grouping with num_recv_rows = the
+# receive capacity; no receive rows are written.
+def _dispatch_grouped_case(x, idx, w, E, R, C, align, fp8=False, recv_delta=0, gcap_delta=0):
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+    from combine_ep_get_02_amd.inputs import fp8_rows
+
+    T, K = idx.shape
+    xs, sc = (fp8_rows(x) if fp8 else (x, None))
+    NS = 0 if sc is None else sc.shape[1]
+    Hd = xs.shape[1]
+    o = oracle.Oracle()
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, align)
+    n = note["num_recv_tokens"]
+    rcap = max(n + recv_delta, 0)
+    args = (idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], E)
+    d = o.dispatch_fp8(xs, sc, *args, recv_capacity=rcap) if fp8 else o.dispatch(xs, *args, recv_capacity=rcap)
+    aligned = note["num_recv_tokens_per_expert"]
+    gcap = max(int(np.maximum(aligned, 0).sum()) + gcap_delta, 0)
+    ref = o.group_by_expert(d["recv_x"], d["recv_topk_idx"], d["recv_topk_weights"], note["recv_gbl_rank_prefix_sum"],
+                            aligned, E, grouped_capacity=gcap, recv_x_scales=d["recv_x_scales"] if fp8 else None,
+                            num_recv_rows=rcap)
+
+    shape = ep.make_shape(T, x.shape[1], K, E, R, C, 0, align)
+    b = ep.allocate(shape, 0)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    ep.run_notify(b)
+    rw = torch.full((max(rcap, 1), K), -3.0, dtype=torch.float32, device="cuda")
+    ri = torch.full((max(rcap, 1), K), -777, dtype=torch.int64, device="cuda")
+    si = torch.full((max(rcap, 1), 2), -777, dtype=torch.int32, device="cuda")
+    ss = torch.full((T, R), -777, dtype=torch.int32, device="cuda")
+    elem = 1 if fp8 else 2
+    gx = torch.full((max(gcap, 1), Hd * elem), 0x5A, dtype=torch.uint8, device="cuda")
+    gs = torch.full((max(gcap, 1), max(NS, 1)), -9.0, dtype=torch.float32, device="cuda")
+    grow = torch.full((max(gcap, 1),), -777, dtype=torch.int32, device="cuda")
+    gw = torch.full((max(gcap, 1),), -9.0, dtype=torch.float32, device="cuda")
+    pos = torch.full((max(rcap, 1), K), -777, dtype=torch.int32, device="cuda")
+    m = torch.full((1,), -777, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    dx = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16 if not fp8 else np.uint8)).cuda()
+    ep.ep_dispatch_grouped(shape, dx, elem, torch.from_numpy(sc).cuda() if NS else None, NS, didx, dw, b.recv_gbl,
+                           b.recv_per_expert, b.workspace, rcap, rw, ri, si, ss, gcap, gx, gs if NS else None, grow, gw,
+                           pos, m, st)
+    torch.cuda.synchronize()
+    rows = min(n, rcap)
+    mm = min(ref["num_grouped_rows"], gcap)
+    gpu = dict(num_grouped_rows=int(m.item()), grouped_x=gx[:mm].cpu().numpy().view(d["recv_x"].dtype),
+               grouped_row=grow[:mm].cpu().numpy(), grouped_weights=gw[:mm].cpu().numpy(),
+               slot_pos=pos[:rcap].cpu().numpy(), send_slot=ss.cpu().numpy(),
+               recv_topk_weights=rw[:rows].cpu().numpy(), recv_topk_idx=ri[:rows].cpu().numpy(),
+               recv_src_info=si[:rows].cpu().numpy(), status=int(st.item()),
+               untouched=bool((grow[mm:gcap] == -777).all().item()) and bool((gx[mm:gcap] == 0x5A).all().item()))
+    want = dict(num_grouped_rows=ref["num_grouped_rows"], grouped_x=ref["grouped_x"][:mm],
+                grouped_row=ref["grouped_row"][:mm], grouped_weights=ref["grouped_weights"][:mm],
+                slot_pos=ref["slot_pos"], send_slot=d["send_slot"], recv_topk_weights=d["recv_topk_weights"][:rows],
+                recv_topk_idx=d["recv_topk_idx"][:rows], recv_src_info=d["recv_src_info"][:rows],
+                status=d["status"] | ref["status"], untouched=True)
+    if NS:
+        gpu["grouped_x_scales"] = gs[:mm].cpu().numpy()
+        want["grouped_x_scales"] = ref["grouped_x_scales"][:mm]
+    return gpu, want
+
+
+@pytest.mark.parametrize("name,align", [("tiny", 4), ("sweep", 128), ("prefill", 1), ("skew", 4), ("large", 8)])
+def test_dispatch_grouped_parity(name, align):
+    print(f"[parity] dispatch_grouped workload={name} align={align}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    gpu, want = _dispatch_grouped_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels,
+                                       align)
+    assert _group_diff(gpu, want) == []
+    assert gpu["status"] == 0
+
+
+@pytest.mark.parametrize("name", ["prefill", "skew"])
+def test_dispatch_grouped_fp8_rows_with_scales(name):
+    print(f"[parity] dispatch_grouped fp8 workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    gpu, want = _dispatch_grouped_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels, 4,
+                                       fp8=True)
+    assert _group_diff(gpu, want) == []
+
+
+def test_dispatch_grouped_short_capacities():
+    # receive rows past a short receive capacity are dropped and not grouped; a short
+    # grouped capacity drops the entries past it (both flagged)
+    print("[parity] dispatch_grouped short capacities", flush=True)
+    x, idx, w = _random_case(3000, 16, 64, 6, 5, 1000, seed=31, mask_frac=0.1, dup=True)
+    for rd, gd in ((-700, 0), (0, -900), (-50, -50), (300, 0)):
+        gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4, recv_delta=rd, gcap_delta=gd)
+        assert _group_diff(gpu, want) == [], (rd, gd)
+        assert (gpu["status"] != 0) == (rd < 0 or gd < 0), (rd, gd, gpu["status"])
+
+
+def test_dispatch_grouped_no_tokens():
+    x, idx, w = _random_case(0, 16, 64, 4, 8, 64, seed=1)
+    gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 8, 4)
+    assert _group_diff(gpu, want) == []
+    assert gpu["num_grouped_rows"] == 0
