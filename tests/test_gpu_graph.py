@@ -3,7 +3,9 @@ stream-ordered calls) and replayed: the library allocates nothing, records no
 memset and needs no host synchronisation inside a step (notify without its
 host read-back), so every call is capturable.  Each replay runs on new input
 values written eagerly between replays, with synchronisations in between, and
-must equal an eager run of the same step on those values bit for bit."""
+must equal an eager run of the same step on those values bit for bit; the
+dispatch straight into the grouped layout, captured in the same graph, must
+give the same grouped rows as the eager dispatch and grouping."""
 import numpy as np
 import pytest
 import torch
@@ -54,6 +56,7 @@ def test_step_in_a_graph_replays_exactly(name):
     gx, gidx, gw = x.clone(), idx.clone(), w.clone()
     b = ep.allocate(shape, cap)
     gb = ep.allocate_group(b, m)
+    gf = ep.allocate_group(b, m)  # the dispatch straight into the grouped layout writes here
     # warm up on a side stream, as torch asks before capture
     s = torch.cuda.Stream()
     s.wait_stream(torch.cuda.current_stream())
@@ -63,6 +66,7 @@ def test_step_in_a_graph_replays_exactly(name):
         ep.run_dispatch(b, gx, gidx, gw)
         ep.run_combine(b)
         ep.run_group(b, gb)
+        ep.run_dispatch_grouped(b, gf, gx, gidx, gw)
     torch.cuda.current_stream().wait_stream(s)
     torch.cuda.synchronize()
 
@@ -73,6 +77,7 @@ def test_step_in_a_graph_replays_exactly(name):
         ep.run_dispatch(b, gx, gidx, gw)
         ep.run_combine(b)
         ep.run_group(b, gb)
+        ep.run_dispatch_grouped(b, gf, gx, gidx, gw)
 
     rng = np.random.default_rng(77)
     for replay in range(3):
@@ -88,6 +93,10 @@ def test_step_in_a_graph_replays_exactly(name):
         got = _outputs(b, gb)
         rb, rg = _eager_reference(shape, gx.clone(), gidx.clone(), gw.clone(), cap, m)
         want = _outputs(rb, rg)
+        mm = int(want["M"].item())
+        got["fused_grouped_x"] = gf.grouped_x[:mm].view(torch.int16).clone()
+        got["fused_grouped_row"] = gf.grouped_row[:mm].clone()
+        want["fused_grouped_x"], want["fused_grouped_row"] = want["grouped_x"], want["grouped_row"]
         bad = [k for k in want if not torch.equal(got[k], want[k])]
         assert not bad, f"replay {replay}: {bad}"
         assert int(got["status"].item()) == 0
