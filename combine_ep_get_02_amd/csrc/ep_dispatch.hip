@@ -216,7 +216,7 @@ constexpr int64_t kMaxPullRowUnits = 1 << 16;  // 1 MiB rows
 // read hit the group's x in the XCD's L2.  Before its tasks, each group's GT
 // token tasks (send_slot, metadata, scales) go to GT of the XCD's waves, a
 // different set for each group.
-template <int CPG, int U, int NT, bool EXACT, int WPB>
+template <int CPG, int U, bool EXACT, int WPB>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParams p) {
     constexpr int GT = CPG * kChunk;  // tokens per group
     const int lane = threadIdx.x & (kWave - 1);
@@ -358,43 +358,34 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
             }
             const int nb = (tasks - wx - base * W + W - 1) / W;  // tasks of this batch
             const int nbatch = nb < kWave ? nb : kWave;
-            for (int j = 0; j < nbatch; j += NT) {
-                // NT tasks per pass: all their loads are issued, then all their
-                // stores.  A task past the batch, or lanes past a ragged row end,
-                // still load (from a valid place) so that no branch sits between
-                // the loads; only their stores are skipped.  Addresses are a
-                // wave-uniform base plus the fixed per-lane offset.
-                u32x4 v[NT][U];
-                u32x4 *dst[NT];
-                int lim[NT];
-                bool ok[NT];
+            for (int j = 0; j < nbatch; ++j) {
+                // the task's U loads are issued, then its U stores; lanes past a
+                // ragged row end still load (from a valid place) so that no branch
+                // sits between the loads, and only their stores are skipped.
+                // Addresses are a wave-uniform base plus the fixed per-lane offset.
+                // (Two tasks per pass measured slower.)
+                const int pk = readlane32(rt_pack, j);
+                const int row = readlane32(rt_row, j);
+                const bool ok = (pk >> 30) != 0;
+                const int64_t t = q0 * kChunk + (pk & 0xff);
+                const int64_t first = (int64_t)((pk >> 8) & 0x3fffff) * U * kWave;
+                const int lim = (int)(p.row_units - first);
+                const u32x4 *src = p.x + t * p.row_units + first;
+                u32x4 *dst = p.recv_x + (int64_t)row * p.row_units + first;
+                u32x4 v[U];
 #pragma unroll
-                for (int q = 0; q < NT; ++q) {
-                    const int jq = j + q < nbatch ? j + q : j;
-                    const int pk = readlane32(rt_pack, jq);
-                    const int row = readlane32(rt_row, jq);
-                    ok[q] = j + q < nbatch && (pk >> 30) != 0;
-                    const int64_t t = q0 * kChunk + (pk & 0xff);
-                    const int64_t first = (int64_t)((pk >> 8) & 0x3fffff) * U * kWave;
-                    lim[q] = (int)(p.row_units - first);
-                    const u32x4 *src = p.x + t * p.row_units + first;
-                    dst[q] = p.recv_x + (int64_t)row * p.row_units + first;
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int cu = u * kWave + lane;
-                        v[q][u] = src[(EXACT || cu < lim[q]) ? cu : lim[q] - 1];
-                    }
+                for (int u = 0; u < U; ++u) {
+                    const int cu = u * kWave + lane;
+                    v[u] = src[(EXACT || cu < lim) ? cu : lim - 1];
                 }
                 // keeps the compiler from moving a load into its store's branch (a
                 // load there would be waited for before the next one is issued)
                 asm volatile("" ::: "memory");
-#pragma unroll
-                for (int q = 0; q < NT; ++q) {
-                    if (!ok[q]) continue;
+                if (ok) {
 #pragma unroll
                     for (int u = 0; u < U; ++u) {
                         const int cu = u * kWave + lane;
-                        if (EXACT || cu < lim[q]) __builtin_nontemporal_store(v[q][u], dst[q] + cu);
+                        if (EXACT || cu < lim) __builtin_nontemporal_store(v[u], dst + cu);
                     }
                 }
             }
@@ -402,9 +393,9 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
     }
 }
 
-template <int CPG, int U, int NT, bool EXACT, int WPB>
+template <int CPG, int U, bool EXACT, int WPB>
 hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
-    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, NT, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
+    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
                        dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
 }
@@ -463,18 +454,18 @@ hipError_t run_tiled(const DispatchParams &p, int vpl, int wpb, int gran, hipStr
 // Pull-form tiling: chunks per token group (cpg), pieces per task (u), waves
 // per block (wpb) and blocks per XCD (bpx); cpg == 0 selects the push form.
 struct PullTiling {
-    int cpg, u, nt, wpb, bpx;
+    int cpg, u, wpb, bpx;
 };
 
 hipError_t run_pull_tiled(const DispatchParams &p, const PullTiling &t, hipStream_t stream) {
     const bool exact = p.row_units % ((int64_t)t.u * kWave) == 0;
-#define EP_PULL_CASE(C, U, N, W) \
-    if (t.cpg == C && t.u == U && t.nt == N && t.wpb == W) \
-        return exact ? run_pull<C, U, N, true, W>(p, t.bpx, stream) : run_pull<C, U, N, false, W>(p, t.bpx, stream);
-    EP_PULL_CASE(2, 1, 1, 8)
-    EP_PULL_CASE(2, 2, 1, 8)
-    EP_PULL_CASE(2, 4, 1, 8)
-    EP_PULL_CASE(2, 8, 1, 8)
+#define EP_PULL_CASE(C, U, W) \
+    if (t.cpg == C && t.u == U && t.wpb == W) \
+        return exact ? run_pull<C, U, true, W>(p, t.bpx, stream) : run_pull<C, U, false, W>(p, t.bpx, stream);
+    EP_PULL_CASE(2, 1, 8)
+    EP_PULL_CASE(2, 2, 8)
+    EP_PULL_CASE(2, 4, 8)
+    EP_PULL_CASE(2, 8, 8)
 #undef EP_PULL_CASE
     return hipErrorInvalidValue;
 }
@@ -490,9 +481,9 @@ hipError_t run_pull_tiled(const DispatchParams &p, const PullTiling &t, hipStrea
 // memory); the whole row (4 or 8 pieces) for shorter rows.  64 blocks of 8
 // waves per XCD: 16 waves per CU.
 PullTiling pull_tiling(int64_t row_units, int64_t num_tokens) {
-    if (row_units < kWave || row_units > kMaxPullRowUnits || num_tokens < 2048) return PullTiling{0, 0, 0, 0, 0};
+    if (row_units < kWave || row_units > kMaxPullRowUnits || num_tokens < 2048) return PullTiling{0, 0, 0, 0};
     const int u = row_units >= 14 * kWave ? 1 : row_units >= 7 * kWave ? 2 : row_units > 4 * kWave ? 8 : 4;
-    return PullTiling{2, u, 1, 8, 64};
+    return PullTiling{2, u, 8, 64};
 }
 
 void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, int *gran) {
