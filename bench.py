@@ -123,12 +123,16 @@ def cpu_baseline(d, wl, n_recv, budget_s: float = 12.0) -> dict:
     o = oracle.Oracle()
     x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
     reps, t0 = 0, time.perf_counter()
-    t_disp = t_comb = 0.0
+    t_lay = t_note = t_disp = t_comb = 0.0
     while True:
+        z = time.perf_counter()
         lay = o.layout(idx, wl.experts, wl.ranks)
+        y = time.perf_counter()
         note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
                         lay["num_tokens_per_expert"], wl.channels, wl.expert_alignment)
         a = time.perf_counter()
+        t_lay += y - z
+        t_note += a - y
         dis = o.dispatch(x, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
                          note["recv_gbl_rank_prefix_sum"], wl.experts)
         b = time.perf_counter()
@@ -145,7 +149,21 @@ def cpu_baseline(d, wl, n_recv, budget_s: float = 12.0) -> dict:
     return {"value": round(alg / dc / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": f"{reps} full {wl.name} steps (layout+notify+dispatch+combine, t={T}, h={H}, k={K}, "
                       f"R={R}); value = dispatch+combine algorithmic bytes / oracle dispatch+combine time",
-            "us_dispatch_plus_combine": round(dc * 1e6, 1), "host_cores": os.cpu_count()}
+            "us_dispatch_plus_combine": round(dc * 1e6, 1),
+            "us_per_stage": {"layout": round(t_lay / reps * 1e6, 1), "notify": round(t_note / reps * 1e6, 1),
+                             "dispatch": round(t_disp / reps * 1e6, 1), "combine": round(t_comb / reps * 1e6, 1)},
+            "host_cores": os.cpu_count(), "host_cpu": host_cpu_model()}
+
+
+def host_cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 class HipEvents:
