@@ -401,7 +401,7 @@ def main() -> int:
         return 0
     if args.gpus != 1:
         print(f"bench.py measures one GPU's share of the path; --gpus {args.gpus} is not supported "
-              f"(this build has no multi-GPU path)", file=sys.stderr)
+              f"(the library has no multi-GPU path)", file=sys.stderr)
         return 2
 
     import torch
