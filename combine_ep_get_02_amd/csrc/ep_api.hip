@@ -35,7 +35,7 @@ ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP
 
 bool workspace_ok(const ep_shape_t *s, const void *ws, size_t bytes) {
     return ws != nullptr && (reinterpret_cast<uintptr_t>(ws) & 255u) == 0 &&
-           bytes >= workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels).total;
+           bytes >= workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels, s->num_topk).total;
 }
 
 // Shared checks and launch of the bf16 and fp8 dispatch entry points.
@@ -97,7 +97,7 @@ const char *ep_status_string(ep_status_t status) {
 
 size_t ep_workspace_bytes(const ep_shape_t *s) {
     if (check_shape(s) != EP_OK) return 0;
-    return workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels).total;
+    return workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels, s->num_topk).total;
 }
 
 ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
@@ -240,7 +240,7 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
 ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
                                 const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
-                                const void *workspace, size_t workspace_bytes, int32_t recv_capacity,
+                                void *workspace, size_t workspace_bytes, int32_t recv_capacity,
                                 float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
                                 int32_t *send_slot, int32_t grouped_capacity, void *grouped_x,
                                 float *grouped_x_scales, int32_t *grouped_row, float *grouped_weights,
@@ -269,6 +269,16 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
         if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr)
             return EP_ERR_INVALID_ARG;
         if (!aligned16(x) || !workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
+    }
+    // the pull form of the row copy reads each (token, slot)'s grouped position from the
+    // workspace: the metadata launch clears it, the positions launch fills it in
+    int32_t *tok_pos = nullptr;
+    if (group_pull_applies(*s, row_bytes / 16)) {
+        const Workspace w = workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels,
+                                             s->num_topk);
+        tok_pos = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + w.tok_pos);
+    }
+    if (s->num_tokens > 0) {
         // 1. the receive metadata, with no receive rows
         DispatchArgs d = {};
         d.x = x;
@@ -282,18 +292,21 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
         d.recv_idx = recv_topk_idx;
         d.src_info = recv_src_info;
         d.send_slot = send_slot;
+        d.tok_pos = tok_pos;
         d.dev_status = dev_status;
         hipError_t e = launch_dispatch(*s, d, stream);
         if (e != hipSuccess) return EP_ERR_HIP;
     }
     // 2. positions over the capacity's rows (rows past the last slab are not read),
     // 3. each token's row read once from x and stored at its slots' grouped positions,
-    //    then the padding rows zeroed
+    //    and the padding rows zeroed
     GroupArgs a = {};
     a.recv_x = x;
     a.from_x = true;
     a.topk_idx = topk_idx;
     a.send_slot = send_slot;
+    a.src_info = recv_src_info;
+    a.tok_pos = tok_pos;
     a.num_tokens = s->num_tokens;
     a.row_units = row_bytes / 16;
     a.recv_scales = x_scales;

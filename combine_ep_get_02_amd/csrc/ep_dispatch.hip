@@ -49,6 +49,7 @@ struct DispatchParams {
     int64_t *recv_idx;
     int32_t *src_info;
     int32_t *send_slot;
+    int32_t *tok_pos;
     int32_t *dev_status;
     int64_t T;
     int64_t row_units;  // 16-byte units per row
@@ -71,10 +72,12 @@ __device__ __forceinline__ void copy_scales(const DispatchParams &p, int64_t t, 
 
 // send_slot of token t and the metadata (a4) of its rows: weights / local ids
 // of the topk slots living on each destination (lane j < k holds slot j's
-// expert id e and weight wt) and {my_rank, t} as the row's source.
+// expert id e and weight wt) and {my_rank, t} as the row's source.  tok_pos
+// (the grouped dispatch only) is cleared to -1 for the grouping to fill in.
 __device__ __forceinline__ void token_metadata(const DispatchParams &p, int64_t t, int slot, uint64_t dests,
                                                int64_t e, float wt, int lane) {
     if (lane < p.R) p.send_slot[t * p.R + lane] = slot;
+    if (p.tok_pos != nullptr && lane < p.K) p.tok_pos[t * p.K + lane] = -1;
     const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
     for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
         const int r = __builtin_ctzll(dd);
@@ -533,7 +536,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.mask = nullptr;
     p.rank_off = nullptr;
     if (a.ws != nullptr) {
-        const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
+        const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
         p.mask = reinterpret_cast<const uint64_t *>(a.ws + w.mask);
         p.rank_off = reinterpret_cast<const int32_t *>(a.ws + w.rank_off);
     }
@@ -544,6 +547,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.recv_idx = a.recv_idx;
     p.src_info = a.src_info;
     p.send_slot = a.send_slot;
+    p.tok_pos = a.tok_pos;
     p.dev_status = a.dev_status;
     p.T = s.num_tokens;
     p.row_units = a.row_units;

@@ -32,17 +32,19 @@ __host__ __device__ inline int64_t num_chunks(int64_t T) { return (T + kChunk - 
 //   node_off  int32  [Q+1][nodes]   the same per node
 //   rank_part int32  [C][R]         tokens of rank r in [64*floor(end_c/64), end_c)
 //   node_part int32  [C][nodes]     the same per node
+//   tok_pos   int32  [t][k]         grouped position of every (token, slot), or -1
+//                                   (dispatch straight into the grouped layout only)
 // The tickets and acc must be zero before the first call; every layout/notify call
 // leaves them zero again.
 struct Workspace {
-    size_t tickets, acc, mask, rank_off, node_off, rank_part, node_part, total;
+    size_t tickets, acc, mask, rank_off, node_off, rank_part, node_part, tok_pos, total;
 };
 constexpr int kTicketLayout = 0;
 constexpr int kTicketNotify = 16;  // separate 64-byte lines
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
-inline Workspace workspace_layout(int64_t T, int R, int E, int C) {
+inline Workspace workspace_layout(int64_t T, int R, int E, int C, int K) {
     Workspace w;
     const int64_t Q = num_chunks(T);
     const int nodes = num_nodes(R);
@@ -54,6 +56,7 @@ inline Workspace workspace_layout(int64_t T, int R, int E, int C) {
     w.node_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(Q + 1) * nodes);
     w.rank_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * R);
     w.node_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * nodes);
+    w.tok_pos = off;   off = align256(off + sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * (size_t)K);
     w.total = off;
     return w;
 }
@@ -86,6 +89,7 @@ struct DispatchArgs {
     int64_t *recv_idx;
     int32_t *src_info;
     int32_t *send_slot;
+    int32_t *tok_pos;  // [t][k] set to -1 (metadata-only launch of the grouped dispatch), or null
     int32_t *dev_status;
 };
 
@@ -98,6 +102,8 @@ struct GroupArgs {
     bool from_x;               // rows straight from x (through topk_idx, send_slot, slot_pos), not recv_x
     const int64_t *topk_idx;   // [t][k] (from_x)
     const int32_t *send_slot;  // [t][R] (from_x)
+    const int32_t *src_info;   // [N][2] {src_rank, token} (from_x)
+    int32_t *tok_pos;          // [t][k] workspace: grouped position of each (token, slot) (from_x)
     int64_t num_tokens;        // t (from_x)
     int64_t row_units;
     const float *recv_scales;  // [N][num_scales] (or x's [t][num_scales]), null when num_scales == 0
@@ -119,6 +125,8 @@ struct GroupArgs {
 constexpr int kMaxGroupExperts = 512;  // local experts per rank the grouping supports
 
 hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t stream);
+// Whether the grouping straight from x takes the pull form (which needs tok_pos).
+bool group_pull_applies(const ep_shape_t &s, int64_t row_units);
 
 hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv_w, const int32_t *send_slot,
                           int32_t num_recv_rows, uint4 *combined_x, float *combined_w, int32_t *dev_status,

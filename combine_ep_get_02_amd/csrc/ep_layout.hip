@@ -172,7 +172,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
 
 hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
                          int32_t *per_expert, uint8_t *in_rank, char *ws, int32_t *dev_status, hipStream_t stream) {
-    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
     LayoutParams p;
     p.topk_idx = topk_idx;
     p.per_rank = per_rank;

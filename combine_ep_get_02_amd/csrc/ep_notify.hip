@@ -341,7 +341,7 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
                          const int32_t *per_node, const int32_t *per_expert, int32_t *gbl, int32_t *rdma,
                          int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,
                          char *ws, int32_t *dev_status, hipStream_t stream) {
-    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels);
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
     NotifyParams p;
     p.in_rank = in_rank;
     p.per_rank = per_rank;

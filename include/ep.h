@@ -71,7 +71,8 @@ enum {
     EP_DEV_BAD_TOPK_IDX = 1,   /* a topk id outside [-1, num_experts): that slot is treated as masked */
     EP_DEV_RECV_OVERFLOW = 2,  /* a receive row >= recv_capacity: the row is not written, send_slot = -1 */
     EP_DEV_COUNT_MISMATCH = 4, /* num_tokens_per_rank / _per_rdma_rank disagree with is_token_in_rank */
-    EP_DEV_BAD_SEND_SLOT = 8   /* a send_slot entry outside its valid range (combine, cached dispatch): skipped */
+    EP_DEV_BAD_SEND_SLOT = 8   /* a send_slot entry outside its valid range (combine, cached dispatch), or an
+                                  inconsistent grouped position (grouped dispatch): skipped */
 };
 
 /* Problem shape (host struct, read during the call only). */
@@ -239,13 +240,19 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
  * ep_dispatch / ep_dispatch_fp8; recv_gbl_rank_prefix_sum and num_recv_tokens_per_expert as
  * ep_notify wrote them; the workspace as ep_notify left it.  Receive rows at or past
  * recv_capacity are dropped as in ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.
- * dev_status (nullable): the flags of both calls.  Limits as for both calls.
- * Four launches (receive metadata, positions, rows, padding).
+ * The call also writes the workspace: from 2048 tokens (rows of 1 KiB to 1 MiB, E <= 2048)
+ * it keeps each (token, slot)'s grouped position there; what ep_dispatch and ep_combine
+ * read from it is not touched.
+ * dev_status (nullable): the flags of both calls, and EP_DEV_BAD_SEND_SLOT if the grouped
+ * positions of one expert's entries of a token group are not consecutive (only with
+ * inconsistent inputs; those rows are skipped).  Limits as for both calls.
+ * Three launches (receive metadata, positions, rows with padding) from 2048 tokens as
+ * above, else four (receive metadata, positions, rows, padding).
  */
 ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
                                 const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
-                                const void *workspace, size_t workspace_bytes, int32_t recv_capacity,
+                                void *workspace, size_t workspace_bytes, int32_t recv_capacity,
                                 float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
                                 int32_t *send_slot, int32_t grouped_capacity, void *grouped_x,
                                 float *grouped_x_scales, int32_t *grouped_row, float *grouped_weights,

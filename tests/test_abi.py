@@ -53,8 +53,8 @@ def test_workspace_bytes(ep):
     s = ep.make_shape(4096, 7168, 8, 256, 64, 24)
     n = ep.ep_workspace_bytes(s)
     # tickets 256 + running counts (64+8+256) + masks (8 B/token) + 65 x 64 chunk offsets
-    # + 65 x 8 + 24 x 64 + 24 x 8, each 256-aligned
-    assert n == 256 + 1536 + 32768 + 16640 + 2304 + 6144 + 768
+    # + 65 x 8 + 24 x 64 + 24 x 8 + grouped positions (4 B per token and slot), each 256-aligned
+    assert n == 256 + 1536 + 32768 + 16640 + 2304 + 6144 + 768 + 131072
     assert ep.ep_workspace_bytes(ep.make_shape(4096, 7168, 8, 255, 64, 24)) == 0  # E % R != 0
 
 

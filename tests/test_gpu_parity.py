@@ -684,6 +684,39 @@ def test_dispatch_grouped_short_capacities():
         assert (gpu["status"] != 0) == (rd < 0 or gd < 0), (rd, gd, gpu["status"])
 
 
+# the pull form of the rows straight from x (from 2048 tokens, rows of 1 KiB to 1 MiB,
+# E <= 2048): ragged token groups and ragged row pieces, k = 32 with duplicates and
+# masked slots, padding from expert_alignment, E at the limit and past it (push form)
+GROUPED_PULL = {
+    # name: (T, R, E, K, C, H, align, extra)
+    "ragged_groups_rows_513_units": (2100, 8, 64, 8, 6, 4104, 4, {}),
+    "k32_r64_duplicates_masked": (2200, 64, 128, 32, 9, 2048, 8, dict(dup=True, mask_frac=0.2)),
+    "rows_1kib_r24_masked": (2049, 24, 48, 4, 7, 512, 1, dict(mask_frac=0.2)),
+    "rows_16kib_k6": (2048, 16, 64, 6, 5, 8192, 3, {}),
+    "e2048": (2048, 64, 2048, 8, 24, 1024, 2, {}),
+    "e4096_push_form": (2048, 64, 4096, 8, 24, 512, 2, {}),
+}
+
+
+@pytest.mark.parametrize("name", sorted(GROUPED_PULL))
+def test_dispatch_grouped_pull_parity(name):
+    T, R, E, K, C, H_, align, extra = GROUPED_PULL[name]
+    print(f"[parity] dispatch_grouped pull={name}", flush=True)
+    x, idx, w = _random_case(T, R, E, K, C, H_, seed=len(name) + 300, **extra)
+    gpu, want = _dispatch_grouped_case(x, idx, w, E, R, C, align)
+    assert _group_diff(gpu, want) == []
+    assert gpu["status"] == 0
+
+
+def test_dispatch_grouped_pull_short_capacities():
+    print("[parity] dispatch_grouped pull short capacities", flush=True)
+    x, idx, w = _random_case(3000, 16, 64, 6, 5, 1024, seed=32, mask_frac=0.1, dup=True)
+    for rd, gd in ((-700, 0), (0, -900), (-50, -50), (300, 0)):
+        gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4, recv_delta=rd, gcap_delta=gd)
+        assert _group_diff(gpu, want) == [], (rd, gd)
+        assert (gpu["status"] != 0) == (rd < 0 or gd < 0), (rd, gd, gpu["status"])
+
+
 def test_dispatch_grouped_no_tokens():
     x, idx, w = _random_case(0, 16, 64, 4, 8, 64, seed=1)
     gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 8, 4)
