@@ -17,7 +17,8 @@
 // masks in LDS and written out as one contiguous byte range with 16/4/1-byte
 // stores.  The last block to finish moves the running counters into the
 // outputs and zeroes them for the next call, so no separate zero-fill launch
-// is needed.  Integer atomics commute: the result is deterministic.
+// is needed; a single block (up to 256 tokens) writes its LDS counts out
+// directly.  Integer atomics commute: the result is deterministic.
 #include "ep_internal.h"
 
 namespace ep {
@@ -132,6 +133,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
             const int row = b / R, r = b - row * R;
             dst[b] = (uint8_t)((s_mask[row] >> r) & 1ull);
         }
+    }
+
+    if (gridDim.x == 1 && lds_experts) {
+        // a single block (t <= 256): its counts are the totals, and the running
+        // counters are not touched
+        for (int i = tid; i < R; i += kLayoutThreads) p.per_rank[i] = s_rank[i];
+        for (int i = tid; i < nodes; i += kLayoutThreads) p.per_node[i] = s_node[i];
+        for (int i = tid; i < E; i += kLayoutThreads) p.per_expert[i] = s_expert[i];
+        return;
     }
 
     // this block's partial counts into the running counters

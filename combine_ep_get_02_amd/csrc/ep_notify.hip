@@ -16,11 +16,13 @@
 // is cut into 64-token chunks, one chunk per wave and one token per lane.
 //   Every wave turns its lanes' is_token_in_rank rows into 64-bit rank masks
 //   (stored for dispatch); a 64x64 bit transpose across the wave hands lane r
-//   the chunk's column for rank r, whose popcount is the (chunk, rank) count.  For each channel whose end falls inside the chunk
-//   it also stores the count of the chunk's tokens before that end.  Every
-//   value has one writer: no atomics.
-//   The last block to finish then scans: it brings the counts, the partials
-//   and the per-rank totals into LDS in one round trip (or works in the
+//   the chunk's column for rank r, whose popcount is the (chunk, rank) count.
+//   For each channel whose end falls inside the chunk it also stores the count
+//   of the chunk's tokens before that end.  Every value has one writer: no
+//   atomics.
+//   The last block to finish (the only one, without an election, up to 1024
+//   tokens) then scans: it brings the counts, the partials and the per-rank
+//   totals into LDS in one round trip (or works in the
 //   workspace when they do not fit), one wave per column (rank or node), each
 //   lane summing a run of chunks and a wave-wide shuffle scan combining the
 //   runs, which turns the counts into exclusive row offsets inside each rank's
@@ -327,7 +329,13 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
     const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
     if (q < Q) count_chunk(p, q, lane);
 
-    if (!elect_last_block(p.ticket)) return;
+    // a single block (up to 1024 tokens) finishes once its own waves are done:
+    // a workgroup barrier (with its workgroup-scope fences) makes their stores
+    // visible, and no ticket is taken
+    if (gridDim.x == 1)
+        __syncthreads();
+    else if (!elect_last_block(p.ticket))
+        return;
     const int64_t NC = p.R + p.nodes;
     if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
         finish_in_lds(p, tid, lane, wave);
