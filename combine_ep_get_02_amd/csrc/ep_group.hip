@@ -445,8 +445,8 @@ __global__ __launch_bounds__(256) void group_pad_kernel(const int32_t *grouped_r
 constexpr int kPullTokens = 128;         // tokens per group
 constexpr int kPullMaxExperts = 2048;
 constexpr int kPullXcds = 8;             // XCDs; consecutive workgroup ids go round-robin over them
-constexpr int kPullWaves = 8;            // waves per block
-constexpr int kPullBlocksPerXcd = 64;    // 2 blocks per CU
+constexpr int kPullWaves = 16;           // waves per block
+constexpr int kPullBlocksPerXcd = 32;    // one block per CU
 constexpr int64_t kPullMinTokens = 2048;
 constexpr int64_t kPullMaxRowUnits = 1 << 16;
 
@@ -645,6 +645,7 @@ hipError_t run_pull(const PullParams &p, hipStream_t stream) {
 // and more, 2 from 7 KiB, 8 above 4 KiB, else 4.
 template <int NE>
 hipError_t run_pull_tiled(const PullParams &p, hipStream_t stream) {
+    if (kPullTokens * p.K > NE * kPullWaves * kWave) return hipErrorInvalidValue;  // every entry has a thread
     const int64_t ru = p.row_units;
     const int u = ru >= 14 * kWave ? 1 : ru >= 7 * kWave ? 2 : ru > 4 * kWave ? 8 : 4;
     const bool exact = ru % (u * kWave) == 0;
@@ -758,7 +759,8 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
         u.K = s.num_topk;
         u.E = s.num_experts;
         u.num_scales = a.num_scales;
-        return s.num_topk <= 8 ? run_pull_tiled<2>(u, stream) : run_pull_tiled<8>(u, stream);
+        // entries per thread: 128 tokens x k slots over 1024 threads
+        return s.num_topk <= 8 ? run_pull_tiled<1>(u, stream) : run_pull_tiled<4>(u, stream);
     }
     if (a.from_x) {  // rows straight from x
         if (a.num_tokens > 0) {
