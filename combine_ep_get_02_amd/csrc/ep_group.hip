@@ -437,7 +437,8 @@ __global__ __launch_bounds__(256) void group_pad_kernel(const int32_t *grouped_r
 // position, with LDS atomics; an exclusive scan of the counts; then each entry
 // at its run's offset plus its distance from the run's first position), and
 // the XCD's waves cut the output into tasks of U 1 KiB pieces, taking tasks
-// k, k+W, k+2W, ... (W = the XCD's wave count).  So the XCD writes one
+// k, k+W, k+2W, ... (W = the XCD's wave count; the scales follow in a pass of
+// their own over the group's entries).  So the XCD writes one
 // advancing window, and every row of x it reads again after the first time
 // is in its L2.  The entries (each slot's position, written by the positions
 // pass, and its expert id) of the block's next group are loaded before the
@@ -623,9 +624,22 @@ __global__ __launch_bounds__(kPullWaves *kWave) void group_pull_kernel(PullParam
                         const int cu = u * kWave + lane;
                         if (EXACT || cu < lim) __builtin_nontemporal_store(v[u], dst + cu);
                     }
-                    if (part == 0)
-                        for (int i = lane; i < p.num_scales; i += kWave)
-                            p.dst_scales[at * p.num_scales + i] = p.x_scales[t * p.num_scales + i];
+                }
+            }
+        }
+        // ---- the scales: entry e = wx, wx + W, ... of the group's output, lanes over
+        // the token's scales (a wave-uniform loop with a per-lane predicate)
+        if (p.num_scales > 0) {
+            for (int e = wx; e < total; e += W) {
+                const int2 le = s_list[e];
+                const int tl = __builtin_amdgcn_readfirstlane(le.x);
+                const int64_t at = __builtin_amdgcn_readfirstlane(le.y);
+                if (tl < 0) continue;  // wave-uniform
+                const int64_t t = g * kPullTokens + tl;
+                for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
+                    const int i = i0 + lane;
+                    const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
+                    if (i < p.num_scales) p.dst_scales[at * p.num_scales + i] = sc;
                 }
             }
         }

@@ -295,6 +295,59 @@ def test_cached_dispatch_bad_slots_bf16():
     assert int(st.item()) == 8 and ref["status"] == 8
 
 
+# cached mode at 2048 tokens and more: any slot map is copied exactly, out-of-range
+# entries are flagged and skipped.  Maps: a random permutation of part of the capacity
+# (no receive order at all), with bad entries; 16, 24 and 64 ranks, rows of 1 KiB to
+# 16 KiB (some ragged), fp8 rows with 56 and 112 scales per token.
+CACHED_LARGE = {
+    # name: (T, R, row elements, element bytes, scales per token, capacity)
+    "bf16_rows_897_units_r16": (2100, 16, 7176, 2, 0, 9000),
+    "bf16_rows_16kib_r24": (2049, 24, 8192, 2, 0, 20000),
+    "fp8_rows_14kib_r64_scales": (2304, 64, 14336, 1, 112, 12000),
+    "bf16_rows_14kib_r64": (2048, 64, 7168, 2, 0, 15000),
+    "bf16_rows_1kib_r24": (2049, 24, 512, 2, 0, 20000),
+    "fp8_rows_7kib_scales": (2304, 64, 7168, 1, 56, 12000),
+}
+
+
+@pytest.mark.parametrize("name", sorted(CACHED_LARGE))
+def test_cached_any_map_and_bad_slots(name):
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+
+    T, R, Hd, elem, NS, cap = CACHED_LARGE[name]
+    print(f"[parity] cached map={name}", flush=True)
+    rng = np.random.default_rng(len(name) + 500)
+    xr = rng.integers(0, 256, size=(T, Hd * elem), dtype=np.uint8)
+    slot = np.full((T, R), -1, np.int32)
+    picks = rng.choice(T * R, cap - 37, replace=False)
+    slot.reshape(-1)[picks] = rng.permutation(cap)[: cap - 37]
+    slot[5, R - 1] = cap + 9
+    slot[T - 1, 0] = -3
+    slot[1000, 2] = cap
+    sc = rng.standard_normal((T, NS)).astype(np.float32) if NS else None
+    shape = ep.make_shape(T, Hd, 2, 2 * R, R, 4)
+    out = torch.full((cap, Hd * elem), 0x77, dtype=torch.uint8, device="cuda")
+    outs = torch.full((cap, max(NS, 1)), -5.0, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_cached(shape, torch.from_numpy(xr).cuda(), elem, torch.from_numpy(sc).cuda() if NS else None, NS,
+                          torch.from_numpy(slot).cuda(), cap, out, outs if NS else None, st)
+    torch.cuda.synchronize()
+    # rows no entry names keep the fill, as in the oracle's output buffer below
+    ref = oracle.Oracle().dispatch_cached(xr, slot, cap, sc)
+    named = np.zeros(cap, bool)
+    ok = (slot >= 0) & (slot < cap)
+    named[slot[ok]] = True
+    got = out.cpu().numpy()
+    assert np.array_equal(got[named], ref["recv_x"][named])
+    assert (got[~named] == 0x77).all()
+    if NS:
+        assert np.array_equal(outs.cpu().numpy()[named], ref["recv_x_scales"][named])
+    assert int(st.item()) == 8 and ref["status"] == 8
+
+
 def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0, bad_ids=False, extra_rows=0,
                 optional=True, extra_id=None):
     """Both sides run layout, notify, dispatch (bf16 or fp8 rows) and then the
@@ -585,7 +638,7 @@ def test_pull_fp8_ragged_groups_and_overflow():
 # ---- dispatch straight into the grouped layout (ep_dispatch_grouped): every output
 # equals the oracle's dispatch followed by its grouping with num_recv_rows = the
 # receive capacity; no receive rows are written.
-def _dispatch_grouped_case(x, idx, w, E, R, C, align, fp8=False, recv_delta=0, gcap_delta=0):
+def _dispatch_grouped_case(x, idx, w, E, R, C, align, fp8=False, recv_delta=0, gcap_delta=0, scale_block=128):
     import torch
 
     import oracle
@@ -593,7 +646,7 @@ def _dispatch_grouped_case(x, idx, w, E, R, C, align, fp8=False, recv_delta=0, g
     from combine_ep_get_02_amd.inputs import fp8_rows
 
     T, K = idx.shape
-    xs, sc = (fp8_rows(x) if fp8 else (x, None))
+    xs, sc = (fp8_rows(x, scale_block) if fp8 else (x, None))
     NS = 0 if sc is None else sc.shape[1]
     Hd = xs.shape[1]
     o = oracle.Oracle()
@@ -704,6 +757,15 @@ def test_dispatch_grouped_pull_parity(name):
     print(f"[parity] dispatch_grouped pull={name}", flush=True)
     x, idx, w = _random_case(T, R, E, K, C, H_, seed=len(name) + 300, **extra)
     gpu, want = _dispatch_grouped_case(x, idx, w, E, R, C, align)
+    assert _group_diff(gpu, want) == []
+    assert gpu["status"] == 0
+
+
+def test_dispatch_grouped_pull_fp8_112_scales():
+    # more scales per token than lanes in a wave, ragged groups, alignment padding
+    print("[parity] dispatch_grouped pull fp8 112 scales", flush=True)
+    x, idx, w = _random_case(2100, 16, 64, 6, 5, 7168, seed=41, mask_frac=0.1)
+    gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4, fp8=True, scale_block=64)
     assert _group_diff(gpu, want) == []
     assert gpu["status"] == 0
 
