@@ -26,6 +26,12 @@
 //  copy: one wave per grouped row copies the receive row it names (zeros for
 //   padding) with 16-byte non-temporal loads and stores; the grouped rows are
 //   written in order, as one contiguous stream.
+// Straight from x (ep_dispatch_grouped, after its metadata launch): the same
+// positions launch, which also records each (token, slot)'s position by token,
+// then the rows: from 2048 tokens in position order, one token group per XCD at
+// a time, padding included (group_pull_kernel); otherwise each token's row
+// pushed to its positions (group_push_kernel) and the padding zeroed after it
+// (group_pad_kernel).
 #include "ep_internal.h"
 
 namespace ep {
@@ -408,9 +414,13 @@ __global__ __launch_bounds__(WPB *kWave) void group_push_kernel(PushParams p) {
 #pragma unroll
         for (int i = 0; i < VPL; ++i)
             if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
-        if (seg == 0)
-            for (int i = lane; i < p.num_scales; i += kWave)
-                p.dst_scales[g * p.num_scales + i] = p.x_scales[t * p.num_scales + i];
+        if (seg == 0) {  // a wave-uniform loop with a per-lane predicate
+            for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
+                const int i = i0 + lane;
+                const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
+                if (i < p.num_scales) p.dst_scales[g * p.num_scales + i] = sc;
+            }
+        }
     }
 }
 

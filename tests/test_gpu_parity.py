@@ -716,7 +716,7 @@ def test_dispatch_grouped_parity(name, align):
     assert gpu["status"] == 0
 
 
-@pytest.mark.parametrize("name", ["prefill", "skew"])
+@pytest.mark.parametrize("name", ["sweep", "prefill", "skew"])
 def test_dispatch_grouped_fp8_rows_with_scales(name):
     print(f"[parity] dispatch_grouped fp8 workload={name}", flush=True)
     d = generate(name)
