@@ -779,6 +779,20 @@ def test_dispatch_grouped_pull_short_capacities():
         assert (gpu["status"] != 0) == (rd < 0 or gd < 0), (rd, gd, gpu["status"])
 
 
+def test_dispatch_grouped_pull_edges():
+    # the pull form with nothing to copy: every slot masked; no receive rows (every
+    # grouped row is padding); no grouped rows (nothing written, overflow flagged)
+    print("[parity] dispatch_grouped pull edges", flush=True)
+    x, idx, w = _random_case(2048, 16, 64, 4, 5, 1024, seed=51, mask_frac=1.0)
+    gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4)
+    assert _group_diff(gpu, want) == [] and gpu["num_grouped_rows"] == 0 and gpu["status"] == 0
+    x, idx, w = _random_case(2048, 16, 64, 4, 5, 1024, seed=52)
+    gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4, recv_delta=-10 ** 6)
+    assert _group_diff(gpu, want) == [] and gpu["num_grouped_rows"] > 0 and gpu["status"] == 2
+    gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 5, 4, gcap_delta=-10 ** 6)
+    assert _group_diff(gpu, want) == [] and gpu["status"] == 2
+
+
 def test_dispatch_grouped_no_tokens():
     x, idx, w = _random_case(0, 16, 64, 4, 8, 64, seed=1)
     gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 8, 4)
