@@ -11,14 +11,14 @@
 // -1, weight 0).
 //
 // Design: two launches.
-//  positions: one 1024-thread block per group of 1024 rows of a slab (one
+//  positions: one 512-thread block per group of 512 rows of a slab (one
 //   tile of 64 rows per wave, one row per lane); a block first counts, per
 //   local id, the entries in the slab's rows before its group.  A wave enumerates the
 //   distinct local ids present in its tile (the lowest lane still holding an
 //   unranked slot names the next id); for each id a DPP wave scan of the
 //   lanes' slot counts gives every slot of that id its rank inside the tile,
 //   stably in (row, slot) order, kept in a register per slot.  The tiles'
-//   totals are scanned across the 16 waves in LDS and added to running per-id
+//   totals are scanned across the block's waves in LDS and added to running per-id
 //   counts; then each slot's position is its segment start + its wave's start
 //   + its rank, and the grouped row index and weight are written there.
 //   Padding positions are marked last.  The kernel is instantiated for up to
@@ -39,8 +39,9 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kGroupWaves = 16;
+constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * kWave;
+static_assert(kMaxGroupExperts <= kGroupThreads, "one thread per local expert of a slab");
 
 struct PositionParams {
     const int64_t *recv_idx;
@@ -97,11 +98,11 @@ __device__ __forceinline__ void slab_bounds(const int32_t *recv_gbl, int r, int6
 }
 
 // KB: slots per row the kernel is built for (k <= KB).  One block per group of
-// up to 1024 rows of one slab (at least one block per slab, so that empty
+// up to 512 rows of one slab (at least one block per slab, so that empty
 // slabs still get their padding).
 template <int KB>
 __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(PositionParams p) {
-    // dynamic LDS: int64 s_off[er] | int32 s_size[er] | int32 s_run[er] | int32 s_tile[16][er]
+    // dynamic LDS: int64 s_off[er] | int32 s_size[er] | int32 s_run[er] | int32 s_tile[waves][er]
     extern __shared__ int64_t s_dyn[];
     __shared__ int64_t s_wsum[kGroupWaves], s_wbase[kGroupWaves], s_wall[kGroupWaves];
     const int er = p.er, K = p.K, R = p.R;
@@ -131,9 +132,9 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     const bool last_group = group == readlane32(groups, r) - 1;
     int64_t lo, hi;
     slab_bounds(p.recv_gbl, r, p.num_rows, &lo, &hi);
-    const int64_t g0 = lo + (int64_t)group * kGroupThreads;  // this block's rows: [g0, min(g0 + 1024, hi))
+    const int64_t g0 = lo + (int64_t)group * kGroupThreads;  // this block's rows: [g0, min(g0 + 512, hi))
 
-    // this slab's segment sizes (er <= 512 < 1024 threads: one each)
+    // this slab's segment sizes (er <= kMaxGroupExperts <= threads: one each)
     const int32_t size_raw = tid < er ? p.aligned[(int64_t)r * er + tid] : 0;
 
     // ---- segment starts: the sizes of all segments of earlier slabs (a block sum),
@@ -755,7 +756,7 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
     q.K = s.num_topk;
     q.er = s.num_experts / s.num_ranks;
     const size_t lds = group_lds_bytes(q.er);
-    // enough blocks for every slab's groups of 1024 rows, at least one per slab
+    // enough blocks for every slab's groups of 512 rows, at least one per slab
     const dim3 grid((unsigned)((q.num_rows + kGroupThreads - 1) / kGroupThreads + q.R));
     if (q.K <= 8)
         hipLaunchKernelGGL(group_positions_kernel<8>, grid, dim3(kGroupThreads), lds, stream, q);
