@@ -2,10 +2,11 @@
 
 They follow the definition of what each stage must move: x read once per token,
 the ids and weights read, every receive row written with its metadata, the
-send_slot map; combine the reverse.  Pinned to the figures the hot-path
-scope table of the survey tabulates from that definition at the expected
-receive-row counts, to a buffer-by-buffer count, and to the committed rocprofv3
-counter summary (measured HBM bytes within 2%).
+send_slot map; combine the reverse.  Pinned to reference figures worked out
+from that definition by hand at each workload's expected receive-row count
+(E[N] = R * (1 - C(E - E/R, k) / C(E, k)) per token for uniform routing, a
+seeded sample for the skewed one), to a buffer-by-buffer count, and to the
+committed rocprofv3 counter summary (measured HBM bytes within 2%).
 """
 import os
 import sys
