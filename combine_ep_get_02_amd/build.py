@@ -40,7 +40,8 @@ ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 def build_c_example(verbose: bool = False) -> str:
     """gcc (C11) build of tests/c_abi_roundtrip.c linked against libep.so and the
     HIP runtime, with run paths so it runs from the tree as it is."""
-    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-I", os.path.join(ROOT, "include"), "-I",
+    # the HIP runtime headers must be told the platform when a plain C compiler reads them
+    cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I",
            os.path.join(ROCM, "include"), C_EXAMPLE_SOURCE, "-L", PKG, "-lep", "-L", os.path.join(ROCM, "lib"),
            "-lamdhip64", "-Wl,-rpath,$ORIGIN/../combine_ep_get_02_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
            "-o", C_EXAMPLE]

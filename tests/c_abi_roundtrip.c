@@ -13,7 +13,6 @@
  * Built by the package build step (gcc, C11) and run by the GPU tests.
  * Exit status 0 and a final "c abi roundtrip ok" line on success.
  */
-#define __HIP_PLATFORM_AMD__ 1
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
