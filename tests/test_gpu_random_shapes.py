@@ -6,13 +6,17 @@
 elements, expert alignments, masked and duplicate ids, and now and then a
 receive capacity a few rows short.  Eight more configurations take dispatch's
 pull form: 2048 to 4100 tokens (ragged 128-token groups), rows of 512 to 7168
-elements (ragged last tasks), 1 to 64 ranks, a capacity 500 rows short."""
+elements (ragged last tasks), 1 to 64 ranks, a capacity 500 rows short.  Eight
+more go through the dispatch straight into the grouped layout at the same token
+counts (its pull form for rows of 1 KiB or more and up to 2048 experts), with
+topk up to 32, alignment padding, short receive and grouped capacities, and fp8
+rows with up to 896 scales per token."""
 import numpy as np
 import pytest
 
 import gpu_harness as H
 import oracle
-from test_gpu_parity import _exact, _fp8_case, _group_case, _group_diff, _random_case
+from test_gpu_parity import _dispatch_grouped_case, _exact, _fp8_case, _group_case, _group_diff, _random_case
 
 pytestmark = pytest.mark.gpu
 
@@ -89,3 +93,36 @@ def test_random_shape_pull(case):
         g8, r8 = _fp8_case(x, idx, w, s["E"], s["R"], s["C"], num_scales_block=8, capacity=cap)
         assert _exact(g8, r8) == []
         assert g8["status"] == r8["status"]
+
+
+GROUPED_CASES = 8
+
+
+def draw_grouped(case: int) -> dict:
+    """Shapes for the dispatch straight into the grouped layout at 2048 tokens or more."""
+    rng = np.random.default_rng(8000 + case)
+    R = int(rng.choice([1, 8, 16, 24, 32, 64]))
+    er = int(rng.choice([1, 2, 4, 8, 16, 32]))
+    E = R * er
+    K = int(rng.integers(1, min(8, E) + 1))
+    if case % 4 == 3:
+        K = int(min(E, rng.integers(9, 33)))
+    return dict(
+        T=int(rng.choice([2048, 2049, 2111, 2176, 3000, 4100])), R=R, E=E, K=K, C=int(rng.integers(1, 40)),
+        H=int(rng.choice([512, 520, 1000, 2056, 3592, 7168])), align=int(rng.choice([1, 2, 4, 16])),
+        mask=float(rng.choice([0.0, 0.2])), dup=bool(case % 3 == 1),
+        recv_delta=-300 if case % 4 == 2 else 0, gcap_delta=-200 if case % 4 == 1 else 0)
+
+
+@pytest.mark.parametrize("case", range(GROUPED_CASES))
+def test_random_shape_grouped_pull(case):
+    s = draw_grouped(case)
+    print(f"[parity] random grouped case {case}: {s}", flush=True)
+    x, idx, w = _random_case(s["T"], s["R"], s["E"], s["K"], s["C"], s["H"], seed=9000 + case, mask_frac=s["mask"],
+                             dup=s["dup"])
+    gpu, want = _dispatch_grouped_case(x, idx, w, s["E"], s["R"], s["C"], s["align"], recv_delta=s["recv_delta"],
+                                       gcap_delta=s["gcap_delta"])
+    assert _group_diff(gpu, want) == []
+    if case % 2 == 0 and s["H"] % 16 == 0:  # fp8 rows of whole 16-byte units, 8-element scale blocks
+        g8, w8 = _dispatch_grouped_case(x, idx, w, s["E"], s["R"], s["C"], s["align"], fp8=True, scale_block=8)
+        assert _group_diff(g8, w8) == []
