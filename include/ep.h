@@ -276,8 +276,11 @@ ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_top
                        int32_t num_recv_rows, void *combined_x, float *combined_topk_weights, int32_t *dev_status,
                        hipStream_t stream);
 
-/* Bytes of workspace ep_get_layout / ep_notify / ep_dispatch need for this shape (0 if s
- * is invalid).  The workspace is device memory, 256-byte aligned, owned by the caller, and
+/* Bytes of workspace ep_get_layout / ep_notify / ep_dispatch / ep_dispatch_grouped need for
+ * this shape (0 if s is invalid).  It holds the completion counters and running counts of
+ * layout and notify, the per-token rank masks and per-chunk row offsets notify leaves for
+ * dispatch, and the per-(token, slot) grouped positions ep_dispatch_grouped keeps between its
+ * own launches.  The workspace is device memory, 256-byte aligned, owned by the caller, and
  * must be zero-filled before its first use (hipMemset once at allocation): its completion
  * counters and running counts must start at zero, and every call leaves them at zero
  * again.  Calls that run concurrently must not share a workspace. */
