@@ -359,8 +359,11 @@ __global__ __launch_bounds__(WPB *kWave) void group_copy_kernel(CopyParams p) {
             if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(z, dst + i * kWave);
     }
     if (seg == 0) {
-        for (int i = lane; i < p.num_scales; i += kWave)
-            p.dst_scales[g * p.num_scales + i] = row >= 0 ? p.src_scales[srow * p.num_scales + i] : 0.0f;
+        for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {  // wave-uniform, per-lane predicate
+            const int i = i0 + lane;
+            const float sc = (i < p.num_scales && row >= 0) ? p.src_scales[srow * p.num_scales + i] : 0.0f;
+            if (i < p.num_scales) p.dst_scales[g * p.num_scales + i] = sc;
+        }
     }
 }
 
@@ -436,7 +439,8 @@ __global__ __launch_bounds__(256) void group_pad_kernel(const int32_t *grouped_r
     if (g >= limit || grouped_row[g] != -1) return;  // whole wave
     const u32x4 z = {0u, 0u, 0u, 0u};
     for (int64_t u = lane; u < row_units; u += kWave) __builtin_nontemporal_store(z, dst + g * row_units + u);
-    for (int i = lane; i < num_scales; i += kWave) dst_scales[g * num_scales + i] = 0.0f;
+    for (int i0 = 0; i0 < num_scales; i0 += kWave)  // wave-uniform, per-lane predicate
+        if (i0 + lane < num_scales) dst_scales[g * num_scales + i0 + lane] = 0.0f;
 }
 
 // ---- straight from x, pull form (many tokens): the grouped rows are produced
@@ -533,7 +537,8 @@ __global__ __launch_bounds__(kPullWaves *kWave) void group_pull_kernel(PullParam
                 const int64_t g = b0 + __builtin_ctzll(pp);
                 u32x4 *d = p.dst + g * p.row_units;
                 for (int64_t u = lane; u < p.row_units; u += kWave) __builtin_nontemporal_store(z, d + u);
-                for (int i = lane; i < p.num_scales; i += kWave) p.dst_scales[g * p.num_scales + i] = 0.0f;
+                for (int i0 = 0; i0 < p.num_scales; i0 += kWave)  // wave-uniform, per-lane predicate
+                    if (i0 + lane < p.num_scales) p.dst_scales[g * p.num_scales + i0 + lane] = 0.0f;
             }
         }
     }
