@@ -83,7 +83,7 @@ def layout_notify_bytes(T, K, R, E, C) -> int:
 PROFILE = os.path.join(ROOT, "profiles", "ep_kernels_prefill_hbm_bytes.txt")
 KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_pull_kernel_fp8": ["ep_dispatch.hip", "ep_internal.h"],
-                  "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dispatch_cached_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
                   "dispatch_grouped_kernels": ["ep_dispatch.hip", "ep_group.hip", "ep_internal.h"],
@@ -348,7 +348,7 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
         and not bool(g.grouped_x[~entries].view(torch.int16).any().item()))
     out["group_by_expert"]["grouped_rows"] = M
     del g
-    for key, kernel in (("dispatch_cached_bf16", "dispatch_kernel_cached_bf16"), ("dispatch_fp8", "dispatch_pull_kernel_fp8"),
+    for key, kernel in (("dispatch_cached_bf16", "dispatch_cached_pull_kernel"), ("dispatch_fp8", "dispatch_pull_kernel_fp8"),
                         ("dispatch_cached_fp8", "dispatch_kernel_cached_fp8")):
         out[key]["traffic"] = measured_traffic(kernel, wl.name)
     out["group_by_expert"]["traffic"] = measured_traffic("group_kernels", wl.name)
