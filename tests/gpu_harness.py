@@ -100,8 +100,13 @@ def run_both(x, topk_idx, topk_weights, E, R, C, my_rank=0, align=1, capacity=No
     ref["recv_src_info"] = dis["recv_src_info"][:rows]
     ref["combined_x"] = com["combined_x"]
     ref["combined_topk_weights"] = com["combined_topk_weights"]
+    # the same weighted sums in binary64, for the secondary bound on the bf16 outputs
+    ref["combined_x_f64"] = orc.combine_f64(dis["recv_x"][:rows], dis["recv_topk_weights"][:rows], dis["send_slot"],
+                                            rows)[0]
     if y is not None:
         ref["combined_x_y"] = orc.combine(y, dis["recv_topk_weights"][:rows], dis["send_slot"], y.shape[0])["combined_x"]
+        ref["combined_x_y_f64"] = orc.combine_f64(y, dis["recv_topk_weights"][:rows], dis["send_slot"],
+                                                  y.shape[0])[0]
     ref["status"] = lay["status"] | note["status"] | dis["status"] | com["status"]
     return gpu, ref
 
@@ -139,7 +144,23 @@ def compare(gpu: dict, ref: dict, tol: float = 1e-2) -> list[str]:
         d = np.abs(g.astype(np.float64) - r.astype(np.float64))
         if d.size and d.max() > tol:
             errs.append(f"{k}: max |diff| {d.max():.4g} > {tol}")
+        # secondary bound against the binary64 sum: max(tol, one bf16 ulp of the
+        # exact value), the most a correctly rounded fp32 chain can be off after
+        # its final rounding to bf16
+        f = ref.get(k + "_f64")
+        if f is not None and f.size:
+            lim = np.maximum(tol, bf16_ulp(f))
+            e = np.abs(g.astype(np.float64) - f)
+            if np.any(e > lim):
+                errs.append(f"{k}: {int((e > lim).sum())} elements beyond max({tol}, ulp_bf16) of the binary64 sum")
     return errs
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (8 significant bits); the subnormal spacing at 0."""
+    a = np.abs(v)
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    return np.where(a > 0, 2.0 ** (e - 7), 2.0 ** -133)
 
 
 def combine_bit_differences(gpu: dict, ref: dict) -> dict:

@@ -253,6 +253,11 @@ def combine_closed_forms(o, x, idx, w, E, R, lay, note, dis) -> list[str]:
     tol = 0.5 * _ulp_bf16(exact) * 1.001
     if np.any(np.abs(got - exact) > tol):
         errs.append(f"scaled combine off by {np.max(np.abs(got - exact) - tol):.3g} beyond half-ulp")
+    # 3) the binary64 evaluation of the same sum: the closed form up to the
+    # rounding of a few binary64 additions (the products W*y are exact there)
+    f64, st = o.combine_f64(y, dis["recv_topk_weights"], slot, n)
+    if st != 0 or np.any(np.abs(f64 - exact) > 1e-12 * np.abs(exact) + 1e-300):
+        errs.append(f"binary64 combine differs from the closed form by {np.max(np.abs(f64 - exact)):.3g}")
     return errs
 
 
@@ -328,6 +333,11 @@ def pin_bruteforce(o, max_cases: int | None = None) -> list[str]:
                     got = bf16_to_f64(com["combined_x"])
                     if np.any(np.abs(got - want) > 0.5 * _ulp_bf16(want) * 1.001):
                         errs.append(f"combine mismatch idx={idx.tolist()} R={R} C={C}")
+                    # the binary64 form: small integers times multiples of 1/8, so
+                    # every partial sum is exact and the results must be equal
+                    f64, st = o.combine_f64(y, dis["recv_topk_weights"], dis["send_slot"], n)
+                    if st != 0 or not np.array_equal(f64, want):
+                        errs.append(f"binary64 combine mismatch idx={idx.tolist()} R={R} C={C}")
     return errs
 
 

@@ -61,6 +61,10 @@ MUTANTS = {
                                 "memcpy(recv_x + s * row_bytes, x + (t > 0 ? t - 1 : t) * row_bytes, (size_t)row_bytes);"),
     "cached_bad_slot_not_flagged": ("                status |= ORC_BAD_SEND_SLOT;\n                continue;\n            }\n            memcpy(recv_x",
                                     "                continue;\n            }\n            memcpy(recv_x"),
+    "combine_f64_keeps_last_rank": ("o[i] += W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);",
+                                    "o[i] = W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);"),
+    "combine_f64_W_keeps_last_term": ("W += (double)recv_topk_weights[(int64_t)s * K + j];",
+                                      "W = (double)recv_topk_weights[(int64_t)s * K + j];"),
     "group_slot_major_order": ("for (int64_t row = lo; row < hi; ++row) {\n                for (int32_t j = 0; j < K; ++j) {",
                                "for (int32_t j = 0; j < K; ++j) {\n                for (int64_t row = lo; row < hi; ++row) {"),
     "group_offsets_unaligned": ("offset += size;", "offset += used;"),
