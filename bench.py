@@ -311,6 +311,16 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
     rows = b.send_slot[live].long()
     tok = torch.arange(T, device=x.device).unsqueeze(1).expand(T, R)[live]
 
+    # dispatch without a workspace: the routing worked out from is_token_in_rank and the
+    # prefix sums inside the call (same metadata outputs, so b's buffers are reused)
+    rx2, ss2 = torch.empty_like(b.recv_x), torch.empty_like(b.send_slot)
+    out["dispatch_no_workspace"] = rate(dispatch_bytes(T, H, K, R, n_recv), mean_us(
+        lambda: ep.ep_dispatch(shape, x, idx, w, b.in_rank, b.gbl, b.recv_gbl, None, n_recv, rx2, b.recv_w,
+                               b.recv_idx, b.src_info, ss2, b.dev_status)))
+    out["dispatch_no_workspace"]["check"] = bool(torch.equal(ss2, b.send_slot) and
+                                                 torch.equal(rx2.view(torch.int16), b.recv_x.view(torch.int16)))
+    del rx2, ss2
+
     cx = torch.empty_like(b.recv_x)
     out["dispatch_cached_bf16"] = rate(dispatch_cached_bytes(T, R, n_recv, 2 * H, 0), mean_us(
         lambda: ep.ep_dispatch_cached(shape, x, 2, None, 0, b.send_slot, n_recv, cx, None, b.dev_status)))
@@ -325,8 +335,8 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
     rs = torch.empty((n_recv, S), dtype=torch.float32, device=x.device)
     slot8 = torch.empty_like(b.send_slot)
     out["dispatch_fp8"] = rate(dispatch_fp8_bytes(T, H, K, R, n_recv, S), mean_us(
-        lambda: ep.ep_dispatch_fp8(shape, x8, sc, S, idx, w, b.recv_gbl, b.workspace, n_recv, rx, rs, b.recv_w,
-                                   b.recv_idx, b.src_info, slot8, b.dev_status)))
+        lambda: ep.ep_dispatch_fp8(shape, x8, sc, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, n_recv, rx,
+                                   rs, b.recv_w, b.recv_idx, b.src_info, slot8, b.dev_status)))
     out["dispatch_fp8"]["check"] = bool(torch.equal(slot8, b.send_slot) and torch.equal(rx[rows], x8[tok])
                                         and torch.equal(rs[rows], sc[tok]))
     out["dispatch_fp8"]["num_scales"] = S

@@ -38,9 +38,22 @@ bool workspace_ok(const ep_shape_t *s, const void *ws, size_t bytes) {
            bytes >= workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels, s->num_topk).total;
 }
 
+// The routing inputs of a dispatch: is_token_in_rank, the channel prefix matrix and
+// the receive prefix sums are required; the workspace is optional (NULL: the routing
+// is worked out from those inputs, which needs channels of at most
+// kMaxDeriveChannelTokens tokens), and when given it must be a whole workspace.
+ep_status_t routing_checked(const ep_shape_t *s, const uint8_t *in_rank, const int32_t *gbl,
+                            const int32_t *recv_gbl, const void *workspace, size_t workspace_bytes) {
+    if (in_rank == nullptr || gbl == nullptr || recv_gbl == nullptr) return EP_ERR_INVALID_ARG;
+    if (workspace != nullptr) return workspace_ok(s, workspace, workspace_bytes) ? EP_OK : EP_ERR_INVALID_ARG;
+    const int64_t tc = ((int64_t)s->num_tokens + s->num_channels - 1) / s->num_channels;
+    return tc <= kMaxDeriveChannelTokens ? EP_OK : EP_ERR_UNSUPPORTED;
+}
+
 // Shared checks and launch of the bf16 and fp8 dispatch entry points.
 ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_bytes, const float *x_scales,
                              int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                             const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                              const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                              int32_t recv_capacity, void *recv_x, float *recv_x_scales, float *recv_topk_weights,
                              int64_t *recv_topk_idx, int32_t *recv_src_info, int32_t *send_slot,
@@ -50,8 +63,7 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
     if (row_bytes % 16 != 0 || recv_capacity < 0 || num_scales < 0) return EP_ERR_INVALID_ARG;
     if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
     if (s->num_tokens == 0) return EP_OK;
-    if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || recv_gbl_rank_prefix_sum == nullptr ||
-        send_slot == nullptr)
+    if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr)
         return EP_ERR_INVALID_ARG;
     if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
         return EP_ERR_INVALID_ARG;
@@ -59,7 +71,9 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
         return EP_ERR_INVALID_ARG;
     if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
     if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
-    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
+    st = routing_checked(s, is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace,
+                         workspace_bytes);
+    if (st != EP_OK) return st;
     DispatchArgs a = {};
     a.x = x;
     a.row_units = row_bytes / 16;
@@ -67,6 +81,8 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
     a.num_scales = num_scales;
     a.topk_idx = topk_idx;
     a.topk_w = topk_weights;
+    a.in_rank = is_token_in_rank;
+    a.gbl = gbl_channel_prefix_matrix;
     a.recv_gbl = recv_gbl_rank_prefix_sum;
     a.ws = static_cast<const char *>(workspace);
     a.cached_slot = nullptr;
@@ -144,23 +160,26 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
 }
 
 ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_idx, const float *topk_weights,
+                        const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
                         int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
     return dispatch_checked(s, x, s ? (int64_t)s->hidden * 2 : 0, nullptr, 0, topk_idx, topk_weights,
-                            recv_gbl_rank_prefix_sum, workspace, workspace_bytes, recv_capacity, recv_x, nullptr,
-                            recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status, stream);
+                            is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace,
+                            workspace_bytes, recv_capacity, recv_x, nullptr, recv_topk_weights, recv_topk_idx,
+                            recv_src_info, send_slot, dev_status, stream);
 }
 
 ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_scales, int32_t num_scales,
-                            const int64_t *topk_idx, const float *topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                            const int64_t *topk_idx, const float *topk_weights, const uint8_t *is_token_in_rank,
+                            const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
                             const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
                             float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
                             int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
     return dispatch_checked(s, x, s ? (int64_t)s->hidden : 0, x_scales, num_scales, topk_idx, topk_weights,
-                            recv_gbl_rank_prefix_sum, workspace, workspace_bytes, recv_capacity, recv_x,
-                            recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status,
-                            stream);
+                            is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace,
+                            workspace_bytes, recv_capacity, recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx,
+                            recv_src_info, send_slot, dev_status, stream);
 }
 
 ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
@@ -239,6 +258,7 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
 
 ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                                const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                                 const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
                                 void *workspace, size_t workspace_bytes, int32_t recv_capacity,
                                 float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
@@ -266,7 +286,8 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
                            (grouped_capacity > 0 && grouped_x_scales == nullptr)))
         return EP_ERR_INVALID_ARG;
     if (s->num_tokens > 0) {
-        if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr)
+        if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr ||
+            is_token_in_rank == nullptr || gbl_channel_prefix_matrix == nullptr)
             return EP_ERR_INVALID_ARG;
         if (!aligned16(x) || !workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
     }
@@ -285,6 +306,8 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
         d.row_units = row_bytes / 16;
         d.topk_idx = topk_idx;
         d.topk_w = topk_weights;
+        d.in_rank = is_token_in_rank;
+        d.gbl = gbl_channel_prefix_matrix;
         d.recv_gbl = recv_gbl_rank_prefix_sum;
         d.ws = static_cast<const char *>(workspace);
         d.cap = recv_capacity;

@@ -5,16 +5,23 @@
 // holds every destination rank's slab in one allocation, laid out
 // [dst_rank][channel]; inside a slab the channel segments follow in channel
 // order with tokens ascending.  Because channels are contiguous ascending token
-// ranges, token t's row on rank r is
-//     slab_begin(r) + #{t' < t : t' goes to r},   slab_begin(r) = recv_gbl[r-1].
+// ranges, token t of channel c has, on rank r, the row
+//     slab_begin(r) + gbl[r][c-1] + #{t' in channel c, t' < t : t' goes to r}
+// (slab_begin(r) = recv_gbl[r-1]), which with a consistent prefix matrix is
+//     slab_begin(r) + #{t' < t : t' goes to r}.
 // For each routed (t, r): recv_x[row] = x[t] (bitwise), the topk weights and
 // local expert ids of the slots whose expert lives on r (0 / -1 elsewhere),
 // src_info[row] = {my_rank, t}, send_slot[t][r] = row.
 //
 // Design (the pages' sender/forwarder rings are transport machinery and are not
-// reproduced).  notify left each token's 64-bit rank mask and, per 64-token
-// chunk, the exclusive row offset inside every slab; with those every row's
-// position is known without a serial scan.  Two forms:
+// reproduced).  Every row's position is known without a serial scan once each
+// 64-token chunk has its tokens' 64-bit rank masks and its row offset inside
+// every slab.  Those come either from the workspace notify filled (checked here
+// against is_token_in_rank and the channel prefix matrix), or, without a
+// workspace, straight from the routing inputs: the masks from is_token_in_rank
+// rows, the offset from the prefix matrix entry of the chunk's channel plus the
+// tokens between the channel's edge and the chunk, counted with the same bit
+// transpose.  Two forms:
 //  - pull (from 2048 tokens, rows of 1 KiB to 1 MiB): the rows are produced in
 //    receive order.  Each XCD takes groups of 128 tokens in turn; a wave finds
 //    the group's rows per rank with a 64x64 bit transpose of the masks and a
@@ -39,9 +46,11 @@ struct DispatchParams {
     const float *x_scales;
     const int64_t *topk_idx;
     const float *topk_w;
+    const uint8_t *in_rank;  // [t][R] is_token_in_rank
+    const int32_t *gbl;      // [R][C] channel prefix matrix (inclusive)
     const int32_t *recv_gbl;
-    const uint64_t *mask;
-    const int32_t *rank_off;
+    const uint64_t *mask;    // workspace: per-token rank masks, or null (derive)
+    const int32_t *rank_off; // workspace: per-chunk row offsets inside each slab, or null (derive)
     const int32_t *cached_slot;
     u32x4 *recv_x;
     float *recv_scales;
@@ -52,9 +61,102 @@ struct DispatchParams {
     int32_t *tok_pos;
     int32_t *dev_status;
     int64_t T;
+    int64_t Tc;         // tokens per channel, ceil(t / C)
     int64_t row_units;  // 16-byte units per row
-    int R, K, E, experts_per_rank, my_rank, cap, S, num_scales;
+    int R, K, E, C, experts_per_rank, my_rank, cap, S, num_scales;
+    int in_unit;        // load unit of an is_token_in_rank row (16, 8 or 1 bytes)
+    bool derive;        // routing from is_token_in_rank and the prefix matrix (no workspace)
 };
+
+// ---------------------------------------------------------------- routing
+// Rank mask of token tok (0 past the last token): from its is_token_in_rank row
+// when deriving, else from the workspace.
+__device__ __forceinline__ uint64_t token_mask(const DispatchParams &p, int64_t tok, bool derive) {
+    if (tok >= p.T) return 0ull;
+    return derive ? load_rank_mask(p.in_rank + tok * p.R, p.R, p.in_unit) : p.mask[tok];
+}
+
+// Lane r < R: the tokens of [x, y) sent to rank r (0 on the other lanes), 64
+// tokens a step: lane l loads token s + l's row, the bit transpose hands lane r
+// the step's column for rank r.
+__device__ int count_tokens(const DispatchParams &p, int64_t x, int64_t y, int lane) {
+    int n = 0;
+    for (int64_t s = x; s < y; s += kChunk) {
+        const int64_t tok = s + lane;
+        const uint64_t m = tok < y ? load_rank_mask(p.in_rank + tok * p.R, p.R, p.in_unit) : 0ull;
+        n += __popcll(transpose64(m));
+    }
+    return n;
+}
+
+// Tokens of a group's columns (lane r: bit l of col[c] = token c*64 + l goes to
+// rank r) at offsets below d, 0 <= d <= 64*CPG.
+template <int CPG>
+__device__ __forceinline__ int count_below(const uint64_t (&col)[CPG], int64_t d) {
+    int n = 0;
+#pragma unroll
+    for (int c = 0; c < CPG; ++c) {
+        const int64_t k = d - c * kChunk;
+        const uint64_t m = k >= kChunk ? ~0ull : (k <= 0 ? 0ull : (1ull << k) - 1ull);
+        n += __popcll(col[c] & m);
+    }
+    return n;
+}
+
+// Lane r < R: #{t < a : token t goes to rank r}, the offset inside slab r of a
+// group of CPG chunks starting at token a (a multiple of 64) with columns col.
+// Channel c holding a covers [b, e); the prefix matrix gives the count before b
+// (entry c-1) and before e (entry c), so the offset is entry c-1 plus the tokens
+// of [b, a), or entry c minus those of [a, e).  The side with fewer tokens beyond
+// the group's own is counted (at most half a channel); other = true takes the
+// other side instead (a second reading of the same offset, for the checks).
+template <int CPG>
+__device__ int derive_offset(const DispatchParams &p, int64_t a, const uint64_t (&col)[CPG], int lane,
+                             bool other = false) {
+    constexpr int64_t GT = CPG * kChunk;
+    const int64_t c = a / p.Tc;
+    const int64_t b = c * p.Tc;
+    const int64_t e = b + p.Tc < p.T ? b + p.Tc : p.T;
+    const int64_t back = a - b;
+    const int64_t fwd = e > a + GT ? e - (a + GT) : 0;
+    int v = 0;
+    if ((fwd <= back) != other) {
+        if (lane < p.R) v = p.gbl[(int64_t)lane * p.C + c];
+        v -= count_below(col, (e < a + GT ? e : a + GT) - a);
+        if (fwd > 0) v -= count_tokens(p, a + GT, e, lane);
+    } else {
+        if (lane < p.R && c > 0) v = p.gbl[(int64_t)lane * p.C + c - 1];
+        v += count_tokens(p, b, a, lane);
+    }
+    return v;
+}
+
+// The routing inputs checked against a group's columns by one wave per group
+// (lane r: off0 = the group's offset inside slab r, alt = the same offset read a
+// second, independent way, slab0 = the slab start).  True when one disagrees:
+//  - off0 != alt;
+//  - a channel start in [a, a + GT] before the last token not at off0 plus the
+//    group's tokens before it (prefix entry c-1);
+//  - in the group holding the last token: a channel total from the last token's
+//    channel on, or a slab size, not the group's offset plus its tokens.
+// Over all groups this checks every entry the rows depend on.
+template <int CPG>
+__device__ bool anchors_disagree(const DispatchParams &p, int64_t a, const uint64_t (&col)[CPG], int off0, int alt,
+                                 int slab0, int lane) {
+    constexpr int64_t GT = CPG * kChunk;
+    const bool rk = lane < p.R;
+    bool bad = rk && off0 != alt;
+    for (int64_t c = (a + p.Tc - 1) / p.Tc; c * p.Tc < p.T && c * p.Tc <= a + GT; ++c) {
+        const int want = (rk && c > 0) ? p.gbl[(int64_t)lane * p.C + c - 1] : 0;
+        bad |= rk && off0 + count_below(col, c * p.Tc - a) != want;
+    }
+    if (a + GT >= p.T) {
+        const int total = off0 + count_below(col, GT);
+        bad |= rk && p.recv_gbl[rk ? lane : 0] - slab0 != total;
+        for (int64_t c = (p.T - 1) / p.Tc; c < p.C; ++c) bad |= rk && p.gbl[(int64_t)lane * p.C + c] != total;
+    }
+    return ballot64(bad) != 0ull;
+}
 
 // Per-token scales (fp8 rows) travel beside the rows: lane r holds the row of
 // destination r (or -1), `dests` has bit r set for every routed destination.
@@ -134,10 +236,18 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
         // ---- routing state: chunk masks, slab bases, this token's topk slots
         const int64_t q = t / kChunk;
         const int my = (int)(t - q * kChunk);
-        const int64_t tok = q * kChunk + lane;
-        const uint64_t m = tok < p.T ? p.mask[tok] : 0ull;
-        int base = 0;
-        if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q * R + lane];
+        const int64_t a = q * kChunk;
+        const uint64_t m = token_mask(p, a + lane, p.derive);
+        const int slab0 = (lane < R && lane > 0) ? p.recv_gbl[lane - 1] : 0;
+        int off = 0;  // lane r: the chunk's offset inside slab r
+        uint64_t colq[1] = {0ull};
+        if (p.derive) {
+            colq[0] = transpose64(m);
+            off = derive_offset<1>(p, a, colq, lane);
+        } else if (lane < R) {
+            off = p.rank_off[q * R + lane];
+        }
+        const int base = lane < R ? slab0 + off : 0;
         if (live && seg == 0 && lane < p.K) {
             e = p.topk_idx[t * p.K + lane];
             wt = p.topk_w[t * p.K + lane];
@@ -151,9 +261,24 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
             const uint64_t b = ballot64((m >> r) & 1ull);
             if (lane == r) slot = base + __popcll(b & before);
         }
-        const bool over = slot >= p.cap;
+        const bool routed = lane < R && ((mine >> lane) & 1ull);
+        const bool over = routed && (slot < 0 || slot >= p.cap);  // a negative row only from bad prefixes
         if (over) slot = -1;
-        if (live && seg == 0 && ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+        if (live && seg == 0) {
+            if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+            // the workspace's mask must be this token's is_token_in_rank row
+            if (!p.derive) {
+                const bool want = lane < R && p.in_rank[t * R + lane] != 0;
+                if (ballot64(want != routed) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
+            }
+            // the first token's wave checks the chunk against the prefix matrix
+            if (my == 0) {
+                if (!p.derive) colq[0] = transpose64(m);
+                const int alt = derive_offset<1>(p, a, colq, lane, p.derive);
+                if (anchors_disagree<1>(p, a, colq, off, alt, slab0, lane) && lane == 0)
+                    flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+            }
+        }
     }
     if (!live) slot = -1;
     const uint64_t dests = ballot64(slot >= 0);
@@ -219,7 +344,7 @@ constexpr int64_t kMaxPullRowUnits = 1 << 16;  // 1 MiB rows
 // read hit the group's x in the XCD's L2.  Before its tasks, each group's GT
 // token tasks (send_slot, metadata, scales) go to GT of the XCD's waves, a
 // different set for each group.
-template <int CPG, int U, bool EXACT, int WPB>
+template <int CPG, int U, bool EXACT, int WPB, bool DERIVE>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParams p) {
     constexpr int GT = CPG * kChunk;  // tokens per group
     const int lane = threadIdx.x & (kWave - 1);
@@ -241,48 +366,73 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
         // group's masks, so its token task does not wait on memory later.
         const int rot = (int)(((g / kXcds) * GT) % W);
         const int kt = wx >= rot ? wx - rot : wx - rot + W;
-        const int64_t t1 = q0 * kChunk + kt;
+        const int64_t a = q0 * kChunk;  // the group's first token
+        const int64_t t1 = a + kt;
         const bool tok1 = kt < GT && t1 < p.T;
         int64_t e1 = -1;
         float w1 = 0.0f;
-        int base1 = 0;
+        bool in1 = false;  // the first token's is_token_in_rank byte (lane r), checked against the workspace
         if (tok1) {
             if (lane < p.K) {
                 e1 = p.topk_idx[t1 * p.K + lane];
                 w1 = p.topk_w[t1 * p.K + lane];
             }
-            if (lane < R) base1 = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[(q0 + kt / kChunk) * R + lane];
+            if (!DERIVE && lane < R) in1 = p.in_rank[t1 * R + lane] != 0;
         }
+        const int slab0 = (lane < R && lane > 0) ? p.recv_gbl[lane - 1] : 0;
+        int off0 = 0;  // lane r: the group's offset inside slab r
+        if (!DERIVE && lane < R) off0 = p.rank_off[q0 * R + lane];
         // lane r: bit l of col[c] set when token (q0 + c)*64 + l goes to rank r
         uint64_t col[CPG];
         int n = 0;
 #pragma unroll
         for (int c = 0; c < CPG; ++c) {
-            const int64_t tok = (q0 + c) * kChunk + lane;
-            col[c] = transpose64(tok < p.T ? p.mask[tok] : 0ull);
+            col[c] = transpose64(token_mask(p, a + c * kChunk + lane, DERIVE));
             n += __popcll(col[c]);  // 0 on lanes >= R
         }
+        if (DERIVE) off0 = derive_offset<CPG>(p, a, col, lane);
         // the group's rows on rank r: [s0, s0 + n) in slab r, run r of the
-        // group's output starting at pex
-        int s0 = 0;
-        if (lane < R) s0 = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[q0 * R + lane];
+        // group's output starting at pex; chunk c's rows start at cb[c]
+        const int s0 = lane < R ? slab0 + off0 : 0;
+        int cb[CPG];
+        {
+            int run = s0;
+#pragma unroll
+            for (int c = 0; c < CPG; ++c) {
+                cb[c] = run;
+                run += __popcll(col[c]);
+            }
+        }
         const int incl = wave_inclusive_scan(n);
         const int pex = lane < R ? incl - n : INT32_MAX;
         const int rows = readlane32(incl, kWave - 1);
+        // one wave per group checks the offsets against the prefix matrix: the
+        // derived offset against the other side of its channel, the workspace's
+        // against the derived one
+        if (kt == 0) {
+            const int alt = derive_offset<CPG>(p, a, col, lane, DERIVE);
+            if (anchors_disagree<CPG>(p, a, col, off0, alt, slab0, lane) && lane == 0)
+                flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+        }
 
         // ---- token tasks: send_slot, metadata, scales (more than one per wave
         // only when the XCD has fewer than GT waves)
         for (int k = kt; k < GT; k += W) {
-            const int64_t t = q0 * kChunk + k;
+            const int64_t t = a + k;
             if (t >= p.T) break;  // wave-uniform; later k are larger
             const int c = k / kChunk, l = k - c * kChunk;
             uint64_t cc = col[0];
+            int base = cb[0];
 #pragma unroll
-            for (int c2 = 1; c2 < CPG; ++c2)
-                if (c == c2) cc = col[c2];
+            for (int c2 = 1; c2 < CPG; ++c2) {
+                if (c == c2) {
+                    cc = col[c2];
+                    base = cb[c2];
+                }
+            }
             int64_t e = e1;
             float wt = w1;
-            int base = base1;
+            bool in = in1;
             if (k != kt) {
                 e = -1;
                 wt = 0.0f;
@@ -290,11 +440,14 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
                     e = p.topk_idx[t * p.K + lane];
                     wt = p.topk_w[t * p.K + lane];
                 }
-                if (lane < R) base = (lane > 0 ? p.recv_gbl[lane - 1] : 0) + p.rank_off[(q0 + c) * R + lane];
+                if (!DERIVE && lane < R) in = p.in_rank[t * R + lane] != 0;
             }
+            const bool routed = lane < R && ((cc >> l) & 1ull);
+            // the workspace's mask must be this token's is_token_in_rank row
+            if (!DERIVE && ballot64(in != routed) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
             int slot = -1;
-            if (lane < R && ((cc >> l) & 1ull)) slot = base + __popcll(cc & ((1ull << l) - 1ull));
-            const bool over = slot >= p.cap;
+            if (routed) slot = base + __popcll(cc & ((1ull << l) - 1ull));
+            const bool over = routed && (slot < 0 || slot >= p.cap);  // a negative row only from bad prefixes
             if (over) slot = -1;
             if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
             const uint64_t dests = ballot64(slot >= 0);
@@ -538,8 +691,11 @@ __global__ __launch_bounds__(kCachedWaves *kWave) void dispatch_cached_pull_kern
 
 template <int CPG, int U, bool EXACT, int WPB>
 hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
-    hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB>), dim3((unsigned)(kXcds * blocks_per_xcd)),
-                       dim3(WPB * kWave), 0, stream, p);
+    const dim3 grid((unsigned)(kXcds * blocks_per_xcd)), block(WPB * kWave);
+    if (p.derive)
+        hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB, true>), grid, block, 0, stream, p);
+    else
+        hipLaunchKernelGGL((dispatch_pull_kernel<CPG, U, EXACT, WPB, false>), grid, block, 0, stream, p);
     return hipGetLastError();
 }
 
@@ -672,13 +828,23 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.x_scales = a.x_scales;
     p.topk_idx = a.topk_idx;
     p.topk_w = a.topk_w;
+    p.in_rank = a.in_rank;
+    p.gbl = a.gbl;
     p.recv_gbl = a.recv_gbl;
     p.mask = nullptr;
     p.rank_off = nullptr;
+    p.derive = a.ws == nullptr;
     if (a.ws != nullptr) {
         const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
         p.mask = reinterpret_cast<const uint64_t *>(a.ws + w.mask);
         p.rank_off = reinterpret_cast<const int32_t *>(a.ws + w.rank_off);
+    }
+    p.C = s.num_channels;
+    p.Tc = ((int64_t)s.num_tokens + p.C - 1) / p.C;
+    {
+        const uintptr_t ia = reinterpret_cast<uintptr_t>(a.in_rank);
+        const int R = s.num_ranks;
+        p.in_unit = (R % 16 == 0 && ia % 16 == 0) ? 16 : (R % 8 == 0 && ia % 8 == 0) ? 8 : 1;
     }
     p.cached_slot = a.cached_slot;
     p.recv_x = reinterpret_cast<u32x4 *>(a.recv_x);

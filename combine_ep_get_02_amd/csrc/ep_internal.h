@@ -79,8 +79,10 @@ struct DispatchArgs {
     int num_scales;
     const int64_t *topk_idx;
     const float *topk_w;
+    const uint8_t *in_rank;      // [t][R] is_token_in_rank (not cached mode)
+    const int32_t *gbl;          // [R][C] channel prefix matrix (not cached mode)
     const int32_t *recv_gbl;
-    const char *ws;
+    const char *ws;              // the workspace notify filled, or null: routing worked out from the above
     const int32_t *cached_slot;  // [t][R] rows of an earlier dispatch (cached mode)
     int32_t cap;
     void *recv_x;
@@ -94,6 +96,8 @@ struct DispatchArgs {
 };
 
 hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream);
+// Longest channel (tokens) for which dispatch works out its routing without a workspace.
+constexpr int64_t kMaxDeriveChannelTokens = 4096;
 
 // Arguments of the grouping by local expert (one launch computing positions,
 // one copying rows).  Rows are row_units 16-byte units.
@@ -185,6 +189,46 @@ __device__ __forceinline__ uint64_t transpose64(uint64_t x) {
 __device__ __forceinline__ uint32_t nonzero_bytes4(uint32_t w) {
     uint32_t hi = (((w & 0x7f7f7f7fu) + 0x7f7f7f7fu) | w) & 0x80808080u;
     return ((hi >> 7) & 1u) | ((hi >> 14) & 2u) | ((hi >> 21) & 4u) | ((hi >> 28) & 8u);
+}
+
+// Rank mask of one is_token_in_rank row (R <= 64 bytes, any non-zero byte counts
+// as 1): bit r set when byte r is non-zero.  load_unit 16 or 8 reads the row in
+// aligned 16- or 8-byte pieces (R a multiple of that and the row aligned to it),
+// 1 byte by byte.
+__device__ __forceinline__ uint64_t load_rank_mask(const uint8_t *row, int R, int load_unit) {
+    uint64_t m = 0;
+    // fixed-bound unrolled loops so all of a row's loads are in flight together
+    if (load_unit == 16) {
+        const uint4 *p = reinterpret_cast<const uint4 *>(row);
+        uint4 v[kMaxRanks / 16];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 16; ++g)
+            if (g < R / 16) v[g] = p[g];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 16; ++g) {
+            if (g < R / 16) {
+                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4) |
+                                      (nonzero_bytes4(v[g].z) << 8) | (nonzero_bytes4(v[g].w) << 12);
+                m |= bits << (16 * g);
+            }
+        }
+    } else if (load_unit == 8) {
+        const uint2 *p = reinterpret_cast<const uint2 *>(row);
+        uint2 v[kMaxRanks / 8];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 8; ++g)
+            if (g < R / 8) v[g] = p[g];
+#pragma unroll
+        for (int g = 0; g < kMaxRanks / 8; ++g) {
+            if (g < R / 8) {
+                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4);
+                m |= bits << (8 * g);
+            }
+        }
+    } else {
+        for (int r = 0; r < R; ++r) m |= (uint64_t)(row[r] != 0) << r;
+    }
+    return m;
 }
 
 __device__ __forceinline__ void flag(int32_t *dev_status, int bits) {

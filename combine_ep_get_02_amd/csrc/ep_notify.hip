@@ -49,42 +49,6 @@ struct NotifyParams {
     int R, C, E, nodes, align, load_unit;
 };
 
-__device__ __forceinline__ uint64_t load_rank_mask(const uint8_t *row, int R, int load_unit) {
-    uint64_t m = 0;
-    // fixed-bound unrolled loops so all of a row's loads are in flight together
-    if (load_unit == 16) {
-        const uint4 *p = reinterpret_cast<const uint4 *>(row);
-        uint4 v[kMaxRanks / 16];
-#pragma unroll
-        for (int g = 0; g < kMaxRanks / 16; ++g)
-            if (g < R / 16) v[g] = p[g];
-#pragma unroll
-        for (int g = 0; g < kMaxRanks / 16; ++g) {
-            if (g < R / 16) {
-                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4) |
-                                      (nonzero_bytes4(v[g].z) << 8) | (nonzero_bytes4(v[g].w) << 12);
-                m |= bits << (16 * g);
-            }
-        }
-    } else if (load_unit == 8) {
-        const uint2 *p = reinterpret_cast<const uint2 *>(row);
-        uint2 v[kMaxRanks / 8];
-#pragma unroll
-        for (int g = 0; g < kMaxRanks / 8; ++g)
-            if (g < R / 8) v[g] = p[g];
-#pragma unroll
-        for (int g = 0; g < kMaxRanks / 8; ++g) {
-            if (g < R / 8) {
-                const uint64_t bits = nonzero_bytes4(v[g].x) | (nonzero_bytes4(v[g].y) << 4);
-                m |= bits << (8 * g);
-            }
-        }
-    } else {
-        for (int r = 0; r < R; ++r) m |= (uint64_t)(row[r] != 0) << r;
-    }
-    return m;
-}
-
 __device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
     const int64_t first = q * kChunk;
     const int64_t tok = first + lane;

@@ -19,6 +19,7 @@ LIBRARY = os.path.join(_PKG, "libep.so")
 
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
 EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
+EP_DEV_STALE_WORKSPACE = 16
 
 EXPORTED = ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
             "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_workspace_bytes", "ep_status_string")
@@ -51,13 +52,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib = ctypes.CDLL(path)
     lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
-    lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
-    lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + \
-        [_P] * 8
+    lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
+    lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                    ctypes.c_int32] + [_P] * 8
     lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
     lib.ep_group_by_expert.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
                                        ctypes.c_int32] + [_P] * 8
-    lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P,
+    lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
     for name in ("ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
@@ -131,21 +132,34 @@ def ep_notify(shape, is_token_in_rank, num_tokens_per_rank, num_tokens_per_rdma_
     return int(host.value) if read_back else None
 
 
-def ep_dispatch(shape, x, topk_idx, topk_weights, recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x,
-                recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status=None, stream=None) -> None:
+def _ws(workspace):
+    """Pointer and size of an optional workspace tensor."""
+    if workspace is None:
+        return None, 0
+    return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def ep_dispatch(shape, x, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+                recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x, recv_topk_weights, recv_topk_idx,
+                recv_src_info, send_slot, dev_status=None, stream=None) -> None:
+    """workspace: the one ep_notify filled for this is_token_in_rank, or None (the routing is
+    then worked out from is_token_in_rank and the prefix sums inside the call)."""
+    ws, ws_bytes = _ws(workspace)
     _check(load().ep_dispatch(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_weights),
-                              _ptr(recv_gbl_rank_prefix_sum), _ptr(workspace),
-                              workspace.numel() * workspace.element_size(), int(recv_capacity), _ptr(recv_x),
+                              _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
+                              _ptr(recv_gbl_rank_prefix_sum), ws, ws_bytes, int(recv_capacity), _ptr(recv_x),
                               _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info), _ptr(send_slot),
                               _ptr(dev_status), _stream(stream)), "ep_dispatch")
 
 
-def ep_dispatch_fp8(shape, x, x_scales, num_scales, topk_idx, topk_weights, recv_gbl_rank_prefix_sum, workspace,
-                    recv_capacity, recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot,
-                    dev_status=None, stream=None) -> None:
+def ep_dispatch_fp8(shape, x, x_scales, num_scales, topk_idx, topk_weights, is_token_in_rank,
+                    gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x,
+                    recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status=None,
+                    stream=None) -> None:
+    ws, ws_bytes = _ws(workspace)
     _check(load().ep_dispatch_fp8(ctypes.byref(shape), _ptr(x), _ptr(x_scales), int(num_scales), _ptr(topk_idx),
-                                  _ptr(topk_weights), _ptr(recv_gbl_rank_prefix_sum), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), int(recv_capacity), _ptr(recv_x),
+                                  _ptr(topk_weights), _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
+                                  _ptr(recv_gbl_rank_prefix_sum), ws, ws_bytes, int(recv_capacity), _ptr(recv_x),
                                   _ptr(recv_x_scales), _ptr(recv_topk_weights), _ptr(recv_topk_idx),
                                   _ptr(recv_src_info), _ptr(send_slot), _ptr(dev_status), _stream(stream)),
            "ep_dispatch_fp8")
@@ -171,14 +185,16 @@ def ep_group_by_expert(shape, recv_x, elem_bytes, recv_x_scales, num_scales, rec
            "ep_group_by_expert")
 
 
-def ep_dispatch_grouped(shape, x, elem_bytes, x_scales, num_scales, topk_idx, topk_weights, recv_gbl_rank_prefix_sum,
-                        num_recv_tokens_per_expert, workspace, recv_capacity, recv_topk_weights, recv_topk_idx,
-                        recv_src_info, send_slot, grouped_capacity, grouped_x, grouped_x_scales, grouped_row,
-                        grouped_weights, slot_pos, num_grouped_rows, dev_status=None, stream=None) -> None:
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+def ep_dispatch_grouped(shape, x, elem_bytes, x_scales, num_scales, topk_idx, topk_weights, is_token_in_rank,
+                        gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, num_recv_tokens_per_expert, workspace,
+                        recv_capacity, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, grouped_capacity,
+                        grouped_x, grouped_x_scales, grouped_row, grouped_weights, slot_pos, num_grouped_rows,
+                        dev_status=None, stream=None) -> None:
+    ws, ws_bytes = _ws(workspace)
     _check(load().ep_dispatch_grouped(ctypes.byref(shape), _ptr(x), int(elem_bytes), _ptr(x_scales), int(num_scales),
-                                      _ptr(topk_idx), _ptr(topk_weights), _ptr(recv_gbl_rank_prefix_sum),
-                                      _ptr(num_recv_tokens_per_expert), _ptr(workspace), ws_bytes, int(recv_capacity),
+                                      _ptr(topk_idx), _ptr(topk_weights), _ptr(is_token_in_rank),
+                                      _ptr(gbl_channel_prefix_matrix), _ptr(recv_gbl_rank_prefix_sum),
+                                      _ptr(num_recv_tokens_per_expert), ws, ws_bytes, int(recv_capacity),
                                       _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info),
                                       _ptr(send_slot), int(grouped_capacity), _ptr(grouped_x), _ptr(grouped_x_scales),
                                       _ptr(grouped_row), _ptr(grouped_weights), _ptr(slot_pos),
@@ -252,9 +268,12 @@ def run_notify(b: Buffers, read_back: bool = False, stream=None) -> int | None:
                      b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, read_back, b.dev_status, stream)
 
 
-def run_dispatch(b: Buffers, x, topk_idx, topk_weights, stream=None) -> None:
-    ep_dispatch(b.shape, x, topk_idx, topk_weights, b.recv_gbl, b.workspace, b.capacity, b.recv_x, b.recv_w,
-                b.recv_idx, b.src_info, b.send_slot, b.dev_status, stream)
+def run_dispatch(b: Buffers, x, topk_idx, topk_weights, use_workspace: bool = True, stream=None) -> None:
+    """use_workspace: take the routing state notify left in b.workspace; False: work it
+    out from b.in_rank and the prefix sums inside the call."""
+    ep_dispatch(b.shape, x, topk_idx, topk_weights, b.in_rank, b.gbl, b.recv_gbl,
+                b.workspace if use_workspace else None, b.capacity, b.recv_x, b.recv_w, b.recv_idx, b.src_info,
+                b.send_slot, b.dev_status, stream)
 
 
 def run_combine(b: Buffers, y=None, num_recv_rows=None, with_weights: bool = True, stream=None) -> None:
@@ -292,6 +311,7 @@ def run_group(b: Buffers, g: GroupBuffers, num_recv_rows=None, stream=None) -> N
 
 def run_dispatch_grouped(b: Buffers, g: GroupBuffers, x, topk_idx, topk_weights, stream=None) -> None:
     """Dispatch of bf16 rows straight into g's grouped layout (b.recv_x is neither written nor read)."""
-    ep_dispatch_grouped(b.shape, x, 2, None, 0, topk_idx, topk_weights, b.recv_gbl, b.recv_per_expert, b.workspace,
+    ep_dispatch_grouped(b.shape, x, 2, None, 0, topk_idx, topk_weights, b.in_rank, b.gbl, b.recv_gbl,
+                        b.recv_per_expert, b.workspace,
                         b.capacity, b.recv_w, b.recv_idx, b.src_info, b.send_slot, g.capacity, g.grouped_x, None,
                         g.grouped_row, g.grouped_w, g.slot_pos, g.num_grouped, b.dev_status, stream)

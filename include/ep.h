@@ -70,9 +70,15 @@ typedef enum {
 enum {
     EP_DEV_BAD_TOPK_IDX = 1,   /* a topk id outside [-1, num_experts): that slot is treated as masked */
     EP_DEV_RECV_OVERFLOW = 2,  /* a receive row >= recv_capacity: the row is not written, send_slot = -1 */
-    EP_DEV_COUNT_MISMATCH = 4, /* num_tokens_per_rank / _per_rdma_rank disagree with is_token_in_rank */
-    EP_DEV_BAD_SEND_SLOT = 8   /* a send_slot entry outside its valid range (combine, cached dispatch), or an
+    EP_DEV_COUNT_MISMATCH = 4, /* counts or prefixes disagree with is_token_in_rank: num_tokens_per_rank /
+                                  _per_rdma_rank (notify), gbl_channel_prefix_matrix or
+                                  recv_gbl_rank_prefix_sum (dispatch) */
+    EP_DEV_BAD_SEND_SLOT = 8,  /* a send_slot entry outside its valid range (combine, cached dispatch), or an
                                   inconsistent grouped position (grouped dispatch): skipped */
+    EP_DEV_STALE_WORKSPACE = 16 /* the workspace does not hold what the call needs: its control words were not
+                                  zero on entry (a workspace never zero-filled, or shared by calls that ran at
+                                  the same time), or the routing state ep_notify left there does not belong to
+                                  this is_token_in_rank.  The call's outputs are then not to be trusted. */
 };
 
 /* Problem shape (host struct, read during the call only). */
@@ -132,14 +138,25 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
                       void *workspace, size_t workspace_bytes, int32_t *dev_status, hipStream_t stream);
 
 /*
- * Stages 3+4, dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch;
- * CUDA与DeepEP article 4.1 SrcInfo]
+ * Stages 3+4, dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch (inputs
+ * isTokenInRank, gblChannelPrefixMatrix, recvGblRankPrefixSum); CUDA与DeepEP article 4.1 SrcInfo]
  * The receive region is laid out [dst_rank][channel]: slab r holds the tokens sent to r,
- * channel segments in channel order, tokens ascending inside a segment; so token t's row
- * on rank r is  prefix[r-1] + #{t' < t sent to r}.
+ * channel segments in channel order, tokens ascending inside a segment.  Channel c of rank r
+ * starts at row  prefix[r-1] + gbl_channel_prefix_matrix[r][c-1]  (0 for r = 0, c = 0), so
+ * token t's row on rank r is that start plus #{t' in channel c, t' < t, sent to r}.
  * In:  x [t][h] bf16; topk_idx [t][k] int64; topk_weights [t][k] f32;
- *      recv_gbl_rank_prefix_sum [R] from ep_notify; workspace as filled by ep_notify
- *      for the same is_token_in_rank.
+ *      is_token_in_rank [t][R] uint8 (any non-zero byte counts as 1),
+ *      gbl_channel_prefix_matrix [R][C] and recv_gbl_rank_prefix_sum [R] as ep_notify
+ *      computes them from that is_token_in_rank.
+ *      workspace (nullable):
+ *        NULL   -- the row of every (token, rank) is worked out inside the call from the
+ *                  three routing inputs: a chunk of 64 tokens is placed from its channel's
+ *                  prefix plus a count over at most half a channel.  Needs ceil(t / C) <= 4096
+ *                  (EP_ERR_UNSUPPORTED otherwise: pass the workspace).
+ *        non-NULL -- the workspace ep_notify filled for this is_token_in_rank: the per-token
+ *                  rank masks and per-chunk row offsets it left there are used instead of
+ *                  being worked out again.  The call checks them against is_token_in_rank
+ *                  and the prefix matrix and sets EP_DEV_STALE_WORKSPACE when they differ.
  * Out (recv_capacity rows allocated by the caller):
  *      recv_x            [cap][h] bf16: bitwise copy of x[t]
  *      recv_topk_weights [cap][k] f32:  w[t][j] where slot j's expert lives on the
@@ -148,9 +165,14 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
  *                                       e - r*(E/R) for those slots, else -1
  *      recv_src_info     [cap][2] int32: {my_rank, t} (8-byte aligned)
  *      send_slot         [t][R]   int32: the row of (t, r), -1 where t is not sent to r
- * Rows >= recv_capacity are skipped and flagged (EP_DEV_RECV_OVERFLOW); their send_slot is -1.
+ * Rows >= recv_capacity (or below 0) are skipped and flagged (EP_DEV_RECV_OVERFLOW); their
+ * send_slot is -1.
+ * dev_status (nullable): EP_DEV_RECV_OVERFLOW; EP_DEV_COUNT_MISMATCH when the prefix matrix or
+ * the receive prefix sums disagree with is_token_in_rank (rows are then placed by the prefix
+ * matrix, unchecked); EP_DEV_STALE_WORKSPACE as above.
  */
 ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_idx, const float *topk_weights,
+                        const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
                         int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
@@ -166,7 +188,8 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
  * Every other argument and output is as in ep_dispatch.
  */
 ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_scales, int32_t num_scales,
-                            const int64_t *topk_idx, const float *topk_weights, const int32_t *recv_gbl_rank_prefix_sum,
+                            const int64_t *topk_idx, const float *topk_weights, const uint8_t *is_token_in_rank,
+                            const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
                             const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
                             float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
                             int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
@@ -236,10 +259,11 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
  *   grouped_x [grouped_capacity][h] = x[t] of the entry's row (bf16 when elem_bytes == 2,
  *             1-byte elements when elem_bytes == 1); grouped_x_scales = that token's
  *             x_scales (num_scales per token, nullable when 0); padding rows are zero.
- * No recv_x is written or read.  In: x, x_scales, topk_idx, topk_weights as for
- * ep_dispatch / ep_dispatch_fp8; recv_gbl_rank_prefix_sum and num_recv_tokens_per_expert as
- * ep_notify wrote them; the workspace as ep_notify left it.  Receive rows at or past
- * recv_capacity are dropped as in ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.
+ * No recv_x is written or read.  In: x, x_scales, topk_idx, topk_weights, is_token_in_rank,
+ * gbl_channel_prefix_matrix and recv_gbl_rank_prefix_sum as for ep_dispatch / ep_dispatch_fp8;
+ * num_recv_tokens_per_expert as ep_notify wrote it; the workspace as ep_notify left it (required
+ * when t > 0, checked as in ep_dispatch).  Receive rows at or past recv_capacity are dropped as in
+ * ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.
  * The call also writes the workspace: from 2048 tokens (rows of 1 KiB to 1 MiB, E <= 2048)
  * it keeps each (token, slot)'s grouped position there; what ep_dispatch and ep_combine
  * read from it is not touched.
@@ -251,6 +275,7 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
  */
 ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
+                                const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                                 const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
                                 void *workspace, size_t workspace_bytes, int32_t recv_capacity,
                                 float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,

@@ -190,7 +190,11 @@ int oracle_notify(int32_t T, int32_t E, int32_t R, int32_t C, int32_t expert_ali
  *                          ([mscclpp] the per-(token, rank) gather map the dispatch
  *                          sender fills and combine reads).
  * Rows at or beyond recv_capacity are not written, their send_slot stays -1
- * and ORC_RECV_OVERFLOW is raised.  recv_topk_idx may be NULL. */
+ * and ORC_RECV_OVERFLOW is raised.  recv_topk_idx may be NULL.
+ * The given prefixes are checked against the walk: a channel segment that does
+ * not start where the walk reaches it, a slab that does not end at its receive
+ * prefix, or a last column (inclusive, so the slab's whole count) that differs
+ * raises ORC_COUNT_MISMATCH; the rows still follow the walk. */
 static int orc_dispatch_rows(int32_t T, int64_t row_bytes, int32_t K, int32_t E, int32_t R, int32_t C,
                              int32_t my_rank, int32_t recv_capacity, const uint8_t *x, const float *x_scales,
                              int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
@@ -231,6 +235,8 @@ static int orc_dispatch_rows(int32_t T, int64_t row_bytes, int32_t K, int32_t E,
             }
         }
         if (row != (int64_t)recv_gbl_rank_prefix_sum[r]) status |= ORC_COUNT_MISMATCH;
+        /* the last column is inclusive: it holds the slab's whole count */
+        if (row != slab_begin + gbl_channel_prefix_matrix[(int64_t)r * C + C - 1]) status |= ORC_COUNT_MISMATCH;
     }
     return status;
 }

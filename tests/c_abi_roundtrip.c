@@ -125,8 +125,9 @@ int main(void) {
     int64_t *recv_idx = dev_alloc(sizeof(int64_t) * n * K);
     int32_t *src_info = dev_alloc(8 * (size_t)n), *send_slot = dev_alloc(4 * (size_t)T * R);
     void *combined = dev_alloc((size_t)T * H * 2);
-    CHECK_EP(ep_dispatch(&shape, d_x, d_idx, d_w, recv_gbl, ws, ws_bytes, n, recv_x, recv_w, recv_idx, src_info,
-                         send_slot, status, stream));
+    /* dispatch from the routing inputs alone (no workspace): is_token_in_rank and the prefix sums */
+    CHECK_EP(ep_dispatch(&shape, d_x, d_idx, d_w, in_rank, gbl, recv_gbl, NULL, 0, n, recv_x, recv_w, recv_idx,
+                         src_info, send_slot, status, stream));
     CHECK_EP(ep_combine(&shape, recv_x, recv_w, send_slot, n, combined, NULL, status, stream));
 
     int32_t *h_aligned = malloc(4 * E);

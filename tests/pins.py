@@ -395,6 +395,41 @@ def pin_workload(o, inputs: dict, hidden: int | None = None) -> list[str]:
     return errs
 
 
+def pin_dispatch_prefix_checks(o, inputs: dict) -> list[str]:
+    """Dispatch flags prefixes that disagree with is_token_in_rank: entries of the
+    channel prefix matrix (first, middle and last columns) and receive prefixes are
+    moved by one in turn, and each must raise the count-mismatch bit.  A moved
+    channel prefix must leave the rows as they were (they follow the walk; a receive
+    prefix is where a slab starts, so it does move rows)."""
+    import oracle as _oracle
+
+    wl = inputs["workload"]
+    x = np.ascontiguousarray(inputs["x"][:, :16])
+    idx, w = inputs["topk_idx"], inputs["topk_weights"]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, 1)
+    gbl, recv = note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"]
+    base = o.dispatch(x, idx, w, lay["is_token_in_rank"], gbl, recv, E)
+    errs = [] if base["status"] == 0 else [f"consistent prefixes flagged: {base['status']}"]
+    edits = [("gbl", r, c) for r in (0, R - 1) for c in (0, C // 2, C - 1)] + [("recv", r, 0) for r in (0, R - 1)]
+    for kind, r, c in edits:
+        g2, rv2 = gbl.copy(), recv.copy()
+        if kind == "gbl":
+            g2[r, c] += 1
+        else:
+            rv2[r] += 1
+        d = o.dispatch(x, idx, w, lay["is_token_in_rank"], g2, rv2, E, recv_capacity=int(recv[-1]) + 1)
+        if not d["status"] & _oracle.COUNT_MISMATCH:
+            errs.append(f"{kind}[{r}][{c}] + 1 not flagged")
+        n = int(recv[-1])
+        if kind == "gbl" and not np.array_equal(d["send_slot"], base["send_slot"]) or \
+                kind == "gbl" and not np.array_equal(d["recv_x"][:n], base["recv_x"]):
+            errs.append(f"{kind}[{r}][{c}] + 1 moved the rows")
+    return errs
+
+
 def pin_fp8_and_cached(o, inputs: dict, hidden: int | None = None) -> list[str]:
     """fp8 dispatch moves the fp8 rows and their scales to the rows the bf16
     routing defines; cached dispatch reproduces a full dispatch from its

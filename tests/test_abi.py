@@ -86,9 +86,10 @@ def _call_all(ep, s):
     codes = [
         lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, p, 1 << 30, None, None),
         lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
-        lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None, None),
+        lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None, None),
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
-        lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None, None),
+        lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
+                            None),
         lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, None, None),
         lib.ep_group_by_expert(ctypes.byref(s), p, 2, None, 0, p, p, p, p, 10, 10, p, None, p, p, p, p, None, None),
     ]
@@ -116,10 +117,18 @@ def test_null_and_misaligned_pointers_rejected(ep):
                          None) == ep.EP_ERR_INVALID_ARG  # no workspace
     assert lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 16, None,
                          None) == ep.EP_ERR_INVALID_ARG  # workspace too small
-    assert lib.ep_dispatch(ctypes.byref(s), odd, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), odd, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None,
                            None) == ep.EP_ERR_INVALID_ARG  # x not 16-byte aligned
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, 1 << 30, -1, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, -1, p, p, None, p, p, None,
                            None) == ep.EP_ERR_INVALID_ARG  # negative capacity
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, None, p, p, p, 1 << 30, 10, p, p, None, p, p, None,
+                           None) == ep.EP_ERR_INVALID_ARG  # no is_token_in_rank
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, None, p, p, 1 << 30, 10, p, p, None, p, p, None,
+                           None) == ep.EP_ERR_INVALID_ARG  # no channel prefix matrix
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, None, p, 1 << 30, 10, p, p, None, p, p, None,
+                           None) == ep.EP_ERR_INVALID_ARG  # no receive prefix sums
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 16, 10, p, p, None, p, p, None,
+                           None) == ep.EP_ERR_INVALID_ARG  # workspace given but too small
     assert lib.ep_combine(ctypes.byref(s), p, p, p, 10, odd, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(s), p, p, None, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_get_layout(None, p, p, p, p, p, p, 1 << 30, None, None) == ep.EP_ERR_INVALID_ARG
@@ -131,12 +140,12 @@ def test_fp8_and_cached_argument_checks(ep):
     s = _shape(ep)
     # fp8 rows must be a whole number of 16-byte units
     s12 = _shape(ep, hidden=7160)
-    assert lib.ep_dispatch_fp8(ctypes.byref(s12), p, p, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
-                               None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, None, 4, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
-                               None) == ep.EP_ERR_INVALID_ARG  # scales missing
-    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 2000, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
-                               None) == ep.EP_ERR_UNSUPPORTED
+    assert lib.ep_dispatch_fp8(ctypes.byref(s12), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+                               None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, None, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+                               None, None) == ep.EP_ERR_INVALID_ARG  # scales missing
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 2000, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+                               None, None) == ep.EP_ERR_UNSUPPORTED
     assert lib.ep_dispatch_cached(ctypes.byref(s), p, 3, None, 0, p, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, None, 10, p, None, None,
                                   None) == ep.EP_ERR_INVALID_ARG
@@ -180,10 +189,10 @@ def test_dispatch_grouped_argument_checks(ep):
     odd = ctypes.c_void_p(264)
     s = _shape(ep)
 
-    def grouped(shape=s, x=p, elem=2, xs=None, ns=0, idx=p, w=p, gbl=p, aligned=p, ws=p, wsb=1 << 30, cap=10, rw=p,
-                ridx=p, src=p, slot=p, gcap=10, gx=p, gxs=None, grow=p, gw=p, pos=p, m=p):
-        return lib.ep_dispatch_grouped(ctypes.byref(shape), x, elem, xs, ns, idx, w, gbl, aligned, ws, wsb, cap, rw,
-                                       ridx, src, slot, gcap, gx, gxs, grow, gw, pos, m, None, None)
+    def grouped(shape=s, x=p, elem=2, xs=None, ns=0, idx=p, w=p, in_rank=p, cpm=p, gbl=p, aligned=p, ws=p,
+                wsb=1 << 30, cap=10, rw=p, ridx=p, src=p, slot=p, gcap=10, gx=p, gxs=None, grow=p, gw=p, pos=p, m=p):
+        return lib.ep_dispatch_grouped(ctypes.byref(shape), x, elem, xs, ns, idx, w, in_rank, cpm, gbl, aligned, ws,
+                                       wsb, cap, rw, ridx, src, slot, gcap, gx, gxs, grow, gw, pos, m, None, None)
 
     assert grouped(elem=3) == ep.EP_ERR_INVALID_ARG
     assert grouped(shape=_shape(ep, hidden=7160), elem=1) == ep.EP_ERR_INVALID_ARG  # not whole 16-byte units
@@ -205,6 +214,9 @@ def test_dispatch_grouped_argument_checks(ep):
     assert grouped(w=None) == ep.EP_ERR_INVALID_ARG
     assert grouped(slot=None) == ep.EP_ERR_INVALID_ARG
     assert grouped(wsb=10) == ep.EP_ERR_INVALID_ARG  # short workspace
+    assert grouped(ws=None, wsb=0) == ep.EP_ERR_INVALID_ARG  # the grouped dispatch needs its workspace
+    assert grouped(in_rank=None) == ep.EP_ERR_INVALID_ARG
+    assert grouped(cpm=None) == ep.EP_ERR_INVALID_ARG
     assert grouped(ns=4, gxs=p) == ep.EP_ERR_INVALID_ARG  # x scales missing
     assert grouped(ns=4, xs=p) == ep.EP_ERR_INVALID_ARG  # grouped scales missing
     assert grouped(ns=2000, xs=p, gxs=p) == ep.EP_ERR_UNSUPPORTED
@@ -216,6 +228,23 @@ def test_empty_dispatch_and_combine_enqueue_nothing(ep):
     # t = 0: nothing to move; the calls succeed without touching any pointer
     lib = ep.load()
     s = _shape(ep, num_tokens=0)
-    assert lib.ep_dispatch(ctypes.byref(s), None, None, None, None, None, 0, 0, None, None, None, None, None,
-                           None, None) == ep.EP_OK
+    assert lib.ep_dispatch(ctypes.byref(s), None, None, None, None, None, None, None, 0, 0, None, None, None, None,
+                           None, None, None) == ep.EP_OK
     assert lib.ep_combine(ctypes.byref(s), None, None, None, 0, None, None, None, None) == ep.EP_OK
+
+
+def test_dispatch_without_workspace_limits(ep):
+    # without a workspace the routing is worked out inside the call, counting at most
+    # half a channel per chunk: channels of up to 4096 tokens are accepted, longer
+    # ones need the workspace notify filled (refused before any launch otherwise)
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+
+    def dispatch(shape, ws, wsb):
+        return lib.ep_dispatch(ctypes.byref(shape), p, p, p, p, p, p, ws, wsb, 10, p, p, None, p, p, None, None)
+
+    long_channels = _shape(ep, num_tokens=100000, num_channels=24)  # 4167 tokens per channel
+    assert dispatch(long_channels, None, 0) == ep.EP_ERR_UNSUPPORTED
+    fp8 = lib.ep_dispatch_fp8(ctypes.byref(long_channels), p, p, 4, p, p, p, p, p, None, 0, 10, p, p, p, None, p, p,
+                              None, None)
+    assert fp8 == ep.EP_ERR_UNSUPPORTED

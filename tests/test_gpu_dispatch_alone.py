@@ -1,0 +1,229 @@
+"""Dispatch as a stage of its own, driven by the oracle's layout and notify outputs.
+
+The oracle computes is_token_in_rank, the channel prefix matrix and the receive
+prefix sums on the CPU; those are uploaded and ep_dispatch (or ep_dispatch_fp8)
+runs alone, without a workspace, so the rows are placed from the routing inputs
+the pages' dispatch takes.  Every output is compared with oracle_dispatch bit
+for bit: the five workloads at full size (the benchmark's launch configuration)
+and ragged shapes on either side of the pull form's threshold, with channels
+from a few tokens to 4096.  The workspace path is checked for what it must
+catch: a workspace notify filled for other routing, and prefix matrices or
+receive prefixes that disagree with is_token_in_rank."""
+import numpy as np
+import pytest
+import torch
+
+import gpu_harness as H
+import oracle
+from combine_ep_get_02_amd import ep
+from combine_ep_get_02_amd.inputs import WORKLOADS, fp8_rows, generate
+
+pytestmark = pytest.mark.gpu
+
+
+def _routing(orc, idx, E, R, C, align=1):
+    lay = orc.layout(idx, E, R)
+    note = orc.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                      lay["num_tokens_per_expert"], C, align)
+    return lay, note
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=None, my_rank=0, fp8=None):
+    """ep_dispatch (bf16 x) or ep_dispatch_fp8 (fp8=(rows, scales)) from uploaded routing
+    inputs into poisoned buffers; returns the outputs as numpy arrays and the status."""
+    T, K = idx.shape
+    Hd = x.shape[1] if fp8 is None else fp8[0].shape[1]
+    shape = ep.make_shape(T, x.shape[1], K, E, R, C, my_rank)
+    c1 = max(cap, 1)
+    rw = torch.full((c1, K), -3.0, dtype=torch.float32, device="cuda")
+    ri = torch.full((c1, K), -777, dtype=torch.int64, device="cuda")
+    si = torch.full((c1, 2), -777, dtype=torch.int32, device="cuda")
+    ss = torch.full((T, R), -777, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_in, d_gbl, d_recv = _dev(in_rank), _dev(gbl.astype(np.int32)), _dev(recv_gbl.astype(np.int32))
+    didx, dw = _dev(idx.astype(np.int64)), _dev(w.astype(np.float32))
+    out = {}
+    if fp8 is None:
+        rx = torch.full((c1, Hd), -1, dtype=torch.int16, device="cuda")
+        ep.ep_dispatch(shape, H.to_dev_bf16(x), didx, dw, d_in, d_gbl, d_recv, workspace, cap, rx, rw, ri, si, ss,
+                       st)
+    else:
+        x8, sc = fp8
+        NS = sc.shape[1]
+        rx = torch.full((c1, Hd), 0xAB, dtype=torch.uint8, device="cuda")
+        rs = torch.full((c1, max(NS, 1)), -2.0, dtype=torch.float32, device="cuda")
+        ep.ep_dispatch_fp8(shape, _dev(x8), _dev(sc) if NS else None, NS, didx, dw, d_in, d_gbl, d_recv, workspace,
+                           cap, rx, rs if NS else None, rw, ri, si, ss, st)
+    torch.cuda.synchronize()
+    rows = min(int(recv_gbl[-1]) if len(recv_gbl) else 0, cap)
+    out["send_slot"] = ss.cpu().numpy()
+    out["recv_x"] = rx[:rows].cpu().numpy().view(np.uint16 if fp8 is None else np.uint8)
+    out["recv_topk_weights"] = rw[:rows].cpu().numpy()
+    out["recv_topk_idx"] = ri[:rows].cpu().numpy()
+    out["recv_src_info"] = si[:rows].cpu().numpy()
+    if fp8 is not None and fp8[1].shape[1]:
+        out["recv_x_scales"] = rs[:rows].cpu().numpy()
+    out["status"] = int(st.item())
+    return out
+
+
+def _reference(orc, x, idx, w, E, in_rank, gbl, recv_gbl, cap, my_rank=0, fp8=None):
+    if fp8 is None:
+        d = orc.dispatch(x, idx, w, in_rank, gbl, recv_gbl, E, my_rank, recv_capacity=cap)
+    else:
+        d = orc.dispatch_fp8(fp8[0], fp8[1], idx, w, in_rank, gbl, recv_gbl, E, my_rank, recv_capacity=cap)
+    rows = min(int(recv_gbl[-1]) if len(recv_gbl) else 0, cap)
+    ref = {k: d[k][:rows] for k in ("recv_x", "recv_topk_weights", "recv_topk_idx", "recv_src_info")}
+    if fp8 is not None and fp8[1].shape[1]:
+        ref["recv_x_scales"] = d["recv_x_scales"][:rows]
+    ref["send_slot"] = d["send_slot"]
+    ref["status"] = d["status"]
+    return ref
+
+
+def _differences(gpu, ref):
+    bad = []
+    for k, r in ref.items():
+        if k == "status":
+            continue
+        g = np.asarray(gpu[k])
+        r = np.asarray(r)
+        if g.shape != r.shape or not np.array_equal(g.view(np.uint8), r.view(np.uint8)):
+            bad.append(k)
+    return bad
+
+
+@pytest.mark.parametrize("name", list(WORKLOADS))
+def test_dispatch_alone_workloads(orc, name):
+    print(f"[dispatch alone] workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    lay, note = _routing(orc, idx, wl.experts, wl.ranks, wl.channels)
+    cap = note["num_recv_tokens"]
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], cap)
+    gpu = _dispatch_alone(x, idx, w, wl.experts, wl.ranks, wl.channels, *args)
+    ref = _reference(orc, x, idx, w, wl.experts, *args)
+    assert _differences(gpu, ref) == []
+    assert gpu["status"] == 0 == ref["status"]
+
+
+# (T, R, E, K, C, hidden, mask_frac, dup, capacity delta): ragged 64-token chunks and
+# 128-token groups, channels of 1 to 4096 tokens, both dispatch forms
+RAGGED = {
+    "pull_ragged_groups_c7": (2113, 64, 256, 8, 7, 7168, 0.0, False, 0),        # 302-token channels
+    "pull_long_channels_c1": (4000, 16, 64, 6, 1, 512 * 8, 0.1, False, 0),       # one 4000-token channel
+    "pull_two_channels_r24": (2500, 24, 48, 5, 2, 1024, 0.2, True, -300),       # 1250-token channels, short capacity
+    "pull_channel_per_token": (2050, 8, 16, 2, 4096, 512, 0.0, False, 0),       # empty channels past the tokens
+    "pull_r1": (2048, 1, 4, 2, 3, 1024, 0.0, False, 0),
+    "push_ragged_r64_k32": (1000, 64, 128, 32, 9, 1024, 0.3, True, 0),
+    "push_narrow_rows_long_channels": (3000, 32, 256, 8, 1, 64, 0.0, False, 0),  # 3000-token channel, 128 B rows
+    "push_small_channels": (333, 16, 64, 6, 50, 800, 0.0, False, -7),
+    "push_r5": (200, 5, 10, 3, 4, 256, 0.0, False, 0),
+}
+
+
+@pytest.mark.parametrize("name", sorted(RAGGED))
+def test_dispatch_alone_ragged(orc, name):
+    T, R, E, K, C, Hd, mask, dup, dcap = RAGGED[name]
+    print(f"[dispatch alone] ragged={name}", flush=True)
+    rng = np.random.default_rng(len(name) * 31 + T)
+    idx = np.stack([rng.choice(E, K, replace=dup) for _ in range(T)]).astype(np.int64)
+    if mask:
+        idx.reshape(-1)[rng.choice(T * K, int(mask * T * K), replace=False)] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, Hd)
+    lay, note = _routing(orc, idx, E, R, C)
+    cap = note["num_recv_tokens"] + dcap
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], cap)
+    gpu = _dispatch_alone(x, idx, w, E, R, C, *args, my_rank=R - 1)
+    ref = _reference(orc, x, idx, w, E, *args, my_rank=R - 1)
+    assert _differences(gpu, ref) == []
+    assert gpu["status"] == ref["status"]
+    assert (gpu["status"] != 0) == (dcap < 0)
+
+
+@pytest.mark.parametrize("name", ["prefill", "sweep"])
+def test_fp8_dispatch_alone(orc, name):
+    print(f"[dispatch alone] fp8 workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    x8, sc = fp8_rows(x)
+    lay, note = _routing(orc, idx, wl.experts, wl.ranks, wl.channels)
+    cap = note["num_recv_tokens"]
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], cap)
+    gpu = _dispatch_alone(x, idx, w, wl.experts, wl.ranks, wl.channels, *args, fp8=(x8, sc))
+    ref = _reference(orc, x, idx, w, wl.experts, *args, fp8=(x8, sc))
+    assert _differences(gpu, ref) == []
+    assert gpu["status"] == 0
+
+
+def _notified_workspace(idx, E, R, C, Hd):
+    """A workspace that ep_get_layout and ep_notify filled on the GPU for routing idx."""
+    T, K = idx.shape
+    b = ep.allocate(ep.make_shape(T, Hd, K, E, R, C), 0)
+    ep.run_layout(b, _dev(idx.astype(np.int64)))
+    ep.run_notify(b)
+    torch.cuda.synchronize()
+    return b.workspace
+
+
+@pytest.mark.parametrize("T,Hd", [(2200, 7168), (500, 7168), (3000, 64)])
+def test_stale_workspace_is_flagged(orc, T, Hd):
+    # notify filled the workspace for routing A; dispatch is given routing B with it
+    print(f"[dispatch alone] stale workspace T={T} h={Hd}", flush=True)
+    R, E, K, C = 32, 128, 6, 12
+    rng = np.random.default_rng(T)
+    idx_a = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    idx_b = idx_a.copy()
+    idx_b[T // 2] = rng.choice(E, K, replace=False)  # one token routed elsewhere
+    idx_b[T // 2, 0] = (idx_a[T // 2, 0] + E // 2) % E
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, Hd)
+    ws = _notified_workspace(idx_a, E, R, C, Hd)
+    lay, note = _routing(orc, idx_b, E, R, C)
+    cap = note["num_recv_tokens"] + 64
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], cap)
+    gpu = _dispatch_alone(x, idx_b, w, E, R, C, *args, workspace=ws)
+    assert gpu["status"] & ep.EP_DEV_STALE_WORKSPACE
+    # the same workspace with its own routing: exact and clean
+    lay_a, note_a = _routing(orc, idx_a, E, R, C)
+    args_a = (lay_a["is_token_in_rank"], note_a["gbl_channel_prefix_matrix"], note_a["recv_gbl_rank_prefix_sum"],
+              note_a["num_recv_tokens"])
+    gpu_a = _dispatch_alone(x, idx_a, w, E, R, C, *args_a, workspace=ws)
+    ref_a = _reference(orc, x, idx_a, w, E, *args_a)
+    assert _differences(gpu_a, ref_a) == [] and gpu_a["status"] == 0
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("what", ["gbl_entry", "recv_prefix", "last_channel"])
+@pytest.mark.parametrize("T,Hd", [(2300, 7168), (700, 512)])
+def test_inconsistent_prefixes_are_flagged(orc, use_ws, what, T, Hd):
+    # a prefix the rows depend on disagrees with is_token_in_rank: the oracle flags it,
+    # and so must the GPU (rows are then placed by the given prefixes, not compared)
+    print(f"[dispatch alone] inconsistent {what} ws={use_ws} T={T}", flush=True)
+    R, E, K, C = 16, 64, 4, 10
+    rng = np.random.default_rng(T + len(what))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, Hd)
+    lay, note = _routing(orc, idx, E, R, C)
+    gbl = note["gbl_channel_prefix_matrix"].copy()
+    recv = note["recv_gbl_rank_prefix_sum"].copy()
+    if what == "gbl_entry":
+        gbl[3, 4] += 1
+    elif what == "recv_prefix":
+        recv[5:] += 2
+    else:
+        gbl[7, C - 1] -= 1
+    cap = note["num_recv_tokens"] + 64
+    ws = _notified_workspace(idx, E, R, C, Hd) if use_ws else None
+    gpu = _dispatch_alone(x, idx, w, E, R, C, lay["is_token_in_rank"], gbl, recv, cap, workspace=ws)
+    ref = _reference(orc, x, idx, w, E, lay["is_token_in_rank"], gbl, recv, cap)
+    assert ref["status"] & oracle.COUNT_MISMATCH
+    assert gpu["status"] & ep.EP_DEV_COUNT_MISMATCH

@@ -203,7 +203,8 @@ def _fp8_case(x, idx, w, E, R, C, num_scales_block=128, capacity=None):
     si = torch.full((max(cap, 1), 2), -777, dtype=torch.int32, device="cuda")
     ss = torch.full((T, R), -777, dtype=torch.int32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
-    ep.ep_dispatch_fp8(shape, dx, dsc, NS, didx, dw, b.recv_gbl, b.workspace, cap, rx, rs if NS else None, rw, ri, si,
+    ep.ep_dispatch_fp8(shape, dx, dsc, NS, didx, dw, b.in_rank, b.gbl, b.recv_gbl, b.workspace, cap, rx,
+                       rs if NS else None, rw, ri, si,
                        ss, st)
     rows = min(n, cap)
     # cached mode: same rows again, into fresh buffers, from the recorded send_slot
@@ -399,7 +400,8 @@ def _group_case(x, idx, w, E, R, C, align, fp8=False, shrink=False, cap_delta=0,
     if fp8:
         rx = torch.zeros((max(rows, 1), Hd), dtype=torch.uint8, device="cuda")
         rs = torch.zeros((max(rows, 1), NS), dtype=torch.float32, device="cuda")
-        ep.ep_dispatch_fp8(shape, torch.from_numpy(xs).cuda(), torch.from_numpy(sc).cuda(), NS, didx, dw, b.recv_gbl,
+        ep.ep_dispatch_fp8(shape, torch.from_numpy(xs).cuda(), torch.from_numpy(sc).cuda(), NS, didx, dw, b.in_rank,
+                           b.gbl, b.recv_gbl,
                            b.workspace, rows, rx, rs, b.recv_w, b.recv_idx, b.src_info, b.send_slot, b.dev_status)
     else:
         rx = b.recv_x
@@ -568,7 +570,8 @@ def test_every_call_without_a_status_word():
         ep.ep_get_layout(shape, didx, b2.per_rank, b2.per_node, b2.per_expert, b2.in_rank, b2.workspace, st)
         ep.ep_notify(shape, b2.in_rank, b2.per_rank, b2.per_node, b2.per_expert, b2.gbl, b2.rdma, b2.recv_gbl,
                      b2.recv_rdma, b2.recv_per_expert, b2.num_recv, b2.workspace, False, st)
-        ep.ep_dispatch(shape, dx, didx, dw, b2.recv_gbl, b2.workspace, cap, b2.recv_x, b2.recv_w, b2.recv_idx,
+        ep.ep_dispatch(shape, dx, didx, dw, b2.in_rank, b2.gbl, b2.recv_gbl, b2.workspace, cap, b2.recv_x, b2.recv_w,
+                       b2.recv_idx,
                        b2.src_info, b2.send_slot, st)
         ep.ep_combine(shape, b2.recv_x, b2.recv_w, b2.send_slot, cap, b2.combined_x, b2.combined_w, st)
         m = int(b2.recv_per_expert.sum().item())
@@ -682,7 +685,8 @@ def _dispatch_grouped_case(x, idx, w, E, R, C, align, fp8=False, recv_delta=0, g
     m = torch.full((1,), -777, dtype=torch.int32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     dx = torch.from_numpy(np.ascontiguousarray(xs).view(np.int16 if not fp8 else np.uint8)).cuda()
-    ep.ep_dispatch_grouped(shape, dx, elem, torch.from_numpy(sc).cuda() if NS else None, NS, didx, dw, b.recv_gbl,
+    ep.ep_dispatch_grouped(shape, dx, elem, torch.from_numpy(sc).cuda() if NS else None, NS, didx, dw, b.in_rank,
+                           b.gbl, b.recv_gbl,
                            b.recv_per_expert, b.workspace, rcap, rw, ri, si, ss, gcap, gx, gs if NS else None, grow, gw,
                            pos, m, st)
     torch.cuda.synchronize()

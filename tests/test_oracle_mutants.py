@@ -61,6 +61,9 @@ MUTANTS = {
                                 "memcpy(recv_x + s * row_bytes, x + (t > 0 ? t - 1 : t) * row_bytes, (size_t)row_bytes);"),
     "cached_bad_slot_not_flagged": ("                status |= ORC_BAD_SEND_SLOT;\n                continue;\n            }\n            memcpy(recv_x",
                                     "                continue;\n            }\n            memcpy(recv_x"),
+    "last_column_unchecked": ("if (row != slab_begin + gbl_channel_prefix_matrix[(int64_t)r * C + C - 1]) status |= ORC_COUNT_MISMATCH;",
+                              ";"),
+    "segment_start_unchecked": ("if (row != seg_begin) status |= ORC_COUNT_MISMATCH;", ";"),
     "combine_f64_keeps_last_rank": ("o[i] += W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);",
                                     "o[i] = W * (double)orc_bf16_to_f32(y[(int64_t)s * H + i]);"),
     "combine_f64_W_keeps_last_term": ("W += (double)recv_topk_weights[(int64_t)s * K + j];",
@@ -89,6 +92,7 @@ CHILD = textwrap.dedent("""
               lambda: pins.pin_fp8_and_cached(o, inputs.generate("tiny")),
               lambda: pins.pin_golden_grouping(o), lambda: pins.pin_group_by_expert(o, inputs.generate("tiny"), 4),
               lambda: pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32),
+              lambda: pins.pin_dispatch_prefix_checks(o, inputs.generate("tiny")),
               lambda: pins.pin_bruteforce(o)]
     errs = []
     for check in checks:  # in order, stopping at the first pin that fails

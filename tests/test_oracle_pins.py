@@ -139,3 +139,8 @@ def test_golden_grouping(orc):
                                         ("large", 8)])
 def test_group_by_expert(orc, workload_inputs, name, align):
     assert pins.pin_group_by_expert(orc, workload_inputs(name), align, hidden=None if name == "tiny" else 32) == []
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep"])
+def test_dispatch_flags_inconsistent_prefixes(orc, workload_inputs, name):
+    assert pins.pin_dispatch_prefix_checks(orc, workload_inputs(name)) == []
