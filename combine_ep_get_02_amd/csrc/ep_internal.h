@@ -23,7 +23,9 @@ __host__ __device__ inline int64_t num_chunks(int64_t T) { return (T + kChunk - 
 
 // Workspace shared by the four stages.  All offsets 256-byte aligned.
 //   tickets   uint32 [64]           completion counters of the multi-block layout and
-//                                   notify kernels; zero between calls
+//                                   notify kernels (work done so far), layout's followed
+//                                   by the counts its finished blocks report (checked by
+//                                   the last block); zero between calls
 //   acc       int32  [R+nodes+E]    layout's running counts; zero between calls
 //   mask      uint64 [t]            bit r set when token t goes to rank r (notify -> dispatch)
 //   rank_off  int32  [Q+1][R]       per-chunk token counts, scanned in place into
@@ -39,8 +41,9 @@ __host__ __device__ inline int64_t num_chunks(int64_t T) { return (T + kChunk - 
 struct Workspace {
     size_t tickets, acc, mask, rank_off, node_off, rank_part, node_part, tok_pos, total;
 };
-constexpr int kTicketLayout = 0;
-constexpr int kTicketNotify = 16;  // separate 64-byte lines
+// uint32 word offsets of the tickets (each a 64-bit ticket, see elect_completing_block)
+constexpr int kTicketLayout = 0;   // counts tokens; words 2..4: valid slots, (token, rank) and (token, node) pairs
+constexpr int kTicketNotify = 16;  // counts chunks (a separate 64-byte line)
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -235,19 +238,41 @@ __device__ __forceinline__ void flag(int32_t *dev_status, int bits) {
     if (dev_status != nullptr && bits != 0) atomicOr(dev_status, bits);
 }
 
-// Last-block election for a multi-block kernel: every thread has finished its
-// global writes; after this returns true in exactly one block (the last to get
-// here), that block sees every other block's writes.  The ticket is reset for
-// the next call by the elected block.
-__device__ __forceinline__ bool elect_last_block(uint32_t *ticket) {
+// Sum over the 64 lanes of a wave (wrapping like the uint32 counters it feeds).
+__device__ __forceinline__ int wave_sum(int v) { return readlane32(wave_inclusive_scan(v), kWave - 1); }
+
+// Completion ticket of a multi-block kernel: a 64-bit word in the workspace,
+// the count of work units done so far in the low half and an epoch in the high
+// half.  Thread 0 of every block reads the epoch when the block starts
+// (ticket_epoch) and hands it to elect_completing_block once the block's global
+// writes are done.
+__device__ __forceinline__ uint32_t ticket_epoch(const uint64_t *ticket) {
+    return (uint32_t)(__hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
+}
+
+// Every block adds its units of work (`mine`: tokens, chunks) to the ticket
+// with a device-scope release; the block that brings the count to `total` is
+// elected, sees every other block's writes from then on, and takes the count
+// back to zero while moving the epoch on.  In a clean call no block arrives
+// after that.  A ticket whose count was not zero on entry (a workspace never
+// cleared, or shared by calls running at the same time) shows as a count past
+// `total`, or as a block arriving after the election (the epoch moved since it
+// started); such a block flags EP_DEV_STALE_WORKSPACE.  (Thread 0 alone holds
+// epoch0; total < 2^32.)
+__device__ __forceinline__ bool elect_completing_block(uint64_t *ticket, uint32_t epoch0, uint32_t mine,
+                                                       uint32_t total, int32_t *dev_status) {
     __shared__ bool last;
     __syncthreads();  // every wave's stores of this block have completed
     if (threadIdx.x == 0) {
         __threadfence();  // one device-scope release for the whole block
-        const uint32_t prev = atomicAdd(ticket, 1u);
-        last = prev == gridDim.x - 1;
+        const uint64_t prev = atomicAdd((unsigned long long *)ticket, (unsigned long long)mine);
+        const uint64_t count = (uint32_t)prev, done = count + mine;
+        const bool same_epoch = (uint32_t)(prev >> 32) == epoch0;
+        last = same_epoch && count <= total && done >= total;
+        if (!same_epoch || done > total) flag(dev_status, EP_DEV_STALE_WORKSPACE);
         if (last) {
-            atomicExch(ticket, 0u);
+            // count - done (zero unless blocks arrived after this one), epoch + 1
+            atomicAdd((unsigned long long *)ticket, (unsigned long long)((1ull << 32) - done));
             __threadfence();  // acquire: other blocks' writes are visible from here on
         }
     }

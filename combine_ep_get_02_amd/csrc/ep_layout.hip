@@ -19,6 +19,11 @@
 // outputs and zeroes them for the next call, so no separate zero-fill launch
 // is needed; a single block (up to 256 tokens) writes its LDS counts out
 // directly.  Integer atomics commute: the result is deterministic.
+// The completion ticket counts tokens, so a ticket that was not zero shows as
+// a count past t and is flagged (see elect_completing_block); beside it every
+// block reports its valid slots and (token, rank) / (token, node) pairs, and
+// the last block checks that each class of running counts adds up to what was
+// reported, so running counts that were not zero are flagged as well.
 #include "ep_internal.h"
 
 namespace ep {
@@ -37,7 +42,8 @@ struct LayoutParams {
     int32_t *per_rank, *per_node, *per_expert;
     uint8_t *in_rank;
     int32_t *acc;  // [R + nodes + E] running counts, zero between calls
-    uint32_t *ticket;
+    uint64_t *ticket;      // completion ticket (tokens)
+    uint32_t *report;      // valid slots, (token, rank) and (token, node) pairs the finished blocks report
     int32_t *dev_status;
     int64_t T;
     int K, E, R, nodes, store_unit;
@@ -47,15 +53,19 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     __shared__ int32_t s_rank[kMaxRanks];
     __shared__ int32_t s_node[kMaxRanks / kRanksPerNode];
     __shared__ uint64_t s_mask[kLayoutThreads];
+    __shared__ uint32_t s_chk[3];  // the block's valid slots, (token, rank) and (token, node) pairs
     extern __shared__ int32_t s_expert[];  // E entries when E <= kMaxLdsExperts
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int R = p.R, E = p.E, K = p.K, nodes = p.nodes;
     const bool lds_experts = E <= kMaxLdsExperts;
+    const bool single = gridDim.x == 1 && lds_experts;  // one block: no ticket, no running counts
+    const uint32_t epoch0 = (!single && tid == 0) ? ticket_epoch(p.ticket) : 0u;
     int32_t *acc_rank = p.acc, *acc_node = p.acc + R, *acc_expert = p.acc + R + nodes;
     for (int i = tid; i < R; i += kLayoutThreads) s_rank[i] = 0;
     for (int i = tid; i < nodes; i += kLayoutThreads) s_node[i] = 0;
+    if (tid < 3) s_chk[tid] = 0;
     if (lds_experts)
         for (int i = tid; i < E; i += kLayoutThreads) s_expert[i] = 0;
     __syncthreads();
@@ -64,7 +74,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     const int64_t t = t0 + tid;
     const int experts_per_rank = E / R;
     uint64_t mask = 0;
-    int bad = 0;
+    int bad = 0, slots = 0;
     if (t < p.T) {
         const int64_t *row = p.topk_idx + t * K;
         // slots in batches of 8: a batch's loads are all in flight before any is used
@@ -81,6 +91,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
                     continue;
                 }
                 const int ei = (int)e;
+                ++slots;
                 if (lds_experts)
                     atomicAdd(&s_expert[ei], 1);
                 else
@@ -103,6 +114,15 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     }
     if (lane < nodes && node_cnt != 0) atomicAdd(&s_node[lane], node_cnt);
     if (ballot64(bad != 0) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_TOPK_IDX);
+    {
+        const int w_slots = wave_sum(slots), w_ranks = wave_sum(__popcll(mask));
+        const int w_nodes = wave_sum(lane < nodes ? node_cnt : 0);
+        if (lane == 0) {
+            atomicAdd(&s_chk[0], (uint32_t)w_slots);
+            atomicAdd(&s_chk[1], (uint32_t)w_ranks);
+            atomicAdd(&s_chk[2], (uint32_t)w_nodes);
+        }
+    }
     __syncthreads();
 
     // is_token_in_rank rows of this block: one contiguous range of nt*R bytes
@@ -135,7 +155,7 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
         }
     }
 
-    if (gridDim.x == 1 && lds_experts) {
+    if (single) {
         // a single block (t <= 256): its counts are the totals, and the running
         // counters are not touched
         for (int i = tid; i < R; i += kLayoutThreads) p.per_rank[i] = s_rank[i];
@@ -152,11 +172,21 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     if (lds_experts)
         for (int i = tid; i < E; i += kLayoutThreads)
             if (s_expert[i] != 0) atomicAdd(&acc_expert[i], s_expert[i]);
+    // what this block reports beside its ticket (ordered before it by the election's fence)
+    if (tid == 0) {
+        atomicAdd(&p.report[0], s_chk[0]);
+        atomicAdd(&p.report[1], s_chk[1]);
+        atomicAdd(&p.report[2], s_chk[2]);
+    }
 
-    if (!elect_last_block(p.ticket)) return;
+    if (!elect_completing_block(p.ticket, epoch0, (uint32_t)nt, (uint32_t)p.T, p.dev_status)) return;
     // last block: publish the totals and leave the counters at zero, four
-    // counters per thread in flight at a time
+    // counters per thread in flight at a time; each class of counts is summed
+    // for the check against the blocks' reports
+    __shared__ uint32_t s_sum[3];
+    if (tid < 3) s_sum[tid] = 0;
     const int n = R + nodes + E;
+    uint32_t sum_e = 0, sum_r = 0, sum_n = 0;
     for (int i0 = tid; i0 < n; i0 += 4 * kLayoutThreads) {
         int32_t v[4];
 #pragma unroll
@@ -168,13 +198,31 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
         for (int u = 0; u < 4; ++u) {
             const int i = i0 + u * kLayoutThreads;
             if (i >= n) continue;
-            if (i < R)
+            if (i < R) {
                 p.per_rank[i] = v[u];
-            else if (i < R + nodes)
+                sum_r += (uint32_t)v[u];
+            } else if (i < R + nodes) {
                 p.per_node[i - R] = v[u];
-            else
+                sum_n += (uint32_t)v[u];
+            } else {
                 p.per_expert[i - R - nodes] = v[u];
+                sum_e += (uint32_t)v[u];
+            }
         }
+    }
+    const int w_e = wave_sum((int)sum_e), w_r = wave_sum((int)sum_r), w_n = wave_sum((int)sum_n);
+    __syncthreads();  // s_sum cleared before any wave adds to it
+    if (lane == 0) {
+        atomicAdd(&s_sum[0], (uint32_t)w_e);
+        atomicAdd(&s_sum[1], (uint32_t)w_r);
+        atomicAdd(&s_sum[2], (uint32_t)w_n);
+    }
+    __syncthreads();
+    if (tid == 0) {
+        const uint32_t slots_all = atomicExch(&p.report[0], 0u), ranks_all = atomicExch(&p.report[1], 0u);
+        const uint32_t nodes_all = atomicExch(&p.report[2], 0u);
+        if (slots_all != s_sum[0] || ranks_all != s_sum[1] || nodes_all != s_sum[2])
+            flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
     }
 }
 
@@ -190,7 +238,8 @@ hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *
     p.per_expert = per_expert;
     p.in_rank = in_rank;
     p.acc = reinterpret_cast<int32_t *>(ws + w.acc);
-    p.ticket = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketLayout;
+    p.ticket = reinterpret_cast<uint64_t *>(reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketLayout);
+    p.report = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketLayout + 2;
     p.dev_status = dev_status;
     p.T = s.num_tokens;
     p.K = s.num_topk;

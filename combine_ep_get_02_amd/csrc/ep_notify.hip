@@ -43,7 +43,7 @@ struct NotifyParams {
     int32_t *gbl, *rdma, *recv_gbl, *recv_rdma, *recv_per_expert, *num_recv;
     uint64_t *mask;
     int32_t *rank_off, *node_off, *rank_part, *node_part;
-    uint32_t *ticket;
+    uint64_t *ticket;  // completion ticket (chunks)
     int32_t *dev_status;
     int64_t T, Tc;
     int R, C, E, nodes, align, load_unit;
@@ -290,16 +290,22 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
     const int wave = tid >> 6;
     const int64_t Q = num_chunks(p.T);
 
+    const uint32_t epoch0 = (gridDim.x > 1 && tid == 0) ? ticket_epoch(p.ticket) : 0u;
     const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
     if (q < Q) count_chunk(p, q, lane);
 
     // a single block (up to 1024 tokens) finishes once its own waves are done:
     // a workgroup barrier (with its workgroup-scope fences) makes their stores
-    // visible, and no ticket is taken
-    if (gridDim.x == 1)
+    // visible, and no ticket is taken.  Otherwise the ticket counts chunks, and
+    // the block that completes them scans (a ticket that was not zero is flagged,
+    // see elect_completing_block).
+    if (gridDim.x == 1) {
         __syncthreads();
-    else if (!elect_last_block(p.ticket))
-        return;
+    } else {
+        const int64_t left = Q - (int64_t)blockIdx.x * kNotifyWaves;
+        const uint32_t mine = (uint32_t)(left < kNotifyWaves ? left : kNotifyWaves);
+        if (!elect_completing_block(p.ticket, epoch0, mine, (uint32_t)Q, p.dev_status)) return;
+    }
     const int64_t NC = p.R + p.nodes;
     if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
         finish_in_lds(p, tid, lane, wave);
@@ -330,7 +336,7 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
     p.node_off = reinterpret_cast<int32_t *>(ws + w.node_off);
     p.rank_part = reinterpret_cast<int32_t *>(ws + w.rank_part);
     p.node_part = reinterpret_cast<int32_t *>(ws + w.node_part);
-    p.ticket = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketNotify;
+    p.ticket = reinterpret_cast<uint64_t *>(reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketNotify);
     p.dev_status = dev_status;
     p.T = s.num_tokens;
     p.C = s.num_channels;

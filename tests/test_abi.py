@@ -248,3 +248,11 @@ def test_dispatch_without_workspace_limits(ep):
     fp8 = lib.ep_dispatch_fp8(ctypes.byref(long_channels), p, p, 4, p, p, p, p, p, None, 0, 10, p, p, p, None, p, p,
                               None, None)
     assert fp8 == ep.EP_ERR_UNSUPPORTED
+
+
+def test_device_status_bits_agree_with_the_header(ep):
+    # the binding's EP_DEV_* values are the header's (EP_DEV_STALE_WORKSPACE among them)
+    text = open(HEADER).read()
+    bits = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"\b(EP_DEV_[A-Z_]+)\s*=\s*(\d+)", text))
+    assert bits == {name: getattr(ep, name) for name in bits}
+    assert bits["EP_DEV_STALE_WORKSPACE"] == 16 and len(set(bits.values())) == len(bits) == 5
