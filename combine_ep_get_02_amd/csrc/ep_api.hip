@@ -131,6 +131,24 @@ ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t 
                                   dev_status, stream));
 }
 
+ep_status_t ep_get_layout_noalloc(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                                  int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (topk_idx == nullptr || is_token_in_rank == nullptr)) return EP_ERR_INVALID_ARG;
+    if (s->num_experts > kNoallocMaxExperts) return EP_ERR_UNSUPPORTED;
+    // the stream must belong to the current device, whose scratch the call uses
+    int device = -1, stream_device = -1;
+    if (hipGetDevice(&device) != hipSuccess || hipStreamGetDevice(stream, &stream_device) != hipSuccess)
+        return EP_ERR_HIP;
+    if (device != stream_device) return EP_ERR_INVALID_ARG;
+    return from_hip(launch_layout_noalloc(*s, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                                          num_tokens_per_expert, is_token_in_rank, dev_status, stream));
+}
+
 ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, const int32_t *num_tokens_per_rank,
                       const int32_t *num_tokens_per_rdma_rank, const int32_t *num_tokens_per_expert,
                       int32_t *gbl_channel_prefix_matrix, int32_t *rdma_channel_prefix_matrix,

@@ -68,6 +68,12 @@ inline Workspace workspace_layout(int64_t T, int R, int E, int C, int K) {
 hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
                          int32_t *per_expert, uint8_t *in_rank, char *ws, int32_t *dev_status, hipStream_t stream);
 
+// The same on the library's static per-GPU scratch, for callers that cannot
+// allocate a workspace (experts up to kNoallocMaxExperts).
+constexpr int kNoallocMaxExperts = 16384;
+hipError_t launch_layout_noalloc(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
+                                 int32_t *per_expert, uint8_t *in_rank, int32_t *dev_status, hipStream_t stream);
+
 hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int32_t *per_rank,
                          const int32_t *per_node, const int32_t *per_expert, int32_t *gbl, int32_t *rdma,
                          int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,

@@ -24,6 +24,8 @@
 // block reports its valid slots and (token, rank) / (token, node) pairs, and
 // the last block checks that each class of running counts adds up to what was
 // reported, so running counts that were not zero are flagged as well.
+#include <mutex>
+
 #include "ep_internal.h"
 
 namespace ep {
@@ -226,7 +228,61 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     }
 }
 
+// Zeroes n words (the scratch of the allocation-free layout, before each call).
+__global__ __launch_bounds__(256) void clear_words_kernel(uint32_t *p, int n) {
+    const int i = blockIdx.x * 256 + threadIdx.x;
+    if (i < n) p[i] = 0u;
+}
+
+// The allocation-free layout's scratch: the layout part of a workspace (the
+// tickets, then the running counts from byte 256) in a static device array, so
+// the call needs no workspace.  Each GPU holds its own copy, at its own
+// address, until the process ends; calls on one GPU share it.
+constexpr size_t kScratchBytes =
+    256 + sizeof(int32_t) * (size_t)(kMaxRanks + kMaxRanks / kRanksPerNode + kNoallocMaxExperts);
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// Device address of this GPU's scratch, looked up once per device (with that
+// device current) and kept; the array's name in host code is not that address.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t scratch_address(int device, void **out) {
+    if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[device] == nullptr) {
+        void *ptr = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        g_scratch_ptr[device] = ptr;
+    }
+    *out = g_scratch_ptr[device];
+    return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_layout_noalloc(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
+                                 int32_t *per_expert, uint8_t *in_rank, int32_t *dev_status, hipStream_t stream) {
+    int device = -1;
+    hipError_t e = hipGetDevice(&device);
+    if (e != hipSuccess) return e;
+    void *ptr = nullptr;
+    e = scratch_address(device, &ptr);
+    if (e != hipSuccess) return e;
+    // the tickets and the running counts must start at zero: cleared by a kernel
+    // (not a memset, so the call can be captured in a graph)
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
+    const int words = (int)((w.acc + sizeof(int32_t) * (size_t)(s.num_ranks + num_nodes(s.num_ranks) +
+                                                               s.num_experts)) / sizeof(uint32_t));
+    hipLaunchKernelGGL(clear_words_kernel, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       static_cast<uint32_t *>(ptr), words);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_layout(s, topk_idx, per_rank, per_node, per_expert, in_rank, static_cast<char *>(ptr), dev_status,
+                         stream);
+}
 
 hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
                          int32_t *per_expert, uint8_t *in_rank, char *ws, int32_t *dev_status, hipStream_t stream) {

@@ -111,6 +111,20 @@ ep_status_t ep_get_layout(const ep_shape_t *s, const int64_t *topk_idx, int32_t 
                           hipStream_t stream);
 
 /*
+ * Stage 1 without a workspace, for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation).  Same inputs,
+ * outputs and dev_status as ep_get_layout; the tickets and running counts live in a static
+ * array of the library (66,080 bytes on each GPU, held until the process ends), which the
+ * call clears with a small kernel before the layout kernel.  Allocates nothing.
+ * Limits: num_experts <= 16384 (EP_ERR_UNSUPPORTED beyond).  The stream must belong to the
+ * current device (EP_ERR_INVALID_ARG otherwise).  Every call on one GPU uses that GPU's
+ * single array: calls that overlap in time on one GPU (on different streams) race.
+ */
+ep_status_t ep_get_layout_noalloc(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                                  int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                                  uint8_t *is_token_in_rank, int32_t *dev_status, hipStream_t stream);
+
+/*
  * Stage 2, notify.  [mscclpp ht_runtime.cc, internodeNotifyDispatch; internode.cu notes,
  * notify_dispatch sm1-x stages 1-3 and sm0 stage 6]
  * In:  is_token_in_rank [t][R] uint8 (any non-zero byte counts as 1) and the three count

@@ -31,7 +31,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["ep_get_layout", "ep_notify", "ep_dispatch", "ep_dispatch_fp8",
+    assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_dispatch",
+                                          "ep_dispatch_fp8",
                                           "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
                                           "ep_combine", "ep_workspace_bytes", "ep_status_string"])
 
@@ -248,6 +249,22 @@ def test_dispatch_without_workspace_limits(ep):
     fp8 = lib.ep_dispatch_fp8(ctypes.byref(long_channels), p, p, 4, p, p, p, p, p, None, 0, 10, p, p, p, None, p, p,
                               None, None)
     assert fp8 == ep.EP_ERR_UNSUPPORTED
+
+
+def test_noalloc_layout_argument_checks(ep):
+    # refused on the host before any device call: a shape beyond the static scratch,
+    # malformed shapes, missing outputs
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+
+    def call(shape, idx=p, rank=p, node=p, expert=p, in_rank=p):
+        return lib.ep_get_layout_noalloc(ctypes.byref(shape), idx, rank, node, expert, in_rank, None, None)
+
+    assert call(_shape(ep, num_experts=16384 * 2, num_ranks=64)) == ep.EP_ERR_UNSUPPORTED
+    assert call(_shape(ep, num_ranks=12)) == ep.EP_ERR_INVALID_ARG
+    assert call(_shape(ep), rank=None) == ep.EP_ERR_INVALID_ARG
+    assert call(_shape(ep), in_rank=None) == ep.EP_ERR_INVALID_ARG
+    assert call(_shape(ep), idx=None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_device_status_bits_agree_with_the_header(ep):
