@@ -110,6 +110,36 @@ __device__ __forceinline__ int count_below(const uint64_t (&col)[CPG], int64_t d
 // of [b, a), or entry c minus those of [a, e).  The side with fewer tokens beyond
 // the group's own is counted (at most half a channel); other = true takes the
 // other side instead (a second reading of the same offset, for the checks).
+// The part of derive_offset that needs no columns: the prefix entry and the
+// tokens counted outside the group; derive_offset = this plus derive_inner.
+template <int CPG>
+__device__ int derive_outer(const DispatchParams &p, int64_t a, int lane) {
+    constexpr int64_t GT = CPG * kChunk;
+    const int64_t c = a / p.Tc;
+    const int64_t b = c * p.Tc;
+    const int64_t e = b + p.Tc < p.T ? b + p.Tc : p.T;
+    const int64_t back = a - b;
+    const int64_t fwd = e > a + GT ? e - (a + GT) : 0;
+    int v = 0;
+    if (fwd <= back) {
+        if (lane < p.R) v = p.gbl[(int64_t)lane * p.C + c];
+        if (fwd > 0) v -= count_tokens(p, a + GT, e, lane);
+    } else {
+        if (lane < p.R && c > 0) v = p.gbl[(int64_t)lane * p.C + c - 1];
+        v += count_tokens(p, b, a, lane);
+    }
+    return v;
+}
+template <int CPG>
+__device__ int derive_inner(const DispatchParams &p, int64_t a, const uint64_t (&col)[CPG]) {
+    constexpr int64_t GT = CPG * kChunk;
+    const int64_t c = a / p.Tc;
+    const int64_t b = c * p.Tc;
+    const int64_t e = b + p.Tc < p.T ? b + p.Tc : p.T;
+    const int64_t fwd = e > a + GT ? e - (a + GT) : 0;
+    return fwd <= a - b ? -count_below(col, (e < a + GT ? e : a + GT) - a) : 0;
+}
+
 template <int CPG>
 __device__ int derive_offset(const DispatchParams &p, int64_t a, const uint64_t (&col)[CPG], int lane,
                              bool other = false) {
@@ -343,18 +373,26 @@ constexpr int64_t kMaxPullRowUnits = 1 << 16;  // 1 MiB rows
 // ordinary loads; a token has ~R*(1-(1-1/R)^k) rows, and all but the first
 // read hit the group's x in the XCD's L2.  Before its tasks, each group's GT
 // token tasks (send_slot, metadata, scales) go to GT of the XCD's waves, a
-// different set for each group.
+// different set for each group.  Without a workspace (DERIVE) the group's
+// columns come from is_token_in_rank rows: waves 0..CPG-1 of each block build
+// one chunk's columns each and wave CPG the part of the group's offsets that
+// lies outside it (prefix entry and count to the channel edge); one barrier,
+// and every wave of the block reads them from LDS (double-buffered by group).
 template <int CPG, int U, bool EXACT, int WPB, bool DERIVE>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParams p) {
     constexpr int GT = CPG * kChunk;  // tokens per group
+    __shared__ uint64_t s_col[2][CPG][kWave];
+    __shared__ int s_outer[2][kWave];
     const int lane = threadIdx.x & (kWave - 1);
     const int xcd = (int)(blockIdx.x % kXcds);
+    const int wib = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));  // wave in block
+    const int64_t G = (num_chunks(p.T) + CPG - 1) / CPG;
     const int W = (int)(gridDim.x / kXcds) * WPB;  // waves per XCD; the grid is a multiple of kXcds
     // wave index inside the XCD, made visibly wave-uniform so that the piece
     // arithmetic below stays on the scalar unit
-    const int wx = (int)(blockIdx.x / kXcds) * WPB + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int wx = (int)(blockIdx.x / kXcds) * WPB + wib;
     const int R = p.R;
-    const int64_t G = (num_chunks(p.T) + CPG - 1) / CPG;
+    int par = 0;
     const int TPR = (int)((p.row_units + U * kWave - 1) / (U * kWave));  // tasks per row
 
     for (int64_t g = xcd; g < G; g += kXcds) {
@@ -385,12 +423,22 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
         // lane r: bit l of col[c] set when token (q0 + c)*64 + l goes to rank r
         uint64_t col[CPG];
         int n = 0;
+        if (DERIVE) {
+            // waves 0..CPG-1 build one chunk's columns each, wave CPG the part of
+            // the offset outside the group; the block's waves read both from LDS
+            if (wib < CPG) s_col[par][wib][lane] = transpose64(token_mask(p, a + wib * kChunk + lane, true));
+            if (wib == CPG) s_outer[par][lane] = derive_outer<CPG>(p, a, lane);
+            __syncthreads();
 #pragma unroll
-        for (int c = 0; c < CPG; ++c) {
-            col[c] = transpose64(token_mask(p, a + c * kChunk + lane, DERIVE));
-            n += __popcll(col[c]);  // 0 on lanes >= R
+            for (int c = 0; c < CPG; ++c) col[c] = s_col[par][c][lane];
+            off0 = s_outer[par][lane] + derive_inner<CPG>(p, a, col);
+            par ^= 1;
+        } else {
+#pragma unroll
+            for (int c = 0; c < CPG; ++c) col[c] = transpose64(token_mask(p, a + c * kChunk + lane, DERIVE));
         }
-        if (DERIVE) off0 = derive_offset<CPG>(p, a, col, lane);
+#pragma unroll
+        for (int c = 0; c < CPG; ++c) n += __popcll(col[c]);  // 0 on lanes >= R
         // the group's rows on rank r: [s0, s0 + n) in slab r, run r of the
         // group's output starting at pex; chunk c's rows start at cb[c]
         const int s0 = lane < R ? slab0 + off0 : 0;
