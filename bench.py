@@ -340,6 +340,11 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
     out["dispatch_fp8"]["check"] = bool(torch.equal(slot8, b.send_slot) and torch.equal(rx[rows], x8[tok])
                                         and torch.equal(rs[rows], sc[tok]))
     out["dispatch_fp8"]["num_scales"] = S
+    out["dispatch_fp8_push"] = rate(dispatch_fp8_bytes(T, H, K, R, n_recv, S), mean_us(
+        lambda: ep.ep_dispatch_fp8(shape, x8, sc, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, n_recv, rx,
+                                   rs, b.recv_w, b.recv_idx, b.src_info, slot8, b.dev_status, form=ep.EP_FORM_PUSH)))
+    out["dispatch_fp8_push"]["check"] = bool(torch.equal(slot8, b.send_slot) and torch.equal(rx[rows], x8[tok])
+                                             and torch.equal(rs[rows], sc[tok]))
     cx8, cs8 = torch.empty_like(rx), torch.empty_like(rs)
     out["dispatch_cached_fp8"] = rate(dispatch_cached_bytes(T, R, n_recv, H, S), mean_us(
         lambda: ep.ep_dispatch_cached(shape, x8, 1, sc, S, b.send_slot, n_recv, cx8, cs8, b.dev_status)))
@@ -516,6 +521,16 @@ def main() -> int:
             calls["combine"]()
             timer.record(c1)
         torch.cuda.synchronize()
+        # the push form, which a caller takes when x is only in HBM
+        pev = [timer.pair() for _ in range(args.cold_steps)]
+        for p0, p1 in pev:
+            calls["layout"]()
+            calls["notify"]()
+            scratch.fill_(7)
+            timer.record(p0)
+            ep.run_dispatch(b, x, idx, w, form=ep.EP_FORM_PUSH)
+            timer.record(p1)
+        torch.cuda.synchronize()
         # the same, with x written again after the scratch write, as the layer before
         # dispatch writes it: x is then in the caches a freshly written tensor is in
         xs = x.clone()
@@ -529,11 +544,18 @@ def main() -> int:
             calls["dispatch"]()
             timer.record(f1)
         torch.cuda.synchronize()
-        cold = {"us_dispatch": round(float(np.mean([timer.elapsed_us(*dp) for dp, _ in cev])), 2),
-                "us_combine": round(float(np.mean([timer.elapsed_us(*cp) for _, cp in cev])), 2),
+        us_cd = float(np.mean([timer.elapsed_us(*dp) for dp, _ in cev]))
+        us_cp = float(np.mean([timer.elapsed_us(*pp) for pp in pev]))
+        us_cc = float(np.mean([timer.elapsed_us(*cp) for _, cp in cev]))
+        cold_bytes = dispatch_bytes(T, H, K, R, n_recv) + combine_bytes(T, H, K, R, n_recv)
+        cold = {"us_dispatch": round(us_cd, 2), "us_dispatch_push": round(us_cp, 2), "us_combine": round(us_cc, 2),
                 "us_dispatch_fresh_x": round(float(np.mean([timer.elapsed_us(*fp) for fp in fev])), 2),
-                "note": "one launch each after a 1 GiB scratch write, single-call events; fresh_x: x copied "
-                        "in again after the scratch write, before dispatch"}
+                "pct_peak_dispatch_plus_combine": round(100 * cold_bytes / (us_cd + us_cc) / 1e3 / HBM_PEAK_GBPS, 2),
+                "pct_peak_dispatch_push_plus_combine":
+                    round(100 * cold_bytes / (us_cp + us_cc) / 1e3 / HBM_PEAK_GBPS, 2),
+                "note": "one launch each after a 1 GiB scratch write, single-call events; us_dispatch: the default "
+                        "(pull) form, us_dispatch_push: EP_FORM_PUSH, the form for x only in HBM; fresh_x: x "
+                        "copied in again after the scratch write, before dispatch"}
         del scratch, xs
 
     variants = None if args.no_variants else time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, args.steps,

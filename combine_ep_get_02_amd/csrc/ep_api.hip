@@ -31,6 +31,8 @@ ep_status_t check_shape(const ep_shape_t *s) {
 
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
+bool form_ok(int32_t form) { return form == EP_FORM_AUTO || form == EP_FORM_PUSH || form == EP_FORM_PULL; }
+
 ep_status_t from_hip(hipError_t e) { return e == hipSuccess ? EP_OK : EP_ERR_HIP; }
 
 bool workspace_ok(const ep_shape_t *s, const void *ws, size_t bytes) {
@@ -56,11 +58,11 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
                              const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                              const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                              int32_t recv_capacity, void *recv_x, float *recv_x_scales, float *recv_topk_weights,
-                             int64_t *recv_topk_idx, int32_t *recv_src_info, int32_t *send_slot,
+                             int64_t *recv_topk_idx, int32_t *recv_src_info, int32_t *send_slot, int32_t form,
                              int32_t *dev_status, hipStream_t stream) {
     ep_status_t st = check_shape(s);
     if (st != EP_OK) return st;
-    if (row_bytes % 16 != 0 || recv_capacity < 0 || num_scales < 0) return EP_ERR_INVALID_ARG;
+    if (row_bytes % 16 != 0 || recv_capacity < 0 || num_scales < 0 || !form_ok(form)) return EP_ERR_INVALID_ARG;
     if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
     if (s->num_tokens == 0) return EP_OK;
     if (x == nullptr || topk_idx == nullptr || topk_weights == nullptr || send_slot == nullptr)
@@ -93,6 +95,7 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
     a.recv_idx = recv_topk_idx;
     a.src_info = recv_src_info;
     a.send_slot = send_slot;
+    a.form = form;
     a.dev_status = dev_status;
     return from_hip(launch_dispatch(*s, a, stream));
 }
@@ -181,11 +184,12 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
                         const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
-                        int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+                        int32_t *recv_src_info, int32_t *send_slot, int32_t form, int32_t *dev_status,
+                        hipStream_t stream) {
     return dispatch_checked(s, x, s ? (int64_t)s->hidden * 2 : 0, nullptr, 0, topk_idx, topk_weights,
                             is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace,
                             workspace_bytes, recv_capacity, recv_x, nullptr, recv_topk_weights, recv_topk_idx,
-                            recv_src_info, send_slot, dev_status, stream);
+                            recv_src_info, send_slot, form, dev_status, stream);
 }
 
 ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_scales, int32_t num_scales,
@@ -193,21 +197,22 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
                             const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
                             const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
                             float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
-                            int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+                            int32_t *recv_src_info, int32_t *send_slot, int32_t form, int32_t *dev_status,
+                            hipStream_t stream) {
     return dispatch_checked(s, x, s ? (int64_t)s->hidden : 0, x_scales, num_scales, topk_idx, topk_weights,
                             is_token_in_rank, gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace,
                             workspace_bytes, recv_capacity, recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx,
-                            recv_src_info, send_slot, dev_status, stream);
+                            recv_src_info, send_slot, form, dev_status, stream);
 }
 
 ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,
-                               float *recv_x_scales, int32_t *dev_status, hipStream_t stream) {
+                               float *recv_x_scales, int32_t form, int32_t *dev_status, hipStream_t stream) {
     ep_status_t st = check_shape(s);
     if (st != EP_OK) return st;
     if (elem_bytes != 1 && elem_bytes != 2) return EP_ERR_INVALID_ARG;
     const int64_t row_bytes = (int64_t)s->hidden * elem_bytes;
-    if (row_bytes % 16 != 0 || recv_capacity < 0) return EP_ERR_INVALID_ARG;
+    if (row_bytes % 16 != 0 || recv_capacity < 0 || !form_ok(form)) return EP_ERR_INVALID_ARG;
     if (num_scales < 0) return EP_ERR_INVALID_ARG;
     if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
     if (s->num_tokens == 0) return EP_OK;
@@ -225,6 +230,7 @@ ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_
     a.cap = recv_capacity;
     a.recv_x = recv_x;
     a.recv_scales = recv_x_scales;
+    a.form = form;
     a.dev_status = dev_status;
     return from_hip(launch_dispatch(*s, a, stream));
 }

@@ -917,7 +917,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
         p.num_scales = 0;  // no rows, so no scales beside them
         return run_meta(p, stream);
     }
-    {
+    if (a.form != EP_FORM_PUSH) {
         const PullTiling pt = pull_tiling(p.row_units, p.T);
         if (pt.cpg > 0 && p.cached_slot == nullptr) return run_pull_tiled(p, pt, stream);
         // cached mode: the pull form for rows of 14 KiB and more

@@ -102,6 +102,7 @@ struct DispatchArgs {
     int32_t *send_slot;
     int32_t *tok_pos;  // [t][k] set to -1 (metadata-only launch of the grouped dispatch), or null
     int32_t *dev_status;
+    int form;          // ep_dispatch_form_t: EP_FORM_PUSH keeps the push form
 };
 
 hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream);

@@ -20,6 +20,7 @@ LIBRARY = os.path.join(_PKG, "libep.so")
 EP_OK, EP_ERR_INVALID_ARG, EP_ERR_UNSUPPORTED, EP_ERR_HIP = 0, 1, 2, 3
 EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEND_SLOT = 1, 2, 4, 8
 EP_DEV_STALE_WORKSPACE = 16
+EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL = 0, 1, 2
 
 EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
             "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_workspace_bytes", "ep_status_string")
@@ -53,10 +54,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.ep_get_layout_noalloc.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P]
     lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
-    lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 7
+    lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 5 + \
+        [ctypes.c_int32, _P, _P]
     lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
-                                    ctypes.c_int32] + [_P] * 8
-    lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
+                                    ctypes.c_int32] + [_P] * 6 + [ctypes.c_int32, _P, _P]
+    lib.ep_dispatch_cached.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P,
+                                       ctypes.c_int32, _P, _P]
     lib.ep_group_by_expert.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32,
                                        ctypes.c_int32] + [_P] * 8
     lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
@@ -151,35 +154,36 @@ def _ws(workspace):
 
 def ep_dispatch(shape, x, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
                 recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x, recv_topk_weights, recv_topk_idx,
-                recv_src_info, send_slot, dev_status=None, stream=None) -> None:
+                recv_src_info, send_slot, dev_status=None, stream=None, form=EP_FORM_AUTO) -> None:
     """workspace: the one ep_notify filled for this is_token_in_rank, or None (the routing is
-    then worked out from is_token_in_rank and the prefix sums inside the call)."""
+    then worked out from is_token_in_rank and the prefix sums inside the call).  form: an
+    EP_FORM_* value (push when x is only in HBM, pull when it was just written)."""
     ws, ws_bytes = _ws(workspace)
     _check(load().ep_dispatch(ctypes.byref(shape), _ptr(x), _ptr(topk_idx), _ptr(topk_weights),
                               _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
                               _ptr(recv_gbl_rank_prefix_sum), ws, ws_bytes, int(recv_capacity), _ptr(recv_x),
                               _ptr(recv_topk_weights), _ptr(recv_topk_idx), _ptr(recv_src_info), _ptr(send_slot),
-                              _ptr(dev_status), _stream(stream)), "ep_dispatch")
+                              int(form), _ptr(dev_status), _stream(stream)), "ep_dispatch")
 
 
 def ep_dispatch_fp8(shape, x, x_scales, num_scales, topk_idx, topk_weights, is_token_in_rank,
                     gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x,
                     recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info, send_slot, dev_status=None,
-                    stream=None) -> None:
+                    stream=None, form=EP_FORM_AUTO) -> None:
     ws, ws_bytes = _ws(workspace)
     _check(load().ep_dispatch_fp8(ctypes.byref(shape), _ptr(x), _ptr(x_scales), int(num_scales), _ptr(topk_idx),
                                   _ptr(topk_weights), _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
                                   _ptr(recv_gbl_rank_prefix_sum), ws, ws_bytes, int(recv_capacity), _ptr(recv_x),
                                   _ptr(recv_x_scales), _ptr(recv_topk_weights), _ptr(recv_topk_idx),
-                                  _ptr(recv_src_info), _ptr(send_slot), _ptr(dev_status), _stream(stream)),
-           "ep_dispatch_fp8")
+                                  _ptr(recv_src_info), _ptr(send_slot), int(form), _ptr(dev_status),
+                                  _stream(stream)), "ep_dispatch_fp8")
 
 
 def ep_dispatch_cached(shape, x, elem_bytes, x_scales, num_scales, send_slot, recv_capacity, recv_x,
-                       recv_x_scales=None, dev_status=None, stream=None) -> None:
+                       recv_x_scales=None, dev_status=None, stream=None, form=EP_FORM_AUTO) -> None:
     _check(load().ep_dispatch_cached(ctypes.byref(shape), _ptr(x), int(elem_bytes), _ptr(x_scales), int(num_scales),
                                      _ptr(send_slot), int(recv_capacity), _ptr(recv_x), _ptr(recv_x_scales),
-                                     _ptr(dev_status), _stream(stream)), "ep_dispatch_cached")
+                                     int(form), _ptr(dev_status), _stream(stream)), "ep_dispatch_cached")
 
 
 def ep_group_by_expert(shape, recv_x, elem_bytes, recv_x_scales, num_scales, recv_topk_idx, recv_topk_weights,
@@ -278,12 +282,13 @@ def run_notify(b: Buffers, read_back: bool = False, stream=None) -> int | None:
                      b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, read_back, b.dev_status, stream)
 
 
-def run_dispatch(b: Buffers, x, topk_idx, topk_weights, use_workspace: bool = True, stream=None) -> None:
+def run_dispatch(b: Buffers, x, topk_idx, topk_weights, use_workspace: bool = True, stream=None,
+                 form=EP_FORM_AUTO) -> None:
     """use_workspace: take the routing state notify left in b.workspace; False: work it
     out from b.in_rank and the prefix sums inside the call."""
     ep_dispatch(b.shape, x, topk_idx, topk_weights, b.in_rank, b.gbl, b.recv_gbl,
                 b.workspace if use_workspace else None, b.capacity, b.recv_x, b.recv_w, b.recv_idx, b.src_info,
-                b.send_slot, b.dev_status, stream)
+                b.send_slot, b.dev_status, stream, form)
 
 
 def run_combine(b: Buffers, y=None, num_recv_rows=None, with_weights: bool = True, stream=None) -> None:

@@ -81,6 +81,23 @@ enum {
                                   this is_token_in_rank.  The call's outputs are then not to be trusted. */
 };
 
+/* Which form of the row copy a dispatch takes.  [mscclpp ht_runtime.cc: the dispatch calls take a
+ * Config, from which the runtime picks the kernel's form (computeIntranodeChannels chooses between
+ * the sender/receiver split and all-sender blocks); here the choice rests on where x is.]
+ *   push: token order -- each token's x row is read once, up front, and stored to all its
+ *         destinations.  Best when x is only in HBM (it reads x as one stream).
+ *   pull: receive order -- each XCD writes one advancing window of the receive region and
+ *         re-reads x from its L2.  Best when x was just written (still in the Infinity Cache,
+ *         as the layer before dispatch leaves it); slower than push when x is only in HBM.
+ *         It applies from 2048 tokens, to rows of 1 KiB to 1 MiB (cached mode: from 14 KiB);
+ *         elsewhere the push form is taken.
+ * The outputs are the same, bit for bit, whichever form runs. */
+typedef enum {
+    EP_FORM_AUTO = 0, /* the library's choice: currently the pull form wherever it applies */
+    EP_FORM_PUSH = 1,
+    EP_FORM_PULL = 2
+} ep_dispatch_form_t;
+
 /* Problem shape (host struct, read during the call only). */
 typedef struct {
     int32_t num_tokens;       /* t >= 0 tokens on this rank                                      */
@@ -181,6 +198,7 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
  *      send_slot         [t][R]   int32: the row of (t, r), -1 where t is not sent to r
  * Rows >= recv_capacity (or below 0) are skipped and flagged (EP_DEV_RECV_OVERFLOW); their
  * send_slot is -1.
+ * form: an ep_dispatch_form_t (EP_FORM_AUTO when the caller does not know where x is).
  * dev_status (nullable): EP_DEV_RECV_OVERFLOW; EP_DEV_COUNT_MISMATCH when the prefix matrix or
  * the receive prefix sums disagree with is_token_in_rank (rows are then placed by the prefix
  * matrix, unchecked); EP_DEV_STALE_WORKSPACE as above.
@@ -189,7 +207,8 @@ ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_
                         const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                         int32_t recv_capacity, void *recv_x, float *recv_topk_weights, int64_t *recv_topk_idx,
-                        int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
+                        int32_t *recv_src_info, int32_t *send_slot, int32_t form, int32_t *dev_status,
+                        hipStream_t stream);
 
 /*
  * Dispatch of fp8 rows.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch:
@@ -206,7 +225,8 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
                             const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
                             const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
                             float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
-                            int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
+                            int32_t *recv_src_info, int32_t *send_slot, int32_t form, int32_t *dev_status,
+                            hipStream_t stream);
 
 /*
  * Cached-mode dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch with
@@ -216,11 +236,11 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
  * routing.  Rows are hidden * elem_bytes bytes (elem_bytes 2 = bf16, 1 = fp8; a multiple
  * of 16); num_scales float scales per token go along when num_scales > 0.  No metadata
  * is written.  Entries outside [-1, recv_capacity) are skipped and flagged
- * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.
+ * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.  form: as for ep_dispatch.
  */
 ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,
-                               float *recv_x_scales, int32_t *dev_status, hipStream_t stream);
+                               float *recv_x_scales, int32_t form, int32_t *dev_status, hipStream_t stream);
 
 /*
  * Grouping of the received rows by local expert, the layout grouped expert GEMMs read.

@@ -127,7 +127,7 @@ int main(void) {
     void *combined = dev_alloc((size_t)T * H * 2);
     /* dispatch from the routing inputs alone (no workspace): is_token_in_rank and the prefix sums */
     CHECK_EP(ep_dispatch(&shape, d_x, d_idx, d_w, in_rank, gbl, recv_gbl, NULL, 0, n, recv_x, recv_w, recv_idx,
-                         src_info, send_slot, status, stream));
+                         src_info, send_slot, EP_FORM_AUTO, status, stream));
     CHECK_EP(ep_combine(&shape, recv_x, recv_w, send_slot, n, combined, NULL, status, stream));
 
     int32_t *h_aligned = malloc(4 * E);

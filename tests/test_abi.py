@@ -87,11 +87,11 @@ def _call_all(ep, s):
     codes = [
         lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, p, 1 << 30, None, None),
         lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
-        lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None, None),
+        lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, 0, None, None),
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
-        lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, None,
-                            None),
-        lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, None, None),
+        lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, 0,
+                            None, None),
+        lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, 0, None, None),
         lib.ep_group_by_expert(ctypes.byref(s), p, 2, None, 0, p, p, p, p, 10, 10, p, None, p, p, p, p, None, None),
     ]
     return codes
@@ -118,17 +118,17 @@ def test_null_and_misaligned_pointers_rejected(ep):
                          None) == ep.EP_ERR_INVALID_ARG  # no workspace
     assert lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 16, None,
                          None) == ep.EP_ERR_INVALID_ARG  # workspace too small
-    assert lib.ep_dispatch(ctypes.byref(s), odd, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), odd, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # x not 16-byte aligned
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, -1, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, -1, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # negative capacity
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, None, p, p, p, 1 << 30, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, None, p, p, p, 1 << 30, 10, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # no is_token_in_rank
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, None, p, p, 1 << 30, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, None, p, p, 1 << 30, 10, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # no channel prefix matrix
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, None, p, 1 << 30, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, None, p, 1 << 30, 10, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # no receive prefix sums
-    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 16, 10, p, p, None, p, p, None,
+    assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 16, 10, p, p, None, p, p, 0, None,
                            None) == ep.EP_ERR_INVALID_ARG  # workspace given but too small
     assert lib.ep_combine(ctypes.byref(s), p, p, p, 10, odd, None, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_combine(ctypes.byref(s), p, p, None, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
@@ -141,17 +141,15 @@ def test_fp8_and_cached_argument_checks(ep):
     s = _shape(ep)
     # fp8 rows must be a whole number of 16-byte units
     s12 = _shape(ep, hidden=7160)
-    assert lib.ep_dispatch_fp8(ctypes.byref(s12), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+    assert lib.ep_dispatch_fp8(ctypes.byref(s12), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, 0,
                                None, None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, None, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, None, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, 0,
                                None, None) == ep.EP_ERR_INVALID_ARG  # scales missing
-    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 2000, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p,
+    assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 2000, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, 0,
                                None, None) == ep.EP_ERR_UNSUPPORTED
-    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 3, None, 0, p, 10, p, None, None, None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, None, 10, p, None, None,
-                                  None) == ep.EP_ERR_INVALID_ARG
-    assert lib.ep_dispatch_cached(ctypes.byref(s12), p, 1, None, 0, p, 10, p, None, None,
-                                  None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 3, None, 0, p, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, None, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dispatch_cached(ctypes.byref(s12), p, 1, None, 0, p, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_group_by_expert_argument_checks(ep):
@@ -230,7 +228,7 @@ def test_empty_dispatch_and_combine_enqueue_nothing(ep):
     lib = ep.load()
     s = _shape(ep, num_tokens=0)
     assert lib.ep_dispatch(ctypes.byref(s), None, None, None, None, None, None, None, 0, 0, None, None, None, None,
-                           None, None, None) == ep.EP_OK
+                           None, 0, None, None) == ep.EP_OK
     assert lib.ep_combine(ctypes.byref(s), None, None, None, 0, None, None, None, None) == ep.EP_OK
 
 
@@ -242,11 +240,11 @@ def test_dispatch_without_workspace_limits(ep):
     p = ctypes.c_void_p(256)
 
     def dispatch(shape, ws, wsb):
-        return lib.ep_dispatch(ctypes.byref(shape), p, p, p, p, p, p, ws, wsb, 10, p, p, None, p, p, None, None)
+        return lib.ep_dispatch(ctypes.byref(shape), p, p, p, p, p, p, ws, wsb, 10, p, p, None, p, p, 0, None, None)
 
     long_channels = _shape(ep, num_tokens=100000, num_channels=24)  # 4167 tokens per channel
     assert dispatch(long_channels, None, 0) == ep.EP_ERR_UNSUPPORTED
-    fp8 = lib.ep_dispatch_fp8(ctypes.byref(long_channels), p, p, 4, p, p, p, p, p, None, 0, 10, p, p, p, None, p, p,
+    fp8 = lib.ep_dispatch_fp8(ctypes.byref(long_channels), p, p, 4, p, p, p, p, p, None, 0, 10, p, p, p, None, p, p, 0,
                               None, None)
     assert fp8 == ep.EP_ERR_UNSUPPORTED
 
@@ -273,3 +271,18 @@ def test_device_status_bits_agree_with_the_header(ep):
     bits = dict((m.group(1), int(m.group(2))) for m in re.finditer(r"\b(EP_DEV_[A-Z_]+)\s*=\s*(\d+)", text))
     assert bits == {name: getattr(ep, name) for name in bits}
     assert bits["EP_DEV_STALE_WORKSPACE"] == 16 and len(set(bits.values())) == len(bits) == 5
+
+
+def test_dispatch_form_must_be_known(ep):
+    # form is one of EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL; anything else is refused on the host
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    s = _shape(ep)
+    assert (ep.EP_FORM_AUTO, ep.EP_FORM_PUSH, ep.EP_FORM_PULL) == (0, 1, 2)
+    for form in (-1, 3, 7):
+        assert lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, form, None,
+                               None) == ep.EP_ERR_INVALID_ARG
+        assert lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, form,
+                                   None, None) == ep.EP_ERR_INVALID_ARG
+        assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, form, None,
+                                      None) == ep.EP_ERR_INVALID_ARG

@@ -32,7 +32,8 @@ def _dev(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=None, my_rank=0, fp8=None):
+def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=None, my_rank=0, fp8=None,
+                    form=ep.EP_FORM_AUTO):
     """ep_dispatch (bf16 x) or ep_dispatch_fp8 (fp8=(rows, scales)) from uploaded routing
     inputs into poisoned buffers; returns the outputs as numpy arrays and the status."""
     T, K = idx.shape
@@ -50,14 +51,14 @@ def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=N
     if fp8 is None:
         rx = torch.full((c1, Hd), -1, dtype=torch.int16, device="cuda")
         ep.ep_dispatch(shape, H.to_dev_bf16(x), didx, dw, d_in, d_gbl, d_recv, workspace, cap, rx, rw, ri, si, ss,
-                       st)
+                       st, form=form)
     else:
         x8, sc = fp8
         NS = sc.shape[1]
         rx = torch.full((c1, Hd), 0xAB, dtype=torch.uint8, device="cuda")
         rs = torch.full((c1, max(NS, 1)), -2.0, dtype=torch.float32, device="cuda")
         ep.ep_dispatch_fp8(shape, _dev(x8), _dev(sc) if NS else None, NS, didx, dw, d_in, d_gbl, d_recv, workspace,
-                           cap, rx, rs if NS else None, rw, ri, si, ss, st)
+                           cap, rx, rs if NS else None, rw, ri, si, ss, st, form=form)
     torch.cuda.synchronize()
     rows = min(int(recv_gbl[-1]) if len(recv_gbl) else 0, cap)
     out["send_slot"] = ss.cpu().numpy()
@@ -227,3 +228,25 @@ def test_inconsistent_prefixes_are_flagged(orc, use_ws, what, T, Hd):
     ref = _reference(orc, x, idx, w, E, lay["is_token_in_rank"], gbl, recv, cap)
     assert ref["status"] & oracle.COUNT_MISMATCH
     assert gpu["status"] & ep.EP_DEV_COUNT_MISMATCH
+
+
+@pytest.mark.parametrize("form", ["push", "pull"])
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("fp8", [False, True])
+def test_dispatch_forms_give_the_same_outputs(orc, form, use_ws, fp8):
+    # the caller's choice of form (push for x only in HBM, pull for x just written) changes
+    # the order of the copies, never the outputs
+    print(f"[dispatch alone] form={form} workspace={use_ws} fp8={fp8}", flush=True)
+    d = generate("skew")
+    wl = d["workload"]
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    lay, note = _routing(orc, idx, wl.experts, wl.ranks, wl.channels)
+    cap = note["num_recv_tokens"]
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"], cap)
+    ws = _notified_workspace(idx, wl.experts, wl.ranks, wl.channels, wl.hidden) if use_ws else None
+    f8 = fp8_rows(x) if fp8 else None
+    gpu = _dispatch_alone(x, idx, w, wl.experts, wl.ranks, wl.channels, *args, workspace=ws, fp8=f8,
+                          form=ep.EP_FORM_PUSH if form == "push" else ep.EP_FORM_PULL)
+    ref = _reference(orc, x, idx, w, wl.experts, *args, fp8=f8)
+    assert _differences(gpu, ref) == []
+    assert gpu["status"] == 0

@@ -314,8 +314,9 @@ CACHED_LARGE = {
 }
 
 
+@pytest.mark.parametrize("form", [0, 1])  # EP_FORM_AUTO (the pull form from 14 KiB rows), EP_FORM_PUSH
 @pytest.mark.parametrize("name", sorted(CACHED_LARGE))
-def test_cached_any_map_and_bad_slots(name):
+def test_cached_any_map_and_bad_slots(name, form):
     import torch
 
     import oracle
@@ -337,7 +338,7 @@ def test_cached_any_map_and_bad_slots(name):
     outs = torch.full((cap, max(NS, 1)), -5.0, dtype=torch.float32, device="cuda")
     st = torch.zeros(1, dtype=torch.int32, device="cuda")
     ep.ep_dispatch_cached(shape, torch.from_numpy(xr).cuda(), elem, torch.from_numpy(sc).cuda() if NS else None, NS,
-                          torch.from_numpy(slot).cuda(), cap, out, outs if NS else None, st)
+                          torch.from_numpy(slot).cuda(), cap, out, outs if NS else None, st, form=form)
     torch.cuda.synchronize()
     # rows no entry names keep the fill, as in the oracle's output buffer below
     ref = oracle.Oracle().dispatch_cached(xr, slot, cap, sc)
