@@ -180,6 +180,36 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
     return EP_OK;
 }
 
+ep_status_t ep_layout_notify(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                             int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                             uint8_t *is_token_in_rank, int32_t *gbl_channel_prefix_matrix,
+                             int32_t *rdma_channel_prefix_matrix, int32_t *recv_gbl_rank_prefix_sum,
+                             int32_t *recv_rdma_rank_prefix_sum, int32_t *num_recv_tokens_per_expert,
+                             int32_t *num_recv_tokens, int32_t *num_recv_tokens_host, void *workspace,
+                             size_t workspace_bytes, int32_t *dev_status, hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (num_tokens_per_rank == nullptr || num_tokens_per_rdma_rank == nullptr || num_tokens_per_expert == nullptr ||
+        gbl_channel_prefix_matrix == nullptr || rdma_channel_prefix_matrix == nullptr ||
+        recv_gbl_rank_prefix_sum == nullptr || recv_rdma_rank_prefix_sum == nullptr ||
+        num_recv_tokens_per_expert == nullptr || num_recv_tokens == nullptr)
+        return EP_ERR_INVALID_ARG;
+    if (s->num_tokens > 0 && (topk_idx == nullptr || is_token_in_rank == nullptr)) return EP_ERR_INVALID_ARG;
+    if (!workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
+    hipError_t e = launch_layout_notify(*s, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank,
+                                        num_tokens_per_expert, is_token_in_rank, gbl_channel_prefix_matrix,
+                                        rdma_channel_prefix_matrix, recv_gbl_rank_prefix_sum,
+                                        recv_rdma_rank_prefix_sum, num_recv_tokens_per_expert, num_recv_tokens,
+                                        static_cast<char *>(workspace), dev_status, stream);
+    if (e != hipSuccess) return EP_ERR_HIP;
+    if (num_recv_tokens_host != nullptr) {
+        e = hipMemcpyAsync(num_recv_tokens_host, num_recv_tokens, sizeof(int32_t), hipMemcpyDeviceToHost, stream);
+        if (e == hipSuccess) e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return EP_ERR_HIP;
+    }
+    return EP_OK;
+}
+
 ep_status_t ep_dispatch(const ep_shape_t *s, const void *x, const int64_t *topk_idx, const float *topk_weights,
                         const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                         const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,

@@ -44,6 +44,7 @@ struct Workspace {
 // uint32 word offsets of the tickets (each a 64-bit ticket, see elect_completing_block)
 constexpr int kTicketLayout = 0;   // counts tokens; words 2..4: valid slots, (token, rank) and (token, node) pairs
 constexpr int kTicketNotify = 16;  // counts chunks (a separate 64-byte line)
+constexpr int kTicketFused = 32;   // layout + notify in one launch: counts chunks; word 34: valid slots
 
 inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -73,6 +74,12 @@ hipError_t launch_layout(const ep_shape_t &s, const int64_t *topk_idx, int32_t *
 constexpr int kNoallocMaxExperts = 16384;
 hipError_t launch_layout_noalloc(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
                                  int32_t *per_expert, uint8_t *in_rank, int32_t *dev_status, hipStream_t stream);
+
+// Layout and notify in one launch (the outputs of both, and notify's workspace state).
+hipError_t launch_layout_notify(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
+                                int32_t *per_expert, uint8_t *in_rank, int32_t *gbl, int32_t *rdma,
+                                int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,
+                                char *ws, int32_t *dev_status, hipStream_t stream);
 
 hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int32_t *per_rank,
                          const int32_t *per_node, const int32_t *per_expert, int32_t *gbl, int32_t *rdma,
@@ -193,6 +200,11 @@ __device__ __forceinline__ uint64_t transpose64(uint64_t x) {
         x = (lane & s) == 0 ? (x & keep[k]) | ((y & keep[k]) << s) : (x & ~keep[k]) | ((y & ~keep[k]) >> s);
     }
     return x;
+}
+
+// byte i of the result = bit i of the low 4 bits of `nib` (a mask nibble as 0/1 bytes)
+__device__ __forceinline__ uint32_t spread4(uint32_t nib) {
+    return (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
 }
 
 // Nonzero-byte test of four packed bytes -> 4 bits (bit i set when byte i != 0).

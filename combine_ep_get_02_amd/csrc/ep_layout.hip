@@ -34,11 +34,6 @@ namespace {
 constexpr int kLayoutThreads = 256;
 constexpr int kMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E counts in the workspace directly
 
-// byte i of the result = bit i of the low 4 bits of `nib`
-__device__ __forceinline__ uint32_t spread4(uint32_t nib) {
-    return (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
-}
-
 struct LayoutParams {
     const int64_t *topk_idx;
     int32_t *per_rank, *per_node, *per_expert;

@@ -47,17 +47,20 @@ struct NotifyParams {
     int32_t *dev_status;
     int64_t T, Tc;
     int R, C, E, nodes, align, load_unit;
+    // fused layout + notify: the per-rank / per-node totals are not inputs but come
+    // from the scan, and are written to tot_rank / tot_node
+    bool fused;
+    int32_t *tot_rank, *tot_node;
 };
 
-__device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
+// The chunk's counts from its tokens' rank masks (lane l: token q*64 + l's mask, 0
+// past the last token): the masks for dispatch, the (chunk, rank) and (chunk, node)
+// counts, and the partial counts at channel ends inside the chunk.
+__device__ void count_chunk_masks(const NotifyParams &p, int64_t q, int lane, uint64_t m) {
     const int64_t first = q * kChunk;
     const int64_t tok = first + lane;
     const int R = p.R, nodes = p.nodes;
-    uint64_t m = 0;
-    if (tok < p.T) {
-        m = load_rank_mask(p.in_rank + tok * R, R, p.load_unit);
-        p.mask[tok] = m;
-    }
+    if (tok < p.T) p.mask[tok] = m;
     const uint64_t my_bits = transpose64(m);  // lane r: which tokens of the chunk go to rank r
     uint64_t my_node_bits = 0;  // lane n: which tokens of the chunk reach node n
     for (int n = 0; n < nodes; ++n) {
@@ -76,6 +79,12 @@ __device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
         if (lane < R) p.rank_part[c * R + lane] = __popcll(my_bits & below);
         if (lane < nodes) p.node_part[c * nodes + lane] = __popcll(my_node_bits & below);
     }
+}
+
+__device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
+    const int64_t tok = q * kChunk + lane;
+    const uint64_t m = tok < p.T ? load_rank_mask(p.in_rank + tok * p.R, p.R, p.load_unit) : 0ull;
+    count_chunk_masks(p, q, lane, m);
 }
 
 // One wave scans one column of the [Q][stride] count matrix into exclusive
@@ -112,6 +121,28 @@ __device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c)
     return (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
 }
 
+// Inclusive prefix sums over destination ranks and nodes (two waves), and N.
+__device__ void recv_prefixes(const NotifyParams &p, int32_t per_rank, int32_t per_node, int lane, int wave) {
+    if (wave == kNotifyWaves - 1) {
+        const int32_t incl = wave_inclusive_scan(per_rank);
+        if (lane < p.R) p.recv_gbl[lane] = incl;
+        if (lane == p.R - 1) p.num_recv[0] = incl;
+    } else if (wave == kNotifyWaves - 2) {
+        const int32_t incl = wave_inclusive_scan(per_node);
+        if (lane < p.nodes) p.recv_rdma[lane] = incl;
+    }
+}
+
+// Fused layout + notify: the per-rank and per-node totals are the scan's column
+// totals (tot[column]); they are written out and the receive prefixes follow them.
+__device__ void finish_totals(const NotifyParams &p, const int32_t *tot, int lane, int wave) {
+    const int32_t per_rank = lane < p.R ? tot[lane] : 0;
+    const int32_t per_node = lane < p.nodes ? tot[p.R + lane] : 0;
+    if (wave == kNotifyWaves - 1 && lane < p.R) p.tot_rank[lane] = per_rank;
+    if (wave == kNotifyWaves - 2 && lane < p.nodes) p.tot_node[lane] = per_node;
+    recv_prefixes(p, per_rank, per_node, lane, wave);
+}
+
 // Last block, small problems: the counts, the partials and the per-rank / per-node
 // totals come into LDS in one round trip, are scanned there, and every output is
 // written from LDS.
@@ -143,8 +174,8 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
                         : 0;
         }
     }
-    const int32_t per_rank = lane < R ? p.per_rank[lane] : 0;
-    const int32_t per_node = lane < nodes ? p.per_node[lane] : 0;
+    const int32_t per_rank = (!p.fused && lane < R) ? p.per_rank[lane] : 0;
+    const int32_t per_node = (!p.fused && lane < nodes) ? p.per_node[lane] : 0;
 #pragma unroll
     for (int k = 0; k < kExpertBatch; ++k) {
         const int e = tid + k * kNotifyThreads;
@@ -209,19 +240,14 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
             }
         }
     }
-    // receive prefix sums over destination ranks and nodes (inclusive)
-    if (wave == kNotifyWaves - 1) {
-        const int32_t incl = wave_inclusive_scan(per_rank);
-        if (lane < R) p.recv_gbl[lane] = incl;
-        if (lane == R - 1) p.num_recv[0] = incl;
-    } else if (wave == kNotifyWaves - 2) {
-        const int32_t incl = wave_inclusive_scan(per_node);
-        if (lane < nodes) p.recv_rdma[lane] = incl;
-    }
+    // receive prefix sums over destination ranks and nodes (inclusive); fused, from
+    // the scan's totals once every column is done
+    if (!p.fused) recv_prefixes(p, per_rank, per_node, lane, wave);
     __syncthreads();
+    if (p.fused) finish_totals(p, s_tot, lane, wave);
 
     // ---- outputs
-    if (wave == kNotifyWaves - 3) {
+    if (!p.fused && wave == kNotifyWaves - 3) {
         const bool bad = (lane < R && s_tot[lane] != per_rank) || (lane < nodes && s_tot[R + lane] != per_node);
         if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
     }
@@ -245,30 +271,28 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
 
 // Last block, large problems: the same steps on the workspace in global memory.
 __device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int wave) {
+    __shared__ int32_t s_tot_g[kMaxRanks + kMaxRanks / kRanksPerNode];
     const int R = p.R, nodes = p.nodes, NC = R + nodes;
     const int64_t Q = num_chunks(p.T);
     for (int col = wave; col < NC; col += kNotifyWaves) {
         const bool is_rank = col < R;
         int32_t *cp = is_rank ? p.rank_off + col : p.node_off + (col - R);
         const int32_t total = scan_column(cp, is_rank ? R : nodes, Q, lane);
-        const int32_t want = is_rank ? p.per_rank[col] : p.per_node[col - R];
-        if (lane == 0 && total != want) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+        if (p.fused) {
+            if (lane == 0) s_tot_g[col] = total;
+        } else {
+            const int32_t want = is_rank ? p.per_rank[col] : p.per_node[col - R];
+            if (lane == 0 && total != want) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+        }
     }
-    if (wave == kNotifyWaves - 1) {
-        const int32_t v = lane < R ? p.per_rank[lane] : 0;
-        const int32_t incl = wave_inclusive_scan(v);
-        if (lane < R) p.recv_gbl[lane] = incl;
-        if (lane == R - 1) p.num_recv[0] = incl;
-    } else if (wave == kNotifyWaves - 2) {
-        const int32_t v = lane < nodes ? p.per_node[lane] : 0;
-        const int32_t incl = wave_inclusive_scan(v);
-        if (lane < nodes) p.recv_rdma[lane] = incl;
-    }
+    if (!p.fused)
+        recv_prefixes(p, lane < R ? p.per_rank[lane] : 0, lane < nodes ? p.per_node[lane] : 0, lane, wave);
     for (int e = tid; e < p.E; e += kNotifyThreads) {
         const int64_t n = p.per_expert[e];
         p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
     }
     __syncthreads();  // scanned offsets visible to the whole block
+    if (p.fused) finish_totals(p, s_tot_g, lane, wave);
     for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
         const int cc = (int)(i / p.C);
         const int64_t c = i % p.C;
@@ -313,7 +337,204 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
         finish_in_global(p, tid, lane, wave);
 }
 
+// ---------------------------------------------------------------- layout + notify in one launch
+// From topk_idx straight to every output of both stages.  Each thread builds its
+// token's rank mask from the topk ids (as the layout does), and each wave, its
+// 64 tokens being one chunk, counts the chunk from those masks in registers (as
+// notify does from is_token_in_rank): one pass over the tokens, one election.
+// The per-expert counts go through an LDS histogram and the running counts; the
+// per-rank and per-node totals are the scan's column totals.  The completing
+// block publishes the expert totals and then finishes as notify does.
+constexpr int kFusedMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E counts in the workspace
+
+struct FusedParams {
+    const int64_t *topk_idx;
+    int32_t *per_expert;
+    uint8_t *in_rank;
+    int32_t *acc_expert;  // running per-expert counts [E], zero between calls
+    uint64_t *ticket;     // completion ticket (chunks)
+    uint32_t *report;     // valid slots the finished blocks report
+    int K, store_unit;
+};
+
+__global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedParams f, NotifyParams p) {
+    __shared__ uint64_t s_mask[kNotifyThreads];
+    __shared__ uint32_t s_slots, s_esum;
+    extern __shared__ int32_t s_expert[];  // E entries when E <= kFusedMaxLdsExperts
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int R = p.R, E = p.E, K = f.K;
+    const bool lds_experts = E <= kFusedMaxLdsExperts;
+    const bool single = gridDim.x == 1;
+    const uint32_t epoch0 = (!single && tid == 0) ? ticket_epoch(f.ticket) : 0u;
+    const int64_t Q = num_chunks(p.T);
+    if (tid == 0) {
+        s_slots = 0;
+        s_esum = 0;
+    }
+    if (lds_experts)
+        for (int e = tid; e < E; e += kNotifyThreads) s_expert[e] = 0;
+    __syncthreads();
+
+    // ---- the token: rank mask, valid slots, expert counts
+    const int64_t t0 = (int64_t)blockIdx.x * kNotifyThreads;
+    const int64_t t = t0 + tid;
+    const int experts_per_rank = E / R;
+    uint64_t mask = 0;
+    int bad = 0, slots = 0;
+    if (t < p.T) {
+        const int64_t *row = f.topk_idx + t * K;
+        for (int j0 = 0; j0 < K; j0 += 8) {  // a batch's loads are in flight together
+            int64_t ev[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) ev[u] = j0 + u < K ? row[j0 + u] : -1;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int64_t e = ev[u];
+                if (e == -1) continue;
+                if (e < -1 || e >= E) {
+                    bad = 1;
+                    continue;
+                }
+                ++slots;
+                if (lds_experts)
+                    atomicAdd(&s_expert[(int)e], 1);
+                else
+                    atomicAdd(&f.acc_expert[(int)e], 1);
+                mask |= 1ull << ((int)e / experts_per_rank);
+            }
+        }
+    }
+    s_mask[tid] = mask;
+    // ---- the wave's chunk, from the masks in registers
+    const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
+    if (q < Q) count_chunk_masks(p, q, lane, mask);
+    if (ballot64(bad != 0) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_TOPK_IDX);
+    const int w_slots = wave_sum(slots);
+    if (lane == 0) atomicAdd(&s_slots, (uint32_t)w_slots);
+    __syncthreads();
+
+    // ---- is_token_in_rank rows of this block: one contiguous range of nt*R bytes
+    {
+        const int64_t left = p.T - t0;
+        const int nt = (int)(left < kNotifyThreads ? (left > 0 ? left : 0) : kNotifyThreads);
+        const int nbytes = nt * R;
+        uint8_t *dst = f.in_rank + t0 * R;
+        if (f.store_unit == 16) {
+            const int upr = R / 16;
+            for (int u = tid; u < nbytes / 16; u += kNotifyThreads) {
+                const int rw = u / upr, part = u - rw * upr;
+                const uint64_t m = s_mask[rw] >> (16 * part);
+                uint4 v;
+                v.x = spread4((uint32_t)m & 0xfu);
+                v.y = spread4((uint32_t)(m >> 4) & 0xfu);
+                v.z = spread4((uint32_t)(m >> 8) & 0xfu);
+                v.w = spread4((uint32_t)(m >> 12) & 0xfu);
+                reinterpret_cast<uint4 *>(dst)[u] = v;
+            }
+        } else if (f.store_unit == 4) {
+            const int upr = R / 4;
+            for (int u = tid; u < nbytes / 4; u += kNotifyThreads) {
+                const int rw = u / upr, part = u - rw * upr;
+                reinterpret_cast<uint32_t *>(dst)[u] = spread4((uint32_t)(s_mask[rw] >> (4 * part)) & 0xfu);
+            }
+        } else {
+            for (int b = tid; b < nbytes; b += kNotifyThreads) {
+                const int rw = b / R, r = b - rw * R;
+                dst[b] = (uint8_t)((s_mask[rw] >> r) & 1ull);
+            }
+        }
+    }
+
+    // ---- completion: the block that completes the chunks goes on
+    if (!single) {
+        if (lds_experts)
+            for (int e = tid; e < E; e += kNotifyThreads)
+                if (s_expert[e] != 0) atomicAdd(&f.acc_expert[e], s_expert[e]);
+        if (tid == 0) atomicAdd(&f.report[0], s_slots);
+        const int64_t left = Q - (int64_t)blockIdx.x * kNotifyWaves;
+        const uint32_t mine = (uint32_t)(left < kNotifyWaves ? left : kNotifyWaves);
+        if (!elect_completing_block(f.ticket, epoch0, mine, (uint32_t)Q, p.dev_status)) return;
+    } else {
+        __syncthreads();
+    }
+    // per-expert totals (checked against the valid slots the blocks reported)
+    uint32_t esum = 0;
+    for (int e = tid; e < E; e += kNotifyThreads) {
+        const int32_t v = (single && lds_experts) ? s_expert[e] : atomicExch(&f.acc_expert[e], 0);
+        f.per_expert[e] = v;
+        esum += (uint32_t)v;
+    }
+    const int w_e = wave_sum((int)esum);
+    if (lane == 0) atomicAdd(&s_esum, (uint32_t)w_e);
+    __syncthreads();  // per_expert and s_esum complete for the whole block
+    if (tid == 0) {
+        const uint32_t want = single ? s_slots : atomicExch(&f.report[0], 0u);
+        if (want != s_esum) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
+    }
+    const int64_t NC = p.R + p.nodes;
+    if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
+        finish_in_lds(p, tid, lane, wave);
+    else
+        finish_in_global(p, tid, lane, wave);
+}
+
 }  // namespace
+
+hipError_t launch_layout_notify(const ep_shape_t &s, const int64_t *topk_idx, int32_t *per_rank, int32_t *per_node,
+                                int32_t *per_expert, uint8_t *in_rank, int32_t *gbl, int32_t *rdma,
+                                int32_t *recv_gbl, int32_t *recv_rdma, int32_t *recv_per_expert, int32_t *num_recv,
+                                char *ws, int32_t *dev_status, hipStream_t stream) {
+    const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
+    NotifyParams p;
+    p.in_rank = in_rank;
+    p.per_rank = nullptr;
+    p.per_node = nullptr;
+    p.per_expert = per_expert;
+    p.gbl = gbl;
+    p.rdma = rdma;
+    p.recv_gbl = recv_gbl;
+    p.recv_rdma = recv_rdma;
+    p.recv_per_expert = recv_per_expert;
+    p.num_recv = num_recv;
+    p.mask = reinterpret_cast<uint64_t *>(ws + w.mask);
+    p.rank_off = reinterpret_cast<int32_t *>(ws + w.rank_off);
+    p.node_off = reinterpret_cast<int32_t *>(ws + w.node_off);
+    p.rank_part = reinterpret_cast<int32_t *>(ws + w.rank_part);
+    p.node_part = reinterpret_cast<int32_t *>(ws + w.node_part);
+    p.ticket = nullptr;
+    p.dev_status = dev_status;
+    p.T = s.num_tokens;
+    p.C = s.num_channels;
+    p.Tc = (p.T + p.C - 1) / p.C;
+    p.R = s.num_ranks;
+    p.E = s.num_experts;
+    p.nodes = num_nodes(p.R);
+    p.align = s.expert_alignment;
+    p.load_unit = 1;
+    p.fused = true;
+    p.tot_rank = per_rank;
+    p.tot_node = per_node;
+    FusedParams f;
+    f.topk_idx = topk_idx;
+    f.per_expert = per_expert;
+    f.in_rank = in_rank;
+    f.acc_expert = reinterpret_cast<int32_t *>(ws + w.acc) + p.R + p.nodes;
+    f.ticket = reinterpret_cast<uint64_t *>(reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketFused);
+    f.report = reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketFused + 2;
+    f.K = s.num_topk;
+    f.store_unit = 1;
+    if (p.R % 16 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 16 == 0)
+        f.store_unit = 16;
+    else if (p.R % 4 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 4 == 0)
+        f.store_unit = 4;
+    const int64_t Q = num_chunks(p.T);
+    const int64_t blocks = Q > 0 ? (Q + kNotifyWaves - 1) / kNotifyWaves : 1;
+    const size_t lds = p.E <= kFusedMaxLdsExperts ? sizeof(int32_t) * (size_t)p.E : 0;
+    hipLaunchKernelGGL(layout_notify_kernel, dim3((unsigned)blocks), dim3(kNotifyThreads), lds, stream, f, p);
+    return hipGetLastError();
+}
 
 hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int32_t *per_rank,
                          const int32_t *per_node, const int32_t *per_expert, int32_t *gbl, int32_t *rdma,
@@ -347,6 +568,8 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
     p.align = s.expert_alignment;
     const uintptr_t a = reinterpret_cast<uintptr_t>(in_rank);
     p.load_unit = (p.R % 16 == 0 && a % 16 == 0) ? 16 : (p.R % 8 == 0 && a % 8 == 0) ? 8 : 1;
+    p.fused = false;
+    p.tot_rank = p.tot_node = nullptr;
 
     const int64_t Q = num_chunks(p.T);
     // at least one block: the last (only) block also handles t = 0

@@ -22,7 +22,7 @@ EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEN
 EP_DEV_STALE_WORKSPACE = 16
 EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL = 0, 1, 2
 
-EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
+EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
             "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
@@ -54,6 +54,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_get_layout.argtypes = [_S, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P, _P]
     lib.ep_get_layout_noalloc.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P]
     lib.ep_notify.argtypes = [_S] + [_P] * 11 + [_P, ctypes.c_size_t, _P, _P]
+    lib.ep_layout_notify.argtypes = [_S] + [_P] * 13 + [ctypes.c_size_t, _P, _P]
     lib.ep_dispatch.argtypes = [_S, _P, _P, _P, _P, _P, _P, _P, ctypes.c_size_t, ctypes.c_int32] + [_P] * 5 + \
         [ctypes.c_int32, _P, _P]
     lib.ep_dispatch_fp8.argtypes = [_S, _P, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
@@ -65,7 +66,7 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
-    for name in ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
+    for name in ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
                  "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
@@ -150,6 +151,24 @@ def _ws(workspace):
     if workspace is None:
         return None, 0
     return _ptr(workspace), workspace.numel() * workspace.element_size()
+
+
+def ep_layout_notify(shape, topk_idx, num_tokens_per_rank, num_tokens_per_rdma_rank, num_tokens_per_expert,
+                     is_token_in_rank, gbl_channel_prefix_matrix, rdma_channel_prefix_matrix, recv_gbl_rank_prefix_sum,
+                     recv_rdma_rank_prefix_sum, num_recv_tokens_per_expert, num_recv_tokens, workspace,
+                     read_back: bool = False, dev_status=None, stream=None) -> int | None:
+    """ep_get_layout and ep_notify in one launch.  Returns N (host int) when ``read_back``
+    is set; the call then waits for the stream."""
+    host = ctypes.c_int32(-1)
+    _check(load().ep_layout_notify(ctypes.byref(shape), _ptr(topk_idx), _ptr(num_tokens_per_rank),
+                                   _ptr(num_tokens_per_rdma_rank), _ptr(num_tokens_per_expert),
+                                   _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
+                                   _ptr(rdma_channel_prefix_matrix), _ptr(recv_gbl_rank_prefix_sum),
+                                   _ptr(recv_rdma_rank_prefix_sum), _ptr(num_recv_tokens_per_expert),
+                                   _ptr(num_recv_tokens), ctypes.addressof(host) if read_back else None,
+                                   _ptr(workspace), workspace.numel() * workspace.element_size(), _ptr(dev_status),
+                                   _stream(stream)), "ep_layout_notify")
+    return int(host.value) if read_back else None
 
 
 def ep_dispatch(shape, x, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
@@ -280,6 +299,12 @@ def run_layout(b: Buffers, topk_idx, stream=None) -> None:
 def run_notify(b: Buffers, read_back: bool = False, stream=None) -> int | None:
     return ep_notify(b.shape, b.in_rank, b.per_rank, b.per_node, b.per_expert, b.gbl, b.rdma, b.recv_gbl,
                      b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, read_back, b.dev_status, stream)
+
+
+def run_layout_notify(b: Buffers, topk_idx, read_back: bool = False, stream=None) -> int | None:
+    return ep_layout_notify(b.shape, topk_idx, b.per_rank, b.per_node, b.per_expert, b.in_rank, b.gbl, b.rdma,
+                            b.recv_gbl, b.recv_rdma, b.recv_per_expert, b.num_recv, b.workspace, read_back,
+                            b.dev_status, stream)
 
 
 def run_dispatch(b: Buffers, x, topk_idx, topk_weights, use_workspace: bool = True, stream=None,

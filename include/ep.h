@@ -7,6 +7,7 @@
  *   ep_get_layout  topk_idx -> token counts per rank / node / expert, is_token_in_rank
  *   ep_notify      counts   -> channel prefix matrices, receive prefix sums,
  *                              aligned per-expert receive counts, N_recv
+ *   ep_layout_notify         -> both of the above in one launch
  *   ep_dispatch    x rows   -> receive region laid out [dst_rank][channel]
  *   ep_combine     expert outputs in receive layout -> weighted sum in token order
  * and beside them:
@@ -167,6 +168,24 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
                       int32_t *recv_gbl_rank_prefix_sum, int32_t *recv_rdma_rank_prefix_sum,
                       int32_t *num_recv_tokens_per_expert, int32_t *num_recv_tokens, int32_t *num_recv_tokens_host,
                       void *workspace, size_t workspace_bytes, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Stages 1+2 in one launch: ep_get_layout then ep_notify, from topk_idx to every output of
+ * both, with the same values bit for bit.  [the sources of both stages]  The token masks are
+ * built once and each 64-token chunk is counted from them in registers, so is_token_in_rank
+ * is written (it is an output) but not read back, and one completion election replaces two.
+ * Out: the four outputs of ep_get_layout and the seven of ep_notify (num_recv_tokens_host as
+ *      there: non-NULL makes the call wait for the stream).
+ * workspace: as for ep_notify (it is left as ep_notify leaves it, for ep_dispatch).
+ * dev_status (nullable): EP_DEV_BAD_TOPK_IDX, EP_DEV_STALE_WORKSPACE.
+ */
+ep_status_t ep_layout_notify(const ep_shape_t *s, const int64_t *topk_idx, int32_t *num_tokens_per_rank,
+                             int32_t *num_tokens_per_rdma_rank, int32_t *num_tokens_per_expert,
+                             uint8_t *is_token_in_rank, int32_t *gbl_channel_prefix_matrix,
+                             int32_t *rdma_channel_prefix_matrix, int32_t *recv_gbl_rank_prefix_sum,
+                             int32_t *recv_rdma_rank_prefix_sum, int32_t *num_recv_tokens_per_expert,
+                             int32_t *num_recv_tokens, int32_t *num_recv_tokens_host, void *workspace,
+                             size_t workspace_bytes, int32_t *dev_status, hipStream_t stream);
 
 /*
  * Stages 3+4, dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch (inputs

@@ -31,7 +31,8 @@ def declared_functions():
 
 
 def test_header_declares_the_boundary():
-    assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_dispatch",
+    assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify",
+                                          "ep_dispatch",
                                           "ep_dispatch_fp8",
                                           "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
                                           "ep_combine", "ep_workspace_bytes", "ep_status_string"])
@@ -87,6 +88,7 @@ def _call_all(ep, s):
     codes = [
         lib.ep_get_layout(ctypes.byref(s), p, p, p, p, p, p, 1 << 30, None, None),
         lib.ep_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
+        lib.ep_layout_notify(ctypes.byref(s), p, p, p, p, p, p, p, p, p, p, p, None, p, 1 << 30, None, None),
         lib.ep_dispatch(ctypes.byref(s), p, p, p, p, p, p, p, 1 << 30, 10, p, p, None, p, p, 0, None, None),
         lib.ep_combine(ctypes.byref(s), p, p, p, 10, p, None, None, None),
         lib.ep_dispatch_fp8(ctypes.byref(s), p, p, 4, p, p, p, p, p, p, 1 << 30, 10, p, p, p, None, p, p, 0,
@@ -99,12 +101,12 @@ def _call_all(ep, s):
 
 @pytest.mark.parametrize("name", sorted(BAD_SHAPES))
 def test_malformed_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 7
+    assert _call_all(ep, _shape(ep, **BAD_SHAPES[name])) == [ep.EP_ERR_INVALID_ARG] * 8
 
 
 @pytest.mark.parametrize("name", sorted(UNSUPPORTED))
 def test_unsupported_shapes_rejected(ep, name):
-    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 7
+    assert _call_all(ep, _shape(ep, **UNSUPPORTED[name])) == [ep.EP_ERR_UNSUPPORTED] * 8
 
 
 def test_null_and_misaligned_pointers_rejected(ep):
@@ -286,3 +288,21 @@ def test_dispatch_form_must_be_known(ep):
                                    None, None) == ep.EP_ERR_INVALID_ARG
         assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, form, None,
                                       None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_layout_notify_argument_checks(ep):
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    s = _shape(ep)
+
+    def call(idx=p, rank=p, gbl=p, n=p, ws=p, wsb=1 << 30, in_rank=p):
+        return lib.ep_layout_notify(ctypes.byref(s), idx, rank, p, p, in_rank, gbl, p, p, p, p, n, None, ws, wsb, None,
+                                    None)
+
+    assert call(idx=None) == ep.EP_ERR_INVALID_ARG
+    assert call(in_rank=None) == ep.EP_ERR_INVALID_ARG
+    assert call(rank=None) == ep.EP_ERR_INVALID_ARG
+    assert call(gbl=None) == ep.EP_ERR_INVALID_ARG
+    assert call(n=None) == ep.EP_ERR_INVALID_ARG
+    assert call(ws=None) == ep.EP_ERR_INVALID_ARG
+    assert call(wsb=16) == ep.EP_ERR_INVALID_ARG
