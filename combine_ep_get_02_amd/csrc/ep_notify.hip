@@ -338,14 +338,31 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
 }
 
 // ---------------------------------------------------------------- layout + notify in one launch
-// From topk_idx straight to every output of both stages.  Each thread builds its
-// token's rank mask from the topk ids (as the layout does), and each wave, its
-// 64 tokens being one chunk, counts the chunk from those masks in registers (as
-// notify does from is_token_in_rank): one pass over the tokens, one election.
-// The per-expert counts go through an LDS histogram and the running counts; the
-// per-rank and per-node totals are the scan's column totals.  The completing
-// block publishes the expert totals and then finishes as notify does.
+// From topk_idx straight to every output of both stages.  A block takes 256
+// tokens (four chunks), four lanes to a token: lane j of a quad reads the token's
+// ids j, j+4, ..., so a wave's loads cover 16 consecutive topk rows, and the
+// quad ORs its rank bits together (as the layout builds a mask).  Waves 0..3
+// then count one chunk each from the masks in LDS (as notify does from
+// is_token_in_rank): one pass over the tokens, one election.  Few waves per CU
+// keep the LDS histogram's atomics and the loads' address work spread over many
+// CUs.  The per-expert counts go through that histogram and the running counts;
+// the per-rank and per-node totals are the scan's column totals.  The completing
+// block publishes the expert totals and then finishes as notify does, with all
+// sixteen waves.
 constexpr int kFusedMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E counts in the workspace
+constexpr int kFusedChunks = 4;            // chunks per block
+constexpr int kFusedTokens = kFusedChunks * kChunk;
+static_assert(kFusedTokens * 4 == kNotifyThreads, "four lanes per token");
+
+// OR of a 64-bit value over the four lanes of each quad (two DPP quad permutations).
+__device__ __forceinline__ uint64_t quad_or64(uint64_t v) {
+    uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+    lo |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+    hi |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0xB1, 0xf, 0xf, false);
+    lo |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)lo, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+    hi |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)hi, 0x4E, 0xf, 0xf, false);
+    return ((uint64_t)hi << 32) | lo;
+}
 
 struct FusedParams {
     const int64_t *topk_idx;
@@ -358,7 +375,7 @@ struct FusedParams {
 };
 
 __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedParams f, NotifyParams p) {
-    __shared__ uint64_t s_mask[kNotifyThreads];
+    __shared__ uint64_t s_mask[kFusedTokens];
     __shared__ uint32_t s_slots, s_esum;
     extern __shared__ int32_t s_expert[];  // E entries when E <= kFusedMaxLdsExperts
     const int tid = threadIdx.x;
@@ -377,48 +394,51 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
         for (int e = tid; e < E; e += kNotifyThreads) s_expert[e] = 0;
     __syncthreads();
 
-    // ---- the token: rank mask, valid slots, expert counts
-    const int64_t t0 = (int64_t)blockIdx.x * kNotifyThreads;
-    const int64_t t = t0 + tid;
+    // ---- the token's slots part, part + 4, ...: rank bits, valid slots, expert counts
+    const int64_t t0 = (int64_t)blockIdx.x * kFusedTokens;
+    const int64_t t = t0 + (tid >> 2);
+    const int part = tid & 3;
     const int experts_per_rank = E / R;
     uint64_t mask = 0;
     int bad = 0, slots = 0;
     if (t < p.T) {
         const int64_t *row = f.topk_idx + t * K;
-        for (int j0 = 0; j0 < K; j0 += 8) {  // a batch's loads are in flight together
-            int64_t ev[8];
+        int64_t ev[kMaxTopk / 4];  // all of the lane's loads in flight together
 #pragma unroll
-            for (int u = 0; u < 8; ++u) ev[u] = j0 + u < K ? row[j0 + u] : -1;
+        for (int u = 0; u < kMaxTopk / 4; ++u) ev[u] = part + 4 * u < K ? row[part + 4 * u] : -1;
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                const int64_t e = ev[u];
-                if (e == -1) continue;
-                if (e < -1 || e >= E) {
-                    bad = 1;
-                    continue;
-                }
-                ++slots;
-                if (lds_experts)
-                    atomicAdd(&s_expert[(int)e], 1);
-                else
-                    atomicAdd(&f.acc_expert[(int)e], 1);
-                mask |= 1ull << ((int)e / experts_per_rank);
+        for (int u = 0; u < kMaxTopk / 4; ++u) {
+            const int64_t e = ev[u];
+            if (e == -1) continue;
+            if (e < -1 || e >= E) {
+                bad = 1;
+                continue;
             }
+            ++slots;
+            if (lds_experts)
+                atomicAdd(&s_expert[(int)e], 1);
+            else
+                atomicAdd(&f.acc_expert[(int)e], 1);
+            mask |= 1ull << ((int)e / experts_per_rank);
         }
     }
-    s_mask[tid] = mask;
-    // ---- the wave's chunk, from the masks in registers
-    const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
-    if (q < Q) count_chunk_masks(p, q, lane, mask);
+    mask = quad_or64(mask);  // every lane of the quad: the token's rank mask
+    if (part == 0) s_mask[tid >> 2] = mask;
     if (ballot64(bad != 0) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_TOPK_IDX);
     const int w_slots = wave_sum(slots);
     if (lane == 0) atomicAdd(&s_slots, (uint32_t)w_slots);
     __syncthreads();
 
+    // ---- the block's chunks, one wave each, from the masks in LDS
+    if (wave < kFusedChunks) {
+        const int64_t q = (int64_t)blockIdx.x * kFusedChunks + wave;
+        if (q < Q) count_chunk_masks(p, q, lane, s_mask[wave * kChunk + lane]);
+    }
+
     // ---- is_token_in_rank rows of this block: one contiguous range of nt*R bytes
     {
         const int64_t left = p.T - t0;
-        const int nt = (int)(left < kNotifyThreads ? (left > 0 ? left : 0) : kNotifyThreads);
+        const int nt = (int)(left < kFusedTokens ? (left > 0 ? left : 0) : kFusedTokens);
         const int nbytes = nt * R;
         uint8_t *dst = f.in_rank + t0 * R;
         if (f.store_unit == 16) {
@@ -453,8 +473,8 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
             for (int e = tid; e < E; e += kNotifyThreads)
                 if (s_expert[e] != 0) atomicAdd(&f.acc_expert[e], s_expert[e]);
         if (tid == 0) atomicAdd(&f.report[0], s_slots);
-        const int64_t left = Q - (int64_t)blockIdx.x * kNotifyWaves;
-        const uint32_t mine = (uint32_t)(left < kNotifyWaves ? left : kNotifyWaves);
+        const int64_t left = Q - (int64_t)blockIdx.x * kFusedChunks;
+        const uint32_t mine = (uint32_t)(left < kFusedChunks ? left : kFusedChunks);
         if (!elect_completing_block(f.ticket, epoch0, mine, (uint32_t)Q, p.dev_status)) return;
     } else {
         __syncthreads();
@@ -530,7 +550,7 @@ hipError_t launch_layout_notify(const ep_shape_t &s, const int64_t *topk_idx, in
     else if (p.R % 4 == 0 && reinterpret_cast<uintptr_t>(in_rank) % 4 == 0)
         f.store_unit = 4;
     const int64_t Q = num_chunks(p.T);
-    const int64_t blocks = Q > 0 ? (Q + kNotifyWaves - 1) / kNotifyWaves : 1;
+    const int64_t blocks = Q > 0 ? (Q + kFusedChunks - 1) / kFusedChunks : 1;
     const size_t lds = p.E <= kFusedMaxLdsExperts ? sizeof(int32_t) * (size_t)p.E : 0;
     hipLaunchKernelGGL(layout_notify_kernel, dim3((unsigned)blocks), dim3(kNotifyThreads), lds, stream, f, p);
     return hipGetLastError();

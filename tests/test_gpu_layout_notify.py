@@ -82,11 +82,14 @@ EDGES = {
     # name: (T, R, E, K, C, align, extra)
     "no_tokens": (0, 16, 64, 4, 8, 1, {}),
     "fewer_tokens_than_channels": (3, 8, 16, 2, 7, 1, {}),
-    "one_block": (1000, 16, 64, 6, 12, 4, {}),
+    "one_block": (200, 16, 64, 6, 12, 4, {}),
+    "few_blocks": (1000, 16, 64, 6, 12, 4, {}),
+    "one_block_k_odd": (256, 8, 40, 5, 3, 1, dict(mask_frac=0.1, bad=True)),
     "one_rank": (1500, 1, 4, 2, 3, 1, {}),
     "three_nodes": (2100, 24, 48, 4, 6, 1, dict(mask_frac=0.2, dup=True)),
     "experts_past_lds": (3000, 64, 16384, 8, 24, 1, {}),
-    "experts_past_lds_one_block": (700, 64, 16384, 8, 24, 1, {}),
+    "experts_past_lds_one_block": (250, 64, 16384, 8, 24, 1, {}),
+    "experts_past_lds_few_blocks": (700, 64, 16384, 8, 24, 1, {}),
     "global_scan": (100000, 64, 256, 8, 24, 1, {}),
     "many_channels": (5000, 16, 64, 4, 4096, 1, {}),
     "k32_bad_ids": (4100, 64, 128, 32, 9, 128, dict(dup=True, bad=True)),
