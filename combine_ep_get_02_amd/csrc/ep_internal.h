@@ -183,26 +183,65 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     return v;
 }
 
+// Value of v held by lane (lane ^ S), the whole wave active.  Inside a row of 16
+// lanes DPP does it: quad permutations for 1 and 2, and for 4 and 8 a mirror
+// (lane ^ 7 in each half row, lane ^ 15 in each row) followed by a second
+// permutation.  Across rows, gfx950's v_permlane16_swap run on (v, v) leaves
+// rows {0, 0, 2, 2} in its first result and rows {1, 1, 3, 3} in its second.
+template <int S>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+    if constexpr (S == 1) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);  // quad_perm [1,0,3,2]
+    } else if constexpr (S == 2) {
+        return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xf, 0xf, false);  // quad_perm [2,3,0,1]
+    } else if constexpr (S == 4) {
+        const int h = __builtin_amdgcn_mov_dpp((int)v, 0x141, 0xf, 0xf, false);  // row_half_mirror: ^ 7
+        return (uint32_t)__builtin_amdgcn_mov_dpp(h, 0x1B, 0xf, 0xf, false);    // quad_perm [3,2,1,0]: ^ 3
+    } else if constexpr (S == 8) {
+        const int m = __builtin_amdgcn_mov_dpp((int)v, 0x140, 0xf, 0xf, false);  // row_mirror: ^ 15
+        return (uint32_t)__builtin_amdgcn_mov_dpp(m, 0x141, 0xf, 0xf, false);   // row_half_mirror: ^ 7
+    } else {
+        static_assert(S == 16, "lane_xor: 1, 2, 4, 8 or 16");
+        const auto sw = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+        return (__lane_id() & 16) ? sw[0] : sw[1];
+    }
+}
+
+// One butterfly step of the transpose below at distance S < 32: each 32-bit half
+// trades its S-wide off-diagonal bit fields with the same half of lane ^ S.
+template <int S>
+__device__ __forceinline__ uint64_t transpose_step(uint64_t x, uint32_t keep) {
+    uint32_t lo = (uint32_t)x, hi = (uint32_t)(x >> 32);
+    const uint32_t ylo = lane_xor<S>(lo), yhi = lane_xor<S>(hi);
+    if ((__lane_id() & S) == 0) {
+        lo = (lo & keep) | ((ylo & keep) << S);
+        hi = (hi & keep) | ((yhi & keep) << S);
+    } else {
+        lo = (lo & ~keep) | ((ylo & ~keep) >> S);
+        hi = (hi & ~keep) | ((yhi & ~keep) >> S);
+    }
+    return ((uint64_t)hi << 32) | lo;
+}
+
 // Transpose of the 64x64 bit matrix whose row t is lane t's 64-bit value:
 // lane r receives column r, i.e. bit t of the result is bit r of lane t -- the
 // same as 64 ballots of "bit r is set", in six butterfly exchange steps (at
-// step s, rows t and t^s swap the s-wide off-diagonal sub-blocks).
+// step s, rows t and t^s swap the s-wide off-diagonal sub-blocks).  The step at
+// distance 32 is one v_permlane32_swap of (low half, high half): lanes 0..31
+// receive the low halves of lanes 32..63 as their new high halves, and lanes
+// 32..63 the high halves of lanes 0..31 as their new low halves.  No LDS
+// traffic; the whole wave must be active.
 __device__ __forceinline__ uint64_t transpose64(uint64_t x) {
-    const int lane = __lane_id();
-    constexpr uint64_t keep[6] = {0x00000000ffffffffull, 0x0000ffff0000ffffull, 0x00ff00ff00ff00ffull,
-                                  0x0f0f0f0f0f0f0f0full, 0x3333333333333333ull, 0x5555555555555555ull};
-#pragma unroll
-    for (int k = 0; k < 6; ++k) {
-        const int s = 32 >> k;
-        const uint32_t lo = __shfl_xor((unsigned)(uint32_t)x, s, kWave);
-        const uint32_t hi = __shfl_xor((unsigned)(uint32_t)(x >> 32), s, kWave);
-        const uint64_t y = ((uint64_t)hi << 32) | lo;
-        x = (lane & s) == 0 ? (x & keep[k]) | ((y & keep[k]) << s) : (x & ~keep[k]) | ((y & ~keep[k]) >> s);
-    }
+    const auto sw = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)(x >> 32), false, false);
+    x = ((uint64_t)sw[1] << 32) | sw[0];
+    x = transpose_step<16>(x, 0x0000ffffu);
+    x = transpose_step<8>(x, 0x00ff00ffu);
+    x = transpose_step<4>(x, 0x0f0f0f0fu);
+    x = transpose_step<2>(x, 0x33333333u);
+    x = transpose_step<1>(x, 0x55555555u);
     return x;
 }
 
-// byte i of the result = bit i of the low 4 bits of `nib` (a mask nibble as 0/1 bytes)
 __device__ __forceinline__ uint32_t spread4(uint32_t nib) {
     return (nib & 1u) | ((nib & 2u) << 7) | ((nib & 4u) << 14) | ((nib & 8u) << 21);
 }

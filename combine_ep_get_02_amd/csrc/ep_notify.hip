@@ -70,8 +70,10 @@ __device__ void count_chunk_masks(const NotifyParams &p, int64_t q, int lane, ui
     }
     if (lane < R) p.rank_off[q * R + lane] = __popcll(my_bits);
     if (lane < nodes) p.node_off[q * nodes + lane] = __popcll(my_node_bits);
-    // channels whose end lies strictly inside this chunk
-    for (int64_t c = first / p.Tc; c < p.C; ++c) {
+    // channels whose end lies strictly inside this chunk (the first channel
+    // that can end past `first` from a 32-bit division whenever T allows)
+    const int64_t c_first = p.T <= INT32_MAX ? (int64_t)((uint32_t)first / (uint32_t)p.Tc) : first / p.Tc;
+    for (int64_t c = c_first; c < p.C; ++c) {
         const int64_t end = (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
         if (end >= first + kChunk) break;
         if (end <= first) continue;
@@ -110,7 +112,9 @@ __device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
 // LDS capacity of the last block for the [Q][NC] counts plus the [C][NC]
 // partials; larger problems scan in global memory instead.
 constexpr int kScanLds = 12288;
-// rows of either matrix one thread loads: ceil(kScanLds / NC / (kNotifyThreads / NC)) for any NC <= 72
+// rows of either matrix one thread of the last block holds: within the LDS
+// capacity, ceil(Q / (threads / NC)) and ceil(C / (threads / NC)) stay at or
+// below 14 for any NC <= 146 (finish_fits_lds checks it all the same)
 constexpr int kPasses = 14;
 // per-expert counts a thread of the last block loads with the others (E <= 4096 in one go)
 constexpr int kExpertBatch = 4;
@@ -143,134 +147,185 @@ __device__ void finish_totals(const NotifyParams &p, const int32_t *tot, int lan
     recv_prefixes(p, per_rank, per_node, lane, wave);
 }
 
-// Last block, small problems: the counts, the partials and the per-rank / per-node
-// totals come into LDS in one round trip, are scanned there, and every output is
-// written from LDS.
-__device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave) {
-    __shared__ int32_t s_cnt[kScanLds];  // [Q+1][NC], then [C][NC] partials behind it
+// Whether the last block finishes in LDS: the [Q + 1][NC] offsets and the
+// [C][NC] partials fit, and every thread's share of rows fits its registers.
+__device__ __forceinline__ bool finish_fits_lds(const NotifyParams &p) {
+    const int64_t NC = p.R + p.nodes, Q = num_chunks(p.T);
+    if ((Q + 1) * NC + (int64_t)p.C * NC > kScanLds) return false;
+    const int64_t S = kNotifyThreads / NC;
+    return (Q + S - 1) / S <= kPasses && ((int64_t)p.C + S - 1) / S <= kPasses && NC <= kColBatch * kNotifyWaves;
+}
+
+// Last block, small problems.  Thread (seg, col) of the S = threads / NC
+// segments owns rows [seg * L, seg * L + L) of column col of the [Q][NC] count
+// matrix (NC = ranks + nodes, L = ceil(Q / S)) and the partial rows seg,
+// seg + S, ...: it loads them in one round trip and scans its rows in registers;
+// the segment totals are scanned per column in LDS (one wave per column); then
+// every thread writes its rows' offsets to the workspace and to LDS, and the
+// prefix matrices are read off LDS at the channel ends.  All indices fit 32 bits
+// (the LDS bound keeps T below 2^20).
+template <bool FUSED, class Mid>
+__device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave, Mid mid) {
+    __shared__ int32_t s_cnt[kScanLds];        // [Q+1][NC] offsets, then [C][NC] partials behind them
+    __shared__ int32_t s_seg[kNotifyThreads];  // [S][NC] segment totals, then their offsets
     __shared__ int32_t s_tot[kMaxRanks + kMaxRanks / kRanksPerNode];
-    // everything below fits kScanLds entries, so 32-bit indices suffice
     const int R = p.R, nodes = p.nodes, NC = R + nodes, C = p.C;
-    const int Q = (int)num_chunks(p.T);
+    const int T = (int)p.T, Tc = (int)p.Tc;
+    const int Q = (T + kChunk - 1) / kChunk;
     int32_t *s_part = s_cnt + (Q + 1) * NC;
-    // fixed (row, column) of this thread: rows advance by RP per pass
-    const int RP = kNotifyThreads / NC;
-    const int r0 = tid / NC, col = tid - r0 * NC;
-    const bool active = r0 < RP;
+    const int S = kNotifyThreads / NC;
+    const int L = (Q + S - 1) / S;
+    const int seg = tid / NC, col = tid - seg * NC;
+    const bool active = seg < S;
     const bool is_rank = col < R;
+    const int stride = is_rank ? R : nodes;
+    int32_t *off = is_rank ? p.rank_off + col : p.node_off + (col - R);
+    const int32_t *part = is_rank ? p.rank_part + col : p.node_part + (col - R);
+    const int q0 = seg * L;
+    const int rows = active ? (Q - q0 < L ? (Q - q0 > 0 ? Q - q0 : 0) : L) : 0;
 
-    // ---- one round trip of loads: at most kPasses rows per thread for each
-    // matrix (rows <= kScanLds / NC, RP = kNotifyThreads / NC), the per-rank,
-    // per-node and first per-expert counts, all issued before any is used
-    int32_t vq[kPasses], vc[kPasses], pe[kExpertBatch];
-    if (active) {
+    // ---- one round trip of loads, all issued before any is used: the thread's
+    // count rows, its partial rows (channels whose end lies inside a chunk; the
+    // others have none), and for notify the totals and per-expert counts.  The
+    // addresses walk by a fixed step, none computed from a loaded value; loads
+    // that only some lanes need are made by all at an index clamped into range,
+    // the rest of the lanes dropping the value where it is used (a load under a
+    // branch would be waited for where the branch joins).
+    int32_t v[kPasses], vp[kPasses], pe[kExpertBatch];
+    {
+        const int32_t *src = off + (ptrdiff_t)q0 * stride;
+        const int32_t *psrc = part + (ptrdiff_t)seg * stride;
+        const ptrdiff_t pstep = (ptrdiff_t)S * stride;
 #pragma unroll
         for (int k = 0; k < kPasses; ++k) {
-            const int q = r0 + k * RP;
-            vq[k] = q < Q ? (is_rank ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)]) : 0;
-            const int c = r0 + k * RP;
-            vc[k] = (c < C && (channel_end(p, c) % kChunk) != 0)
-                        ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
-                        : 0;
+            v[k] = k < rows ? *src : 0;
+            src += stride;
+            const int c = seg + k * S;
+            const int end = (c + 1) * Tc < T ? (c + 1) * Tc : T;
+            vp[k] = (active && c < C && end % kChunk != 0) ? *psrc : 0;
+            psrc += pstep;
         }
     }
-    const int32_t per_rank = (!p.fused && lane < R) ? p.per_rank[lane] : 0;
-    const int32_t per_node = (!p.fused && lane < nodes) ? p.per_node[lane] : 0;
+    int32_t per_rank = 0, per_node = 0;
+    if constexpr (!FUSED) {
+        per_rank = p.per_rank[lane < R ? lane : 0];
+        per_node = p.per_node[lane < nodes ? lane : 0];
 #pragma unroll
-    for (int k = 0; k < kExpertBatch; ++k) {
-        const int e = tid + k * kNotifyThreads;
-        pe[k] = e < p.E ? p.per_expert[e] : 0;
-    }
-    if (active) {
-#pragma unroll
-        for (int k = 0; k < kPasses; ++k) {
-            const int q = r0 + k * RP;
-            if (q < Q) s_cnt[q * NC + col] = vq[k];
-            const int c = r0 + k * RP;
-            if (c < C) s_part[c * NC + col] = vc[k];
+        for (int k = 0; k < kExpertBatch; ++k) {
+            const int e = tid + k * kNotifyThreads;
+            pe[k] = p.per_expert[e < p.E ? e : 0];
         }
-        // rows beyond kPasses passes (none within the LDS size limit)
-        for (int q = r0 + kPasses * RP; q < Q; q += RP)
-            s_cnt[q * NC + col] = is_rank ? p.rank_off[q * R + col] : p.node_off[q * nodes + (col - R)];
-        for (int c = r0 + kPasses * RP; c < C; c += RP)
-            s_part[c * NC + col] = (channel_end(p, c) % kChunk) != 0
-                                       ? (is_rank ? p.rank_part[c * R + col] : p.node_part[c * nodes + (col - R)])
-                                       : 0;
     }
-    // aligned per-expert counts need nothing from the scan
-    auto aligned = [&](int32_t n) { return (int32_t)(((int64_t)n + p.align - 1) / p.align * p.align); };
+    mid();  // the caller's work that waits on its own memory round trip, overlapped with these loads
+
+    // ---- the segment in registers: v[k] becomes row q0 + k's offset inside it
+    int32_t run = 0;
 #pragma unroll
-    for (int k = 0; k < kExpertBatch; ++k) {
-        const int e = tid + k * kNotifyThreads;
-        if (e < p.E) p.recv_per_expert[e] = aligned(pe[k]);
+    for (int k = 0; k < kPasses; ++k) {
+        const int32_t x = v[k];
+        v[k] = run;
+        run += x;
     }
-    for (int e = tid + kExpertBatch * kNotifyThreads; e < p.E; e += kNotifyThreads)
-        p.recv_per_expert[e] = aligned(p.per_expert[e]);
+    if (active) s_seg[seg * NC + col] = run;
+#pragma unroll
+    for (int k = 0; k < kPasses; ++k) {
+        const int c = seg + k * S;
+        if (active && c < C) s_part[c * NC + col] = vp[k];
+    }
+    if constexpr (!FUSED) {  // aligned per-expert counts need nothing from the scan
+        per_rank = lane < R ? per_rank : 0;
+        per_node = lane < nodes ? per_node : 0;
+        auto aligned = [&](int32_t n) { return (int32_t)(((int64_t)n + p.align - 1) / p.align * p.align); };
+#pragma unroll
+        for (int k = 0; k < kExpertBatch; ++k) {
+            const int e = tid + k * kNotifyThreads;
+            if (e < p.E) p.recv_per_expert[e] = aligned(pe[k]);
+        }
+        for (int e = tid + kExpertBatch * kNotifyThreads; e < p.E; e += kNotifyThreads)
+            p.recv_per_expert[e] = aligned(p.per_expert[e]);
+    }
     __syncthreads();
 
-    // ---- scans: one wave per column, lanes over runs of chunks; a wave's
-    // columns (up to kColBatch) are read together so their LDS loads overlap
-    const int per = (Q + kWave - 1) / kWave;
-    const int b = lane * per;
-    const int e = (b + per) < Q ? (b + per) : Q;
-    for (int c0 = wave; c0 < NC; c0 += kNotifyWaves * kColBatch) {
-        int32_t sum[kColBatch];
+    // ---- segment offsets, one wave per column (lanes over segments); the
+    // column totals go to s_tot
+    if (S <= kWave) {
+        int32_t x[kColBatch];
 #pragma unroll
         for (int k = 0; k < kColBatch; ++k) {
-            const int cc = c0 + k * kNotifyWaves;
-            sum[k] = 0;
-            if (cc < NC)
-                for (int q = b; q < e; ++q) sum[k] += s_cnt[q * NC + cc];
+            const int cc = wave + k * kNotifyWaves;
+            x[k] = (lane < S && cc < NC) ? s_seg[lane * NC + cc] : 0;
         }
 #pragma unroll
         for (int k = 0; k < kColBatch; ++k) {
-            const int cc = c0 + k * kNotifyWaves;  // the same for the whole wave
+            const int cc = wave + k * kNotifyWaves;  // the same for the whole wave
             if (cc >= NC) break;
-            const int32_t incl = wave_inclusive_scan(sum[k]);
-            int32_t run = incl - sum[k];
-            for (int q = b; q < e; ++q) {
-                const int32_t v = s_cnt[q * NC + cc];
-                s_cnt[q * NC + cc] = run;
-                run += v;
+            const int32_t incl = wave_inclusive_scan(x[k]);
+            if (lane < S) s_seg[lane * NC + cc] = incl - x[k];
+            if (lane == kWave - 1) s_tot[cc] = incl;
+        }
+    } else {  // NC < 16: up to 8 segments a lane, at most one column a wave
+        const int per = (S + kWave - 1) / kWave;
+        const int b = lane * per, e = b + per < S ? b + per : S;
+        for (int cc = wave; cc < NC; cc += kNotifyWaves) {
+            int32_t sum = 0;
+            for (int g = b; g < e; ++g) sum += s_seg[g * NC + cc];
+            const int32_t incl = wave_inclusive_scan(sum);
+            int32_t r2 = incl - sum;
+            for (int g = b; g < e; ++g) {
+                const int32_t x = s_seg[g * NC + cc];
+                s_seg[g * NC + cc] = r2;
+                r2 += x;
             }
-            const int32_t total = readlane32(incl, kWave - 1);
-            if (lane == 0) {
-                s_cnt[Q * NC + cc] = total;
-                s_tot[cc] = total;
-            }
+            if (lane == kWave - 1) s_tot[cc] = incl;
         }
     }
-    // receive prefix sums over destination ranks and nodes (inclusive); fused, from
-    // the scan's totals once every column is done
-    if (!p.fused) recv_prefixes(p, per_rank, per_node, lane, wave);
     __syncthreads();
-    if (p.fused) finish_totals(p, s_tot, lane, wave);
 
-    // ---- outputs
-    if (!p.fused && wave == kNotifyWaves - 3) {
-        const bool bad = (lane < R && s_tot[lane] != per_rank) || (lane < nodes && s_tot[R + lane] != per_node);
-        if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
-    }
+    // ---- every row's offset: to the workspace (dispatch reads it) and to LDS;
+    // row Q holds the column totals
     if (active) {
-        for (int q = r0; q <= Q; q += RP) {
-            if (is_rank)
-                p.rank_off[q * R + col] = s_cnt[q * NC + col];
-            else
-                p.node_off[q * nodes + (col - R)] = s_cnt[q * NC + col];
+        const int32_t base = s_seg[seg * NC + col];
+#pragma unroll
+        for (int k = 0; k < kPasses; ++k) {
+            if (k < rows) {
+                const int32_t o = base + v[k];
+                off[(q0 + k) * stride] = o;
+                s_cnt[(q0 + k) * NC + col] = o;
+            }
         }
-        for (int c = r0; c < C; c += RP) {
-            const int qe = (int)(channel_end(p, c) / kChunk);
-            const int32_t v = s_cnt[qe * NC + col] + s_part[c * NC + col];
-            if (is_rank)
-                p.gbl[col * C + c] = v;
-            else
-                p.rdma[(col - R) * C + c] = v;
+        if (seg == 0) {
+            off[Q * stride] = s_tot[col];
+            s_cnt[Q * NC + col] = s_tot[col];
+        }
+    }
+    // receive prefix sums over destination ranks and nodes (inclusive): fused,
+    // from the scan's totals; notify, from its inputs, checked against the totals
+    if constexpr (FUSED) {
+        finish_totals(p, s_tot, lane, wave);
+    } else {
+        recv_prefixes(p, per_rank, per_node, lane, wave);
+        if (wave == kNotifyWaves - 3) {
+            const bool bad = (lane < R && s_tot[lane] != per_rank) || (lane < nodes && s_tot[R + lane] != per_node);
+            if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+        }
+    }
+    __syncthreads();
+
+    // ---- the prefix matrices: at channel c's end, the offset of the chunk it
+    // ends in plus the chunk's tokens before the end
+    if (active) {
+        int32_t *dst = is_rank ? p.gbl + col * C : p.rdma + (col - R) * C;
+        for (int c = seg; c < C; c += S) {
+            const int end = (c + 1) * Tc < T ? (c + 1) * Tc : T;
+            dst[c] = s_cnt[(end / kChunk) * NC + col] + s_part[c * NC + col];
         }
     }
 }
 
 // Last block, large problems: the same steps on the workspace in global memory.
-__device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int wave) {
+template <class Mid>
+__device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int wave, Mid mid) {
+    mid();
     __shared__ int32_t s_tot_g[kMaxRanks + kMaxRanks / kRanksPerNode];
     const int R = p.R, nodes = p.nodes, NC = R + nodes;
     const int64_t Q = num_chunks(p.T);
@@ -287,10 +342,11 @@ __device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int w
     }
     if (!p.fused)
         recv_prefixes(p, lane < R ? p.per_rank[lane] : 0, lane < nodes ? p.per_node[lane] : 0, lane, wave);
-    for (int e = tid; e < p.E; e += kNotifyThreads) {
-        const int64_t n = p.per_expert[e];
-        p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
-    }
+    if (!p.fused)  // fused, the expert totals' loop writes them
+        for (int e = tid; e < p.E; e += kNotifyThreads) {
+            const int64_t n = p.per_expert[e];
+            p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
+        }
     __syncthreads();  // scanned offsets visible to the whole block
     if (p.fused) finish_totals(p, s_tot_g, lane, wave);
     for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
@@ -330,11 +386,10 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
         const uint32_t mine = (uint32_t)(left < kNotifyWaves ? left : kNotifyWaves);
         if (!elect_completing_block(p.ticket, epoch0, mine, (uint32_t)Q, p.dev_status)) return;
     }
-    const int64_t NC = p.R + p.nodes;
-    if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
-        finish_in_lds(p, tid, lane, wave);
+    if (finish_fits_lds(p))
+        finish_in_lds<false>(p, tid, lane, wave, [] {});
     else
-        finish_in_global(p, tid, lane, wave);
+        finish_in_global(p, tid, lane, wave, [] {});
 }
 
 // ---------------------------------------------------------------- layout + notify in one launch
@@ -479,25 +534,54 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
     } else {
         __syncthreads();
     }
-    // per-expert totals (checked against the valid slots the blocks reported)
-    uint32_t esum = 0;
-    for (int e = tid; e < E; e += kNotifyThreads) {
-        const int32_t v = (single && lds_experts) ? s_expert[e] : atomicExch(&f.acc_expert[e], 0);
-        f.per_expert[e] = v;
-        esum += (uint32_t)v;
+    // The slots the blocks reported and the first per-expert running counts are
+    // read now; their values are used only once the finish's loads are in flight
+    // (the per-expert totals and their aligned counts, in `mid`) and at the end
+    // (the valid-slot check), so all of them share one round trip.  Every block
+    // has made its last addition to them before the election, so the elected
+    // block reads them (agent-scope loads) and clears them (agent-scope stores)
+    // alone.  Every lane makes the loads, at indices clamped into range.
+    const bool from_lds = single && lds_experts;
+    const uint32_t reported = single ? s_slots : __hip_atomic_load(f.report, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t ev[kExpertBatch];
+#pragma unroll
+    for (int k = 0; k < kExpertBatch; ++k) {
+        const int e = tid + k * kNotifyThreads;
+        const int ec = e < E ? e : 0;
+        ev[k] = from_lds ? s_expert[ec] : __hip_atomic_load(&f.acc_expert[ec], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    const int w_e = wave_sum((int)esum);
-    if (lane == 0) atomicAdd(&s_esum, (uint32_t)w_e);
-    __syncthreads();  // per_expert and s_esum complete for the whole block
-    if (tid == 0) {
-        const uint32_t want = single ? s_slots : atomicExch(&f.report[0], 0u);
-        if (want != s_esum) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
-    }
-    const int64_t NC = p.R + p.nodes;
-    if ((Q + 1) * NC + (int64_t)p.C * NC <= kScanLds)
-        finish_in_lds(p, tid, lane, wave);
+    auto mid = [&] {
+        auto publish = [&](int e, int32_t v) {
+            f.per_expert[e] = v;
+            p.recv_per_expert[e] = (int32_t)(((int64_t)v + p.align - 1) / p.align * p.align);
+            if (!from_lds) __hip_atomic_store(&f.acc_expert[e], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        };
+        uint32_t esum = 0;
+#pragma unroll
+        for (int k = 0; k < kExpertBatch; ++k) {
+            const int e = tid + k * kNotifyThreads;
+            if (e < E) {
+                publish(e, ev[k]);
+                esum += (uint32_t)ev[k];
+            }
+        }
+        for (int e = tid + kExpertBatch * kNotifyThreads; e < E; e += kNotifyThreads) {
+            const int32_t v = from_lds ? s_expert[e] : atomicExch(&f.acc_expert[e], 0);
+            publish(e, v);
+            esum += (uint32_t)v;
+        }
+        const int w_e = wave_sum((int)esum);
+        if (lane == 0) atomicAdd(&s_esum, (uint32_t)w_e);
+    };
+    if (finish_fits_lds(p))
+        finish_in_lds<true>(p, tid, lane, wave, mid);
     else
-        finish_in_global(p, tid, lane, wave);
+        finish_in_global(p, tid, lane, wave, mid);
+    // every wave added its expert sum before the finish's first barrier
+    if (tid == 0) {
+        if (!single) __hip_atomic_store(f.report, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (reported != s_esum) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
+    }
 }
 
 }  // namespace
