@@ -1,8 +1,10 @@
 """Benchmark of the expert-parallel dispatch/combine core on one MI355X.
 
-One step = the whole path on one batch: ep_get_layout, ep_notify, ep_dispatch,
-ep_combine (identity experts: combine reads dispatch's receive rows), all on
-torch's current stream, inputs already resident in HBM.  The default workload
+One step = the whole path on one batch: ep_layout_notify (the layout and notify
+stages in one launch), ep_dispatch, ep_combine (identity experts: combine reads
+dispatch's receive rows), all on torch's current stream, inputs already resident
+in HBM.  The two-launch form of the first stages (ep_get_layout, then ep_notify)
+is timed beside it.  The default workload
 is the prefill one: 4096 tokens, hidden 7168 bf16, top-8 of 256 experts over 64
 emulated ranks (8 nodes x 8), 24 channels, seed 0.
 
@@ -83,7 +85,7 @@ def layout_notify_bytes(T, K, R, E, C) -> int:
 PROFILE = os.path.join(ROOT, "profiles", "ep_kernels_prefill_hbm_bytes.txt")
 KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_pull_kernel_fp8": ["ep_dispatch.hip", "ep_internal.h"],
-                  "dispatch_cached_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
                   "dispatch_grouped_kernels": ["ep_dispatch.hip", "ep_group.hip", "ep_internal.h"],
@@ -258,6 +260,7 @@ def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) ->
         del probe
         b = ep.allocate(shape, n)
         calls = {"layout": lambda: ep.run_layout(b, idx), "notify": lambda: ep.run_notify(b),
+                 "layout_notify": lambda: ep.run_layout_notify(b, idx),
                  "dispatch": lambda: ep.run_dispatch(b, x, idx, w), "combine": lambda: ep.run_combine(b)}
         for f in calls.values():
             f()
@@ -266,8 +269,8 @@ def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) ->
         # the whole step from a HIP graph: no host launch cost between the kernels
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            for f in calls.values():
-                f()
+            for k in ("layout_notify", "dispatch", "combine"):
+                calls[k]()
         graph_us = timer.mean_us(graph.replay, brackets * per)
         db, cb = dispatch_bytes(T, H, K, R, n), combine_bytes(T, H, K, R, n)
         live = b.in_rank.bool().any(1)
@@ -278,6 +281,7 @@ def time_workloads(ep, inputs, names, timer, brackets: int = 5, per: int = 4) ->
             "us_dispatch_median": round(med["dispatch"], 2), "us_dispatch_min": round(t["dispatch"][0], 2),
             "us_combine_median": round(med["combine"], 2), "us_combine_min": round(t["combine"][0], 2),
             "us_layout_median": round(med["layout"], 2), "us_notify_median": round(med["notify"], 2),
+            "us_layout_notify_median": round(med["layout_notify"], 2),
             "us_step_graph": round(graph_us, 2),
             "GB/s_dispatch_plus_combine": round((db + cb) / (med["dispatch"] + med["combine"]) / 1e3, 2),
             "pct_peak": round(100 * (db + cb) / (med["dispatch"] + med["combine"]) / 1e3 / HBM_PEAK_GBPS, 2),
@@ -363,7 +367,7 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
         and not bool(g.grouped_x[~entries].view(torch.int16).any().item()))
     out["group_by_expert"]["grouped_rows"] = M
     del g
-    for key, kernel in (("dispatch_cached_bf16", "dispatch_cached_pull_kernel"), ("dispatch_fp8", "dispatch_pull_kernel_fp8"),
+    for key, kernel in (("dispatch_cached_bf16", "dispatch_kernel_cached_bf16"), ("dispatch_fp8", "dispatch_pull_kernel_fp8"),
                         ("dispatch_cached_fp8", "dispatch_kernel_cached_fp8")):
         out[key]["traffic"] = measured_traffic(kernel, wl.name)
     out["group_by_expert"]["traffic"] = measured_traffic("group_kernels", wl.name)
@@ -445,11 +449,11 @@ def main() -> int:
 
     timer = HipEvents()
     calls = {"layout": lambda: ep.run_layout(b, idx), "notify": lambda: ep.run_notify(b),
+             "layout_notify": lambda: ep.run_layout_notify(b, idx),
              "dispatch": lambda: ep.run_dispatch(b, x, idx, w), "combine": lambda: ep.run_combine(b)}
 
     def step(ev=None):
-        calls["layout"]()
-        calls["notify"]()
+        calls["layout_notify"]()
         if ev is not None:
             timer.record(ev[0])
         calls["dispatch"]()
@@ -498,7 +502,7 @@ def main() -> int:
         wall = (time.perf_counter() - w0) / args.steps
         graph = {"us_per_step_gpu": round(timer.elapsed_us(ga, gc) / args.steps, 2),
                  "ms_per_step_wall": round(wall * 1e3, 4),
-                 "note": "layout+notify+dispatch+combine captured with torch.cuda.graph, K replays back to back"}
+                 "note": "layout_notify+dispatch+combine captured with torch.cuda.graph, K replays back to back"}
 
     # correctness guard on the measured buffers: identity experts return x
     live = b.in_rank.bool().any(1)
@@ -510,8 +514,7 @@ def main() -> int:
         scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
         cev = [(timer.pair(), timer.pair()) for _ in range(args.cold_steps)]
         for (d0, d1), (c0, c1) in cev:
-            calls["layout"]()
-            calls["notify"]()
+            calls["layout_notify"]()
             scratch.fill_(7)
             timer.record(d0)
             calls["dispatch"]()
@@ -524,8 +527,7 @@ def main() -> int:
         # the push form, which a caller takes when x is only in HBM
         pev = [timer.pair() for _ in range(args.cold_steps)]
         for p0, p1 in pev:
-            calls["layout"]()
-            calls["notify"]()
+            calls["layout_notify"]()
             scratch.fill_(7)
             timer.record(p0)
             ep.run_dispatch(b, x, idx, w, form=ep.EP_FORM_PUSH)
@@ -536,8 +538,7 @@ def main() -> int:
         xs = x.clone()
         fev = [timer.pair() for _ in range(args.cold_steps)]
         for f0, f1 in fev:
-            calls["layout"]()
-            calls["notify"]()
+            calls["layout_notify"]()
             scratch.fill_(7)
             x.copy_(xs)
             timer.record(f0)
@@ -597,6 +598,7 @@ def main() -> int:
         "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "us_layout": round(us["layout"], 2),
         "us_notify": round(us["notify"], 2),
+        "us_layout_notify": round(us["layout_notify"], 2),
         "us_dispatch": round(us["dispatch"], 2),
         "us_combine": round(us["combine"], 2),
         "timing": "value: dispatch+combine bytes / mean time between one event pair per timed step around "

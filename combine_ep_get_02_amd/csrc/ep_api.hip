@@ -244,7 +244,7 @@ ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_
     const int64_t row_bytes = (int64_t)s->hidden * elem_bytes;
     if (row_bytes % 16 != 0 || recv_capacity < 0 || !form_ok(form)) return EP_ERR_INVALID_ARG;
     if (num_scales < 0) return EP_ERR_INVALID_ARG;
-    if (num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
+    if (num_scales > kMaxScales || form == EP_FORM_PULL) return EP_ERR_UNSUPPORTED;  // cached mode: push form only
     if (s->num_tokens == 0) return EP_OK;
     if (x == nullptr || send_slot == nullptr) return EP_ERR_INVALID_ARG;
     if (recv_capacity > 0 && recv_x == nullptr) return EP_ERR_INVALID_ARG;

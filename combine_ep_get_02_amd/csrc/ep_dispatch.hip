@@ -50,7 +50,8 @@ struct DispatchParams {
     const int32_t *gbl;      // [R][C] channel prefix matrix (inclusive)
     const int32_t *recv_gbl;
     const uint64_t *mask;    // workspace: per-token rank masks, or null (derive)
-    const int32_t *rank_off; // workspace: per-chunk row offsets inside each slab, or null (derive)
+    const int32_t *rank_off;  // workspace: per-chunk row offsets inside each chunk's group, or null (derive)
+    const int32_t *rank_base; // workspace: per-group row offsets inside each slab (a chunk starts at the sum)
     const int32_t *cached_slot;
     u32x4 *recv_x;
     float *recv_scales;
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
             colq[0] = transpose64(m);
             off = derive_offset<1>(p, a, colq, lane);
         } else if (lane < R) {
-            off = p.rank_off[q * R + lane];
+            off = p.rank_base[(q / kGroupChunks) * R + lane] + p.rank_off[q * R + lane];
         }
         const int base = lane < R ? slab0 + off : 0;
         if (live && seg == 0 && lane < p.K) {
@@ -419,7 +420,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
         }
         const int slab0 = (lane < R && lane > 0) ? p.recv_gbl[lane - 1] : 0;
         int off0 = 0;  // lane r: the group's offset inside slab r
-        if (!DERIVE && lane < R) off0 = p.rank_off[q0 * R + lane];
+        if (!DERIVE && lane < R) off0 = p.rank_base[(q0 / kGroupChunks) * R + lane] + p.rank_off[q0 * R + lane];
         // lane r: bit l of col[c] set when token (q0 + c)*64 + l goes to rank r
         uint64_t col[CPG];
         int n = 0;
@@ -597,146 +598,6 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
     }
 }
 
-// Cached mode, pull form (many tokens, rows of 14 KiB and more): the rows a
-// recorded send_slot names, written in receive order as by dispatch_pull_kernel.
-// For every 128-token group, every block of the owning XCD stages the group's
-// send_slot rows in LDS (read coalesced and validated), and one wave ballot per
-// (chunk, rank) gives the rank's column of the chunk's tokens.  A task then finds
-// its rank and token as in the pull form and takes its row from the staged entry
-// itself: any map is copied exactly, and a map written by dispatch (a rank's
-// rows consecutive in token order) is written as one advancing window per XCD.
-// The scales follow the group's rows in a pass of their own over the staged
-// entries.  Narrower rows stay on the push form: the staging costs each block a
-// 32 KiB read and two barriers per group, which 7 KiB rows do not repay.
-constexpr int kCachedWaves = 16;
-constexpr int kCachedBlocksPerXcd = 32;  // one block per CU
-constexpr int kCachedTokens = 2 * kChunk;
-
-template <bool EXACT>
-__global__ __launch_bounds__(kCachedWaves *kWave) void dispatch_cached_pull_kernel(DispatchParams p) {
-    constexpr int NT = kCachedWaves * kWave;
-    constexpr int GT = kCachedTokens;
-    constexpr int SR = kMaxRanks + 1;         // staged row stride (padded against bank conflicts)
-    constexpr int PER = GT * kMaxRanks / NT;  // staged entries per thread
-    __shared__ int32_t s_slot[GT * SR];
-    __shared__ uint64_t s_col[2][kMaxRanks];
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int xcd = (int)(blockIdx.x % kXcds);
-    const int W = (int)(gridDim.x / kXcds) * kCachedWaves;  // waves per XCD; the grid is a multiple of kXcds
-    const int wx = (int)(blockIdx.x / kXcds) * kCachedWaves + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    const int R = p.R;
-    const int64_t G = (p.T + GT - 1) / GT;
-    const int TPR = (int)((p.row_units + kWave - 1) / kWave);  // one 1 KiB piece per task
-    bool bad = false;
-
-    for (int64_t g = xcd; g < G; g += kXcds) {
-        // ---- stage: entry i = t * R + r of the group (its send_slot rows as they lie in memory)
-        const int64_t e0 = g * GT * R;
-        const int64_t e_end = p.T * R;
-        int v[PER];
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = tid + k * NT;
-            v[k] = -1;
-            if (i < GT * R && e0 + i < e_end) v[k] = p.cached_slot[e0 + i];
-        }
-#pragma unroll
-        for (int k = 0; k < PER; ++k) {
-            const int i = tid + k * NT;
-            if (i < GT * R) {
-                const int t = i / R, r = i - t * R;
-                int sl = v[k];
-                if (sl < -1 || sl >= p.cap) {
-                    bad = true;
-                    sl = -1;
-                }
-                s_slot[t * SR + r] = sl;
-            }
-        }
-        __syncthreads();
-        // column masks: wave w takes (chunk, rank) pairs w, w+16, ...; lane = token of the chunk
-        for (int cr = tid >> 6; cr < 2 * R; cr += kCachedWaves) {
-            const int c = cr / R, r = cr - c * R;
-            const uint64_t b = ballot64(s_slot[(c * kChunk + lane) * SR + r] >= 0);
-            if (lane == 0) s_col[c][r] = b;
-        }
-        __syncthreads();
-
-        // lane r: the group's tokens on rank r, and where the rank's run starts in the group's output
-        uint64_t col0 = 0, col1 = 0;
-        if (lane < R) {
-            col0 = s_col[0][lane];
-            col1 = s_col[1][lane];
-        }
-        const int n = __popcll(col0) + __popcll(col1);
-        const int incl = wave_inclusive_scan(n);
-        const int pex = lane < R ? incl - n : INT32_MAX;
-        const int tasks = readlane32(incl, kWave - 1) * TPR;
-        for (int base = 0; wx + base * W < tasks; base += kWave) {
-            int rt_row, rt_pack;  // lane i: task base + i: row; token in group | part << 8 | ok << 30
-            {
-                const int kk = wx + (base + lane) * W;
-                const bool valid = kk < tasks;
-                const int k = valid ? kk : wx + base * W;
-                const int rr = k / TPR, part = k - rr * TPR;
-                int r = 0;
-#pragma unroll
-                for (int step = 32; step >= 1; step >>= 1) {
-                    const int cand = r + step;
-                    if (__shfl(pex, cand, kWave) <= rr) r = cand;
-                }
-                const int o = rr - __shfl(pex, r, kWave);
-                const uint32_t a0 = __shfl((unsigned)(uint32_t)col0, r, kWave);
-                const uint32_t a1 = __shfl((unsigned)(uint32_t)(col0 >> 32), r, kWave);
-                const uint32_t b0 = __shfl((unsigned)(uint32_t)col1, r, kWave);
-                const uint32_t b1 = __shfl((unsigned)(uint32_t)(col1 >> 32), r, kWave);
-                const uint64_t c0 = ((uint64_t)a1 << 32) | a0, c1 = ((uint64_t)b1 << 32) | b0;
-                const int p0 = __popcll(c0);
-                const bool second = o >= p0;
-                const uint64_t cc = second ? c1 : c0;
-                const int oc = second ? o - p0 : o;
-                const bool found = oc < __popcll(cc);
-                const int tok = found ? (second ? kChunk : 0) + nth_set_bit(cc, oc) : 0;
-                const int row = found ? s_slot[tok * SR + r] : -1;
-                const bool ok = valid && row >= 0;
-                rt_row = ok ? row : 0;
-                rt_pack = tok | (part << 8) | ((int)ok << 30);
-            }
-            const int nb = (tasks - wx - base * W + W - 1) / W;  // tasks of this batch
-            const int nbatch = nb < kWave ? nb : kWave;
-            for (int j = 0; j < nbatch; ++j) {
-                const int pk = readlane32(rt_pack, j);
-                const int row = readlane32(rt_row, j);
-                const bool ok = (pk >> 30) != 0;
-                const int64_t t = g * GT + (pk & 0xff);
-                const int64_t first = (int64_t)((pk >> 8) & 0x3fffff) * kWave;
-                const int lim = (int)(p.row_units - first);
-                const int cu = (EXACT || lane < lim) ? lane : lim - 1;
-                const u32x4 vv = p.x[t * p.row_units + first + cu];
-                asm volatile("" ::: "memory");
-                if (ok && (EXACT || lane < lim)) __builtin_nontemporal_store(vv, p.recv_x + (int64_t)row * p.row_units + first + lane);
-            }
-        }
-        // ---- the scales: staged entry e = wx, wx + W, ... with a row, lanes over the token's scales
-        if (p.num_scales > 0) {
-            for (int e = wx; e < GT * R; e += W) {
-                const int t = e / R, r = e - t * R;
-                const int row = __builtin_amdgcn_readfirstlane(s_slot[t * SR + r]);
-                if (row < 0) continue;  // wave-uniform
-                const int64_t tok = g * GT + t;
-                for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
-                    const int i = i0 + lane;
-                    const float sc = i < p.num_scales ? p.x_scales[tok * p.num_scales + i] : 0.0f;
-                    if (i < p.num_scales) p.recv_scales[(int64_t)row * p.num_scales + i] = sc;
-                }
-            }
-        }
-        __syncthreads();  // every wave is done with the staged entries before the next group's
-    }
-    if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
-}
-
 template <int CPG, int U, bool EXACT, int WPB>
 hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
     const dim3 grid((unsigned)(kXcds * blocks_per_xcd)), block(WPB * kWave);
@@ -880,12 +741,13 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.gbl = a.gbl;
     p.recv_gbl = a.recv_gbl;
     p.mask = nullptr;
-    p.rank_off = nullptr;
+    p.rank_off = p.rank_base = nullptr;
     p.derive = a.ws == nullptr;
     if (a.ws != nullptr) {
         const Workspace w = workspace_layout(s.num_tokens, s.num_ranks, s.num_experts, s.num_channels, s.num_topk);
         p.mask = reinterpret_cast<const uint64_t *>(a.ws + w.mask);
         p.rank_off = reinterpret_cast<const int32_t *>(a.ws + w.rank_off);
+        p.rank_base = reinterpret_cast<const int32_t *>(a.ws + w.rank_base);
     }
     p.C = s.num_channels;
     p.Tc = ((int64_t)s.num_tokens + p.C - 1) / p.C;
@@ -917,18 +779,10 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
         p.num_scales = 0;  // no rows, so no scales beside them
         return run_meta(p, stream);
     }
-    if (a.form != EP_FORM_PUSH) {
+    // cached mode always takes the push form
+    if (a.form != EP_FORM_PUSH && p.cached_slot == nullptr) {
         const PullTiling pt = pull_tiling(p.row_units, p.T);
-        if (pt.cpg > 0 && p.cached_slot == nullptr) return run_pull_tiled(p, pt, stream);
-        // cached mode: the pull form for rows of 14 KiB and more
-        if (pt.cpg > 0 && p.row_units >= 14 * kWave) {
-            const dim3 grid((unsigned)(kXcds * kCachedBlocksPerXcd)), block(kCachedWaves * kWave);
-            if (p.row_units % kWave == 0)
-                hipLaunchKernelGGL(dispatch_cached_pull_kernel<true>, grid, block, 0, stream, p);
-            else
-                hipLaunchKernelGGL(dispatch_cached_pull_kernel<false>, grid, block, 0, stream, p);
-            return hipGetLastError();
-        }
+        if (pt.cpg > 0) return run_pull_tiled(p, pt, stream);
     }
     int vpl, wpb, gran;
     dispatch_tiling(p.row_units, p.T, &vpl, &wpb, &gran);

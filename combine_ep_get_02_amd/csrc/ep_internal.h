@@ -20,6 +20,10 @@ constexpr int kChunk = 64;            // tokens per routing chunk (one per lane)
 
 __host__ __device__ inline int num_nodes(int R) { return R / kRanksPerNode > 0 ? R / kRanksPerNode : 1; }
 __host__ __device__ inline int64_t num_chunks(int64_t T) { return (T + kChunk - 1) / kChunk; }
+// Chunks per offset group: a chunk's row offset inside a rank's slab is its
+// group's offset (rank_base) plus its offset inside the group (rank_off).
+constexpr int kGroupChunks = 4;
+__host__ __device__ inline int64_t num_groups(int64_t T) { return (num_chunks(T) + kGroupChunks - 1) / kGroupChunks; }
 
 // Workspace shared by the four stages.  All offsets 256-byte aligned.
 //   tickets   uint32 [64]           completion counters of the multi-block layout and
@@ -28,18 +32,23 @@ __host__ __device__ inline int64_t num_chunks(int64_t T) { return (T + kChunk - 
 //                                   the last block); zero between calls
 //   acc       int32  [R+nodes+E]    layout's running counts; zero between calls
 //   mask      uint64 [t]            bit r set when token t goes to rank r (notify -> dispatch)
-//   rank_off  int32  [Q+1][R]       per-chunk token counts, scanned in place into
-//                                   exclusive offsets inside each rank's slab; row Q
-//                                   holds the totals
-//   node_off  int32  [Q+1][nodes]   the same per node
-//   rank_part int32  [C][R]         tokens of rank r in [64*floor(end_c/64), end_c)
+//   rank_off  int32  [Q][R]         chunk q's row offset inside its group: tokens of
+//                                   rank r in the group's chunks before q
+//   rank_base int32  [G][R]         group g's token counts, scanned in place into the
+//                                   group's row offset inside each rank's slab
+//                                   (G = ceil(Q / kGroupChunks)); chunk q starts at
+//                                   rank_base[q / 4][r] + rank_off[q][r]
+//   node_base int32  [G][nodes]     the same per node
+//   rank_part int32  [C][R]         at channel c's end (when it falls in chunk
+//                                   q = end / 64 < Q): rank_off[q][r] plus the tokens
+//                                   of rank r in [64*q, end)
 //   node_part int32  [C][nodes]     the same per node
 //   tok_pos   int32  [t][k]         grouped position of every (token, slot), or -1
 //                                   (dispatch straight into the grouped layout only)
 // The tickets and acc must be zero before the first call; every layout/notify call
 // leaves them zero again.
 struct Workspace {
-    size_t tickets, acc, mask, rank_off, node_off, rank_part, node_part, tok_pos, total;
+    size_t tickets, acc, mask, rank_off, rank_base, node_base, rank_part, node_part, tok_pos, total;
 };
 // uint32 word offsets of the tickets (each a 64-bit ticket, see elect_completing_block)
 constexpr int kTicketLayout = 0;   // counts tokens; words 2..4: valid slots, (token, rank) and (token, node) pairs
@@ -50,14 +59,15 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline Workspace workspace_layout(int64_t T, int R, int E, int C, int K) {
     Workspace w;
-    const int64_t Q = num_chunks(T);
+    const int64_t Q = num_chunks(T), G = num_groups(T);
     const int nodes = num_nodes(R);
     size_t off = 0;
     w.tickets = off;   off = align256(off + sizeof(uint32_t) * 64);
     w.acc = off;       off = align256(off + sizeof(int32_t) * (size_t)(R + nodes + E));
     w.mask = off;      off = align256(off + sizeof(uint64_t) * (size_t)(T > 0 ? T : 1));
-    w.rank_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(Q + 1) * R);
-    w.node_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(Q + 1) * nodes);
+    w.rank_off = off;  off = align256(off + sizeof(int32_t) * (size_t)(Q > 0 ? Q : 1) * R);
+    w.rank_base = off; off = align256(off + sizeof(int32_t) * (size_t)(G > 0 ? G : 1) * R);
+    w.node_base = off; off = align256(off + sizeof(int32_t) * (size_t)(G > 0 ? G : 1) * nodes);
     w.rank_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * R);
     w.node_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * nodes);
     w.tok_pos = off;   off = align256(off + sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * (size_t)K);
@@ -301,9 +311,8 @@ __device__ __forceinline__ int wave_sum(int v) { return readlane32(wave_inclusiv
 
 // Completion ticket of a multi-block kernel: a 64-bit word in the workspace,
 // the count of work units done so far in the low half and an epoch in the high
-// half.  Thread 0 of every block reads the epoch when the block starts
-// (ticket_epoch) and hands it to elect_completing_block once the block's global
-// writes are done.
+// half.  Every block reads the epoch when it starts (ticket_epoch) and thread 0
+// hands it to elect_completing_block once the block's global writes are done.
 __device__ __forceinline__ uint32_t ticket_epoch(const uint64_t *ticket) {
     return (uint32_t)(__hip_atomic_load(ticket, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 32);
 }

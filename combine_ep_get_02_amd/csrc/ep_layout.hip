@@ -58,7 +58,9 @@ __global__ __launch_bounds__(kLayoutThreads) void layout_kernel(LayoutParams p) 
     const int R = p.R, E = p.E, K = p.K, nodes = p.nodes;
     const bool lds_experts = E <= kMaxLdsExperts;
     const bool single = gridDim.x == 1 && lds_experts;  // one block: no ticket, no running counts
-    const uint32_t epoch0 = (!single && tid == 0) ? ticket_epoch(p.ticket) : 0u;
+    // every lane reads the epoch (thread 0 uses it): a load under a branch would be
+    // waited for where the branch joins, before this wave issues its own loads
+    const uint32_t epoch0 = ticket_epoch(p.ticket);
     int32_t *acc_rank = p.acc, *acc_node = p.acc + R, *acc_expert = p.acc + R + nodes;
     for (int i = tid; i < R; i += kLayoutThreads) s_rank[i] = 0;
     for (int i = tid; i < nodes; i += kLayoutThreads) s_node[i] = 0;

@@ -13,22 +13,26 @@
 // Channel c owns tokens [c*Tc, min((c+1)*Tc, t)), Tc = ceil(t / C).
 //
 // Design (not the pages' one-SM-per-channel loop): one launch.  The token axis
-// is cut into 64-token chunks, one chunk per wave and one token per lane.
+// is cut into 64-token chunks, one chunk per wave and one token per lane, and
+// the chunks into groups of four.
 //   Every wave turns its lanes' is_token_in_rank rows into 64-bit rank masks
 //   (stored for dispatch); a 64x64 bit transpose across the wave hands lane r
 //   the chunk's column for rank r, whose popcount is the (chunk, rank) count.
-//   For each channel whose end falls inside the chunk it also stores the count
-//   of the chunk's tokens before that end.  Every value has one writer: no
-//   atomics.
+//   The four waves of a group trade their counts through LDS: each stores its
+//   chunk's offset inside the group, and for each channel whose end falls in
+//   its chunk the value there (that offset plus the chunk's tokens before the
+//   end); the group's last chunk stores the group's totals.  Every value has
+//   one writer: no atomics.
 //   The last block to finish (the only one, without an election, up to 1024
-//   tokens) then scans: it brings the counts, the partials and the per-rank
-//   totals into LDS in one round trip (or works in the
-//   workspace when they do not fit), one wave per column (rank or node), each
-//   lane summing a run of chunks and a wave-wide shuffle scan combining the
-//   runs, which turns the counts into exclusive row offsets inside each rank's
-//   slab (what dispatch needs).  A channel's prefix is the offset of the chunk
-//   holding its end plus the partial count stored for it.  The receive
-//   prefixes over ranks and nodes are one wave scan each.
+//   tokens) then scans only the group totals: it brings them into LDS in one
+//   round trip (or works in the workspace when they do not fit), each thread
+//   scanning a run of groups of one column (rank or node) in registers and one
+//   wave per column combining the runs with a shuffle scan, which gives each
+//   group's row offset inside each rank's slab.  A chunk's offset (what
+//   dispatch needs) is its group's offset plus its offset inside the group; a
+//   channel's prefix is the offset of the group holding its end plus the value
+//   stored for it.  The receive prefixes over ranks and nodes are one wave scan
+//   each.
 #include "ep_internal.h"
 
 namespace ep {
@@ -42,7 +46,7 @@ struct NotifyParams {
     const int32_t *per_rank, *per_node, *per_expert;
     int32_t *gbl, *rdma, *recv_gbl, *recv_rdma, *recv_per_expert, *num_recv;
     uint64_t *mask;
-    int32_t *rank_off, *node_off, *rank_part, *node_part;
+    int32_t *rank_off, *rank_base, *node_base, *rank_part, *node_part;
     uint64_t *ticket;  // completion ticket (chunks)
     int32_t *dev_status;
     int64_t T, Tc;
@@ -53,48 +57,72 @@ struct NotifyParams {
     int32_t *tot_rank, *tot_node;
 };
 
-// The chunk's counts from its tokens' rank masks (lane l: token q*64 + l's mask, 0
-// past the last token): the masks for dispatch, the (chunk, rank) and (chunk, node)
-// counts, and the partial counts at channel ends inside the chunk.
-__device__ void count_chunk_masks(const NotifyParams &p, int64_t q, int lane, uint64_t m) {
-    const int64_t first = q * kChunk;
-    const int64_t tok = first + lane;
+// A chunk's columns: lane r (< R) holds which of the chunk's 64 tokens go to
+// rank r, lane n (< nodes) which of them reach node n.
+struct ChunkCols {
+    uint64_t rank_bits, node_bits;
+};
+
+// The chunk's columns from its tokens' rank masks (lane l: token q*64 + l's
+// mask, 0 past the last token).  Stores the masks for dispatch and the chunk's
+// per-rank and per-node counts into the LDS row s_row (ranks, then nodes).
+__device__ ChunkCols chunk_columns(const NotifyParams &p, int64_t q, int lane, uint64_t m, int32_t *s_row) {
+    const int64_t tok = q * kChunk + lane;
     const int R = p.R, nodes = p.nodes;
     if (tok < p.T) p.mask[tok] = m;
-    const uint64_t my_bits = transpose64(m);  // lane r: which tokens of the chunk go to rank r
-    uint64_t my_node_bits = 0;  // lane n: which tokens of the chunk reach node n
+    ChunkCols cc;
+    cc.rank_bits = transpose64(m);
+    cc.node_bits = 0;
     for (int n = 0; n < nodes; ++n) {
         const bool any = R < kRanksPerNode ? m != 0 : ((m >> (n * kRanksPerNode)) & 0xffull) != 0;
         const uint64_t b = ballot64(any);
-        my_node_bits = (lane == n) ? b : my_node_bits;
+        cc.node_bits = (lane == n) ? b : cc.node_bits;
     }
-    if (lane < R) p.rank_off[q * R + lane] = __popcll(my_bits);
-    if (lane < nodes) p.node_off[q * nodes + lane] = __popcll(my_node_bits);
-    // channels whose end lies strictly inside this chunk (the first channel
-    // that can end past `first` from a 32-bit division whenever T allows)
-    const int64_t c_first = p.T <= INT32_MAX ? (int64_t)((uint32_t)first / (uint32_t)p.Tc) : first / p.Tc;
-    for (int64_t c = c_first; c < p.C; ++c) {
+    if (lane < R) s_row[lane] = __popcll(cc.rank_bits);
+    if (lane < nodes) s_row[R + lane] = __popcll(cc.node_bits);
+    return cc;
+}
+
+// Chunk q, the w-th of the nw chunks of its group (LDS rows s_grp[0..nw) hold
+// the group's chunk counts): its offset inside the group (the tokens of the
+// group's earlier chunks) goes to rank_off, the value at each channel end that
+// falls in [64q, 64q + 64) -- that offset plus the chunk's tokens before the end
+// -- to rank_part / node_part, and, from the group's last chunk, the group's
+// totals to rank_base / node_base.
+__device__ void chunk_offsets(const NotifyParams &p, int64_t q, int lane, const ChunkCols &cc, const int32_t *s_grp,
+                              int w, int nw) {
+    const int R = p.R, nodes = p.nodes, NC = R + nodes;
+    int32_t ro = 0, no = 0;
+    for (int j = 0; j < w; ++j) {
+        if (lane < R) ro += s_grp[j * NC + lane];
+        if (lane < nodes) no += s_grp[j * NC + R + lane];
+    }
+    if (lane < R) p.rank_off[q * R + lane] = ro;
+    const int64_t first = q * kChunk;
+    // from the channel before the one holding token `first` (it may end exactly
+    // there); a 32-bit division whenever T allows
+    const int64_t c_hold = p.T <= INT32_MAX ? (int64_t)((uint32_t)first / (uint32_t)p.Tc) : first / p.Tc;
+    for (int64_t c = c_hold > 0 ? c_hold - 1 : 0; c < p.C; ++c) {
         const int64_t end = (c + 1) * p.Tc < p.T ? (c + 1) * p.Tc : p.T;
         if (end >= first + kChunk) break;
-        if (end <= first) continue;
-        const uint64_t below = (1ull << (end - first)) - 1ull;
-        if (lane < R) p.rank_part[c * R + lane] = __popcll(my_bits & below);
-        if (lane < nodes) p.node_part[c * nodes + lane] = __popcll(my_node_bits & below);
+        if (end < first) continue;
+        const uint64_t below = (1ull << (end - first)) - 1ull;  // end - first in [0, 63]
+        if (lane < R) p.rank_part[c * R + lane] = ro + __popcll(cc.rank_bits & below);
+        if (lane < nodes) p.node_part[c * nodes + lane] = no + __popcll(cc.node_bits & below);
+    }
+    if (w == nw - 1) {
+        const int64_t g = q / kGroupChunks;
+        if (lane < R) p.rank_base[g * R + lane] = ro + __popcll(cc.rank_bits);
+        if (lane < nodes) p.node_base[g * nodes + lane] = no + __popcll(cc.node_bits);
     }
 }
 
-__device__ void count_chunk(const NotifyParams &p, int64_t q, int lane) {
-    const int64_t tok = q * kChunk + lane;
-    const uint64_t m = tok < p.T ? load_rank_mask(p.in_rank + tok * p.R, p.R, p.load_unit) : 0ull;
-    count_chunk_masks(p, q, lane, m);
-}
-
-// One wave scans one column of the [Q][stride] count matrix into exclusive
-// offsets, and writes the total into row Q.  Returns the total.
-__device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
-    const int64_t per = (Q + kWave - 1) / kWave;
+// One wave scans one column of a [rows][stride] count matrix in place into
+// exclusive offsets.  Returns the column's total.
+__device__ int32_t scan_column(int32_t *col, int stride, int64_t rows, int lane) {
+    const int64_t per = (rows + kWave - 1) / kWave;
     const int64_t b = lane * per;
-    const int64_t e = (b + per) < Q ? (b + per) : Q;
+    const int64_t e = (b + per) < rows ? (b + per) : rows;
     int32_t s = 0;
     for (int64_t row = b; row < e; ++row) s += col[row * stride];
     const int32_t incl = wave_inclusive_scan(s);
@@ -104,21 +132,15 @@ __device__ int32_t scan_column(int32_t *col, int stride, int64_t Q, int lane) {
         col[row * stride] = run;
         run += v;
     }
-    const int32_t total = readlane32(incl, kWave - 1);
-    if (lane == 0) col[Q * stride] = total;
-    return total;
+    return readlane32(incl, kWave - 1);
 }
 
-// LDS capacity of the last block for the [Q][NC] counts plus the [C][NC]
-// partials; larger problems scan in global memory instead.
-constexpr int kScanLds = 12288;
-// rows of either matrix one thread of the last block holds: within the LDS
-// capacity, ceil(Q / (threads / NC)) and ceil(C / (threads / NC)) stay at or
-// below 14 for any NC <= 146 (finish_fits_lds checks it all the same)
-constexpr int kPasses = 14;
+// groups of a column one lane of the last block holds: 1 (up to 64 groups, 16384
+// tokens) or 4 (up to 256 groups); larger problems finish in global memory
+constexpr int kMaxGroupsPerLane = 4;
 // per-expert counts a thread of the last block loads with the others (E <= 4096 in one go)
 constexpr int kExpertBatch = 4;
-// columns (ranks + nodes <= 72) a wave scans together: ceil(72 / 16)
+// columns (ranks + nodes <= 72) a wave of the last block takes: ceil(72 / 16)
 constexpr int kColBatch = 5;
 
 __device__ __forceinline__ int64_t channel_end(const NotifyParams &p, int64_t c) {
@@ -147,66 +169,52 @@ __device__ void finish_totals(const NotifyParams &p, const int32_t *tot, int lan
     recv_prefixes(p, per_rank, per_node, lane, wave);
 }
 
-// Whether the last block finishes in LDS: the [Q + 1][NC] offsets and the
-// [C][NC] partials fit, and every thread's share of rows fits its registers.
-__device__ __forceinline__ bool finish_fits_lds(const NotifyParams &p) {
-    const int64_t NC = p.R + p.nodes, Q = num_chunks(p.T);
-    if ((Q + 1) * NC + (int64_t)p.C * NC > kScanLds) return false;
-    const int64_t S = kNotifyThreads / NC;
-    return (Q + S - 1) / S <= kPasses && ((int64_t)p.C + S - 1) / S <= kPasses && NC <= kColBatch * kNotifyWaves;
+// Groups of a column per lane for the last block's column-wise finish (1 or 4),
+// or 0 when the problem finishes in global memory instead (more than 256 groups,
+// T of 2^20 or more, or more columns than its waves take).
+__device__ __forceinline__ int finish_groups_per_lane(const NotifyParams &p) {
+    const int64_t G = num_groups(p.T);
+    if (p.T >= (1 << 20) || p.R + p.nodes > kColBatch * kNotifyWaves) return 0;
+    return G <= kWave ? 1 : G <= kMaxGroupsPerLane * kWave ? kMaxGroupsPerLane : 0;
 }
 
-// Last block, small problems.  Thread (seg, col) of the S = threads / NC
-// segments owns rows [seg * L, seg * L + L) of column col of the [Q][NC] count
-// matrix (NC = ranks + nodes, L = ceil(Q / S)) and the partial rows seg,
-// seg + S, ...: it loads them in one round trip and scans its rows in registers;
-// the segment totals are scanned per column in LDS (one wave per column); then
-// every thread writes its rows' offsets to the workspace and to LDS, and the
-// prefix matrices are read off LDS at the channel ends.  All indices fit 32 bits
-// (the LDS bound keeps T below 2^20).
-template <bool FUSED, class Mid>
-__device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave, Mid mid) {
-    __shared__ int32_t s_cnt[kScanLds];        // [Q+1][NC] offsets, then [C][NC] partials behind them
-    __shared__ int32_t s_seg[kNotifyThreads];  // [S][NC] segment totals, then their offsets
+// Last block, up to 64 * PG groups: one wave per column (ranks, then nodes; wave
+// w takes columns w, w + 16, ...), no barrier until the totals.  Lane j holds
+// groups j*PG .. j*PG + PG - 1 of the column; all of a wave's loads (its columns'
+// group totals and the values stored at channel ends j, j + 64, ... -- the first
+// 64 in this round trip) are made before any is used.  A column's group offsets
+// come from the lane's running sum and a wave scan, go back to the workspace
+// (dispatch adds them to its chunks' offsets) and to a row of LDS the wave
+// alone uses; lane j then takes channel j: the offset of the group its end falls
+// in plus the value stored for the end (an end at t = 64 Q is the column total),
+// so each prefix-matrix row goes out in consecutive words.  All indices fit 32
+// bits (T < 2^20 here).
+template <bool FUSED, int PG, class Mid>
+__device__ void finish_by_columns(const NotifyParams &p, int tid, int lane, int wave, Mid mid) {
+    __shared__ int32_t s_goff[kNotifyWaves][kMaxGroupsPerLane * kWave];  // a wave's column of group offsets
     __shared__ int32_t s_tot[kMaxRanks + kMaxRanks / kRanksPerNode];
     const int R = p.R, nodes = p.nodes, NC = R + nodes, C = p.C;
     const int T = (int)p.T, Tc = (int)p.Tc;
-    const int Q = (T + kChunk - 1) / kChunk;
-    int32_t *s_part = s_cnt + (Q + 1) * NC;
-    const int S = kNotifyThreads / NC;
-    const int L = (Q + S - 1) / S;
-    const int seg = tid / NC, col = tid - seg * NC;
-    const bool active = seg < S;
-    const bool is_rank = col < R;
-    const int stride = is_rank ? R : nodes;
-    int32_t *off = is_rank ? p.rank_off + col : p.node_off + (col - R);
-    const int32_t *part = is_rank ? p.rank_part + col : p.node_part + (col - R);
-    const int q0 = seg * L;
-    const int rows = active ? (Q - q0 < L ? (Q - q0 > 0 ? Q - q0 : 0) : L) : 0;
+    const int Q = (T + kChunk - 1) / kChunk, G = (Q + kGroupChunks - 1) / kGroupChunks;
+    auto end_of = [&](int c) { return (c + 1) * Tc < T ? (c + 1) * Tc : T; };
 
-    // ---- one round trip of loads, all issued before any is used: the thread's
-    // count rows, its partial rows (channels whose end lies inside a chunk; the
-    // others have none), and for notify the totals and per-expert counts.  The
-    // addresses walk by a fixed step, none computed from a loaded value; loads
-    // that only some lanes need are made by all at an index clamped into range,
-    // the rest of the lanes dropping the value where it is used (a load under a
-    // branch would be waited for where the branch joins).
-    int32_t v[kPasses], vp[kPasses], pe[kExpertBatch];
-    {
-        const int32_t *src = off + (ptrdiff_t)q0 * stride;
-        const int32_t *psrc = part + (ptrdiff_t)seg * stride;
-        const ptrdiff_t pstep = (ptrdiff_t)S * stride;
+    // ---- one round trip of loads for all of the wave's columns (and, for
+    // notify, the totals and per-expert counts), issued before any is used
+    int32_t gv[kColBatch][PG], cv[kColBatch];
+    const bool c_in = lane < C && end_of(lane) < Q * kChunk;  // channel `lane` ends inside a chunk
 #pragma unroll
-        for (int k = 0; k < kPasses; ++k) {
-            v[k] = k < rows ? *src : 0;
-            src += stride;
-            const int c = seg + k * S;
-            const int end = (c + 1) * Tc < T ? (c + 1) * Tc : T;
-            vp[k] = (active && c < C && end % kChunk != 0) ? *psrc : 0;
-            psrc += pstep;
-        }
+    for (int k = 0; k < kColBatch; ++k) {
+        const int col = wave + k * kNotifyWaves;  // the same for the whole wave
+        const bool on = col < NC;
+        const bool is_rank = col < R;
+        const int stride = is_rank ? R : nodes;
+        const int32_t *gsrc = (is_rank ? p.rank_base + col : p.node_base + (col - R)) + (ptrdiff_t)lane * PG * stride;
+        const int32_t *csrc = (is_rank ? p.rank_part + col : p.node_part + (col - R)) + (ptrdiff_t)lane * stride;
+#pragma unroll
+        for (int i = 0; i < PG; ++i) gv[k][i] = (on && lane * PG + i < G) ? gsrc[i * stride] : 0;
+        cv[k] = (on && c_in) ? *csrc : 0;
     }
-    int32_t per_rank = 0, per_node = 0;
+    int32_t per_rank = 0, per_node = 0, pe[kExpertBatch];
     if constexpr (!FUSED) {
         per_rank = p.per_rank[lane < R ? lane : 0];
         per_node = p.per_node[lane < nodes ? lane : 0];
@@ -216,22 +224,44 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
             pe[k] = p.per_expert[e < p.E ? e : 0];
         }
     }
-    mid();  // the caller's work that waits on its own memory round trip, overlapped with these loads
 
-    // ---- the segment in registers: v[k] becomes row q0 + k's offset inside it
-    int32_t run = 0;
+    // ---- per column: offsets, then the prefix-matrix row
 #pragma unroll
-    for (int k = 0; k < kPasses; ++k) {
-        const int32_t x = v[k];
-        v[k] = run;
-        run += x;
-    }
-    if (active) s_seg[seg * NC + col] = run;
+    for (int k = 0; k < kColBatch; ++k) {
+        const int col = wave + k * kNotifyWaves;
+        if (col >= NC) break;  // wave-uniform
+        const bool is_rank = col < R;
+        const int stride = is_rank ? R : nodes;
+        int32_t *gdst = (is_rank ? p.rank_base + col : p.node_base + (col - R)) + (ptrdiff_t)lane * PG * stride;
+        int32_t run = 0;
 #pragma unroll
-    for (int k = 0; k < kPasses; ++k) {
-        const int c = seg + k * S;
-        if (active && c < C) s_part[c * NC + col] = vp[k];
+        for (int i = 0; i < PG; ++i) run += gv[k][i];
+        const int32_t incl = wave_inclusive_scan(run);
+        const int32_t total = readlane32(incl, kWave - 1);
+        run = incl - run;
+#pragma unroll
+        for (int i = 0; i < PG; ++i) {
+            if (lane * PG + i < G) {
+                gdst[i * stride] = run;
+                s_goff[wave][lane * PG + i] = run;
+            }
+            run += gv[k][i];
+        }
+        if (lane == 0) s_tot[col] = total;
+        int32_t *row = is_rank ? p.gbl + col * C : p.rdma + (col - R) * C;
+        auto prefix = [&](int c, int32_t at_end) {
+            const int qe = end_of(c) / kChunk;
+            return qe < Q ? s_goff[wave][qe / kGroupChunks] + at_end : total;
+        };
+        if (lane < C) row[lane] = prefix(lane, cv[k]);
+        const int32_t *csrc = is_rank ? p.rank_part + col : p.node_part + (col - R);
+        for (int c = lane + kWave; c < C; c += kWave)
+            row[c] = prefix(c, end_of(c) < Q * kChunk ? csrc[c * stride] : 0);
     }
+    // the caller's work that waits on its own memory round trip (made beside these
+    // loads), after every load above is consumed: a wait for one of them after its
+    // stores would wait for those stores too
+    mid();
     if constexpr (!FUSED) {  // aligned per-expert counts need nothing from the scan
         per_rank = lane < R ? per_rank : 0;
         per_node = lane < nodes ? per_node : 0;
@@ -244,60 +274,8 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
         for (int e = tid + kExpertBatch * kNotifyThreads; e < p.E; e += kNotifyThreads)
             p.recv_per_expert[e] = aligned(p.per_expert[e]);
     }
-    __syncthreads();
+    __syncthreads();  // s_tot complete
 
-    // ---- segment offsets, one wave per column (lanes over segments); the
-    // column totals go to s_tot
-    if (S <= kWave) {
-        int32_t x[kColBatch];
-#pragma unroll
-        for (int k = 0; k < kColBatch; ++k) {
-            const int cc = wave + k * kNotifyWaves;
-            x[k] = (lane < S && cc < NC) ? s_seg[lane * NC + cc] : 0;
-        }
-#pragma unroll
-        for (int k = 0; k < kColBatch; ++k) {
-            const int cc = wave + k * kNotifyWaves;  // the same for the whole wave
-            if (cc >= NC) break;
-            const int32_t incl = wave_inclusive_scan(x[k]);
-            if (lane < S) s_seg[lane * NC + cc] = incl - x[k];
-            if (lane == kWave - 1) s_tot[cc] = incl;
-        }
-    } else {  // NC < 16: up to 8 segments a lane, at most one column a wave
-        const int per = (S + kWave - 1) / kWave;
-        const int b = lane * per, e = b + per < S ? b + per : S;
-        for (int cc = wave; cc < NC; cc += kNotifyWaves) {
-            int32_t sum = 0;
-            for (int g = b; g < e; ++g) sum += s_seg[g * NC + cc];
-            const int32_t incl = wave_inclusive_scan(sum);
-            int32_t r2 = incl - sum;
-            for (int g = b; g < e; ++g) {
-                const int32_t x = s_seg[g * NC + cc];
-                s_seg[g * NC + cc] = r2;
-                r2 += x;
-            }
-            if (lane == kWave - 1) s_tot[cc] = incl;
-        }
-    }
-    __syncthreads();
-
-    // ---- every row's offset: to the workspace (dispatch reads it) and to LDS;
-    // row Q holds the column totals
-    if (active) {
-        const int32_t base = s_seg[seg * NC + col];
-#pragma unroll
-        for (int k = 0; k < kPasses; ++k) {
-            if (k < rows) {
-                const int32_t o = base + v[k];
-                off[(q0 + k) * stride] = o;
-                s_cnt[(q0 + k) * NC + col] = o;
-            }
-        }
-        if (seg == 0) {
-            off[Q * stride] = s_tot[col];
-            s_cnt[Q * NC + col] = s_tot[col];
-        }
-    }
     // receive prefix sums over destination ranks and nodes (inclusive): fused,
     // from the scan's totals; notify, from its inputs, checked against the totals
     if constexpr (FUSED) {
@@ -309,17 +287,6 @@ __device__ void finish_in_lds(const NotifyParams &p, int tid, int lane, int wave
             if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
         }
     }
-    __syncthreads();
-
-    // ---- the prefix matrices: at channel c's end, the offset of the chunk it
-    // ends in plus the chunk's tokens before the end
-    if (active) {
-        int32_t *dst = is_rank ? p.gbl + col * C : p.rdma + (col - R) * C;
-        for (int c = seg; c < C; c += S) {
-            const int end = (c + 1) * Tc < T ? (c + 1) * Tc : T;
-            dst[c] = s_cnt[(end / kChunk) * NC + col] + s_part[c * NC + col];
-        }
-    }
 }
 
 // Last block, large problems: the same steps on the workspace in global memory.
@@ -328,51 +295,68 @@ __device__ void finish_in_global(const NotifyParams &p, int tid, int lane, int w
     mid();
     __shared__ int32_t s_tot_g[kMaxRanks + kMaxRanks / kRanksPerNode];
     const int R = p.R, nodes = p.nodes, NC = R + nodes;
-    const int64_t Q = num_chunks(p.T);
+    const int64_t Q = num_chunks(p.T), G = num_groups(p.T);
     for (int col = wave; col < NC; col += kNotifyWaves) {
         const bool is_rank = col < R;
-        int32_t *cp = is_rank ? p.rank_off + col : p.node_off + (col - R);
-        const int32_t total = scan_column(cp, is_rank ? R : nodes, Q, lane);
-        if (p.fused) {
-            if (lane == 0) s_tot_g[col] = total;
-        } else {
+        int32_t *cp = is_rank ? p.rank_base + col : p.node_base + (col - R);
+        const int32_t total = scan_column(cp, is_rank ? R : nodes, G, lane);
+        if (lane == 0) s_tot_g[col] = total;
+        if (!p.fused) {
             const int32_t want = is_rank ? p.per_rank[col] : p.per_node[col - R];
             if (lane == 0 && total != want) flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
         }
     }
-    if (!p.fused)
+    if (!p.fused) {
         recv_prefixes(p, lane < R ? p.per_rank[lane] : 0, lane < nodes ? p.per_node[lane] : 0, lane, wave);
-    if (!p.fused)  // fused, the expert totals' loop writes them
-        for (int e = tid; e < p.E; e += kNotifyThreads) {
+        for (int e = tid; e < p.E; e += kNotifyThreads) {  // fused, the expert totals' loop writes them
             const int64_t n = p.per_expert[e];
             p.recv_per_expert[e] = (int32_t)((n + p.align - 1) / p.align * p.align);
         }
-    __syncthreads();  // scanned offsets visible to the whole block
+    }
+    __syncthreads();  // the group offsets and totals visible to the whole block
     if (p.fused) finish_totals(p, s_tot_g, lane, wave);
     for (int64_t i = tid; i < (int64_t)NC * p.C; i += kNotifyThreads) {
         const int cc = (int)(i / p.C);
         const int64_t c = i % p.C;
-        const int64_t end = channel_end(p, c);
-        const int64_t qe = end / kChunk;
-        const bool inside = (end % kChunk) != 0;
+        const int64_t qe = channel_end(p, c) / kChunk;
+        const int64_t g = qe / kGroupChunks;
         if (cc < R) {
-            p.gbl[cc * (int64_t)p.C + c] = p.rank_off[qe * R + cc] + (inside ? p.rank_part[c * R + cc] : 0);
+            p.gbl[cc * (int64_t)p.C + c] = qe < Q ? p.rank_base[g * R + cc] + p.rank_part[c * R + cc] : s_tot_g[cc];
         } else {
             const int n = cc - R;
-            p.rdma[n * (int64_t)p.C + c] = p.node_off[qe * nodes + n] + (inside ? p.node_part[c * nodes + n] : 0);
+            p.rdma[n * (int64_t)p.C + c] = qe < Q ? p.node_base[g * nodes + n] + p.node_part[c * nodes + n] : s_tot_g[cc];
         }
     }
 }
 
+static_assert(kNotifyWaves % kGroupChunks == 0, "a block holds whole groups of chunks");
+
 __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) {
+    __shared__ int32_t s_grp[kNotifyWaves * (kMaxRanks + kMaxRanks / kRanksPerNode)];  // [wave][NC] chunk counts
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
     const int64_t Q = num_chunks(p.T);
+    const int NC = p.R + p.nodes;
 
-    const uint32_t epoch0 = (gridDim.x > 1 && tid == 0) ? ticket_epoch(p.ticket) : 0u;
+    // every lane reads the epoch (thread 0 uses it): a load under a branch would be
+    // waited for where the branch joins, before this wave issues its own loads
+    const uint32_t epoch0 = ticket_epoch(p.ticket);
+    // the wave's chunk from its tokens' is_token_in_rank rows, then its offsets
+    // inside its group once the group's four waves have counted
     const int64_t q = (int64_t)blockIdx.x * kNotifyWaves + wave;
-    if (q < Q) count_chunk(p, q, lane);
+    ChunkCols cc{0ull, 0ull};
+    if (q < Q) {
+        const int64_t tok = q * kChunk + lane;
+        const uint64_t m = tok < p.T ? load_rank_mask(p.in_rank + tok * p.R, p.R, p.load_unit) : 0ull;
+        cc = chunk_columns(p, q, lane, m, s_grp + wave * NC);
+    }
+    __syncthreads();
+    if (q < Q) {
+        const int w = wave % kGroupChunks;
+        const int64_t left = Q - (q - w);
+        chunk_offsets(p, q, lane, cc, s_grp + (wave - w) * NC, w, (int)(left < kGroupChunks ? left : kGroupChunks));
+    }
 
     // a single block (up to 1024 tokens) finishes once its own waves are done:
     // a workgroup barrier (with its workgroup-scope fences) makes their stores
@@ -386,8 +370,11 @@ __global__ __launch_bounds__(kNotifyThreads) void notify_kernel(NotifyParams p) 
         const uint32_t mine = (uint32_t)(left < kNotifyWaves ? left : kNotifyWaves);
         if (!elect_completing_block(p.ticket, epoch0, mine, (uint32_t)Q, p.dev_status)) return;
     }
-    if (finish_fits_lds(p))
-        finish_in_lds<false>(p, tid, lane, wave, [] {});
+    const int pg = finish_groups_per_lane(p);
+    if (pg == 1)
+        finish_by_columns<false, 1>(p, tid, lane, wave, [] {});
+    else if (pg == kMaxGroupsPerLane)
+        finish_by_columns<false, kMaxGroupsPerLane>(p, tid, lane, wave, [] {});
     else
         finish_in_global(p, tid, lane, wave, [] {});
 }
@@ -408,6 +395,7 @@ constexpr int kFusedMaxLdsExperts = 8192;  // 32 KiB of LDS histogram; larger E 
 constexpr int kFusedChunks = 4;            // chunks per block
 constexpr int kFusedTokens = kFusedChunks * kChunk;
 static_assert(kFusedTokens * 4 == kNotifyThreads, "four lanes per token");
+static_assert(kFusedChunks == kGroupChunks, "a block's chunks are one group");
 
 // OR of a 64-bit value over the four lanes of each quad (two DPP quad permutations).
 __device__ __forceinline__ uint64_t quad_or64(uint64_t v) {
@@ -429,8 +417,14 @@ struct FusedParams {
     int K, store_unit;
 };
 
+// SINGLE: a one-block grid (up to 256 tokens), which finishes without an election
+// and keeps the per-expert counts in LDS; a compile-time choice, so that neither
+// instantiation carries the other's branches between its loads.  KQ: topk slots
+// per lane, ceil(topk / 4) rounded up to 2 or 8.
+template <bool SINGLE, int KQ>
 __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedParams f, NotifyParams p) {
     __shared__ uint64_t s_mask[kFusedTokens];
+    __shared__ int32_t s_grp[kFusedChunks * (kMaxRanks + kMaxRanks / kRanksPerNode)];  // [chunk][NC] counts
     __shared__ uint32_t s_slots, s_esum;
     extern __shared__ int32_t s_expert[];  // E entries when E <= kFusedMaxLdsExperts
     const int tid = threadIdx.x;
@@ -438,8 +432,8 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
     const int wave = tid >> 6;
     const int R = p.R, E = p.E, K = f.K;
     const bool lds_experts = E <= kFusedMaxLdsExperts;
-    const bool single = gridDim.x == 1;
-    const uint32_t epoch0 = (!single && tid == 0) ? ticket_epoch(f.ticket) : 0u;
+    constexpr bool single = SINGLE;
+    const uint32_t epoch0 = SINGLE ? 0u : ticket_epoch(f.ticket);  // every lane, as in notify_kernel
     const int64_t Q = num_chunks(p.T);
     if (tid == 0) {
         s_slots = 0;
@@ -458,11 +452,11 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
     int bad = 0, slots = 0;
     if (t < p.T) {
         const int64_t *row = f.topk_idx + t * K;
-        int64_t ev[kMaxTopk / 4];  // all of the lane's loads in flight together
+        int64_t ev[KQ];  // all of the lane's loads in flight together
 #pragma unroll
-        for (int u = 0; u < kMaxTopk / 4; ++u) ev[u] = part + 4 * u < K ? row[part + 4 * u] : -1;
+        for (int u = 0; u < KQ; ++u) ev[u] = part + 4 * u < K ? row[part + 4 * u] : -1;
 #pragma unroll
-        for (int u = 0; u < kMaxTopk / 4; ++u) {
+        for (int u = 0; u < KQ; ++u) {
             const int64_t e = ev[u];
             if (e == -1) continue;
             if (e < -1 || e >= E) {
@@ -484,11 +478,11 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
     if (lane == 0) atomicAdd(&s_slots, (uint32_t)w_slots);
     __syncthreads();
 
-    // ---- the block's chunks, one wave each, from the masks in LDS
-    if (wave < kFusedChunks) {
-        const int64_t q = (int64_t)blockIdx.x * kFusedChunks + wave;
-        if (q < Q) count_chunk_masks(p, q, lane, s_mask[wave * kChunk + lane]);
-    }
+    // ---- the block's chunks (one group), one wave each, from the masks in LDS
+    const int64_t q = (int64_t)blockIdx.x * kFusedChunks + wave;
+    const bool counts = wave < kFusedChunks && q < Q;
+    ChunkCols cc{0ull, 0ull};
+    if (counts) cc = chunk_columns(p, q, lane, s_mask[wave * kChunk + lane], s_grp + wave * (R + p.nodes));
 
     // ---- is_token_in_rank rows of this block: one contiguous range of nt*R bytes
     {
@@ -522,6 +516,13 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
         }
     }
 
+    // ---- the chunks' offsets inside the group, once all four have counted
+    __syncthreads();
+    if (counts) {
+        const int64_t left = Q - (int64_t)blockIdx.x * kFusedChunks;
+        chunk_offsets(p, q, lane, cc, s_grp, wave, (int)(left < kFusedChunks ? left : kFusedChunks));
+    }
+
     // ---- completion: the block that completes the chunks goes on
     if (!single) {
         if (lds_experts)
@@ -553,7 +554,10 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
     auto mid = [&] {
         auto publish = [&](int e, int32_t v) {
             f.per_expert[e] = v;
-            p.recv_per_expert[e] = (int32_t)(((int64_t)v + p.align - 1) / p.align * p.align);
+            // a count (0 <= v < 2^31) rounded up in 32-bit unsigned arithmetic: the
+            // same low 32 bits as in 64-bit
+            const uint32_t a = (uint32_t)p.align;
+            p.recv_per_expert[e] = (int32_t)(((uint32_t)v + a - 1u) / a * a);
             if (!from_lds) __hip_atomic_store(&f.acc_expert[e], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         };
         uint32_t esum = 0;
@@ -573,8 +577,11 @@ __global__ __launch_bounds__(kNotifyThreads) void layout_notify_kernel(FusedPara
         const int w_e = wave_sum((int)esum);
         if (lane == 0) atomicAdd(&s_esum, (uint32_t)w_e);
     };
-    if (finish_fits_lds(p))
-        finish_in_lds<true>(p, tid, lane, wave, mid);
+    const int pg = finish_groups_per_lane(p);
+    if (pg == 1)
+        finish_by_columns<true, 1>(p, tid, lane, wave, mid);
+    else if (pg == kMaxGroupsPerLane)
+        finish_by_columns<true, kMaxGroupsPerLane>(p, tid, lane, wave, mid);
     else
         finish_in_global(p, tid, lane, wave, mid);
     // every wave added its expert sum before the finish's first barrier
@@ -604,7 +611,8 @@ hipError_t launch_layout_notify(const ep_shape_t &s, const int64_t *topk_idx, in
     p.num_recv = num_recv;
     p.mask = reinterpret_cast<uint64_t *>(ws + w.mask);
     p.rank_off = reinterpret_cast<int32_t *>(ws + w.rank_off);
-    p.node_off = reinterpret_cast<int32_t *>(ws + w.node_off);
+    p.rank_base = reinterpret_cast<int32_t *>(ws + w.rank_base);
+    p.node_base = reinterpret_cast<int32_t *>(ws + w.node_base);
     p.rank_part = reinterpret_cast<int32_t *>(ws + w.rank_part);
     p.node_part = reinterpret_cast<int32_t *>(ws + w.node_part);
     p.ticket = nullptr;
@@ -636,7 +644,19 @@ hipError_t launch_layout_notify(const ep_shape_t &s, const int64_t *topk_idx, in
     const int64_t Q = num_chunks(p.T);
     const int64_t blocks = Q > 0 ? (Q + kFusedChunks - 1) / kFusedChunks : 1;
     const size_t lds = p.E <= kFusedMaxLdsExperts ? sizeof(int32_t) * (size_t)p.E : 0;
-    hipLaunchKernelGGL(layout_notify_kernel, dim3((unsigned)blocks), dim3(kNotifyThreads), lds, stream, f, p);
+    static_assert(kMaxTopk == 4 * 8, "KQ = 8 covers every topk");
+    const dim3 grid((unsigned)blocks), block(kNotifyThreads);
+    if (f.K <= 8) {
+        if (blocks == 1)
+            hipLaunchKernelGGL((layout_notify_kernel<true, 2>), grid, block, lds, stream, f, p);
+        else
+            hipLaunchKernelGGL((layout_notify_kernel<false, 2>), grid, block, lds, stream, f, p);
+    } else {
+        if (blocks == 1)
+            hipLaunchKernelGGL((layout_notify_kernel<true, 8>), grid, block, lds, stream, f, p);
+        else
+            hipLaunchKernelGGL((layout_notify_kernel<false, 8>), grid, block, lds, stream, f, p);
+    }
     return hipGetLastError();
 }
 
@@ -658,7 +678,8 @@ hipError_t launch_notify(const ep_shape_t &s, const uint8_t *in_rank, const int3
     p.num_recv = num_recv;
     p.mask = reinterpret_cast<uint64_t *>(ws + w.mask);
     p.rank_off = reinterpret_cast<int32_t *>(ws + w.rank_off);
-    p.node_off = reinterpret_cast<int32_t *>(ws + w.node_off);
+    p.rank_base = reinterpret_cast<int32_t *>(ws + w.rank_base);
+    p.node_base = reinterpret_cast<int32_t *>(ws + w.node_base);
     p.rank_part = reinterpret_cast<int32_t *>(ws + w.rank_part);
     p.node_part = reinterpret_cast<int32_t *>(ws + w.node_part);
     p.ticket = reinterpret_cast<uint64_t *>(reinterpret_cast<uint32_t *>(ws + w.tickets) + kTicketNotify);

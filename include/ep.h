@@ -90,7 +90,7 @@ enum {
  *   pull: receive order -- each XCD writes one advancing window of the receive region and
  *         re-reads x from its L2.  Best when x was just written (still in the Infinity Cache,
  *         as the layer before dispatch leaves it); slower than push when x is only in HBM.
- *         It applies from 2048 tokens, to rows of 1 KiB to 1 MiB (cached mode: from 14 KiB);
+ *         It applies from 2048 tokens, to rows of 1 KiB to 1 MiB, and not to cached mode;
  *         elsewhere the push form is taken.
  * The outputs are the same, bit for bit, whichever form runs. */
 typedef enum {
@@ -255,7 +255,9 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
  * routing.  Rows are hidden * elem_bytes bytes (elem_bytes 2 = bf16, 1 = fp8; a multiple
  * of 16); num_scales float scales per token go along when num_scales > 0.  No metadata
  * is written.  Entries outside [-1, recv_capacity) are skipped and flagged
- * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.  form: as for ep_dispatch.
+ * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.  form: EP_FORM_AUTO
+ * or EP_FORM_PUSH, both the push form; EP_FORM_PULL returns EP_ERR_UNSUPPORTED (cached mode has
+ * no pull form).
  */
 ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,

@@ -54,9 +54,10 @@ def test_status_strings(ep):
 def test_workspace_bytes(ep):
     s = ep.make_shape(4096, 7168, 8, 256, 64, 24)
     n = ep.ep_workspace_bytes(s)
-    # tickets 256 + running counts (64+8+256) + masks (8 B/token) + 65 x 64 chunk offsets
-    # + 65 x 8 + 24 x 64 + 24 x 8 + grouped positions (4 B per token and slot), each 256-aligned
-    assert n == 256 + 1536 + 32768 + 16640 + 2304 + 6144 + 768 + 131072
+    # tickets 256 + running counts (64+8+256) + masks (8 B/token) + 64 x 64 chunk offsets
+    # + 16 x 64 and 16 x 8 group offsets (four chunks a group) + 24 x 64 + 24 x 8 channel-end
+    # values + grouped positions (4 B per token and slot), each 256-aligned
+    assert n == 256 + 1536 + 32768 + 16384 + 4096 + 512 + 6144 + 768 + 131072
     assert ep.ep_workspace_bytes(ep.make_shape(4096, 7168, 8, 255, 64, 24)) == 0  # E % R != 0
 
 
@@ -288,6 +289,15 @@ def test_dispatch_form_must_be_known(ep):
                                    None, None) == ep.EP_ERR_INVALID_ARG
         assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, form, None,
                                       None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_cached_dispatch_has_no_pull_form(ep):
+    # cached mode copies rows with the push form only: EP_FORM_PULL is refused on the host
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    s = _shape(ep)
+    assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, p, 10, p, None, ep.EP_FORM_PULL, None,
+                                  None) == ep.EP_ERR_UNSUPPORTED
 
 
 def test_layout_notify_argument_checks(ep):

@@ -91,6 +91,8 @@ EDGES = {
     "experts_past_lds_one_block": (250, 64, 16384, 8, 24, 1, {}),
     "experts_past_lds_few_blocks": (700, 64, 16384, 8, 24, 1, {}),
     "global_scan": (100000, 64, 256, 8, 24, 1, {}),
+    "four_groups_a_lane": (40000, 64, 256, 8, 24, 1, {}),
+    "just_past_64_groups": (16400, 16, 64, 6, 32, 1, {}),
     "many_channels": (5000, 16, 64, 4, 4096, 1, {}),
     "k32_bad_ids": (4100, 64, 128, 32, 9, 128, dict(dup=True, bad=True)),
     "five_ranks": (2000, 5, 10, 3, 4, 1, dict(mask_frac=1.0)),

@@ -308,13 +308,11 @@ CACHED_LARGE = {
     "bf16_rows_14kib_r64": (2048, 64, 7168, 2, 0, 15000),
     "bf16_rows_1kib_r24": (2049, 24, 512, 2, 0, 20000),
     "fp8_rows_7kib_scales": (2304, 64, 7168, 1, 56, 12000),
-    # the shape an earlier trial (scales copied inside the row-task loop) lost row pieces at;
-    # tests/test_pull_task_cover.py models the task enumeration on this very map
     "bf16_rows_14kib_r64_scales56": (2304, 64, 7168, 2, 56, 12000),
 }
 
 
-@pytest.mark.parametrize("form", [0, 1])  # EP_FORM_AUTO (the pull form from 14 KiB rows), EP_FORM_PUSH
+@pytest.mark.parametrize("form", [0, 1])  # EP_FORM_AUTO and EP_FORM_PUSH: cached mode's one (push) form
 @pytest.mark.parametrize("name", sorted(CACHED_LARGE))
 def test_cached_any_map_and_bad_slots(name, form):
     import torch

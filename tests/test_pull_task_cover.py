@@ -1,22 +1,17 @@
 """A host model of how the pull-form kernels hand out their row tasks.
 
-dispatch_pull_kernel, dispatch_cached_pull_kernel and group_pull_kernel share
-one enumeration: per token group, the output is cut into tasks (a run of U
-1 KiB pieces of one row, TPR tasks per row); the XCD's W waves take tasks
-k = wx, wx + W, ...; a wave resolves them 64 at a time (lane i takes the task
-base + i: its rank by a binary search over the run starts, its token by a
-select-bit over the rank's column, or its entry of the group's list) and then
-works through them in a loop of nbatch readlanes.  The model below restates
-that arithmetic step by step, in integers, and checks that it issues every
-(row, piece) of a group exactly once and at the row the routing defines (the
-oracle's send_slot, or the grouping's positions).
-
-It runs on the shape of an earlier cached-mode trial that left 1 KiB pieces
-of 9 rows unwritten (2304 tokens, 64 ranks, 14 KiB rows, 56 scales; the trial
-copied scales inside the row-task loop), with the slot map the GPU test
-builds for that shape, and on the benchmark's workloads.  A pass rules out the
-task arithmetic as the cause of such a loss: no task is skipped, repeated or
-sent to another row by the enumeration or the routing."""
+dispatch_pull_kernel and group_pull_kernel share one enumeration: per token
+group, the output is cut into tasks (a run of U 1 KiB pieces of one row, TPR
+tasks per row); the XCD's W waves take tasks k = wx, wx + W, ...; a wave
+resolves them 64 at a time (lane i takes the task base + i: its rank by a
+binary search over the run starts, its token by a select-bit over the rank's
+column, or its entry of the group's list) and then works through them in a
+loop of nbatch readlanes.  The model below restates that arithmetic step by
+step, in integers, and checks that it issues every (row, piece) of a group
+exactly once and at the row the routing defines (the oracle's send_slot, or
+the grouping's positions), on the benchmark's workloads.  A pass rules out the
+task arithmetic as the cause of a lost or repeated piece: no task is skipped,
+repeated or sent to another row by the enumeration or the routing."""
 import numpy as np
 import pytest
 
@@ -69,67 +64,6 @@ def _route_rank(pex: np.ndarray, rr: int) -> int:
             r = cand
         step >>= 1
     return r
-
-
-def _cover_cached(slot: np.ndarray, cap: int, row_units: int, W: int = 512):
-    """dispatch_cached_pull_kernel: 128-token groups, one 1 KiB piece per task."""
-    T, R = slot.shape
-    GT = 2 * CHUNK
-    TPR = (row_units + CHUNK - 1) // CHUNK
-    issued = {}
-    for g in range((T + GT - 1) // GT):
-        s = np.full((GT, R), -1, np.int64)
-        part = slot[g * GT:(g + 1) * GT].astype(np.int64)
-        s[:part.shape[0]] = np.where((part >= -1) & (part < cap), part, -1)
-        cols = [[sum(1 << l for l in range(CHUNK) if s[c * CHUNK + l, r] >= 0) for r in range(R)] for c in (0, 1)]
-        n = [bin(cols[0][r]).count("1") + bin(cols[1][r]).count("1") for r in range(R)]
-        pex = np.full(64, 2 ** 31 - 1, np.int64)
-        pex[:R] = np.cumsum([0] + n[:-1])
-        tasks = sum(n) * TPR
-        for wx in range(W):
-            for k in _wave_tasks(wx, W, tasks):
-                rr, piece = divmod(k, TPR)
-                r = _route_rank(pex, rr)
-                o = rr - pex[r]
-                c0, c1 = cols[0][r], cols[1][r]
-                p0 = bin(c0).count("1")
-                second = o >= p0
-                cc = c1 if second else c0
-                oc = o - p0 if second else o
-                assert oc < bin(cc).count("1")
-                tok = (CHUNK if second else 0) + _nth_set_bit(cc, oc)
-                row = int(s[tok, r])
-                assert row >= 0
-                key = (row, piece)
-                assert key not in issued, f"(row {row}, piece {piece}) issued twice"
-                issued[key] = g * GT + tok
-    return issued, TPR
-
-
-CACHED_SHAPES = {
-    # (T, R, row elements, element bytes, capacity): the lost-piece trial's shape first
-    "bf16_rows_14kib_r64_scales56": (2304, 64, 7168, 2, 12000),
-    "fp8_rows_14kib_r64_scales": (2304, 64, 14336, 1, 12000),
-    "bf16_rows_16kib_r24": (2049, 24, 8192, 2, 20000),
-}
-
-
-@pytest.mark.parametrize("name", sorted(CACHED_SHAPES))
-def test_cached_pull_tasks_cover_every_piece_once(name):
-    T, R, Hd, elem, cap = CACHED_SHAPES[name]
-    # the slot map the GPU test builds for this shape (test_cached_any_map_and_bad_slots)
-    rng = np.random.default_rng(len(name) + 500)
-    rng.integers(0, 256, size=(T, Hd * elem), dtype=np.uint8)
-    slot = np.full((T, R), -1, np.int32)
-    picks = rng.choice(T * R, cap - 37, replace=False)
-    slot.reshape(-1)[picks] = rng.permutation(cap)[: cap - 37]
-    slot[5, R - 1] = cap + 9
-    slot[T - 1, 0] = -3
-    slot[1000, 2] = cap
-    issued, TPR = _cover_cached(slot, cap, Hd * elem // 16)
-    valid = (slot >= 0) & (slot < cap)
-    want = {(int(slot[t, r]), p): t for t, r in zip(*np.nonzero(valid)) for p in range(TPR)}
-    assert issued == want
 
 
 def _routing(name):
