@@ -59,20 +59,21 @@ struct PositionParams {
     int R, K, er;
 };
 
+// Inclusive prefix sum over the wave of non-negative values below 2^41 (the
+// segment sizes summed here are int32 counts, at most 64 a lane): the low 16
+// bits and the rest are scanned as two 32-bit DPP scans (each sum stays below
+// 2^31 over 64 lanes) and recombined exactly.
 __device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
-    const int lane = __lane_id();
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-        const int64_t o = __shfl_up(v, d, kWave);
-        if (lane >= d) v += o;
-    }
-    return v;
+    const int lo = wave_inclusive_scan((int)(v & 0xffff));
+    const int hi = wave_inclusive_scan((int)(v >> 16));
+    return ((int64_t)hi << 16) + lo;
 }
 
 __device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-#pragma unroll
-    for (int d = kWave / 2; d > 0; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
+    const int64_t incl = wave_inclusive_scan64(v);
+    const uint32_t lo = (uint32_t)readlane32((int)(uint32_t)incl, kWave - 1);
+    const uint32_t hi = (uint32_t)readlane32((int)(uint32_t)(incl >> 32), kWave - 1);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Key of the lowest set slot of `pending` (the slot order is the entry order).
@@ -115,13 +116,15 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     const int lane = tid & (kWave - 1);
     const int wave = tid >> 6;
 
-    // ---- which slab and which group of it: lane l of every wave counts slab l's groups
+    // ---- which slab and which group of it: lane l of every wave counts slab l's
+    // groups (every lane loads, at a rank clamped into range: a load under a branch
+    // would be waited for where the branch joins)
     int groups = 0;
-    if (lane < R) {
+    {
         int64_t l0, h0;
-        slab_bounds(p.recv_gbl, lane, p.num_rows, &l0, &h0);
+        slab_bounds(p.recv_gbl, lane < R ? lane : R - 1, p.num_rows, &l0, &h0);
         const int64_t n = h0 - l0;
-        groups = n > 0 ? (int)((n + kGroupThreads - 1) / kGroupThreads) : 1;
+        groups = lane < R ? (n > 0 ? (int)((n + kGroupThreads - 1) / kGroupThreads) : 1) : 0;
     }
     const int ends = wave_inclusive_scan(groups);  // lane l: groups of slabs 0..l
     const int total_groups = readlane32(ends, kWave - 1);
@@ -134,18 +137,49 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     slab_bounds(p.recv_gbl, r, p.num_rows, &lo, &hi);
     const int64_t g0 = lo + (int64_t)group * kGroupThreads;  // this block's rows: [g0, min(g0 + 512, hi))
 
-    // this slab's segment sizes (er <= kMaxGroupExperts <= threads: one each)
-    const int32_t size_raw = tid < er ? p.aligned[(int64_t)r * er + tid] : 0;
+    // ---- this group's rows (one tile of 64 rows per wave, one row per lane): ids and
+    // weights, loaded first, together with the segment sizes below
+    bool bad = false, over = false;
+    const int64_t row = g0 + tid;
+    const bool in = row < hi;
+    const bool in_any = g0 < hi;  // the same for the whole block
+    int key[KB];
+    int rank[KB];        // rank of the slot among the tile's entries of its id
+    float wt[KB];        // the slot's weight (fetched with the ids when KB <= 16)
+    uint32_t valid = 0;  // bit j: slot j holds a local id of this slab
+    const bool want_w = p.grouped_w != nullptr;
+    // the row's ids (and weights, and token) loaded by every lane at once, at a row
+    // and slot clamped into range, before any is used
+    int64_t vid[KB];
+    int64_t src_tok = -1;
+    if (in_any) {  // block-uniform: rows exist
+        const int64_t lrow = in ? row : 0;
+#pragma unroll
+        for (int j = 0; j < KB; ++j) {
+            const int jj = j < K ? j : K - 1;
+            vid[j] = p.recv_idx[lrow * K + jj];
+            if (KB <= 16 && want_w) wt[j] = p.recv_w[lrow * K + jj];
+        }
+        if (p.tok_pos != nullptr) src_tok = p.src_info[lrow].y;
+    }
+    // this slab's segment sizes (er <= kMaxGroupExperts <= threads: one each) and
+    // the first pass of the sums below, loaded at once at clamped indices
+    const int64_t n_before = (int64_t)r * er, n_all = (int64_t)R * er;
+    const int32_t size_ld = p.aligned[(int64_t)r * er + (tid < er ? tid : 0)];
+    const int32_t before_ld = p.aligned[tid < n_before ? tid : 0];
+    const int32_t all_ld = p.aligned[tid < n_all ? tid : 0];
+    const int32_t size_raw = tid < er ? size_ld : 0;
 
     // ---- segment starts: the sizes of all segments of earlier slabs (a block sum),
     // then a scan over this slab's
-    int64_t part = 0, all = 0;
-    for (int64_t e = tid; e < (int64_t)r * er; e += kGroupThreads) {
+    int64_t part = tid < n_before && before_ld > 0 ? before_ld : 0, all = 0;
+    for (int64_t e = tid + kGroupThreads; e < n_before; e += kGroupThreads) {
         const int32_t a = p.aligned[e];
         part += a > 0 ? a : 0;
     }
     if (b == 0) {  // one block reports the total
-        for (int64_t e = tid; e < (int64_t)R * er; e += kGroupThreads) {
+        all = tid < n_all && all_ld > 0 ? all_ld : 0;
+        for (int64_t e = tid + kGroupThreads; e < n_all; e += kGroupThreads) {
             const int32_t a = p.aligned[e];
             all += a > 0 ? a : 0;
         }
@@ -184,24 +218,14 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
             for (int j = 0; j < KB; ++j)
                 if (pkey[u][j] >= 0) atomicAdd(&tile[pkey[u][j]], 1);
     }
-    // ---- this group's rows (one tile of 64 rows per wave, one row per lane): ids and weights
-    bool bad = false, over = false;
-    const int64_t row = g0 + tid;
-    const bool in = row < hi;
-    int key[KB];
-    int rank[KB];        // rank of the slot among the tile's entries of its id
-    float wt[KB];        // the slot's weight (fetched with the ids when KB <= 16)
-    uint32_t valid = 0;  // bit j: slot j holds a local id of this slab
-    const bool want_w = p.grouped_w != nullptr;
-    const int64_t src_tok = (p.tok_pos != nullptr && in) ? p.src_info[row].y : -1;
+    src_tok = in ? src_tok : -1;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
         key[j] = -1;
         rank[j] = 0;
-        wt[j] = 0.0f;
+        if (!(KB <= 16 && want_w) || !(j < K && in)) wt[j] = 0.0f;
         if (j < K && in) {
-            const int64_t v = p.recv_idx[row * K + j];
-            if (KB <= 16 && want_w) wt[j] = p.recv_w[row * K + j];
+            const int64_t v = vid[j];
             if (v >= 0 && v < er) {
                 key[j] = (int)v;
                 valid |= 1u << j;
