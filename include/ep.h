@@ -172,8 +172,8 @@ ep_status_t ep_notify(const ep_shape_t *s, const uint8_t *is_token_in_rank, cons
 /*
  * Stages 1+2 in one launch: ep_get_layout then ep_notify, from topk_idx to every output of
  * both, with the same values bit for bit.  [the sources of both stages]  The token masks are
- * built once and each 64-token chunk is counted from them in registers, so is_token_in_rank
- * is written (it is an output) but not read back, and one completion election replaces two.
+ * built once and each 64-token chunk is counted from them on chip, so is_token_in_rank is
+ * written (it is an output) but not read back, and one completion election replaces two.
  * Out: the four outputs of ep_get_layout and the seven of ep_notify (num_recv_tokens_host as
  *      there: non-NULL makes the call wait for the stream).
  * workspace: as for ep_notify (it is left as ep_notify leaves it, for ep_dispatch).
