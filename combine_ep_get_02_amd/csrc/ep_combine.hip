@@ -20,6 +20,12 @@
 // in ascending rank order into per-lane fp32 accumulators with v_fma_f32; the
 // wave ends with one bf16 store per element.  HBM traffic: the ~8 rows read per
 // token plus the one row written.
+// For wide rows and many tokens the outputs go out in bursts instead: a block
+// of 16 waves takes 8 consecutive tokens (their segments in turn), keeps the
+// bf16 results in LDS, and after its last gather writes the 8 rows as one
+// contiguous run.  Every result is computed the same way in both kernels.
+#include <mutex>
+
 #include "ep_internal.h"
 
 namespace ep {
@@ -74,13 +80,11 @@ __device__ __forceinline__ void fma_seg(float (&acc)[VPL][8], const u32x4 (&v)[V
     }
 }
 
-template <int VPL, bool EXACT, int WPB>
-__global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
-    const int lane = threadIdx.x & (kWave - 1);
-    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
-    if (w >= p.T * p.S) return;  // whole wave leaves together
-    const int64_t t = w / p.S;
-    const int seg = (int)(w - t * p.S);
+// One wave's task: token t, row segment seg.  Returns the segment's bf16
+// results (packed in pairs) in o; the segment-0 wave also flags bad slots and
+// writes the combined weights.
+template <int VPL, bool EXACT>
+__device__ __forceinline__ void combine_task(const CombineParams &p, int64_t t, int seg, int lane, u32x4 (&o)[VPL]) {
     const int K = p.K;
     const int64_t U = p.row_units;
     const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
@@ -160,17 +164,56 @@ __global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
         fetch(a, ra);
         fetch(b, rb);
     }
+#pragma unroll
+    for (int i = 0; i < VPL; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[i][k] = to_bf16(acc[i][2 * k]) | (to_bf16(acc[i][2 * k + 1]) << 16);
+}
 
+// One wave per (token, row segment); each wave stores its segment.
+template <int VPL, bool EXACT, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void combine_kernel(CombineParams p) {
+    const int lane = threadIdx.x & (kWave - 1);
+    const int64_t w = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
+    if (w >= p.T * p.S) return;  // whole wave leaves together
+    const int64_t t = w / p.S;
+    const int seg = (int)(w - t * p.S);
+    const int64_t U = p.row_units;
+    const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
+    u32x4 o[VPL];
+    combine_task<VPL, EXACT>(p, t, seg, lane, o);
     u32x4 *dst = p.out + t * U + c0;
 #pragma unroll
-    for (int i = 0; i < VPL; ++i) {
-        if (EXACT || c0 + i * kWave < U) {
-            u32x4 o;
+    for (int i = 0; i < VPL; ++i)
+        if (EXACT || c0 + i * kWave < U) __builtin_nontemporal_store(o[i], dst + i * kWave);
+}
+
+// TB consecutive tokens per block of WPB waves: the waves take the tokens'
+// segments in turn and keep the results in LDS (TB rows), then the block
+// writes the TB rows as one contiguous run.
+template <int VPL, bool EXACT, int TB, int WPB>
+__global__ __launch_bounds__(WPB *kWave) void combine_staged_kernel(CombineParams p) {
+    extern __shared__ u32x4 s_rows[];  // [TB][row_units]
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x >> 6;
+    const int64_t t0 = (int64_t)blockIdx.x * TB;
+    const int64_t U = p.row_units;
+    const int tasks = TB * p.S;
+    for (int k = wave; k < tasks; k += WPB) {
+        const int tl = k / p.S;
+        const int seg = k - tl * p.S;
+        if (t0 + tl >= p.T) break;  // the wave's later tasks are later tokens
+        u32x4 o[VPL];
+        combine_task<VPL, EXACT>(p, t0 + tl, seg, lane, o);
+        const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) o[k] = to_bf16(acc[i][2 * k]) | (to_bf16(acc[i][2 * k + 1]) << 16);
-            __builtin_nontemporal_store(o, dst + i * kWave);
-        }
+        for (int i = 0; i < VPL; ++i)
+            if (EXACT || c0 + i * kWave < U) s_rows[tl * U + c0 + i * kWave] = o[i];
     }
+    __syncthreads();
+    const int64_t rows = p.T - t0 < TB ? p.T - t0 : TB;
+    u32x4 *dst = p.out + t0 * U;
+    for (int64_t i = threadIdx.x; i < rows * U; i += WPB * kWave) __builtin_nontemporal_store(s_rows[i], dst + i);
 }
 
 template <int VPL, bool EXACT, int WPB>
@@ -180,6 +223,41 @@ hipError_t run(CombineParams p, hipStream_t stream) {
     const int64_t blocks = (waves + WPB - 1) / WPB;
     hipLaunchKernelGGL((combine_kernel<VPL, EXACT, WPB>), dim3((unsigned)blocks), dim3(WPB * kWave), 0, stream, p);
     return hipGetLastError();
+}
+
+// Staged form: 2 KiB segments, 8 tokens per block of 16 waves (fewer tokens when
+// 8 rows would not fit kStagedLds bytes of LDS).
+constexpr int kStagedWaves = 16;
+constexpr size_t kStagedLds = 112 * 1024;
+
+template <bool EXACT, int TB>
+hipError_t run_staged_tb(CombineParams p, hipStream_t stream) {
+    p.S = (int)((p.row_units + 2 * kWave - 1) / (2 * kWave));
+    const size_t lds = (size_t)TB * p.row_units * sizeof(u32x4);
+    static std::once_flag once;  // the kernel's dynamic LDS limit, raised once per process
+    static hipError_t attr = hipSuccess;
+    std::call_once(once, [] {
+        attr = hipFuncSetAttribute(reinterpret_cast<const void *>(&combine_staged_kernel<2, EXACT, TB, kStagedWaves>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)kStagedLds);
+    });
+    if (attr != hipSuccess) return attr;
+    const int64_t blocks = (p.T + TB - 1) / TB;
+    hipLaunchKernelGGL((combine_staged_kernel<2, EXACT, TB, kStagedWaves>), dim3((unsigned)blocks),
+                       dim3(kStagedWaves * kWave), lds, stream, p);
+    return hipGetLastError();
+}
+
+// Tokens per block of the staged form for these rows (0: the rows are too wide).
+int staged_tokens(int64_t row_units) {
+    const int64_t fit = (int64_t)(kStagedLds / (sizeof(u32x4) * (size_t)row_units));
+    return fit >= 8 ? 8 : fit >= 4 ? 4 : fit >= 2 ? 2 : 0;
+}
+
+hipError_t run_staged(const CombineParams &p, int tb, hipStream_t stream) {
+    const bool exact = p.row_units % (2 * kWave) == 0;
+    if (tb == 8) return exact ? run_staged_tb<true, 8>(p, stream) : run_staged_tb<false, 8>(p, stream);
+    if (tb == 4) return exact ? run_staged_tb<true, 4>(p, stream) : run_staged_tb<false, 4>(p, stream);
+    return exact ? run_staged_tb<true, 2>(p, stream) : run_staged_tb<false, 2>(p, stream);
 }
 
 hipError_t run_tiled(const CombineParams &p, int vpl, int wpb, hipStream_t stream) {
@@ -229,6 +307,10 @@ hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv
     p.K = s.num_topk;
     p.nrows = num_recv_rows;
     p.S = 1;
+    // rows of 14 KiB and more from 4096 tokens: the staged form (prefill 87 -> 82.5 us,
+    // skew 75.5 -> 72.3; 4 KiB rows at 16384 tokens were slower staged, 142 against 138)
+    const int tb = staged_tokens(p.row_units);
+    if (p.row_units >= 14 * kWave && p.T >= 4096 && tb > 0) return run_staged(p, tb, stream);
     int vpl, wpb;
     combine_tiling(p.row_units, p.T, &vpl, &wpb);
     return run_tiled(p, vpl, wpb, stream);
