@@ -173,6 +173,52 @@ def test_combine_flags_bad_send_slot():
     assert int(st.item()) == 8 and ref["status"] == 8
 
 
+# Combine of wide rows from 4096 tokens takes the staged form (consecutive tokens
+# per block, rows written from LDS): 8 tokens a block for 14 KiB rows, 4 up to
+# 28 KiB, 2 up to 56 KiB, the unstaged kernel beyond.  Ragged last blocks, rows
+# that are not whole 2 KiB segments, tokens with no row and a bad slot.
+STAGED = {
+    # name: (T, R, K, H, fraction of (token, rank) pairs with a row)
+    "eight_tokens_ragged_last_block": (4100, 8, 4, 7168, 0.5),
+    "four_tokens_rows_897_units": (4099, 8, 2, 7176, 0.5),
+    "four_tokens_20kib_rows": (4096, 8, 2, 10240, 0.4),
+    "two_tokens_32kib_rows_one_token_last": (4097, 4, 2, 16384, 0.5),
+    "two_tokens_56kib_rows": (4096, 2, 1, 28672, 0.5),
+    "unstaged_64kib_rows": (4096, 2, 1, 32768, 0.5),
+    "unstaged_below_4096_tokens": (4095, 8, 4, 7168, 0.5),
+}
+
+
+@pytest.mark.parametrize("name", sorted(STAGED))
+def test_combine_staged_shapes(name):
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+
+    T, R, K, Hd, frac = STAGED[name]
+    print(f"[parity] combine staged shape={name}", flush=True)
+    rng = np.random.default_rng(len(name) * 31 + T)
+    have = rng.random((T, R)) < frac
+    n = int(have.sum())
+    slot = np.full((T, R), -1, np.int32)
+    slot[have] = rng.permutation(n).astype(np.int32)
+    slot[T - 1, R - 1] = n + 3  # out of range: flagged, the row skipped
+    y = H.random_rows(rng, n, Hd)
+    rw = rng.random((n, K)).astype(np.float32)
+    ref = oracle.Oracle().combine(y, rw, slot, n)
+    shape = ep.make_shape(T, Hd, K, 2 * R, R, 4)
+    out = torch.empty((T, Hd), dtype=torch.bfloat16, device="cuda")
+    out.view(torch.int16).fill_(-1)
+    cw = torch.empty((T, K), dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_combine(shape, H.to_dev_bf16(y), torch.from_numpy(rw).cuda(), torch.from_numpy(slot).cuda(), n, out, cw, st)
+    torch.cuda.synchronize()
+    assert np.array_equal(H.bf16_host(out), ref["combined_x"])
+    assert np.array_equal(cw.cpu().numpy(), ref["combined_topk_weights"])
+    assert int(st.item()) == ref["status"] == 8
+
+
 # ---------------------------------------------------------------- fp8 rows and cached mode
 def _fp8_case(x, idx, w, E, R, C, num_scales_block=128, capacity=None):
     """GPU: layout, notify, ep_dispatch_fp8, then ep_dispatch_cached of the same
