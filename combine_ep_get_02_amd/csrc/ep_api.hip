@@ -345,32 +345,38 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
             return EP_ERR_INVALID_ARG;
         if (!aligned16(x) || !workspace_ok(s, workspace, workspace_bytes)) return EP_ERR_INVALID_ARG;
     }
-    // the pull form of the row copy reads each (token, slot)'s grouped position from the
-    // workspace: the metadata launch clears it, the positions launch fills it in
-    int32_t *tok_pos = nullptr;
-    if (group_pull_applies(*s, row_bytes / 16)) {
-        const Workspace w = workspace_layout(s->num_tokens, s->num_ranks, s->num_experts, s->num_channels,
-                                             s->num_topk);
-        tok_pos = reinterpret_cast<int32_t *>(static_cast<char *>(workspace) + w.tok_pos);
+    DispatchArgs d = {};
+    d.x = x;
+    d.row_units = row_bytes / 16;
+    d.topk_idx = topk_idx;
+    d.topk_w = topk_weights;
+    d.in_rank = is_token_in_rank;
+    d.gbl = gbl_channel_prefix_matrix;
+    d.recv_gbl = recv_gbl_rank_prefix_sum;
+    d.ws = static_cast<const char *>(workspace);
+    d.cap = recv_capacity;
+    d.recv_w = recv_topk_weights;
+    d.recv_idx = recv_topk_idx;
+    d.src_info = recv_src_info;
+    d.send_slot = send_slot;
+    d.dev_status = dev_status;
+    if (s->num_tokens > 0 && grouped_pull_applies(*s, row_bytes / 16)) {
+        // one launch: routing, receive metadata, positions in token order, grouped rows, padding
+        d.x_scales = x_scales;
+        d.num_scales = num_scales;
+        GroupedPullArgs g = {};
+        g.aligned = num_recv_tokens_per_expert;
+        g.cap = grouped_capacity;
+        g.grouped_x = grouped_x;
+        g.grouped_scales = grouped_x_scales;
+        g.grouped_row = grouped_row;
+        g.grouped_w = grouped_weights;
+        g.slot_pos = slot_pos;
+        g.num_grouped = num_grouped_rows;
+        return from_hip(launch_dispatch_grouped_pull(*s, d, g, stream));
     }
     if (s->num_tokens > 0) {
         // 1. the receive metadata, with no receive rows
-        DispatchArgs d = {};
-        d.x = x;
-        d.row_units = row_bytes / 16;
-        d.topk_idx = topk_idx;
-        d.topk_w = topk_weights;
-        d.in_rank = is_token_in_rank;
-        d.gbl = gbl_channel_prefix_matrix;
-        d.recv_gbl = recv_gbl_rank_prefix_sum;
-        d.ws = static_cast<const char *>(workspace);
-        d.cap = recv_capacity;
-        d.recv_w = recv_topk_weights;
-        d.recv_idx = recv_topk_idx;
-        d.src_info = recv_src_info;
-        d.send_slot = send_slot;
-        d.tok_pos = tok_pos;
-        d.dev_status = dev_status;
         hipError_t e = launch_dispatch(*s, d, stream);
         if (e != hipSuccess) return EP_ERR_HIP;
     }
@@ -382,8 +388,6 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
     a.from_x = true;
     a.topk_idx = topk_idx;
     a.send_slot = send_slot;
-    a.src_info = recv_src_info;
-    a.tok_pos = tok_pos;
     a.num_tokens = s->num_tokens;
     a.row_units = row_bytes / 16;
     a.recv_scales = x_scales;

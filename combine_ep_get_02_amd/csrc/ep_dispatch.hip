@@ -59,7 +59,6 @@ struct DispatchParams {
     int64_t *recv_idx;
     int32_t *src_info;
     int32_t *send_slot;
-    int32_t *tok_pos;
     int32_t *dev_status;
     int64_t T;
     int64_t Tc;         // tokens per channel, ceil(t / C)
@@ -205,12 +204,13 @@ __device__ __forceinline__ void copy_scales(const DispatchParams &p, int64_t t, 
 
 // send_slot of token t and the metadata (a4) of its rows: weights / local ids
 // of the topk slots living on each destination (lane j < k holds slot j's
-// expert id e and weight wt) and {my_rank, t} as the row's source.  tok_pos
-// (the grouped dispatch only) is cleared to -1 for the grouping to fill in.
+// expert id e and weight wt) and {my_rank, t} as the row's source.  With
+// slot_pos (dispatch straight into the grouped layout), lane j's grouped
+// position `pos` (or -1) goes to the row of slot j's rank, -1 to the others.
 __device__ __forceinline__ void token_metadata(const DispatchParams &p, int64_t t, int slot, uint64_t dests,
-                                               int64_t e, float wt, int lane) {
+                                               int64_t e, float wt, int lane, int32_t *slot_pos = nullptr,
+                                               int pos = -1) {
     if (lane < p.R) p.send_slot[t * p.R + lane] = slot;
-    if (p.tok_pos != nullptr && lane < p.K) p.tok_pos[t * p.K + lane] = -1;
     const int erank = (e >= 0 && e < p.E) ? (int)e / p.experts_per_rank : -1;
     for (uint64_t dd = dests; dd != 0ull; dd &= dd - 1ull) {
         const int r = __builtin_ctzll(dd);
@@ -219,6 +219,7 @@ __device__ __forceinline__ void token_metadata(const DispatchParams &p, int64_t 
             const bool on = erank == r;
             p.recv_w[s * p.K + lane] = on ? wt : 0.0f;
             if (p.recv_idx != nullptr) p.recv_idx[s * p.K + lane] = on ? e - (int64_t)r * p.experts_per_rank : -1;
+            if (slot_pos != nullptr) slot_pos[s * p.K + lane] = on ? pos : -1;
         }
         if (lane == 0) reinterpret_cast<int2 *>(p.src_info)[s] = make_int2(p.my_rank, (int)t);
     }
@@ -598,6 +599,579 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
     }
 }
 
+// ---------------------------------------------------------------- straight into the grouped layout
+// Dispatch straight into the grouped layout of ep_group.hip, pull form (from
+// 2048 tokens), in one launch.  A slab's rows follow their tokens, so in
+// (token, slot) order an entry's place inside its expert's segment is the
+// number of entries of that expert in earlier (token, slot) pairs: no pass in
+// receive order is needed.  Tokens go in groups of kGpTokens (two chunks); XCD
+// j owns groups j, j+8, ... as in the receive dispatch's pull form.  Every
+// block keeps per expert the received entries of all tokens before its current
+// group (counted by itself from topk_idx: the groups before its first, then
+// the seven groups between two of its own, their ids loaded while the current
+// group is copied), and ranks the current group's entries stably per expert: a
+// wave finds the lanes sharing its id with one ballot per id bit, the waves'
+// counts go to a byte table (expert x wave) and each entry adds those of the
+// waves before it.  With the segment starts that gives every entry's position.
+// Then, per group: its token tasks (send_slot, receive metadata, slot_pos,
+// grouped_row and weights) spread over the XCD's waves; its grouped rows in
+// position order (runs expert by expert) as tasks of U 1 KiB pieces over the
+// XCD's waves, x read again from the XCD's L2; its scales.  After the last
+// group the padding rows, over the whole grid.  Receive rows at or past the
+// capacity are the last rows of their slabs, so per rank a token index bounds
+// the received tokens; it is found once, and only when rows are dropped.
+constexpr int kGpTokens = 2 * kChunk;     // tokens per group
+constexpr int kGpWaves = 16;              // waves per block
+constexpr int kGpThreads = kGpWaves * kWave;
+constexpr int kGpBlocksPerXcd = 32;       // one block per CU
+constexpr int kGpMaxExperts = 2048;
+constexpr int kGpMaxEntries = kGpTokens * kMaxTopk;
+constexpr int kGpNoLimit = INT32_MAX;     // token threshold of a rank with no dropped row
+
+struct GroupedOut {
+    const int32_t *aligned;  // [E] segment sizes (a negative size counts as 0)
+    u32x4 *dst;              // [gcap][row]
+    float *dst_scales;       // [gcap][num_scales]
+    int32_t *grouped_row;    // [gcap]
+    float *grouped_w;        // [gcap], or null
+    int32_t *slot_pos;       // [cap][k]
+    int32_t *num_grouped;    // [1]
+    int64_t gcap;
+};
+
+// Expert ids of entries tid + n * kGpThreads of the tokens from a (-1 past the
+// last token and for an id that names no expert); clamped loads, so no branch
+// sits between them.
+template <int NE>
+__device__ __forceinline__ void gp_load_ids(const DispatchParams &p, int64_t a, int tid, int (&ids)[NE]) {
+    const int n_ent = kGpTokens * p.K;
+    const int64_t e0 = a * p.K, e_end = p.T * p.K;
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        const int i = tid + n * kGpThreads;
+        const bool in = i < n_ent && e0 + i < e_end;
+        const int64_t v = p.topk_idx[in ? e0 + i : 0];
+        ids[n] = in && v >= 0 && v < p.E ? (int)v : -1;
+    }
+}
+
+// Whether entry (token t, expert id v or -1) has a receive row: t is before its
+// rank's threshold when rows are dropped.
+__device__ __forceinline__ bool gp_received(const DispatchParams &p, int v, int64_t t, bool drops,
+                                            const int *s_thr) {
+    if (v < 0) return false;
+    return !drops || t < s_thr[v / p.experts_per_rank];
+}
+
+// The received entries of tokens [t0, t1) added to cnt per expert (LDS atomics).
+__device__ void gp_count(const DispatchParams &p, int64_t t0, int64_t t1, int tid, bool drops, const int *s_thr,
+                         int *cnt) {
+    constexpr int B = 4;
+    const int64_t i0 = t0 * p.K, i1 = t1 * p.K;
+    for (int64_t i = i0 + tid; i < i1; i += (int64_t)B * kGpThreads) {
+        int64_t v[B];
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int64_t at = i + (int64_t)u * kGpThreads;
+            v[u] = p.topk_idx[at < i1 ? at : i0];
+        }
+#pragma unroll
+        for (int u = 0; u < B; ++u) {
+            const int64_t at = i + (int64_t)u * kGpThreads;
+            const int id = v[u] >= 0 && v[u] < p.E ? (int)v[u] : -1;
+            if (at < i1 && gp_received(p, id, at / p.K, drops, s_thr)) atomicAdd(&cnt[id], 1);
+        }
+    }
+}
+
+// First token of rank r (wave-uniform) whose receive row is at or past the
+// capacity, or kGpNoLimit: the chunk is found from the workspace's offsets
+// (groups of four chunks, then the chunk), the token from the chunk's masks.
+__device__ int gp_rank_threshold(const DispatchParams &p, int r, int lane) {
+    const int slab0 = r > 0 ? p.recv_gbl[r - 1] : 0;
+    const int m = p.cap - slab0;  // receive rows of rank r below the capacity
+    if (m >= p.recv_gbl[r] - slab0) return kGpNoLimit;
+    if (m <= 0) return 0;
+    const int64_t Q = num_chunks(p.T), G4 = num_groups(p.T);
+    int64_t g4 = 0;  // the last group of chunks whose rows start at or before row m
+    for (int64_t b = 0; b < G4; b += kWave) {
+        const int64_t gi = b + lane;
+        const int v = p.rank_base[(gi < G4 ? gi : G4 - 1) * p.R + r];
+        const uint64_t le = ballot64(gi < G4 && v <= m);
+        if (le != 0ull) g4 = b + 63 - __builtin_clzll(le);
+        if (le != ~0ull) break;
+    }
+    const int64_t q = g4 * kGroupChunks + lane;
+    const bool qin = lane < kGroupChunks && q < Q;
+    const int off = p.rank_base[g4 * p.R + r] + p.rank_off[(qin ? q : g4 * kGroupChunks) * p.R + r];
+    const uint64_t lq = ballot64(qin && off <= m);
+    const int ql = lq != 0ull ? 63 - __builtin_clzll(lq) : 0;
+    const int64_t qs = g4 * kGroupChunks + ql;
+    const int k = m - readlane32(off, ql);
+    const int64_t tok = qs * kChunk + lane;
+    const uint64_t mk = p.mask[tok < p.T ? tok : p.T - 1];
+    const uint64_t col = ballot64(tok < p.T && ((mk >> r) & 1ull));
+    if (k < 0 || k >= __popcll(col)) {  // only with a workspace that disagrees with itself
+        const int64_t end = (qs + 1) * kChunk;
+        return (int)(end < p.T ? end : p.T);
+    }
+    return (int)(qs * kChunk + nth_set_bit(col, k));
+}
+
+// Sum of the bytes of v below byte w (w wave-uniform), and of all 16.
+__device__ __forceinline__ int bytes_below(u32x4 v, int w) {
+    int s = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+        const int nb = w - 4 * d;
+        const uint32_t keep = nb >= 4 ? 0xffffffffu : nb <= 0 ? 0u : (1u << (8 * nb)) - 1u;
+        s = (int)__builtin_amdgcn_sad_u8(v[d] & keep, 0u, (uint32_t)s);
+    }
+    return s;
+}
+__device__ __forceinline__ int bytes_sum(u32x4 v) {
+    uint32_t s = 0;
+#pragma unroll
+    for (int d = 0; d < 4; ++d) s = __builtin_amdgcn_sad_u8(v[d], 0u, s);
+    return (int)s;
+}
+
+// Exclusive scan of v[0..E) into out over the block (ept consecutive entries a
+// thread); returns the total.  Ends with a barrier.
+__device__ __forceinline__ int gp_block_scan(const int *v, int *out, int E, int tid, int *s_w32) {
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    const int ept = (E + kGpThreads - 1) / kGpThreads;
+    const int e_lo = tid * ept;
+    int run = 0;
+    for (int i = 0; i < ept; ++i)
+        if (e_lo + i < E) run += v[e_lo + i];
+    const int incl = wave_inclusive_scan(run);
+    if (lane == kWave - 1) s_w32[wave] = incl;
+    __syncthreads();
+    int before = incl - run, total = 0;
+    for (int w = 0; w < kGpWaves; ++w) {
+        if (w < wave) before += s_w32[w];
+        total += s_w32[w];
+    }
+    for (int i = 0; i < ept; ++i) {
+        if (e_lo + i < E) {
+            const int c = v[e_lo + i];
+            out[e_lo + i] = before;
+            before += c;
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
+// The group's counts per expert (earlier passes' in s_run plus the byte table's
+// rows) into s_run, and their exclusive scan over the experts into s_pre; the
+// byte table cleared for the next pass.  Returns the group's total.  Ends with a
+// barrier.
+__device__ __forceinline__ int gp_counts_scan(u32x4 *s_cnt, int *s_run, int *s_pre, bool add_run, int E, int tid,
+                                              int *s_w32) {
+    const int lane = tid & (kWave - 1), wave = tid >> 6;
+    const int ept = (E + kGpThreads - 1) / kGpThreads;
+    const int e_lo = tid * ept;
+    int run = 0;
+    for (int i = 0; i < ept; ++i) {
+        if (e_lo + i < E) {
+            const int c = (add_run ? s_run[e_lo + i] : 0) + bytes_sum(s_cnt[e_lo + i]);
+            s_run[e_lo + i] = c;
+            run += c;
+        }
+    }
+    const int incl = wave_inclusive_scan(run);
+    if (lane == kWave - 1) s_w32[wave] = incl;
+    __syncthreads();
+    for (int e = tid; e < E; e += kGpThreads) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
+    int before = incl - run, total = 0;
+    for (int w = 0; w < kGpWaves; ++w) {
+        if (w < wave) before += s_w32[w];
+        total += s_w32[w];
+    }
+    for (int i = 0; i < ept; ++i) {
+        if (e_lo + i < E) {
+            s_pre[e_lo + i] = before;
+            before += s_run[e_lo + i];
+        }
+    }
+    __syncthreads();
+    return total;
+}
+
+// The ids of the NB groups of tokens from t0 (entry tid of each), as expert ids
+// or -1, to be counted into s_base (only with one entry a thread).
+template <int NB>
+__device__ __forceinline__ void gp_load_groups(const DispatchParams &p, int64_t t0, int64_t t1, int tid,
+                                               int (&ids)[NB]) {
+    const int n_ent = kGpTokens * p.K;
+    const int64_t e0 = t0 * p.K, e_end = (t1 < p.T ? t1 : p.T) * p.K;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int64_t at = e0 + (int64_t)u * n_ent + tid;
+        const bool in = tid < n_ent && at < e_end;
+        const int64_t v = p.topk_idx[in ? at : 0];
+        ids[u] = in && v >= 0 && v < p.E ? (int)v : -1;
+    }
+}
+template <int NB>
+__device__ __forceinline__ void gp_count_groups(const DispatchParams &p, int64_t t0, int tid, const int (&ids)[NB],
+                                                bool drops, const int *s_thr, int *cnt) {
+    const int n_ent = kGpTokens * p.K;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+        const int64_t at = t0 * p.K + (int64_t)u * n_ent + tid;
+        if (gp_received(p, ids[u], at / p.K, drops, s_thr)) atomicAdd(&cnt[ids[u]], 1);
+    }
+}
+
+template <int U, bool EXACT, int NE>
+__global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(DispatchParams p, GroupedOut o) {
+    constexpr int NT = kGpThreads;
+    constexpr int NB = NE == 1 ? kXcds - 1 : 1;  // groups between two of an XCD's (counted from registers)
+    __shared__ int s_seg[kGpMaxExperts];    // segment start (clamped to INT32_MAX)
+    __shared__ int s_size[kGpMaxExperts];   // segment size
+    __shared__ int s_base[kGpMaxExperts];   // received entries in the tokens before the current group
+    __shared__ int s_run[kGpMaxExperts];    // the current group's received entries
+    __shared__ int s_pre[kGpMaxExperts];    // where the expert's run starts in the group's output
+    __shared__ u32x4 s_cnt[kGpMaxExperts];  // byte w: entries of wave w in the current pass
+    __shared__ int2 s_list[kGpMaxEntries];  // the group's output: {token in group, position}
+    __shared__ int s_epos[kGpMaxEntries];   // each entry's position, or -1
+    __shared__ int s_thr[kWave];            // per rank: first token with no receive row
+    __shared__ int64_t s_w64[kGpWaves];
+    __shared__ int s_w32[kGpWaves];
+    uint8_t *s_cnt8 = reinterpret_cast<uint8_t *>(s_cnt);
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid >> 6;
+    const int xcd = (int)(blockIdx.x % kXcds);
+    const int W = (int)(gridDim.x / kXcds) * kGpWaves;  // waves per XCD; the grid is a multiple of 8
+    const int wx = (int)(blockIdx.x / kXcds) * kGpWaves + __builtin_amdgcn_readfirstlane(wave);
+    const int K = p.K, E = p.E, R = p.R;
+    const int n_ent = kGpTokens * K;
+    const int64_t G = (p.T + kGpTokens - 1) / kGpTokens;
+    const int TPR = (int)((p.row_units + U * kWave - 1) / (U * kWave));  // tasks per row
+    const int nbits = E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    const int rl = lane < R ? lane : R - 1;
+    const int slab0 = (lane < R && lane > 0) ? p.recv_gbl[rl - 1 > 0 ? rl - 1 : 0] : 0;  // lane r: slab r's start
+
+    // ---- loads first: the first group's ids and routing, the segment sizes, the
+    // ids of the groups before it
+    int raw[NE];
+    if (xcd < G) gp_load_ids<NE>(p, (int64_t)xcd * kGpTokens, tid, raw);
+    const int ept = (E + NT - 1) / NT;
+    const int e_lo = tid * ept;
+    int al[2] = {0, 0};  // ept <= 2
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        if (i < ept) al[i] = o.aligned[e_lo + i < E ? e_lo + i : 0];
+    const int64_t g_first = xcd < G ? xcd : G;
+    int pc[NB];
+    if (NE == 1) gp_load_groups<NB>(p, 0, g_first * kGpTokens, tid, pc);
+    const int n_recv_all = p.recv_gbl[R - 1];
+
+    // ---- segment sizes and starts: a block scan over the experts
+    int64_t run = 0;
+    for (int i = 0; i < ept; ++i) {
+        if (e_lo + i < E) {
+            const int sz = al[i] > 0 ? al[i] : 0;
+            s_size[e_lo + i] = sz;
+            run += sz;
+        }
+    }
+    const int64_t incl = wave_inclusive_scan64(run);
+    if (lane == kWave - 1) s_w64[wave] = incl;
+    for (int e = tid; e < E; e += NT) {
+        s_base[e] = 0;
+        s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
+    }
+    // rows are dropped only when the capacity is below the receive total
+    const bool drops = n_recv_all > p.cap;
+    for (int r = wave; r < R; r += kGpWaves) {
+        const int thr = drops ? gp_rank_threshold(p, r, lane) : kGpNoLimit;
+        if (lane == 0) s_thr[r] = thr;
+    }
+    // slot_pos of the rows past the last slab (capacity slack): in no segment
+    {
+        int64_t hi = n_recv_all < p.cap ? n_recv_all : p.cap;
+        hi = hi > 0 ? hi : 0;
+        const int64_t gt = (int64_t)blockIdx.x * NT + tid, GT = (int64_t)gridDim.x * NT;
+        for (int64_t i = hi * K + gt; i < (int64_t)p.cap * K; i += GT) o.slot_pos[i] = -1;
+    }
+    __syncthreads();
+    int64_t before = incl - run, total = 0;
+    for (int w = 0; w < kGpWaves; ++w) {
+        if (w < wave) before += s_w64[w];
+        total += s_w64[w];
+    }
+    for (int i = 0; i < ept; ++i) {
+        if (e_lo + i < E) {
+            s_seg[e_lo + i] = (int)(before < INT32_MAX ? before : INT32_MAX);
+            before += s_size[e_lo + i];
+        }
+    }
+    const int64_t limit = total < o.gcap ? total : o.gcap;
+    if (blockIdx.x == 0 && tid == 0) o.num_grouped[0] = (int32_t)(total < INT32_MAX ? total : INT32_MAX);
+    // the entries of the tokens before this XCD's first group
+    if (NE == 1)
+        gp_count_groups<NB>(p, 0, tid, pc, drops, s_thr, s_base);
+    else
+        gp_count(p, 0, g_first * kGpTokens < p.T ? g_first * kGpTokens : p.T, tid, drops, s_thr, s_base);
+    __syncthreads();
+
+    // ---- the routing inputs checked against the workspace, one group a wave of
+    // XCD 0 (whose blocks have no tokens to count before their first group)
+    if (xcd == 0) {
+        for (int64_t g = wx; g < G; g += W) {
+            const int64_t a = g * kGpTokens, q0 = g * 2;
+            uint64_t col[2];
+#pragma unroll
+            for (int c = 0; c < 2; ++c) col[c] = transpose64(token_mask(p, a + c * kChunk + lane, false));
+            const int off = p.rank_base[(q0 / kGroupChunks) * R + rl] + p.rank_off[q0 * R + rl];
+            const int alt = derive_offset<2>(p, a, col, lane, false);
+            if (anchors_disagree<2>(p, a, col, off, alt, slab0, lane) && lane == 0)
+                flag(p.dev_status, EP_DEV_COUNT_MISMATCH);
+        }
+    }
+
+    // the first group's keys (the next group's are made during each group, before
+    // its copies, from ids loaded at its start)
+    int key_c[NE];
+#pragma unroll
+    for (int n = 0; n < NE; ++n)
+        key_c[n] = gp_received(p, raw[n], (int64_t)xcd * kGpTokens + (tid + n * NT) / K, drops, s_thr) ? raw[n] : -1;
+
+    for (int64_t g = xcd; g < G; g += kXcds) {
+        const int64_t a = g * kGpTokens;  // the group's first token
+        const bool next = g + kXcds < G;
+        int key[NE], rank[NE];
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            key[n] = key_c[n];
+            rank[n] = 0;
+        }
+        // ---- loads issued now and used after the positions, by when this wave's
+        // stores of the last group have long completed (a load used right away
+        // would wait for them): the next group's ids, and the ids of the groups up
+        // to it
+        if (next) gp_load_ids<NE>(p, (g + kXcds) * kGpTokens, tid, raw);
+        int ob[NB];
+        if (NE == 1) gp_load_groups<NB>(p, a + kGpTokens, a + (int64_t)kXcds * kGpTokens, tid, ob);
+
+        // ---- stable ranks of the group's entries per expert, pass by pass
+        int total_g = 0;
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            const int kk = key[n];
+            uint64_t peers = ballot64(kk >= 0);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = ((kk >> b) & 1) != 0;
+                const uint64_t B = ballot64(bit);
+                peers &= bit ? B : ~B;
+            }
+            const int inw = __popcll(peers & lt);
+            if (kk >= 0 && inw == 0) s_cnt8[kk * 16 + wave] = (uint8_t)__popcll(peers);
+            __syncthreads();
+            if (kk >= 0) rank[n] = (n > 0 ? s_run[kk] : 0) + bytes_below(s_cnt[kk], wave) + inw;
+            if (n > 0) __syncthreads();  // s_run is read before it moves on
+            if (n + 1 < NE) {
+                for (int e = tid; e < E; e += NT) s_run[e] = (n > 0 ? s_run[e] : 0) + bytes_sum(s_cnt[e]);
+                __syncthreads();
+                for (int e = tid; e < E; e += NT) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
+                __syncthreads();
+            } else {
+                total_g = gp_counts_scan(s_cnt, s_run, s_pre, n > 0, E, tid, s_w32);
+            }
+        }
+
+        // ---- positions: segment start + entries before the group + rank
+        bool over = false;
+#pragma unroll
+        for (int n = 0; n < NE; ++n) {
+            const int i = tid + n * NT;
+            if (i < n_ent) {
+                const int kk = key[n];
+                int at = -1;
+                if (kk >= 0) {
+                    const int64_t li = (int64_t)s_base[kk] + rank[n];
+                    const int64_t pos = (int64_t)s_seg[kk] + li;
+                    const bool placed = li < s_size[kk] && pos < limit;
+                    if (placed) at = (int)pos;
+                    over |= !placed;
+                    s_list[s_pre[kk] + rank[n]] = make_int2(placed ? i / K : -1, at);
+                }
+                s_epos[i] = at;
+            }
+        }
+        if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+        __syncthreads();
+        // ---- the next group's keys, from the loads above
+        if (next) {
+            const int64_t an = (g + kXcds) * kGpTokens;
+#pragma unroll
+            for (int n = 0; n < NE; ++n)
+                key_c[n] = gp_received(p, raw[n], an + (tid + n * NT) / K, drops, s_thr) ? raw[n] : -1;
+        }
+        // ---- entries before this XCD's next group: this group's, then the groups
+        // up to it (s_base is next read after the group's last barrier)
+        for (int e = tid; e < E; e += NT)
+            if (s_run[e] != 0) atomicAdd(&s_base[e], s_run[e]);
+        if (NE == 1) gp_count_groups<NB>(p, a + kGpTokens, tid, ob, drops, s_thr, s_base);
+
+        // ---- token tasks: send_slot, receive metadata, slot_pos, grouped_row and
+        // weights (more than one per wave only when the XCD has fewer waves than
+        // the group has tokens)
+        const int rot = (int)(((g / kXcds) * kGpTokens) % W);
+        const int kt = wx >= rot ? wx - rot : wx - rot + W;
+        for (int k = kt; k < kGpTokens; k += W) {
+            const int64_t t = a + k;
+            if (t >= p.T) break;  // wave-uniform; later k are larger
+            // the token's chunk: lane r holds rank r's column and where the chunk's
+            // rows start in slab r (the group's offset plus the first chunk's rows)
+            const int c = k / kChunk, l = k - c * kChunk;
+            const uint64_t m0 = token_mask(p, a + lane, false);
+            const uint64_t m1 = token_mask(p, a + kChunk + lane, false);
+            const int off0 = p.rank_base[((g * 2) / kGroupChunks) * R + rl] + p.rank_off[(g * 2) * R + rl];
+            const int jl = lane < K ? lane : K - 1;
+            const int64_t e_ld = p.topk_idx[t * K + jl];
+            const float w_ld = p.topk_w[t * K + jl];
+            const bool in = p.in_rank[t * R + rl] != 0;
+            const int pos_ld = s_epos[k * K + jl];
+            const int64_t e = lane < K ? e_ld : -1;
+            const float wt = lane < K ? w_ld : 0.0f;
+            const int pos = lane < K ? pos_ld : -1;
+            const uint64_t c0 = transpose64(m0);
+            const uint64_t cc = c == 0 ? c0 : transpose64(m1);
+            const int base = (lane < R ? slab0 + off0 : 0) + (c == 0 ? 0 : (int)__popcll(c0));
+            const bool routed = lane < R && ((cc >> l) & 1ull);
+            // the workspace's mask must be this token's is_token_in_rank row
+            if (ballot64((lane < R && in) != routed) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_STALE_WORKSPACE);
+            int slot = routed ? base + __popcll(cc & ((1ull << l) - 1ull)) : -1;
+            const bool drop = routed && (slot < 0 || slot >= p.cap);  // a negative row only from bad prefixes
+            if (drop) slot = -1;
+            if (ballot64(drop) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
+            const uint64_t dests = ballot64(slot >= 0);
+            token_metadata(p, t, slot, dests, e, wt, lane, o.slot_pos, pos);
+            // a placed entry's row: the receive row of its rank
+            const int er = (e >= 0 && e < E) ? (int)e / p.experts_per_rank : 0;
+            const int srow = __shfl(slot, er, kWave);
+            if (pos >= 0) {
+                o.grouped_row[pos] = srow;
+                if (o.grouped_w != nullptr) o.grouped_w[pos] = wt;
+            }
+        }
+
+        // ---- the group's grouped rows in position order: task k is piece-run
+        // (k % TPR) of output entry (k / TPR); the wave's tasks k = wx + n*W are
+        // resolved 64 at a time, lane i taking n = base + i, and read back with
+        // two readlanes each
+        const int tasks = total_g * TPR;
+        for (int base = 0; wx + base * W < tasks; base += kWave) {
+            int rt_pos, rt_pack;  // lane i: the task's position; token in group | part << 8 | ok << 30
+            {
+                const int kk = wx + (base + lane) * W;
+                const bool valid = kk < tasks;
+                const int k = valid ? kk : 0;
+                const int ent = k / TPR, part = k - ent * TPR;
+                const int2 le = s_list[ent];
+                const bool ok = valid && le.x >= 0;
+                rt_pos = ok ? le.y : 0;
+                rt_pack = (ok ? le.x : 0) | (part << 8) | ((int)ok << 30);
+            }
+            const int nb = (tasks - wx - base * W + W - 1) / W;  // tasks of this batch
+            const int nbatch = nb < kWave ? nb : kWave;
+            for (int j = 0; j < nbatch; ++j) {
+                // U loads, then U stores; lanes past a ragged row end load from a
+                // valid place and skip their store
+                const int pk = readlane32(rt_pack, j);
+                const int64_t at = readlane32(rt_pos, j);
+                const bool ok = (pk >> 30) != 0;
+                const int64_t t = a + (pk & 0xff);
+                const int part = (pk >> 8) & 0x3fffff;
+                const int64_t first = (int64_t)part * U * kWave;
+                const int lim = (int)(p.row_units - first);
+                const u32x4 *src = p.x + t * p.row_units + first;
+                u32x4 *dst = o.dst + at * p.row_units + first;
+                u32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const int cu = u * kWave + lane;
+                    v[u] = src[(EXACT || cu < lim) ? cu : lim - 1];
+                }
+                asm volatile("" ::: "memory");
+                if (ok) {
+#pragma unroll
+                    for (int u = 0; u < U; ++u) {
+                        const int cu = u * kWave + lane;
+                        if (EXACT || cu < lim) __builtin_nontemporal_store(v[u], dst + cu);
+                    }
+                }
+            }
+        }
+        // ---- the scales: output entry e = wx, wx + W, ..., lanes over the token's
+        // scales (a wave-uniform loop with a per-lane predicate)
+        if (p.num_scales > 0) {
+            for (int e = wx; e < total_g; e += W) {
+                const int2 le = s_list[e];
+                const int tl = __builtin_amdgcn_readfirstlane(le.x);
+                const int64_t at = __builtin_amdgcn_readfirstlane(le.y);
+                if (tl < 0) continue;  // wave-uniform
+                const int64_t t = a + tl;
+                for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
+                    const int i = i0 + lane;
+                    const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
+                    if (i < p.num_scales) o.dst_scales[at * p.num_scales + i] = sc;
+                }
+            }
+        }
+        if (NE != 1) {
+            const int64_t t1 = a + (int64_t)kXcds * kGpTokens;
+            gp_count(p, a + kGpTokens, t1 < p.T ? t1 : p.T, tid, drops, s_thr, s_base);
+        }
+        __syncthreads();  // every wave is done with the group's tables before they are rebuilt
+    }
+
+    // ---- padding: positions [start + placed, start + size) of every segment below
+    // the limit (every block holds the same counts now), over the grid's waves
+    for (int e = tid; e < E; e += NT) {
+        const int64_t st = s_seg[e], sz = s_size[e];
+        const int64_t used = s_base[e] < sz ? s_base[e] : sz;
+        const int64_t end = st + sz < limit ? st + sz : limit;
+        const int64_t n = end - (st + used);
+        s_run[e] = n > 0 ? (int)n : 0;
+    }
+    __syncthreads();
+    const int P = gp_block_scan(s_run, s_pre, E, tid, s_w32);
+    const int64_t gw = (int64_t)blockIdx.x * kGpWaves + wave, GW = (int64_t)gridDim.x * kGpWaves;
+    const u32x4 z = {0u, 0u, 0u, 0u};
+    for (int64_t b0 = gw * kWave; b0 < P; b0 += GW * kWave) {
+        // lane i: padding row b0 + i -- its expert (the last with s_pre <= it) and position
+        const int64_t k = b0 + lane;
+        int lo = 0, hi = E - 1;
+        while (lo < hi) {  // per-lane binary search; at most 11 steps
+            const int mid = (lo + hi + 1) >> 1;
+            if (s_pre[mid] <= k) lo = mid; else hi = mid - 1;
+        }
+        const int64_t st = s_seg[lo], sz = s_size[lo];
+        const int64_t used = s_base[lo] < sz ? s_base[lo] : sz;
+        const int pos = (int)(st + used + (k - s_pre[lo]));
+        if (k < P) {
+            o.grouped_row[pos] = -1;
+            if (o.grouped_w != nullptr) o.grouped_w[pos] = 0.0f;
+        }
+        const int64_t nb = P - b0 < kWave ? P - b0 : kWave;
+        for (int j = 0; j < nb; ++j) {
+            const int64_t at = readlane32(pos, j);
+            u32x4 *d = o.dst + at * p.row_units;
+            for (int64_t u = lane; u < p.row_units; u += kWave) __builtin_nontemporal_store(z, d + u);
+            for (int i0 = 0; i0 < p.num_scales; i0 += kWave)  // wave-uniform, per-lane predicate
+                if (i0 + lane < p.num_scales) o.dst_scales[at * p.num_scales + i0 + lane] = 0.0f;
+        }
+    }
+}
+
 template <int CPG, int U, bool EXACT, int WPB>
 hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
     const dim3 grid((unsigned)(kXcds * blocks_per_xcd)), block(WPB * kWave);
@@ -719,19 +1293,33 @@ void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, 
     }
 }
 
-}  // namespace
-
-// Metadata only (no receive rows): send_slot, weights, local ids, src_info,
-// one wave per token.
-hipError_t run_meta(DispatchParams p, hipStream_t stream) {
-    p.S = 1;
-    const int64_t blocks = (p.T + 7) / 8;
-    hipLaunchKernelGGL((dispatch_kernel<0, true, 8, 0, false>), dim3((unsigned)blocks), dim3(8 * kWave), 0, stream, p);
+template <int U, bool EXACT, int NE>
+hipError_t run_grouped_pull(const DispatchParams &p, const GroupedOut &o, hipStream_t stream) {
+    hipLaunchKernelGGL((dispatch_grouped_pull_kernel<U, EXACT, NE>), dim3((unsigned)(kXcds * kGpBlocksPerXcd)),
+                       dim3(kGpThreads), 0, stream, p, o);
     return hipGetLastError();
 }
 
-hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream) {
-    if (s.num_tokens == 0) return hipSuccess;
+// Pieces per task as for the receive dispatch's pull form: 1 for rows of 14 KiB
+// and more, 2 from 7 KiB, else 4 (2 with more than 8 slots a token), so that
+// the 1024-thread blocks keep to 128 registers with nothing spilled.
+template <int NE>
+hipError_t run_grouped_pull_tiled(const DispatchParams &p, const GroupedOut &o, hipStream_t stream) {
+    const int64_t ru = p.row_units;
+    const int u = ru >= 14 * kWave ? 1 : ru >= 7 * kWave || NE > 1 ? 2 : 4;
+    const bool exact = ru % (u * kWave) == 0;
+#define EP_GP_CASE(UU) \
+    if (u == UU) return exact ? run_grouped_pull<UU, true, NE>(p, o, stream) : run_grouped_pull<UU, false, NE>(p, o, stream);
+    EP_GP_CASE(1)
+    EP_GP_CASE(2)
+    if constexpr (NE == 1) {
+        EP_GP_CASE(4)
+    }
+#undef EP_GP_CASE
+    return hipErrorInvalidValue;
+}
+
+DispatchParams make_params(const ep_shape_t &s, const DispatchArgs &a) {
     DispatchParams p;
     p.x = reinterpret_cast<const u32x4 *>(a.x);
     p.x_scales = a.x_scales;
@@ -763,7 +1351,6 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.recv_idx = a.recv_idx;
     p.src_info = a.src_info;
     p.send_slot = a.send_slot;
-    p.tok_pos = a.tok_pos;
     p.dev_status = a.dev_status;
     p.T = s.num_tokens;
     p.row_units = a.row_units;
@@ -775,6 +1362,23 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     p.cap = a.cap;
     p.num_scales = a.num_scales;
     p.S = 1;
+    return p;
+}
+
+}  // namespace
+
+// Metadata only (no receive rows): send_slot, weights, local ids, src_info,
+// one wave per token.
+hipError_t run_meta(DispatchParams p, hipStream_t stream) {
+    p.S = 1;
+    const int64_t blocks = (p.T + 7) / 8;
+    hipLaunchKernelGGL((dispatch_kernel<0, true, 8, 0, false>), dim3((unsigned)blocks), dim3(8 * kWave), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream) {
+    if (s.num_tokens == 0) return hipSuccess;
+    DispatchParams p = make_params(s, a);
     if (p.recv_x == nullptr && p.cached_slot == nullptr) {
         p.num_scales = 0;  // no rows, so no scales beside them
         return run_meta(p, stream);
@@ -787,6 +1391,28 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
     int vpl, wpb, gran;
     dispatch_tiling(p.row_units, p.T, &vpl, &wpb, &gran);
     return run_tiled(p, vpl, wpb, gran, stream);
+}
+
+bool grouped_pull_applies(const ep_shape_t &s, int64_t row_units) {
+    return s.num_tokens >= 2048 && row_units >= kWave && row_units <= kMaxPullRowUnits &&
+           s.num_experts <= kGpMaxExperts && s.num_topk <= kMaxTopk;
+}
+
+hipError_t launch_dispatch_grouped_pull(const ep_shape_t &s, const DispatchArgs &a, const GroupedPullArgs &g,
+                                        hipStream_t stream) {
+    if (s.num_tokens == 0) return hipSuccess;
+    if (a.ws == nullptr || !grouped_pull_applies(s, a.row_units)) return hipErrorInvalidValue;
+    const DispatchParams p = make_params(s, a);
+    GroupedOut o;
+    o.aligned = g.aligned;
+    o.dst = reinterpret_cast<u32x4 *>(g.grouped_x);
+    o.dst_scales = g.grouped_scales;
+    o.grouped_row = g.grouped_row;
+    o.grouped_w = g.grouped_w;
+    o.slot_pos = g.slot_pos;
+    o.num_grouped = g.num_grouped;
+    o.gcap = g.cap;
+    return s.num_topk <= 8 ? run_grouped_pull_tiled<1>(p, o, stream) : run_grouped_pull_tiled<4>(p, o, stream);
 }
 
 }  // namespace ep

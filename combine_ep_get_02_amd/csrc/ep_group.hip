@@ -26,12 +26,11 @@
 //  copy: one wave per grouped row copies the receive row it names (zeros for
 //   padding) with 16-byte non-temporal loads and stores; the grouped rows are
 //   written in order, as one contiguous stream.
-// Straight from x (ep_dispatch_grouped, after its metadata launch): the same
-// positions launch, which also records each (token, slot)'s position by token,
-// then the rows: from 2048 tokens in position order, one token group per XCD at
-// a time, padding included (group_pull_kernel); otherwise each token's row
-// pushed to its positions (group_push_kernel) and the padding zeroed after it
-// (group_pad_kernel).
+// Straight from x (ep_dispatch_grouped below 2048 tokens, after its metadata
+// launch): the same positions launch, then each token's row pushed to its
+// positions (group_push_kernel) and the padding zeroed after it
+// (group_pad_kernel).  From 2048 tokens the whole call is one launch in
+// ep_dispatch.hip, which finds the same positions in token order.
 #include "ep_internal.h"
 
 namespace ep {
@@ -53,28 +52,9 @@ struct PositionParams {
     int32_t *slot_pos;
     int32_t *num_grouped;
     int32_t *dev_status;
-    const int2 *src_info;  // with tok_pos: the token of each row
-    int32_t *tok_pos;      // [T][K], or null: the position of each (token, slot) too
-    int64_t num_rows, cap, T;
+    int64_t num_rows, cap;
     int R, K, er;
 };
-
-// Inclusive prefix sum over the wave of non-negative values below 2^41 (the
-// segment sizes summed here are int32 counts, at most 64 a lane): the low 16
-// bits and the rest are scanned as two 32-bit DPP scans (each sum stays below
-// 2^31 over 64 lanes) and recombined exactly.
-__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
-    const int lo = wave_inclusive_scan((int)(v & 0xffff));
-    const int hi = wave_inclusive_scan((int)(v >> 16));
-    return ((int64_t)hi << 16) + lo;
-}
-
-__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
-    const int64_t incl = wave_inclusive_scan64(v);
-    const uint32_t lo = (uint32_t)readlane32((int)(uint32_t)incl, kWave - 1);
-    const uint32_t hi = (uint32_t)readlane32((int)(uint32_t)(incl >> 32), kWave - 1);
-    return (int64_t)(((uint64_t)hi << 32) | lo);
-}
 
 // Key of the lowest set slot of `pending` (the slot order is the entry order).
 template <int KB>
@@ -151,7 +131,6 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
     // the row's ids (and weights, and token) loaded by every lane at once, at a row
     // and slot clamped into range, before any is used
     int64_t vid[KB];
-    int64_t src_tok = -1;
     if (in_any) {  // block-uniform: rows exist
         const int64_t lrow = in ? row : 0;
 #pragma unroll
@@ -160,7 +139,6 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
             vid[j] = p.recv_idx[lrow * K + jj];
             if (KB <= 16 && want_w) wt[j] = p.recv_w[lrow * K + jj];
         }
-        if (p.tok_pos != nullptr) src_tok = p.src_info[lrow].y;
     }
     // this slab's segment sizes (er <= kMaxGroupExperts <= threads: one each) and
     // the first pass of the sums below, loaded at once at clamped indices
@@ -218,7 +196,6 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
             for (int j = 0; j < KB; ++j)
                 if (pkey[u][j] >= 0) atomicAdd(&tile[pkey[u][j]], 1);
     }
-    src_tok = in ? src_tok : -1;
 #pragma unroll
     for (int j = 0; j < KB; ++j) {
         key[j] = -1;
@@ -310,9 +287,6 @@ __global__ __launch_bounds__(kGroupThreads) void group_positions_kernel(Position
                 }
             }
             if (p.slot_pos != nullptr) p.slot_pos[row * K + j] = at;
-            // a slot of this slab's rank: the one row of its token that names it
-            if (p.tok_pos != nullptr && ((valid >> j) & 1u) && src_tok >= 0 && src_tok < p.T)
-                p.tok_pos[src_tok * K + j] = at;
         }
     }
 
@@ -467,252 +441,6 @@ __global__ __launch_bounds__(256) void group_pad_kernel(const int32_t *grouped_r
         if (i0 + lane < num_scales) dst_scales[g * num_scales + i0 + lane] = 0.0f;
 }
 
-// ---- straight from x, pull form (many tokens): the grouped rows are produced
-// in position order.  Tokens are taken in groups of kPullTokens; XCD j owns
-// groups j, j+8, ...  Inside a segment the entries follow their tokens, so a
-// group's entries of expert e form one contiguous run of segment e, and the
-// group's output is its runs in expert order.  Every block of the XCD puts the
-// group's entries in that order in LDS (per expert: the count and the lowest
-// position, with LDS atomics; an exclusive scan of the counts; then each entry
-// at its run's offset plus its distance from the run's first position), and
-// the XCD's waves cut the output into tasks of U 1 KiB pieces, taking tasks
-// k, k+W, k+2W, ... (W = the XCD's wave count; the scales follow in a pass of
-// their own over the group's entries).  So the XCD writes one
-// advancing window, and every row of x it reads again after the first time
-// is in its L2.  The entries (each slot's position, written by the positions
-// pass, and its expert id) of the block's next group are loaded before the
-// current group's copies.  Padding rows are zeroed first, by the whole grid.
-constexpr int kPullTokens = 128;         // tokens per group
-constexpr int kPullMaxExperts = 2048;
-constexpr int kPullXcds = 8;             // XCDs; consecutive workgroup ids go round-robin over them
-constexpr int kPullWaves = 16;           // waves per block
-constexpr int kPullBlocksPerXcd = 32;    // one block per CU
-constexpr int64_t kPullMinTokens = 2048;
-constexpr int64_t kPullMaxRowUnits = 1 << 16;
-
-struct PullParams {
-    const u32x4 *x;
-    const float *x_scales;
-    const int64_t *topk_idx;
-    const int32_t *tok_pos;      // [T][K] grouped position of each (token, slot), or -1
-    const int32_t *grouped_row;  // -1 marks padding
-    const int32_t *num_grouped;
-    u32x4 *dst;
-    float *dst_scales;
-    int32_t *dev_status;
-    int64_t T, row_units, cap;
-    int K, E, num_scales;
-};
-
-// Entries i = tid + n * NT of group g, in [token][slot] order: position and raw expert id.
-template <int NE, int NT>
-__device__ __forceinline__ void load_pull_entries(const PullParams &p, int64_t g, int tid, int (&pos)[NE],
-                                                  int64_t (&raw)[NE]) {
-    const int n_ent = kPullTokens * p.K;
-    const int64_t e0 = g * kPullTokens * p.K;
-    const int64_t e_end = p.T * p.K;
-#pragma unroll
-    for (int n = 0; n < NE; ++n) {
-        const int i = tid + n * NT;
-        pos[n] = -1;
-        raw[n] = -1;
-        if (i < n_ent && e0 + i < e_end) {
-            pos[n] = p.tok_pos[e0 + i];
-            raw[n] = p.topk_idx[e0 + i];
-        }
-    }
-}
-
-template <int U, bool EXACT, int NE>
-__global__ __launch_bounds__(kPullWaves *kWave) void group_pull_kernel(PullParams p) {
-    constexpr int NT = kPullWaves * kWave;
-    __shared__ int s_cnt[kPullMaxExperts];  // entries of the group per expert
-    __shared__ int s_min[kPullMaxExperts];  // their lowest position
-    __shared__ int s_pre[kPullMaxExperts];  // where the expert's run starts in the group's output
-    __shared__ int2 s_list[kPullTokens * kMaxTopk];  // the group's output: {token in group, position}
-    __shared__ int s_wsum[kPullWaves];
-    __shared__ int s_total;
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid >> 6;
-    const int xcd = (int)(blockIdx.x % kPullXcds);
-    const int W = (int)(gridDim.x / kPullXcds) * kPullWaves;  // waves per XCD; the grid is a multiple of 8
-    const int wx = (int)(blockIdx.x / kPullXcds) * kPullWaves + __builtin_amdgcn_readfirstlane(wave);
-    const int K = p.K, E = p.E;
-    const int n_ent = kPullTokens * K;
-    int64_t limit = p.num_grouped[0];
-    limit = limit < p.cap ? limit : p.cap;
-    const int64_t G = (p.T + kPullTokens - 1) / kPullTokens;
-    const int TPR = (int)((p.row_units + U * kWave - 1) / (U * kWave));  // tasks per row
-
-    int pos[NE];
-    int64_t raw[NE];
-    if (xcd < G) load_pull_entries<NE, NT>(p, xcd, tid, pos, raw);
-
-    // ---- padding rows: zero row and scales (one position per lane, the grid's waves in turn)
-    {
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        const int64_t gw = (int64_t)blockIdx.x * kPullWaves + wave;
-        const int64_t GW = (int64_t)gridDim.x * kPullWaves;
-        for (int64_t b0 = gw * kWave; b0 < limit; b0 += GW * kWave) {
-            const int64_t q = b0 + lane;
-            const bool pad = q < limit && p.grouped_row[q] == -1;
-            for (uint64_t pp = ballot64(pad); pp != 0ull; pp &= pp - 1ull) {
-                const int64_t g = b0 + __builtin_ctzll(pp);
-                u32x4 *d = p.dst + g * p.row_units;
-                for (int64_t u = lane; u < p.row_units; u += kWave) __builtin_nontemporal_store(z, d + u);
-                for (int i0 = 0; i0 < p.num_scales; i0 += kWave)  // wave-uniform, per-lane predicate
-                    if (i0 + lane < p.num_scales) p.dst_scales[g * p.num_scales + i0 + lane] = 0.0f;
-            }
-        }
-    }
-
-    bool bad = false;
-    for (int64_t g = xcd; g < G; g += kPullXcds) {
-        // ---- the group's entries in position order
-        for (int e = tid; e < E; e += NT) {
-            s_cnt[e] = 0;
-            s_min[e] = INT32_MAX;
-        }
-        for (int i = tid; i < n_ent; i += NT) s_list[i] = make_int2(-1, -1);
-        __syncthreads();
-        int key[NE];
-#pragma unroll
-        for (int n = 0; n < NE; ++n) {
-            key[n] = (pos[n] >= 0 && pos[n] < limit && raw[n] >= 0 && raw[n] < E) ? (int)raw[n] : -1;
-            if (key[n] >= 0) {
-                atomicAdd(&s_cnt[key[n]], 1);
-                atomicMin(&s_min[key[n]], pos[n]);
-            }
-        }
-        __syncthreads();
-        {  // exclusive scan of the counts over the experts (a run of ept experts per thread)
-            const int ept = (E + NT - 1) / NT;
-            const int e_lo = tid * ept;
-            int run = 0;
-            for (int i = 0; i < ept; ++i)
-                if (e_lo + i < E) run += s_cnt[e_lo + i];
-            const int incl = wave_inclusive_scan(run);
-            if (lane == kWave - 1) s_wsum[wave] = incl;
-            __syncthreads();
-            int before = incl - run;
-            for (int w2 = 0; w2 < wave; ++w2) before += s_wsum[w2];
-            if (tid == NT - 1) s_total = before + run;
-            for (int i = 0; i < ept; ++i) {
-                if (e_lo + i < E) {
-                    s_pre[e_lo + i] = before;
-                    before += s_cnt[e_lo + i];
-                }
-            }
-        }
-        __syncthreads();
-#pragma unroll
-        for (int n = 0; n < NE; ++n) {
-            if (key[n] >= 0) {
-                // a run holds consecutive positions: anything else is a broken slot map
-                const int d = pos[n] - s_min[key[n]];
-                if (d < s_cnt[key[n]])
-                    s_list[s_pre[key[n]] + d] = make_int2((tid + n * NT) / K, pos[n]);
-                else
-                    bad = true;
-            }
-        }
-        if (g + kPullXcds < G) load_pull_entries<NE, NT>(p, g + kPullXcds, tid, pos, raw);
-        __syncthreads();
-        const int total = __builtin_amdgcn_readfirstlane(s_total);
-
-        // ---- the copies: task k is piece-run (k % TPR) of entry (k / TPR); the
-        // wave's tasks k = wx + n*W are resolved 64 at a time, lane i taking
-        // n = base + i, and read back with two readlanes each
-        const int tasks = total * TPR;
-        for (int base = 0; wx + base * W < tasks; base += kWave) {
-            int rt_pos, rt_pack;  // lane i: the task's position; token in group | part << 8 | ok << 30
-            {
-                const int kk = wx + (base + lane) * W;
-                const bool valid = kk < tasks;
-                const int k = valid ? kk : 0;
-                const int ent = k / TPR, part = k - ent * TPR;
-                const int2 le = s_list[ent];
-                const bool ok = valid && le.x >= 0;
-                rt_pos = ok ? le.y : 0;
-                rt_pack = (ok ? le.x : 0) | (part << 8) | ((int)ok << 30);
-            }
-            const int nb = (tasks - wx - base * W + W - 1) / W;  // tasks of this batch
-            const int nbatch = nb < kWave ? nb : kWave;
-            for (int j = 0; j < nbatch; ++j) {
-                // U loads, then U stores; lanes past a ragged row end load from a
-                // valid place and skip their store
-                const int pk = readlane32(rt_pack, j);
-                const int64_t at = readlane32(rt_pos, j);
-                const bool ok = (pk >> 30) != 0;
-                const int64_t t = g * kPullTokens + (pk & 0xff);
-                const int part = (pk >> 8) & 0x3fffff;
-                const int64_t first = (int64_t)part * U * kWave;
-                const int lim = (int)(p.row_units - first);
-                const u32x4 *src = p.x + t * p.row_units + first;
-                u32x4 *dst = p.dst + at * p.row_units + first;
-                u32x4 v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) {
-                    const int cu = u * kWave + lane;
-                    v[u] = src[(EXACT || cu < lim) ? cu : lim - 1];
-                }
-                asm volatile("" ::: "memory");
-                if (ok) {
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int cu = u * kWave + lane;
-                        if (EXACT || cu < lim) __builtin_nontemporal_store(v[u], dst + cu);
-                    }
-                }
-            }
-        }
-        // ---- the scales: entry e = wx, wx + W, ... of the group's output, lanes over
-        // the token's scales (a wave-uniform loop with a per-lane predicate)
-        if (p.num_scales > 0) {
-            for (int e = wx; e < total; e += W) {
-                const int2 le = s_list[e];
-                const int tl = __builtin_amdgcn_readfirstlane(le.x);
-                const int64_t at = __builtin_amdgcn_readfirstlane(le.y);
-                if (tl < 0) continue;  // wave-uniform
-                const int64_t t = g * kPullTokens + tl;
-                for (int i0 = 0; i0 < p.num_scales; i0 += kWave) {
-                    const int i = i0 + lane;
-                    const float sc = i < p.num_scales ? p.x_scales[t * p.num_scales + i] : 0.0f;
-                    if (i < p.num_scales) p.dst_scales[at * p.num_scales + i] = sc;
-                }
-            }
-        }
-        __syncthreads();  // every wave is done with the list before it is rebuilt
-    }
-    if (ballot64(bad) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_BAD_SEND_SLOT);
-}
-
-template <int U, bool EXACT, int NE>
-hipError_t run_pull(const PullParams &p, hipStream_t stream) {
-    hipLaunchKernelGGL((group_pull_kernel<U, EXACT, NE>), dim3((unsigned)(kPullXcds * kPullBlocksPerXcd)),
-                       dim3(kPullWaves * kWave), 0, stream, p);
-    return hipGetLastError();
-}
-
-// Pieces per task as for the receive dispatch's pull form: 1 for rows of 14 KiB
-// and more, 2 from 7 KiB, 8 above 4 KiB, else 4.
-template <int NE>
-hipError_t run_pull_tiled(const PullParams &p, hipStream_t stream) {
-    if (kPullTokens * p.K > NE * kPullWaves * kWave) return hipErrorInvalidValue;  // every entry has a thread
-    const int64_t ru = p.row_units;
-    const int u = ru >= 14 * kWave ? 1 : ru >= 7 * kWave ? 2 : ru > 4 * kWave ? 8 : 4;
-    const bool exact = ru % (u * kWave) == 0;
-#define EP_PULL_CASE(UU) \
-    if (u == UU) return exact ? run_pull<UU, true, NE>(p, stream) : run_pull<UU, false, NE>(p, stream);
-    EP_PULL_CASE(1)
-    EP_PULL_CASE(2)
-    EP_PULL_CASE(4)
-    EP_PULL_CASE(8)
-#undef EP_PULL_CASE
-    return hipErrorInvalidValue;
-}
-
 template <int VPL, bool EXACT, int WPB>
 hipError_t run_push(PushParams p, hipStream_t stream) {
     p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
@@ -756,11 +484,6 @@ void copy_tiling(int64_t row_units, int *vpl, int *wpb) {
 
 }  // namespace
 
-bool group_pull_applies(const ep_shape_t &s, int64_t row_units) {
-    return s.num_tokens >= kPullMinTokens && row_units >= kWave && row_units <= kPullMaxRowUnits &&
-           s.num_experts <= kPullMaxExperts && s.num_topk <= kMaxTopk;
-}
-
 size_t group_lds_bytes(int er) { return (size_t)er * (sizeof(int64_t) + 2 * sizeof(int32_t) + kGroupWaves * sizeof(int32_t)); }
 
 hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t stream) {
@@ -776,11 +499,6 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
     q.dev_status = a.dev_status;
     q.num_rows = a.num_rows;
     q.cap = a.cap;
-    // the pull form finds each (token, slot)'s position in tok_pos
-    const bool pull = a.from_x && a.tok_pos != nullptr && group_pull_applies(s, a.row_units);
-    q.src_info = pull ? reinterpret_cast<const int2 *>(a.src_info) : nullptr;
-    q.tok_pos = pull ? a.tok_pos : nullptr;
-    q.T = a.num_tokens;
     q.R = s.num_ranks;
     q.K = s.num_topk;
     q.er = s.num_experts / s.num_ranks;
@@ -796,26 +514,6 @@ hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t str
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.cap == 0) return err;
 
-    if (pull) {  // rows straight from x, in position order; padding in the same launch
-        PullParams u;
-        u.x = reinterpret_cast<const u32x4 *>(a.recv_x);
-        u.x_scales = a.recv_scales;
-        u.topk_idx = a.topk_idx;
-        u.tok_pos = a.tok_pos;
-        u.grouped_row = a.grouped_row;
-        u.num_grouped = a.num_grouped;
-        u.dst = reinterpret_cast<u32x4 *>(a.grouped_x);
-        u.dst_scales = a.grouped_scales;
-        u.dev_status = a.dev_status;
-        u.T = a.num_tokens;
-        u.row_units = a.row_units;
-        u.cap = a.cap;
-        u.K = s.num_topk;
-        u.E = s.num_experts;
-        u.num_scales = a.num_scales;
-        // entries per thread: 128 tokens x k slots over 1024 threads
-        return s.num_topk <= 8 ? run_pull_tiled<1>(u, stream) : run_pull_tiled<4>(u, stream);
-    }
     if (a.from_x) {  // rows straight from x
         if (a.num_tokens > 0) {
             PushParams u;

@@ -43,12 +43,10 @@ __host__ __device__ inline int64_t num_groups(int64_t T) { return (num_chunks(T)
 //                                   q = end / 64 < Q): rank_off[q][r] plus the tokens
 //                                   of rank r in [64*q, end)
 //   node_part int32  [C][nodes]     the same per node
-//   tok_pos   int32  [t][k]         grouped position of every (token, slot), or -1
-//                                   (dispatch straight into the grouped layout only)
 // The tickets and acc must be zero before the first call; every layout/notify call
 // leaves them zero again.
 struct Workspace {
-    size_t tickets, acc, mask, rank_off, rank_base, node_base, rank_part, node_part, tok_pos, total;
+    size_t tickets, acc, mask, rank_off, rank_base, node_base, rank_part, node_part, total;
 };
 // uint32 word offsets of the tickets (each a 64-bit ticket, see elect_completing_block)
 constexpr int kTicketLayout = 0;   // counts tokens; words 2..4: valid slots, (token, rank) and (token, node) pairs
@@ -59,6 +57,7 @@ inline size_t align256(size_t v) { return (v + 255) & ~size_t(255); }
 
 inline Workspace workspace_layout(int64_t T, int R, int E, int C, int K) {
     Workspace w;
+    (void)K;  // no part of the layout depends on k
     const int64_t Q = num_chunks(T), G = num_groups(T);
     const int nodes = num_nodes(R);
     size_t off = 0;
@@ -70,7 +69,6 @@ inline Workspace workspace_layout(int64_t T, int R, int E, int C, int K) {
     w.node_base = off; off = align256(off + sizeof(int32_t) * (size_t)(G > 0 ? G : 1) * nodes);
     w.rank_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * R);
     w.node_part = off; off = align256(off + sizeof(int32_t) * (size_t)C * nodes);
-    w.tok_pos = off;   off = align256(off + sizeof(int32_t) * (size_t)(T > 0 ? T : 1) * (size_t)K);
     w.total = off;
     return w;
 }
@@ -117,7 +115,6 @@ struct DispatchArgs {
     int64_t *recv_idx;
     int32_t *src_info;
     int32_t *send_slot;
-    int32_t *tok_pos;  // [t][k] set to -1 (metadata-only launch of the grouped dispatch), or null
     int32_t *dev_status;
     int form;          // ep_dispatch_form_t: EP_FORM_PUSH keeps the push form
 };
@@ -133,8 +130,6 @@ struct GroupArgs {
     bool from_x;               // rows straight from x (through topk_idx, send_slot, slot_pos), not recv_x
     const int64_t *topk_idx;   // [t][k] (from_x)
     const int32_t *send_slot;  // [t][R] (from_x)
-    const int32_t *src_info;   // [N][2] {src_rank, token} (from_x)
-    int32_t *tok_pos;          // [t][k] workspace: grouped position of each (token, slot) (from_x)
     int64_t num_tokens;        // t (from_x)
     int64_t row_units;
     const float *recv_scales;  // [N][num_scales] (or x's [t][num_scales]), null when num_scales == 0
@@ -156,8 +151,24 @@ struct GroupArgs {
 constexpr int kMaxGroupExperts = 512;  // local experts per rank the grouping supports
 
 hipError_t launch_group(const ep_shape_t &s, const GroupArgs &a, hipStream_t stream);
-// Whether the grouping straight from x takes the pull form (which needs tok_pos).
-bool group_pull_applies(const ep_shape_t &s, int64_t row_units);
+
+// Outputs of the dispatch straight into the grouped layout, pull form (one
+// launch: routing, receive metadata, positions, grouped rows and padding).
+struct GroupedPullArgs {
+    const int32_t *aligned;  // [E] segment sizes
+    int32_t cap;             // grouped rows allocated
+    void *grouped_x;
+    float *grouped_scales;
+    int32_t *grouped_row;    // [cap]
+    float *grouped_w;        // [cap], may be null
+    int32_t *slot_pos;       // [recv capacity][k]
+    int32_t *num_grouped;    // [1]
+};
+// Whether the dispatch straight into the grouped layout takes that form (from 2048
+// tokens, rows of 1 KiB to 1 MiB, at most 2048 experts); it needs the workspace.
+bool grouped_pull_applies(const ep_shape_t &s, int64_t row_units);
+hipError_t launch_dispatch_grouped_pull(const ep_shape_t &s, const DispatchArgs &a, const GroupedPullArgs &g,
+                                        hipStream_t stream);
 
 hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv_w, const int32_t *send_slot,
                           int32_t num_recv_rows, uint4 *combined_x, float *combined_w, int32_t *dev_status,
@@ -191,6 +202,23 @@ __device__ __forceinline__ int wave_inclusive_scan(int v) {
     v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 into rows 1, 3
     v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 into rows 2, 3
     return v;
+}
+
+// Inclusive prefix sum over the wave of non-negative values below 2^41 (sums of
+// a few int32 sizes a lane): the low 16 bits and the rest are scanned as two
+// 32-bit DPP scans (each sum stays below 2^31 over 64 lanes) and recombined
+// exactly.
+__device__ __forceinline__ int64_t wave_inclusive_scan64(int64_t v) {
+    const int lo = wave_inclusive_scan((int)(v & 0xffff));
+    const int hi = wave_inclusive_scan((int)(v >> 16));
+    return ((int64_t)hi << 16) + lo;
+}
+
+__device__ __forceinline__ int64_t wave_sum64(int64_t v) {
+    const int64_t incl = wave_inclusive_scan64(v);
+    const uint32_t lo = (uint32_t)readlane32((int)(uint32_t)incl, kWave - 1);
+    const uint32_t hi = (uint32_t)readlane32((int)(uint32_t)(incl >> 32), kWave - 1);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Value of v held by lane (lane ^ S), the whole wave active.  Inside a row of 16

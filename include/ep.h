@@ -74,8 +74,8 @@ enum {
     EP_DEV_COUNT_MISMATCH = 4, /* counts or prefixes disagree with is_token_in_rank: num_tokens_per_rank /
                                   _per_rdma_rank (notify), gbl_channel_prefix_matrix or
                                   recv_gbl_rank_prefix_sum (dispatch) */
-    EP_DEV_BAD_SEND_SLOT = 8,  /* a send_slot entry outside its valid range (combine, cached dispatch), or an
-                                  inconsistent grouped position (grouped dispatch): skipped */
+    EP_DEV_BAD_SEND_SLOT = 8,  /* a send_slot entry outside its valid range (combine, cached dispatch):
+                                  skipped */
     EP_DEV_STALE_WORKSPACE = 16 /* the workspace does not hold what the call needs: its control words were not
                                   zero on entry (a workspace never zero-filled, or shared by calls that ran at
                                   the same time), or the routing state ep_notify left there does not belong to
@@ -318,15 +318,12 @@ ep_status_t ep_group_by_expert(const ep_shape_t *s, const void *recv_x, int32_t 
  * gbl_channel_prefix_matrix and recv_gbl_rank_prefix_sum as for ep_dispatch / ep_dispatch_fp8;
  * num_recv_tokens_per_expert as ep_notify wrote it; the workspace as ep_notify left it (required
  * when t > 0, checked as in ep_dispatch).  Receive rows at or past recv_capacity are dropped as in
- * ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.
- * The call also writes the workspace: from 2048 tokens (rows of 1 KiB to 1 MiB, E <= 2048)
- * it keeps each (token, slot)'s grouped position there; what ep_dispatch and ep_combine
- * read from it is not touched.
- * dev_status (nullable): the flags of both calls, and EP_DEV_BAD_SEND_SLOT if the grouped
- * positions of one expert's entries of a token group are not consecutive (only with
- * inconsistent inputs; those rows are skipped).  Limits as for both calls.
- * Three launches (receive metadata, positions, rows with padding) from 2048 tokens as
- * above, else four (receive metadata, positions, rows, padding).
+ * ep_dispatch (EP_DEV_RECV_OVERFLOW) and not grouped.  The workspace is only read.
+ * dev_status (nullable): the flags of both calls.  Limits as for both calls.
+ * From 2048 tokens (rows of 1 KiB to 1 MiB, E <= 2048) one launch: a slab's rows follow
+ * their tokens, so an entry's place in its segment is the number of entries of its expert
+ * in earlier (token, slot) pairs, found in token order with no pass over the receive rows.
+ * Otherwise four launches (receive metadata, positions over the receive rows, rows, padding).
  */
 ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
@@ -358,9 +355,8 @@ ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_top
 
 /* Bytes of workspace ep_get_layout / ep_notify / ep_dispatch / ep_dispatch_grouped need for
  * this shape (0 if s is invalid).  It holds the completion counters and running counts of
- * layout and notify, the per-token rank masks and per-chunk row offsets notify leaves for
- * dispatch, and the per-(token, slot) grouped positions ep_dispatch_grouped keeps between its
- * own launches.  The workspace is device memory, 256-byte aligned, owned by the caller, and
+ * layout and notify, and the per-token rank masks and per-chunk row offsets notify leaves for
+ * dispatch.  The workspace is device memory, 256-byte aligned, owned by the caller, and
  * must be zero-filled before its first use (hipMemset once at allocation): its completion
  * counters and running counts must start at zero, and every call leaves them at zero
  * again.  Calls that run concurrently must not share a workspace. */

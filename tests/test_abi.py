@@ -56,8 +56,8 @@ def test_workspace_bytes(ep):
     n = ep.ep_workspace_bytes(s)
     # tickets 256 + running counts (64+8+256) + masks (8 B/token) + 64 x 64 chunk offsets
     # + 16 x 64 and 16 x 8 group offsets (four chunks a group) + 24 x 64 + 24 x 8 channel-end
-    # values + grouped positions (4 B per token and slot), each 256-aligned
-    assert n == 256 + 1536 + 32768 + 16384 + 4096 + 512 + 6144 + 768 + 131072
+    # values, each 256-aligned
+    assert n == 256 + 1536 + 32768 + 16384 + 4096 + 512 + 6144 + 768
     assert ep.ep_workspace_bytes(ep.make_shape(4096, 7168, 8, 255, 64, 24)) == 0  # E % R != 0
 
 

@@ -14,7 +14,7 @@ import pytest
 
 from combine_ep_get_02_amd import build as hip_build
 
-PULL_KERNELS = ("dispatch_pull_kernel", "group_pull_kernel")
+PULL_KERNELS = ("dispatch_pull_kernel", "dispatch_grouped_pull_kernel")
 
 
 def _report(src: str) -> dict:
