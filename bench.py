@@ -88,7 +88,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_bf16": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
-                  "dispatch_grouped_kernels": ["ep_dispatch.hip", "ep_group.hip", "ep_internal.h"],
+                  "dispatch_grouped_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"],
                   "combine_staged_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
@@ -390,7 +390,7 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
         int(g2.num_grouped.item()) == M and torch.equal(g2.grouped_row, g.grouped_row)
         and torch.equal(g2.grouped_x.view(torch.int16), g.grouped_x.view(torch.int16)))
     out["dispatch_grouped"]["grouped_rows"] = M
-    out["dispatch_grouped"]["traffic"] = measured_traffic("dispatch_grouped_kernels", wl.name)
+    out["dispatch_grouped"]["traffic"] = measured_traffic("dispatch_grouped_pull_kernel", wl.name)
     del g, g2
     out["dev_status"] = int(b.dev_status.item())
     return out
