@@ -608,11 +608,17 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
 // j owns groups j, j+8, ... as in the receive dispatch's pull form.  Every
 // block keeps per expert the received entries of all tokens before its current
 // group (counted by itself from topk_idx: the groups before its first, then
-// the seven groups between two of its own, their ids loaded while the current
-// group is copied), and ranks the current group's entries stably per expert: a
-// wave finds the lanes sharing its id with one ballot per id bit, the waves'
-// counts go to a byte table (expert x wave) and each entry adds those of the
-// waves before it.  With the segment starts that gives every entry's position.
+// the seven groups between two of its own, their ids loaded at a group's start
+// and counted before its copies), and ranks the current group's entries stably
+// per expert: a wave finds the lanes sharing its id with one ballot per id bit,
+// the waves' counts go to a byte table (expert x wave) and each entry adds
+// those of the waves before it.  The group's counts are scanned over the
+// experts (by every wave at once up to 512 experts, so that only two barriers
+// sit in the ranking).  With the segment starts that gives every entry's
+// position.  Loads whose values are used after a group's copies would wait for
+// all of the wave's stores (one counter covers both), so everything the next
+// group needs from memory is loaded at the start of a group and resolved
+// before its copies.
 // Then, per group: its token tasks (send_slot, receive metadata, slot_pos,
 // grouped_row and weights) spread over the XCD's waves; its grouped rows in
 // position order (runs expert by expert) as tasks of U 1 KiB pieces over the
@@ -627,6 +633,7 @@ constexpr int kGpBlocksPerXcd = 32;       // one block per CU
 constexpr int kGpMaxExperts = 2048;
 constexpr int kGpMaxEntries = kGpTokens * kMaxTopk;
 constexpr int kGpNoLimit = INT32_MAX;     // token threshold of a rank with no dropped row
+constexpr int kGpWaveScanExperts = 512;   // up to this many, every wave scans the group's counts
 
 struct GroupedOut {
     const int32_t *aligned;  // [E] segment sizes (a negative size counts as 0)
@@ -962,9 +969,12 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
 
         // ---- stable ranks of the group's entries per expert, pass by pass
         int total_g = 0;
-#pragma unroll
-        for (int n = 0; n < NE; ++n) {
-            const int kk = key[n];
+        if (NE == 1 && E <= kGpWaveScanExperts) {
+            // one pass, few experts: after the byte table is complete every wave
+            // works out the group's counts and their exclusive scan over the experts
+            // (lane l: experts l, l + 64, ...) and writes the starts, the same values
+            // from every wave, so no barrier sits between them and their use
+            const int kk = key[0];
             uint64_t peers = ballot64(kk >= 0);
             for (int b = 0; b < nbits; ++b) {
                 const bool bit = ((kk >> b) & 1) != 0;
@@ -974,15 +984,40 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
             const int inw = __popcll(peers & lt);
             if (kk >= 0 && inw == 0) s_cnt8[kk * 16 + wave] = (uint8_t)__popcll(peers);
             __syncthreads();
-            if (kk >= 0) rank[n] = (n > 0 ? s_run[kk] : 0) + bytes_below(s_cnt[kk], wave) + inw;
-            if (n > 0) __syncthreads();  // s_run is read before it moves on
-            if (n + 1 < NE) {
-                for (int e = tid; e < E; e += NT) s_run[e] = (n > 0 ? s_run[e] : 0) + bytes_sum(s_cnt[e]);
+            for (int e0 = 0; e0 < E; e0 += kWave) {
+                const int e = e0 + lane;
+                const int c = e < E ? bytes_sum(s_cnt[e]) : 0;
+                const int inc = wave_inclusive_scan(c);
+                if (e < E) {
+                    s_pre[e] = total_g + inc - c;
+                    if (wave == 0) s_run[e] = c;
+                }
+                total_g += readlane32(inc, kWave - 1);
+            }
+            if (kk >= 0) rank[0] = bytes_below(s_cnt[kk], wave) + inw;
+        } else {
+#pragma unroll
+            for (int n = 0; n < NE; ++n) {
+                const int kk = key[n];
+                uint64_t peers = ballot64(kk >= 0);
+                for (int b = 0; b < nbits; ++b) {
+                    const bool bit = ((kk >> b) & 1) != 0;
+                    const uint64_t B = ballot64(bit);
+                    peers &= bit ? B : ~B;
+                }
+                const int inw = __popcll(peers & lt);
+                if (kk >= 0 && inw == 0) s_cnt8[kk * 16 + wave] = (uint8_t)__popcll(peers);
                 __syncthreads();
-                for (int e = tid; e < E; e += NT) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
-                __syncthreads();
-            } else {
-                total_g = gp_counts_scan(s_cnt, s_run, s_pre, n > 0, E, tid, s_w32);
+                if (kk >= 0) rank[n] = (n > 0 ? s_run[kk] : 0) + bytes_below(s_cnt[kk], wave) + inw;
+                if (n > 0) __syncthreads();  // s_run is read before it moves on
+                if (n + 1 < NE) {
+                    for (int e = tid; e < E; e += NT) s_run[e] = (n > 0 ? s_run[e] : 0) + bytes_sum(s_cnt[e]);
+                    __syncthreads();
+                    for (int e = tid; e < E; e += NT) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
+                    __syncthreads();
+                } else {
+                    total_g = gp_counts_scan(s_cnt, s_run, s_pre, n > 0, E, tid, s_w32);
+                }
             }
         }
 
@@ -1007,6 +1042,8 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
         }
         if (ballot64(over) != 0ull && lane == 0) flag(p.dev_status, EP_DEV_RECV_OVERFLOW);
         __syncthreads();
+        if (NE == 1 && E <= kGpWaveScanExperts)  // every wave is past its last read of the table
+            for (int e = tid; e < E; e += NT) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
         // ---- the next group's keys, from the loads above
         if (next) {
             const int64_t an = (g + kXcds) * kGpTokens;
