@@ -609,7 +609,8 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
 // block keeps per expert the received entries of all tokens before its current
 // group (counted by itself from topk_idx: the groups before its first, then
 // the seven groups between two of its own, their ids loaded at a group's start
-// and counted before its copies), and ranks the current group's entries stably
+// and counted before its copies, or after them with more than 8 slots a token),
+// and ranks the current group's entries stably
 // per expert: a wave finds the lanes sharing its id with one ballot per id bit,
 // the waves' counts go to a byte table (expert x wave) and each entry adds
 // those of the waves before it.  The group's counts are scanned over the
@@ -625,7 +626,9 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
 // XCD's waves, x read again from the XCD's L2; its scales.  After the last
 // group the padding rows, over the whole grid.  Receive rows at or past the
 // capacity are the last rows of their slabs, so per rank a token index bounds
-// the received tokens; it is found once, and only when rows are dropped.
+// the received tokens; it is found once, and only when rows are dropped.  The
+// routing inputs are checked against the workspace as in the receive dispatch,
+// once per group, by XCD 0's waves before their first group.
 constexpr int kGpTokens = 2 * kChunk;     // tokens per group
 constexpr int kGpWaves = 16;              // waves per block
 constexpr int kGpThreads = kGpWaves * kWave;

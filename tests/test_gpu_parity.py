@@ -845,6 +845,62 @@ def test_dispatch_grouped_pull_edges():
     assert _group_diff(gpu, want) == [] and gpu["status"] == 2
 
 
+@pytest.mark.parametrize("T", [2300, 900])
+@pytest.mark.parametrize("what", ["stale_workspace", "gbl_entry", "recv_prefix"])
+def test_dispatch_grouped_flags_inconsistent_routing(T, what):
+    # the one-launch form (from 2048 tokens) and the four-launch form check the routing
+    # inputs as ep_dispatch does: a workspace notify filled for another routing, or a
+    # prefix that disagrees with is_token_in_rank, is flagged
+    import torch
+
+    import oracle
+    from combine_ep_get_02_amd import ep
+
+    print(f"[parity] dispatch_grouped inconsistent {what} T={T}", flush=True)
+    R, E, K, C, Hd, align = 16, 64, 4, 10, 512, 4
+    x, idx, w = _random_case(T, R, E, K, C, Hd, seed=T + len(what))
+    o = oracle.Oracle()
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, align)
+    gbl = note["gbl_channel_prefix_matrix"].copy()
+    recv = note["recv_gbl_rank_prefix_sum"].copy()
+    shape = ep.make_shape(T, Hd, K, E, R, C, 0, align)
+    b = ep.allocate(shape, 0)
+    ws_idx = idx.copy()
+    if what == "stale_workspace":  # notify ran for a routing with one token sent elsewhere
+        ws_idx[T // 2, 0] = (idx[T // 2, 0] + E // 2) % E
+    elif what == "gbl_entry":
+        gbl[3, 4] += 1
+    else:
+        recv[5:] += 2
+    ep.run_layout(b, torch.from_numpy(ws_idx).cuda())
+    ep.run_notify(b)
+    n = note["num_recv_tokens"]
+    rcap = n + 64
+    aligned = note["num_recv_tokens_per_expert"]
+    gcap = int(np.maximum(aligned, 0).sum())
+    i32 = dict(dtype=torch.int32, device="cuda")
+    rw = torch.empty((rcap, K), dtype=torch.float32, device="cuda")
+    ri = torch.empty((rcap, K), dtype=torch.int64, device="cuda")
+    si = torch.empty((rcap, 2), **i32)
+    ss = torch.empty((T, R), **i32)
+    gx = torch.empty((gcap, Hd), dtype=torch.int16, device="cuda")
+    grow = torch.empty(gcap, **i32)
+    gw = torch.empty(gcap, dtype=torch.float32, device="cuda")
+    pos = torch.empty((rcap, K), **i32)
+    m = torch.empty(1, **i32)
+    st = torch.zeros(1, **i32)
+    ep.ep_dispatch_grouped(shape, torch.from_numpy(x.view(np.int16)).cuda(), 2, None, 0, torch.from_numpy(idx).cuda(),
+                           torch.from_numpy(w).cuda(), torch.from_numpy(lay["is_token_in_rank"]).cuda(),
+                           torch.from_numpy(gbl).cuda(), torch.from_numpy(recv).cuda(),
+                           torch.from_numpy(aligned).cuda(), b.workspace, rcap, rw, ri, si, ss, gcap, gx, None, grow, gw,
+                           pos, m, st)
+    torch.cuda.synchronize()
+    want = ep.EP_DEV_STALE_WORKSPACE if what == "stale_workspace" else ep.EP_DEV_COUNT_MISMATCH
+    assert int(st.item()) & want, int(st.item())
+
+
 def test_dispatch_grouped_no_tokens():
     x, idx, w = _random_case(0, 16, 64, 4, 8, 64, seed=1)
     gpu, want = _dispatch_grouped_case(x, idx, w, 64, 16, 8, 4)
