@@ -99,11 +99,22 @@ def combine_kernel_name(T, H) -> str:
     return "combine_staged_kernel" if 2 * H >= 14 * 1024 and T >= 4096 else "combine_kernel"
 
 
+def source_code_only(text: bytes) -> bytes:
+    """A HIP source without its comments and with runs of white space made one
+    space: what the counters' validity depends on (a comment edit leaves it)."""
+    import re
+
+    s = text.decode()
+    s = re.sub(r"/\*.*?\*/", " ", s, flags=re.S)
+    s = re.sub(r"//[^\n]*", " ", s)
+    return re.sub(r"\s+", " ", s).strip().encode()
+
+
 def measured_traffic(kernel: str, workload: str):
     """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
     summary (FETCH_SIZE + WRITE_SIZE, each scaled by a plain copy of known
     size), or None when that summary does not cover this workload or the
-    kernel's sources changed since the counters were taken."""
+    kernel's sources (comments aside) changed since the counters were taken."""
     import hashlib
 
     if workload != "prefill" or not os.path.exists(PROFILE):
@@ -111,7 +122,7 @@ def measured_traffic(kernel: str, workload: str):
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "combine_ep_get_02_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+            h.update(source_code_only(fh.read()))
     fields = {}
     with open(PROFILE) as fh:
         for line in fh:
