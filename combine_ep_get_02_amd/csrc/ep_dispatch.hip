@@ -649,19 +649,17 @@ struct GroupedOut {
     int64_t gcap;
 };
 
-// Expert ids of entries tid + n * kGpThreads of the tokens from a (-1 past the
-// last token and for an id that names no expert); clamped loads, so no branch
-// sits between them.
+// Raw ids of entries tid + n * kGpThreads of the tokens from a, loaded at
+// clamped places (no branch around the loads, and nothing uses them yet: a use
+// would wait for the wave's earlier stores too); gp_keys makes them keys.
 template <int NE>
-__device__ __forceinline__ void gp_load_ids(const DispatchParams &p, int64_t a, int tid, int (&ids)[NE]) {
+__device__ __forceinline__ void gp_load_ids(const DispatchParams &p, int64_t a, int tid, int64_t (&raw)[NE]) {
     const int n_ent = kGpTokens * p.K;
     const int64_t e0 = a * p.K, e_end = p.T * p.K;
 #pragma unroll
     for (int n = 0; n < NE; ++n) {
         const int i = tid + n * kGpThreads;
-        const bool in = i < n_ent && e0 + i < e_end;
-        const int64_t v = p.topk_idx[in ? e0 + i : 0];
-        ids[n] = in && v >= 0 && v < p.E ? (int)v : -1;
+        raw[n] = p.topk_idx[i < n_ent && e0 + i < e_end ? e0 + i : 0];
     }
 }
 
@@ -671,6 +669,23 @@ __device__ __forceinline__ bool gp_received(const DispatchParams &p, int v, int6
                                             const int *s_thr) {
     if (v < 0) return false;
     return !drops || t < s_thr[v / p.experts_per_rank];
+}
+
+// The keys of the group of tokens from a: the expert id of each entry with a
+// receive row, else -1 (past the last token, an id naming no expert, a dropped
+// row).
+template <int NE>
+__device__ __forceinline__ void gp_keys(const DispatchParams &p, int64_t a, int tid, const int64_t (&raw)[NE],
+                                        bool drops, const int *s_thr, int (&key)[NE]) {
+    const int n_ent = kGpTokens * p.K;
+    const int64_t e0 = a * p.K, e_end = p.T * p.K;
+#pragma unroll
+    for (int n = 0; n < NE; ++n) {
+        const int i = tid + n * kGpThreads;
+        const bool in = i < n_ent && e0 + i < e_end && raw[n] >= 0 && raw[n] < p.E;
+        const int v = in ? (int)raw[n] : -1;
+        key[n] = gp_received(p, v, a + i / p.K, drops, s_thr) ? v : -1;
+    }
 }
 
 // The received entries of tokens [t0, t1) added to cnt per expert (LDS atomics).
@@ -869,8 +884,8 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
 
     // ---- loads first: the first group's ids and routing, the segment sizes, the
     // ids of the groups before it
-    int raw[NE];
-    if (xcd < G) gp_load_ids<NE>(p, (int64_t)xcd * kGpTokens, tid, raw);
+    int64_t raw[NE];
+    gp_load_ids<NE>(p, (int64_t)(xcd < G ? xcd : 0) * kGpTokens, tid, raw);
     const int ept = (E + NT - 1) / NT;
     const int e_lo = tid * ept;
     int al[2] = {0, 0};  // ept <= 2
@@ -949,9 +964,7 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
     // the first group's keys (the next group's are made during each group, before
     // its copies, from ids loaded at its start)
     int key_c[NE];
-#pragma unroll
-    for (int n = 0; n < NE; ++n)
-        key_c[n] = gp_received(p, raw[n], (int64_t)xcd * kGpTokens + (tid + n * NT) / K, drops, s_thr) ? raw[n] : -1;
+    gp_keys<NE>(p, (int64_t)xcd * kGpTokens, tid, raw, drops, s_thr, key_c);
 
     for (int64_t g = xcd; g < G; g += kXcds) {
         const int64_t a = g * kGpTokens;  // the group's first token
@@ -966,7 +979,10 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
         // stores of the last group have long completed (a load used right away
         // would wait for them): the next group's ids, and the ids of the groups up
         // to it
-        if (next) gp_load_ids<NE>(p, (g + kXcds) * kGpTokens, tid, raw);
+        gp_load_ids<NE>(p, (next ? g + kXcds : g) * kGpTokens, tid, raw);
+        // (with several entries a thread the ids become keys at once, which keeps
+        // registers free for the ranking but waits for the last group's stores)
+        if (NE > 1 && next) gp_keys<NE>(p, (g + kXcds) * kGpTokens, tid, raw, drops, s_thr, key_c);
         int ob[NB];
         if (NE == 1) gp_load_groups<NB>(p, a + kGpTokens, a + (int64_t)kXcds * kGpTokens, tid, ob);
 
@@ -1048,12 +1064,7 @@ __global__ __launch_bounds__(kGpThreads) void dispatch_grouped_pull_kernel(Dispa
         if (NE == 1 && E <= kGpWaveScanExperts)  // every wave is past its last read of the table
             for (int e = tid; e < E; e += NT) s_cnt[e] = u32x4{0u, 0u, 0u, 0u};
         // ---- the next group's keys, from the loads above
-        if (next) {
-            const int64_t an = (g + kXcds) * kGpTokens;
-#pragma unroll
-            for (int n = 0; n < NE; ++n)
-                key_c[n] = gp_received(p, raw[n], an + (tid + n * NT) / K, drops, s_thr) ? raw[n] : -1;
-        }
+        if (NE == 1 && next) gp_keys<NE>(p, (g + kXcds) * kGpTokens, tid, raw, drops, s_thr, key_c);
         // ---- entries before this XCD's next group: this group's, then the groups
         // up to it (s_base is next read after the group's last barrier)
         for (int e = tid; e < E; e += NT)
