@@ -800,6 +800,13 @@ GROUPED_PULL = {
     "rows_16kib_k6": (2048, 16, 64, 6, 5, 8192, 3, {}),
     "e2048": (2048, 64, 2048, 8, 24, 1024, 2, {}),
     "e4096_push_form": (2048, 64, 4096, 8, 24, 512, 2, {}),
+    # ~20 groups an XCD: the per-expert counts carried over many rounds
+    "many_groups_t20000": (20000, 64, 256, 8, 24, 512, 4, dict(mask_frac=0.05)),
+    # 16 slots a token: the ranking in two passes, the counts between groups after the copies
+    "k16_many_groups": (9000, 32, 128, 16, 12, 512, 1, dict(dup=True)),
+    # 512 experts (every wave scans the counts) and 640 (the block scan)
+    "e512_wave_scan": (4100, 64, 512, 8, 24, 512, 1, {}),
+    "e640_block_scan": (4100, 64, 640, 8, 24, 512, 1, {}),
 }
 
 
