@@ -820,6 +820,28 @@ def test_dispatch_grouped_pull_parity(name):
     assert gpu["status"] == 0
 
 
+@pytest.mark.parametrize("H_", [7168, 1024])
+def test_all_tokens_to_one_rank(H_):
+    # the most skewed routing: every token's slots on the experts of rank 3, so one slab
+    # holds every receive row and 63 are empty; the pull forms of dispatch (runs of
+    # length 0 around the only one), combine and the one-launch grouped dispatch (every
+    # group's entries in 8 segments, 128 a wave's worth of one id at most)
+    print(f"[parity] all tokens to one rank h={H_}", flush=True)
+    T, R, E, K, C, align = 4096, 64, 512, 8, 24, 4
+    rng = np.random.default_rng(77 + H_)
+    epr = E // R
+    idx = (3 * epr + np.stack([rng.permutation(epr)[:K] for _ in range(T)])).astype(np.int64)
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, H_)
+    gpu, ref = H.run_both(x, idx, w, E, R, C)
+    assert H.compare(gpu, ref) == []
+    assert all(v == 0 for v in H.combine_bit_differences(gpu, ref).values())
+    assert gpu["num_recv_tokens"] == T and gpu["dev_status"] == 0
+    g, want = _dispatch_grouped_case(x, idx, w, E, R, C, align)
+    assert _group_diff(g, want) == []
+    assert g["status"] == 0
+
+
 def test_dispatch_grouped_pull_fp8_112_scales():
     # more scales per token than lanes in a wave, ragged groups, alignment padding
     print("[parity] dispatch_grouped pull fp8 112 scales", flush=True)
