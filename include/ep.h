@@ -329,7 +329,7 @@ ep_status_t ep_dispatch_grouped(const ep_shape_t *s, const void *x, int32_t elem
                                 int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
                                 const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                                 const int32_t *recv_gbl_rank_prefix_sum, const int32_t *num_recv_tokens_per_expert,
-                                void *workspace, size_t workspace_bytes, int32_t recv_capacity,
+                                const void *workspace, size_t workspace_bytes, int32_t recv_capacity,
                                 float *recv_topk_weights, int64_t *recv_topk_idx, int32_t *recv_src_info,
                                 int32_t *send_slot, int32_t grouped_capacity, void *grouped_x,
                                 float *grouped_x_scales, int32_t *grouped_row, float *grouped_weights,
