@@ -556,7 +556,7 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_pull_kernel(DispatchParam
                 }
                 // o < the run's length by construction; checked, so that a bad
                 // offset can only drop the row, never pick a token past t
-                const bool found = oc < __popcll(cc);
+                const bool found = (unsigned)oc < __popcll(cc);
                 const int tok = found ? c * kChunk + nth_set_bit(cc, oc) : 0;
                 const bool ok = valid && found && row >= 0 && row < p.cap;  // rows past the capacity: dropped
                 rt_row = ok ? row : 0;
@@ -736,7 +736,7 @@ __device__ int gp_rank_threshold(const DispatchParams &p, int r, int lane) {
     const int64_t tok = qs * kChunk + lane;
     const uint64_t mk = p.mask[tok < p.T ? tok : p.T - 1];
     const uint64_t col = ballot64(tok < p.T && ((mk >> r) & 1ull));
-    if (k < 0 || k >= __popcll(col)) {  // only with a workspace that disagrees with itself
+    if (k < 0 || k >= (int)__popcll(col)) {  // only with a workspace that disagrees with itself
         const int64_t end = (qs + 1) * kChunk;
         return (int)(end < p.T ? end : p.T);
     }
