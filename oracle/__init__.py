@@ -50,10 +50,15 @@ def _declare(lib: ctypes.CDLL) -> ctypes.CDLL:
     lib.oracle_dispatch_cached.argtypes = [_I, _I, _L, _P, _P, _I, _P, _I, _P, _P]
     lib.oracle_group_by_expert.argtypes = [_I, _I, _I, _L, _P, _P, _I, _P, _P, _P, _P, _I, _I] + [_P] * 6
     lib.oracle_bf16_round.argtypes = [_P, _P, _L]
+    lib.oracle_e4m3_encode.argtypes = [_P, _P, _L]
+    lib.oracle_e4m3_decode.argtypes = [_P, _P, _L]
+    lib.oracle_quantize_e4m3.argtypes = [_L, _I, _I, _P, _P, _P]
+    lib.oracle_dequantize_e4m3.argtypes = [_L, _I, _I, _P, _P, _P]
     for name in ("oracle_layout", "oracle_notify", "oracle_dispatch", "oracle_combine", "oracle_combine_f64",
-                 "oracle_dispatch_fp8", "oracle_dispatch_cached"):
+                 "oracle_dispatch_fp8", "oracle_dispatch_cached", "oracle_quantize_e4m3", "oracle_dequantize_e4m3"):
         getattr(lib, name).restype = ctypes.c_int
-    lib.oracle_bf16_round.restype = None
+    for name in ("oracle_bf16_round", "oracle_e4m3_encode", "oracle_e4m3_decode"):
+        getattr(lib, name).restype = None
     return lib
 
 
@@ -254,6 +259,42 @@ class Oracle:
         f = np.ascontiguousarray(f, dtype=np.float32)
         out = np.zeros(f.shape, np.uint16)
         self.lib.oracle_bf16_round(_ptr(f), _ptr(out), f.size)
+        return out
+
+    def e4m3_encode(self, v: np.ndarray) -> np.ndarray:
+        """Nearest E4M3 pattern (ties to even) of binary32 values with |v| <= 448."""
+        v = np.ascontiguousarray(v, dtype=np.float32)
+        out = np.zeros(v.shape, np.uint8)
+        self.lib.oracle_e4m3_encode(_ptr(v), _ptr(out), v.size)
+        return out
+
+    def e4m3_decode(self, c: np.ndarray) -> np.ndarray:
+        """The value of each E4M3 pattern (binary64; NaN for S.1111.111)."""
+        c = np.ascontiguousarray(c, dtype=np.uint8)
+        out = np.zeros(c.shape, np.float64)
+        self.lib.oracle_e4m3_decode(_ptr(c), _ptr(out), c.size)
+        return out
+
+    def quantize_e4m3(self, x: np.ndarray, num_scales: int):
+        """bf16 rows [rows][H] (uint16 patterns) -> (codes uint8 [rows][H], scales f32 [rows][num_scales])."""
+        x = np.ascontiguousarray(x, dtype=np.uint16)
+        rows, H = x.shape
+        codes = np.zeros((rows, H), np.uint8)
+        scales = np.zeros((rows, num_scales), np.float32)
+        rc = self.lib.oracle_quantize_e4m3(rows, H, num_scales, _ptr(x), _ptr(codes), _ptr(scales))
+        if rc != 0:
+            raise ValueError(f"num_scales {num_scales} does not divide hidden {H}")
+        return codes, scales
+
+    def dequantize_e4m3(self, codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+        """E4M3 codes [rows][H] and scales [rows][S] -> bf16 patterns [rows][H]."""
+        codes = np.ascontiguousarray(codes, dtype=np.uint8)
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        rows, H = codes.shape
+        out = np.zeros((rows, H), np.uint16)
+        rc = self.lib.oracle_dequantize_e4m3(rows, H, scales.shape[1], _ptr(codes), _ptr(scales), _ptr(out))
+        if rc != 0:
+            raise ValueError(f"num_scales {scales.shape[1]} does not divide hidden {H}")
         return out
 
     def full(self, x, topk_idx, topk_weights, E: int, R: int, C: int, expert_alignment: int = 1,

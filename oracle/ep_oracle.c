@@ -1,7 +1,8 @@
 /*
  * ep_oracle.c -- plain, slow, single-threaded CPU oracle for the expert-parallel
- * dispatch/combine core (layout, notify, dispatch, combine, and the grouping of
- * received rows by local expert) on one GPU's share.
+ * dispatch/combine core (layout, notify, dispatch, combine, the grouping of
+ * received rows by local expert, and the E4M3 quantiser that makes the fp8
+ * rows and scales the fp8 dispatch carries) on one GPU's share.
  *
  * TEST INFRASTRUCTURE ONLY.  Only the tests, the smoke check and the CPU-baseline
  * leg of the benchmark may load this library.  The product path (the HIP library
@@ -463,4 +464,114 @@ int oracle_group_by_expert(int32_t E, int32_t R, int32_t K, int64_t row_bytes, c
     }
     *num_grouped_rows = (int32_t)offset;
     return status;
+}
+
+/* ------------------------------------------------------------------------- */
+/* fp8 rows and their scales.  [mscclpp] intranodeDispatch / internodeDispatch
+ * take x with an element size of one byte together with xScales, numScales
+ * float scales per token, and return them as recvXScales (the "FP8 scale
+ * buffer"); combine stays bf16.  How x and its scales are produced is not on
+ * the pages.  Reading (the quantiser this library offers for that input):
+ *  - element format: OCP FP8 E4M3.  One sign bit, four exponent bits (bias 7)
+ *    and three mantissa bits; a zero exponent field holds the subnormals
+ *    m * 2^-9; the patterns S.1111.111 are NaN; there are no infinities; the
+ *    largest finite value is 1.75 * 2^8 = 448.
+ *  - a row of H channels splits into S = num_scales groups of g = H / S
+ *    consecutive channels; group q of row t takes
+ *        a = max(max over the group of |x|, 2^-64)       (exact in binary32)
+ *        scale[t][q] = a / 448                            (binary32 division)
+ *        code[t][i]  = e4m3(clamp(x[t][i] * (448 / a), -448, 448))
+ *    with 448 / a and the product each rounded to binary32 and e4m3() the
+ *    nearest value, ties to the even code; -0 and negative values that round
+ *    to zero keep the sign bit.  The floor 2^-64 keeps 448 / a finite and the
+ *    scale a normal binary32 number for an all-zero (or tiny) group.
+ *  - dequantisation: out[t][i] = bf16_rne(value(code[t][i]) * scale[t][q]),
+ *    the product rounded to binary32.
+ * Inputs are finite; a group holding an infinity or NaN is outside the
+ * reading (its codes are not defined here). */
+
+/* The value of an E4M3 pattern, straight from the field definition. */
+static double orc_e4m3_value(uint8_t c) {
+    const int sign = c >> 7, ex = (c >> 3) & 15, man = c & 7;
+    if (ex == 15 && man == 7) return NAN;
+    double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E4M3 pattern to a finite v with |v| <= 448, ties to the even
+ * pattern.  Normal range (|v| >= 2^-6): with |v| = f * 2^E, 1 <= f < 2, the
+ * representable neighbours are spaced 2^(E-3) apart, so the mantissa is
+ * rint(|v| / 2^(E-3)) in [8, 16]; 16 carries into the next binade.  Below
+ * 2^-6 the spacing is the subnormal step 2^-9. */
+static uint8_t orc_e4m3_rne(float v) {
+    const double mag = fabs((double)v);
+    uint8_t code;
+    if (mag >= ldexp(1.0, -6)) {
+        int e;
+        (void)frexp(mag, &e); /* mag = m * 2^e, 0.5 <= m < 1 */
+        int E = e - 1;
+        double q = rint(ldexp(mag, 3 - E)); /* exact scaling; rint rounds half to even */
+        if (q == 16.0) {
+            q = 8.0;
+            E += 1;
+        }
+        code = (uint8_t)(((E + 7) << 3) | ((int)q - 8));
+    } else {
+        code = (uint8_t)rint(ldexp(mag, 9)); /* 0..8; 8 is the smallest normal */
+    }
+    return signbit(v) ? (uint8_t)(code | 0x80) : code;
+}
+
+/* Exposed for the pins (compared with a library conversion and a brute-force
+ * nearest-value search). */
+void oracle_e4m3_encode(const float *in, uint8_t *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_rne(in[i]);
+}
+void oracle_e4m3_decode(const uint8_t *in, double *out, int64_t n) {
+    for (int64_t i = 0; i < n; ++i) out[i] = orc_e4m3_value(in[i]);
+}
+
+/* Quantise rows [rows][H] bf16 to E4M3 codes [rows][H] and scales
+ * [rows][num_scales] as read above.  Returns 0, or -1 when num_scales does not
+ * divide H. */
+int oracle_quantize_e4m3(int64_t rows, int32_t H, int32_t num_scales, const uint16_t *x, uint8_t *codes,
+                         float *scales) {
+    if (num_scales <= 0 || H % num_scales != 0) return -1;
+    const int32_t g = H / num_scales;
+    for (int64_t t = 0; t < rows; ++t) {
+        for (int32_t q = 0; q < num_scales; ++q) {
+            const uint16_t *xg = x + t * H + (int64_t)q * g;
+            float a = 0.0f;
+            for (int32_t i = 0; i < g; ++i) {
+                const float m = fabsf(orc_bf16_to_f32(xg[i]));
+                if (m > a) a = m;
+            }
+            if (a < 0x1p-64f) a = 0x1p-64f;
+            const float inv = 448.0f / a;
+            scales[t * num_scales + q] = a / 448.0f;
+            for (int32_t i = 0; i < g; ++i) {
+                float v = orc_bf16_to_f32(xg[i]) * inv;
+                if (v > 448.0f) v = 448.0f;
+                if (v < -448.0f) v = -448.0f;
+                codes[t * H + (int64_t)q * g + i] = orc_e4m3_rne(v);
+            }
+        }
+    }
+    return 0;
+}
+
+/* Dequantise codes [rows][H] with scales [rows][num_scales] to bf16 [rows][H]:
+ * value(code) * scale rounded to binary32, then to bf16 (nearest, ties to
+ * even).  value() is exact in binary32.  Returns 0, or -1 when num_scales
+ * does not divide H. */
+int oracle_dequantize_e4m3(int64_t rows, int32_t H, int32_t num_scales, const uint8_t *codes, const float *scales,
+                           uint16_t *out) {
+    if (num_scales <= 0 || H % num_scales != 0) return -1;
+    const int32_t g = H / num_scales;
+    for (int64_t t = 0; t < rows; ++t)
+        for (int32_t i = 0; i < H; ++i) {
+            const float v = (float)orc_e4m3_value(codes[t * H + i]);
+            out[t * H + i] = orc_f32_to_bf16_rne(v * scales[t * num_scales + i / g]);
+        }
+    return 0;
 }

@@ -629,3 +629,160 @@ def expected_ranks_per_token(E: int, R: int, K: int) -> float:
     """Closed form for uniform routing without replacement: R*(1 - C(E-E/R, K)/C(E, K))."""
     er = E // R
     return R * (1.0 - math.comb(E - er, K) / math.comb(E, K))
+
+
+# --------------------------------------------------------------------------- fp8 (E4M3) quantiser
+def _torch_e4m3_values() -> np.ndarray:
+    """The value of every E4M3 pattern by torch's own float8_e4m3fn decoding (NaN where torch says so)."""
+    import torch
+
+    return torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _torch_e4m3_codes(v: np.ndarray) -> np.ndarray:
+    """torch's float8_e4m3fn cast (nearest, ties to even) as bit patterns; exact inside [-448, 448]."""
+    import torch
+
+    return torch.from_numpy(np.ascontiguousarray(v, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _e4m3_probe_values(rng) -> np.ndarray:
+    """Binary32 values inside [-448, 448]: every finite bf16 pattern there, every midpoint between
+    neighbouring E4M3 values and one binary32 step either side of it, and log-uniform randoms."""
+    allbf = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    allbf = allbf[np.isfinite(allbf) & (np.abs(allbf) <= 448)]
+    pos = np.sort(_torch_e4m3_values()[:0x7F])  # 0 .. 448, the non-negative finite values
+    mids = ((pos[1:] + pos[:-1]) / 2).astype(np.float32)  # exact in binary32
+    near = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(448))])
+    rnd = (np.exp2(rng.uniform(-14, 8.8, 200000)) * rng.choice([-1.0, 1.0], 200000)).astype(np.float32)
+    rnd = rnd[np.abs(rnd) <= 448]
+    return np.concatenate([allbf, near, -near, rnd, np.array([0.0, -0.0, 448, -448], np.float32)])
+
+
+def pin_e4m3(o) -> list[str]:
+    """The oracle's E4M3 decode against torch's for all 256 patterns; its encode against torch's
+    cast over every bf16 value, every tie and random values in range; and against a brute-force
+    nearest-value search (ties to the even pattern) that shares nothing with either."""
+    errs = []
+    want_vals = _torch_e4m3_values()
+    got_vals = o.e4m3_decode(np.arange(256, dtype=np.uint8))
+    same = (got_vals == want_vals) | (np.isnan(got_vals) & np.isnan(want_vals))
+    if not same.all():
+        errs.append(f"E4M3 decode differs from torch at patterns {np.flatnonzero(~same)[:8].tolist()}")
+    rng = np.random.default_rng(11)
+    v = _e4m3_probe_values(rng)
+    got = o.e4m3_encode(v)
+    want = _torch_e4m3_codes(v)
+    if not np.array_equal(got, want):
+        bad = np.flatnonzero(got != want)
+        errs.append(f"E4M3 encode differs from torch on {bad.size} values, e.g. {v[bad[:4]].tolist()}")
+    # brute force on a sample: the nearest finite value, the even pattern on a tie, the sign kept
+    s = np.concatenate([v[rng.choice(v.size, 6000, replace=False)], v[-4:]])
+    table = want_vals.copy()
+    finite = np.flatnonzero(~np.isnan(table))
+    dist = np.abs(table[finite][None, :] - s.astype(np.float64)[:, None])
+    best = dist.min(axis=1)
+    c = o.e4m3_encode(s)
+    cval = o.e4m3_decode(c)
+    if not np.array_equal(np.abs(cval - s.astype(np.float64)), best):
+        errs.append("E4M3 encode is not the nearest value")
+    tie = (dist == best[:, None]).sum(axis=1) > 1
+    nz = cval != 0  # both signed zeros tie at 0: the sign rule below decides those
+    if np.any((c[tie & nz] & 1) != 0):
+        errs.append("E4M3 tie not broken to the even pattern")
+    if not np.array_equal(c >> 7, np.signbit(s).astype(np.uint8)):
+        errs.append("E4M3 sign bit is not the sign of the input")
+    return errs
+
+
+def quantize_groups(rng, rows: int, hidden: int, num_scales: int) -> np.ndarray:
+    """bf16 rows whose groups of hidden/num_scales channels span the binary32 exponent range: each group
+    is normal values at its own power-of-two scale 2^[-120, 120], and a few groups are special (all zero,
+    signed zeros, one non-zero value, bf16 subnormals, a huge spread, a largest value exactly 448)."""
+    g = hidden // num_scales
+    e = rng.integers(-120, 121, size=(rows, num_scales, 1)).astype(np.float64)
+    x = (rng.standard_normal((rows, num_scales, g)) * np.exp2(e)).astype(np.float32)
+    x = x.reshape(rows * num_scales, g)
+    n = x.shape[0]
+    picks = rng.choice(n, size=min(n, 7), replace=False)
+    specials = [np.zeros(g, np.float32),
+                np.where(np.arange(g) % 2 == 0, 0.0, -0.0).astype(np.float32),
+                np.where(np.arange(g) == g // 2, -3.5, 0.0).astype(np.float32),
+                (rng.standard_normal(g) * 1e-39).astype(np.float32),
+                (rng.standard_normal(g) * np.exp2(rng.integers(-60, 60, g))).astype(np.float32),
+                np.concatenate([[448.0], rng.uniform(-448, 448, g - 1)]).astype(np.float32),
+                np.concatenate([rng.uniform(-300, 300, g - 1), [-448.0]]).astype(np.float32)]
+    for p, sp in zip(picks, specials):
+        x[p] = sp
+    bits = x.view(np.uint32)
+    return (bits >> 16).astype(np.uint16).reshape(rows, hidden)  # truncation gives exact bf16 values
+
+
+def pin_quantize(o) -> list[str]:
+    """Properties the quantiser's reading fixes, none of them its formula retyped: the largest
+    magnitude of a group lands on +-448; the round trip value(code) * scale stays within half an E4M3
+    step of x (relative 2^-4, or 2^-10 scales in the subnormal range); scaling a group by a power of two
+    scales its scale alike and keeps its codes; a group whose largest value is 448 has scale 1 and
+    torch's own codes; an all-zero group has zero codes and a positive finite scale; and the
+    dequantiser matches torch's float8 -> bf16 conversion at scale 1 and a power-of-two scale."""
+    import torch
+
+    errs = []
+    rng = np.random.default_rng(12)
+    for rows, hidden, S in ((37, 256, 2), (5, 2048, 16), (3, 64, 4), (2, 1024, 1)):
+        g = hidden // S
+        x = quantize_groups(rng, rows, hidden, S)
+        codes, scales = o.quantize_e4m3(x, S)
+        xf = bf16_to_f64(x).reshape(rows, S, g)
+        cv = o.e4m3_decode(codes).reshape(rows, S, g)
+        sc = scales.astype(np.float64)[:, :, None]
+        amax = np.abs(xf).max(axis=2)
+        live = amax >= 2.0 ** -64
+        top = np.abs(xf) == amax[:, :, None]
+        if not np.all(np.abs(cv[top & live[:, :, None]]) == 448):
+            errs.append(f"quantize {rows}x{hidden}/{S}: a group's largest value is not coded +-448")
+        if not np.all((cv[amax == 0] == 0)) or not np.all(np.isfinite(scales)) or not np.all(scales > 0):
+            errs.append(f"quantize {rows}x{hidden}/{S}: an all-zero group is not zero codes with a positive scale")
+        err = np.abs(cv * sc - xf)
+        bound = (2.0 ** -4 + 2.0 ** -20) * np.abs(xf) + 2.0 ** -10 * sc * (1 + 2.0 ** -20)
+        if not np.all(err <= bound):
+            errs.append(f"quantize {rows}x{hidden}/{S}: round-trip error above half an E4M3 step")
+        if not np.array_equal(np.signbit(cv), np.signbit(xf)):
+            errs.append(f"quantize {rows}x{hidden}/{S}: code sign differs from x")
+        # power-of-two invariance, on groups well above the 2^-64 floor with no bf16 subnormal
+        # (so that the scaling is exact)
+        k = 5
+        e = rng.integers(-50, 91, size=(rows, S, 1)).astype(np.float64)
+        xm = (rng.standard_normal((rows, S, g)) * np.exp2(e)).astype(np.float32).reshape(rows, hidden)
+        xm_bits = (xm.view(np.uint32) >> 16).astype(np.uint16)
+        xs = (bf16_to_f64(xm_bits) * 2.0 ** k).astype(np.float32)
+        xs_bits = (xs.view(np.uint32) >> 16).astype(np.uint16)
+        c1, s1 = o.quantize_e4m3(xm_bits, S)
+        c2, s2 = o.quantize_e4m3(xs_bits, S)
+        if not (np.array_equal(c2, c1) and np.array_equal(s2, s1 * np.float32(2.0 ** k))):
+            errs.append(f"quantize {rows}x{hidden}/{S}: not invariant under a power-of-two scaling")
+    # largest value exactly 448: scale 1, codes as torch's cast of x itself
+    g = 128
+    x448 = np.concatenate([[448.0], rng.uniform(-448, 448, g - 1)]).astype(np.float32)
+    xb = (x448.view(np.uint32) >> 16).astype(np.uint16)[None, :]
+    c448, s448 = o.quantize_e4m3(xb, 1)
+    if s448[0, 0] != 1.0 or not np.array_equal(c448[0], _torch_e4m3_codes(bf16_to_f64(xb[0]).astype(np.float32))):
+        errs.append("quantize: a group whose largest value is 448 is not torch's cast with scale 1")
+    # dequantiser: every finite pattern at scale 1 and 2^-7, against torch's conversions
+    pats = np.arange(256, dtype=np.uint8)
+    pats = pats[(pats & 0x7F) != 0x7F]
+    for sc in (1.0, 2.0 ** -7):
+        got = o.dequantize_e4m3(pats[None, :], np.array([[sc]], np.float32))[0]
+        want = (torch.from_numpy(pats.copy()).view(torch.float8_e4m3fn).to(torch.float32) * sc).to(torch.bfloat16)
+        if not np.array_equal(got, want.view(torch.int16).numpy().view(np.uint16)):
+            errs.append(f"dequantize at scale {sc} differs from torch's conversion")
+    # round trip through the dequantiser: within half an E4M3 step plus half a bf16 step
+    x = quantize_groups(rng, 9, 512, 4)
+    codes, scales = o.quantize_e4m3(x, 4)
+    back = bf16_to_f64(o.dequantize_e4m3(codes, scales))
+    xf = bf16_to_f64(x)
+    sc = np.repeat(scales.astype(np.float64), 128, axis=1)
+    bound = (2.0 ** -4 + 2.0 ** -8 + 2.0 ** -11) * np.abs(xf) + 2.0 ** -9 * sc
+    if not np.all(np.abs(back - xf) <= bound):
+        errs.append("dequantize(quantize(x)) strays from x")
+    return errs

@@ -78,6 +78,30 @@ MUTANTS = {
                               "grouped_weights[pos] = recv_topk_weights[row * K];"),
     "group_segment_bound_ignored": ("if (used >= size || pos >= grouped_capacity) {",
                                     "if (pos >= grouped_capacity) {"),
+    "e4m3_bias_eight": ("code = (uint8_t)(((E + 7) << 3) | ((int)q - 8));",
+                        "code = (uint8_t)(((E + 8) << 3) | ((int)q - 8));"),
+    "e4m3_ties_away": ("double q = rint(ldexp(mag, 3 - E));", "double q = floor(ldexp(mag, 3 - E) + 0.5);"),
+    "e4m3_truncates": ("double q = rint(ldexp(mag, 3 - E));", "double q = floor(ldexp(mag, 3 - E));"),
+    "e4m3_subnormal_step": ("code = (uint8_t)rint(ldexp(mag, 9));", "code = (uint8_t)rint(ldexp(mag, 10));"),
+    "e4m3_subnormal_ties_away": ("code = (uint8_t)rint(ldexp(mag, 9));",
+                                 "code = (uint8_t)floor(ldexp(mag, 9) + 0.5);"),
+    "e4m3_normal_threshold": ("if (mag >= ldexp(1.0, -6)) {", "if (mag >= ldexp(1.0, -7)) {"),
+    "e4m3_sign_dropped": ("return signbit(v) ? (uint8_t)(code | 0x80) : code;", "return code;"),
+    "e4m3_decode_no_subnormals": (
+        "double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);",
+        "double mag = ldexp(1.0 + man / 8.0, ex - 7);"),
+    "e4m3_decode_bias": (
+        "double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 7);",
+        "double mag = ex == 0 ? ldexp((double)man, -9) : ldexp(1.0 + man / 8.0, ex - 8);"),
+    "e4m3_decode_nan_pattern": ("if (ex == 15 && man == 7) return NAN;", "if (ex == 15 && man == 6) return NAN;"),
+    "quant_scale_divisor": ("scales[t * num_scales + q] = a / 448.0f;", "scales[t * num_scales + q] = a / 240.0f;"),
+    "quant_inverse_numerator": ("const float inv = 448.0f / a;", "const float inv = 240.0f / a;"),
+    "quant_amax_signed": ("const float m = fabsf(orc_bf16_to_f32(xg[i]));", "const float m = orc_bf16_to_f32(xg[i]);"),
+    "quant_no_floor": ("if (a < 0x1p-64f) a = 0x1p-64f;", ";"),
+    "quant_group_stride": ("const uint16_t *xg = x + t * H + (int64_t)q * g;", "const uint16_t *xg = x + t * H + q;"),
+    "quant_amax_skips_last": ("for (int32_t i = 0; i < g; ++i) {\n                const float m",
+                              "for (int32_t i = 0; i < g - 1; ++i) {\n                const float m"),
+    "dequant_scale_index": ("scales[t * num_scales + i / g]", "scales[t * num_scales + i % num_scales]"),
 }
 
 CHILD = textwrap.dedent("""
@@ -93,7 +117,7 @@ CHILD = textwrap.dedent("""
               lambda: pins.pin_golden_grouping(o), lambda: pins.pin_group_by_expert(o, inputs.generate("tiny"), 4),
               lambda: pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32),
               lambda: pins.pin_dispatch_prefix_checks(o, inputs.generate("tiny")),
-              lambda: pins.pin_bruteforce(o)]
+              lambda: pins.pin_bruteforce(o), lambda: pins.pin_e4m3(o), lambda: pins.pin_quantize(o)]
     errs = []
     for check in checks:  # in order, stopping at the first pin that fails
         errs = check()

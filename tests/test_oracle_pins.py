@@ -17,6 +17,14 @@ def test_bruteforce_tiny_shapes(orc):
     assert pins.pin_bruteforce(orc) == []
 
 
+def test_e4m3_against_library_and_bruteforce(orc):
+    assert pins.pin_e4m3(orc) == []
+
+
+def test_quantize_properties(orc):
+    assert pins.pin_quantize(orc) == []
+
+
 def test_bf16_rounding_matches_library(orc):
     assert pins.pin_bf16_rounding(orc) == []
 
