@@ -57,6 +57,11 @@ def dispatch_fp8_bytes(T, H, K, R, N, S) -> int:
     return T * (H + 4 * S) + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
 
 
+def quantize_bytes(T, H, S) -> int:
+    """bf16 rows read once, E4M3 rows (1 byte an element) and S fp32 scales per row written."""
+    return T * 2 * H + T * (H + 4 * S)
+
+
 def dispatch_cached_bytes(T, R, N, row_bytes, S) -> int:
     """rows (and their scales) read once per token, the [t][R] send_slot map
     read, every receive row (and its scales) written."""
@@ -89,6 +94,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_kernel_cached_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
                   "dispatch_grouped_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
+                  "quantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"],
                   "combine_staged_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
@@ -371,7 +377,31 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
     out["dispatch_cached_fp8"] = rate(dispatch_cached_bytes(T, R, n_recv, H, S), mean_us(
         lambda: ep.ep_dispatch_cached(shape, x8, 1, sc, S, b.send_slot, n_recv, cx8, cs8, b.dev_status)))
     out["dispatch_cached_fp8"]["check"] = bool(torch.equal(cx8, rx) and torch.equal(cs8, rs))
-    del cx8, cs8, rx, rs, x8, sc
+    del cx8, cs8
+
+    # the library's E4M3 quantiser on the same bf16 rows (groups of 128 channels), alone and
+    # followed by the fp8 dispatch of what it wrote: a caller's whole fp8 path from bf16 rows.
+    # Checked by what the quantiser fixes: every group's largest magnitude is coded +-448, and the
+    # scales are amax / 448 as the caller-side recipe above makes them.
+    q8 = torch.empty((T, H), dtype=torch.uint8, device=x.device)
+    qs = torch.empty((T, S), dtype=torch.float32, device=x.device)
+    out["quantize_fp8"] = rate(quantize_bytes(T, H, S), mean_us(lambda: ep.ep_quantize_fp8(x, T, H, S, q8, qs)))
+    qv = q8.cpu().view(torch.float8_e4m3fn).float().view(T, S, H // S)
+    out["quantize_fp8"]["check"] = bool(torch.all(qv.abs().amax(dim=2) == 448.0) and torch.equal(qs, sc))
+    out["quantize_fp8"]["num_scales"] = S
+    out["quantize_fp8"]["traffic"] = measured_traffic("quantize_e4m3_kernel", wl.name)
+    del qv
+
+    def quant_then_dispatch():
+        ep.ep_quantize_fp8(x, T, H, S, q8, qs)
+        ep.ep_dispatch_fp8(shape, q8, qs, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, n_recv, rx, rs,
+                           b.recv_w, b.recv_idx, b.src_info, slot8, b.dev_status)
+
+    out["quantize_then_dispatch_fp8"] = rate(quantize_bytes(T, H, S) + dispatch_fp8_bytes(T, H, K, R, n_recv, S),
+                                             mean_us(quant_then_dispatch))
+    out["quantize_then_dispatch_fp8"]["check"] = bool(torch.equal(slot8, b.send_slot) and
+                                                      torch.equal(rx[rows], q8[tok]) and torch.equal(rs[rows], qs[tok]))
+    del rx, rs, x8, sc, q8, qs
 
     # grouping of the receive rows by local expert (bf16 rows of the dispatch just measured)
     M = int(b.recv_per_expert.sum().item())

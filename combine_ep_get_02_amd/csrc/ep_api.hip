@@ -100,6 +100,22 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
     return from_hip(launch_dispatch(*s, a, stream));
 }
 
+// Shared checks of the quantiser and the dequantiser: rows >= 0, hidden a positive multiple of
+// 16, groups of 16 << l channels (0 <= l <= 6), rows and code buffers 16-byte aligned, scales
+// 4-byte aligned.
+ep_status_t quant_checked(const void *rows16, const void *codes, const float *scales, int64_t num_rows,
+                          int32_t hidden, int32_t num_scales) {
+    if (num_rows < 0 || hidden < kQuantChannels || hidden % kQuantChannels != 0 || num_scales < 1 ||
+        hidden % num_scales != 0)
+        return EP_ERR_INVALID_ARG;
+    if (quant_lanes_log2(hidden, num_scales) < 0) return EP_ERR_UNSUPPORTED;
+    if (num_rows == 0) return EP_OK;
+    if (rows16 == nullptr || codes == nullptr || scales == nullptr) return EP_ERR_INVALID_ARG;
+    if (!aligned16(rows16) || !aligned16(codes) || (reinterpret_cast<uintptr_t>(scales) & 3u) != 0)
+        return EP_ERR_INVALID_ARG;
+    return EP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -420,6 +436,20 @@ ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_top
     if (!aligned16(combined_x) || (y != nullptr && !aligned16(y))) return EP_ERR_INVALID_ARG;
     return from_hip(launch_combine(*s, static_cast<const uint4 *>(y), recv_topk_weights, send_slot, num_recv_rows,
                                    static_cast<uint4 *>(combined_x), combined_topk_weights, dev_status, stream));
+}
+
+ep_status_t ep_quantize_fp8(const void *x, int64_t num_rows, int32_t hidden, int32_t num_scales, void *x_fp8,
+                            float *x_scales, hipStream_t stream) {
+    const ep_status_t st = quant_checked(x, x_fp8, x_scales, num_rows, hidden, num_scales);
+    if (st != EP_OK || num_rows == 0) return st;
+    return from_hip(launch_quantize(x, num_rows, hidden, num_scales, x_fp8, x_scales, stream));
+}
+
+ep_status_t ep_dequantize_fp8(const void *x_fp8, const float *x_scales, int64_t num_rows, int32_t hidden,
+                              int32_t num_scales, void *out, hipStream_t stream) {
+    const ep_status_t st = quant_checked(out, x_fp8, x_scales, num_rows, hidden, num_scales);
+    if (st != EP_OK || num_rows == 0) return st;
+    return from_hip(launch_dequantize(x_fp8, x_scales, num_rows, hidden, num_scales, out, stream));
 }
 
 }  // extern "C"

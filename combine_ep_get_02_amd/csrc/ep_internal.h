@@ -174,6 +174,16 @@ hipError_t launch_combine(const ep_shape_t &s, const uint4 *y, const float *recv
                           int32_t num_recv_rows, uint4 *combined_x, float *combined_w, int32_t *dev_status,
                           hipStream_t stream);
 
+// E4M3 quantiser: channels per lane, and log2 of the lanes per scale group for a row of
+// `hidden` channels cut into num_scales groups (-1 unless the group is 16 << l channels,
+// 0 <= l <= 6).
+constexpr int kQuantChannels = 16;
+int quant_lanes_log2(int hidden, int num_scales);
+hipError_t launch_quantize(const void *x, int64_t rows, int hidden, int num_scales, void *codes, float *scales,
+                           hipStream_t stream);
+hipError_t launch_dequantize(const void *codes, const float *scales, int64_t rows, int hidden, int num_scales,
+                             void *out, hipStream_t stream);
+
 // ---------------------------------------------------------------- wave64 helpers
 __device__ __forceinline__ uint64_t ballot64(bool p) { return __ballot(p); }
 

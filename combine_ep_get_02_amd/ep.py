@@ -22,8 +22,9 @@ EP_DEV_BAD_TOPK_IDX, EP_DEV_RECV_OVERFLOW, EP_DEV_COUNT_MISMATCH, EP_DEV_BAD_SEN
 EP_DEV_STALE_WORKSPACE = 16
 EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL = 0, 1, 2
 
-EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-            "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_workspace_bytes", "ep_status_string")
+EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8",
+            "ep_quantize_fp8", "ep_dequantize_fp8", "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
+            "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
 class EpError(RuntimeError):
@@ -66,8 +67,10 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
+    lib.ep_quantize_fp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
+    lib.ep_dequantize_fp8.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
     for name in ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-                 "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine"):
+                 "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_quantize_fp8", "ep_dequantize_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -240,6 +243,16 @@ def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x
     _check(load().ep_combine(ctypes.byref(shape), _ptr(y), _ptr(recv_topk_weights), _ptr(send_slot),
                              int(num_recv_rows), _ptr(combined_x), _ptr(combined_topk_weights), _ptr(dev_status),
                              _stream(stream)), "ep_combine")
+
+
+def ep_quantize_fp8(x, num_rows, hidden, num_scales, x_fp8, x_scales, stream=None) -> None:
+    _check(load().ep_quantize_fp8(_ptr(x), int(num_rows), int(hidden), int(num_scales), _ptr(x_fp8), _ptr(x_scales),
+                                  _stream(stream)), "ep_quantize_fp8")
+
+
+def ep_dequantize_fp8(x_fp8, x_scales, num_rows, hidden, num_scales, out, stream=None) -> None:
+    _check(load().ep_dequantize_fp8(_ptr(x_fp8), _ptr(x_scales), int(num_rows), int(hidden), int(num_scales),
+                                    _ptr(out), _stream(stream)), "ep_dequantize_fp8")
 
 
 # ----------------------------------------------------------------------------- buffers

@@ -12,6 +12,7 @@
  *   ep_combine     expert outputs in receive layout -> weighted sum in token order
  * and beside them:
  *   ep_dispatch_fp8     dispatch of 1-byte (fp8) rows with their per-token scales
+ *   ep_quantize_fp8     bf16 rows -> E4M3 rows and scales for it; ep_dequantize_fp8 back
  *   ep_dispatch_cached  new rows to the rows an earlier dispatch assigned (cached mode)
  *   ep_group_by_expert  receive rows regrouped into per-expert segments for grouped GEMMs
  *   ep_dispatch_grouped dispatch straight into those segments, with no receive rows
@@ -246,6 +247,43 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
                             float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
                             int32_t *recv_src_info, int32_t *send_slot, int32_t form, int32_t *dev_status,
                             hipStream_t stream);
+
+/*
+ * fp8 rows and scales for ep_dispatch_fp8, made from bf16 rows.  [mscclpp ht_runtime.cc,
+ * intranodeDispatch / internodeDispatch take x with a one-byte element size together with
+ * xScales, numScales floats per token; how they are produced is not on the pages -- this is
+ * the library's quantiser for that input.]
+ * A row of `hidden` channels is cut into num_scales groups of g = hidden / num_scales
+ * consecutive channels.  For group q of row t:
+ *   a = max(largest |x| of the group, 2^-64)
+ *   x_scales[t][q] = a / 448                                  (f32, correctly rounded)
+ *   x_fp8[t][i]    = e4m3(clamp(x[t][i] * (448 / a), -448, 448))
+ * with 448 / a and the product each rounded to f32, and e4m3() the nearest OCP FP8 E4M3 value
+ * (sign, 4 exponent bits with bias 7, 3 mantissa bits; no infinities; largest finite 448), ties to
+ * the even pattern; the sign bit of x is kept, also for values that round to zero.  Then
+ * x ~ value(x_fp8) * x_scales within half an E4M3 step: 2^-4 |x|, or 2^-10 of the scale for the
+ * smallest values of a group.
+ * In:  x [num_rows][hidden] bf16, finite (the codes and scale of a group holding an infinity or
+ *      NaN are not defined).
+ * Out: x_fp8 [num_rows][hidden] uint8; x_scales [num_rows][num_scales] f32 (4-byte aligned).
+ * Limits: hidden a positive multiple of 16 (EP_ERR_INVALID_ARG otherwise, and when num_scales
+ * does not divide hidden); g = 16, 32, 64, 128, 256, 512 or 1024 (EP_ERR_UNSUPPORTED otherwise).
+ * x and x_fp8 16-byte aligned.  num_rows == 0 enqueues nothing.  One launch, no workspace.
+ */
+ep_status_t ep_quantize_fp8(const void *x, int64_t num_rows, int32_t hidden, int32_t num_scales, void *x_fp8,
+                            float *x_scales, hipStream_t stream);
+
+/*
+ * The inverse of ep_quantize_fp8, for rows an fp8 dispatch delivered (recv_x, recv_x_scales).
+ * [the same reading of the pages' fp8 rows and FP8 scale buffer]
+ *   out[t][i] = bf16(value(x_fp8[t][i]) * x_scales[t][i / g])
+ * with the product rounded to f32 and then to bf16 (nearest, ties to even).  The patterns 0x7F and
+ * 0xFF (E4M3 NaN, which the quantiser never writes) give a bf16 NaN.
+ * In:  x_fp8 [num_rows][hidden] uint8, x_scales [num_rows][num_scales] f32.
+ * Out: out [num_rows][hidden] bf16.  Limits and alignment as for ep_quantize_fp8 (out in place of x).
+ */
+ep_status_t ep_dequantize_fp8(const void *x_fp8, const float *x_scales, int64_t num_rows, int32_t hidden,
+                              int32_t num_scales, void *out, hipStream_t stream);
 
 /*
  * Cached-mode dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch with

@@ -33,7 +33,7 @@ def declared_functions():
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify",
                                           "ep_dispatch",
-                                          "ep_dispatch_fp8",
+                                          "ep_dispatch_fp8", "ep_quantize_fp8", "ep_dequantize_fp8",
                                           "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
                                           "ep_combine", "ep_workspace_bytes", "ep_status_string"])
 
@@ -153,6 +153,29 @@ def test_fp8_and_cached_argument_checks(ep):
     assert lib.ep_dispatch_cached(ctypes.byref(s), p, 3, None, 0, p, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_dispatch_cached(ctypes.byref(s), p, 2, None, 0, None, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_dispatch_cached(ctypes.byref(s12), p, 1, None, 0, p, 10, p, None, 0, None, None) == ep.EP_ERR_INVALID_ARG
+
+
+def test_quantize_argument_checks(ep):
+    lib = ep.load()
+    p = ctypes.c_void_p(256)
+    for fn in (lambda *a: lib.ep_quantize_fp8(p, a[0], a[1], a[2], p, p, None),
+               lambda *a: lib.ep_dequantize_fp8(p, p, a[0], a[1], a[2], p, None)):
+        assert fn(-1, 7168, 56) == ep.EP_ERR_INVALID_ARG      # negative row count
+        assert fn(4, 7160, 56) == ep.EP_ERR_INVALID_ARG       # hidden not a multiple of 16
+        assert fn(4, 0, 1) == ep.EP_ERR_INVALID_ARG
+        assert fn(4, 7168, 0) == ep.EP_ERR_INVALID_ARG
+        assert fn(4, 7168, 3) == ep.EP_ERR_INVALID_ARG        # 3 does not divide 7168
+        assert fn(4, 7168, 64) == ep.EP_ERR_UNSUPPORTED       # groups of 112 channels
+        assert fn(4, 4096, 2) == ep.EP_ERR_UNSUPPORTED        # groups of 2048 channels
+        assert fn(4, 96, 12) == ep.EP_ERR_UNSUPPORTED         # groups of 8 channels
+        assert fn(0, 7168, 56) == ep.EP_OK                    # nothing to do, nothing enqueued
+    q = ctypes.c_void_p(264)  # 8-byte aligned only
+    assert lib.ep_quantize_fp8(q, 4, 7168, 56, p, p, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_quantize_fp8(p, 4, 7168, 56, q, p, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_quantize_fp8(p, 4, 7168, 56, p, ctypes.c_void_p(258), None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_quantize_fp8(None, 4, 7168, 56, p, p, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dequantize_fp8(p, None, 4, 7168, 56, p, None) == ep.EP_ERR_INVALID_ARG
+    assert lib.ep_dequantize_fp8(p, p, 4, 7168, 56, q, None) == ep.EP_ERR_INVALID_ARG
 
 
 def test_group_by_expert_argument_checks(ep):

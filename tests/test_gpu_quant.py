@@ -1,0 +1,182 @@
+"""Parity of the E4M3 quantiser and dequantiser (ep_quantize_fp8, ep_dequantize_fp8) with the
+oracle, bit for bit, through the C ABI: every bf16 value of [-448, 448] at scale 1, groups of 16
+to 1024 channels with ragged row counts and rows that are not a whole number of 1024 channels,
+groups that are all zero, signed zeros, bf16 subnormals or span the whole exponent range, the
+prefill size, and the chain quantise -> ep_dispatch_fp8 -> dequantise against the same chain in
+the oracle."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import pins
+from combine_ep_get_02_amd import ep
+from combine_ep_get_02_amd.inputs import generate
+from gpu_harness import bf16_host, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+
+def _quant_gpu(x: np.ndarray, S: int):
+    rows, H = x.shape
+    dx = to_dev_bf16(x) if rows else torch.empty((0, H), dtype=torch.bfloat16, device="cuda")
+    q = torch.full((max(rows, 1), H), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((max(rows, 1), S), -2.0, dtype=torch.float32, device="cuda")
+    ep.ep_quantize_fp8(dx, rows, H, S, q, s)
+    torch.cuda.synchronize()
+    return q[:rows].cpu().numpy(), s[:rows].cpu().numpy(), q, s
+
+
+def _dequant_gpu(codes: np.ndarray, scales: np.ndarray):
+    rows, H = codes.shape
+    dq = torch.from_numpy(np.ascontiguousarray(codes)).cuda()
+    ds = torch.from_numpy(np.ascontiguousarray(scales, dtype=np.float32)).cuda()
+    out = torch.full((max(rows, 1), H), -1, dtype=torch.int16, device="cuda").view(torch.bfloat16)
+    ep.ep_dequantize_fp8(dq, ds, rows, H, scales.shape[1], out)
+    torch.cuda.synchronize()
+    return bf16_host(out[:rows])
+
+
+def _same_codes(name, got, want):
+    assert got.shape == want.shape, name
+    bad = np.flatnonzero(got.reshape(-1) != want.reshape(-1))
+    assert bad.size == 0, f"{name}: {bad.size} codes differ, first at {bad[:5].tolist()}: " \
+                          f"{got.reshape(-1)[bad[:5]].tolist()} vs {want.reshape(-1)[bad[:5]].tolist()}"
+
+
+def _same_scales(name, got, want):
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32)), \
+        f"{name}: {int((got.view(np.uint32) != want.view(np.uint32)).sum())} scales differ"
+
+
+def test_quantize_every_bf16_value_at_scale_one():
+    """Each group of 128 starts with 448 (or ends with -448), so 448 / a = 1 and the kernel's
+    conversion meets every bf16 value of [-448, 448] unscaled: this checks gfx950's conversion
+    (nearest, ties to even, signed zero, subnormals) against the oracle's definition."""
+    print("[quant] every bf16 value at scale 1", flush=True)
+    o = oracle.Oracle()
+    allbf = (np.arange(1 << 16, dtype=np.uint32) << 16).view(np.float32)
+    vals = allbf[np.isfinite(allbf) & (np.abs(allbf) <= 448)]
+    bits = (vals.view(np.uint32) >> 16).astype(np.uint16)
+    per = 127
+    groups = -(-bits.size // per)
+    body = np.zeros(groups * per, np.uint16)
+    body[: bits.size] = bits
+    body = body.reshape(groups, per)
+    head = np.full((groups, 1), 0x43E0, np.uint16)  # 448.0
+    for lead, name in ((np.hstack([head, body]), "448 first"), (np.hstack([body, head | 0x8000]), "-448 last")):
+        filler = np.zeros(((-groups) % 8, 128), np.uint16)  # whole rows of 1024: groups of 448, 0, 0, ...
+        filler[:, 0] = 0x43E0
+        x = np.vstack([lead, filler]).reshape(-1, 1024)
+        S = x.shape[1] // 128
+        gq, gs, _, _ = _quant_gpu(x, S)
+        rq, rs = o.quantize_e4m3(x, S)
+        _same_scales(name, gs, rs)
+        assert np.all(gs == 1.0)
+        _same_codes(name, gq, rq)
+
+
+# (rows, hidden, num_scales): groups of 16 .. 1024 channels; rows not a whole number of 1024
+# channels (48, 96, 896, 2560, 1536); row counts that leave a wave half used
+QUANT_SHAPES = [(37, 48, 3), (5, 96, 3), (129, 896, 14), (33, 7168, 56), (17, 2560, 10), (9, 1536, 3),
+                (3, 7168, 7), (1, 1024, 1), (64, 64, 1), (2, 16, 1)]
+
+
+@pytest.mark.parametrize("rows,hidden,S", QUANT_SHAPES)
+def test_quantize_groups_parity(rows, hidden, S):
+    print(f"[quant] rows={rows} hidden={hidden} scales={S}", flush=True)
+    rng = np.random.default_rng(1000 + rows * 7 + hidden)
+    x = pins.quantize_groups(rng, rows, hidden, S)
+    gq, gs, _, _ = _quant_gpu(x, S)
+    rq, rs = oracle.Oracle().quantize_e4m3(x, S)
+    _same_scales("scales", gs, rs)
+    _same_codes("codes", gq, rq)
+
+
+def test_quantize_leaves_rows_past_the_end_alone():
+    """Rows past num_rows (and their scales) are not written."""
+    print("[quant] rows past the end", flush=True)
+    rng = np.random.default_rng(5)
+    x = pins.quantize_groups(rng, 6, 896, 7)
+    dx = to_dev_bf16(x)
+    q = torch.full((8, 896), 0xAB, dtype=torch.uint8, device="cuda")
+    s = torch.full((8, 7), -2.0, dtype=torch.float32, device="cuda")
+    ep.ep_quantize_fp8(dx, 5, 896, 7, q, s)
+    torch.cuda.synchronize()
+    rq, rs = oracle.Oracle().quantize_e4m3(x[:5], 7)
+    _same_codes("codes", q[:5].cpu().numpy(), rq)
+    _same_scales("scales", s[:5].cpu().numpy(), rs)
+    assert torch.all(q[5:] == 0xAB) and torch.all(s[5:] == -2.0)
+
+
+def test_quantize_prefill_size():
+    """The fp8 dispatch's workload: 4096 tokens of 7168 channels, 56 scales per token."""
+    print("[quant] prefill 4096 x 7168 / 56", flush=True)
+    x = generate("prefill")["x"]
+    gq, gs, _, _ = _quant_gpu(x, 56)
+    rq, rs = oracle.Oracle().quantize_e4m3(x, 56)
+    _same_scales("scales", gs, rs)
+    _same_codes("codes", gq, rq)
+
+
+@pytest.mark.parametrize("rows,hidden,S", [(257, 256, 2), (3, 7168, 56), (40, 48, 3), (2, 1024, 1)])
+def test_dequantize_parity(rows, hidden, S):
+    """Every code pattern, with scales of every magnitude; E4M3 NaN patterns must give NaN."""
+    print(f"[dequant] rows={rows} hidden={hidden} scales={S}", flush=True)
+    rng = np.random.default_rng(77 + rows)
+    codes = rng.integers(0, 256, size=(rows, hidden), dtype=np.uint8)
+    codes.reshape(-1)[:256] = np.arange(256, dtype=np.uint8)[: min(256, codes.size)]
+    scales = np.exp2(rng.uniform(-80, 80, size=(rows, S))).astype(np.float32)
+    scales.reshape(-1)[:3] = np.array([1.0, 2.0 ** -7, 3.0], np.float32)[: min(3, scales.size)]
+    got = _dequant_gpu(codes, scales)
+    want = oracle.Oracle().dequantize_e4m3(codes, scales)
+    nan = (codes & 0x7F) == 0x7F
+    gnan = ((got & 0x7F80) == 0x7F80) & ((got & 0x7F) != 0)
+    assert np.array_equal(gnan, nan), "NaN codes and NaN outputs differ"
+    assert np.array_equal(got[~nan], want[~nan]), f"{int((got[~nan] != want[~nan]).sum())} values differ"
+
+
+@pytest.mark.parametrize("name", ["sweep", "prefill"])
+def test_quantize_dispatch_dequantize_chain(name):
+    """x -> ep_quantize_fp8 -> ep_dispatch_fp8 -> ep_dequantize_fp8 on the received rows, against
+    the oracle's quantiser, fp8 dispatch and dequantiser on the same inputs."""
+    print(f"[quant] chain workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    T, H = x.shape
+    S = H // 128
+    K = idx.shape[1]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    shape = ep.make_shape(T, H, K, E, R, C)
+    b = ep.allocate(shape, 0)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    n = ep.run_notify(b, read_back=True)
+    _, _, dq, dsc = _quant_gpu(x, S)
+    cap = T * min(R, K)
+    rx = torch.full((cap, H), 0xAB, dtype=torch.uint8, device="cuda")
+    rs = torch.full((cap, S), -2.0, dtype=torch.float32, device="cuda")
+    rw = torch.empty((cap, K), dtype=torch.float32, device="cuda")
+    si = torch.empty((cap, 2), dtype=torch.int32, device="cuda")
+    ss = torch.empty((T, R), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_fp8(shape, dq, dsc, S, didx, dw, b.in_rank, b.gbl, b.recv_gbl, b.workspace, cap, rx, rs, rw, None,
+                       si, ss, st)
+    out = torch.empty((max(n, 1), H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_dequantize_fp8(rx, rs, n, H, S, out)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    o = oracle.Oracle()
+    q, s = o.quantize_e4m3(x, S)
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, 1)
+    dd = o.dispatch_fp8(q, s, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                        note["recv_gbl_rank_prefix_sum"], E, recv_capacity=cap)
+    assert n == note["num_recv_tokens"]
+    _same_codes("recv_x", rx[:n].cpu().numpy(), dd["recv_x"][:n])
+    _same_scales("recv_x_scales", rs[:n].cpu().numpy(), dd["recv_x_scales"][:n])
+    back = o.dequantize_e4m3(dd["recv_x"][:n], dd["recv_x_scales"][:n])
+    assert np.array_equal(bf16_host(out[:n]), back)
