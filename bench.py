@@ -57,6 +57,12 @@ def dispatch_fp8_bytes(T, H, K, R, N, S) -> int:
     return T * (H + 4 * S) + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
 
 
+def dispatch_to_fp8_bytes(T, H, K, R, N, S) -> int:
+    """the quantising dispatch: bf16 x read once per token, ids and weights read, every receive row written
+    as E4M3 codes with its S fp32 scales and its metadata, and the [t][R] send_slot map written."""
+    return T * 2 * H + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
+
+
 def quantize_bytes(T, H, S) -> int:
     """bf16 rows read once, E4M3 rows (1 byte an element) and S fp32 scales per row written."""
     return T * 2 * H + T * (H + 4 * S)
@@ -95,6 +101,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "group_kernels": ["ep_group.hip", "ep_internal.h"],
                   "dispatch_grouped_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "quantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
+                  "dispatch_kernel_to_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"],
                   "combine_staged_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
@@ -401,6 +408,15 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
                                              mean_us(quant_then_dispatch))
     out["quantize_then_dispatch_fp8"]["check"] = bool(torch.equal(slot8, b.send_slot) and
                                                       torch.equal(rx[rows], q8[tok]) and torch.equal(rs[rows], qs[tok]))
+    # the same path in one launch: each token's bf16 row read once and quantised once (push form);
+    # checked against the two calls just made
+    rx2, rs2, slot2 = torch.empty_like(rx), torch.empty_like(rs), torch.empty_like(slot8)
+    out["dispatch_to_fp8"] = rate(dispatch_to_fp8_bytes(T, H, K, R, n_recv, S), mean_us(
+        lambda: ep.ep_dispatch_to_fp8(shape, x, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, n_recv, rx2, rs2,
+                                      b.recv_w, b.recv_idx, b.src_info, slot2, b.dev_status)))
+    out["dispatch_to_fp8"]["check"] = bool(torch.equal(slot2, slot8) and torch.equal(rx2, rx) and torch.equal(rs2, rs))
+    out["dispatch_to_fp8"]["traffic"] = measured_traffic("dispatch_kernel_to_fp8", wl.name)
+    del rx2, rs2, slot2
     del rx, rs, x8, sc, q8, qs
 
     # grouping of the receive rows by local expert (bf16 rows of the dispatch just measured)

@@ -52,14 +52,16 @@ ep_status_t routing_checked(const ep_shape_t *s, const uint8_t *in_rank, const i
     return tc <= kMaxDeriveChannelTokens ? EP_OK : EP_ERR_UNSUPPORTED;
 }
 
-// Shared checks and launch of the bf16 and fp8 dispatch entry points.
+// Shared checks and launch of the bf16, fp8 and quantising dispatch entry points.
+// quant_log2 >= 0: x is bf16, rows leave as E4M3 codes of row_bytes bytes with
+// num_scales scales made on the way (x_scales is not read); -1 otherwise.
 ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_bytes, const float *x_scales,
                              int32_t num_scales, const int64_t *topk_idx, const float *topk_weights,
                              const uint8_t *is_token_in_rank, const int32_t *gbl_channel_prefix_matrix,
                              const int32_t *recv_gbl_rank_prefix_sum, const void *workspace, size_t workspace_bytes,
                              int32_t recv_capacity, void *recv_x, float *recv_x_scales, float *recv_topk_weights,
                              int64_t *recv_topk_idx, int32_t *recv_src_info, int32_t *send_slot, int32_t form,
-                             int32_t *dev_status, hipStream_t stream) {
+                             int32_t *dev_status, hipStream_t stream, int quant_log2 = -1) {
     ep_status_t st = check_shape(s);
     if (st != EP_OK) return st;
     if (row_bytes % 16 != 0 || recv_capacity < 0 || num_scales < 0 || !form_ok(form)) return EP_ERR_INVALID_ARG;
@@ -69,7 +71,7 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
         return EP_ERR_INVALID_ARG;
     if (recv_capacity > 0 && (recv_x == nullptr || recv_topk_weights == nullptr || recv_src_info == nullptr))
         return EP_ERR_INVALID_ARG;
-    if (num_scales > 0 && (x_scales == nullptr || (recv_capacity > 0 && recv_x_scales == nullptr)))
+    if (num_scales > 0 && ((quant_log2 < 0 && x_scales == nullptr) || (recv_capacity > 0 && recv_x_scales == nullptr)))
         return EP_ERR_INVALID_ARG;
     if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
     if (recv_src_info != nullptr && (reinterpret_cast<uintptr_t>(recv_src_info) & 7u) != 0) return EP_ERR_INVALID_ARG;
@@ -97,6 +99,8 @@ ep_status_t dispatch_checked(const ep_shape_t *s, const void *x, int64_t row_byt
     a.send_slot = send_slot;
     a.form = form;
     a.dev_status = dev_status;
+    a.quantize = quant_log2 >= 0;
+    a.quant_log2 = quant_log2 >= 0 ? quant_log2 : 0;
     return from_hip(launch_dispatch(*s, a, stream));
 }
 
@@ -436,6 +440,22 @@ ep_status_t ep_combine(const ep_shape_t *s, const void *y, const float *recv_top
     if (!aligned16(combined_x) || (y != nullptr && !aligned16(y))) return EP_ERR_INVALID_ARG;
     return from_hip(launch_combine(*s, static_cast<const uint4 *>(y), recv_topk_weights, send_slot, num_recv_rows,
                                    static_cast<uint4 *>(combined_x), combined_topk_weights, dev_status, stream));
+}
+
+ep_status_t ep_dispatch_to_fp8(const ep_shape_t *s, const void *x, int32_t num_scales, const int64_t *topk_idx,
+                              const float *topk_weights, const uint8_t *is_token_in_rank,
+                              const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
+                              const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
+                              float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
+                              int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
+    if (s == nullptr) return EP_ERR_INVALID_ARG;
+    if (s->hidden % kQuantChannels != 0 || num_scales < 1 || s->hidden % num_scales != 0) return EP_ERR_INVALID_ARG;
+    const int l = quant_lanes_log2(s->hidden, num_scales);
+    if (l < 0) return EP_ERR_UNSUPPORTED;
+    return dispatch_checked(s, x, (int64_t)s->hidden, nullptr, num_scales, topk_idx, topk_weights, is_token_in_rank,
+                            gbl_channel_prefix_matrix, recv_gbl_rank_prefix_sum, workspace, workspace_bytes,
+                            recv_capacity, recv_x, recv_x_scales, recv_topk_weights, recv_topk_idx, recv_src_info,
+                            send_slot, EP_FORM_PUSH, dev_status, stream, l);
 }
 
 ep_status_t ep_quantize_fp8(const void *x, int64_t num_rows, int32_t hidden, int32_t num_scales, void *x_fp8,

@@ -65,6 +65,7 @@ struct DispatchParams {
     int64_t row_units;  // 16-byte units per row
     int R, K, E, C, experts_per_rank, my_rank, cap, S, num_scales;
     int in_unit;        // load unit of an is_token_in_rank row (16, 8 or 1 bytes)
+    int quant_log2;     // quantising dispatch: log2 of the lanes per scale group
     bool derive;        // routing from is_token_in_rank and the prefix matrix (no workspace)
 };
 
@@ -230,7 +231,12 @@ __device__ __forceinline__ void token_metadata(const DispatchParams &p, int64_t 
 // slabs instead of spreading over all of them.  GRAN == 0: free-running waves.
 // CACHED: the rows come from send_slot of an earlier dispatch with the same
 // routing (p.cached_slot); no routing, metadata or send_slot output.
-template <int VPL, bool EXACT, int WPB, int GRAN, bool CACHED>
+// QUANT: x is bf16 and each row leaves as E4M3 codes plus its scales (the
+// quantiser of ep_quantize_fp8, run once per token segment before the stores).
+// Units are then those of the fp8 row: lane i of slice j owns 16 channels, two
+// 16-byte loads of x and one 16-byte store per destination; a scale group is
+// 1 << quant_log2 aligned lanes, and its first lane stores the group's scale.
+template <int VPL, bool EXACT, int WPB, int GRAN, bool CACHED, bool QUANT = false>
 __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t w0 = (int64_t)blockIdx.x * WPB + (threadIdx.x >> 6);
@@ -244,11 +250,26 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
 
     // ---- the x segment: issued first, consumed last
     const int64_t c0 = (int64_t)seg * VPL * kWave + lane;
-    const u32x4 *src = p.x + t * p.row_units + c0;
     u32x4 v[VPL > 0 ? VPL : 1];  // VPL == 0: metadata only, no row
+    u32x4 vh[QUANT ? VPL : 1];   // QUANT: channels 8-15 of the lane's 16 (v holds 0-7)
+    if constexpr (QUANT) {
+        const u32x4 *src = p.x + 2 * (t * p.row_units + c0);  // two bf16 units per fp8 unit
+        const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < VPL; ++i)
-        if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+        for (int i = 0; i < VPL; ++i) {
+            if (EXACT || c0 + i * kWave < p.row_units) {
+                v[i] = __builtin_nontemporal_load(src + 2 * i * kWave);
+                vh[i] = __builtin_nontemporal_load(src + 2 * i * kWave + 1);
+            } else {
+                v[i] = vh[i] = zero;  // past the row: whole groups of zeros, never stored
+            }
+        }
+    } else {
+        const u32x4 *src = p.x + t * p.row_units + c0;
+#pragma unroll
+        for (int i = 0; i < VPL; ++i)
+            if (EXACT || c0 + i * kWave < p.row_units) v[i] = __builtin_nontemporal_load(src + i * kWave);
+    }
 
     int slot = -1;
     int64_t e = -1;
@@ -315,10 +336,17 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
     if (!live) slot = -1;
     const uint64_t dests = ballot64(slot >= 0);
 
-    if (live && seg == 0) copy_scales(p, t, slot, dests, lane);
+    if (!QUANT && live && seg == 0) copy_scales(p, t, slot, dests, lane);
     if (!CACHED && live && seg == 0) token_metadata(p, t, slot, dests, e, wt, lane);
 
     if (VPL == 0) return;  // metadata only
+    // ---- QUANT: the segment's codes (in v) and its groups' scales, once for every destination
+    float qs[QUANT ? VPL : 1];
+    if constexpr (QUANT) {
+#pragma unroll
+        for (int i = 0; i < VPL; ++i) v[i] = e4m3_quantize16(v[i], vh[i], p.quant_log2, &qs[i]);
+    }
+    const bool qlead = QUANT && (lane & ((1 << p.quant_log2) - 1)) == 0;
     // ---- row copy (a4): the segment to every destination, ranks ascending
     auto store_to = [&](uint64_t dd) {
         for (; dd != 0ull; dd &= dd - 1ull) {
@@ -328,6 +356,12 @@ __global__ __launch_bounds__(WPB *kWave) void dispatch_kernel(DispatchParams p) 
 #pragma unroll
             for (int i = 0; i < VPL; ++i)
                 if (EXACT || c0 + i * kWave < p.row_units) __builtin_nontemporal_store(v[i], dst + i * kWave);
+            if constexpr (QUANT) {
+                float *ds = p.recv_scales + s * p.num_scales;
+#pragma unroll
+                for (int i = 0; i < VPL; ++i)
+                    if (qlead && (EXACT || c0 + i * kWave < p.row_units)) ds[(c0 + i * kWave) >> p.quant_log2] = qs[i];
+            }
         }
     };
     if (GRAN == 0) {
@@ -1233,12 +1267,15 @@ hipError_t run_pull(DispatchParams p, int blocks_per_xcd, hipStream_t stream) {
     return hipGetLastError();
 }
 
-template <int VPL, bool EXACT, int WPB, int GRAN>
+template <int VPL, bool EXACT, int WPB, int GRAN, bool QUANT = false>
 hipError_t run(DispatchParams p, hipStream_t stream) {
     p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    if (p.cached_slot != nullptr)
+    if constexpr (QUANT)
+        hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, false, true>), dim3((unsigned)blocks),
+                           dim3(WPB * kWave), 0, stream, p);
+    else if (p.cached_slot != nullptr)
         hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, true>), dim3((unsigned)blocks), dim3(WPB * kWave),
                            0, stream, p);
     else
@@ -1344,6 +1381,17 @@ void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, 
     }
 }
 
+// The quantising dispatch (push form).  For 7168 channels from 4096 tokens whole rows
+// per wave, 4 free-running waves per block: 56.8 us at prefill, against 59.3-60.6 with
+// the rank sweep of the fp8 rows (16 waves, a barrier every 4 ranks), 57.0-57.5 with 8
+// or 16 free-running waves, 58.0-61.8 with the row split over 2, 4 or 7 waves (one run).
+// Below 4096 tokens 4096-channel segments; other widths 1024-channel segments, 8 waves.
+hipError_t run_quant_tiled(const DispatchParams &p, hipStream_t stream) {
+    if (p.row_units == 7 * kWave)
+        return p.T >= 4096 ? run<7, true, 4, 0, true>(p, stream) : run<4, false, 4, 0, true>(p, stream);
+    return p.row_units % kWave == 0 ? run<1, true, 8, 0, true>(p, stream) : run<1, false, 8, 0, true>(p, stream);
+}
+
 template <int U, bool EXACT, int NE>
 hipError_t run_grouped_pull(const DispatchParams &p, const GroupedOut &o, hipStream_t stream) {
     hipLaunchKernelGGL((dispatch_grouped_pull_kernel<U, EXACT, NE>), dim3((unsigned)(kXcds * kGpBlocksPerXcd)),
@@ -1412,6 +1460,7 @@ DispatchParams make_params(const ep_shape_t &s, const DispatchArgs &a) {
     p.my_rank = s.my_rank;
     p.cap = a.cap;
     p.num_scales = a.num_scales;
+    p.quant_log2 = a.quantize ? a.quant_log2 : 0;
     p.S = 1;
     return p;
 }
@@ -1434,6 +1483,7 @@ hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream
         p.num_scales = 0;  // no rows, so no scales beside them
         return run_meta(p, stream);
     }
+    if (a.quantize) return run_quant_tiled(p, stream);
     // cached mode always takes the push form
     if (a.form != EP_FORM_PUSH && p.cached_slot == nullptr) {
         const PullTiling pt = pull_tiling(p.row_units, p.T);

@@ -117,6 +117,9 @@ struct DispatchArgs {
     int32_t *send_slot;
     int32_t *dev_status;
     int form;          // ep_dispatch_form_t: EP_FORM_PUSH keeps the push form
+    bool quantize;     // x is bf16 and every row leaves as E4M3 codes with num_scales scales
+                       // (push form; row_units counts the 16-byte units of the fp8 row)
+    int quant_log2;    // with quantize: log2 of the lanes (16 channels each) per scale group
 };
 
 hipError_t launch_dispatch(const ep_shape_t &s, const DispatchArgs &a, hipStream_t stream);
@@ -383,6 +386,61 @@ __device__ __forceinline__ bool elect_completing_block(uint64_t *ticket, uint32_
     }
     __syncthreads();
     return last;
+}
+
+// ---------------------------------------------------------------- E4M3 quantiser
+// Shared by ep_quantize_fp8 and the dispatch that quantises on the way (one code path,
+// so both give the same codes and scales).  A group of 16 << lanes_log2 channels is
+// 1 << lanes_log2 aligned lanes, each owning 16 consecutive channels.
+//   a = max(largest |x| of the group, 2^-64); scale = a / 448;
+//   code = e4m3(clamp(x * (448 / a), -448, 448)), nearest with ties to even
+// (v_cvt_pk_fp8_f32 under the default rounding mode; OCP E4M3, bias 7, largest 448).
+typedef unsigned int qvec4 __attribute__((ext_vector_type(4)));
+constexpr float kE4m3Max = 448.0f;
+constexpr float kE4m3AmaxFloor = 0x1p-64f;  // keeps 448 / a finite and the scale a normal number
+
+__device__ __forceinline__ uint32_t e4m3_pack4(float v0, float v1, float v2, float v3) {
+    v0 = __builtin_amdgcn_fmed3f(v0, -kE4m3Max, kE4m3Max);
+    v1 = __builtin_amdgcn_fmed3f(v1, -kE4m3Max, kE4m3Max);
+    v2 = __builtin_amdgcn_fmed3f(v2, -kE4m3Max, kE4m3Max);
+    v3 = __builtin_amdgcn_fmed3f(v3, -kE4m3Max, kE4m3Max);
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);  // bytes 0, 1
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);       // bytes 2, 3
+    return (uint32_t)w;
+}
+
+// Larger magnitude of each half of two bf16 pairs: for finite values the magnitude's bit
+// pattern (sign cleared) orders as its value, so one packed 16-bit integer max serves.
+__device__ __forceinline__ uint32_t bf16x2_absmax(uint32_t m, uint32_t w) {
+    typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+    const u16x2 a = __builtin_bit_cast(u16x2, w & 0x7fff7fffu), b = __builtin_bit_cast(u16x2, m);
+    return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(a, b));
+}
+
+// lo / hi: the lane's channels 0-7 / 8-15 as bf16 pairs.  Every lane of the wave must
+// call this together (the group's maximum is a butterfly of lane shuffles); lanes that own
+// no channels pass zeros and form whole groups of their own.
+__device__ __forceinline__ qvec4 e4m3_quantize16(qvec4 lo, qvec4 hi, int lanes_log2, float *scale) {
+    uint32_t mm = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) mm = bf16x2_absmax(bf16x2_absmax(mm, lo[k]), hi[k]);
+    const uint32_t mb = (mm & 0xffffu) > (mm >> 16) ? (mm & 0xffffu) : (mm >> 16);
+    float m = __uint_as_float(mb << 16);
+    for (int s = 1; s < (1 << lanes_log2); s <<= 1) m = fmaxf(m, __shfl_xor(m, s));
+    m = fmaxf(m, kE4m3AmaxFloor);
+    const float inv = kE4m3Max / m;
+    *scale = m / kE4m3Max;
+    qvec4 c;
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+        c[k] = e4m3_pack4(__uint_as_float(lo[2 * k] << 16) * inv, __uint_as_float(lo[2 * k] & 0xffff0000u) * inv,
+                          __uint_as_float(lo[2 * k + 1] << 16) * inv,
+                          __uint_as_float(lo[2 * k + 1] & 0xffff0000u) * inv);
+        c[2 + k] = e4m3_pack4(__uint_as_float(hi[2 * k] << 16) * inv, __uint_as_float(hi[2 * k] & 0xffff0000u) * inv,
+                              __uint_as_float(hi[2 * k + 1] << 16) * inv,
+                              __uint_as_float(hi[2 * k + 1] & 0xffff0000u) * inv);
+    }
+    return c;
 }
 
 }  // namespace ep

@@ -24,7 +24,9 @@
 // The conversions are gfx950's own: v_cvt_pk_fp8_f32 (nearest-even under the
 // default rounding mode; its input is clamped to +-448 first, so no input is out
 // of range) and v_cvt_pk_f32_fp8 (exact).  fp32 division is the compiler's
-// correctly rounded sequence, once per group.
+// correctly rounded sequence, once per group.  The per-lane quantisation step
+// (e4m3_quantize16, ep_internal.h) is the one the dispatch that quantises on the
+// way runs too.
 #include "ep_internal.h"
 
 namespace ep {
@@ -35,8 +37,6 @@ typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kQuantWaves = 4;          // waves per block
 constexpr int64_t kQuantMaxBlocks = 1 << 16;
-constexpr float kE4m3Max = 448.0f;
-constexpr float kAmaxFloor = 0x1p-64f;  // keeps 448 / a finite and the scale a normal number
 
 struct QuantParams {
     const u32x4 *x;      // bf16 [units][2]: unit u = channels 16u .. 16u+15 of the flattened rows
@@ -54,9 +54,6 @@ struct DequantParams {
     int lanes_log2;
 };
 
-__device__ __forceinline__ float bf16_lo(uint32_t u) { return __uint_as_float(u << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
-
 // fp32 -> bf16, nearest, ties to even; NaN stays a quiet NaN.
 __device__ __forceinline__ uint32_t to_bf16(float f) {
     const uint32_t u = __float_as_uint(f);
@@ -64,21 +61,10 @@ __device__ __forceinline__ uint32_t to_bf16(float f) {
     return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
 }
 
-// Four codes (one dword) from four values already scaled.
-__device__ __forceinline__ uint32_t pack_e4m3(float v0, float v1, float v2, float v3) {
-    v0 = __builtin_amdgcn_fmed3f(v0, -kE4m3Max, kE4m3Max);
-    v1 = __builtin_amdgcn_fmed3f(v1, -kE4m3Max, kE4m3Max);
-    v2 = __builtin_amdgcn_fmed3f(v2, -kE4m3Max, kE4m3Max);
-    v3 = __builtin_amdgcn_fmed3f(v3, -kE4m3Max, kE4m3Max);
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v0, v1, 0, false);  // bytes 0, 1
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v2, v3, w, true);       // bytes 2, 3
-    return (uint32_t)w;
-}
-
 __global__ __launch_bounds__(kQuantWaves *kWave) void quantize_e4m3_kernel(QuantParams p) {
     const int lane = threadIdx.x & (kWave - 1);
     const int64_t nwaves = (int64_t)gridDim.x * kQuantWaves;
-    const int L = 1 << p.lanes_log2;
+    const int lead_mask = (1 << p.lanes_log2) - 1;
     for (int64_t w = (int64_t)blockIdx.x * kQuantWaves + (threadIdx.x >> 6); w * kWave < p.units; w += nwaves) {
         const int64_t u = w * kWave + lane;
         const bool on = u < p.units;  // a wave's idle tail lanes form whole groups of their own
@@ -87,26 +73,11 @@ __global__ __launch_bounds__(kQuantWaves *kWave) void quantize_e4m3_kernel(Quant
             a = p.x[2 * u];
             b = p.x[2 * u + 1];
         }
-        float f[16];
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            f[2 * k] = bf16_lo(a[k]);
-            f[2 * k + 1] = bf16_hi(a[k]);
-            f[8 + 2 * k] = bf16_lo(b[k]);
-            f[8 + 2 * k + 1] = bf16_hi(b[k]);
-        }
-        float m = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) m = fmaxf(m, fabsf(f[i]));
-        for (int s = 1; s < L; s <<= 1) m = fmaxf(m, __shfl_xor(m, s));  // the group's lanes only
-        m = fmaxf(m, kAmaxFloor);
-        const float inv = kE4m3Max / m;
-        u32x4 c;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) c[k] = pack_e4m3(f[4 * k] * inv, f[4 * k + 1] * inv, f[4 * k + 2] * inv, f[4 * k + 3] * inv);
+        float scale;
+        const u32x4 c = e4m3_quantize16(a, b, p.lanes_log2, &scale);
         if (on) {
             p.codes[u] = c;
-            if ((lane & (L - 1)) == 0) p.scales[u >> p.lanes_log2] = m / kE4m3Max;
+            if ((lane & lead_mask) == 0) p.scales[u >> p.lanes_log2] = scale;
         }
     }
 }

@@ -23,7 +23,7 @@ EP_DEV_STALE_WORKSPACE = 16
 EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL = 0, 1, 2
 
 EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8",
-            "ep_quantize_fp8", "ep_dequantize_fp8", "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
+            "ep_dispatch_to_fp8", "ep_quantize_fp8", "ep_dequantize_fp8", "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
             "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
@@ -67,10 +67,13 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_dispatch_grouped.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, _P,
                                         ctypes.c_size_t, ctypes.c_int32, _P, _P, _P, _P, ctypes.c_int32] + [_P] * 8
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
+    lib.ep_dispatch_to_fp8.argtypes = [_S, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
+                                       ctypes.c_int32] + [_P] * 8
     lib.ep_quantize_fp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
     lib.ep_dequantize_fp8.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
     for name in ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
-                 "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_quantize_fp8", "ep_dequantize_fp8"):
+                 "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_quantize_fp8", "ep_dequantize_fp8",
+                 "ep_dispatch_to_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -243,6 +246,18 @@ def ep_combine(shape, y, recv_topk_weights, send_slot, num_recv_rows, combined_x
     _check(load().ep_combine(ctypes.byref(shape), _ptr(y), _ptr(recv_topk_weights), _ptr(send_slot),
                              int(num_recv_rows), _ptr(combined_x), _ptr(combined_topk_weights), _ptr(dev_status),
                              _stream(stream)), "ep_combine")
+
+
+def ep_dispatch_to_fp8(shape, x, num_scales, topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+                       recv_gbl_rank_prefix_sum, workspace, recv_capacity, recv_x, recv_x_scales, recv_topk_weights,
+                       recv_topk_idx, recv_src_info, send_slot, dev_status=None, stream=None) -> None:
+    ws, ws_bytes = _ws(workspace)
+    _check(load().ep_dispatch_to_fp8(ctypes.byref(shape), _ptr(x), int(num_scales), _ptr(topk_idx), _ptr(topk_weights),
+                                     _ptr(is_token_in_rank), _ptr(gbl_channel_prefix_matrix),
+                                     _ptr(recv_gbl_rank_prefix_sum), ws, ws_bytes, int(recv_capacity), _ptr(recv_x),
+                                     _ptr(recv_x_scales), _ptr(recv_topk_weights), _ptr(recv_topk_idx),
+                                     _ptr(recv_src_info), _ptr(send_slot), _ptr(dev_status), _stream(stream)),
+           "ep_dispatch_to_fp8")
 
 
 def ep_quantize_fp8(x, num_rows, hidden, num_scales, x_fp8, x_scales, stream=None) -> None:

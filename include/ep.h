@@ -13,6 +13,7 @@
  * and beside them:
  *   ep_dispatch_fp8     dispatch of 1-byte (fp8) rows with their per-token scales
  *   ep_quantize_fp8     bf16 rows -> E4M3 rows and scales for it; ep_dequantize_fp8 back
+ *   ep_dispatch_to_fp8  bf16 rows in, fp8 rows and scales out: the two above in one launch
  *   ep_dispatch_cached  new rows to the rows an earlier dispatch assigned (cached mode)
  *   ep_group_by_expert  receive rows regrouped into per-expert segments for grouped GEMMs
  *   ep_dispatch_grouped dispatch straight into those segments, with no receive rows
@@ -272,6 +273,31 @@ ep_status_t ep_dispatch_fp8(const ep_shape_t *s, const void *x, const float *x_s
  */
 ep_status_t ep_quantize_fp8(const void *x, int64_t num_rows, int32_t hidden, int32_t num_scales, void *x_fp8,
                             float *x_scales, hipStream_t stream);
+
+/*
+ * Dispatch of bf16 rows that arrive as fp8 rows with scales: ep_quantize_fp8 of x followed by
+ * ep_dispatch_fp8 of its codes and scales, in one launch and bit for bit the same outputs.
+ * [mscclpp ht_runtime.cc, intranodeDispatch / internodeDispatch with xElementSize 1 and xScales:
+ * the receive side gets fp8 rows and the FP8 scale buffer; the quantiser as for ep_quantize_fp8]
+ * Each token's row is read once (2h bytes), quantised once per group of hidden / num_scales
+ * channels, and its h-byte codes and num_scales scales are stored to every destination rank, so
+ * neither the fp8 copy of x nor its scales pass through HBM on this rank.
+ * In:  x [t][h] bf16 (finite); num_scales as for ep_quantize_fp8 (groups of 16 to 1024 channels);
+ *      topk_idx, topk_weights, is_token_in_rank, gbl_channel_prefix_matrix,
+ *      recv_gbl_rank_prefix_sum and workspace (nullable) as for ep_dispatch.
+ * Out: recv_x [cap][h] uint8 E4M3 codes; recv_x_scales [cap][num_scales] f32; recv_topk_weights,
+ *      recv_topk_idx (nullable), recv_src_info and send_slot as for ep_dispatch.
+ * The row copy takes the push form (token order; the pull form has no quantising variant).
+ * Limits: hidden % 16 == 0 and num_scales dividing it (EP_ERR_INVALID_ARG), groups of
+ * 16 << l channels, 0 <= l <= 6 (EP_ERR_UNSUPPORTED); the rest as for ep_dispatch_fp8.
+ * dev_status (nullable): as for ep_dispatch.
+ */
+ep_status_t ep_dispatch_to_fp8(const ep_shape_t *s, const void *x, int32_t num_scales, const int64_t *topk_idx,
+                              const float *topk_weights, const uint8_t *is_token_in_rank,
+                              const int32_t *gbl_channel_prefix_matrix, const int32_t *recv_gbl_rank_prefix_sum,
+                              const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
+                              float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
+                              int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream);
 
 /*
  * The inverse of ep_quantize_fp8, for rows an fp8 dispatch delivered (recv_x, recv_x_scales).

@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify",
                                           "ep_dispatch",
                                           "ep_dispatch_fp8", "ep_quantize_fp8", "ep_dequantize_fp8",
+                                          "ep_dispatch_to_fp8",
                                           "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
                                           "ep_combine", "ep_workspace_bytes", "ep_status_string"])
 
@@ -169,6 +170,15 @@ def test_quantize_argument_checks(ep):
         assert fn(4, 4096, 2) == ep.EP_ERR_UNSUPPORTED        # groups of 2048 channels
         assert fn(4, 96, 12) == ep.EP_ERR_UNSUPPORTED         # groups of 8 channels
         assert fn(0, 7168, 56) == ep.EP_OK                    # nothing to do, nothing enqueued
+    s = _shape(ep)
+    d = lambda sh, S, **kw: lib.ep_dispatch_to_fp8(ctypes.byref(sh), kw.get("x", p), S, p, p, p, p, p, None, 0,  # noqa: E731
+                                                   kw.get("cap", 10), p, kw.get("rs", p), p, p, p, p, None, None)
+    assert d(s, 3) == ep.EP_ERR_INVALID_ARG                    # 3 does not divide hidden
+    assert d(s, 64) == ep.EP_ERR_UNSUPPORTED                   # groups of 112 channels
+    assert d(_shape(ep, hidden=7160), 1) == ep.EP_ERR_INVALID_ARG
+    assert d(s, 56, rs=None) == ep.EP_ERR_INVALID_ARG          # scales out missing
+    assert d(s, 56, x=ctypes.c_void_p(264)) == ep.EP_ERR_INVALID_ARG  # x not 16-byte aligned
+    assert d(s, 56, x=None) == ep.EP_ERR_INVALID_ARG
     q = ctypes.c_void_p(264)  # 8-byte aligned only
     assert lib.ep_quantize_fp8(q, 4, 7168, 56, p, p, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_quantize_fp8(p, 4, 7168, 56, q, p, None) == ep.EP_ERR_INVALID_ARG

@@ -4,6 +4,8 @@ to 1024 channels with ragged row counts and rows that are not a whole number of 
 groups that are all zero, signed zeros, bf16 subnormals or span the whole exponent range, the
 prefill size, and the chain quantise -> ep_dispatch_fp8 -> dequantise against the same chain in
 the oracle."""
+import zlib
+
 import numpy as np
 import pytest
 import torch
@@ -180,3 +182,97 @@ def test_quantize_dispatch_dequantize_chain(name):
     _same_scales("recv_x_scales", rs[:n].cpu().numpy(), dd["recv_x_scales"][:n])
     back = o.dequantize_e4m3(dd["recv_x"][:n], dd["recv_x_scales"][:n])
     assert np.array_equal(bf16_host(out[:n]), back)
+
+
+def _dispatch_to_fp8_case(x, idx, w, E, R, C, S, capacity=None, use_workspace=True):
+    """GPU: layout, notify, then ep_dispatch_to_fp8; oracle: quantise, layout, notify, fp8 dispatch."""
+    T, H = x.shape
+    K = idx.shape[1]
+    shape = ep.make_shape(T, H, K, E, R, C)
+    cap = capacity if capacity is not None else T * min(R, K)
+    b = ep.allocate(shape, 0)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    n = ep.run_notify(b, read_back=True)
+    rows = min(n, cap)
+    dx = to_dev_bf16(x)
+    rx = torch.full((max(cap, 1), H), 0xAB, dtype=torch.uint8, device="cuda")
+    rs = torch.full((max(cap, 1), S), -2.0, dtype=torch.float32, device="cuda")
+    rw = torch.full((max(cap, 1), K), -3.0, dtype=torch.float32, device="cuda")
+    ri = torch.full((max(cap, 1), K), -777, dtype=torch.int64, device="cuda")
+    si = torch.full((max(cap, 1), 2), -777, dtype=torch.int32, device="cuda")
+    ss = torch.full((T, R), -777, dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_to_fp8(shape, dx, S, didx, dw, b.in_rank, b.gbl, b.recv_gbl, b.workspace if use_workspace else None,
+                          cap, rx, rs, rw, ri, si, ss, st)
+    torch.cuda.synchronize()
+    gpu = dict(send_slot=ss.cpu().numpy(), recv_x=rx[:rows].cpu().numpy(), recv_x_scales=rs[:rows].cpu().numpy(),
+               recv_topk_weights=rw[:rows].cpu().numpy(), recv_topk_idx=ri[:rows].cpu().numpy(),
+               recv_src_info=si[:rows].cpu().numpy(), status=int(st.item()))
+    o = oracle.Oracle()
+    q, s = o.quantize_e4m3(x, S)
+    lay = o.layout(idx, E, R)
+    note = o.notify(lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+                    lay["num_tokens_per_expert"], C, 1)
+    d = o.dispatch_fp8(q, s, idx, w, lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                       note["recv_gbl_rank_prefix_sum"], E, recv_capacity=cap)
+    ref = dict(send_slot=d["send_slot"], recv_x=d["recv_x"][:rows], recv_x_scales=d["recv_x_scales"][:rows],
+               recv_topk_weights=d["recv_topk_weights"][:rows], recv_topk_idx=d["recv_topk_idx"][:rows],
+               recv_src_info=d["recv_src_info"][:rows], status=d["status"])
+    return gpu, ref
+
+
+def _assert_same(gpu, ref):
+    bad = [k for k in ref if k != "status" and not np.array_equal(np.asarray(gpu[k]).view(np.uint8),
+                                                                   np.asarray(ref[k]).view(np.uint8))]
+    assert not bad, bad
+    assert gpu["status"] == ref["status"], (gpu["status"], ref["status"])
+
+
+@pytest.mark.parametrize("name", ["tiny", "sweep", "prefill", "skew", "large"])
+def test_dispatch_to_fp8_workloads(name):
+    """The five workloads at full size, groups of 128 channels (large: 4096 channels, 32 scales)."""
+    print(f"[quant] dispatch_to_fp8 workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    gpu, ref = _dispatch_to_fp8_case(d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels,
+                                     wl.hidden // 128)
+    _assert_same(gpu, ref)
+
+
+# (tokens, hidden, num_scales, ranks, experts, topk, channels, capacity delta, workspace): every tiling
+# of the quantising push form (whole 7168-channel rows with the rank sweep from 4096 tokens, 4096-channel
+# segments below, 1024-channel segments for other widths, ragged when the width is not a whole number of
+# them), groups of 16 to 1024 channels, a receive capacity short of N, and no workspace
+DISPATCH_TO_FP8 = {
+    "h7168_t4100_ragged_groups_of_tokens": (4100, 7168, 56, 16, 64, 6, 20, 0, True),
+    "h7168_t2304_segments": (2304, 7168, 7, 64, 256, 8, 24, 0, True),
+    "h7168_t300_g16_no_ws": (300, 7168, 448, 8, 32, 4, 6, 0, False),
+    "h896_g64_ragged_segment": (777, 896, 14, 24, 48, 5, 9, -40, True),
+    "h2560_g256": (513, 2560, 10, 4, 16, 3, 4, 0, False),
+    "h1024_g1024": (200, 1024, 1, 32, 64, 8, 3, -100, True),
+    "h48_g16": (129, 48, 3, 2, 4, 2, 2, 0, True),
+}
+
+
+@pytest.mark.parametrize("case", sorted(DISPATCH_TO_FP8))
+def test_dispatch_to_fp8_shapes(case):
+    T, H, S, R, E, K, C, dcap, use_ws = DISPATCH_TO_FP8[case]
+    print(f"[quant] dispatch_to_fp8 {case}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    x = pins.quantize_groups(rng, T, H, S)
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    idx[rng.random((T, K)) < 0.1] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    n_ref = None
+    cap = None
+    if dcap:
+        o = oracle.Oracle()
+        lay = o.layout(idx, E, R)
+        n_ref = int(lay["num_tokens_per_rank"].sum())
+        cap = n_ref + dcap
+    gpu, ref = _dispatch_to_fp8_case(x, idx, w, E, R, C, S, capacity=cap, use_workspace=use_ws)
+    _assert_same(gpu, ref)
+    if dcap < 0:
+        assert gpu["status"] & ep.EP_DEV_RECV_OVERFLOW
