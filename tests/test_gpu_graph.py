@@ -100,3 +100,76 @@ def test_step_in_a_graph_replays_exactly(name):
         bad = [k for k in want if not torch.equal(got[k], want[k])]
         assert not bad, f"replay {replay}: {bad}"
         assert int(got["status"].item()) == 0
+
+
+def _fp8_calls(shape, b, x, idx, w, S, out):
+    """layout, notify, the quantiser, the fp8 dispatch of its output, the quantising dispatch and the
+    dequantiser of its rows, all on torch's current stream into the buffers of `out`"""
+    T, H = shape.num_tokens, shape.hidden
+    cap = out["rx"].shape[0]
+    ep.run_layout(b, idx)
+    ep.run_notify(b)
+    ep.ep_quantize_fp8(x, T, H, S, out["q"], out["qs"])
+    ep.ep_dispatch_fp8(shape, out["q"], out["qs"], S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, cap,
+                       out["rx"], out["rs"], b.recv_w, b.recv_idx, b.src_info, out["slot"], b.dev_status)
+    ep.ep_dispatch_to_fp8(shape, x, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, cap, out["tx"], out["ts"],
+                          b.recv_w, b.recv_idx, b.src_info, out["tslot"], b.dev_status)
+    ep.ep_dequantize_fp8(out["tx"], out["ts"], cap, H, S, out["back"])
+
+
+def _fp8_buffers(T, H, S, R, cap):
+    u8, f32, i32 = dict(dtype=torch.uint8, device="cuda"), dict(dtype=torch.float32, device="cuda"), \
+        dict(dtype=torch.int32, device="cuda")
+    return {"q": torch.zeros((T, H), **u8), "qs": torch.zeros((T, S), **f32), "rx": torch.zeros((cap, H), **u8),
+            "rs": torch.zeros((cap, S), **f32), "slot": torch.zeros((T, R), **i32), "tx": torch.zeros((cap, H), **u8),
+            "ts": torch.zeros((cap, S), **f32), "tslot": torch.zeros((T, R), **i32),
+            "back": torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda")}
+
+
+def test_fp8_path_in_a_graph_replays_exactly():
+    """The quantiser, the fp8 dispatch of its output, the quantising dispatch and the dequantiser, captured
+    after layout and notify in one graph and replayed on new inputs: every replay equals an eager run."""
+    print("[graph] fp8 path, workload=sweep", flush=True)
+    d = generate("sweep")
+    wl = d["workload"]
+    T, H, K, E, R, C = wl.tokens, wl.hidden, wl.topk, wl.experts, wl.ranks, wl.channels
+    S = H // 128
+    shape = ep.make_shape(T, H, K, E, R, C)
+    x = torch.from_numpy(d["x"].view(np.int16)).cuda().view(torch.bfloat16)
+    idx = torch.from_numpy(d["topk_idx"]).cuda()
+    w = torch.from_numpy(d["topk_weights"]).cuda()
+    cap = T * min(R, K)
+    gx, gidx, gw = x.clone(), idx.clone(), w.clone()
+    b = ep.allocate(shape, cap)
+    out = _fp8_buffers(T, H, S, R, cap)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        _fp8_calls(shape, b, gx, gidx, gw, S, out)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _fp8_calls(shape, b, gx, gidx, gw, S, out)
+    rng = np.random.default_rng(78)
+    for replay in range(3):
+        perm = torch.from_numpy(rng.permutation(T)).cuda()
+        gidx.copy_(idx[perm])
+        gw.copy_(w[perm])
+        gx.copy_((x.float() * float(2 * replay + 3)).to(torch.bfloat16))
+        b.dev_status.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        rb = ep.allocate(shape, cap)
+        ref = _fp8_buffers(T, H, S, R, cap)
+        _fp8_calls(shape, rb, gx.clone(), gidx.clone(), gw.clone(), S, ref)
+        torch.cuda.synchronize()
+        n = int(rb.num_recv.item())
+        bad = [k for k in ("q", "qs", "slot", "tslot") if not torch.equal(out[k], ref[k])]
+        bad += [k for k in ("rx", "rs", "tx", "ts") if not torch.equal(out[k][:n], ref[k][:n])]
+        if not torch.equal(out["back"][:n].view(torch.int16), ref["back"][:n].view(torch.int16)):
+            bad.append("back")
+        assert not bad, f"replay {replay}: {bad}"
+        assert torch.equal(out["tx"][:n], out["rx"][:n]) and torch.equal(out["ts"][:n], out["rs"][:n])
+        assert int(b.dev_status.item()) == 0
