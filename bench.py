@@ -537,7 +537,8 @@ def main() -> int:
         step(events[i])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    us_dc = float(np.mean([timer.elapsed_us(a, c) for a, c in events]))
+    dc_steps = [timer.elapsed_us(a, c) for a, c in events]
+    us_dc = float(np.mean(dc_steps))
 
     # each kernel's average launch duration: K back-to-back launches between one event pair
     us = {k: timer.mean_us(f, args.steps) for k, f in calls.items()}
@@ -659,6 +660,7 @@ def main() -> int:
                                f"({max(1, R // 8)} nodes x 8), channels={C}, uniform routing, seed {wl.seed}",
                    "global_batch": T, "seq_len": 1, "parallelism": "single GPU share (one source rank)"},
         "us_per_iter_dispatch_plus_combine": round(us_dc, 2),
+        "us_dispatch_plus_combine_median_min": [round(float(np.median(dc_steps)), 2), round(float(min(dc_steps)), 2)],
         "pct_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
         "us_layout": round(us["layout"], 2),
         "us_notify": round(us["notify"], 2),
