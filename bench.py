@@ -63,6 +63,11 @@ def dispatch_to_fp8_bytes(T, H, K, R, N, S) -> int:
     return T * 2 * H + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
 
 
+def dequantize_bytes(N, H, S) -> int:
+    """E4M3 rows and their S fp32 scales read once, bf16 rows written."""
+    return N * (H + 4 * S) + N * 2 * H
+
+
 def quantize_bytes(T, H, S) -> int:
     """bf16 rows read once, E4M3 rows (1 byte an element) and S fp32 scales per row written."""
     return T * 2 * H + T * (H + 4 * S)
@@ -102,6 +107,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "dispatch_grouped_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "quantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
                   "dispatch_kernel_to_fp8": ["ep_dispatch.hip", "ep_internal.h"],
+                  "dequantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"],
                   "combine_staged_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
@@ -416,7 +422,17 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
                                       b.recv_w, b.recv_idx, b.src_info, slot2, b.dev_status)))
     out["dispatch_to_fp8"]["check"] = bool(torch.equal(slot2, slot8) and torch.equal(rx2, rx) and torch.equal(rs2, rs))
     out["dispatch_to_fp8"]["traffic"] = measured_traffic("dispatch_kernel_to_fp8", wl.name)
-    del rx2, rs2, slot2
+    # the receive side's dequantiser on those rows (E4M3 codes and scales -> bf16); checked on the host on
+    # a sample of rows: torch's float8 decoding times the scale in fp32, rounded to bf16 by torch
+    back = torch.empty((n_recv, H), dtype=torch.bfloat16, device=x.device)
+    out["dequantize_fp8"] = rate(dequantize_bytes(n_recv, H, S),
+                                 mean_us(lambda: ep.ep_dequantize_fp8(rx2, rs2, n_recv, H, S, back)))
+    hs = min(n_recv, 512)
+    want = (rx2[:hs].cpu().view(torch.float8_e4m3fn).float() *
+            rs2[:hs].cpu().repeat_interleave(H // S, dim=1)).to(torch.bfloat16)
+    out["dequantize_fp8"]["check"] = bool(torch.equal(back[:hs].cpu().view(torch.int16), want.view(torch.int16)))
+    out["dequantize_fp8"]["traffic"] = measured_traffic("dequantize_e4m3_kernel", wl.name)
+    del rx2, rs2, slot2, back
     del rx, rs, x8, sc, q8, qs
 
     # grouping of the receive rows by local expert (bf16 rows of the dispatch just measured)
