@@ -448,7 +448,8 @@ ep_status_t ep_dispatch_to_fp8(const ep_shape_t *s, const void *x, int32_t num_s
                               const void *workspace, size_t workspace_bytes, int32_t recv_capacity, void *recv_x,
                               float *recv_x_scales, float *recv_topk_weights, int64_t *recv_topk_idx,
                               int32_t *recv_src_info, int32_t *send_slot, int32_t *dev_status, hipStream_t stream) {
-    if (s == nullptr) return EP_ERR_INVALID_ARG;
+    const ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
     if (s->hidden % kQuantChannels != 0 || num_scales < 1 || s->hidden % num_scales != 0) return EP_ERR_INVALID_ARG;
     const int l = quant_lanes_log2(s->hidden, num_scales);
     if (l < 0) return EP_ERR_UNSUPPORTED;

@@ -179,6 +179,10 @@ def test_quantize_argument_checks(ep):
     assert d(s, 56, rs=None) == ep.EP_ERR_INVALID_ARG          # scales out missing
     assert d(s, 56, x=ctypes.c_void_p(264)) == ep.EP_ERR_INVALID_ARG  # x not 16-byte aligned
     assert d(s, 56, x=None) == ep.EP_ERR_INVALID_ARG
+    assert d(_shape(ep, hidden=0), 1) == ep.EP_ERR_INVALID_ARG  # the shape is checked first
+    assert lib.ep_dispatch_to_fp8(None, p, 56, p, p, p, p, p, None, 0, 10, p, p, p, p, p, p, None, None) == \
+        ep.EP_ERR_INVALID_ARG
+    assert d(_shape(ep, num_tokens=0), 56) == ep.EP_OK            # no tokens: nothing to do, nothing enqueued
     q = ctypes.c_void_p(264)  # 8-byte aligned only
     assert lib.ep_quantize_fp8(q, 4, 7168, 56, p, p, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_quantize_fp8(p, 4, 7168, 56, q, p, None) == ep.EP_ERR_INVALID_ARG
