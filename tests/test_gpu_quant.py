@@ -276,3 +276,32 @@ def test_dispatch_to_fp8_shapes(case):
     _assert_same(gpu, ref)
     if dcap < 0:
         assert gpu["status"] & ep.EP_DEV_RECV_OVERFLOW
+
+
+def test_quantize_and_dequantize_past_the_grid_cap():
+    """More units than the launch's 65,536 blocks cover at once (16,400 rows of 16,384 channels: 16.8M
+    lanes' worth against 16.78M), so waves loop; rows are independent, so the oracle checks a sample of
+    them (first, last and random rows, and every row the second pass of the loop reaches)."""
+    print("[quant] 16400 x 16384 / 128 scales (grid-stride loop)", flush=True)
+    rows, H, S = 16400, 16384, 128
+    per_pass = 65536 * 4 * 64 * 16 // H  # rows the first pass of the loop covers
+    assert rows > per_pass
+    rng = np.random.default_rng(31)
+    x = (rng.standard_normal((rows, H), dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    dx = to_dev_bf16(x)
+    q = torch.empty((rows, H), dtype=torch.uint8, device="cuda")
+    s = torch.empty((rows, S), dtype=torch.float32, device="cuda")
+    ep.ep_quantize_fp8(dx, rows, H, S, q, s)
+    back = torch.empty((rows, H), dtype=torch.bfloat16, device="cuda")
+    ep.ep_dequantize_fp8(q, s, rows, H, S, back)
+    torch.cuda.synchronize()
+    del dx
+    sample = np.unique(np.concatenate([np.arange(8), np.arange(per_pass - 4, rows),
+                                       rng.choice(rows, 64, replace=False)]))
+    ts = torch.from_numpy(sample).cuda()
+    gq, gs, gb = q[ts].cpu().numpy(), s[ts].cpu().numpy(), bf16_host(back[ts])
+    o = oracle.Oracle()
+    rq, rs = o.quantize_e4m3(x[sample], S)
+    _same_scales("scales", gs, rs)
+    _same_codes("codes", gq, rq)
+    assert np.array_equal(gb, o.dequantize_e4m3(rq, rs))
