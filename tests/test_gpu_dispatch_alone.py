@@ -33,9 +33,10 @@ def _dev(a):
 
 
 def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=None, my_rank=0, fp8=None,
-                    form=ep.EP_FORM_AUTO):
-    """ep_dispatch (bf16 x) or ep_dispatch_fp8 (fp8=(rows, scales)) from uploaded routing
-    inputs into poisoned buffers; returns the outputs as numpy arrays and the status."""
+                    form=ep.EP_FORM_AUTO, quant=0):
+    """ep_dispatch (bf16 x), ep_dispatch_fp8 (fp8=(rows, scales)) or, with quant=S, ep_dispatch_to_fp8
+    (bf16 x quantised to E4M3 with S scales) from uploaded routing inputs into poisoned buffers;
+    returns the outputs as numpy arrays and the status."""
     T, K = idx.shape
     Hd = x.shape[1] if fp8 is None else fp8[0].shape[1]
     shape = ep.make_shape(T, x.shape[1], K, E, R, C, my_rank)
@@ -48,7 +49,12 @@ def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=N
     d_in, d_gbl, d_recv = _dev(in_rank), _dev(gbl.astype(np.int32)), _dev(recv_gbl.astype(np.int32))
     didx, dw = _dev(idx.astype(np.int64)), _dev(w.astype(np.float32))
     out = {}
-    if fp8 is None:
+    if quant:
+        rx = torch.full((c1, Hd), 0xAB, dtype=torch.uint8, device="cuda")
+        rs = torch.full((c1, quant), -2.0, dtype=torch.float32, device="cuda")
+        ep.ep_dispatch_to_fp8(shape, H.to_dev_bf16(x), quant, didx, dw, d_in, d_gbl, d_recv, workspace, cap, rx, rs,
+                              rw, ri, si, ss, st)
+    elif fp8 is None:
         rx = torch.full((c1, Hd), -1, dtype=torch.int16, device="cuda")
         ep.ep_dispatch(shape, H.to_dev_bf16(x), didx, dw, d_in, d_gbl, d_recv, workspace, cap, rx, rw, ri, si, ss,
                        st, form=form)
@@ -62,11 +68,11 @@ def _dispatch_alone(x, idx, w, E, R, C, in_rank, gbl, recv_gbl, cap, workspace=N
     torch.cuda.synchronize()
     rows = min(int(recv_gbl[-1]) if len(recv_gbl) else 0, cap)
     out["send_slot"] = ss.cpu().numpy()
-    out["recv_x"] = rx[:rows].cpu().numpy().view(np.uint16 if fp8 is None else np.uint8)
+    out["recv_x"] = rx[:rows].cpu().numpy().view(np.uint16 if fp8 is None and not quant else np.uint8)
     out["recv_topk_weights"] = rw[:rows].cpu().numpy()
     out["recv_topk_idx"] = ri[:rows].cpu().numpy()
     out["recv_src_info"] = si[:rows].cpu().numpy()
-    if fp8 is not None and fp8[1].shape[1]:
+    if quant or (fp8 is not None and fp8[1].shape[1]):
         out["recv_x_scales"] = rs[:rows].cpu().numpy()
     out["status"] = int(st.item())
     return out
@@ -250,3 +256,80 @@ def test_dispatch_forms_give_the_same_outputs(orc, form, use_ws, fp8):
     ref = _reference(orc, x, idx, w, wl.experts, *args, fp8=f8)
     assert _differences(gpu, ref) == []
     assert gpu["status"] == 0
+
+
+def _quant_reference(orc, x, idx, w, E, in_rank, gbl, recv_gbl, cap, S):
+    """the oracle's quantiser, then its fp8 dispatch: what ep_dispatch_to_fp8 is defined as"""
+    return _reference(orc, x, idx, w, E, in_rank, gbl, recv_gbl, cap, fp8=orc.quantize_e4m3(x, S))
+
+
+@pytest.mark.parametrize("name", ["prefill", "ragged"])
+def test_dispatch_to_fp8_alone(orc, name):
+    """ep_dispatch_to_fp8 on the oracle's layout and notify outputs, no workspace: bit for bit against the
+    oracle's quantiser then fp8 dispatch (prefill; and 2111 tokens of 896 channels, 24 ranks, 7 channels)."""
+    print(f"[dispatch alone] dispatch_to_fp8 {name}", flush=True)
+    if name == "prefill":
+        d = generate("prefill")
+        wl = d["workload"]
+        x, idx, w, E, R, C, S = d["x"], d["topk_idx"], d["topk_weights"], wl.experts, wl.ranks, wl.channels, 56
+    else:
+        rng = np.random.default_rng(2111)
+        T, Hd, R, E, K, C, S = 2111, 896, 24, 96, 5, 7, 14
+        idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+        idx[rng.random((T, K)) < 0.15] = -1
+        w = rng.random((T, K)).astype(np.float32)
+        x = H.random_rows(rng, T, Hd)
+    lay, note = _routing(orc, idx, E, R, C)
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"],
+            note["num_recv_tokens"])
+    gpu = _dispatch_alone(x, idx, w, E, R, C, *args, quant=S)
+    ref = _quant_reference(orc, x, idx, w, E, *args, S)
+    assert _differences(gpu, ref) == [] and gpu["status"] == ref["status"] == 0
+
+
+def test_dispatch_to_fp8_flags_a_stale_workspace(orc):
+    print("[dispatch alone] dispatch_to_fp8 stale workspace", flush=True)
+    T, Hd, R, E, K, C, S = 2200, 7168, 32, 128, 6, 12, 56
+    rng = np.random.default_rng(22)
+    idx_a = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    idx_b = idx_a.copy()
+    t = T // 3  # routed to one rank it did not reach before, so its is_token_in_rank row differs
+    r = next(r for r in range(R) if r not in set((idx_a[t] // (E // R)).tolist()))
+    idx_b[t] = -1
+    idx_b[t, 0] = r * (E // R)
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, Hd)
+    ws = _notified_workspace(idx_a, E, R, C, Hd)
+    lay, note = _routing(orc, idx_b, E, R, C)
+    args = (lay["is_token_in_rank"], note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"],
+            note["num_recv_tokens"] + 64)
+    assert _dispatch_alone(x, idx_b, w, E, R, C, *args, workspace=ws, quant=S)["status"] & ep.EP_DEV_STALE_WORKSPACE
+    lay_a, note_a = _routing(orc, idx_a, E, R, C)
+    args_a = (lay_a["is_token_in_rank"], note_a["gbl_channel_prefix_matrix"], note_a["recv_gbl_rank_prefix_sum"],
+              note_a["num_recv_tokens"])
+    gpu_a = _dispatch_alone(x, idx_a, w, E, R, C, *args_a, workspace=ws, quant=S)
+    assert _differences(gpu_a, _quant_reference(orc, x, idx_a, w, E, *args_a, S)) == [] and gpu_a["status"] == 0
+
+
+@pytest.mark.parametrize("use_ws", [False, True])
+@pytest.mark.parametrize("what", ["gbl_entry", "recv_prefix", "last_channel"])
+def test_dispatch_to_fp8_flags_inconsistent_prefixes(orc, use_ws, what):
+    print(f"[dispatch alone] dispatch_to_fp8 inconsistent {what} ws={use_ws}", flush=True)
+    T, Hd, R, E, K, C, S = 2300, 7168, 16, 64, 4, 10, 56
+    rng = np.random.default_rng(T + len(what))
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    w = rng.random((T, K)).astype(np.float32)
+    x = H.random_rows(rng, T, Hd)
+    lay, note = _routing(orc, idx, E, R, C)
+    gbl = note["gbl_channel_prefix_matrix"].copy()
+    recv = note["recv_gbl_rank_prefix_sum"].copy()
+    if what == "gbl_entry":
+        gbl[3, 4] += 1
+    elif what == "recv_prefix":
+        recv[5:] += 2
+    else:
+        gbl[7, C - 1] -= 1
+    cap = note["num_recv_tokens"] + 64
+    ws = _notified_workspace(idx, E, R, C, Hd) if use_ws else None
+    gpu = _dispatch_alone(x, idx, w, E, R, C, lay["is_token_in_rank"], gbl, recv, cap, workspace=ws, quant=S)
+    assert gpu["status"] & ep.EP_DEV_COUNT_MISMATCH
