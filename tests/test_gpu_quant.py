@@ -305,3 +305,47 @@ def test_quantize_and_dequantize_past_the_grid_cap():
     _same_scales("scales", gs, rs)
     _same_codes("codes", gq, rq)
     assert np.array_equal(gb, o.dequantize_e4m3(rq, rs))
+
+
+QUANT_RANDOM_CASES = 10
+
+
+def draw_quant(case: int) -> dict:
+    """A seeded random configuration of the quantising dispatch: token counts around the chunk and
+    128-token group boundaries and across the 4096-token tiling switch, 1 to 64 ranks, groups of 16
+    to 1024 channels (every fourth case 7168 channels in 56 groups, the whole-row tilings), masked and
+    duplicate ids, a capacity a few rows short, with or without the workspace."""
+    rng = np.random.default_rng(7000 + case)
+    R = int(rng.choice([1, 2, 4, 8, 16, 24, 32, 64]))
+    E = R * int(rng.choice([1, 2, 4, 8, 16]))
+    K = int(rng.integers(1, min(8, E) + 1))
+    T = int(rng.choice([1, 63, 65, 333, 1000, 2049, 4096, 4100, 5000]))
+    C = int(rng.integers(1, 50))
+    if case % 4 == 0:
+        g, S = 128, 56
+    else:
+        g = int(rng.choice([16, 32, 64, 128, 256, 512, 1024]))
+        S = int(rng.integers(1, max(1, min(64, 8192 // g)) + 1))
+    return dict(T=T, R=R, E=E, K=K, C=C, H=g * S, S=S, mask=float(rng.choice([0.0, 0.1, 0.4])),
+                dup=bool(case % 3 == 1), short=bool(case % 4 == 2),
+                ws=bool(case % 2 == 0) or -(-T // C) > 4096)
+
+
+@pytest.mark.parametrize("case", range(QUANT_RANDOM_CASES))
+def test_dispatch_to_fp8_random_shapes(case):
+    c = draw_quant(case)
+    print(f"[quant] dispatch_to_fp8 random case {case}: {c}", flush=True)
+    rng = np.random.default_rng(8000 + case)
+    T, R, E, K = c["T"], c["R"], c["E"], c["K"]
+    idx = np.stack([rng.choice(E, K, replace=c["dup"]) for _ in range(T)]).astype(np.int64)
+    if c["mask"]:
+        flat = rng.choice(T * K, int(c["mask"] * T * K), replace=False)
+        idx.reshape(-1)[flat] = -1
+    w = rng.random((T, K)).astype(np.float32)
+    x = pins.quantize_groups(rng, T, c["H"], c["S"])
+    cap = None
+    if c["short"]:
+        n = int(oracle.Oracle().layout(idx, E, R)["num_tokens_per_rank"].sum())
+        cap = max(0, n - 5)
+    gpu, ref = _dispatch_to_fp8_case(x, idx, w, E, R, c["C"], c["S"], capacity=cap, use_workspace=c["ws"])
+    _assert_same(gpu, ref)
