@@ -63,6 +63,12 @@ def dispatch_to_fp8_bytes(T, H, K, R, N, S) -> int:
     return T * 2 * H + T * K * 12 + N * (H + 4 * S + 4 * K + 8 * K + 8) + 4 * T * R
 
 
+def dispatch_cached_to_fp8_bytes(T, H, R, N, S) -> int:
+    """the cached quantising dispatch: bf16 x and the [t][R] send_slot map read once, every receive row
+    written as E4M3 codes with its S fp32 scales."""
+    return T * 2 * H + 4 * T * R + N * (H + 4 * S)
+
+
 def dequantize_bytes(N, H, S) -> int:
     """E4M3 rows and their S fp32 scales read once, bf16 rows written."""
     return N * (H + 4 * S) + N * 2 * H
@@ -108,6 +114,7 @@ KERNEL_SOURCES = {"dispatch_pull_kernel": ["ep_dispatch.hip", "ep_internal.h"],
                   "quantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
                   "dispatch_kernel_to_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "dequantize_e4m3_kernel": ["ep_quant.hip", "ep_internal.h"],
+                  "dispatch_kernel_cached_to_fp8": ["ep_dispatch.hip", "ep_internal.h"],
                   "combine_kernel": ["ep_combine.hip", "ep_internal.h"],
                   "combine_staged_kernel": ["ep_combine.hip", "ep_internal.h"]}
 
@@ -422,6 +429,13 @@ def time_variants(ep, inputs, d, shape, b, x, idx, w, n_recv, steps: int, timer)
                                       b.recv_w, b.recv_idx, b.src_info, slot2, b.dev_status)))
     out["dispatch_to_fp8"]["check"] = bool(torch.equal(slot2, slot8) and torch.equal(rx2, rx) and torch.equal(rs2, rs))
     out["dispatch_to_fp8"]["traffic"] = measured_traffic("dispatch_kernel_to_fp8", wl.name)
+    # the same in cached mode, from the send_slot just written: the same codes and scales
+    cq, cqs = torch.empty_like(rx2), torch.empty_like(rs2)
+    out["dispatch_cached_to_fp8"] = rate(dispatch_cached_to_fp8_bytes(T, H, R, n_recv, S), mean_us(
+        lambda: ep.ep_dispatch_cached_to_fp8(shape, x, S, slot2, n_recv, cq, cqs, b.dev_status)))
+    out["dispatch_cached_to_fp8"]["check"] = bool(torch.equal(cq, rx2) and torch.equal(cqs, rs2))
+    out["dispatch_cached_to_fp8"]["traffic"] = measured_traffic("dispatch_kernel_cached_to_fp8", wl.name)
+    del cq, cqs
     # the receive side's dequantiser on those rows (E4M3 codes and scales -> bf16); checked on the host on
     # a sample of rows: torch's float8 decoding times the scale in fp32, rounded to bf16 by torch
     back = torch.empty((n_recv, H), dtype=torch.bfloat16, device=x.device)

@@ -459,6 +459,35 @@ ep_status_t ep_dispatch_to_fp8(const ep_shape_t *s, const void *x, int32_t num_s
                             send_slot, EP_FORM_PUSH, dev_status, stream, l);
 }
 
+ep_status_t ep_dispatch_cached_to_fp8(const ep_shape_t *s, const void *x, int32_t num_scales, const int32_t *send_slot,
+                                     int32_t recv_capacity, void *recv_x, float *recv_x_scales, int32_t *dev_status,
+                                     hipStream_t stream) {
+    ep_status_t st = check_shape(s);
+    if (st != EP_OK) return st;
+    if (s->hidden % kQuantChannels != 0 || num_scales < 1 || s->hidden % num_scales != 0 || recv_capacity < 0)
+        return EP_ERR_INVALID_ARG;
+    const int l = quant_lanes_log2(s->hidden, num_scales);
+    if (l < 0 || num_scales > kMaxScales) return EP_ERR_UNSUPPORTED;
+    if (s->num_tokens == 0) return EP_OK;
+    if (x == nullptr || send_slot == nullptr) return EP_ERR_INVALID_ARG;
+    if (recv_capacity > 0 && (recv_x == nullptr || recv_x_scales == nullptr)) return EP_ERR_INVALID_ARG;
+    if (!aligned16(x) || (recv_x != nullptr && !aligned16(recv_x))) return EP_ERR_INVALID_ARG;
+    DispatchArgs a = {};
+    a.x = x;
+    a.row_units = s->hidden / 16;  // units of the fp8 row
+    a.x_scales = nullptr;
+    a.num_scales = num_scales;
+    a.cached_slot = send_slot;
+    a.cap = recv_capacity;
+    a.recv_x = recv_x;
+    a.recv_scales = recv_x_scales;
+    a.form = EP_FORM_PUSH;
+    a.dev_status = dev_status;
+    a.quantize = true;
+    a.quant_log2 = l;
+    return from_hip(launch_dispatch(*s, a, stream));
+}
+
 ep_status_t ep_quantize_fp8(const void *x, int64_t num_rows, int32_t hidden, int32_t num_scales, void *x_fp8,
                             float *x_scales, hipStream_t stream) {
     const ep_status_t st = quant_checked(x, x_fp8, x_scales, num_rows, hidden, num_scales);

@@ -1272,10 +1272,14 @@ hipError_t run(DispatchParams p, hipStream_t stream) {
     p.S = (int)((p.row_units + VPL * kWave - 1) / (VPL * kWave));
     const int64_t waves = p.T * p.S;
     const int64_t blocks = (waves + WPB - 1) / WPB;
-    if constexpr (QUANT)
-        hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, false, true>), dim3((unsigned)blocks),
-                           dim3(WPB * kWave), 0, stream, p);
-    else if (p.cached_slot != nullptr)
+    if constexpr (QUANT) {
+        if (p.cached_slot != nullptr)
+            hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, true, true>), dim3((unsigned)blocks),
+                               dim3(WPB * kWave), 0, stream, p);
+        else
+            hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, false, true>), dim3((unsigned)blocks),
+                               dim3(WPB * kWave), 0, stream, p);
+    } else if (p.cached_slot != nullptr)
         hipLaunchKernelGGL((dispatch_kernel<VPL, EXACT, WPB, GRAN, true>), dim3((unsigned)blocks), dim3(WPB * kWave),
                            0, stream, p);
     else
@@ -1381,14 +1385,17 @@ void dispatch_tiling(int64_t row_units, int64_t num_tokens, int *vpl, int *wpb, 
     }
 }
 
-// The quantising dispatch (push form).  For 7168 channels from 4096 tokens whole rows
+// The quantising dispatch (push form; also its cached mode).  For 7168 channels from 4096 tokens whole rows
 // per wave, 4 free-running waves per block: 56.8 us at prefill, against 59.3-60.6 with
 // the rank sweep of the fp8 rows (16 waves, a barrier every 4 ranks), 57.0-57.5 with 8
 // or 16 free-running waves, 58.0-61.8 with the row split over 2, 4 or 7 waves (one run).
+// Its cached mode, which has no routing to do before its stores, takes the rank sweep:
+// 52.5-53.4 us against 56.7-58.4 free-running (53.8-54.5 with a barrier every rank).
 // Below 4096 tokens 4096-channel segments; other widths 1024-channel segments, 8 waves.
 hipError_t run_quant_tiled(const DispatchParams &p, hipStream_t stream) {
-    if (p.row_units == 7 * kWave)
-        return p.T >= 4096 ? run<7, true, 4, 0, true>(p, stream) : run<4, false, 4, 0, true>(p, stream);
+    if (p.row_units == 7 * kWave && p.T >= 4096)
+        return p.cached_slot != nullptr ? run<7, true, 16, 4, true>(p, stream) : run<7, true, 4, 0, true>(p, stream);
+    if (p.row_units == 7 * kWave) return run<4, false, 4, 0, true>(p, stream);
     return p.row_units % kWave == 0 ? run<1, true, 8, 0, true>(p, stream) : run<1, false, 8, 0, true>(p, stream);
 }
 

@@ -23,7 +23,8 @@ EP_DEV_STALE_WORKSPACE = 16
 EP_FORM_AUTO, EP_FORM_PUSH, EP_FORM_PULL = 0, 1, 2
 
 EXPORTED = ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8",
-            "ep_dispatch_to_fp8", "ep_quantize_fp8", "ep_dequantize_fp8", "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
+            "ep_dispatch_to_fp8", "ep_quantize_fp8", "ep_dequantize_fp8", "ep_dispatch_cached",
+            "ep_dispatch_cached_to_fp8", "ep_group_by_expert", "ep_dispatch_grouped",
             "ep_combine", "ep_workspace_bytes", "ep_status_string")
 
 
@@ -69,11 +70,12 @@ def load(path: str = LIBRARY) -> ctypes.CDLL:
     lib.ep_combine.argtypes = [_S, _P, _P, _P, ctypes.c_int32, _P, _P, _P, _P]
     lib.ep_dispatch_to_fp8.argtypes = [_S, _P, ctypes.c_int32, _P, _P, _P, _P, _P, _P, ctypes.c_size_t,
                                        ctypes.c_int32] + [_P] * 8
+    lib.ep_dispatch_cached_to_fp8.argtypes = [_S, _P, ctypes.c_int32, _P, ctypes.c_int32, _P, _P, _P, _P]
     lib.ep_quantize_fp8.argtypes = [_P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P, _P]
     lib.ep_dequantize_fp8.argtypes = [_P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, _P, _P]
     for name in ("ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify", "ep_dispatch", "ep_dispatch_fp8", "ep_dispatch_cached",
                  "ep_group_by_expert", "ep_dispatch_grouped", "ep_combine", "ep_quantize_fp8", "ep_dequantize_fp8",
-                 "ep_dispatch_to_fp8"):
+                 "ep_dispatch_to_fp8", "ep_dispatch_cached_to_fp8"):
         getattr(lib, name).restype = ctypes.c_int
     lib.ep_workspace_bytes.argtypes = [_S]
     lib.ep_workspace_bytes.restype = ctypes.c_size_t
@@ -258,6 +260,13 @@ def ep_dispatch_to_fp8(shape, x, num_scales, topk_idx, topk_weights, is_token_in
                                      _ptr(recv_x_scales), _ptr(recv_topk_weights), _ptr(recv_topk_idx),
                                      _ptr(recv_src_info), _ptr(send_slot), _ptr(dev_status), _stream(stream)),
            "ep_dispatch_to_fp8")
+
+
+def ep_dispatch_cached_to_fp8(shape, x, num_scales, send_slot, recv_capacity, recv_x, recv_x_scales, dev_status=None,
+                              stream=None) -> None:
+    _check(load().ep_dispatch_cached_to_fp8(ctypes.byref(shape), _ptr(x), int(num_scales), _ptr(send_slot),
+                                            int(recv_capacity), _ptr(recv_x), _ptr(recv_x_scales), _ptr(dev_status),
+                                            _stream(stream)), "ep_dispatch_cached_to_fp8")
 
 
 def ep_quantize_fp8(x, num_rows, hidden, num_scales, x_fp8, x_scales, stream=None) -> None:

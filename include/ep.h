@@ -14,6 +14,7 @@
  *   ep_dispatch_fp8     dispatch of 1-byte (fp8) rows with their per-token scales
  *   ep_quantize_fp8     bf16 rows -> E4M3 rows and scales for it; ep_dequantize_fp8 back
  *   ep_dispatch_to_fp8  bf16 rows in, fp8 rows and scales out: the two above in one launch
+ *   ep_dispatch_cached_to_fp8  the same for cached mode
  *   ep_dispatch_cached  new rows to the rows an earlier dispatch assigned (cached mode)
  *   ep_group_by_expert  receive rows regrouped into per-expert segments for grouped GEMMs
  *   ep_dispatch_grouped dispatch straight into those segments, with no receive rows
@@ -326,6 +327,22 @@ ep_status_t ep_dequantize_fp8(const void *x_fp8, const float *x_scales, int64_t 
 ep_status_t ep_dispatch_cached(const ep_shape_t *s, const void *x, int32_t elem_bytes, const float *x_scales,
                                int32_t num_scales, const int32_t *send_slot, int32_t recv_capacity, void *recv_x,
                                float *recv_x_scales, int32_t form, int32_t *dev_status, hipStream_t stream);
+
+/*
+ * Cached-mode dispatch of bf16 rows that arrive as fp8 rows with scales: ep_quantize_fp8 of x
+ * followed by ep_dispatch_cached of its codes and scales (elem_bytes 1), in one launch and bit for
+ * bit the same outputs.  [mscclpp ht_runtime.cc, cached mode of intranodeDispatch /
+ * internodeDispatch with xScales; the quantiser as for ep_quantize_fp8]
+ * Each token's row is read once and quantised once; its codes and scales go to every row
+ * send_slot[t][r] >= 0 names (send_slot as an earlier dispatch of the same routing wrote it).
+ * In:  x [t][h] bf16 (finite); num_scales as for ep_quantize_fp8; send_slot [t][R].
+ * Out: recv_x [cap][h] uint8 E4M3 codes; recv_x_scales [cap][num_scales] f32.  No metadata.
+ * Entries outside [-1, recv_capacity) are skipped and flagged (EP_DEV_BAD_SEND_SLOT).  Push form.
+ * Limits as for ep_dispatch_to_fp8.
+ */
+ep_status_t ep_dispatch_cached_to_fp8(const ep_shape_t *s, const void *x, int32_t num_scales, const int32_t *send_slot,
+                                     int32_t recv_capacity, void *recv_x, float *recv_x_scales, int32_t *dev_status,
+                                     hipStream_t stream);
 
 /*
  * Grouping of the received rows by local expert, the layout grouped expert GEMMs read.

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted(["ep_get_layout", "ep_get_layout_noalloc", "ep_notify", "ep_layout_notify",
                                           "ep_dispatch",
                                           "ep_dispatch_fp8", "ep_quantize_fp8", "ep_dequantize_fp8",
-                                          "ep_dispatch_to_fp8",
+                                          "ep_dispatch_to_fp8", "ep_dispatch_cached_to_fp8",
                                           "ep_dispatch_cached", "ep_group_by_expert", "ep_dispatch_grouped",
                                           "ep_combine", "ep_workspace_bytes", "ep_status_string"])
 
@@ -183,6 +183,17 @@ def test_quantize_argument_checks(ep):
     assert lib.ep_dispatch_to_fp8(None, p, 56, p, p, p, p, p, None, 0, 10, p, p, p, p, p, p, None, None) == \
         ep.EP_ERR_INVALID_ARG
     assert d(_shape(ep, num_tokens=0), 56) == ep.EP_OK            # no tokens: nothing to do, nothing enqueued
+    cq = lambda sh, S, **kw: lib.ep_dispatch_cached_to_fp8(ctypes.byref(sh), kw.get("x", p), S,  # noqa: E731
+                                                           kw.get("slot", p), kw.get("cap", 10), kw.get("rx", p),
+                                                           kw.get("rs", p), None, None)
+    assert cq(s, 3) == ep.EP_ERR_INVALID_ARG
+    assert cq(s, 64) == ep.EP_ERR_UNSUPPORTED
+    assert cq(_shape(ep, hidden=7160), 1) == ep.EP_ERR_INVALID_ARG
+    assert cq(s, 56, cap=-1) == ep.EP_ERR_INVALID_ARG
+    assert cq(s, 56, slot=None) == ep.EP_ERR_INVALID_ARG
+    assert cq(s, 56, rs=None) == ep.EP_ERR_INVALID_ARG
+    assert cq(s, 56, rx=ctypes.c_void_p(264)) == ep.EP_ERR_INVALID_ARG
+    assert cq(_shape(ep, num_tokens=0), 56) == ep.EP_OK
     q = ctypes.c_void_p(264)  # 8-byte aligned only
     assert lib.ep_quantize_fp8(q, 4, 7168, 56, p, p, None) == ep.EP_ERR_INVALID_ARG
     assert lib.ep_quantize_fp8(p, 4, 7168, 56, q, p, None) == ep.EP_ERR_INVALID_ARG

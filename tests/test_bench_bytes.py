@@ -51,6 +51,7 @@ def test_bytes_are_the_buffers_moved():
     assert bench.dispatch_cached_bytes(T, R, N, 2 * H, 0) == x + slot + recv_x
     assert bench.quantize_bytes(T, H, S) == x + x8 + sc
     assert bench.dequantize_bytes(N, H, S) == r8 + rsc + recv_x
+    assert bench.dispatch_cached_to_fp8_bytes(T, H, R, N, S) == x + slot + r8 + rsc
     assert bench.dispatch_to_fp8_bytes(T, H, K, R, N, S) == x + idx + w + r8 + rsc + recv_w + recv_idx + src + slot
     g_x, g_row, g_w, pos = nb((M, H), np.int16), nb((M,), np.int32), nb((M,), np.float32), nb((N, K), np.int32)
     assert bench.group_bytes(H, K, N, M) == recv_x + recv_idx + recv_w + g_x + g_row + g_w + pos

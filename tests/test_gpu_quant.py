@@ -349,3 +349,80 @@ def test_dispatch_to_fp8_random_shapes(case):
         cap = max(0, n - 5)
     gpu, ref = _dispatch_to_fp8_case(x, idx, w, E, R, c["C"], c["S"], capacity=cap, use_workspace=c["ws"])
     _assert_same(gpu, ref)
+
+
+@pytest.mark.parametrize("name", ["sweep", "prefill", "large"])
+def test_dispatch_cached_to_fp8_replays_the_layout(name):
+    """ep_dispatch_cached_to_fp8 with the send_slot ep_dispatch_to_fp8 wrote: the same codes and scales at
+    the same rows, and the oracle's quantiser then cached dispatch bit for bit."""
+    print(f"[quant] dispatch_cached_to_fp8 workload={name}", flush=True)
+    d = generate(name)
+    wl = d["workload"]
+    x, idx, w = d["x"], d["topk_idx"], d["topk_weights"]
+    T, H = x.shape
+    K, S = idx.shape[1], H // 128
+    shape = ep.make_shape(T, H, K, wl.experts, wl.ranks, wl.channels)
+    b = ep.allocate(shape, 0)
+    didx = torch.from_numpy(np.ascontiguousarray(idx)).cuda()
+    dw = torch.from_numpy(np.ascontiguousarray(w)).cuda()
+    ep.run_layout(b, didx)
+    n = ep.run_notify(b, read_back=True)
+    dx = to_dev_bf16(x)
+    rx = torch.empty((n, H), dtype=torch.uint8, device="cuda")
+    rs = torch.empty((n, S), dtype=torch.float32, device="cuda")
+    rw = torch.empty((n, K), dtype=torch.float32, device="cuda")
+    si = torch.empty((n, 2), dtype=torch.int32, device="cuda")
+    ss = torch.empty((T, wl.ranks), dtype=torch.int32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_to_fp8(shape, dx, S, didx, dw, b.in_rank, b.gbl, b.recv_gbl, b.workspace, n, rx, rs, rw, None, si,
+                          ss, st)
+    cx = torch.full((n, H), 0x5A, dtype=torch.uint8, device="cuda")
+    cs = torch.full((n, S), -4.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch_cached_to_fp8(shape, dx, S, ss, n, cx, cs, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    assert torch.equal(cx, rx) and torch.equal(cs, rs)
+    o = oracle.Oracle()
+    q, s = o.quantize_e4m3(x, S)
+    ref = o.dispatch_cached(q, ss.cpu().numpy(), n, s)
+    _same_codes("recv_x", cx.cpu().numpy(), ref["recv_x"])
+    _same_scales("recv_x_scales", cs.cpu().numpy(), ref["recv_x_scales"])
+
+
+# (tokens, ranks, hidden, num_scales, capacity): whole 7168-channel rows from 4096 tokens, 4096-channel
+# segments below, and 896-channel rows (1024-channel segments, ragged)
+CACHED_QUANT = {"t4100_r16_h7168": (4100, 16, 7168, 56, 30000), "t2304_r64_h7168_g16": (2304, 64, 7168, 448, 12000),
+                "t777_r24_h896_g64": (777, 24, 896, 14, 9000)}
+
+
+@pytest.mark.parametrize("case", sorted(CACHED_QUANT))
+def test_dispatch_cached_to_fp8_any_map_and_bad_slots(case):
+    """A random injective map over part of the capacity with entries past it and below -1: named rows get
+    the oracle's codes and scales, bad entries are skipped and flagged, other rows keep their contents."""
+    T, R, H, S, cap = CACHED_QUANT[case]
+    print(f"[quant] dispatch_cached_to_fp8 map={case}", flush=True)
+    rng = np.random.default_rng(zlib.crc32(case.encode()))
+    x = pins.quantize_groups(rng, T, H, S)
+    slot = np.full((T, R), -1, np.int32)
+    picks = rng.choice(T * R, cap - 41, replace=False)
+    slot.reshape(-1)[picks] = rng.permutation(cap)[: cap - 41]
+    slot[3, R - 1] = cap + 5
+    slot[T - 1, 0] = -2
+    slot[T // 2, 1 % R] = cap
+    shape = ep.make_shape(T, H, 2, 2 * R, R, 4)
+    out = torch.full((cap, H), 0x77, dtype=torch.uint8, device="cuda")
+    outs = torch.full((cap, S), -5.0, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_cached_to_fp8(shape, to_dev_bf16(x), S, torch.from_numpy(slot).cuda(), cap, out, outs, st)
+    torch.cuda.synchronize()
+    o = oracle.Oracle()
+    q, s = o.quantize_e4m3(x, S)
+    ref = o.dispatch_cached(q, slot, cap, s)
+    named = np.zeros(cap, bool)
+    ok = (slot >= 0) & (slot < cap)
+    named[slot[ok]] = True
+    got, gots = out.cpu().numpy(), outs.cpu().numpy()
+    _same_codes("recv_x", got[named], ref["recv_x"][named])
+    _same_scales("recv_x_scales", gots[named], ref["recv_x_scales"][named])
+    assert (got[~named] == 0x77).all() and (gots[~named] == -5.0).all()
+    assert int(st.item()) == ep.EP_DEV_BAD_SEND_SLOT and ref["status"] == ep.EP_DEV_BAD_SEND_SLOT
