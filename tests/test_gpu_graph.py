@@ -103,8 +103,9 @@ def test_step_in_a_graph_replays_exactly(name):
 
 
 def _fp8_calls(shape, b, x, idx, w, S, out):
-    """layout, notify, the quantiser, the fp8 dispatch of its output, the quantising dispatch and the
-    dequantiser of its rows, all on torch's current stream into the buffers of `out`"""
+    """layout, notify, the quantiser, the fp8 dispatch of its output, the quantising dispatch, the
+    dequantiser of its rows and the cached quantising dispatch from its send_slot, all on torch's current
+    stream into the buffers of `out`"""
     T, H = shape.num_tokens, shape.hidden
     cap = out["rx"].shape[0]
     ep.run_layout(b, idx)
@@ -115,6 +116,7 @@ def _fp8_calls(shape, b, x, idx, w, S, out):
     ep.ep_dispatch_to_fp8(shape, x, S, idx, w, b.in_rank, b.gbl, b.recv_gbl, b.workspace, cap, out["tx"], out["ts"],
                           b.recv_w, b.recv_idx, b.src_info, out["tslot"], b.dev_status)
     ep.ep_dequantize_fp8(out["tx"], out["ts"], cap, H, S, out["back"])
+    ep.ep_dispatch_cached_to_fp8(shape, x, S, out["tslot"], cap, out["cx"], out["cs"], b.dev_status)
 
 
 def _fp8_buffers(T, H, S, R, cap):
@@ -123,11 +125,13 @@ def _fp8_buffers(T, H, S, R, cap):
     return {"q": torch.zeros((T, H), **u8), "qs": torch.zeros((T, S), **f32), "rx": torch.zeros((cap, H), **u8),
             "rs": torch.zeros((cap, S), **f32), "slot": torch.zeros((T, R), **i32), "tx": torch.zeros((cap, H), **u8),
             "ts": torch.zeros((cap, S), **f32), "tslot": torch.zeros((T, R), **i32),
-            "back": torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda")}
+            "back": torch.zeros((cap, H), dtype=torch.bfloat16, device="cuda"), "cx": torch.zeros((cap, H), **u8),
+            "cs": torch.zeros((cap, S), **f32)}
 
 
 def test_fp8_path_in_a_graph_replays_exactly():
-    """The quantiser, the fp8 dispatch of its output, the quantising dispatch and the dequantiser, captured
+    """The quantiser, the fp8 dispatch of its output, the quantising dispatch, the dequantiser and the cached
+    quantising dispatch, captured
     after layout and notify in one graph and replayed on new inputs: every replay equals an eager run."""
     print("[graph] fp8 path, workload=sweep", flush=True)
     d = generate("sweep")
@@ -167,7 +171,7 @@ def test_fp8_path_in_a_graph_replays_exactly():
         torch.cuda.synchronize()
         n = int(rb.num_recv.item())
         bad = [k for k in ("q", "qs", "slot", "tslot") if not torch.equal(out[k], ref[k])]
-        bad += [k for k in ("rx", "rs", "tx", "ts") if not torch.equal(out[k][:n], ref[k][:n])]
+        bad += [k for k in ("rx", "rs", "tx", "ts", "cx", "cs") if not torch.equal(out[k][:n], ref[k][:n])]
         if not torch.equal(out["back"][:n].view(torch.int16), ref["back"][:n].view(torch.int16)):
             bad.append("back")
         assert not bad, f"replay {replay}: {bad}"
