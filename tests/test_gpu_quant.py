@@ -426,3 +426,25 @@ def test_dispatch_cached_to_fp8_any_map_and_bad_slots(case):
     _same_scales("recv_x_scales", gots[named], ref["recv_x_scales"][named])
     assert (got[~named] == 0x77).all() and (gots[~named] == -5.0).all()
     assert int(st.item()) == ep.EP_DEV_BAD_SEND_SLOT and ref["status"] == ep.EP_DEV_BAD_SEND_SLOT
+
+
+def test_quantising_dispatches_with_no_receive_capacity():
+    """Capacity 0: every routed (token, rank) is dropped and flagged, send_slot is -1 throughout, nothing
+    is stored (the oracle agrees); the cached form with a map of only -1 entries stores nothing either."""
+    print("[quant] dispatch_to_fp8 with capacity 0", flush=True)
+    rng = np.random.default_rng(90)
+    T, H, S, R, E, K, C = 300, 896, 14, 16, 64, 4, 5
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    w = rng.random((T, K)).astype(np.float32)
+    x = pins.quantize_groups(rng, T, H, S)
+    gpu, ref = _dispatch_to_fp8_case(x, idx, w, E, R, C, S, capacity=0)
+    _assert_same(gpu, ref)
+    assert gpu["status"] == ep.EP_DEV_RECV_OVERFLOW and (gpu["send_slot"] == -1).all()
+    shape = ep.make_shape(T, H, K, E, R, C)
+    out = torch.full((4, H), 0x77, dtype=torch.uint8, device="cuda")
+    outs = torch.full((4, S), -5.0, dtype=torch.float32, device="cuda")
+    st = torch.zeros(1, dtype=torch.int32, device="cuda")
+    none = torch.full((T, R), -1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_cached_to_fp8(shape, to_dev_bf16(x), S, none, 4, out, outs, st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0 and (out == 0x77).all() and (outs == -5.0).all()
