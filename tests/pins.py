@@ -430,6 +430,46 @@ def pin_dispatch_prefix_checks(o, inputs: dict) -> list[str]:
     return errs
 
 
+def pin_count_checks_and_overflow(o, inputs: dict) -> list[str]:
+    """Notify's counts must be the map's: with consistent inputs its status is 0, and a per-rank or per-node
+    count moved by one (first and last rank, first and last node) must raise the count-mismatch bit.  A
+    receive capacity below N drops exactly the rows the full dispatch put at or past it: the status is the
+    overflow bit alone (the prefixes still agree with the map), the kept rows and their metadata are the
+    full dispatch's, and send_slot keeps exactly the entries below the capacity."""
+    import oracle as _oracle
+
+    wl = inputs["workload"]
+    x = np.ascontiguousarray(inputs["x"][:, :16])
+    idx, w = inputs["topk_idx"], inputs["topk_weights"]
+    E, R, C = wl.experts, wl.ranks, wl.channels
+    nodes = max(1, R // 8)
+    lay = o.layout(idx, E, R)
+    args = (lay["is_token_in_rank"], lay["num_tokens_per_rank"], lay["num_tokens_per_rdma_rank"],
+            lay["num_tokens_per_expert"], C, 1)
+    note = o.notify(*args)
+    errs = [] if note["status"] == 0 else [f"consistent counts flagged: {note['status']}"]
+    for which, i in [("rank", 0), ("rank", R - 1), ("node", 0), ("node", nodes - 1)]:
+        per_rank, per_node = lay["num_tokens_per_rank"].copy(), lay["num_tokens_per_rdma_rank"].copy()
+        (per_rank if which == "rank" else per_node)[i] += 1
+        st = o.notify(lay["is_token_in_rank"], per_rank, per_node, lay["num_tokens_per_expert"], C, 1)["status"]
+        if not st & _oracle.COUNT_MISMATCH:
+            errs.append(f"notify: {which} count {i} + 1 not flagged")
+    gbl, recv = note["gbl_channel_prefix_matrix"], note["recv_gbl_rank_prefix_sum"]
+    full = o.dispatch(x, idx, w, lay["is_token_in_rank"], gbl, recv, E)
+    n = int(recv[-1])
+    cap = n - 10
+    d = o.dispatch(x, idx, w, lay["is_token_in_rank"], gbl, recv, E, recv_capacity=cap)
+    if d["status"] != _oracle.RECV_OVERFLOW:
+        errs.append(f"overflow status {d['status']}, want the overflow bit alone")
+    want_slot = np.where(full["send_slot"] < cap, full["send_slot"], -1)
+    if not np.array_equal(d["send_slot"], want_slot):
+        errs.append("overflow: send_slot differs from the full dispatch's entries below the capacity")
+    for k in ("recv_x", "recv_topk_weights", "recv_topk_idx", "recv_src_info"):
+        if not np.array_equal(d[k][:cap], full[k][:cap]):
+            errs.append(f"overflow: {k} of the kept rows differs")
+    return errs
+
+
 def pin_fp8_and_cached(o, inputs: dict, hidden: int | None = None) -> list[str]:
     """fp8 dispatch moves the fp8 rows and their scales to the rows the bf16
     routing defines; cached dispatch reproduces a full dispatch from its

@@ -102,6 +102,22 @@ MUTANTS = {
     "quant_amax_skips_last": ("for (int32_t i = 0; i < g; ++i) {\n                const float m",
                               "for (int32_t i = 0; i < g - 1; ++i) {\n                const float m"),
     "dequant_scale_index": ("scales[t * num_scales + i / g]", "scales[t * num_scales + i % num_scales]"),
+    "dequant_scale_dropped": ("out[t * H + i] = orc_f32_to_bf16_rne(v * scales[t * num_scales + i / g]);",
+                              "out[t * H + i] = orc_f32_to_bf16_rne(v);"),
+    "rdma_prefix_skips_node_first_rank": (
+        "for (int32_t r = n * 8; r < R && r < (n + 1) * 8; ++r)\n                    any |= is_token_in_rank[t * R + r] != 0;",
+        "for (int32_t r = n * 8 + 1; r < R && r < (n + 1) * 8; ++r)\n                    any |= is_token_in_rank[t * R + r] != 0;"),
+    "rdma_prefix_not_cumulative": ("running += any;", "running = any;"),
+    "gbl_counts_rank0_column": ("running += is_token_in_rank[t * R + r] != 0;", "running += is_token_in_rank[t * R] != 0;"),
+    "recv_rdma_prefix_exclusive": ("sum += num_tokens_per_rdma_rank[n];\n        recv_rdma_rank_prefix_sum[n] = sum;",
+                                   "recv_rdma_rank_prefix_sum[n] = sum;\n        sum += num_tokens_per_rdma_rank[n];"),
+    "num_recv_is_last_rank": ("*num_recv_tokens = sum;", "*num_recv_tokens = num_tokens_per_rank[R - 1];"),
+    "notify_rank_count_unchecked": ("if (running != num_tokens_per_rank[r]) status |= ORC_COUNT_MISMATCH;", ";"),
+    "notify_node_count_unchecked": ("if (running != num_tokens_per_rdma_rank[n]) status |= ORC_COUNT_MISMATCH;", ";"),
+    "overflow_row_not_advanced": ("status |= ORC_RECV_OVERFLOW;\n                    ++row;\n                    continue;",
+                                  "status |= ORC_RECV_OVERFLOW;\n                    continue;"),
+    "weights_of_slot0": ("recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K + j] : 0.0f;",
+                         "recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K] : 0.0f;"),
 }
 
 CHILD = textwrap.dedent("""
@@ -117,6 +133,7 @@ CHILD = textwrap.dedent("""
               lambda: pins.pin_golden_grouping(o), lambda: pins.pin_group_by_expert(o, inputs.generate("tiny"), 4),
               lambda: pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32),
               lambda: pins.pin_dispatch_prefix_checks(o, inputs.generate("tiny")),
+              lambda: pins.pin_count_checks_and_overflow(o, inputs.generate("sweep")),
               lambda: pins.pin_bruteforce(o), lambda: pins.pin_e4m3(o), lambda: pins.pin_quantize(o)]
     errs = []
     for check in checks:  # in order, stopping at the first pin that fails

@@ -133,6 +133,10 @@ def test_edge_receive_capacity_overflow(orc, workload_inputs):
     assert np.sort(dis["send_slot"][dis["send_slot"] >= 0]).tolist() == list(range(cap))
 
 
+def test_count_checks_and_overflow(orc, workload_inputs):
+    assert pins.pin_count_checks_and_overflow(orc, workload_inputs("sweep")) == []
+
+
 @pytest.mark.parametrize("name", ["tiny", "sweep", "skew"])
 def test_fp8_and_cached_dispatch(orc, workload_inputs, name):
     assert pins.pin_fp8_and_cached(orc, workload_inputs(name), hidden=None if name == "tiny" else 512) == []
