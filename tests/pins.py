@@ -826,3 +826,84 @@ def pin_quantize(o) -> list[str]:
     if not np.all(np.abs(back - xf) <= bound):
         errs.append("dequantize(quantize(x)) strays from x")
     return errs
+
+
+# --------------------------------------------------------------------------- status bits
+def pin_flags(o) -> list[str]:
+    """Each status bit fires where the definitions put it, and the offending item is skipped exactly as if it
+    were masked: topk ids outside [-1, E) in layout; send_slot entries outside [-1, N) in combine (N itself
+    included); a local id outside [-1, E/R) in a slab row of the grouping.  Consistent inputs raise nothing.
+    Combined weights start from zero whatever the output buffer held before."""
+    import ctypes
+
+    import oracle as _oracle
+
+    errs = []
+    rng = np.random.default_rng(21)
+    T, K, E, R, C, H = 40, 4, 16, 4, 3, 16
+    idx = np.stack([rng.choice(E, K, replace=False) for _ in range(T)]).astype(np.int64)
+    bad = idx.copy()
+    bad[3, 1], bad[7, 0], bad[9, 3] = E, -2, E + 5
+    masked = bad.copy()
+    masked[3, 1] = masked[7, 0] = masked[9, 3] = -1
+    lb, lm = o.layout(bad, E, R), o.layout(masked, E, R)
+    if lb["status"] != _oracle.BAD_TOPK_IDX or lm["status"] != 0:
+        errs.append(f"layout status {lb['status']} / {lm['status']}, want the bad-id bit / 0")
+    for k in ("num_tokens_per_rank", "num_tokens_per_rdma_rank", "num_tokens_per_expert", "is_token_in_rank"):
+        if not np.array_equal(lb[k], lm[k]):
+            errs.append(f"layout: a bad id not treated as masked in {k}")
+    # combine: entries at N, below -1 and past N skipped and flagged
+    note = o.notify(lm["is_token_in_rank"], lm["num_tokens_per_rank"], lm["num_tokens_per_rdma_rank"],
+                    lm["num_tokens_per_expert"], C, 1)
+    x = _bf16_from_float(rng.integers(-8, 8, size=(T, H)).astype(np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    d = o.dispatch(x, masked, w, lm["is_token_in_rank"], note["gbl_channel_prefix_matrix"],
+                   note["recv_gbl_rank_prefix_sum"], E)
+    n = note["num_recv_tokens"]
+    y = _bf16_from_float(rng.integers(-8, 8, size=(n, H)).astype(np.float32))
+    ss = d["send_slot"].copy()
+    free = np.argwhere(ss == -1)
+    used = np.argwhere(ss >= 0)
+    ss_bad = ss.copy()
+    ss_bad[tuple(free[0])] = n
+    ss_bad[tuple(free[1])] = -2
+    ss_bad[tuple(used[0])] = n + 3
+    ss_ref = np.where((ss_bad < -1) | (ss_bad >= n), -1, ss_bad).astype(np.int32)
+    # one more row of data past N in y and the weights: an entry equal to N must not reach it
+    y_ext = np.vstack([y, _bf16_from_float(np.full((1, H), 3.0, np.float32))])
+    w_ext = np.vstack([d["recv_topk_weights"], np.full((1, K), 0.5, np.float32)])
+    cb, cr = o.combine(y_ext, w_ext, ss_bad, n), o.combine(y_ext, w_ext, ss_ref, n)
+    if cb["status"] != _oracle.BAD_SEND_SLOT or cr["status"] != 0:
+        errs.append(f"combine status {cb['status']} / {cr['status']}, want the bad-slot bit / 0")
+    ss_n = ss.copy()
+    ss_n[tuple(free[0])] = n
+    if o.combine(y_ext, w_ext, ss_n, n)["status"] != _oracle.BAD_SEND_SLOT:
+        errs.append("combine: an entry equal to N not flagged")
+    if not (np.array_equal(cb["combined_x"], cr["combined_x"]) and
+            np.array_equal(cb["combined_topk_weights"], cr["combined_topk_weights"])):
+        errs.append("combine: a bad slot not skipped")
+    # combined weights start from zero: the same call with output buffers full of stale values
+    recv_w = np.ascontiguousarray(d["recv_topk_weights"], dtype=np.float32)
+    out = np.full((T, H), 0x3F80, np.uint16)
+    cw = np.full((T, K), 7.0, np.float32)
+    scratch = np.full(H, 5.0, np.float32)
+    p = lambda a: a.ctypes.data_as(ctypes.c_void_p)  # noqa: E731
+    o.lib.oracle_combine(T, H, K, R, n, p(np.ascontiguousarray(y)), p(recv_w), p(ss_ref), p(out), p(cw), p(scratch))
+    if not (np.array_equal(out, cr["combined_x"]) and np.array_equal(cw, cr["combined_topk_weights"])):
+        errs.append("combine: outputs depend on what the output buffers held")
+    # grouping: a bad local id in a slab row is flagged and skipped like a masked slot
+    note4 = o.notify(lm["is_token_in_rank"], lm["num_tokens_per_rank"], lm["num_tokens_per_rdma_rank"],
+                     lm["num_tokens_per_expert"], C, 4)
+    ridx = d["recv_topk_idx"].copy()
+    row, j = np.argwhere(ridx >= 0)[5]
+    ridx_bad, ridx_masked = ridx.copy(), ridx.copy()
+    ridx_bad[row, j], ridx_masked[row, j] = E // R, -1
+    args = (d["recv_topk_weights"], note4["recv_gbl_rank_prefix_sum"], note4["num_recv_tokens_per_expert"], E)
+    gb = o.group_by_expert(d["recv_x"], ridx_bad, *args)
+    gm = o.group_by_expert(d["recv_x"], ridx_masked, *args)
+    if gb["status"] != _oracle.BAD_TOPK_IDX or gm["status"] != 0:
+        errs.append(f"grouping status {gb['status']} / {gm['status']}, want the bad-id bit / 0")
+    for k in ("grouped_x", "grouped_row", "slot_pos"):
+        if not np.array_equal(gb[k], gm[k]):
+            errs.append(f"grouping: a bad local id not skipped ({k})")
+    return errs

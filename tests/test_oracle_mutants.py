@@ -116,6 +116,31 @@ MUTANTS = {
     "notify_node_count_unchecked": ("if (running != num_tokens_per_rdma_rank[n]) status |= ORC_COUNT_MISMATCH;", ";"),
     "overflow_row_not_advanced": ("status |= ORC_RECV_OVERFLOW;\n                    ++row;\n                    continue;",
                                   "status |= ORC_RECV_OVERFLOW;\n                    continue;"),
+    "bad_topk_not_flagged": ("        *status |= ORC_BAD_TOPK_IDX;\n        return 0;", "        return 0;"),
+    "combine_bad_slot_not_flagged": (
+        "            if (s < -1 || s >= num_recv) {\n                status |= ORC_BAD_SEND_SLOT;\n                continue;\n"
+        "            }\n            float W = 0.0f;",
+        "            if (s < -1 || s >= num_recv) {\n                continue;\n            }\n            float W = 0.0f;"),
+    "combine_slot_bound_inclusive": (
+        "            if (s < -1 || s >= num_recv) {\n                status |= ORC_BAD_SEND_SLOT;\n                continue;\n"
+        "            }\n            float W = 0.0f;",
+        "            if (s < -1 || s > num_recv) {\n                status |= ORC_BAD_SEND_SLOT;\n                continue;\n"
+        "            }\n            float W = 0.0f;"),
+    "combined_weights_not_cleared": (
+        "        if (combined_topk_weights)\n            for (int32_t j = 0; j < K; ++j) combined_topk_weights[t * K + j] = 0.0f;",
+        ""),
+    "combine_acc_not_cleared": ("        for (int32_t i = 0; i < H; ++i) acc_scratch[i] = 0.0f;", ""),
+    "group_bad_id_not_flagged": (
+        "if (i < last * K && (recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er)) status |= ORC_BAD_TOPK_IDX;", ";"),
+    "group_reads_slack_ids": (
+        "if (i < last * K && (recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er)) status |= ORC_BAD_TOPK_IDX;",
+        "if ((recv_topk_idx[i] < -1 || recv_topk_idx[i] >= er)) status |= ORC_BAD_TOPK_IDX;"),
+    "group_overflow_not_flagged": ("                        status |= ORC_RECV_OVERFLOW;\n                        continue;",
+                                   "                        continue;"),
+    "recv_idx_unmasked": ("recv_topk_idx[row * K + j] = on_r ? e - (int64_t)r * experts_per_rank : -1;",
+                          "recv_topk_idx[row * K + j] = e - (int64_t)r * experts_per_rank;"),
+    "fp8_scales_of_row": ("recv_x_scales[row * num_scales + i] = x_scales[t * num_scales + i];",
+                          "recv_x_scales[row * num_scales + i] = x_scales[(row % T) * num_scales + i];"),
     "weights_of_slot0": ("recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K + j] : 0.0f;",
                          "recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K] : 0.0f;"),
 }
@@ -133,7 +158,7 @@ CHILD = textwrap.dedent("""
               lambda: pins.pin_golden_grouping(o), lambda: pins.pin_group_by_expert(o, inputs.generate("tiny"), 4),
               lambda: pins.pin_group_by_expert(o, inputs.generate("sweep"), 1, hidden=32),
               lambda: pins.pin_dispatch_prefix_checks(o, inputs.generate("tiny")),
-              lambda: pins.pin_count_checks_and_overflow(o, inputs.generate("sweep")),
+              lambda: pins.pin_count_checks_and_overflow(o, inputs.generate("sweep")), lambda: pins.pin_flags(o),
               lambda: pins.pin_bruteforce(o), lambda: pins.pin_e4m3(o), lambda: pins.pin_quantize(o)]
     errs = []
     for check in checks:  # in order, stopping at the first pin that fails

@@ -133,6 +133,10 @@ def test_edge_receive_capacity_overflow(orc, workload_inputs):
     assert np.sort(dis["send_slot"][dis["send_slot"] >= 0]).tolist() == list(range(cap))
 
 
+def test_status_flags(orc):
+    assert pins.pin_flags(orc) == []
+
+
 def test_count_checks_and_overflow(orc, workload_inputs):
     assert pins.pin_count_checks_and_overflow(orc, workload_inputs("sweep")) == []
 
