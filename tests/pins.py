@@ -906,4 +906,26 @@ def pin_flags(o) -> list[str]:
     for k in ("grouped_x", "grouped_row", "slot_pos"):
         if not np.array_equal(gb[k], gm[k]):
             errs.append(f"grouping: a bad local id not skipped ({k})")
+    # the grouping's outputs (rows, scales, row indices, weights, padding included) do not depend on what the
+    # output buffers held: the same call with buffers full of stale values
+    xs = rng.standard_normal((d["recv_x"].shape[0], 3)).astype(np.float32)
+    fresh = o.group_by_expert(d["recv_x"], ridx_masked, *args, recv_x_scales=xs)
+    m = fresh["num_grouped_rows"]
+    rx = np.ascontiguousarray(d["recv_x"])
+    gx = np.full((m, H), 0xABAB, np.uint16)
+    gs = np.full((m, 3), 7.0, np.float32)
+    grow = np.full(m, 99, np.int32)
+    gw = np.full(m, 9.0, np.float32)
+    pos = np.full(ridx.shape, 77, np.int32)
+    mm = np.zeros(1, np.int32)
+    idx_c = np.ascontiguousarray(ridx_masked, dtype=np.int64)
+    w_c = np.ascontiguousarray(d["recv_topk_weights"], dtype=np.float32)
+    gbl = np.ascontiguousarray(note4["recv_gbl_rank_prefix_sum"], dtype=np.int32)
+    al = np.ascontiguousarray(note4["num_recv_tokens_per_expert"], dtype=np.int32)
+    o.lib.oracle_group_by_expert(E, R, K, H * 2, p(rx), p(xs), 3, p(idx_c), p(w_c), p(gbl), p(al), rx.shape[0], m,
+                                 p(gx), p(gs), p(grow), p(gw), p(pos), p(mm))
+    for k, got in (("grouped_x", gx), ("grouped_x_scales", gs), ("grouped_row", grow), ("grouped_weights", gw),
+                   ("slot_pos", pos)):
+        if not np.array_equal(got, fresh[k]):
+            errs.append(f"grouping: {k} depends on what the output buffer held")
     return errs

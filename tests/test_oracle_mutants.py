@@ -141,6 +141,17 @@ MUTANTS = {
                           "recv_topk_idx[row * K + j] = e - (int64_t)r * experts_per_rank;"),
     "fp8_scales_of_row": ("recv_x_scales[row * num_scales + i] = x_scales[t * num_scales + i];",
                           "recv_x_scales[row * num_scales + i] = x_scales[(row % T) * num_scales + i];"),
+    "group_padding_x_not_zeroed": ("memset(grouped_x + pos * row_bytes, 0, (size_t)row_bytes);", ";"),
+    "group_padding_scales_not_zeroed": (
+        "for (int32_t s = 0; s < num_scales; ++s) grouped_x_scales[pos * num_scales + s] = 0.0f;", ";"),
+    "group_padding_weight_not_zeroed": ("                grouped_weights[pos] = 0.0f;", ";"),
+    "group_slot_pos_not_reset": ("        slot_pos[i] = -1;", ";"),
+    "cached_scales_not_copied": (
+        "for (int32_t i = 0; i < num_scales; ++i) recv_x_scales[s * num_scales + i] = x_scales[t * num_scales + i];",
+        ";"),
+    "e4m3_decode_sign_dropped": ("return sign ? -mag : mag;", "return mag;"),
+    "quant_codes_group_stride": ("codes[t * H + (int64_t)q * g + i] = orc_e4m3_rne(v);",
+                                 "codes[t * H + i] = orc_e4m3_rne(v);"),
     "weights_of_slot0": ("recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K + j] : 0.0f;",
                          "recv_topk_weights[row * K + j] = on_r ? topk_weights[t * K] : 0.0f;"),
 }
