@@ -448,3 +448,24 @@ def test_quantising_dispatches_with_no_receive_capacity():
     ep.ep_dispatch_cached_to_fp8(shape, to_dev_bf16(x), S, none, 4, out, outs, st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0 and (out == 0x77).all() and (outs == -5.0).all()
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_quantize_dequantize_random_shapes(case):
+    """Seeded random shapes for the quantiser and the dequantiser: 1 to 3000 rows, groups of 16 to 1024
+    channels, 1 to 64 groups a row (rows up to 16384 channels), bit for bit against the oracle both ways."""
+    rng = np.random.default_rng(9000 + case)
+    g = int(rng.choice([16, 32, 64, 128, 256, 512, 1024]))
+    S = int(rng.integers(1, min(64, 16384 // g) + 1))
+    rows = int(rng.choice([1, 2, 7, 63, 64, 65, 500, 3000]))
+    print(f"[quant] random case {case}: rows={rows} hidden={g * S} groups of {g}", flush=True)
+    x = pins.quantize_groups(rng, rows, g * S, S)
+    gq, gs, dq, ds = _quant_gpu(x, S)
+    o = oracle.Oracle()
+    rq, rs = o.quantize_e4m3(x, S)
+    _same_scales("scales", gs, rs)
+    _same_codes("codes", gq, rq)
+    back = torch.empty((rows, g * S), dtype=torch.bfloat16, device="cuda")
+    ep.ep_dequantize_fp8(dq, ds, rows, g * S, S, back)
+    torch.cuda.synchronize()
+    assert np.array_equal(bf16_host(back), o.dequantize_e4m3(rq, rs))
