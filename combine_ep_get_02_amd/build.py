@@ -43,7 +43,7 @@ def build_c_example(verbose: bool = False) -> str:
     # the HIP runtime headers must be told the platform when a plain C compiler reads them
     cmd = ["gcc", "-std=c11", "-O2", "-Wall", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(ROOT, "include"), "-I",
            os.path.join(ROCM, "include"), C_EXAMPLE_SOURCE, "-L", PKG, "-lep", "-L", os.path.join(ROCM, "lib"),
-           "-lamdhip64", "-Wl,-rpath,$ORIGIN/../combine_ep_get_02_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
+           "-lamdhip64", "-lm", "-Wl,-rpath,$ORIGIN/../combine_ep_get_02_amd", "-Wl,-rpath," + os.path.join(ROCM, "lib"),
            "-o", C_EXAMPLE]
     if verbose:
         print(" ".join(cmd), flush=True)

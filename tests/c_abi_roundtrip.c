@@ -9,10 +9,15 @@
  *     token (as values: the fp32 accumulator starts at +0) and +0 elsewhere;
  *   - the grouping holds one entry per valid topk slot, each grouped row is
  *     the receive row it names, and the grouped row total is the sum of the
- *     aligned per-expert counts.
+ *     aligned per-expert counts;
+ *   - the fp8 path: the quantiser codes each group's largest magnitude as
+ *     +-448; the quantising dispatch assigns the same rows as ep_dispatch and
+ *     delivers the quantiser's codes and scales there, as does its cached
+ *     mode; the dequantised rows are within half an E4M3 step of x.
  * Built by the package build step (gcc, C11) and run by the GPU tests.
  * Exit status 0 and a final "c abi roundtrip ok" line on success.
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -196,6 +201,58 @@ int main(void) {
         }
     }
     if (entries != valid_slots) FAIL("%d grouped entries, %d valid slots", entries, valid_slots);
+
+    /* the fp8 path: quantiser, quantising dispatch (and its cached mode), dequantiser */
+    const int S = H / 128;
+    uint8_t *d_q = dev_alloc((size_t)T * H), *d_rq = dev_alloc((size_t)n * H), *d_cq = dev_alloc((size_t)n * H);
+    float *d_qs = dev_alloc(4 * (size_t)T * S), *d_rs = dev_alloc(4 * (size_t)n * S), *d_cs = dev_alloc(4 * (size_t)n * S);
+    int32_t *send_slot8 = dev_alloc(4 * (size_t)T * R);
+    void *back = dev_alloc((size_t)n * H * 2);
+    CHECK_EP(ep_quantize_fp8(d_x, T, H, S, d_q, d_qs, stream));
+    CHECK_EP(ep_dispatch_to_fp8(&shape, d_x, S, d_idx, d_w, in_rank, gbl, recv_gbl, ws, ws_bytes, n, d_rq, d_rs, recv_w,
+                                recv_idx, src_info, send_slot8, status, stream));
+    CHECK_EP(ep_dispatch_cached_to_fp8(&shape, d_x, S, send_slot8, n, d_cq, d_cs, status, stream));
+    CHECK_EP(ep_dequantize_fp8(d_rq, d_rs, n, H, S, back, stream));
+    CHECK_HIP(hipStreamSynchronize(stream));
+    uint8_t *h_q = malloc((size_t)T * H), *h_rq = malloc((size_t)n * H), *h_cq = malloc((size_t)n * H);
+    float *h_qs = malloc(4 * (size_t)T * S), *h_rs = malloc(4 * (size_t)n * S), *h_cs = malloc(4 * (size_t)n * S);
+    int32_t *h_slot8 = malloc(4 * (size_t)T * R);
+    uint16_t *h_back = malloc(2 * (size_t)n * H);
+    CHECK_HIP(hipMemcpy(h_q, d_q, (size_t)T * H, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_rq, d_rq, (size_t)n * H, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_cq, d_cq, (size_t)n * H, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_qs, d_qs, 4 * (size_t)T * S, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_rs, d_rs, 4 * (size_t)n * S, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_cs, d_cs, 4 * (size_t)n * S, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_slot8, send_slot8, 4 * (size_t)T * R, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(h_back, back, 2 * (size_t)n * H, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(&h_status, status, 4, hipMemcpyDeviceToHost));
+    if (h_status != 0) FAIL("device status %d after the fp8 path", h_status);
+    for (int t = 0; t < T; ++t) {
+        for (int q = 0; q < S; ++q) { /* the group's largest magnitude (first one) is coded +-448 */
+            int at = q * 128;
+            for (int i = q * 128; i < (q + 1) * 128; ++i)
+                if (fabsf(bf16_value(x[t * H + i])) > fabsf(bf16_value(x[t * H + at]))) at = i;
+            if (bf16_value(x[t * H + at]) != 0.0f && (h_q[(size_t)t * H + at] & 0x7f) != 0x7e)
+                FAIL("quantiser: largest magnitude of token %d group %d coded 0x%02x", t, q, h_q[(size_t)t * H + at]);
+        }
+        for (int r = 0; r < R; ++r) {
+            const int s = h_slot8[t * R + r];
+            if (s != h_slot[t * R + r]) FAIL("quantising dispatch: send_slot[%d][%d] = %d, ep_dispatch %d", t, r, s,
+                                             h_slot[t * R + r]);
+            if (s < 0) continue;
+            if (memcmp(h_rq + (size_t)s * H, h_q + (size_t)t * H, H) || memcmp(h_cq + (size_t)s * H, h_q + (size_t)t * H, H))
+                FAIL("row %d does not hold token %d's codes", s, t);
+            if (memcmp(h_rs + (size_t)s * S, h_qs + (size_t)t * S, 4 * S) ||
+                memcmp(h_cs + (size_t)s * S, h_qs + (size_t)t * S, 4 * S))
+                FAIL("row %d does not hold token %d's scales", s, t);
+            for (int i = 0; i < H; ++i) { /* half an E4M3 step (1/16) plus the bf16 rounding (1/256) */
+                const float xv = bf16_value(x[t * H + i]), bv = bf16_value(h_back[(size_t)s * H + i]);
+                if (fabsf(bv - xv) > fabsf(xv) * (1.0f / 16 + 1.0f / 256) + 1e-6f)
+                    FAIL("dequantised row %d channel %d = %g, x = %g", s, i, bv, xv);
+            }
+        }
+    }
 
     /* host-side argument checks answer without touching the device */
     ep_shape_t bad = shape;
