@@ -1,7 +1,8 @@
 """The library driven from plain C (tests/c_abi_roundtrip.c, built by the
-package build step): layout, notify, dispatch, combine and the grouping by
-expert through include/ep.h with device memory from the HIP runtime alone,
-checked on the host for properties that hold for any routing."""
+package build step): layout, notify, dispatch, combine, the grouping by expert
+and the fp8 path (quantiser, quantising dispatch and its cached mode,
+dequantiser) through include/ep.h with device memory from the HIP runtime
+alone, checked on the host for properties that hold for any routing."""
 import os
 import subprocess
 
