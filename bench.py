@@ -491,7 +491,9 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the cached-mode and fp8-row dispatch timings reported beside the metric")
+                    help="skip the timings reported beside the metric: dispatch without a workspace, cached mode, "
+                         "fp8 rows, the E4M3 quantiser and dequantiser, the quantising dispatches, the grouping "
+                         "and the dispatch straight into the grouped layout")
     ap.add_argument("--no-graph", action="store_true", help="skip the HIP-graph replay timing of the step")
     ap.add_argument("--no-other-workloads", action="store_true",
                     help="skip the dispatch/combine timings of the other four workloads reported beside the metric")
