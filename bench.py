@@ -15,9 +15,11 @@ pair per step around the two calls, averaged).  Each kernel's own average
 launch duration -- the roofline figure -- is taken from back-to-back launches
 between one event pair, which is what a kernel trace reports for it.
 ``ms_per_step`` is the wall time of a whole step including layout and notify.
-Beside the metric: the cached-mode and fp8-row dispatch forms, the grouping by
-expert and the dispatch straight into the grouped layout, a cold-cache
-cross-check and the oracle's throughput on the host.  Prints one JSON line.
+Beside the metric: the cached-mode and fp8-row dispatch forms, the E4M3
+quantiser, the quantising dispatch and its cached mode, the dequantiser, the
+grouping by expert and the dispatch straight into the grouped layout, a
+cold-cache cross-check and the oracle's throughput on the host.  Prints one
+JSON line.
 
     python bench.py [--steps K] [--warmup W] [--workload prefill] [--no-cpu-baseline] [--no-variants]
                     [--no-other-workloads] [--cold-steps N]
