@@ -316,8 +316,8 @@ ep_status_t ep_dequantize_fp8(const void *x_fp8, const float *x_scales, int64_t 
  * Cached-mode dispatch.  [mscclpp ht_runtime.cc, internodeDispatch / intranodeDispatch with
  * cachedMode: the layout of an earlier call is reused -- no counting, no notification]
  * Copies row t to recv_x[send_slot[t][r]] for every r with send_slot[t][r] >= 0, where
- * send_slot [t][R] was written by an earlier ep_dispatch / ep_dispatch_fp8 for the same
- * routing.  Rows are hidden * elem_bytes bytes (elem_bytes 2 = bf16, 1 = fp8; a multiple
+ * send_slot [t][R] was written by an earlier ep_dispatch / ep_dispatch_fp8 / ep_dispatch_to_fp8
+ * for the same routing.  Rows are hidden * elem_bytes bytes (elem_bytes 2 = bf16, 1 = fp8; a multiple
  * of 16); num_scales float scales per token go along when num_scales > 0.  No metadata
  * is written.  Entries outside [-1, recv_capacity) are skipped and flagged
  * (EP_DEV_BAD_SEND_SLOT).  Needs no workspace and no layout/notify call.  form: EP_FORM_AUTO
